@@ -1,0 +1,171 @@
+/*
+ * tq.h -- C ABI of libtq: TurboQuant-style two-stage compression of attention K/V vectors
+ * and attention / top-k search computed from the compressed codes, on AMD MI355X (gfx950).
+ *
+ * The method (sources: the pages' titles and sections):
+ *   stage 1  7minutos.es TurboQuant walkthrough, "Etapa 1 (PolarQuant)": rotate with a random
+ *            orthogonal Pi, quantise each coordinate of the direction with a Lloyd-Max codebook
+ *            for the Beta law of a rotated coordinate, store indices; sudonull.com "Cómo
+ *            funciona PolarQuant": the radius (norm) is stored beside the direction.
+ *   stage 2  same walkthrough, "Etapa 2 (Corrección Residual)": the residual's sign sketch
+ *            sign(S r) under a Gaussian projection S, plus the residual's L2 norm.
+ *   decode   same walkthrough, the K~_QJL formula and K~ = K^ + K~_QJL; hada.io TurboQuant
+ *            page, "QJL: técnica de 1 bit com overhead zero": the query stays in high precision;
+ *            TurboESM summary, section 2.E: scores, online softmax and the weighted sum of V
+ *            over the compressed cache without materialising a dequantised copy.
+ *   search   hada.io page, "Desempenho em busca vetorial": inner-product top-k from the codes.
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers unless the parameter name starts with host_.
+ *   - The caller owns all memory.  No call allocates or frees device memory and none
+ *     synchronises; kernels are enqueued on `stream` (a hipStream_t, NULL = default stream).
+ *   - Argument checks run on the host before any launch and return a negative status; a
+ *     failed launch returns TQ_EHIP.  Faults inside kernels surface at the caller's next
+ *     synchronisation.  No C++ exception crosses this interface.
+ *   - Calls are reentrant: the library keeps no mutable global state.
+ *   - Inputs must be finite.  A vector norm of 65520 or more does not fit fp16 and is out of
+ *     contract (it is stored as +inf).
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = -1,       /* NULL pointer, negative size, inconsistent shapes          */
+  TQ_EUNSUPPORTED = -2, /* (d, bits, m, heads-per-group, dtype) not built            */
+  TQ_EALIGN = -3,       /* plane stride or pointer alignment violated                */
+  TQ_EWORKSPACE = -4,   /* workspace NULL or smaller than tq_workspace_bytes         */
+  TQ_EHIP = -5          /* a HIP launch failed                                       */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
+
+/* Shared codec of one (d, bits, m) configuration.  Borrowed device pointers.
+ *   rot         [n_rot][d][d] fp32 row-major, y = rot[r] x (Haar Pi, or Pi composed with a
+ *               per-head basis: TurboESM summary, section 2.B, one rotation per layer/head).
+ *   sketch      [m][d] fp32 row-major Gaussian S (NULL when m == 0: stage 1 only).
+ *   centroids   [2^bits] fp32 ascending Lloyd-Max levels of the unit-direction coordinate.
+ *   thresholds  [2^bits - 1] fp32 midpoints between adjacent centroids.
+ *   vecs_per_rot  vector v of a cache uses rot[min(v / vecs_per_rot, n_rot - 1)]; 0 or
+ *               n_rot == 1 means rot[0] for all.                                           */
+typedef struct {
+  int32_t d, bits, m;
+  int32_t n_rot;
+  int64_t vecs_per_rot;
+  const float *rot;
+  const float *sketch;
+  const float *centroids;
+  const float *thresholds;
+} tq_codec;
+
+/* Compressed vectors as three planes (structure of arrays), caller-allocated.
+ *   idx    [n][idx_stride] bytes: the bits-per-coordinate index stream, coordinate i at bit
+ *          bits*i, least significant bit first, little-endian bytes; pad bits and bytes zero.
+ *          idx_stride >= ceil(d*bits/8) and a multiple of 4.
+ *   sign   [n][sign_stride] bytes: QJL bit j = [ (S r)_j >= 0 ], same bit order; NULL when
+ *          m == 0.  sign_stride >= ceil(m/8) and a multiple of 4.
+ *   norms  [n] uint32: low 16 bits fp16 ||x|| (round to nearest even of the exact norm), high
+ *          16 bits fp16 ||r|| (the stage-1 residual in the rotated space).
+ * Plane base pointers must be 16-byte aligned.                                              */
+typedef struct {
+  uint8_t *idx;
+  int64_t idx_stride;
+  uint8_t *sign;
+  int64_t sign_stride;
+  uint32_t *norms;
+} tq_codes;
+
+/* ---------------------------------------------------------------- codec construction (host) */
+
+/* Haar-random orthogonal d x d matrix (fp32, row-major) from `seed`: QR (Householder, fp64)
+ * of a Gaussian matrix drawn from the SplitMix64 stream `seed` (Box-Muller pairs, row-major
+ * fill), with the signs of R's diagonal moved into Q.  Walkthrough "Etapa 1": y = R x with R
+ * a random orthogonal matrix.  host_out: [d][d].  3 <= d <= 1024.                          */
+int tq_make_rotation(uint64_t seed, int32_t d, float *host_out);
+
+/* n_rot rotations Pi @ B_r (composed in fp64, stored fp32) with Pi = Haar(seed_pi) and
+ * B_r = Haar(host_basis_seeds[r]).  host_out: [n_rot][d][d].                                */
+int tq_make_head_rotations(uint64_t seed_pi, const uint64_t *host_basis_seeds, int32_t n_rot,
+                           int32_t d, float *host_out);
+
+/* Gaussian QJL projection S (fp32 [m][d] row-major) from the SplitMix64 stream `seed`
+ * (walkthrough "Etapa 2": a random projection matrix S).                                    */
+int tq_make_sketch(uint64_t seed, int32_t m, int32_t d, float *host_out);
+
+/* Lloyd-Max codebook with 2^bits levels for the density (1-x^2)^((d-3)/2)/B(1/2,(d-1)/2) of
+ * one coordinate of a uniform unit vector (walkthrough "Etapa 1": the Beta law and the
+ * Lloyd-Max iteration; the codebook depends only on (d, bits)).  fp64 iteration with
+ * Gauss-Legendre cell integrals, symmetrised, rounded to fp32.
+ * host_centroids: [2^bits] ascending; host_thresholds: [2^bits - 1].  1 <= bits <= 8.       */
+int tq_make_codebook(int32_t d, int32_t bits, float *host_centroids, float *host_thresholds);
+
+/* ---------------------------------------------------------------- device operations */
+
+/* Encode n vectors (stages 1 and 2; walkthrough "Etapa 1" and "Etapa 2").
+ *   x        [n] rows of ld_x elements of type dt (row v starts at x + v*ld_x elements).
+ *   flags    TQ_ENC_PRE_ROTATED: x already holds y = Pi x as fp32 (dt must be TQ_F32); the
+ *            stored norm is then that of y.  Otherwise the norm is that of x and y = Pi x is
+ *            computed on the device.
+ *   first    index of x's first row in the whole cache (selects the per-block rotation).
+ *   y_tap    optional [n][d] fp32 output of the rotated vectors used (NULL to skip).
+ * Per vector: n16 = fp16(||x||); idx_i = #{ j : y_i >= fl32(nbar * t_j) }; r_i =
+ * fl32(y_i - fl32(nbar * c[idx_i])); rn16 = fp16(||r||); sign bits of S r (exact sign).
+ * Supported (d, bits, m): d in {64, 128, 200}, bits in {2, 3, 4}, m in {0, d}.             */
+#define TQ_ENC_PRE_ROTATED 1u
+int tq_encode(const tq_codec *codec, const void *x, tq_dtype dt, int64_t n, int64_t ld_x,
+              uint32_t flags, int64_t first, tq_codes out, float *y_tap, void *stream);
+
+/* Estimated logits of every (query head, key) pair (spec estimator):
+ *   s = nbar * <Pi q, c[idx]> + rnbar * sqrt(pi/2)/m * <S Pi q, 2 bits - 1>
+ * (walkthrough "Etapa 2", K~ = K^ + K~_QJL, taken in the rotated space).
+ *   q       [n_seq][hq][d] fp32 queries (post-RoPE).  The cache k holds [n_seq][hkv][n_keys]
+ *           vectors; query head h reads kv head h / (hq / hkv) (hq % hkv == 0).
+ *   logits  [n_seq][hq][n_keys] fp32, unscaled (no 1/sqrt(d)).
+ *   ws      workspace of tq_workspace_bytes(TQ_OP_SCORES, ...) bytes, 256-byte aligned.     */
+int tq_scores(const tq_codec *kc, const float *q, int64_t n_seq, int32_t hq, int32_t hkv,
+              int64_t n_keys, tq_codes k, float *logits, void *ws, size_t ws_bytes, void *stream);
+
+/* One decode step of attention over the compressed cache (TurboESM summary, section 2.E):
+ * out[s][h] = sum_n softmax_n(scale * s_n) * v~_n, with s_n the estimate of tq_scores and
+ * v~_n = Pi_V^T (nbar_n c_V[idx_n] + [m_V > 0] sqrt(pi/2)/m_V rnbar_n S_V^T (2 bits_n - 1)).
+ *   q [n_seq][hq][d] fp32; caches [n_seq][hkv][n_ctx]; out [n_seq][hq][d] fp32.
+ *   kc, vc may differ in bits and m (e.g. 2-bit + QJL keys, 3-bit values), not in d.       */
+int tq_attend_decode(const tq_codec *kc, const tq_codec *vc, const float *q, int64_t n_seq,
+                     int32_t hq, int32_t hkv, int64_t n_ctx, tq_codes k, tq_codes v, float scale,
+                     float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Inner-product top-k search over an encoded database (one shared rotation):
+ * for each query the k database rows with the largest estimated <q, x> (ties: smaller row
+ * index first).  queries [n_q][d] fp32; out_idx [n_q][k] int64; out_score [n_q][k] fp32.
+ * 1 <= k <= 32.                                                                              */
+int tq_search_topk(const tq_codec *c, const float *queries, int64_t n_q, tq_codes db,
+                   int64_t n_db, int32_t k, int64_t *out_idx, float *out_score, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- helpers */
+
+#define TQ_OP_SCORES 0
+#define TQ_OP_ATTEND 1
+#define TQ_OP_SEARCH 2
+/* Workspace bytes for `op` (0 when none).  SCORES/ATTEND: n_seq, hq, hkv, n = n_keys/n_ctx,
+ * vc used by ATTEND only (may be NULL otherwise).  SEARCH: n_seq = n_q, hq = k, n = n_db.    */
+size_t tq_workspace_bytes(int op, const tq_codec *kc, const tq_codec *vc, int64_t n_seq,
+                          int32_t hq, int32_t hkv, int64_t n);
+
+/* Static description of a status code. */
+const char *tq_status_str(int status);
+
+/* Library version string. */
+const char *tq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H */

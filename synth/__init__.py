@@ -185,3 +185,29 @@ def search_data(n_db: int = SEARCH_N_DB, n_q: int = SEARCH_N_Q, d: int = SEARCH_
 def pre_rotated(n: int, d: int, seed: int) -> np.ndarray:
     """fp32 N(0, 1) vectors standing for already-rotated inputs y (the rotated law of Gaussian data)."""
     return np.random.default_rng(seed).standard_normal((n, d)).astype(np.float32)
+
+
+def random_codes(n: int, d: int, bits: int, m: int, idx_stride: int, sign_stride: int, seed: int):
+    """Synthetic code planes (uniform index/sign bits, plausible fp16 norms) for scoring tests.
+
+    Returns (idx uint8 [n, idx_stride], sign uint8 [n, sign_stride] or None, norms uint32 [n]);
+    bits beyond the record and pad bytes are zero.  The norms are fp16 patterns of
+    |N(0,1)| * sqrt(d) (key norm) and 0.35 |N(0,1)| * sqrt(d) (residual norm).
+    """
+    g = np.random.default_rng(seed)
+    nb = d * bits
+    idx = np.zeros((n, idx_stride), np.uint8)
+    full, rem = divmod(nb, 8)
+    idx[:, :full] = g.integers(0, 256, (n, full), dtype=np.uint8)
+    if rem:
+        idx[:, full] = g.integers(0, 1 << rem, n, dtype=np.uint8)
+    sign = None
+    if m > 0:
+        sign = np.zeros((n, sign_stride), np.uint8)
+        sf, sr = divmod(m, 8)
+        sign[:, :sf] = g.integers(0, 256, (n, sf), dtype=np.uint8)
+        if sr:
+            sign[:, sf] = g.integers(0, 1 << sr, n, dtype=np.uint8)
+    n16 = (np.abs(g.standard_normal(n)) * np.sqrt(d)).astype(np.float16).view(np.uint16).astype(np.uint32)
+    r16 = (0.35 * np.abs(g.standard_normal(n)) * np.sqrt(d)).astype(np.float16).view(np.uint16).astype(np.uint32)
+    return idx, sign, (r16 << 16) | n16

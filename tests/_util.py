@@ -1,0 +1,30 @@
+"""Helpers shared by the GPU parity tests (no method arithmetic: marshalling and comparisons)."""
+
+import numpy as np
+
+from oracle import quantize as oq
+
+
+def to_device_codes(tq, idx, sign, norms, device="cuda"):
+    import torch
+
+    return tq.Codes(torch.from_numpy(np.ascontiguousarray(idx)).to(device),
+                    None if sign is None else torch.from_numpy(np.ascontiguousarray(sign)).to(device),
+                    torch.from_numpy(np.ascontiguousarray(norms).view(np.int32)).to(device))
+
+
+def oracle_codes(idx, sign, norms):
+    return oq.Codes(idx, sign, np.asarray(norms, np.uint32))
+
+
+def rel_err_rows(got, want):
+    """max_n |got - want| / max_n |want| per row of the last axis (want in fp64)."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    num = np.max(np.abs(got - want), axis=-1)
+    den = np.maximum(np.max(np.abs(want), axis=-1), 1e-30)
+    return num / den
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)

@@ -1,0 +1,195 @@
+"""GPU encode parity against the oracle.
+
+Pre-rotated mode: given identical fp32 rotated inputs, the packed index stream, the sign
+stream and the norm words must be bit-identical (the norms and signs are defined by exact
+real quantities on both sides).  Full mode: the rotation is an fp32 contraction on the GPU,
+so y differs from the oracle's correctly rounded y within the contraction's error bound; the
+norm word's low half (the input's norm) must still match exactly, and every other mismatch
+must be explained by that bound.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import codec as oc
+from oracle import quantize as oq
+from tests._util import say
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+tq = pytest.importorskip("vector_quantization_amd")
+
+CASES = [(64, 2, 64), (64, 3, 64), (128, 2, 128), (128, 3, 0), (128, 3, 128), (200, 2, 200), (64, 4, 0),
+         (200, 3, 0)]
+
+
+def _codecs(d, bits, m, rot_seed=1, sketch_seed=2, basis=None, vpr=0):
+    lib = tq.make_codec(d, bits, m, rot_seed, sketch_seed, basis_seeds=basis, vecs_per_rot=vpr)
+    ora = oc.make_codec(d, bits, m, rot_seed, sketch_seed, basis_seeds=basis, vecs_per_rot=vpr)
+    return lib, ora
+
+
+def _edge_rows(d):
+    b = float(np.nextafter(np.float16(1.0), np.float16(2.0)))
+    mid = np.float32(0.5 * (1.0 + b))  # an fp16 midpoint: the norm ties, rounds to even (1.0)
+    rows = np.zeros((6, d), np.float32)
+    rows[1, 3] = mid
+    rows[2, 3] = mid
+    rows[2, 7] = np.float32(2.0 ** -20)  # just above the midpoint
+    rows[3] = np.float32(1e-30)  # tiny (squares far below fp32 range, fine in fp64)
+    rows[4, :] = np.float32(3000.0)  # large norm, still below 65520
+    rows[5, ::2] = np.float32(-0.5)
+    return rows
+
+
+def _gpu_encode(lib_codec, x_np, pre, dtype=None, first=0, tap=False):
+    x = torch.from_numpy(x_np).to("cuda")
+    if dtype is not None:
+        x = x.to(dtype)
+    ytap = torch.empty((x.shape[0], lib_codec.d), dtype=torch.float32, device="cuda") if tap else None
+    codes = tq.encode(lib_codec, x, pre_rotated=pre, first=first, y_tap=ytap)
+    torch.cuda.synchronize()
+    idx, sign, norms = codes.numpy()
+    return idx, sign, norms, (None if ytap is None else ytap.cpu().numpy())
+
+
+@pytest.mark.parametrize("d,bits,m", CASES)
+def test_pre_rotated_bit_exact(d, bits, m):
+    say("encode pre-rotated", d, bits, m)
+    lib, ora = _codecs(d, bits, m)
+    y = np.concatenate([_edge_rows(d), synth.pre_rotated(4099, d, seed=d * 10 + bits)])
+    y[200:300] *= np.float32(1e-3)
+    y[300:400] *= np.float32(300.0)
+    idx, sign, norms, _ = _gpu_encode(lib, y, pre=True)
+    want = oq.encode(y, ora, pre_rotated=True, idx_stride=lib.idx_stride, sign_stride=lib.sign_stride)
+    assert np.array_equal(norms, want.norms)
+    assert np.array_equal(idx, want.idx)
+    if m > 0:
+        assert np.array_equal(sign, want.sign)
+    # the tie row rounds to even
+    assert norms[1] & 0xFFFF == np.float16(1.0).view(np.uint16)
+    assert norms[0] == 0
+
+
+def test_exact_sign_fallback_with_crafted_sketch():
+    # rows of S whose dot product with r is exactly zero force the exact expansion path
+    d, bits, m = 64, 2, 64
+    g = np.random.default_rng(5)
+    S = g.standard_normal((m, d)).astype(np.float32)
+    S[0] = 0
+    S[1] = 0
+    S[1, 0], S[1, 1] = 1.0, -1.0
+    S[2] = 0
+    S[2, 2], S[2, 3] = 3.0, 3.0
+    S[3] = 0
+    S[3, 4], S[3, 5], S[3, 6] = 2.0 ** 30, 1.0, -(2.0 ** 30)
+    rot = np.eye(d, dtype=np.float32)
+    c, t = tq.make_codebook(d, bits)
+    lib = tq.codec_from_arrays(d, bits, m, rot, S, c, t)
+    cb = oc.lloyd_max_beta(d, bits)
+    ora = oc.Codec(d, bits, m, rot[None], S, cb.centroids, cb.thresholds)
+    y = synth.pre_rotated(512, d, seed=77)
+    y[:, 1] = y[:, 0]  # r_0 == r_1: row 1 sums to exactly 0
+    y[:, 3] = -y[:, 2]  # r_3 == -r_2: row 2 sums to exactly 0
+    y[:, 6] = y[:, 4]  # row 3: 2^30 r_4 + r_5 - 2^30 r_4 == r_5
+    idx, sign, norms, _ = _gpu_encode(lib, y, pre=True)
+    want = oq.encode(y, ora, pre_rotated=True, idx_stride=lib.idx_stride, sign_stride=lib.sign_stride, keep=True)
+    assert np.array_equal(norms, want.norms)
+    assert np.array_equal(idx, want.idx)
+    assert np.array_equal(sign, want.sign)
+    bits0 = oq.unpack_bits(sign, 1, m)
+    assert np.all(bits0[:, 0] == 1) and np.all(bits0[:, 1] == 1) and np.all(bits0[:, 2] == 1)
+    assert np.array_equal(bits0[:, 3], (want.resid[:, 5] >= 0).astype(np.uint32))
+
+
+def _explained_mismatches(x, lib, ora, gpu, want, first=0):
+    """Check full-mode GPU codes against the oracle's, allowing only bound-explained differences."""
+    d, bits, m = ora.d, ora.bits, ora.m
+    idx_g, sign_g, norms_g, ytap = gpu
+    x64 = np.asarray(x, np.float64)
+    rid = ora.rot_index(x64.shape[0], first)
+    y_ex = np.empty_like(x64)
+    bound = np.empty_like(x64)
+    for r in np.unique(rid):
+        sel = rid == r
+        P = ora.rot[r].astype(np.float64)
+        y_ex[sel] = x64[sel] @ P.T
+        bound[sel] = (d + 2) * 2.0 ** -24 * (np.abs(x64[sel]) @ np.abs(P).T) + 1e-45
+    # (1) rotation within the fp32 contraction bound
+    assert np.all(np.abs(ytap.astype(np.float64) - y_ex) <= bound)
+    # (2) the input's norm is exact
+    assert np.array_equal(norms_g & 0xFFFF, want.norms & 0xFFFF)
+    # (3) index mismatches only where y is within the bound of a scaled threshold
+    ig = oq.unpack_bits(idx_g, bits, d).astype(np.int64)
+    iw = want.index.astype(np.int64)
+    nbar = oq.f16_value(want.norms & 0xFFFF).astype(np.float32)
+    thr = (nbar[:, None] * ora.thresholds[None, :]).astype(np.float64)
+    near = np.min(np.abs(y_ex[:, :, None] - thr[:, None, :]), axis=2) <= 2 * bound + np.abs(y_ex) * 2.0 ** -23
+    bad = (ig != iw) & ~near
+    assert not bad.any(), np.argwhere(bad)[:5]
+    same_rows = np.all(ig == iw, axis=1)
+    assert np.mean(~same_rows) < 0.02
+    # (4) on rows with equal indices the residuals differ by the y difference only
+    if m > 0:
+        sg = oq.unpack_bits(sign_g, 1, m)
+        sw = want.bits
+        r = want.resid.astype(np.float64)
+        dr = np.abs(ytap.astype(np.float64) - want.y.astype(np.float64)) + 1e-45
+        zb = dr @ np.abs(ora.sketch.astype(np.float64)).T
+        z = r @ ora.sketch.astype(np.float64).T
+        diff = (sg != sw) & same_rows[:, None]
+        assert np.all(np.abs(z[diff]) <= 2 * zb[diff] + 1e-30)
+    rn_diff = ((norms_g >> 16) != (want.norms >> 16)) & same_rows
+    assert np.mean(rn_diff) < 0.01
+    return np.mean(~same_rows)
+
+
+@pytest.mark.parametrize("d,bits,m,dtype", [(64, 2, 64, "float32"), (64, 3, 64, "float16"), (128, 2, 128, "bfloat16"),
+                                            (128, 3, 0, "bfloat16"), (200, 2, 200, "float32")])
+def test_full_mode_matches_within_rotation_bound(d, bits, m, dtype):
+    say("encode full", d, bits, m, dtype)
+    lib, ora = _codecs(d, bits, m)
+    g = np.random.default_rng(d + bits)
+    x = (g.standard_normal((3001, d)) * np.where(g.random(d) < 0.05, 10.0, 1.0)).astype(np.float32)
+    tdt = getattr(torch, dtype)
+    x_rounded = torch.from_numpy(x).to(tdt).to(torch.float32).numpy()  # the values the GPU sees
+    gpu = _gpu_encode(lib, x, pre=False, dtype=tdt, tap=True)
+    want = oq.encode(x_rounded, ora, idx_stride=lib.idx_stride, sign_stride=lib.sign_stride, keep=True)
+    frac = _explained_mismatches(x_rounded, lib, ora, gpu, want)
+    say("  rows with an index flip:", frac)
+
+
+def test_full_mode_per_head_rotations():
+    # ESM-2-shaped slice: per-(layer, head) rotation Pi @ B_h, 3-bit + QJL, fp16 input
+    d, bits, m, N = 64, 3, 64, 256
+    seeds = [synth.esm2_basis_seed(l, h) for l in range(2) for h in range(3)]
+    lib, ora = _codecs(d, bits, m, basis=seeds, vpr=N)
+    K, V, q = synth.esm2(layers=2, heads=3, seq=N)
+    x = K.reshape(-1, d).astype(np.float32)
+    gpu = _gpu_encode(lib, x, pre=False, dtype=torch.float16, tap=True)
+    want = oq.encode(x, ora, idx_stride=lib.idx_stride, sign_stride=lib.sign_stride, keep=True)
+    _explained_mismatches(x, lib, ora, gpu, want)
+
+
+def test_encode_offset_first_selects_rotation_block():
+    d, bits, m, N = 64, 2, 64, 100
+    seeds = [11, 12, 13, 14]
+    lib, ora = _codecs(d, bits, m, basis=seeds, vpr=N)
+    x = synth.pre_rotated(150, d, seed=3)  # rows 250..399 of a cache: blocks 2 and 3
+    gpu = _gpu_encode(lib, x, pre=False, first=250, tap=True)
+    want = oq.encode(x, ora, first=250, idx_stride=lib.idx_stride, sign_stride=lib.sign_stride, keep=True)
+    _explained_mismatches(x, lib, ora, gpu, want, first=250)
+
+
+def test_encode_deterministic_and_pads_zero():
+    lib, ora = _codecs(200, 2, 200)
+    y = synth.pre_rotated(777, 200, seed=9)
+    a = _gpu_encode(lib, y, pre=True)
+    b = _gpu_encode(lib, y, pre=True)
+    for u, v in zip(a[:3], b[:3]):
+        assert np.array_equal(u, v)
+    assert np.all(a[0][:, 50:] == 0)  # 400 index bits -> bytes 50, 51 are padding
+    assert np.all(a[1][:, 25:] == 0)

@@ -1,0 +1,127 @@
+"""GPU score stream against the oracle: same codes in, logits within 1e-3 relative per row
+(max_n |gpu - oracle| / max_n |oracle| for each (sequence, query head)).
+
+Small cases take codes from the oracle's encoder; the full-size cases (the 8B-class decode
+step and the 131k-token decode in the bench's launch configuration) take seeded synthetic
+code planes and compare sampled rows."""
+
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import codec as oc
+from oracle import estimate as oe
+from oracle import quantize as oq
+from tests._util import oracle_codes, rel_err_rows, say, to_device_codes
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+tq = pytest.importorskip("vector_quantization_amd")
+
+TOL = 1e-3
+
+
+def _run(lib, ora, K, q, n_keys, hkv, first_rot_blocks=True):
+    """Oracle-encode K ([S*hkv*N, d] fp32), score on GPU and in the oracle."""
+    codes = oq.encode(K, ora, idx_stride=lib.idx_stride, sign_stride=lib.sign_stride)
+    dc = to_device_codes(tq, codes.idx, codes.sign, codes.norms)
+    qd = torch.from_numpy(np.ascontiguousarray(q, np.float32)).cuda()
+    got = tq.scores(lib, qd, dc, n_keys, hkv).cpu().numpy()
+    want = oe.scores(q.astype(np.float64), codes, ora, n_keys, hkv)
+    return got, want
+
+
+def test_tiny_workload():
+    say("scores tiny")
+    K, V, q = synth.tiny()
+    w = synth.TINY
+    lib = tq.make_codec(w.d, w.k_bits, w.k_m, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
+    ora = oc.make_codec(w.d, w.k_bits, w.k_m, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
+    got, want = _run(lib, ora, K, q.reshape(1, 1, -1), 256, 1)
+    err = rel_err_rows(got, want)
+    say("  rel err", err.max())
+    assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("d,bits,m,hq,hkv,S,N", [
+    (64, 3, 64, 20, 20, 2, 1024),      # ESM-2 shape (per-head rotations below)
+    (128, 2, 128, 32, 8, 1, 40000),    # 8B GQA shape, 3 chunks + ragged tail
+    (128, 2, 128, 16, 8, 2, 777),      # two heads per kv head
+    (128, 3, 0, 8, 8, 2, 513),         # MSE only
+    (200, 2, 200, 1, 1, 3, 3001),      # search shape
+    (64, 4, 64, 8, 2, 1, 300),
+])
+def test_scores_match_oracle(d, bits, m, hq, hkv, S, N):
+    say("scores", d, bits, m, hq, hkv, S, N)
+    lib = tq.make_codec(d, bits, m, 1, 2)
+    ora = oc.make_codec(d, bits, m, 1, 2)
+    g = np.random.default_rng(d + bits + hq)
+    K = (g.standard_normal((S * hkv * N, d)) * np.where(g.random(d) < 0.03, 10.0, 1.0)).astype(np.float32)
+    q = g.standard_normal((S, hq, d)).astype(np.float32)
+    got, want = _run(lib, ora, K, q, N, hkv)
+    err = rel_err_rows(got, want)
+    say("  max rel err", err.max())
+    assert err.max() <= TOL
+
+
+def test_scores_per_head_rotations_esm2_slice():
+    say("scores esm2 slice")
+    d, bits, m, N, layers, heads = 64, 3, 64, 1024, 2, 20
+    seeds = [synth.esm2_basis_seed(l, h) for l in range(layers) for h in range(heads)]
+    lib = tq.make_codec(d, bits, m, 1, 2, basis_seeds=seeds, vecs_per_rot=N)
+    ora = oc.make_codec(d, bits, m, 1, 2, basis_seeds=seeds, vecs_per_rot=N)
+    K, V, q = synth.esm2(layers=layers, heads=heads, seq=N)
+    got, want = _run(lib, ora, K.reshape(-1, d).astype(np.float32), q, N, heads)
+    err = rel_err_rows(got, want)
+    say("  max rel err", err.max())
+    assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("wname", ["gqa", "long"])
+def test_full_size_sampled_rows(wname):
+    """All layers x batch x heads at full context, in the bench's launch configuration."""
+    w = synth.GQA_DECODE if wname == "gqa" else synth.LONG_CTX
+    say("scores full size", w.name)
+    lib = tq.make_codec(w.d, w.k_bits, w.k_m, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
+    ora = oc.make_codec(w.d, w.k_bits, w.k_m, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
+    n_vec = w.n_seq * w.hkv * w.n_ctx
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    codes = tq.alloc_codes(lib, n_vec)
+    codes.idx.copy_(torch.randint(0, 256, codes.idx.shape, generator=gen, device="cuda", dtype=torch.uint8))
+    codes.sign.copy_(torch.randint(0, 256, codes.sign.shape, generator=gen, device="cuda", dtype=torch.uint8))
+    nrm = torch.randn(n_vec, generator=gen, device="cuda").abs() * math.sqrt(w.d)
+    rn = torch.randn(n_vec, generator=gen, device="cuda").abs() * (0.35 * math.sqrt(w.d))
+    lo = nrm.half().view(torch.int16).to(torch.int32) & 0xFFFF
+    hi = rn.half().view(torch.int16).to(torch.int32) & 0xFFFF
+    codes.norms.copy_(lo | (hi << 16))
+    q = torch.randn((w.n_seq, w.hq, w.d), generator=gen, device="cuda")
+    logits = tq.scores(lib, q, codes, w.n_ctx, w.hkv)
+    torch.cuda.synchronize()
+    rows = [(0, 0), (0, 5), (w.n_seq - 1, w.hq - 1), (w.n_seq // 2, 13)]
+    qn = q.cpu().numpy().astype(np.float64)
+    for s, h in rows:
+        blk = s * w.hkv + h // w.group
+        sl = slice(blk * w.n_ctx, (blk + 1) * w.n_ctx)
+        oc_codes = oracle_codes(codes.idx[sl].cpu().numpy(), codes.sign[sl].cpu().numpy(),
+                                codes.norms[sl].cpu().numpy().view(np.uint32))
+        want = oe.scores_one(qn[s, h], oc_codes, ora)
+        got = logits[s, h].cpu().numpy()
+        err = rel_err_rows(got[None], want[None])[0]
+        say("  row", s, h, "rel err", err)
+        assert err <= TOL
+
+
+def test_scores_empty_and_tiny_n():
+    lib = tq.make_codec(64, 2, 64, 1, 2)
+    q = torch.randn((1, 1, 64), device="cuda")
+    codes = tq.alloc_codes(lib, 1)
+    y = torch.randn((1, 64), device="cuda")
+    tq.encode(lib, y, pre_rotated=True, out=codes)
+    out = tq.scores(lib, q, codes, 1, 1)
+    torch.cuda.synchronize()
+    assert out.shape == (1, 1, 1) and torch.isfinite(out).all()
+    e = tq.scores(lib, torch.empty((0, 1, 64), device="cuda"), codes, 1, 1)
+    assert e.shape == (0, 1, 1)

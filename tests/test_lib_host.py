@@ -1,0 +1,124 @@
+"""libtq on the CPU: exported symbols, host codec construction against the oracle, and the
+argument checks that return before any launch.  No kernel runs here."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import vector_quantization_amd as tq
+from oracle import codec as oc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "tq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(tq_\w+)\s*\(", txt, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 11
+    out = subprocess.run(["nm", "-D", "--defined-only", tq.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (tq_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(tq.lib, n)
+    assert set(tq.EXPORTED) == set(names)
+
+
+@pytest.mark.parametrize("d", [64, 128, 200])
+def test_rotation_and_sketch_match_oracle(d):
+    a = tq.make_rotation(1, d)
+    assert np.array_equal(a, oc.haar_rotation(1, d))
+    p = a.astype(np.float64)
+    assert np.max(np.abs(p.T @ p - np.eye(d))) < 2e-6
+    assert np.array_equal(tq.make_sketch(2, d, d), oc.gaussian_sketch(2, d, d))
+    assert np.array_equal(tq.make_sketch(9, 24, d), oc.gaussian_sketch(9, 24, d))
+
+
+@pytest.mark.parametrize("d", [64, 128, 200])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_codebook_matches_oracle_bit_exact(d, bits):
+    c, t = tq.make_codebook(d, bits)
+    cb = oc.lloyd_max_beta(d, bits)
+    assert np.array_equal(c, cb.centroids)
+    assert np.array_equal(t, cb.thresholds)
+
+
+def test_codebook_small_d_and_one_bit():
+    for d, bits in [(3, 2), (3, 3), (16, 1), (32, 2)]:
+        c, t = tq.make_codebook(d, bits)
+        cb = oc.lloyd_max_beta(d, bits)
+        assert np.max(np.abs(c - cb.centroids)) <= 2 * np.spacing(np.abs(cb.centroids)).max()
+
+
+def test_head_rotations_match_oracle():
+    seeds = [(2 << 32) | (l << 16) | h for l in range(2) for h in range(3)]
+    a = tq.make_head_rotations(1, seeds, 64)
+    b = oc.head_rotations(1, seeds, 64)
+    assert np.max(np.abs(a - b)) <= 2 * np.spacing(np.float32(1.0))
+
+
+def test_host_argument_errors():
+    out = np.empty((4, 4), np.float32)
+    assert tq.lib.tq_make_rotation(1, 2, out.ctypes.data) == -2
+    assert tq.lib.tq_make_rotation(1, 64, None) == -1
+    assert tq.lib.tq_make_sketch(1, 0, 4, out.ctypes.data) == -1
+    c = np.empty(4, np.float32)
+    assert tq.lib.tq_make_codebook(64, 9, c.ctypes.data, c.ctypes.data) == -2
+    assert tq.lib.tq_status_str(-4).decode() == "workspace missing or too small"
+
+
+def _fake_codec(d=128, bits=2, m=128):
+    fake = 0x10000  # never dereferenced: checks return before any launch
+    return tq._Codec(d, bits, m, 1, 0, fake, fake if m else 0, fake, fake)
+
+
+def _fake_codes(idx_stride=32, sign_stride=16, idx=0x20000, sign=0x30000):
+    return tq._Codes(idx, idx_stride, sign, sign_stride, 0x40000)
+
+
+def test_device_call_argument_errors():
+    L = tq.lib
+    S = ctypes.c_void_p(0)
+    x = ctypes.c_void_p(0x50000)
+    cc = _fake_codec()
+    # NULL codec, unsupported d, bad m, bad flags
+    assert L.tq_encode(None, x, 0, 4, 128, 0, 0, _fake_codes(), None, S) == -1
+    assert L.tq_encode(ctypes.byref(_fake_codec(d=96)), x, 0, 4, 96, 0, 0, _fake_codes(), None, S) == -2
+    assert L.tq_encode(ctypes.byref(_fake_codec(m=64)), x, 0, 4, 128, 0, 0, _fake_codes(), None, S) == -2
+    assert L.tq_encode(ctypes.byref(cc), x, 0, 4, 128, 7, 0, _fake_codes(), None, S) == -1
+    assert L.tq_encode(ctypes.byref(cc), x, 1, 4, 128, 1, 0, _fake_codes(), None, S) == -1  # pre-rotated needs fp32
+    # strides: too small, not a multiple of the vector width, misaligned plane
+    assert L.tq_encode(ctypes.byref(cc), x, 0, 4, 128, 0, 0, _fake_codes(idx_stride=28), None, S) == -1
+    assert L.tq_encode(ctypes.byref(cc), x, 0, 4, 128, 0, 0, _fake_codes(idx_stride=36), None, S) == -3
+    assert L.tq_encode(ctypes.byref(cc), x, 0, 4, 128, 0, 0, _fake_codes(idx=0x20004), None, S) == -3
+    assert L.tq_encode(ctypes.byref(cc), x, 0, 4, 100, 0, 0, _fake_codes(), None, S) == -1  # ld_x < d
+    # n == 0 is a no-op
+    assert L.tq_encode(ctypes.byref(cc), x, 0, 0, 128, 0, 0, _fake_codes(), None, S) == 0
+    # scores: GQA shape, workspace
+    q = ctypes.c_void_p(0x60000)
+    lg = ctypes.c_void_p(0x70000)
+    assert L.tq_scores(ctypes.byref(cc), q, 2, 6, 4, 16, _fake_codes(), lg, None, 0, S) == -1
+    need = L.tq_workspace_bytes(0, ctypes.byref(cc), None, 2, 8, 2, 16)
+    assert need == 2 * 8 * (128 + 128) * 4
+    assert L.tq_scores(ctypes.byref(cc), q, 2, 8, 2, 16, _fake_codes(), lg, None, 0, S) == -4
+    assert L.tq_scores(ctypes.byref(cc), q, 2, 8, 2, 16, _fake_codes(), lg, ctypes.c_void_p(0x80000), need - 1, S) == -4
+    assert L.tq_scores(ctypes.byref(cc), q, 2, 8, 2, 16, _fake_codes(), lg, ctypes.c_void_p(0x80010), need, S) == -3
+    # search: k range
+    assert L.tq_search_topk(ctypes.byref(cc), q, 3, _fake_codes(), 100, 33, lg, lg, None, 0, S) == -1
+    assert L.tq_search_topk(ctypes.byref(cc), q, 3, _fake_codes(), 5, 10, lg, lg, None, 0, S) == -1
+
+
+def test_min_strides():
+    assert tq.min_stride(128 * 2) == 32
+    assert tq.min_stride(64 * 3) == 24
+    assert tq.min_stride(200 * 2) == 52
+    assert tq.min_stride(200) == 28
+    assert tq.min_stride(0) == 0

@@ -1,0 +1,127 @@
+// C ABI entry points of libtq: argument validation, then the launchers of the .hip units.
+// Every check runs on the host before any launch; see include/tq.h for the contract.
+
+#include <cstdint>
+
+#include "tq_internal.h"
+
+namespace {
+
+using tq::CodecView;
+using tq::CodesView;
+
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// vector width (bytes) the kernels use for a record of `words` 32-bit words
+inline int64_t vec_bytes(int64_t words) { return words % 4 == 0 ? 16 : (words % 2 == 0 ? 8 : 4); }
+
+int check_codec(const tq_codec *c) {
+  if (!c) return TQ_EINVAL;
+  if (!tq::supported_d(c->d) || !tq::supported_bits(c->bits) || !tq::supported_m(c->d, c->m))
+    return TQ_EUNSUPPORTED;
+  if (!c->rot || !c->centroids || !c->thresholds || c->n_rot < 1 || c->vecs_per_rot < 0) return TQ_EINVAL;
+  if (c->m > 0 && !c->sketch) return TQ_EINVAL;
+  if (!aligned(c->rot, 16) || (c->sketch && !aligned(c->sketch, 16))) return TQ_EALIGN;
+  return TQ_OK;
+}
+
+int check_codes(const tq_codec *c, const tq_codes &k) {
+  if (!k.idx || !k.norms) return TQ_EINVAL;
+  const int64_t iw = ((int64_t)c->d * c->bits + 31) / 32;
+  if (k.idx_stride < 4 * iw) return TQ_EINVAL;
+  if (k.idx_stride % vec_bytes(iw) != 0 || !aligned(k.idx, 16) || !aligned(k.norms, 4)) return TQ_EALIGN;
+  if (c->m > 0) {
+    const int64_t sw = ((int64_t)c->m + 31) / 32;
+    if (!k.sign) return TQ_EINVAL;
+    if (k.sign_stride < 4 * sw) return TQ_EINVAL;
+    if (k.sign_stride % vec_bytes(sw) != 0 || !aligned(k.sign, 16)) return TQ_EALIGN;
+  }
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" int tq_encode(const tq_codec *codec, const void *x, tq_dtype dt, int64_t n, int64_t ld_x,
+                         uint32_t flags, int64_t first, tq_codes out, float *y_tap, void *stream) {
+  int rc = check_codec(codec);
+  if (rc != TQ_OK) return rc;
+  if (n < 0 || first < 0) return TQ_EINVAL;
+  if (n == 0) return TQ_OK;
+  if (!x || ld_x < codec->d) return TQ_EINVAL;
+  if (dt != TQ_F32 && dt != TQ_F16 && dt != TQ_BF16) return TQ_EINVAL;
+  const bool pre = (flags & TQ_ENC_PRE_ROTATED) != 0;
+  if ((flags & ~TQ_ENC_PRE_ROTATED) != 0) return TQ_EINVAL;
+  if (pre && dt != TQ_F32) return TQ_EINVAL;
+  rc = check_codes(codec, out);
+  if (rc != TQ_OK) return rc;
+  return tq::launch_encode(tq::view(*codec), x, (int)dt, n, ld_x, pre, first, tq::view(out), y_tap, stream);
+}
+
+extern "C" size_t tq_workspace_bytes(int op, const tq_codec *kc, const tq_codec *vc, int64_t n_seq, int32_t hq,
+                                     int32_t hkv, int64_t n) {
+  if (!kc || n_seq < 0 || n < 0) return 0;
+  const tq::ScoreShape s{n_seq, hq, hkv, n};
+  switch (op) {
+    case TQ_OP_SCORES: return tq::scores_workspace(tq::view(*kc), s);
+    case TQ_OP_ATTEND: return vc ? tq::attend_workspace(tq::view(*kc), tq::view(*vc), s) : 0;
+    case TQ_OP_SEARCH: return tq::search_workspace(tq::view(*kc), n_seq, hq, n);
+    default: return 0;
+  }
+}
+
+extern "C" int tq_scores(const tq_codec *kc, const float *q, int64_t n_seq, int32_t hq, int32_t hkv,
+                         int64_t n_keys, tq_codes k, float *logits, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_codec(kc);
+  if (rc != TQ_OK) return rc;
+  if (n_seq < 0 || n_keys < 0 || hq < 1 || hkv < 1 || hq % hkv != 0) return TQ_EINVAL;
+  if (n_seq == 0 || n_keys == 0) return TQ_OK;
+  if (!q || !logits) return TQ_EINVAL;
+  rc = check_codes(kc, k);
+  if (rc != TQ_OK) return rc;
+  const tq::ScoreShape s{n_seq, hq, hkv, n_keys};
+  const size_t need = tq::scores_workspace(tq::view(*kc), s);
+  if (!ws || ws_bytes < need) return TQ_EWORKSPACE;
+  if (!aligned(ws, 256)) return TQ_EALIGN;
+  return tq::launch_scores(tq::view(*kc), q, s, tq::view(k), logits, ws, ws_bytes, stream);
+}
+
+extern "C" int tq_attend_decode(const tq_codec *kc, const tq_codec *vc, const float *q, int64_t n_seq, int32_t hq,
+                                int32_t hkv, int64_t n_ctx, tq_codes k, tq_codes v, float scale, float *out,
+                                void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_codec(kc);
+  if (rc != TQ_OK) return rc;
+  rc = check_codec(vc);
+  if (rc != TQ_OK) return rc;
+  if (kc->d != vc->d) return TQ_EINVAL;
+  if (n_seq < 0 || n_ctx < 1 || hq < 1 || hkv < 1 || hq % hkv != 0) return TQ_EINVAL;
+  if (n_seq == 0) return TQ_OK;
+  if (!q || !out) return TQ_EINVAL;
+  rc = check_codes(kc, k);
+  if (rc != TQ_OK) return rc;
+  rc = check_codes(vc, v);
+  if (rc != TQ_OK) return rc;
+  const tq::ScoreShape s{n_seq, hq, hkv, n_ctx};
+  const size_t need = tq::attend_workspace(tq::view(*kc), tq::view(*vc), s);
+  if (!ws || ws_bytes < need) return TQ_EWORKSPACE;
+  if (!aligned(ws, 256)) return TQ_EALIGN;
+  return tq::launch_attend(tq::view(*kc), tq::view(*vc), q, s, tq::view(k), tq::view(v), scale, out, ws,
+                           ws_bytes, stream);
+}
+
+extern "C" int tq_search_topk(const tq_codec *c, const float *queries, int64_t n_q, tq_codes db, int64_t n_db,
+                              int32_t k, int64_t *out_idx, float *out_score, void *ws, size_t ws_bytes,
+                              void *stream) {
+  int rc = check_codec(c);
+  if (rc != TQ_OK) return rc;
+  if (c->n_rot != 1) return TQ_EINVAL;
+  if (n_q < 0 || n_db < 1 || k < 1 || k > 32 || k > n_db) return TQ_EINVAL;
+  if (n_q == 0) return TQ_OK;
+  if (!queries || !out_idx || !out_score) return TQ_EINVAL;
+  rc = check_codes(c, db);
+  if (rc != TQ_OK) return rc;
+  const size_t need = tq::search_workspace(tq::view(*c), n_q, k, n_db);
+  if (need > 0 && (!ws || ws_bytes < need)) return TQ_EWORKSPACE;
+  if (ws && !aligned(ws, 256)) return TQ_EALIGN;
+  return tq::launch_search(tq::view(*c), queries, n_q, tq::view(db), n_db, k, out_idx, out_score, ws, ws_bytes,
+                           stream);
+}

@@ -1,0 +1,101 @@
+// Device helpers for libtq kernels on gfx950 (wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <cstdint>
+
+namespace tq {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_float(uint32_t b) {
+  return __half2float(__ushort_as_half((unsigned short)(b & 0xFFFFu)));
+}
+
+__host__ __device__ __forceinline__ double f16_bits_to_double_ext(uint32_t bits) {
+  // value of a non-negative fp16 pattern; 0x7C00 stands for 65536 (the overflow step)
+  if (bits >= 0x7C00u) return 65536.0;
+  const uint32_t e = bits >> 10, f = bits & 0x3FFu;
+  if (e == 0) return (double)f * 0x1p-24;
+  return ((double)(1024u + f)) * ldexp(1.0, (int)e - 25);
+}
+
+// Round a non-negative double to the nearest fp16 (ties to even); >= 65520 gives +inf.
+__device__ __forceinline__ uint32_t f64_to_f16_rne(double v) {
+  if (!(v < 65520.0)) return 0x7C00u;
+  if (v < 0x1p-14) return (uint32_t)rint(v * 0x1p24);  // subnormal grid 2^-24 (may reach 0x400)
+  int e2;
+  (void)frexp(v, &e2);          // v = f 2^e2, f in [0.5, 1)
+  const int E = e2 - 1;         // v in [2^E, 2^(E+1)), -14 <= E <= 15
+  const double q = ldexp(v, 10 - E);  // [1024, 2048)
+  const uint32_t r = (uint32_t)rint(q);
+  return (uint32_t)((E + 15) << 10) + (r - 1024u);
+}
+
+// ---------------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sumf(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// ---------------------------------------------------------------- exact sums
+
+// Knuth's TwoSum: s + e == a + b exactly.
+__device__ __forceinline__ void two_sum(double a, double b, double &s, double &e) {
+  s = a + b;
+  const double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+
+// Exact sign (-1, 0, +1) of the sum of n doubles, each exact, by Shewchuk's Grow-Expansion
+// with zero elimination ("Adaptive Precision Floating-Point Arithmetic and Fast Robust
+// Geometric Predicates", 1997): the running sum is kept as a non-overlapping expansion in
+// increasing magnitude, whose last component carries the sign.  buf holds n doubles.
+// Run by one lane.
+__device__ inline int expansion_sign(const double *terms, int n, double *buf) {
+  int len = 0;
+  for (int k = 0; k < n; ++k) {
+    double q = terms[k];
+    int out = 0;
+    for (int i = 0; i < len; ++i) {
+      double s, h;
+      two_sum(q, buf[i], s, h);
+      q = s;
+      if (h != 0.0) buf[out++] = h;
+    }
+    if (q != 0.0) buf[out++] = q;
+    len = out;
+  }
+  if (len == 0) return 0;
+  return buf[len - 1] > 0.0 ? 1 : -1;
+}
+
+}  // namespace tq

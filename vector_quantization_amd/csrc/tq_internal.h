@@ -1,0 +1,67 @@
+// Internal declarations shared by libtq's translation units (not part of the C ABI).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+// host codec construction (tq_host.cpp)
+void gaussian_fill(uint64_t seed, int64_t count, double *out);
+void haar_rotation64(uint64_t seed, int d, std::vector<double> &q);
+int lloyd_max_codebook(int d, int bits, std::vector<double> &c, std::vector<double> &t);
+
+// Everything a kernel needs about one codec, by value.
+struct CodecView {
+  int d, bits, m, n_rot;
+  int64_t vecs_per_rot;
+  const float *rot, *sketch, *centroids, *thresholds;
+};
+
+struct CodesView {
+  uint8_t *idx;
+  int64_t idx_stride;
+  uint8_t *sign;
+  int64_t sign_stride;
+  uint32_t *norms;
+};
+
+inline CodecView view(const tq_codec &c) {
+  return CodecView{c.d, c.bits, c.m, c.n_rot, c.vecs_per_rot, c.rot, c.sketch, c.centroids, c.thresholds};
+}
+inline CodesView view(const tq_codes &c) {
+  return CodesView{c.idx, c.idx_stride, c.sign, c.sign_stride, c.norms};
+}
+
+// launchers (one per .hip translation unit); return a tq_status
+int launch_encode(const CodecView &c, const void *x, int dt, int64_t n, int64_t ld_x, bool pre_rotated,
+                  int64_t first, const CodesView &out, float *y_tap, void *stream);
+
+struct ScoreShape {
+  int64_t n_seq;
+  int hq, hkv;
+  int64_t n;
+};
+size_t scores_workspace(const CodecView &kc, const ScoreShape &s);
+int launch_scores(const CodecView &kc, const float *q, const ScoreShape &s, const CodesView &k,
+                  float *logits, void *ws, size_t ws_bytes, void *stream);
+
+size_t attend_workspace(const CodecView &kc, const CodecView &vc, const ScoreShape &s);
+int launch_attend(const CodecView &kc, const CodecView &vc, const float *q, const ScoreShape &s,
+                  const CodesView &k, const CodesView &v, float scale, float *out, void *ws,
+                  size_t ws_bytes, void *stream);
+
+size_t search_workspace(const CodecView &c, int64_t n_q, int k, int64_t n_db);
+int launch_search(const CodecView &c, const float *queries, int64_t n_q, const CodesView &db,
+                  int64_t n_db, int k, int64_t *out_idx, float *out_score, void *ws, size_t ws_bytes,
+                  void *stream);
+
+// supported device configurations
+inline bool supported_d(int d) { return d == 64 || d == 128 || d == 200; }
+inline bool supported_bits(int b) { return b >= 2 && b <= 4; }
+inline bool supported_m(int d, int m) { return m == 0 || m == d; }
+
+}  // namespace tq

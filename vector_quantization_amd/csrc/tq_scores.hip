@@ -1,0 +1,254 @@
+// Query preparation and the score stream over a compressed key cache.
+//
+// Sources: 7minutos.es TurboQuant walkthrough, "Etapa 2 (Corrección Residual)" (the QJL term
+// sqrt(pi/2)/m ||r|| S^T sign(S r) and K~ = K^ + K~_QJL); hada.io TurboQuant page, "QJL:
+// técnica de 1 bit com overhead zero" (high-precision query against 1-bit data); sudonull.com
+// "Cómo funciona PolarQuant" (norm times quantised direction).  The estimate is evaluated in
+// the rotated space: <q, k~> = nbar <Pi q, c[idx]> + rnbar sqrt(pi/2)/m <S Pi q, 2 bits - 1>.
+//
+// qprep: one wavefront per query head computes q~ = Pi_r q and q^ = S q~ in fp32.
+// score: one workgroup per (sequence, kv head, head subgroup, key chunk) builds the lookup
+// tables of its G query heads in LDS (tq_lut.h), then streams the chunk's code planes from
+// HBM, one key per thread per step, and writes fp32 logits for the G heads.
+
+#include "tq_device.h"
+#include "tq_internal.h"
+#include "tq_lut.h"
+
+namespace tq {
+
+struct QprepArgs {
+  const float *q;
+  int64_t n_heads;  // n_seq * hq
+  int hq, hkv;
+  int64_t n_keys;   // vectors per kv block (selects the block's rotation)
+  const float *rot;
+  int n_rot;
+  int64_t vecs_per_rot;
+  const float *sketch;
+  float *qt, *qh;
+};
+
+template <int D, int M>
+__global__ __launch_bounds__(256) void qprep_kernel(QprepArgs a) {
+  constexpr int C = (D + kWave - 1) / kWave;
+  constexpr int CM = (M + kWave - 1) / kWave;
+  __shared__ float qs[4][D];
+  __shared__ float ts[4][D];
+  const int lane = lane_id(), wid = threadIdx.x / kWave;
+  const int64_t hidx = (int64_t)blockIdx.x * 4 + wid;
+  if (hidx >= a.n_heads) return;
+  const int64_t s = hidx / a.hq;
+  const int h = (int)(hidx % a.hq);
+  const int64_t blk = s * a.hkv + h / (a.hq / a.hkv);
+  int64_t rid = 0;
+  if (a.n_rot > 1 && a.vecs_per_rot > 0) {
+    rid = (blk * a.n_keys) / a.vecs_per_rot;
+    if (rid > a.n_rot - 1) rid = a.n_rot - 1;
+  }
+  const float *R = a.rot + rid * (int64_t)D * D;
+  for (int i = lane; i < D; i += kWave) qs[wid][i] = a.q[hidx * D + i];
+  wave_lds_fence();
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int i = lane + kWave * c;
+    if (i < D) {
+      float acc = 0.0f;
+      for (int k = 0; k < D; ++k) acc = fmaf(R[(int64_t)i * D + k], qs[wid][k], acc);
+      ts[wid][i] = acc;
+      a.qt[hidx * D + i] = acc;
+    }
+  }
+  if constexpr (M > 0) {
+    wave_lds_fence();
+#pragma unroll
+    for (int c = 0; c < CM; ++c) {
+      const int j = lane + kWave * c;
+      if (j < M) {
+        float acc = 0.0f;
+        for (int k = 0; k < D; ++k) acc = fmaf(a.sketch[(int64_t)j * D + k], ts[wid][k], acc);
+        a.qh[hidx * M + j] = acc;
+      }
+    }
+  }
+}
+
+struct ScoreArgs {
+  const float *qt, *qh, *centroids;
+  int64_t n_seq, n_keys;
+  int hq, hkv, nsub, n_chunks, chunk;
+  const uint8_t *idx;
+  int64_t idx_stride;
+  const uint8_t *sign;
+  int64_t sign_stride;
+  const uint32_t *norms;
+  float *logits;
+};
+
+template <int W>
+__device__ __forceinline__ void load_words(const uint8_t *p, uint32_t (&w)[W]) {
+  if constexpr (W % 4 == 0) {
+    const uint4 *p4 = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const uint4 v = p4[i];
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (W % 2 == 0) {
+    const uint2 *p2 = reinterpret_cast<const uint2 *>(p);
+#pragma unroll
+    for (int i = 0; i < W / 2; ++i) {
+      const uint2 v = p2[i];
+      w[2 * i] = v.x; w[2 * i + 1] = v.y;
+    }
+  } else {
+    const uint32_t *p1 = reinterpret_cast<const uint32_t *>(p);
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = p1[i];
+  }
+}
+
+template <int D, int BITS, int M, int G, int NT>
+__global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
+  using C = Lut<D, BITS, M, G>;
+  constexpr int SWN = C::SW > 0 ? C::SW : 1;
+  __shared__ __align__(16) uint8_t tabs[C::BYTES];
+  __shared__ float qt[G * D];
+  __shared__ float qh[G * (M > 0 ? M : 1)];
+  __shared__ float cb[C::L];
+  __shared__ float scm[G], scq[G];
+
+  const int64_t b = blockIdx.x;
+  const int chunk = (int)(b % a.n_chunks);
+  const int64_t rest = b / a.n_chunks;
+  const int sub = (int)(rest % a.nsub);
+  const int64_t blk = rest / a.nsub;  // s * hkv + kvh
+  const int64_t s = blk / a.hkv;
+  const int kvh = (int)(blk % a.hkv);
+  const int g = a.hq / a.hkv;
+  const int h0 = kvh * g + sub * G;  // first query head of this group
+  const int64_t qrow = s * a.hq + h0;
+
+  for (int i = threadIdx.x; i < G * D; i += NT) qt[i] = a.qt[qrow * D + i];
+  if constexpr (M > 0)
+    for (int i = threadIdx.x; i < G * M; i += NT) qh[i] = a.qh[qrow * M + i];
+  if (threadIdx.x < C::L) cb[threadIdx.x] = a.centroids[threadIdx.x];
+  __syncthreads();
+  HeadScales<G> hs;
+  {
+    const float cmax = fmaxf(fabsf(cb[0]), fabsf(cb[C::L - 1]));
+    float sm[G], sq[G];
+    table_scales<D, BITS, M, G>(qt, qh, cmax, sm, sq, hs);
+    if (threadIdx.x < G) {
+      scm[threadIdx.x] = sm[threadIdx.x];
+      scq[threadIdx.x] = sq[threadIdx.x];
+    }
+  }
+  __syncthreads();
+  build_luts<D, BITS, M, G, NT>(tabs, tabs + C::MSE_BYTES, qt, qh, cb, scm, scq);
+  __syncthreads();
+
+  const float kappa = M > 0 ? 1.2533141373155003f / (float)(M > 0 ? M : 1) : 0.0f;  // sqrt(pi/2)/m
+  const int64_t t0 = (int64_t)chunk * a.chunk;
+  int64_t t1 = t0 + a.chunk;
+  if (t1 > a.n_keys) t1 = a.n_keys;
+  const int64_t vbase = blk * a.n_keys;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += NT) {
+    const int64_t v = vbase + t;
+    uint32_t iw[C::IW];
+    uint32_t sw[SWN];
+    load_words<C::IW>(a.idx + v * a.idx_stride, iw);
+    if constexpr (M > 0) load_words<C::SW>(a.sign + v * a.sign_stride, sw);
+    const uint32_t nw = a.norms[v];
+    float am[G], aq[G];
+    lut_score<D, BITS, M, G>(iw, sw, tabs, tabs + C::MSE_BYTES, hs, am, aq);
+    const float nbar = f16_bits_to_float(nw & 0xFFFFu);
+    const float rq = f16_bits_to_float(nw >> 16) * kappa;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float sc = nbar * am[h];
+      if constexpr (M > 0) sc = fmaf(rq, aq[h], sc);
+      a.logits[(qrow + h) * a.n_keys + t] = sc;
+    }
+  }
+}
+
+size_t scores_workspace(const CodecView &kc, const ScoreShape &s) {
+  return (size_t)s.n_seq * s.hq * (size_t)(kc.d + kc.m) * sizeof(float);
+}
+
+template <int D, int M>
+static int launch_qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh,
+                        hipStream_t st) {
+  QprepArgs a{q, s.n_seq * s.hq, s.hq, s.hkv, s.n, kc.rot, kc.n_rot, kc.vecs_per_rot, kc.sketch, qt, qh};
+  const int64_t blocks = (a.n_heads + 3) / 4;
+  hipLaunchKernelGGL((qprep_kernel<D, M>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+int qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh, hipStream_t st) {
+  const int D = kc.d, M = kc.m;
+#define TQ_QP(DD, MM) if (D == DD && M == MM) return launch_qprep<DD, MM>(kc, q, s, qt, qh, st);
+  TQ_QP(64, 0) TQ_QP(64, 64) TQ_QP(128, 0) TQ_QP(128, 128) TQ_QP(200, 0) TQ_QP(200, 200)
+#undef TQ_QP
+  return TQ_EUNSUPPORTED;
+}
+
+// heads per lookup entry for a GQA group of g heads
+static int pick_g(int g) {
+  if (g % 4 == 0) return 4;
+  if (g % 2 == 0) return 2;
+  return 1;
+}
+
+template <int D, int BITS, int M, int G>
+static int launch_score_g(const ScoreArgs &a0, const ScoreShape &s, hipStream_t st) {
+  constexpr int NT = (Lut<D, BITS, M, G>::BYTES > 48 * 1024) ? 1024 : 256;
+  ScoreArgs a = a0;
+  a.nsub = (s.hq / s.hkv) / G;
+  a.chunk = 16384;
+  if (s.n < a.chunk) a.chunk = (int)((s.n + NT - 1) / NT * NT);
+  if (a.chunk < NT) a.chunk = NT;
+  a.n_chunks = (int)((s.n + a.chunk - 1) / a.chunk);
+  const int64_t blocks = s.n_seq * s.hkv * a.nsub * a.n_chunks;
+  hipLaunchKernelGGL((score_kernel<D, BITS, M, G, NT>), dim3((unsigned)blocks), dim3(NT), 0, st, a);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+template <int D, int BITS, int M, int G>
+constexpr bool lut_fits() {
+  return Lut<D, BITS, M, G>::BYTES + G * (D + M) * 4 + 512 <= 160 * 1024;
+}
+
+template <int D, int BITS, int M>
+static int launch_score_dbm(const ScoreArgs &a, const ScoreShape &s, hipStream_t st) {
+  const int want = pick_g(s.hq / s.hkv);
+  if (want >= 4) {
+    if constexpr (lut_fits<D, BITS, M, 4>()) return launch_score_g<D, BITS, M, 4>(a, s, st);
+  }
+  if (want >= 2) {
+    if constexpr (lut_fits<D, BITS, M, 2>()) return launch_score_g<D, BITS, M, 2>(a, s, st);
+  }
+  return launch_score_g<D, BITS, M, 1>(a, s, st);
+}
+
+int launch_scores(const CodecView &kc, const float *q, const ScoreShape &s, const CodesView &k, float *logits,
+                  void *ws, size_t ws_bytes, void *stream) {
+  if (s.n == 0 || s.n_seq == 0) return TQ_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float *qt = reinterpret_cast<float *>(ws);
+  float *qh = qt + (size_t)s.n_seq * s.hq * kc.d;
+  int rc = qprep(kc, q, s, qt, qh, st);
+  if (rc != TQ_OK) return rc;
+  ScoreArgs a{qt, qh, kc.centroids, s.n_seq, s.n, s.hq, s.hkv, 1, 1, 1,
+              k.idx, k.idx_stride, k.sign, k.sign_stride, k.norms, logits};
+  const int D = kc.d, B = kc.bits, M = kc.m;
+#define TQ_SC(DD, BB, MM) if (D == DD && B == BB && M == MM) return launch_score_dbm<DD, BB, MM>(a, s, st);
+  TQ_SC(64, 2, 64) TQ_SC(64, 3, 64) TQ_SC(64, 4, 64) TQ_SC(64, 2, 0) TQ_SC(64, 3, 0) TQ_SC(64, 4, 0)
+  TQ_SC(128, 2, 128) TQ_SC(128, 3, 128) TQ_SC(128, 4, 128) TQ_SC(128, 2, 0) TQ_SC(128, 3, 0) TQ_SC(128, 4, 0)
+  TQ_SC(200, 2, 200) TQ_SC(200, 3, 200) TQ_SC(200, 2, 0) TQ_SC(200, 3, 0)
+#undef TQ_SC
+  return TQ_EUNSUPPORTED;
+}
+
+}  // namespace tq
