@@ -1,0 +1,210 @@
+"""Benchmark of the compressed-KV decode path on one MI355X.
+
+Workload (default): 8B-class GQA decode step -- 32 layers, 32 query / 8 KV heads, d = 128,
+batch 8, 32768 cached tokens; keys 2-bit index + 1-bit QJL (m = 128), values 3-bit index.
+The cache is encoded once from seeded bf16 K/V (bulk encode, timed on its own); a timed step
+is one decode step over the resident compressed cache for all layers: the score stream
+(tq_scores, the headline) followed by attention (tq_attend_decode).
+
+Prints one JSON line.  value = decode-scoring GB/s: algorithmic bytes of one tq_scores call
+(the key code planes, unpadded, + the fp32 logits written + the queries read) divided by the
+call's average duration measured with HIP events on the launch stream.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "compressed-KV decode scoring GB/s (% HBM peak) + keys/s; encode vectors/s"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["gqa", "long"], default="gqa")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attend", action="store_true")
+    ap.add_argument("--encode-reps", type=int, default=3)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, K, q, seed_rot, seed_sk):
+    """Time the oracle's scoring of one (layer, batch) slice: all kv heads, full context."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import codec as oc
+    from oracle import estimate as oe
+    from oracle import quantize as oq
+
+    ora = oc.make_codec(w.d, w.k_bits, w.k_m, seed_rot, seed_sk)
+    kx = K[0, 0].float().cpu().numpy().reshape(-1, w.d)  # [hkv * n_ctx, d]
+    qx = q[0, 0].cpu().numpy().astype(np.float64)  # [hq, d]
+    t0 = time.perf_counter()
+    codes = oq.encode(kx, ora)
+    t_enc = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for h in range(w.hq):
+        kvh = h // w.group
+        sl = slice(kvh * w.n_ctx, (kvh + 1) * w.n_ctx)
+        oe.scores_one(qx[h], oq.Codes(codes.idx[sl], codes.sign[sl], codes.norms[sl]), ora)
+    t_sc = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    keys = w.hkv * w.n_ctx
+    return {
+        "value": keys / t_sc, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"layer 0, batch 0: {w.hkv} kv heads x {w.n_ctx} keys scored for {w.hq} query heads "
+                   f"({t_sc:.1f} s); oracle encode of the same {keys} keys took {t_enc:.1f} s "
+                   f"({keys / t_enc:.3g} vectors/s)"),
+        "encode_vectors_per_s": keys / t_enc,
+        "affinity_cores": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {a.gpus}); the multi-GPU split of this "
+              "path is a design note, not a measured configuration.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    import vector_quantization_amd as tq
+
+    w = synth.GQA_DECODE if a.workload == "gqa" else synth.LONG_CTX
+    dev = "cuda"
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    log("workload", w)
+    K, V, q = synth.gqa_decode(w, seed=2 if a.workload == "gqa" else 3, device=dev)
+    kc = tq.make_codec(w.d, w.k_bits, w.k_m, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
+    vc = tq.make_codec(w.d, w.v_bits, w.v_m, synth.SEED_ROT_V, synth.SEED_SKETCH_V)
+    n_vec = w.n_seq * w.hkv * w.n_ctx
+    kcodes = tq.alloc_codes(kc, n_vec)
+    vcodes = tq.alloc_codes(vc, n_vec)
+
+    # ---- bulk encode of the whole prefix (K and V), timed on its own
+    Kf, Vf = K.reshape(-1, w.d), V.reshape(-1, w.d)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    tq.encode(kc, Kf, out=kcodes)
+    tq.encode(vc, Vf, out=vcodes)
+    torch.cuda.synchronize()
+    enc_k, enc_v = [], []
+    for _ in range(a.encode_reps):
+        ev[0].record(stream)
+        tq.encode(kc, Kf, out=kcodes)
+        ev[1].record(stream)
+        tq.encode(vc, Vf, out=vcodes)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        enc_k.append(ev[0].elapsed_time(ev[1]))
+        enc_v.append(ev[1].elapsed_time(ev[2]))
+    t_enc_k, t_enc_v = float(np.median(enc_k)), float(np.median(enc_v))
+    log(f"encode K {t_enc_k:.2f} ms, V {t_enc_v:.2f} ms")
+    qf = q.reshape(w.n_seq, w.hq, w.d).contiguous()
+    logits = torch.empty((w.n_seq, w.hq, w.n_ctx), dtype=torch.float32, device=dev)
+    out = torch.empty((w.n_seq, w.hq, w.d), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(w.d)
+    do_attend = not a.no_attend
+    if do_attend:
+        try:
+            tq.attend_decode(kc, vc, qf, kcodes, vcodes, w.n_ctx, w.hkv, scale, out=out)
+        except tq.TQError as e:
+            log("attend unavailable:", e)
+            do_attend = False
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        tq.scores(kc, qf, kcodes, w.n_ctx, w.hkv, logits=logits)
+        if evs:
+            evs[1].record(stream)
+        if do_attend:
+            tq.attend_decode(kc, vc, qf, kcodes, vcodes, w.n_ctx, w.hkv, scale, out=out)
+        if evs:
+            evs[2].record(stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sc_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    at_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    t_sc = float(np.mean(sc_ms))
+    t_at = float(np.mean(at_ms)) if do_attend else None
+    ms_step = wall * 1e3 / a.steps
+
+    keys = w.n_seq * w.hkv * w.n_ctx
+    code_b_k = (w.d * w.k_bits + 7) // 8 + (w.k_m + 7) // 8 + 4
+    code_b_v = (w.d * w.v_bits + 7) // 8 + (w.v_m + 7) // 8 + 4
+    q_bytes = w.n_seq * w.hq * w.d * 4
+    score_bytes = keys * code_b_k + w.n_seq * w.hq * w.n_ctx * 4 + q_bytes
+    attend_bytes = keys * (code_b_k + code_b_v) + q_bytes + w.n_seq * w.hq * w.d * 4
+    gbps = score_bytes / (t_sc * 1e-3) / 1e9
+    enc_in = n_vec * w.d * 2
+    enc_out_k = n_vec * code_b_k
+    enc_out_v = n_vec * code_b_v
+    res = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded bf16 K/V, N(0,1) with 2% channels x10; fp32 queries)",
+        "config": {
+            "workload": f"{w.name}: {w.layers} layers x batch {w.batch}, {w.hq} q / {w.hkv} kv heads, d={w.d}, "
+                        f"{w.n_ctx} cached tokens; K {w.k_bits}-bit + QJL m={w.k_m}, V {w.v_bits}-bit",
+            "layers": w.layers, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "head_dim": w.d, "n_ctx": w.n_ctx,
+            "k_bits": w.k_bits, "k_qjl_m": w.k_m, "v_bits": w.v_bits, "v_qjl_m": w.v_m,
+        },
+        "scores_ms": round(t_sc, 4),
+        "scores_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "keys_per_s": keys / (t_sc * 1e-3),
+        "qk_pairs_per_s": keys * w.group / (t_sc * 1e-3),
+        "scores_algorithmic_bytes": score_bytes,
+        "attend_ms": None if t_at is None else round(t_at, 4),
+        "attend_GBps": None if t_at is None else round(attend_bytes / (t_at * 1e-3) / 1e9, 1),
+        "attend_algorithmic_bytes": attend_bytes,
+        "encode_ms": {"K": round(t_enc_k, 3), "V": round(t_enc_v, 3)},
+        "encode_vectors_per_s": round(2 * n_vec / ((t_enc_k + t_enc_v) * 1e-3)),
+        "encode_GBps": round((2 * enc_in + enc_out_k + enc_out_v) / ((t_enc_k + t_enc_v) * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "score_kernel (+ its qprep launch inside the timed call)"},
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(w, K, q, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -137,10 +137,27 @@ def topk_rows(score_rows: np.ndarray, k: int):
     return idx, np.take_along_axis(score_rows, idx, axis=1)
 
 
+def search_scores(queries: np.ndarray, db: Codes, codec: Codec, chunk: int = 65536) -> np.ndarray:
+    """Estimated <q, x_n> for every query and database row ([Q, n_db]; single shared rotation)."""
+    qs = np.asarray(queries, dtype=np.float64)
+    qt = qs @ codec.rot[0].astype(np.float64).T
+    qh = qt @ codec.sketch.astype(np.float64).T if codec.m > 0 else None
+    c = codec.centroids.astype(np.float64)
+    n = db.norms.shape[0]
+    out = np.empty((qs.shape[0], n), dtype=np.float64)
+    for a in range(0, n, chunk):
+        part = _slice(db, a, min(n, a + chunk))
+        index, signs, nbar, rnbar = unpack(part, codec)
+        s = nbar[None, :] * (qt @ c[index].T)
+        if codec.m > 0:
+            s = s + (rnbar * qjl_scale(codec.m))[None, :] * (qh @ signs.T)
+        out[:, a:a + index.shape[0]] = s
+    return out
+
+
 def search_topk(queries: np.ndarray, db: Codes, codec: Codec, k: int):
     """Top-k database vectors per query by estimated inner product (single shared rotation)."""
-    rows = np.stack([scores_one(qv, db, codec, 0) for qv in np.asarray(queries)])
-    return topk_rows(rows, k)
+    return topk_rows(search_scores(queries, db, codec), k)
 
 
 def exact_topk(queries: np.ndarray, db: np.ndarray, k: int):

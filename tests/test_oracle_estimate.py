@@ -178,3 +178,14 @@ def test_search_recall_sane():
     assert estimate.recall_at_k(e, e) == 1.0
     assert estimate.recall_at_k(a, e) > 0.4
     assert estimate.one_at_k(a, e) > 0.6
+
+
+def test_search_scores_equal_per_query_estimates():
+    d = 64
+    c = codec.make_codec(d, 2, 32, 1, 2)
+    g = np.random.default_rng(10)
+    codes = quantize.encode(g.standard_normal((300, d)).astype(np.float32), c)
+    qs = g.standard_normal((4, d))
+    got = estimate.search_scores(qs, codes, c, chunk=77)
+    want = np.stack([estimate.scores_one(q, codes, c) for q in qs])
+    assert np.allclose(got, want, rtol=0, atol=1e-12 * np.abs(want).max())

@@ -1,13 +1,410 @@
-// Decode attention over the compressed cache (placeholder until the split-K kernel lands).
+// One decode step of attention over the compressed K/V cache.
+//
+// Sources: TurboESM summary (gist.science), section 2.E: a single fused decode kernel loads
+// the compressed cache, unpacks the indices, applies the QJL correction and the inverse
+// rotation Pi^T, and runs attention with an online softmax, with no dequantised fp16 copy;
+// 7minutos.es TurboQuant walkthrough, "Etapa 2 (Corrección Residual)": the dequantised value
+// is v~ = Pi^T (nbar c[idx] + sqrt(pi/2)/m rnbar S^T (2 bits - 1)).
+//
+// Split over the context (flash-decoding): attend_partial runs one workgroup per (sequence,
+// kv head, head subgroup, context chunk).  It scores each tile of tokens with the key lookup
+// tables (tq_lut.h), keeps a running max and sum per query head, and accumulates the
+// softmax-weighted values in the rotated space -- nbar_n c_V[idx_n] per coordinate and, when
+// V carries QJL bits, rnbar_n sqrt(pi/2)/m (2 bits - 1) per sketch row -- so no rotation is
+// applied per token.  attend_combine merges the chunks of each query head and applies S_V^T
+// and Pi_V^T once.
+
 #include "tq_device.h"
 #include "tq_internal.h"
+#include "tq_lut.h"
 
 namespace tq {
 
-size_t attend_workspace(const CodecView &, const CodecView &, const ScoreShape &) { return 0; }
+int qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh, hipStream_t st);
 
-int launch_attend(const CodecView &, const CodecView &, const float *, const ScoreShape &, const CodesView &,
-                  const CodesView &, float, float *, void *, size_t, void *) {
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttArgs {
+  const float *qt, *qh, *kcent, *vcent;
+  int64_t n_seq, n_ctx;
+  int hq, hkv, nsub, n_chunks, chunk;
+  float scale_log2;  // softmax scale * log2(e)
+  const uint8_t *kidx;
+  int64_t kidx_stride;
+  const uint8_t *ksign;
+  int64_t ksign_stride;
+  const uint32_t *knorms;
+  const uint8_t *vidx;
+  int64_t vidx_stride;
+  const uint8_t *vsign;
+  int64_t vsign_stride;
+  const uint32_t *vnorms;
+  float *part;  // [n_seq * hq][n_chunks][2 + d + m_V]
+};
+
+template <int W>
+__device__ __forceinline__ void load_words_a(const uint8_t *p, uint32_t (&w)[W]) {
+  if constexpr (W % 4 == 0) {
+    const uint4 *p4 = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const uint4 v = p4[i];
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (W % 2 == 0) {
+    const uint2 *p2 = reinterpret_cast<const uint2 *>(p);
+#pragma unroll
+    for (int i = 0; i < W / 2; ++i) {
+      const uint2 v = p2[i];
+      w[2 * i] = v.x; w[2 * i + 1] = v.y;
+    }
+  } else {
+    const uint32_t *p1 = reinterpret_cast<const uint32_t *>(p);
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = p1[i];
+  }
+}
+
+template <int D, int KB, int KM, int VB, int VM, int G, int NT>
+__global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
+  using CK = Lut<D, KB, KM, G>;
+  constexpr int KSW = CK::SW > 0 ? CK::SW : 1;
+  constexpr int IWV = (D * VB + 31) / 32;
+  constexpr int SWV = (VM + 31) / 32;
+  constexpr int NOUT = D + VM;
+  constexpr int TPO = NT / NOUT;  // threads sharing one output coordinate
+  constexpr int TOK = NT / TPO;   // tokens of a tile handled by one thread in the value phase
+  constexpr int NW = NT / kWave;
+  static_assert(NT % NOUT == 0, "threads must cover the output coordinates evenly");
+  constexpr int LV = 1 << VB;
+
+  __shared__ __align__(16) uint8_t tabs[CK::BYTES];
+  __shared__ float qt[G * D];
+  __shared__ float qh[G * (KM > 0 ? KM : 1)];
+  __shared__ float cbk[1 << KB];
+  __shared__ float cbv[LV];
+  __shared__ float scm[G], scq[G];
+  __shared__ uint32_t vtile[NT * IWV];
+  __shared__ uint32_t vstile[VM > 0 ? NT * SWV : 1];
+  __shared__ __align__(16) float wt[NT * G];
+  __shared__ __align__(16) float wq[VM > 0 ? NT * G : 1];
+  __shared__ float red_max[NW * G], red_sum[NW * G];
+
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  const int64_t b = blockIdx.x;
+  const int chunk = (int)(b % a.n_chunks);
+  const int64_t rest = b / a.n_chunks;
+  const int sub = (int)(rest % a.nsub);
+  const int64_t blk = rest / a.nsub;
+  const int64_t s = blk / a.hkv;
+  const int kvh = (int)(blk % a.hkv);
+  const int h0 = kvh * (a.hq / a.hkv) + sub * G;
+  const int64_t qrow = s * a.hq + h0;
+
+  for (int i = tid; i < G * D; i += NT) qt[i] = a.qt[qrow * D + i];
+  if constexpr (KM > 0)
+    for (int i = tid; i < G * KM; i += NT) qh[i] = a.qh[qrow * KM + i];
+  if (tid < (1 << KB)) cbk[tid] = a.kcent[tid];
+  if (tid < LV) cbv[tid] = a.vcent[tid];
+  __syncthreads();
+  HeadScales<G> hs;
+  {
+    const float cmax = fmaxf(fabsf(cbk[0]), fabsf(cbk[(1 << KB) - 1]));
+    float sm[G], sq[G];
+    table_scales<D, KB, KM, G>(qt, qh, cmax, sm, sq, hs);
+    if (tid < G) {
+      scm[tid] = sm[tid];
+      scq[tid] = sq[tid];
+    }
+  }
+  __syncthreads();
+  build_luts<D, KB, KM, G, NT>(tabs, tabs + CK::MSE_BYTES, qt, qh, cbk, scm, scq);
+  __syncthreads();
+
+  const float kappa_k = KM > 0 ? 1.2533141373155003f / (float)(KM > 0 ? KM : 1) : 0.0f;
+  const float kappa_v = VM > 0 ? 1.2533141373155003f / (float)(VM > 0 ? VM : 1) : 0.0f;
+  const int64_t t0 = (int64_t)chunk * a.chunk;
+  int64_t t1 = t0 + a.chunk;
+  if (t1 > a.n_ctx) t1 = a.n_ctx;
+  const int64_t vbase = blk * a.n_ctx;
+
+  // value-phase role of this thread
+  const int o = tid % NOUT;
+  const int part = tid / NOUT;
+  int vw0 = 0, vsh = 0;
+  if (o < D) {
+    vw0 = (o * VB) >> 5;
+    vsh = (o * VB) & 31;
+  }
+
+  float mrun[G], lrun[G], acc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    mrun[h] = -INFINITY;
+    lrun[h] = 0.0f;
+    acc[h] = 0.0f;
+  }
+
+  for (int64_t tile = t0; tile < t1; tile += NT) {
+    // ---- phase A: one token per thread: logits, value codes to LDS
+    const int64_t t = tile + tid;
+    const bool valid = t < t1;
+    float lg[G];
+    float vn = 0.0f, vr = 0.0f;
+    if (valid) {
+      const int64_t v = vbase + t;
+      uint32_t iw[CK::IW];
+      uint32_t sw[KSW];
+      load_words_a<CK::IW>(a.kidx + v * a.kidx_stride, iw);
+      if constexpr (KM > 0) load_words_a<CK::SW>(a.ksign + v * a.ksign_stride, sw);
+      const uint32_t nw = a.knorms[v];
+      uint32_t vwv[IWV];
+      load_words_a<IWV>(a.vidx + v * a.vidx_stride, vwv);
+#pragma unroll
+      for (int i = 0; i < IWV; ++i) vtile[tid * IWV + i] = vwv[i];
+      if constexpr (VM > 0) {
+        uint32_t vs[SWV];
+        load_words_a<SWV>(a.vsign + v * a.vsign_stride, vs);
+#pragma unroll
+        for (int i = 0; i < SWV; ++i) vstile[tid * SWV + i] = vs[i];
+      }
+      const uint32_t vnw = a.vnorms[v];
+      vn = f16_bits_to_float(vnw & 0xFFFFu);
+      vr = f16_bits_to_float(vnw >> 16) * kappa_v;
+      float am[G], aq[G];
+      lut_score<D, KB, KM, G>(iw, sw, tabs, tabs + CK::MSE_BYTES, hs, am, aq);
+      const float nbar = f16_bits_to_float(nw & 0xFFFFu);
+      const float rq = f16_bits_to_float(nw >> 16) * kappa_k;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float sc = nbar * am[h];
+        if constexpr (KM > 0) sc = fmaf(rq, aq[h], sc);
+        lg[h] = sc * a.scale_log2;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) lg[h] = -INFINITY;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mx = wave_max(lg[h]);
+      if (lane == 0) red_max[wid * G + h] = mx;
+    }
+    __syncthreads();
+    float mnew[G], alpha[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = mrun[h];
+      for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red_max[w * G + h]);
+      mnew[h] = mx;
+      alpha[h] = exp2f(mrun[h] - mx);  // 0 on the first tile (mrun = -inf)
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p = valid ? exp2f(lg[h] - mnew[h]) : 0.0f;
+      wt[tid * G + h] = p * vn;
+      if constexpr (VM > 0) wq[tid * G + h] = p * vr;
+      const float ps = wave_sumf(p);
+      if (lane == 0) red_sum[wid * G + h] = ps;
+    }
+    __syncthreads();
+    // ---- phase B: weighted values, one output coordinate per thread, a slice of the tile
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float ps = 0.0f;
+      for (int w = 0; w < NW; ++w) ps += red_sum[w * G + h];
+      lrun[h] = fmaf(lrun[h], alpha[h], ps);
+      acc[h] *= alpha[h];
+      mrun[h] = mnew[h];
+    }
+    int nt = (int)(t1 - tile);
+    if (nt > NT) nt = NT;
+    const int n0 = part * TOK;
+    int n1 = n0 + TOK;
+    if (n1 > nt) n1 = nt;
+    if (o < D) {
+      for (int n = n0; n < n1; ++n) {
+        const uint32_t w0 = vtile[n * IWV + vw0];
+        const uint32_t w1 = (vw0 + 1 < IWV) ? vtile[n * IWV + vw0 + 1] : 0u;
+        const uint32_t code = (uint32_t)(((((uint64_t)w1) << 32) | w0) >> vsh) & (LV - 1);
+        const float c = cbv[code];
+        if constexpr (G == 4) {
+          const float4 wv = *reinterpret_cast<const float4 *>(&wt[n * G]);
+          acc[0] = fmaf(wv.x, c, acc[0]);
+          acc[1] = fmaf(wv.y, c, acc[1]);
+          acc[2] = fmaf(wv.z, c, acc[2]);
+          acc[3] = fmaf(wv.w, c, acc[3]);
+        } else {
+#pragma unroll
+          for (int h = 0; h < G; ++h) acc[h] = fmaf(wt[n * G + h], c, acc[h]);
+        }
+      }
+    } else if constexpr (VM > 0) {
+      const int j = o - D;
+      for (int n = n0; n < n1; ++n) {
+        const uint32_t bit = (vstile[n * SWV + (j >> 5)] >> (j & 31)) & 1u;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float x = wq[n * G + h];
+          acc[h] += bit ? x : -x;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- reduce the TPO slices of each coordinate and write this chunk's partial state
+  float *red = reinterpret_cast<float *>(tabs);  // tables are no longer needed
+#pragma unroll
+  for (int h = 0; h < G; ++h) red[(part * NOUT + o) * G + h] = acc[h];
+  __syncthreads();
+  if (part == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float sacc = 0.0f;
+      for (int pp = 0; pp < TPO; ++pp) sacc += red[(pp * NOUT + o) * G + h];
+      float *dst = a.part + ((qrow + h) * a.n_chunks + chunk) * (int64_t)(2 + NOUT);
+      dst[2 + o] = sacc;
+      if (o == 0) {
+        dst[0] = mrun[h];
+        dst[1] = lrun[h];
+      }
+    }
+  }
+}
+
+struct CombArgs {
+  const float *part;
+  int64_t n_heads;  // n_seq * hq
+  int hq, hkv, n_chunks;
+  int64_t n_ctx;
+  const float *vrot;
+  int n_rot;
+  int64_t vecs_per_rot;
+  const float *vsketch;
+  float *out;
+};
+
+template <int D, int VM>
+__global__ __launch_bounds__(256) void attend_combine(CombArgs a) {
+  constexpr int NOUT = D + VM;
+  __shared__ float av[4][NOUT];
+  __shared__ float uv[4][D];
+  const int lane = lane_id(), wid = threadIdx.x / kWave;
+  const int64_t hidx = (int64_t)blockIdx.x * 4 + wid;
+  if (hidx >= a.n_heads) return;
+  const float *p = a.part + hidx * a.n_chunks * (int64_t)(2 + NOUT);
+  float m = -INFINITY;
+  for (int c = lane; c < a.n_chunks; c += kWave) m = fmaxf(m, p[c * (2 + NOUT)]);
+  m = wave_max(m);
+  float l = 0.0f;
+  for (int c = lane; c < a.n_chunks; c += kWave) l += exp2f(p[c * (2 + NOUT)] - m) * p[c * (2 + NOUT) + 1];
+  l = wave_sumf(l);
+  const float inv = 1.0f / l;
+  for (int o = lane; o < NOUT; o += kWave) {
+    float sacc = 0.0f;
+    for (int c = 0; c < a.n_chunks; ++c) sacc = fmaf(exp2f(p[c * (2 + NOUT)] - m), p[c * (2 + NOUT) + 2 + o], sacc);
+    av[wid][o] = sacc * inv;
+  }
+  wave_lds_fence();
+  // u = A_rot + S_V^T A_sk in the rotated space (A_sk already carries sqrt(pi/2)/m)
+  for (int i = lane; i < D; i += kWave) {
+    float u = av[wid][i];
+    if constexpr (VM > 0) {
+      for (int j = 0; j < VM; ++j) u = fmaf(a.vsketch[(int64_t)j * D + i], av[wid][D + j], u);
+    }
+    uv[wid][i] = u;
+  }
+  wave_lds_fence();
+  const int64_t s = hidx / a.hq;
+  const int h = (int)(hidx % a.hq);
+  const int64_t blk = s * a.hkv + h / (a.hq / a.hkv);
+  int64_t rid = 0;
+  if (a.n_rot > 1 && a.vecs_per_rot > 0) {
+    rid = (blk * a.n_ctx) / a.vecs_per_rot;
+    if (rid > a.n_rot - 1) rid = a.n_rot - 1;
+  }
+  const float *R = a.vrot + rid * (int64_t)D * D;
+  for (int k = lane; k < D; k += kWave) {
+    float o = 0.0f;
+    for (int i = 0; i < D; ++i) o = fmaf(R[(int64_t)i * D + k], uv[wid][i], o);  // (Pi^T u)_k
+    a.out[hidx * D + k] = o;
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+static int att_chunk(const ScoreShape &s) {
+  const int64_t pairs = s.n_seq * s.hkv;
+  int ch = pairs >= 2048 ? 8192 : 4096;
+  while (ch > 512 && pairs * ((s.n + ch - 1) / ch) < 1024) ch /= 2;
+  return ch;
+}
+
+static int att_g(int g) { return g % 4 == 0 ? 4 : (g % 2 == 0 ? 2 : 1); }
+
+size_t attend_workspace(const CodecView &kc, const CodecView &vc, const ScoreShape &s) {
+  const int64_t nch = (s.n + att_chunk(s) - 1) / att_chunk(s);
+  const size_t q = (size_t)s.n_seq * s.hq * (size_t)(kc.d + kc.m) * sizeof(float);
+  const size_t q_al = (q + 255) / 256 * 256;
+  return q_al + (size_t)s.n_seq * s.hq * nch * (size_t)(2 + vc.d + vc.m) * sizeof(float);
+}
+
+template <int D, int KB, int KM, int VB, int VM, int G>
+static int launch_att(const AttArgs &a0, const ScoreShape &s, hipStream_t st) {
+  constexpr int NOUT = D + VM;
+  constexpr int NT = (G == 4) ? 512 : (NOUT > 256 ? 512 : 256);
+  AttArgs a = a0;
+  a.nsub = (s.hq / s.hkv) / G;
+  hipLaunchKernelGGL((attend_partial<D, KB, KM, VB, VM, G, NT>), dim3((unsigned)(s.n_seq * s.hkv * a.nsub * a.n_chunks)),
+                     dim3(NT), 0, st, a);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+template <int D, int KB, int KM, int VB, int VM>
+static int launch_att_g(const AttArgs &a, const ScoreShape &s, hipStream_t st) {
+  switch (att_g(s.hq / s.hkv)) {
+    case 4: return launch_att<D, KB, KM, VB, VM, 4>(a, s, st);
+    case 2: return launch_att<D, KB, KM, VB, VM, 2>(a, s, st);
+    default: return launch_att<D, KB, KM, VB, VM, 1>(a, s, st);
+  }
+}
+
+template <int D, int VM>
+static int launch_comb(const CombArgs &c, hipStream_t st) {
+  hipLaunchKernelGGL((attend_combine<D, VM>), dim3((unsigned)((c.n_heads + 3) / 4)), dim3(256), 0, st, c);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+int launch_attend(const CodecView &kc, const CodecView &vc, const float *q, const ScoreShape &s, const CodesView &k,
+                  const CodesView &v, float scale, float *out, void *ws, size_t ws_bytes, void *stream) {
+  if (s.n_seq == 0) return TQ_OK;
+  (void)ws_bytes;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float *qt = reinterpret_cast<float *>(ws);
+  float *qh = qt + (size_t)s.n_seq * s.hq * kc.d;
+  const size_t qbytes = (size_t)s.n_seq * s.hq * (size_t)(kc.d + kc.m) * sizeof(float);
+  float *part = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + (qbytes + 255) / 256 * 256);
+  int rc = qprep(kc, q, s, qt, qh, st);
+  if (rc != TQ_OK) return rc;
+  const int ch = att_chunk(s);
+  const int nch = (int)((s.n + ch - 1) / ch);
+  AttArgs a{qt, qh, kc.centroids, vc.centroids, s.n_seq, s.n, s.hq, s.hkv, 1, nch, ch, scale * kLog2e,
+            k.idx, k.idx_stride, k.sign, k.sign_stride, k.norms, v.idx, v.idx_stride, v.sign, v.sign_stride,
+            v.norms, part};
+  const int D = kc.d, KB = kc.bits, KM = kc.m, VB = vc.bits, VM = vc.m;
+  rc = TQ_EUNSUPPORTED;
+#define TQ_AT(DD, A, B, C, E) \
+  if (D == DD && KB == A && KM == B && VB == C && VM == E) rc = launch_att_g<DD, A, B, C, E>(a, s, st); else
+  TQ_AT(64, 2, 64, 2, 64) TQ_AT(64, 3, 64, 3, 64) TQ_AT(64, 2, 64, 3, 0) TQ_AT(128, 2, 128, 3, 0)
+  TQ_AT(128, 3, 0, 3, 0) TQ_AT(128, 2, 128, 2, 128) TQ_AT(128, 3, 128, 3, 128) {}
+#undef TQ_AT
+  if (rc != TQ_OK) return rc;
+  CombArgs c{part, s.n_seq * s.hq, s.hq, s.hkv, nch, s.n, vc.rot, vc.n_rot, vc.vecs_per_rot, vc.sketch, out};
+  if (D == 64 && VM == 64) return launch_comb<64, 64>(c, st);
+  if (D == 64 && VM == 0) return launch_comb<64, 0>(c, st);
+  if (D == 128 && VM == 0) return launch_comb<128, 0>(c, st);
+  if (D == 128 && VM == 128) return launch_comb<128, 128>(c, st);
   return TQ_EUNSUPPORTED;
 }
 

@@ -12,9 +12,12 @@
 // then one LDS lookup per group, summed in fp32.
 //
 // Several query heads that read the same kv head (GQA) share one lookup: an entry holds G
-// heads' values.  G = 1 and 2 store fp32; G = 4 stores fp16 values scaled per head by a
-// power of two (so the largest possible entry is about 2^14), which keeps the LDS footprint
-// at 8 bytes per entry; sums stay fp32.
+// heads' values.  G = 1 and 2 store fp32.  G = 4 stores each head's value as a 16-bit
+// fixed-point integer (8 bytes per entry, so the four heads' tables of a 128-dimensional
+// 2-bit + QJL key fit LDS), scaled per head and table so that the largest entry the table can
+// hold maps to 32767; the 16-bit values are summed exactly in 32-bit integers and converted
+// once per key.  The only rounding is the quantisation of each entry, at most half a unit of
+// (largest entry) / 32767.
 #pragma once
 
 #include "tq_device.h"
@@ -29,7 +32,7 @@ struct Lut {
   static constexpr int NG = D / CPG;
   static constexpr int TS = 1 << GB;
   static constexpr int NQ = M / 8;
-  static constexpr bool F16 = (G == 4);
+  static constexpr bool I16 = (G == 4);
   static constexpr int EB = (G == 1) ? 4 : 8;  // entry bytes
   static constexpr int MSE_BYTES = NG * TS * EB;
   static constexpr int QJL_BYTES = NQ * 256 * EB;
@@ -46,14 +49,12 @@ struct HeadScales {
   float inv_q[G];
 };
 
-// Power-of-two scale 2^e with 2^e * bound <= 2^14 (bound > 0), as float.
-__device__ __forceinline__ float pow2_scale_for(float bound) {
-  if (!(bound > 0.0f)) return 1.0f;
-  int e;
-  (void)frexpf(bound, &e);  // bound < 2^e
-  int s = 14 - e;
-  s = s > 100 ? 100 : (s < -100 ? -100 : s);
-  return ldexpf(1.0f, s);
+// Four scaled values -> four 16-bit fixed-point integers (round to nearest), packed.
+__device__ __forceinline__ uint2 pack_i16x4(const float (&v)[4]) {
+  uint32_t q[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) q[h] = (uint32_t)(int)rintf(fminf(fmaxf(v[h], -32767.0f), 32767.0f)) & 0xFFFFu;
+  return make_uint2(q[0] | (q[1] << 16), q[2] | (q[3] << 16));
 }
 
 // Build the tables of G query heads in LDS.  qt [G][D] and qh [G][M] (fp32) and the codebook
@@ -81,11 +82,7 @@ __device__ void build_luts(uint8_t *mse, uint8_t *qjl, const float *qt, const fl
     } else if constexpr (G == 2) {
       reinterpret_cast<float2 *>(mse)[e] = make_float2(v[0], v[1]);
     } else {
-      const uint32_t lo = (uint32_t)__half_as_ushort(__float2half_rn(v[0])) |
-                          ((uint32_t)__half_as_ushort(__float2half_rn(v[1])) << 16);
-      const uint32_t hi = (uint32_t)__half_as_ushort(__float2half_rn(v[2])) |
-                          ((uint32_t)__half_as_ushort(__float2half_rn(v[3])) << 16);
-      reinterpret_cast<uint2 *>(mse)[e] = make_uint2(lo, hi);
+      reinterpret_cast<uint2 *>(mse)[e] = pack_i16x4(v);
     }
   }
   if constexpr (M > 0) {
@@ -107,19 +104,16 @@ __device__ void build_luts(uint8_t *mse, uint8_t *qjl, const float *qt, const fl
       } else if constexpr (G == 2) {
         reinterpret_cast<float2 *>(qjl)[e] = make_float2(v[0], v[1]);
       } else {
-        const uint32_t lo = (uint32_t)__half_as_ushort(__float2half_rn(v[0])) |
-                            ((uint32_t)__half_as_ushort(__float2half_rn(v[1])) << 16);
-        const uint32_t hi = (uint32_t)__half_as_ushort(__float2half_rn(v[2])) |
-                            ((uint32_t)__half_as_ushort(__float2half_rn(v[3])) << 16);
-        reinterpret_cast<uint2 *>(qjl)[e] = make_uint2(lo, hi);
+        reinterpret_cast<uint2 *>(qjl)[e] = pack_i16x4(v);
       }
     }
   }
 }
 
-// Per-head table scales: fp32 tables use 1; fp16 tables use 2^e so that the largest entry
-// bound (CPG max|c| max|q~| or 8 max|q^|) maps to at most 2^14.  Computed by every wave
-// redundantly from qt/qh in LDS (values identical across waves).
+// Per-head table scales.  fp32 tables use 1.  16-bit tables map the largest entry a table
+// can hold -- max over positions of cmax * sum |q~| over the position's coordinates for the
+// index tables, sum |q^| over the byte's rows for the sign tables -- to 32767.  Every wave
+// computes the values redundantly from qt/qh in LDS (identical across waves).
 template <int D, int BITS, int M, int G>
 __device__ void table_scales(const float *qt, const float *qh, float cmax, float *scale_m, float *scale_q,
                              HeadScales<G> &hs) {
@@ -127,30 +121,46 @@ __device__ void table_scales(const float *qt, const float *qh, float cmax, float
   const int lane = lane_id();
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float sm = 1.0f, sq = 1.0f;
-    if constexpr (C::F16) {
+    float sm = 1.0f, sq = 1.0f, im = 1.0f, iq = 1.0f;
+    if constexpr (C::I16) {
       float a = 0.0f;
-      for (int i = lane; i < D; i += kWave) a = fmaxf(a, fabsf(qt[h * D + i]));
-      a = wave_max(a);
-      sm = pow2_scale_for(a * cmax * C::CPG);
+      for (int p = lane; p < C::NG; p += kWave) {
+        float t = 0.0f;
+#pragma unroll
+        for (int u = 0; u < C::CPG; ++u) t += fabsf(qt[h * D + C::CPG * p + u]);
+        a = fmaxf(a, t);
+      }
+      a = wave_max(a) * cmax;
+      if (a > 0.0f) {
+        sm = 32767.0f / a;
+        im = a / 32767.0f;
+      }
       if constexpr (M > 0) {
         float b = 0.0f;
-        for (int i = lane; i < M; i += kWave) b = fmaxf(b, fabsf(qh[h * M + i]));
+        for (int p = lane; p < C::NQ; p += kWave) {
+          float t = 0.0f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) t += fabsf(qh[h * M + 8 * p + u]);
+          b = fmaxf(b, t);
+        }
         b = wave_max(b);
-        sq = pow2_scale_for(b * 8.0f);
+        if (b > 0.0f) {
+          sq = 32767.0f / b;
+          iq = b / 32767.0f;
+        }
       }
     }
     scale_m[h] = sm;
     scale_q[h] = sq;
-    hs.inv_m[h] = 1.0f / sm;
-    hs.inv_q[h] = 1.0f / sq;
+    hs.inv_m[h] = im;
+    hs.inv_q[h] = iq;
   }
 }
 
-// acc[h] += entry[h] * inv[h].  For fp16 entries this is one v_fma_mix_f32 per head (the
-// fp16 operand is widened inside the FMA; inv is the exact power-of-two descale).
-template <int G, bool F16>
-__device__ __forceinline__ void lut_accumulate(const uint8_t *tab, int entry, float (&acc)[G], const float (&inv)[G]) {
+// acc[h] += entry[h] for fp32 tables (G = 1, 2); iacc[h] += entry[h] for 16-bit tables
+// (G = 4: one v_dot2c_i32_i16 per head, the entry pair dotted with (1, 0) or (0, 1)).
+template <int G>
+__device__ __forceinline__ void lut_accumulate(const uint8_t *tab, int entry, float (&acc)[G], int (&iacc)[G]) {
   if constexpr (G == 1) {
     acc[0] += reinterpret_cast<const float *>(tab)[entry];
   } else if constexpr (G == 2) {
@@ -158,14 +168,14 @@ __device__ __forceinline__ void lut_accumulate(const uint8_t *tab, int entry, fl
     acc[0] += e.x;
     acc[1] += e.y;
   } else {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    typedef short s2 __attribute__((ext_vector_type(2)));
+    const s2 lo = {1, 0}, hi = {0, 1};
     const uint2 e = reinterpret_cast<const uint2 *>(tab)[entry];
-    const h2 p = __builtin_bit_cast(h2, e.x);
-    const h2 q = __builtin_bit_cast(h2, e.y);
-    acc[0] = __builtin_fmaf((float)p.x, inv[0], acc[0]);
-    acc[1] = __builtin_fmaf((float)p.y, inv[1], acc[1]);
-    acc[2] = __builtin_fmaf((float)q.x, inv[2], acc[2]);
-    acc[3] = __builtin_fmaf((float)q.y, inv[3], acc[3]);
+    const s2 x = __builtin_bit_cast(s2, e.x), y = __builtin_bit_cast(s2, e.y);
+    iacc[0] = __builtin_amdgcn_sdot2(x, lo, iacc[0], false);
+    iacc[1] = __builtin_amdgcn_sdot2(x, hi, iacc[1], false);
+    iacc[2] = __builtin_amdgcn_sdot2(y, lo, iacc[2], false);
+    iacc[3] = __builtin_amdgcn_sdot2(y, hi, iacc[3], false);
   }
 }
 
@@ -180,25 +190,36 @@ __device__ __forceinline__ int group_code(const uint32_t (&w)[IW], int p) {
 }
 
 // Score one key against the G heads whose tables are in LDS.  Returns the two sums (index
-// part and sign part) per head, descaled to query units.
+// part and sign part) per head, in query units.
 template <int D, int BITS, int M, int G>
 __device__ __forceinline__ void lut_score(const uint32_t (&iw)[Lut<D, BITS, M, G>::IW],
                                           const uint32_t (&sw)[Lut<D, BITS, M, G>::SW > 0 ? Lut<D, BITS, M, G>::SW : 1],
                                           const uint8_t *mse, const uint8_t *qjl, const HeadScales<G> &hs,
                                           float (&am)[G], float (&aq)[G]) {
   using C = Lut<D, BITS, M, G>;
+  int im[G], iq[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) am[h] = aq[h] = 0.0f;
+  for (int h = 0; h < G; ++h) {
+    am[h] = aq[h] = 0.0f;
+    im[h] = iq[h] = 0;
+  }
 #pragma unroll
   for (int p = 0; p < C::NG; ++p) {
     const int code = group_code<BITS, C::IW, C::GB>(iw, p);
-    lut_accumulate<G, C::F16>(mse, p * C::TS + code, am, hs.inv_m);
+    lut_accumulate<G>(mse, p * C::TS + code, am, im);
   }
   if constexpr (M > 0) {
 #pragma unroll
     for (int p = 0; p < C::NQ; ++p) {
       const int byte = (sw[p >> 2] >> (8 * (p & 3))) & 0xFF;
-      lut_accumulate<G, C::F16>(qjl, p * 256 + byte, aq, hs.inv_q);
+      lut_accumulate<G>(qjl, p * 256 + byte, aq, iq);
+    }
+  }
+  if constexpr (C::I16) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      am[h] = (float)im[h] * hs.inv_m[h];
+      aq[h] = (float)iq[h] * hs.inv_q[h];
     }
   }
 }
