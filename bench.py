@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attend", action="store_true")
     ap.add_argument("--encode-reps", type=int, default=3)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -200,6 +202,13 @@ def main():
                      "kernel": "score_kernel (+ its qprep launch inside the timed call)"},
         "gpu": torch.cuda.get_device_name(0),
     }
+    if a.calibrate:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calibration_copy_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, K, q, synth.SEED_ROT_K, synth.SEED_SKETCH_K)

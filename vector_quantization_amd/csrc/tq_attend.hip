@@ -72,17 +72,23 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   constexpr int IWV = (D * VB + 31) / 32;
   constexpr int SWV = (VM + 31) / 32;
   constexpr int NOUT = D + VM;
-  constexpr int TPO = NT / NOUT;  // threads sharing one output coordinate
-  constexpr int TOK = NT / TPO;   // tokens of a tile handled by one thread in the value phase
+  constexpr int CPT = 8;             // consecutive output coordinates per thread (value phase)
+  constexpr int NCG = NOUT / CPT;    // coordinate groups
+  constexpr int TPO = NT / NCG;      // threads sharing one coordinate group (token slices)
+  constexpr int TOK = NT / TPO;      // tokens of a tile handled by one thread in the value phase
   constexpr int NW = NT / kWave;
-  static_assert(NT % NOUT == 0, "threads must cover the output coordinates evenly");
+  static_assert(D % CPT == 0 && VM % CPT == 0 && NT % NCG == 0, "threads must cover the outputs evenly");
   constexpr int LV = 1 << VB;
+  constexpr int LP = LV * LV;        // entries of the two-code value table
+  constexpr int RCAP = Lut<D, KB, KM, G>::BYTES / (NOUT * G * 4);  // slices per reduction round
+  static_assert(RCAP >= 1, "final reduction reuses the table space");
 
   __shared__ __align__(16) uint8_t tabs[CK::BYTES];
   __shared__ float qt[G * D];
   __shared__ float qh[G * (KM > 0 ? KM : 1)];
   __shared__ float cbk[1 << KB];
   __shared__ float cbv[LV];
+  __shared__ float2 cbv2[LP];  // (c[a], c[b]) for the two-code group (b << VB) | a
   __shared__ float scm[G], scq[G];
   __shared__ uint32_t vtile[NT * IWV];
   __shared__ uint32_t vstile[VM > 0 ? NT * SWV : 1];
@@ -106,6 +112,7 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
     for (int i = tid; i < G * KM; i += NT) qh[i] = a.qh[qrow * KM + i];
   if (tid < (1 << KB)) cbk[tid] = a.kcent[tid];
   if (tid < LV) cbv[tid] = a.vcent[tid];
+  for (int e = tid; e < LP; e += NT) cbv2[e] = make_float2(a.vcent[e & (LV - 1)], a.vcent[e >> VB]);
   __syncthreads();
   HeadScales<G> hs;
   {
@@ -128,23 +135,47 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   if (t1 > a.n_ctx) t1 = a.n_ctx;
   const int64_t vbase = blk * a.n_ctx;
 
-  // value-phase role of this thread
-  const int o = tid % NOUT;
-  const int part = tid / NOUT;
-  int vw0 = 0, vsh = 0;
-  if (o < D) {
-    vw0 = (o * VB) >> 5;
-    vsh = (o * VB) & 31;
-  }
+  // value-phase role of this thread: coordinates o0 .. o0 + CPT - 1, tokens part*TOK ..
+  const int o0 = (tid % NCG) * CPT;
+  const int part = tid / NCG;
+  const bool is_val = o0 < D;
+  const int vw0 = is_val ? (o0 * VB) >> 5 : 0;
+  const int vsh = is_val ? (o0 * VB) & 31 : 0;
+  const int vw1i = (vw0 + 1 < IWV) ? vw0 + 1 : vw0;  // a clamped second word: its bits are masked off when unused
+  const int sj = is_val ? 0 : o0 - D;  // first sketch row (value QJL part)
 
-  float mrun[G], lrun[G], acc[G];
+  float mrun[G], lrun[G], acc[CPT][G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     mrun[h] = -INFINITY;
     lrun[h] = 0.0f;
-    acc[h] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[c][h] = 0.0f;
   }
 
+  // Records of the next tile are loaded into registers before the current tile's value
+  // phase, so that HBM latency overlaps the arithmetic (the tile loop has barriers).
+  struct Rec {
+    uint32_t iw[CK::IW];
+    uint32_t sw[KSW];
+    uint32_t nw;
+    uint32_t vw[IWV];
+    uint32_t vs[VM > 0 ? SWV : 1];
+    uint32_t vnw;
+  };
+  auto load_rec = [&](int64_t t, Rec &r) {
+    if (t < t1) {
+      const int64_t v = vbase + t;
+      load_words_a<CK::IW>(a.kidx + v * a.kidx_stride, r.iw);
+      if constexpr (KM > 0) load_words_a<CK::SW>(a.ksign + v * a.ksign_stride, r.sw);
+      r.nw = a.knorms[v];
+      load_words_a<IWV>(a.vidx + v * a.vidx_stride, r.vw);
+      if constexpr (VM > 0) load_words_a<SWV>(a.vsign + v * a.vsign_stride, r.vs);
+      r.vnw = a.vnorms[v];
+    }
+  };
+  Rec cur;
+  load_rec(t0 + tid, cur);
   for (int64_t tile = t0; tile < t1; tile += NT) {
     // ---- phase A: one token per thread: logits, value codes to LDS
     const int64_t t = tile + tid;
@@ -152,29 +183,18 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
     float lg[G];
     float vn = 0.0f, vr = 0.0f;
     if (valid) {
-      const int64_t v = vbase + t;
-      uint32_t iw[CK::IW];
-      uint32_t sw[KSW];
-      load_words_a<CK::IW>(a.kidx + v * a.kidx_stride, iw);
-      if constexpr (KM > 0) load_words_a<CK::SW>(a.ksign + v * a.ksign_stride, sw);
-      const uint32_t nw = a.knorms[v];
-      uint32_t vwv[IWV];
-      load_words_a<IWV>(a.vidx + v * a.vidx_stride, vwv);
 #pragma unroll
-      for (int i = 0; i < IWV; ++i) vtile[tid * IWV + i] = vwv[i];
+      for (int i = 0; i < IWV; ++i) vtile[tid * IWV + i] = cur.vw[i];
       if constexpr (VM > 0) {
-        uint32_t vs[SWV];
-        load_words_a<SWV>(a.vsign + v * a.vsign_stride, vs);
 #pragma unroll
-        for (int i = 0; i < SWV; ++i) vstile[tid * SWV + i] = vs[i];
+        for (int i = 0; i < SWV; ++i) vstile[tid * SWV + i] = cur.vs[i];
       }
-      const uint32_t vnw = a.vnorms[v];
-      vn = f16_bits_to_float(vnw & 0xFFFFu);
-      vr = f16_bits_to_float(vnw >> 16) * kappa_v;
+      vn = f16_bits_to_float(cur.vnw & 0xFFFFu);
+      vr = f16_bits_to_float(cur.vnw >> 16) * kappa_v;
       float am[G], aq[G];
-      lut_score<D, KB, KM, G>(iw, sw, tabs, tabs + CK::MSE_BYTES, hs, am, aq);
-      const float nbar = f16_bits_to_float(nw & 0xFFFFu);
-      const float rq = f16_bits_to_float(nw >> 16) * kappa_k;
+      lut_score<D, KB, KM, G>(cur.iw, cur.sw, tabs, tabs + CK::MSE_BYTES, hs, am, aq);
+      const float nbar = f16_bits_to_float(cur.nw & 0xFFFFu);
+      const float rq = f16_bits_to_float(cur.nw >> 16) * kappa_k;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float sc = nbar * am[h];
@@ -185,6 +205,7 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h) lg[h] = -INFINITY;
     }
+    load_rec(tile + NT + tid, cur);  // the next tile's records (registers of this tile are consumed)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float mx = wave_max(lg[h]);
@@ -208,63 +229,90 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
       if (lane == 0) red_sum[wid * G + h] = ps;
     }
     __syncthreads();
-    // ---- phase B: weighted values, one output coordinate per thread, a slice of the tile
+    // ---- phase B: weighted values; tokens past the end carry weight 0
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float ps = 0.0f;
       for (int w = 0; w < NW; ++w) ps += red_sum[w * G + h];
       lrun[h] = fmaf(lrun[h], alpha[h], ps);
-      acc[h] *= alpha[h];
       mrun[h] = mnew[h];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[c][h] *= alpha[h];
     }
-    int nt = (int)(t1 - tile);
-    if (nt > NT) nt = NT;
     const int n0 = part * TOK;
-    int n1 = n0 + TOK;
-    if (n1 > nt) n1 = nt;
-    if (o < D) {
-      for (int n = n0; n < n1; ++n) {
+    if (is_val) {
+#pragma unroll 4
+      for (int n = n0; n < n0 + TOK; ++n) {
         const uint32_t w0 = vtile[n * IWV + vw0];
-        const uint32_t w1 = (vw0 + 1 < IWV) ? vtile[n * IWV + vw0 + 1] : 0u;
-        const uint32_t code = (uint32_t)(((((uint64_t)w1) << 32) | w0) >> vsh) & (LV - 1);
-        const float c = cbv[code];
+        const uint32_t w1 = vtile[n * IWV + vw1i];
+        const uint32_t bits = (uint32_t)(((((uint64_t)w1) << 32) | w0) >> vsh);
+        float wv[G];
         if constexpr (G == 4) {
-          const float4 wv = *reinterpret_cast<const float4 *>(&wt[n * G]);
-          acc[0] = fmaf(wv.x, c, acc[0]);
-          acc[1] = fmaf(wv.y, c, acc[1]);
-          acc[2] = fmaf(wv.z, c, acc[2]);
-          acc[3] = fmaf(wv.w, c, acc[3]);
+          const float4 t4 = *reinterpret_cast<const float4 *>(&wt[n * G]);
+          wv[0] = t4.x; wv[1] = t4.y; wv[2] = t4.z; wv[3] = t4.w;
         } else {
 #pragma unroll
-          for (int h = 0; h < G; ++h) acc[h] = fmaf(wt[n * G + h], c, acc[h]);
+          for (int h = 0; h < G; ++h) wv[h] = wt[n * G + h];
+        }
+#pragma unroll
+        for (int c = 0; c < CPT; c += 2) {
+          const float2 cv = cbv2[(bits >> (VB * c)) & (LP - 1)];
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            acc[c][h] = fmaf(wv[h], cv.x, acc[c][h]);
+            acc[c + 1][h] = fmaf(wv[h], cv.y, acc[c + 1][h]);
+          }
         }
       }
     } else if constexpr (VM > 0) {
-      const int j = o - D;
-      for (int n = n0; n < n1; ++n) {
-        const uint32_t bit = (vstile[n * SWV + (j >> 5)] >> (j & 31)) & 1u;
+#pragma unroll 4
+      for (int n = n0; n < n0 + TOK; ++n) {
+        const uint32_t sb = vstile[n * SWV + (sj >> 5)] >> (sj & 31);  // CPT rows within one word
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float x = wq[n * G + h];
-          acc[h] += bit ? x : -x;
+        for (int c = 0; c < CPT; ++c) {
+          const bool pos = (sb >> c) & 1u;
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float x = wq[n * G + h];
+            acc[c][h] += pos ? x : -x;
+          }
         }
       }
     }
     __syncthreads();
   }
 
-  // ---- reduce the TPO slices of each coordinate and write this chunk's partial state
+  // ---- reduce the TPO slices of each coordinate (in rounds of RCAP slices through the table
+  // space) and write this chunk's partial state
   float *red = reinterpret_cast<float *>(tabs);  // tables are no longer needed
+  constexpr int OPT = (NOUT * G + NT - 1) / NT;  // outputs per thread
+  float osum[OPT];
 #pragma unroll
-  for (int h = 0; h < G; ++h) red[(part * NOUT + o) * G + h] = acc[h];
-  __syncthreads();
-  if (part == 0) {
+  for (int u = 0; u < OPT; ++u) osum[u] = 0.0f;
+  for (int r0 = 0; r0 < TPO; r0 += RCAP) {
+    __syncthreads();
+    if (part >= r0 && part < r0 + RCAP) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float sacc = 0.0f;
-      for (int pp = 0; pp < TPO; ++pp) sacc += red[(pp * NOUT + o) * G + h];
+      for (int c = 0; c < CPT; ++c)
+#pragma unroll
+        for (int h = 0; h < G; ++h) red[((part - r0) * NOUT + o0 + c) * G + h] = acc[c][h];
+    }
+    __syncthreads();
+    const int nr = (TPO - r0) < RCAP ? (TPO - r0) : RCAP;
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int e = tid + u * NT;
+      if (e < NOUT * G)
+        for (int pp = 0; pp < nr; ++pp) osum[u] += red[pp * NOUT * G + e];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < OPT; ++u) {
+    const int e = tid + u * NT;
+    if (e < NOUT * G) {
+      const int o = e / G, h = e % G;
       float *dst = a.part + ((qrow + h) * a.n_chunks + chunk) * (int64_t)(2 + NOUT);
-      dst[2 + o] = sacc;
+      dst[2 + o] = osum[u];
       if (o == 0) {
         dst[0] = mrun[h];
         dst[1] = lrun[h];

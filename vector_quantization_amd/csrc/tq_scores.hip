@@ -73,6 +73,88 @@ __global__ __launch_bounds__(256) void qprep_kernel(QprepArgs a) {
   }
 }
 
+// Tiled variant for a codec with one shared rotation: a block takes 16 query heads and
+// computes q~ = q Pi^T, then q^ = q~ S^T, staging 8-column tiles of Pi (or S) transposed in
+// LDS so that the output columns are read without bank conflicts.
+constexpr int kQpHeads = 16;
+constexpr int kQpKt = 8;
+
+template <int D, int M>
+__global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
+  constexpr int NOUT = D > M ? D : M;
+  constexpr int TPC = (256 / NOUT) >= 1 ? 256 / NOUT : 1;  // threads per output column
+  constexpr int HPT = kQpHeads / TPC;                      // heads per thread
+  __shared__ float qs[kQpHeads][D + 1];
+  __shared__ float rt[kQpKt][NOUT + 1];
+  const int tid = threadIdx.x;
+  const int64_t h0 = (int64_t)blockIdx.x * kQpHeads;
+  for (int e = tid; e < kQpHeads * D; e += 256) {
+    int64_t h = h0 + e / D;
+    if (h > a.n_heads - 1) h = a.n_heads - 1;
+    qs[e / D][e % D] = a.q[h * D + e % D];
+  }
+  const int col = tid % NOUT;
+  const int hs = tid / NOUT;
+  const bool active = hs < TPC;
+  float acc[HPT];
+  // ---- q~ = q Pi^T
+#pragma unroll
+  for (int j = 0; j < HPT; ++j) acc[j] = 0.0f;
+  for (int k0 = 0; k0 < D; k0 += kQpKt) {
+    __syncthreads();
+    for (int e = tid; e < D * kQpKt; e += 256) {
+      const int i = e / kQpKt, kk = e % kQpKt;
+      rt[kk][i] = a.rot[(int64_t)i * D + k0 + kk];
+    }
+    __syncthreads();
+    if (active && col < D) {
+#pragma unroll
+      for (int kk = 0; kk < kQpKt; ++kk) {
+        const float r = rt[kk][col];
+#pragma unroll
+        for (int j = 0; j < HPT; ++j) acc[j] = fmaf(r, qs[hs * HPT + j][k0 + kk], acc[j]);
+      }
+    }
+  }
+  __syncthreads();
+  if (active && col < D) {
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) {
+      const int64_t h = h0 + hs * HPT + j;
+      qs[hs * HPT + j][col] = acc[j];
+      if (h < a.n_heads) a.qt[h * D + col] = acc[j];
+    }
+  }
+  if constexpr (M > 0) {
+    // ---- q^ = q~ S^T
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) acc[j] = 0.0f;
+    for (int k0 = 0; k0 < D; k0 += kQpKt) {
+      __syncthreads();
+      for (int e = tid; e < M * kQpKt; e += 256) {
+        const int i = e / kQpKt, kk = e % kQpKt;
+        rt[kk][i] = a.sketch[(int64_t)i * D + k0 + kk];
+      }
+      __syncthreads();
+      if (active && col < M) {
+#pragma unroll
+        for (int kk = 0; kk < kQpKt; ++kk) {
+          const float r = rt[kk][col];
+#pragma unroll
+          for (int j = 0; j < HPT; ++j) acc[j] = fmaf(r, qs[hs * HPT + j][k0 + kk], acc[j]);
+        }
+      }
+    }
+    if (active && col < M) {
+#pragma unroll
+      for (int j = 0; j < HPT; ++j) {
+        const int64_t h = h0 + hs * HPT + j;
+        if (h < a.n_heads) a.qh[h * M + col] = acc[j];
+      }
+    }
+  }
+}
+
 struct ScoreArgs {
   const float *qt, *qh, *centroids;
   int64_t n_seq, n_keys;
@@ -181,8 +263,13 @@ template <int D, int M>
 static int launch_qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh,
                         hipStream_t st) {
   QprepArgs a{q, s.n_seq * s.hq, s.hq, s.hkv, s.n, kc.rot, kc.n_rot, kc.vecs_per_rot, kc.sketch, qt, qh};
-  const int64_t blocks = (a.n_heads + 3) / 4;
-  hipLaunchKernelGGL((qprep_kernel<D, M>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  if (kc.n_rot == 1 || kc.vecs_per_rot == 0) {
+    const int64_t blocks = (a.n_heads + kQpHeads - 1) / kQpHeads;
+    hipLaunchKernelGGL((qprep_tiled<D, M>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  } else {
+    const int64_t blocks = (a.n_heads + 3) / 4;
+    hipLaunchKernelGGL((qprep_kernel<D, M>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 
