@@ -15,8 +15,8 @@
 // cannot, an exact expansion sum decides (Shewchuk's Grow-Expansion), so the stored bits are
 // those of the exact real quantities.
 //
-// Layout: one wavefront per vector.  Lane l owns coordinates l + 64c (c < ceil(d/64)) and
-// sketch rows l + 64c.  The index stream is packed from an LDS copy of the codes, the sign
+// encode_kernel (any d, per-vector rotations, unaligned input): one wavefront per vector.
+// Lane l owns coordinates l + 64c (c < ceil(d/64)) and sketch rows l + 64c.  The index stream is packed from an LDS copy of the codes, the sign
 // stream straight from wave ballots (lane l -> bit l).
 
 #include "tq_device.h"
@@ -261,10 +261,467 @@ __global__ __launch_bounds__(kWave *kEncWaves) void encode_kernel(EncArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ MFMA encode (d = 64, 128)
+//
+// Persistent workgroups of NTH threads.  Each wavefront keeps, in registers, the bf16 hi/lo
+// split of its column slice of Pi^T and of S^T as MFMA B operands (loaded once).  Per tile
+// of T vectors (T * d = 8192 elements):
+//   1. the inputs go to LDS as fp32 (exact) and as a bf16 hi/lo split (A operand);
+//   2. the exact fp16 norm of each input row (32 coordinates per thread, fp64 sums, exact
+//      fallback as in encode_kernel);
+//   3. y = x Pi^T with v_mfma_f32_16x16x16bf16_1k: hi*hi + hi*lo (+ lo*hi when the input is
+//      not bf16), fp32 accumulation -- y within about 2^-16 of the exact product;
+//   4. indices, residual and its exact fp16 norm, 32 coordinates per thread, index words
+//      assembled in registers;
+//   5. z = r S^T by the same split MFMA.  Its error is below 2^-13 ||S_j|| ||r||, so z decides
+//      the sign bit outside that band; inside it a wavefront computes the fp64 dot product
+//      and, if that is still undecided, the exact expansion -- the bit is always the sign of
+//      the exact real dot product, as in encode_kernel.
+
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_bits_f(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
+  const uint32_t h = bf16_rne_bits(x);
+  hi = (uint16_t)h;
+  lo = (uint16_t)bf16_rne_bits(__fsub_rn(x, bf16_bits_f(h)));
+}
+
+// B fragment of a 16x16x16 MFMA for rows n (output) and k-step ks of a row-major [rows][D]
+// fp32 matrix W, B[k][n] = W[n][k]: lane l holds W[n0 + l%16][16 ks + 4 (l/16) + 0..3].
+template <int D>
+__device__ __forceinline__ void load_bfrag(const float *W, int n0, int ks, bf16x4 &hi, bf16x4 &lo) {
+  const int l = lane_id();
+  const float4 w = *reinterpret_cast<const float4 *>(W + (int64_t)(n0 + (l & 15)) * D + 16 * ks + 4 * (l >> 4));
+  const float wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint16_t h, o;
+    split_bf16(wv[j], h, o);
+    hi[j] = (short)h;
+    lo[j] = (short)o;
+  }
+}
+
+template <int TPV>
+__device__ __forceinline__ double group_sum(double v) {
+  if constexpr (TPV >= 2) v += __shfl_xor(v, 1, kWave);
+  if constexpr (TPV >= 4) v += __shfl_xor(v, 2, kWave);
+  return v;
+}
+
+// fp16 candidate for sqrt(s) and whether the fp64 sum s (error <= (D+2) u s) decides it.
+template <int D>
+__device__ __forceinline__ uint32_t f16_norm_candidate(double s, bool &ok) {
+  const double slack = 4.0 * (D + 2) * 0x1p-53;
+  const uint32_t h = f64_to_f16_rne(sqrt(s));
+  ok = h < 0x7C00u;
+  if (ok) {
+    const double vh = f16_bits_to_double_ext(h);
+    const double up = 0.5 * (vh + f16_bits_to_double_ext(h + 1));
+    if (!(s < up * up * (1.0 - slack))) ok = false;
+    if (h > 0) {
+      const double dn = 0.5 * (vh + f16_bits_to_double_ext(h - 1));
+      if (!(s > dn * dn * (1.0 + slack))) ok = false;
+    }
+  }
+  return h;
+}
+
+template <int D, int BITS, int M, int TIN, bool PRE, int NTH>
+__global__ __launch_bounds__(NTH) void encode_mfma(EncArgs a) {
+  constexpr int NW = NTH / kWave;  // wavefronts; each owns NCT / NW column tiles of y and z
+  constexpr int T = NTH * 32 / D;  // vectors per tile (128)
+  constexpr int TPV = D / 32;      // scalar threads per vector, 32 coordinates each
+  constexpr int NRT = T / 16;
+  constexpr int NCT = D / 16;
+  constexpr int WCT = NCT / NW;
+  constexpr int NKS = D / 16;
+  constexpr int MCT = M / 16;
+  constexpr int WMCT = M > 0 ? MCT / NW : 1;
+  constexpr bool XLO = !PRE && TIN != TQ_BF16;  // input needs a lo part in bf16
+  constexpr int L = 1 << BITS;
+  constexpr int LDA = D + 8;
+  constexpr int LDF = D + 1;
+  constexpr int C = D / kWave;
+  static_assert(NCT % NW == 0 && WCT >= 1 && (M == 0 || M == D), "supported shapes");
+
+  __shared__ __align__(16) uint16_t ah[T * LDA];
+  __shared__ __align__(16) uint16_t al[T * LDA];
+  __shared__ float fv[T * LDF];
+  __shared__ uint32_t nws[T];
+  __shared__ float rn2[T];
+  __shared__ uint32_t flag[T];
+  __shared__ uint16_t sbits[T * (M > 0 ? MCT : 1)];
+  __shared__ double xterms[NW][D + 2];
+  __shared__ double xbuf[NW][D + 2];
+  __shared__ float cbs[L], ths[L];
+
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  if (tid < L) cbs[tid] = a.centroids[tid];
+  if (tid < L - 1) ths[tid] = a.thresholds[tid];
+
+  bf16x4 ph[WCT][NKS], pl[WCT][NKS];
+  bf16x4 sh[WMCT][NKS], sl[WMCT][NKS];
+  float snorm[WMCT];
+  if constexpr (!PRE) {
+#pragma unroll
+    for (int ct = 0; ct < WCT; ++ct)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) load_bfrag<D>(a.rot, 16 * (wid * WCT + ct), ks, ph[ct][ks], pl[ct][ks]);
+  }
+  if constexpr (M > 0) {
+#pragma unroll
+    for (int mc = 0; mc < WMCT; ++mc) {
+      const int n0 = 16 * (wid * WMCT + mc);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) load_bfrag<D>(a.sketch, n0, ks, sh[mc][ks], sl[mc][ks]);
+      double q = 0.0;
+      for (int k = 0; k < D; ++k) {
+        const double v = a.sketch[(int64_t)(n0 + (lane & 15)) * D + k];
+        q += v * v;
+      }
+      snorm[mc] = (float)sqrt(q) * (1.0f + 0x1p-20f);
+    }
+  }
+  __syncthreads();
+  float thr_unused = ths[0];
+  (void)thr_unused;
+
+  const int vr = tid / TPV, ch = tid % TPV;
+  const int iw_all = (int)(a.idx_stride >> 2);
+  const int sw_all = M > 0 ? (int)(a.sign_stride >> 2) : 0;
+  uint32_t *idxw = reinterpret_cast<uint32_t *>(a.idx);
+  uint32_t *sgnw = reinterpret_cast<uint32_t *>(a.sign);
+
+  // The tile is read as 16-byte chunks (8 bf16/fp16 or 4 fp32 elements of one row); the next
+  // tile's chunks are loaded into registers while the current tile is processed.
+  constexpr int EB = (TIN == TQ_F32) ? 4 : 2;
+  constexpr int EPC = 16 / EB;               // elements per chunk
+  constexpr int NCH = T * D / EPC / NTH;     // chunks per thread
+  static_assert(D % EPC == 0 && (T * D / EPC) % NTH == 0, "tile chunking");
+  uint4 pre[NCH];
+  auto load_tile = [&](int64_t t0v) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int e = (tid + i * NTH) * EPC;
+      const int64_t v = t0v + e / D;
+      pre[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (v < a.n)
+        pre[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(a.x) + (v * a.ld_x + e % D) * EB);
+    }
+  };
+  load_tile((int64_t)blockIdx.x * T);
+  for (int64_t tile = blockIdx.x; tile * T < a.n; tile += gridDim.x) {
+    const int64_t v0 = tile * T;
+    // ---- 1. the prefetched tile to LDS (fp32 values and the bf16 hi/lo split)
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int e = (tid + i * NTH) * EPC;
+      const int r = e / D, c0 = e % D;
+      const uint32_t w[4] = {pre[i].x, pre[i].y, pre[i].z, pre[i].w};
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) {
+        float x;
+        if constexpr (TIN == TQ_F32) x = __uint_as_float(w[u]);
+        else if constexpr (TIN == TQ_F16) x = __half2float(__ushort_as_half((unsigned short)(w[u >> 1] >> (16 * (u & 1)))));
+        else x = bf16_bits_to_float((uint16_t)(w[u >> 1] >> (16 * (u & 1))));
+        const int c = c0 + u;
+        fv[r * LDF + c] = x;
+        if constexpr (!PRE) {
+          uint16_t hi, lo;
+          split_bf16(x, hi, lo);
+          ah[r * LDA + c] = hi;
+          if constexpr (XLO) al[r * LDA + c] = lo;
+        } else {
+          if (a.y_tap && v0 + r < a.n) a.y_tap[(v0 + r) * D + c] = x;
+        }
+      }
+    }
+    load_tile((tile + gridDim.x) * T);
+    __syncthreads();
+    // ---- 2. exact fp16 norm of the input rows
+    {
+      double s = 0.0;
+#pragma unroll 8
+      for (int k = 0; k < 32; ++k) {
+        const double x = fv[vr * LDF + ch * 32 + k];
+        s += x * x;
+      }
+      s = group_sum<TPV>(s);
+      bool ok;
+      const uint32_t h = f16_norm_candidate<D>(s, ok);
+      if (ch == 0) {
+        nws[vr] = h;
+        flag[vr] = ok ? 0u : 1u;
+      }
+    }
+    __syncthreads();
+    for (int r = wid; r < T; r += NW) {
+      if (flag[r]) {
+        float xv[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) xv[c] = fv[r * LDF + lane + kWave * c];
+        const uint32_t h = wave_norm_f16<D, C>(xv, xterms[wid], xbuf[wid]);
+        if (lane == 0) nws[r] = h;
+      }
+    }
+    __syncthreads();
+    // ---- 3. y = x Pi^T
+    if constexpr (!PRE) {
+      f32x4 acc[NRT][WCT];
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < WCT; ++ct) acc[rt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      // k-step outermost, row tiles innermost: consecutive MFMAs update independent tiles
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int ct = 0; ct < WCT; ++ct) {
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt) {
+            const bf16x4 xh = *reinterpret_cast<const bf16x4 *>(&ah[(16 * rt + (lane & 15)) * LDA + 16 * ks + 4 * (lane >> 4)]);
+            acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, ph[ct][ks], acc[rt][ct], 0, 0, 0);
+          }
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt) {
+            const bf16x4 xh = *reinterpret_cast<const bf16x4 *>(&ah[(16 * rt + (lane & 15)) * LDA + 16 * ks + 4 * (lane >> 4)]);
+            acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, pl[ct][ks], acc[rt][ct], 0, 0, 0);
+          }
+          if constexpr (XLO) {
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+              const bf16x4 xl = *reinterpret_cast<const bf16x4 *>(&al[(16 * rt + (lane & 15)) * LDA + 16 * ks + 4 * (lane >> 4)]);
+              acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xl, ph[ct][ks], acc[rt][ct], 0, 0, 0);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < WCT; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rt + 4 * (lane >> 4) + i;
+            const int col = 16 * (wid * WCT + ct) + (lane & 15);
+            fv[row * LDF + col] = acc[rt][ct][i];
+            if (a.y_tap && v0 + row < a.n) a.y_tap[(v0 + row) * D + col] = acc[rt][ct][i];
+          }
+      __syncthreads();
+    }
+    // ---- 4. indices and residual, 32 coordinates per thread
+    {
+      const uint32_t n16 = nws[vr];
+      const float nbar = f16_bits_to_float(n16);
+      float thr[L - 1];
+#pragma unroll
+      for (int j = 0; j < L - 1; ++j) thr[j] = __fmul_rn(nbar, ths[j]);
+      uint64_t w0 = 0, w1 = 0;  // the thread's 32 * BITS index bits (at most 128)
+      double s2 = 0.0;
+#pragma unroll 4
+      for (int k = 0; k < 32; ++k) {
+        const int col = ch * 32 + k;
+        const float y = fv[vr * LDF + col];
+        uint32_t q = 0;
+#pragma unroll
+        for (int j = 0; j < L - 1; ++j) q += (y >= thr[j]) ? 1u : 0u;
+        const float r = __fsub_rn(y, __fmul_rn(nbar, cbs[q]));
+        fv[vr * LDF + col] = r;
+        if constexpr (M > 0) {
+          uint16_t hi, lo;
+          split_bf16(r, hi, lo);
+          ah[vr * LDA + col] = hi;
+          al[vr * LDA + col] = lo;
+        }
+        s2 += (double)r * (double)r;
+        const int b = BITS * k;
+        if (b < 64) {
+          w0 |= (uint64_t)q << b;
+          if (b + BITS > 64) w1 |= (uint64_t)q >> (64 - b);
+        } else {
+          w1 |= (uint64_t)q << (b - 64);
+        }
+      }
+      const int64_t v = v0 + vr;
+      if (v < a.n) {
+        const uint32_t wds[4] = {(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)};
+#pragma unroll
+        for (int w = 0; w < BITS; ++w) idxw[v * iw_all + ch * BITS + w] = wds[w];
+        if (ch == 0)
+          for (int w = D * BITS / 32; w < iw_all; ++w) idxw[v * iw_all + w] = 0u;
+      }
+      s2 = group_sum<TPV>(s2);
+      bool ok;
+      const uint32_t h = f16_norm_candidate<D>(s2, ok);
+      if (ch == 0) {
+        nws[vr] = n16 | (h << 16);
+        flag[vr] = ok ? 0u : 1u;
+        rn2[vr] = (float)s2;
+      }
+    }
+    __syncthreads();
+    for (int r = wid; r < T; r += NW) {
+      if (flag[r]) {
+        float xv[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) xv[c] = fv[r * LDF + lane + kWave * c];
+        const uint32_t h = wave_norm_f16<D, C>(xv, xterms[wid], xbuf[wid]);
+        if (lane == 0) nws[r] = (nws[r] & 0xFFFFu) | (h << 16);
+      }
+    }
+    __syncthreads();
+    // ---- 5. sign bits of z = r S^T
+    if constexpr (M > 0) {
+      f32x4 acc[NRT][WMCT];
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int mc = 0; mc < WMCT; ++mc) acc[rt][mc] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int mc = 0; mc < WMCT; ++mc) {
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt) {
+            const bf16x4 rh = *reinterpret_cast<const bf16x4 *>(&ah[(16 * rt + (lane & 15)) * LDA + 16 * ks + 4 * (lane >> 4)]);
+            acc[rt][mc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(rh, sh[mc][ks], acc[rt][mc], 0, 0, 0);
+          }
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt) {
+            const bf16x4 rl = *reinterpret_cast<const bf16x4 *>(&al[(16 * rt + (lane & 15)) * LDA + 16 * ks + 4 * (lane >> 4)]);
+            acc[rt][mc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(rl, sh[mc][ks], acc[rt][mc], 0, 0, 0);
+          }
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt) {
+            const bf16x4 rh = *reinterpret_cast<const bf16x4 *>(&ah[(16 * rt + (lane & 15)) * LDA + 16 * ks + 4 * (lane >> 4)]);
+            acc[rt][mc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(rh, sl[mc][ks], acc[rt][mc], 0, 0, 0);
+          }
+        }
+      }
+      static_assert(NRT * WMCT * 4 <= 32, "one bit per accumulator element in a 32-bit mask");
+      // pass 1: sign and "undecided" flag of every accumulator element, as per-lane bit masks
+      uint32_t bitm = 0u, ambm = 0u;
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int mc = 0; mc < WMCT; ++mc)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = (rt * WMCT + mc) * 4 + i;
+            const int row = 16 * rt + 4 * (lane >> 4) + i;
+            const float z = acc[rt][mc][i];
+            const float r2 = rn2[row];
+            const float tau = r2 < 1e-30f ? INFINITY : 0x1p-13f * snorm[mc] * sqrtf(r2);
+            bitm |= (z >= 0.0f ? 1u : 0u) << e;
+            ambm |= (fabsf(z) <= tau ? 1u : 0u) << e;
+          }
+      // pass 2: undecided elements, one at a time for the whole wavefront: fp64 dot product
+      // with its error bound, then the exact expansion if the bound still does not decide
+      uint64_t pend = __ballot(ambm != 0u);
+      while (pend) {
+        const int src = __ffsll((unsigned long long)pend) - 1;
+        const uint32_t sm = (uint32_t)__shfl((int)ambm, src, kWave);
+        const int e = __ffs(sm) - 1;
+        const int i = e & 3, mc = (e >> 2) % WMCT, rt = (e >> 2) / WMCT;
+        const int srow = 16 * rt + 4 * (src >> 4) + i;
+        const int j = 16 * (wid * WMCT + mc) + (src & 15);
+        double ps = 0.0, pa = 0.0;
+        for (int k = lane; k < D; k += kWave) {
+          const double p = (double)a.sketch[(int64_t)j * D + k] * (double)fv[srow * LDF + k];
+          ps += p;
+          pa += fabs(p);
+        }
+        ps = wave_sum(ps);
+        pa = wave_sum(pa);
+        int sg;
+        if (fabs(ps) > 2.0 * (D + 2) * 0x1p-53 * pa) {
+          sg = ps > 0.0 ? 1 : -1;
+        } else {
+          for (int k = lane; k < D; k += kWave)
+            xterms[wid][k] = (double)a.sketch[(int64_t)j * D + k] * (double)fv[srow * LDF + k];
+          wave_lds_fence();
+          sg = 0;
+          if (lane == 0) sg = expansion_sign(xterms[wid], D, xbuf[wid]);
+          wave_lds_fence();
+          sg = __shfl(sg, 0, kWave);
+        }
+        if (lane == src) {
+          bitm = (bitm & ~(1u << e)) | ((sg >= 0 ? 1u : 0u) << e);
+          ambm &= ~(1u << e);
+        }
+        pend = __ballot(ambm != 0u);
+      }
+      // pass 3: 16-bit chunks of sketch rows per vector
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int mc = 0; mc < WMCT; ++mc)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = (rt * WMCT + mc) * 4 + i;
+            const uint64_t bm = __ballot((bitm >> e) & 1u);
+            if (lane < 4) {
+              const int rowg = 16 * rt + 4 * lane + i;
+              sbits[rowg * MCT + wid * WMCT + mc] = (uint16_t)((bm >> (16 * lane)) & 0xFFFFu);
+            }
+          }
+      __syncthreads();
+      for (int e = tid; e < T * sw_all; e += NTH) {
+        const int r = e / sw_all, w = e % sw_all;
+        const int64_t v = v0 + r;
+        if (v < a.n) {
+          uint32_t word = 0u;
+          if (2 * w < MCT) word = sbits[r * MCT + 2 * w];
+          if (2 * w + 1 < MCT) word |= (uint32_t)sbits[r * MCT + 2 * w + 1] << 16;
+          sgnw[v * sw_all + w] = word;
+        }
+      }
+    }
+    for (int r = tid; r < T; r += NTH)
+      if (v0 + r < a.n) a.norms[v0 + r] = nws[r];
+    __syncthreads();
+  }
+}
+
+template <int D, int BITS, int M, int TIN, bool PRE>
+static void launch_mfma(const EncArgs &a, hipStream_t st) {
+  constexpr int NTH = D == 128 ? 512 : 256;  // tiles of 128 vectors; 16 columns of y per wavefront
+  constexpr int T = NTH * 32 / D;
+  int64_t tiles = (a.n + T - 1) / T;
+  if (tiles > 256 * 2) tiles = 256 * 2;
+  hipLaunchKernelGGL((encode_mfma<D, BITS, M, TIN, PRE, NTH>), dim3((unsigned)tiles), dim3(NTH), 0, st, a);
+}
+
 template <int D, int BITS, int M>
 static int launch_enc_dm(const EncArgs &a, int dt, bool pre, hipStream_t st) {
-  const int64_t waves = (a.n + 0) ;
-  int64_t blocks = (waves + kEncWaves - 1) / kEncWaves;
+  if constexpr (D == 64 || D == 128) {
+    const int eb = dt == TQ_F32 ? 4 : 2;
+    const bool vec_ok = ((uintptr_t)a.x % 16 == 0) && ((a.ld_x * eb) % 16 == 0);
+    if ((a.n_rot == 1 || a.vecs_per_rot == 0) && vec_ok) {
+      if (pre) {
+        if (dt != TQ_F32) return TQ_EINVAL;
+        launch_mfma<D, BITS, M, TQ_F32, true>(a, st);
+      } else if (dt == TQ_F32) {
+        launch_mfma<D, BITS, M, TQ_F32, false>(a, st);
+      } else if (dt == TQ_F16) {
+        launch_mfma<D, BITS, M, TQ_F16, false>(a, st);
+      } else if (dt == TQ_BF16) {
+        launch_mfma<D, BITS, M, TQ_BF16, false>(a, st);
+      } else {
+        return TQ_EINVAL;
+      }
+      return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+    }
+  }
+  int64_t blocks = (a.n + kEncWaves - 1) / kEncWaves;
   if (blocks > 256 * 64) blocks = 256 * 64;
   if (blocks < 1) blocks = 1;
   dim3 grid((unsigned)blocks), block(kWave * kEncWaves);
