@@ -22,6 +22,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+SCORE_SOURCES = ("tq_scores.hip", "tq_lut.h", "tq_device.h", "tq_internal.h")
+SCORE_KERNELS = ("tq::qprep_tiled<128, 128>", "tq::score_kernel<128, 2, 128, 4, 1024>")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_kernel_gqa8b_decode_b8_32k_traffic.txt")
 METRIC = "compressed-KV decode scoring GB/s (% HBM peak) + keys/s; encode vectors/s"
 
 
@@ -41,6 +44,36 @@ def parse():
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for hardware byte counters)")
     return ap.parse_args()
+
+
+def score_source_hash():
+    """sha256 over the sources the score stream is compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in SCORE_SOURCES:
+        with open(os.path.join(ROOT, "vector_quantization_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel_names):
+    """HBM bytes per tq_scores call from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE scaled by the copy calibration), or None when the kernels have changed since
+    the counters were taken."""
+    try:
+        lines = open(TRAFFIC_PROFILE).read().splitlines()
+    except OSError:
+        return None
+    vals, src = {}, None
+    for ln in lines:
+        if ln.startswith("source_sha256:"):
+            src = ln.split(":", 1)[1].strip()
+        elif ln.startswith("traffic_bytes_per_launch["):
+            k, v = ln[len("traffic_bytes_per_launch["):].split("]:", 1)
+            vals[k] = float(v)
+    if src != score_source_hash() or not all(k in vals for k in kernel_names):
+        return None
+    return sum(vals[k] for k in kernel_names)
 
 
 def cpu_baseline(w, K, q, seed_rot, seed_sk):
@@ -198,8 +231,9 @@ def main():
         "encode_vectors_per_s": round(2 * n_vec / ((t_enc_k + t_enc_v) * 1e-3)),
         "encode_GBps": round((2 * enc_in + enc_out_k + enc_out_v) / ((t_enc_k + t_enc_v) * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "score_kernel (+ its qprep launch inside the timed call)"},
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(SCORE_KERNELS) if a.workload == "gqa" else None,
+                     "kernel": " + ".join(SCORE_KERNELS) + " (one tq_scores call)"},
         "gpu": torch.cuda.get_device_name(0),
     }
     if a.calibrate:
