@@ -52,7 +52,8 @@ typedef enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
  *               per-head basis: TurboESM summary, section 2.B, one rotation per layer/head).
  *   sketch      [m][d] fp32 row-major Gaussian S (NULL when m == 0: stage 1 only).
  *   centroids   [2^bits] fp32 ascending Lloyd-Max levels of the unit-direction coordinate.
- *   thresholds  [2^bits - 1] fp32 midpoints between adjacent centroids.
+ *   thresholds  [2^bits - 1] fp32 midpoints between adjacent centroids, ascending (the
+ *               encoder finds #{j : y >= nbar t_j} by binary descent, which relies on it).
  *   vecs_per_rot  vector v of a cache uses rot[min(v / vecs_per_rot, n_rot - 1)]; 0 or
  *               n_rot == 1 means rot[0] for all.                                           */
 typedef struct {

@@ -263,57 +263,48 @@ __global__ __launch_bounds__(kWave *kEncWaves) void encode_kernel(EncArgs a) {
 
 // ------------------------------------------------------------------ MFMA encode (d = 64, 128)
 //
-// Persistent workgroups of NTH threads.  Each wavefront keeps, in registers, the bf16 hi/lo
-// split of its column slice of Pi^T and of S^T as MFMA B operands (loaded once).  Per tile
-// of T vectors (T * d = 8192 elements):
-//   1. the inputs go to LDS as fp32 (exact) and as a bf16 hi/lo split (A operand);
-//   2. the exact fp16 norm of each input row (32 coordinates per thread, fp64 sums, exact
-//      fallback as in encode_kernel);
-//   3. y = x Pi^T with v_mfma_f32_16x16x16bf16_1k: hi*hi + hi*lo (+ lo*hi when the input is
-//      not bf16), fp32 accumulation -- y within about 2^-16 of the exact product;
-//   4. indices, residual and its exact fp16 norm, 32 coordinates per thread, index words
-//      assembled in registers;
-//   5. z = r S^T by the same split MFMA.  Its error is below 2^-13 ||S_j|| ||r||, so z decides
-//      the sign bit outside that band; inside it a wavefront computes the fp64 dot product
-//      and, if that is still undecided, the exact expansion -- the bit is always the sign of
-//      the exact real dot product, as in encode_kernel.
+// Persistent workgroups of NW wavefronts; every wavefront runs its own passes of 32 vectors
+// (two 16-vector tiles) with no workgroup barrier after set-up.  At set-up the workgroup
+// splits Pi and S into bf16 hi + lo parts and stores them in LDS as MFMA A fragments of
+// v_mfma_f32_16x16x32_bf16 (lane l holds A[l%16][8(l/16) + 0..7]).  The input is the B
+// operand (lane l holds B[8(l/16) + j][l%16] = x[vector l%16][32 ks + 8(l/16) + j]), read from
+// HBM straight into registers as one 16-byte chunk per lane and k-step.
+//
+// The rows of Pi and S are stored permuted: row m of 16-row tile t is output coordinate
+// tile_coord(t, m).  The MFMA result D[4(l/16) + i][l%16] of the tile pair (2u, 2u+1) then
+// gives lane l the 8 consecutive coordinates 32u + 8(l/16) + 0..7 of vector l%16 -- the same
+// coordinates the lane holds of the input, and exactly the B operand of the next product.
+// So per vector, four lanes (l%16 fixed) each own 32 coordinates through the whole pass:
+//   1. exact fp16 norm of the input: fp64 sum over the lane's values, reduced over the four
+//      lanes; where the fp64 bound cannot decide, Shewchuk's expansion (one lane);
+//   2. y = Pi x: hi*x + lo*x (+ hi*x_lo when the input is not bf16), fp32 accumulation;
+//   3. indices and residual on the lane's own coordinates; the index fields of the four
+//      lanes are OR-combined by lane shuffles into whole words;
+//   4. exact fp16 norm of the residual, as in 1;
+//   5. z = S r by the same split MFMA (S_hi r_hi + S_hi r_lo + S_lo r_hi).  Its error is below
+//      2^-13 ||S_j|| ||r|| (bf16 split error 3 * 2^-16 plus 3d fp32 additions); outside that
+//      band the sign of z is the sign of the exact dot product; inside it the wavefront
+//      computes the fp64 dot product with its error bound and, if still undecided, the exact
+//      expansion.  Each lane's 8 sketch rows form one byte of the sign stream.
 
-typedef short bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ float bf16_bits_f(uint32_t b) { return __uint_as_float(b << 16); }
-
-__device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
-  const uint32_t h = bf16_rne_bits(x);
-  hi = (uint16_t)h;
-  lo = (uint16_t)bf16_rne_bits(__fsub_rn(x, bf16_bits_f(h)));
+// Output coordinate of row m of 16-row tile t (see above).
+__device__ __forceinline__ int tile_coord(int t, int m) {
+  return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
 }
 
-// B fragment of a 16x16x16 MFMA for rows n (output) and k-step ks of a row-major [rows][D]
-// fp32 matrix W, B[k][n] = W[n][k]: lane l holds W[n0 + l%16][16 ks + 4 (l/16) + 0..3].
-template <int D>
-__device__ __forceinline__ void load_bfrag(const float *W, int n0, int ks, bf16x4 &hi, bf16x4 &lo) {
-  const int l = lane_id();
-  const float4 w = *reinterpret_cast<const float4 *>(W + (int64_t)(n0 + (l & 15)) * D + 16 * ks + 4 * (l >> 4));
-  const float wv[4] = {w.x, w.y, w.z, w.w};
+// bf16 hi/lo split of 8 floats: hi = RNE(x), lo = RNE(x - hi); x - hi is exact in fp32.
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint16_t h, o;
-    split_bf16(wv[j], h, o);
-    hi[j] = (short)h;
-    lo[j] = (short)o;
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 h = (__bf16)x[j];
+    hi[j] = h;
+    lo[j] = (__bf16)__fsub_rn(x[j], (float)h);
   }
-}
-
-template <int TPV>
-__device__ __forceinline__ double group_sum(double v) {
-  if constexpr (TPV >= 2) v += __shfl_xor(v, 1, kWave);
-  if constexpr (TPV >= 4) v += __shfl_xor(v, 2, kWave);
-  return v;
 }
 
 // fp16 candidate for sqrt(s) and whether the fp64 sum s (error <= (D+2) u s) decides it.
@@ -334,370 +325,588 @@ __device__ __forceinline__ uint32_t f16_norm_candidate(double s, bool &ok) {
   return h;
 }
 
-template <int D, int BITS, int M, int TIN, bool PRE, int NTH>
-__global__ __launch_bounds__(NTH) void encode_mfma(EncArgs a) {
-  constexpr int NW = NTH / kWave;  // wavefronts; each owns NCT / NW column tiles of y and z
-  constexpr int T = NTH * 32 / D;  // vectors per tile (128)
-  constexpr int TPV = D / 32;      // scalar threads per vector, 32 coordinates each
-  constexpr int NRT = T / 16;
-  constexpr int NCT = D / 16;
-  constexpr int WCT = NCT / NW;
-  constexpr int NKS = D / 16;
-  constexpr int MCT = M / 16;
-  constexpr int WMCT = M > 0 ? MCT / NW : 1;
-  constexpr bool XLO = !PRE && TIN != TQ_BF16;  // input needs a lo part in bf16
-  constexpr int L = 1 << BITS;
-  constexpr int LDA = D + 8;
-  constexpr int LDF = D + 1;
-  constexpr int C = D / kWave;
-  static_assert(NCT % NW == 0 && WCT >= 1 && (M == 0 || M == D), "supported shapes");
-
-  __shared__ __align__(16) uint16_t ah[T * LDA];
-  __shared__ __align__(16) uint16_t al[T * LDA];
-  __shared__ float fv[T * LDF];
-  __shared__ uint32_t nws[T];
-  __shared__ float rn2[T];
-  __shared__ uint32_t flag[T];
-  __shared__ uint16_t sbits[T * (M > 0 ? MCT : 1)];
-  __shared__ double xterms[NW][D + 2];
-  __shared__ double xbuf[NW][D + 2];
-  __shared__ float cbs[L], ths[L];
-
-  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
-  if (tid < L) cbs[tid] = a.centroids[tid];
-  if (tid < L - 1) ths[tid] = a.thresholds[tid];
-
-  bf16x4 ph[WCT][NKS], pl[WCT][NKS];
-  bf16x4 sh[WMCT][NKS], sl[WMCT][NKS];
-  float snorm[WMCT];
-  if constexpr (!PRE) {
-#pragma unroll
-    for (int ct = 0; ct < WCT; ++ct)
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) load_bfrag<D>(a.rot, 16 * (wid * WCT + ct), ks, ph[ct][ks], pl[ct][ks]);
+// fp16 candidate for sqrt(s) where s is within relative 8 * 2^-24 of the exact sum of squares
+// (fp32 partial sums of at most 8 terms, combined in fp64), and whether s decides it.  The
+// squared fp16 midpoints are exact in fp32.  Below 2^-60 the exact norm is under 2^-29.9
+// (even if fp32 underflow was flushed), which rounds to 0.
+__device__ __forceinline__ uint32_t f16_norm_fast(double s, bool &ok) {
+  const float sf = (float)s;
+  if (sf < 0x1p-60f) {
+    ok = true;
+    return 0u;
   }
-  if constexpr (M > 0) {
+  const uint32_t h = (uint32_t)__half_as_ushort(__float2half_rn(__builtin_amdgcn_sqrtf(sf)));
+  const float v = __half2float(__ushort_as_half((unsigned short)h));
+  const float vu = h >= 0x7BFFu ? 65536.0f : __half2float(__ushort_as_half((unsigned short)(h + 1)));
+  const float vd = h == 0u ? 0.0f : __half2float(__ushort_as_half((unsigned short)(h - 1)));
+  const float mu = 0.5f * (v + vu), md = 0.5f * (v + vd);
+  const double e = 20.0 * 0x1p-24;  // 2.5 times the partial sums' error bound
+  ok = sf <= 0x1p32f && h < 0x7C00u && s < (double)(mu * mu) * (1.0 - e) &&
+       (h == 0u || s > (double)(md * md) * (1.0 + e));
+  return h;
+}
+
+// idx = #{ j : y >= thr[j] } for ascending thr, by binary descent: bit b of idx compares y
+// with the threshold that splits what the higher bits left; the candidates of each level are
+// selected from registers as soon as the bit above is known.
+template <int BITS>
+__device__ __forceinline__ uint32_t quantize_index(float y, const float (&t)[(1 << BITS) - 1]) {
+  static_assert(BITS >= 2 && BITS <= 4, "index widths");
+  if constexpr (BITS == 2) {
+    const bool b1 = y >= t[1];
+    const bool b0 = y >= (b1 ? t[2] : t[0]);
+    return (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+  } else if constexpr (BITS == 3) {
+    const bool b2 = y >= t[3];
+    const float c1 = b2 ? t[5] : t[1];
+    const float ca = b2 ? t[6] : t[2];
+    const float cb = b2 ? t[4] : t[0];
+    const bool b1 = y >= c1;
+    const bool b0 = y >= (b1 ? ca : cb);
+    return (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+  } else {
+    const bool b3 = y >= t[7];
+    const float c2 = b3 ? t[11] : t[3];
+    const float p1a = b3 ? t[13] : t[5], p1b = b3 ? t[9] : t[1];
+    const float p11 = b3 ? t[14] : t[6], p10 = b3 ? t[12] : t[4];
+    const float p01 = b3 ? t[10] : t[2], p00 = b3 ? t[8] : t[0];
+    const bool b2 = y >= c2;
+    const float c1 = b2 ? p1a : p1b;
+    const float q1 = b2 ? p11 : p01, q0 = b2 ? p10 : p00;
+    const bool b1 = y >= c1;
+    const bool b0 = y >= (b1 ? q1 : q0);
+    return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+  }
+}
+
+// Exact fp16 RNE of sqrt(sum of terms[0..cnt)), starting from candidate h: compares the exact
+// sum with squared fp16 midpoints (each exact in fp64).  terms needs cnt + 1 entries, buf
+// cnt + 1.  Run by one lane.
+__device__ uint32_t f16_norm_exact(double *terms, int cnt, uint32_t h, double *buf) {
+  uint32_t hh = h >= 0x7C00u ? 0x7BFFu : h;
+  while (hh < 0x7C00u) {
+    const double mu = 0.5 * (f16_bits_to_double_ext(hh) + f16_bits_to_double_ext(hh + 1));
+    terms[cnt] = -(mu * mu);
+    const int cmp = expansion_sign(terms, cnt + 1, buf);
+    if (cmp > 0 || (cmp == 0 && ((hh + 1) & 1u) == 0)) ++hh;
+    else break;
+  }
+  while (hh > 0) {
+    const double mu = 0.5 * (f16_bits_to_double_ext(hh - 1) + f16_bits_to_double_ext(hh));
+    terms[cnt] = -(mu * mu);
+    const int cmp = expansion_sign(terms, cnt + 1, buf);
+    if (cmp < 0 || (cmp == 0 && ((hh - 1) & 1u) == 0)) --hh;
+    else break;
+  }
+  return hh;
+}
+
+// Store the A fragments of the row-permuted, bf16-split matrix W [rows][D] (fp32, row-major):
+// frag[((t * KS + ks) * 2 + hl) * 64 + lane] = 8 bf16 of part hl (0 = hi, 1 = lo) of
+// W[tile_coord(t, lane % 16)][32 ks + 8 (lane / 16) + 0..7].
+template <int D>
+__device__ void build_afrags(const float *W, int rows, uint4 *frag, int nthreads) {
+  constexpr int KS = D / 32;
+  for (int e = threadIdx.x; e < (rows / 16) * KS * 64; e += nthreads) {
+    const int lane = e % 64, ks = (e / 64) % KS, t = e / (64 * KS);
+    const float *src = W + (int64_t)tile_coord(t, lane % 16) * D + 32 * ks + 8 * (lane / 16);
+    float v[8];
+    const float4 a = reinterpret_cast<const float4 *>(src)[0], b = reinterpret_cast<const float4 *>(src)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    bf16x8 hi, lo;
+    split8(v, hi, lo);
+    frag[((t * KS + ks) * 2 + 0) * 64 + lane] = __builtin_bit_cast(uint4, hi);
+    frag[((t * KS + ks) * 2 + 1) * 64 + lane] = __builtin_bit_cast(uint4, lo);
+  }
+}
+
+__device__ __forceinline__ bf16x8 afrag(const uint4 *frag, int t, int ks, int hl, int KS) {
+  return __builtin_bit_cast(bf16x8, frag[((t * KS + ks) * 2 + hl) * 64 + lane_id()]);
+}
+
+// The 8 input elements of a lane for one k-step, as floats.
+template <int TIN, int U4>
+__device__ __forceinline__ void raw_to_f32(const uint4 (&r)[U4], float (&x)[8]) {
+  if constexpr (U4 == 2) {
+    const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
 #pragma unroll
-    for (int mc = 0; mc < WMCT; ++mc) {
-      const int n0 = 16 * (wid * WMCT + mc);
+    for (int j = 0; j < 8; ++j) x[j] = __uint_as_float(w[j]);
+  } else {
+    const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) load_bfrag<D>(a.sketch, n0, ks, sh[mc][ks], sl[mc][ks]);
-      double q = 0.0;
-      for (int k = 0; k < D; ++k) {
-        const double v = a.sketch[(int64_t)(n0 + (lane & 15)) * D + k];
-        q += v * v;
-      }
-      snorm[mc] = (float)sqrt(q) * (1.0f + 0x1p-20f);
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t h = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      if constexpr (TIN == TQ_F16) x[j] = __half2float(__ushort_as_half((unsigned short)h));
+      else x[j] = bf16_bits_to_float((uint16_t)h);
     }
   }
-  __syncthreads();
-  float thr_unused = ths[0];
-  (void)thr_unused;
+}
 
-  const int vr = tid / TPV, ch = tid % TPV;
+template <int D, int BITS, int M, int TIN, bool PRE, int NW>
+__global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
+  constexpr int KS = D / 32;   // k-steps; also 8-coordinate groups u per lane
+  constexpr int CT = D / 16;   // 16-row tiles of y
+  constexpr int MT = M / 16;   // 16-row tiles of z
+  constexpr int NV = 2;        // 16-vector tiles per pass
+  constexpr int L = 1 << BITS;
+  constexpr bool XLO = !PRE && TIN != TQ_BF16;            // input needs a lo part
+  constexpr int U4 = (PRE || TIN == TQ_F32) ? 2 : 1;      // 16-byte chunks per 8 elements
+  constexpr int EB = (PRE || TIN == TQ_F32) ? 4 : 2;
+  constexpr int IWV = D * BITS / 32;                       // index words per vector
+  static_assert(D % 32 == 0 && (M == 0 || M == D), "supported shapes");
+
+  __shared__ uint4 fpi[PRE ? 1 : CT * KS * 2 * 64];
+  __shared__ uint4 fsk[M > 0 ? MT * KS * 2 * 64 : 1];
+  // per wavefront: the exact-fallback terms and buffer, also the staging of packed records
+  __shared__ __align__(16) double wscr[NW][2 * (D + 2)];
+  __shared__ float cbs[L];
+  __shared__ float smax_s;
+
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  const int n = lane & 15, g = lane >> 4;
+  double *xt = wscr[wid], *xb = wscr[wid] + (D + 2);
+  uint8_t *stg = reinterpret_cast<uint8_t *>(wscr[wid]);
+  constexpr int IB = D * BITS / 8;  // index bytes per vector
+  constexpr int SB = M / 8;         // sign bytes per vector
+  static_assert(NV * 16 * IB <= 2 * (D + 2) * 8 && NV * 16 * SB <= 2 * (D + 2) * 8, "staging fits");
+  if (tid < L) cbs[tid] = a.centroids[tid];
+  if constexpr (!PRE) build_afrags<D>(a.rot, D, fpi, NW * 64);
+  if constexpr (M > 0) {
+    build_afrags<D>(a.sketch, M, fsk, NW * 64);
+    if (wid == 0) {
+      float mx = 0.0f;
+      for (int q = lane; q < M; q += kWave) {
+        double ss = 0.0;
+        for (int k = 0; k < D; ++k) {
+          const double v = a.sketch[(int64_t)q * D + k];
+          ss += v * v;
+        }
+        mx = fmaxf(mx, (float)sqrt(ss));
+      }
+      mx = wave_max(mx);
+      if (lane == 0) smax_s = mx * (1.0f + 0x1p-20f);
+    }
+  }
+  float th[L - 1];
+#pragma unroll
+  for (int j = 0; j < L - 1; ++j) th[j] = a.thresholds[j];
+  __syncthreads();
+  const float smax = M > 0 ? smax_s : 0.0f;
+
   const int iw_all = (int)(a.idx_stride >> 2);
   const int sw_all = M > 0 ? (int)(a.sign_stride >> 2) : 0;
   uint32_t *idxw = reinterpret_cast<uint32_t *>(a.idx);
   uint32_t *sgnw = reinterpret_cast<uint32_t *>(a.sign);
+  const int64_t wstep = (int64_t)gridDim.x * NW * 16 * NV;
 
-  // The tile is read as 16-byte chunks (8 bf16/fp16 or 4 fp32 elements of one row); the next
-  // tile's chunks are loaded into registers while the current tile is processed.
-  constexpr int EB = (TIN == TQ_F32) ? 4 : 2;
-  constexpr int EPC = 16 / EB;               // elements per chunk
-  constexpr int NCH = T * D / EPC / NTH;     // chunks per thread
-  static_assert(D % EPC == 0 && (T * D / EPC) % NTH == 0, "tile chunking");
-  uint4 pre[NCH];
-  auto load_tile = [&](int64_t t0v) {
+  uint4 raw[NV][KS][U4];
+  auto load_pass = [&](int64_t v0) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int e = (tid + i * NTH) * EPC;
-      const int64_t v = t0v + e / D;
-      pre[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (v < a.n)
-        pre[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(a.x) + (v * a.ld_x + e % D) * EB);
+    for (int t = 0; t < NV; ++t) {
+      const int64_t v = v0 + 16 * t + n;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int w = 0; w < U4; ++w) {
+          raw[t][ks][w] = make_uint4(0u, 0u, 0u, 0u);
+          if (v < a.n)
+            raw[t][ks][w] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(a.x) +
+                                                             (v * a.ld_x + 32 * ks + 8 * g + 4 * w) * EB);
+        }
     }
   };
-  load_tile((int64_t)blockIdx.x * T);
-  for (int64_t tile = blockIdx.x; tile * T < a.n; tile += gridDim.x) {
-    const int64_t v0 = tile * T;
-    // ---- 1. the prefetched tile to LDS (fp32 values and the bf16 hi/lo split)
+
+  int64_t v0 = ((int64_t)blockIdx.x * NW + wid) * 16 * NV;
+  load_pass(v0);
+  for (; v0 < a.n; v0 += wstep) {
+    // ---- 1. exact fp16 norm of the input (of y in pre-rotated mode)
+    uint32_t n16[NV];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int e = (tid + i * NTH) * EPC;
-      const int r = e / D, c0 = e % D;
-      const uint32_t w[4] = {pre[i].x, pre[i].y, pre[i].z, pre[i].w};
-#pragma unroll
-      for (int u = 0; u < EPC; ++u) {
-        float x;
-        if constexpr (TIN == TQ_F32) x = __uint_as_float(w[u]);
-        else if constexpr (TIN == TQ_F16) x = __half2float(__ushort_as_half((unsigned short)(w[u >> 1] >> (16 * (u & 1)))));
-        else x = bf16_bits_to_float((uint16_t)(w[u >> 1] >> (16 * (u & 1))));
-        const int c = c0 + u;
-        fv[r * LDF + c] = x;
-        if constexpr (!PRE) {
-          uint16_t hi, lo;
-          split_bf16(x, hi, lo);
-          ah[r * LDA + c] = hi;
-          if constexpr (XLO) al[r * LDA + c] = lo;
-        } else {
-          if (a.y_tap && v0 + r < a.n) a.y_tap[(v0 + r) * D + c] = x;
-        }
-      }
-    }
-    load_tile((tile + gridDim.x) * T);
-    __syncthreads();
-    // ---- 2. exact fp16 norm of the input rows
-    {
+    for (int t = 0; t < NV; ++t) {
       double s = 0.0;
-#pragma unroll 8
-      for (int k = 0; k < 32; ++k) {
-        const double x = fv[vr * LDF + ch * 32 + k];
-        s += x * x;
-      }
-      s = group_sum<TPV>(s);
-      bool ok;
-      const uint32_t h = f16_norm_candidate<D>(s, ok);
-      if (ch == 0) {
-        nws[vr] = h;
-        flag[vr] = ok ? 0u : 1u;
-      }
-    }
-    __syncthreads();
-    for (int r = wid; r < T; r += NW) {
-      if (flag[r]) {
-        float xv[C];
 #pragma unroll
-        for (int c = 0; c < C; ++c) xv[c] = fv[r * LDF + lane + kWave * c];
-        const uint32_t h = wave_norm_f16<D, C>(xv, xterms[wid], xbuf[wid]);
-        if (lane == 0) nws[r] = h;
-      }
-    }
-    __syncthreads();
-    // ---- 3. y = x Pi^T
-    if constexpr (!PRE) {
-      f32x4 acc[NRT][WCT];
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < WCT; ++ct) acc[rt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      // k-step outermost, row tiles innermost: consecutive MFMAs update independent tiles
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int ct = 0; ct < WCT; ++ct) {
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) {
-            const bf16x4 xh = *reinterpret_cast<const bf16x4 *>(&ah[(16 * rt + (lane & 15)) * LDA + 16 * ks + 4 * (lane >> 4)]);
-            acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, ph[ct][ks], acc[rt][ct], 0, 0, 0);
-          }
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) {
-            const bf16x4 xh = *reinterpret_cast<const bf16x4 *>(&ah[(16 * rt + (lane & 15)) * LDA + 16 * ks + 4 * (lane >> 4)]);
-            acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, pl[ct][ks], acc[rt][ct], 0, 0, 0);
-          }
-          if constexpr (XLO) {
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-              const bf16x4 xl = *reinterpret_cast<const bf16x4 *>(&al[(16 * rt + (lane & 15)) * LDA + 16 * ks + 4 * (lane >> 4)]);
-              acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xl, ph[ct][ks], acc[rt][ct], 0, 0, 0);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < WCT; ++ct)
+      for (int ks = 0; ks < KS; ++ks) {
+        float p = 0.0f;  // 8 squares, at most 8 roundings
+        if constexpr (!PRE && TIN == TQ_BF16) {
+          const uint32_t w[4] = {raw[t][ks][0].x, raw[t][ks][0].y, raw[t][ks][0].z, raw[t][ks][0].w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int row = 16 * rt + 4 * (lane >> 4) + i;
-            const int col = 16 * (wid * WCT + ct) + (lane & 15);
-            fv[row * LDF + col] = acc[rt][ct][i];
-            if (a.y_tap && v0 + row < a.n) a.y_tap[(v0 + row) * D + col] = acc[rt][ct][i];
+            const bf16x2 v = __builtin_bit_cast(bf16x2, w[i]);
+            p = __builtin_amdgcn_fdot2_f32_bf16(v, v, p, false);
           }
-      __syncthreads();
+        } else if constexpr (!PRE && TIN == TQ_F16) {
+          const uint32_t w[4] = {raw[t][ks][0].x, raw[t][ks][0].y, raw[t][ks][0].z, raw[t][ks][0].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f16x2 v = __builtin_bit_cast(f16x2, w[i]);
+            p = __builtin_amdgcn_fdot2(v, v, p, false);
+          }
+        } else {
+          float x[8];
+          raw_to_f32<TQ_F32, U4>(raw[t][ks], x);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) p = fmaf(x[j], x[j], p);
+        }
+        s += (double)p;
+      }
+      s += __shfl_xor(s, 16, kWave);
+      s += __shfl_xor(s, 32, kWave);
+      bool ok;
+      n16[t] = f16_norm_fast(s, ok);
+      if (__ballot(!ok)) {
+        // fp64 sum (error <= (D+2) u s), then the exact expansion where even that cannot decide
+        double s4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          float x[8];
+          raw_to_f32<PRE ? TQ_F32 : TIN, U4>(raw[t][ks], x);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s4[j & 3] = fma((double)x[j], (double)x[j], s4[j & 3]);
+        }
+        double s64 = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        s64 += __shfl_xor(s64, 16, kWave);
+        s64 += __shfl_xor(s64, 32, kWave);
+        bool ok64;
+        const uint32_t h64 = f16_norm_candidate<D>(s64, ok64);
+        if (!ok) n16[t] = h64;
+        uint64_t bad = __ballot(!ok && !ok64 && g == 0);
+        while (bad) {
+          const int n0 = __ffsll((unsigned long long)bad) - 1;
+          if (n == n0) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              float x[8];
+              raw_to_f32<PRE ? TQ_F32 : TIN, U4>(raw[t][ks], x);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) xt[8 * KS * g + 8 * ks + j] = (double)x[j] * (double)x[j];
+            }
+          }
+          wave_lds_fence();
+          uint32_t h = 0;
+          if (lane == n0) h = f16_norm_exact(xt, D, n16[t], xb);
+          wave_lds_fence();
+          h = (uint32_t)__shfl((int)h, n0, kWave);
+          if (n == n0) n16[t] = h;
+          bad &= bad - 1;
+        }
+      }
     }
-    // ---- 4. indices and residual, 32 coordinates per thread
-    {
-      const uint32_t n16 = nws[vr];
-      const float nbar = f16_bits_to_float(n16);
+
+    // ---- 2. y = Pi x (coordinates 32u + 8g + j of vector 16t + n in yv[t][u][j])
+    float yv[NV][KS][8];
+    if constexpr (PRE) {
+#pragma unroll
+      for (int t = 0; t < NV; ++t)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) raw_to_f32<TQ_F32, U4>(raw[t][ks], yv[t][ks]);
+    } else {
+      bf16x8 xh[NV][KS], xl[XLO ? NV : 1][XLO ? KS : 1];
+#pragma unroll
+      for (int t = 0; t < NV; ++t)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if constexpr (TIN == TQ_BF16) {
+            xh[t][ks] = __builtin_bit_cast(bf16x8, raw[t][ks][0]);
+          } else {
+            float x[8];
+            raw_to_f32<TIN, U4>(raw[t][ks], x);
+            split8(x, xh[t][ks], xl[t][ks]);
+          }
+        }
+      f32x4 acc[NV][CT];
+#pragma unroll
+      for (int t = 0; t < NV; ++t)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[t][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      // the hi and lo parts in separate sweeps: consecutive MFMAs update different tiles
+#pragma unroll
+      for (int hl = 0; hl < (XLO ? 3 : 2); ++hl)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const bf16x8 af = afrag(fpi, ct, ks, hl == 1 ? 1 : 0, KS);
+#pragma unroll
+            for (int t = 0; t < NV; ++t) {
+              if constexpr (XLO) {
+                acc[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, hl == 2 ? xl[t][ks] : xh[t][ks], acc[t][ct], 0, 0, 0);
+              } else {
+                acc[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, xh[t][ks], acc[t][ct], 0, 0, 0);
+              }
+            }
+          }
+#pragma unroll
+      for (int t = 0; t < NV; ++t)
+#pragma unroll
+        for (int u = 0; u < KS; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) yv[t][u][j] = acc[t][2 * u + (j >> 2)][j & 3];
+    }
+    // the next pass's input is in flight while this one finishes (with a sketch, only once the
+    // z products are issued: its registers are free then)
+    if constexpr (M == 0) load_pass(v0 + wstep);
+    if (a.y_tap) {
+#pragma unroll
+      for (int t = 0; t < NV; ++t) {
+        const int64_t v = v0 + 16 * t + n;
+        if (v < a.n) {
+#pragma unroll
+          for (int u = 0; u < KS; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a.y_tap[v * D + 32 * u + 8 * g + j] = yv[t][u][j];
+        }
+      }
+    }
+
+    // ---- 3. indices and residual; 4. residual norm
+    uint32_t rn16[NV];
+    double rn2[NV];
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+      const float nbar = f16_bits_to_float(n16[t]);
       float thr[L - 1];
 #pragma unroll
-      for (int j = 0; j < L - 1; ++j) thr[j] = __fmul_rn(nbar, ths[j]);
-      uint64_t w0 = 0, w1 = 0;  // the thread's 32 * BITS index bits (at most 128)
+      for (int j = 0; j < L - 1; ++j) thr[j] = __fmul_rn(nbar, th[j]);
       double s2 = 0.0;
-#pragma unroll 4
-      for (int k = 0; k < 32; ++k) {
-        const int col = ch * 32 + k;
-        const float y = fv[vr * LDF + col];
-        uint32_t q = 0;
 #pragma unroll
-        for (int j = 0; j < L - 1; ++j) q += (y >= thr[j]) ? 1u : 0u;
-        const float r = __fsub_rn(y, __fmul_rn(nbar, cbs[q]));
-        fv[vr * LDF + col] = r;
-        if constexpr (M > 0) {
-          uint16_t hi, lo;
-          split_bf16(r, hi, lo);
-          ah[vr * LDA + col] = hi;
-          al[vr * LDA + col] = lo;
+      for (int u = 0; u < KS; ++u) {
+        uint32_t qv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qv[j] = quantize_index<BITS>(yv[t][u][j], thr);
+        uint32_t field = 0u;  // 8 * BITS bits: coordinates 32u + 8g + 0..7
+        float p = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float r = __fsub_rn(yv[t][u][j], __fmul_rn(nbar, cbs[qv[j]]));
+          yv[t][u][j] = r;
+          p = fmaf(r, r, p);
+          field |= qv[j] << (BITS * j);
         }
-        s2 += (double)r * (double)r;
-        const int b = BITS * k;
-        if (b < 64) {
-          w0 |= (uint64_t)q << b;
-          if (b + BITS > 64) w1 |= (uint64_t)q >> (64 - b);
+        s2 += (double)p;
+        // the field is bytes BITS (4u + g) .. + BITS - 1 of the vector's index record
+        uint8_t *dst = stg + IB * (16 * t + n) + BITS * (4 * u + g);
+        if constexpr (BITS == 2) {
+          *reinterpret_cast<uint16_t *>(dst) = (uint16_t)field;
+        } else if constexpr (BITS == 4) {
+          *reinterpret_cast<uint32_t *>(dst) = field;
         } else {
-          w1 |= (uint64_t)q << (b - 64);
+          dst[0] = (uint8_t)field;
+          dst[1] = (uint8_t)(field >> 8);
+          dst[2] = (uint8_t)(field >> 16);
         }
       }
-      const int64_t v = v0 + vr;
-      if (v < a.n) {
-        const uint32_t wds[4] = {(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)};
-#pragma unroll
-        for (int w = 0; w < BITS; ++w) idxw[v * iw_all + ch * BITS + w] = wds[w];
-        if (ch == 0)
-          for (int w = D * BITS / 32; w < iw_all; ++w) idxw[v * iw_all + w] = 0u;
+      // staged index records of tile t -> HBM, 8 bytes per lane and step
+      wave_lds_fence();
+      for (int e = lane; e < 16 * IB / 8; e += kWave) {
+        const int vv = e / (IB / 8), w = e % (IB / 8);
+        const int64_t v = v0 + 16 * t + vv;
+        if (v < a.n)
+          *reinterpret_cast<uint2 *>(a.idx + v * a.idx_stride + 8 * w) =
+              *reinterpret_cast<const uint2 *>(stg + IB * (16 * t + vv) + 8 * w);
       }
-      s2 = group_sum<TPV>(s2);
+      wave_lds_fence();
+      const int64_t v = v0 + 16 * t + n;
+      if (g == 0 && v < a.n)
+        for (int w = IWV; w < iw_all; ++w) idxw[v * iw_all + w] = 0u;
+      s2 += __shfl_xor(s2, 16, kWave);
+      s2 += __shfl_xor(s2, 32, kWave);
       bool ok;
-      const uint32_t h = f16_norm_candidate<D>(s2, ok);
-      if (ch == 0) {
-        nws[vr] = n16 | (h << 16);
-        flag[vr] = ok ? 0u : 1u;
-        rn2[vr] = (float)s2;
-      }
-    }
-    __syncthreads();
-    for (int r = wid; r < T; r += NW) {
-      if (flag[r]) {
-        float xv[C];
+      rn16[t] = f16_norm_fast(s2, ok);
+      if (__ballot(!ok)) {
+        double s4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int c = 0; c < C; ++c) xv[c] = fv[r * LDF + lane + kWave * c];
-        const uint32_t h = wave_norm_f16<D, C>(xv, xterms[wid], xbuf[wid]);
-        if (lane == 0) nws[r] = (nws[r] & 0xFFFFu) | (h << 16);
+        for (int u = 0; u < KS; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s4[j & 3] = fma((double)yv[t][u][j], (double)yv[t][u][j], s4[j & 3]);
+        double s64 = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        s64 += __shfl_xor(s64, 16, kWave);
+        s64 += __shfl_xor(s64, 32, kWave);
+        s2 = s64;
+        bool ok64;
+        const uint32_t h64 = f16_norm_candidate<D>(s64, ok64);
+        if (!ok) rn16[t] = h64;
+        uint64_t bad = __ballot(!ok && !ok64 && g == 0);
+        while (bad) {
+          const int n0 = __ffsll((unsigned long long)bad) - 1;
+          if (n == n0) {
+#pragma unroll
+            for (int u = 0; u < KS; ++u)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) xt[8 * KS * g + 8 * u + j] = (double)yv[t][u][j] * (double)yv[t][u][j];
+          }
+          wave_lds_fence();
+          uint32_t h = 0;
+          if (lane == n0) h = f16_norm_exact(xt, D, rn16[t], xb);
+          wave_lds_fence();
+          h = (uint32_t)__shfl((int)h, n0, kWave);
+          if (n == n0) rn16[t] = h;
+          bad &= bad - 1;
+        }
       }
+      rn2[t] = s2;
+      if (g == 0 && v < a.n) a.norms[v] = (rn16[t] << 16) | n16[t];
     }
-    __syncthreads();
-    // ---- 5. sign bits of z = r S^T
+
+    // ---- 5. sign bits of z = S r
     if constexpr (M > 0) {
-      f32x4 acc[NRT][WMCT];
+      constexpr int NB = M / 32;  // sign bytes per lane per tile: sketch rows 32b + 8g + 0..7
+      float tau[NV];
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
+      for (int t = 0; t < NV; ++t) {
+        // A tiny r (products near the fp32 underflow) leaves every sign to the fp64 path,
+        // except r = 0 exactly: then z = 0 exactly and every bit is 1.
+        const bool tiny = rn2[t] < 1e-30;
+        bool zero = false;
+        if (__ballot(tiny)) {
+          float rmax = 0.0f;
 #pragma unroll
-        for (int mc = 0; mc < WMCT; ++mc) acc[rt][mc] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          for (int u = 0; u < KS; ++u)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int mc = 0; mc < WMCT; ++mc) {
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) {
-            const bf16x4 rh = *reinterpret_cast<const bf16x4 *>(&ah[(16 * rt + (lane & 15)) * LDA + 16 * ks + 4 * (lane >> 4)]);
-            acc[rt][mc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(rh, sh[mc][ks], acc[rt][mc], 0, 0, 0);
-          }
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) {
-            const bf16x4 rl = *reinterpret_cast<const bf16x4 *>(&al[(16 * rt + (lane & 15)) * LDA + 16 * ks + 4 * (lane >> 4)]);
-            acc[rt][mc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(rl, sh[mc][ks], acc[rt][mc], 0, 0, 0);
-          }
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) {
-            const bf16x4 rh = *reinterpret_cast<const bf16x4 *>(&ah[(16 * rt + (lane & 15)) * LDA + 16 * ks + 4 * (lane >> 4)]);
-            acc[rt][mc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(rh, sl[mc][ks], acc[rt][mc], 0, 0, 0);
-          }
+            for (int j = 0; j < 8; ++j) rmax = fmaxf(rmax, fabsf(yv[t][u][j]));
+          rmax = fmaxf(rmax, __shfl_xor(rmax, 16, kWave));
+          rmax = fmaxf(rmax, __shfl_xor(rmax, 32, kWave));
+          zero = rmax == 0.0f;
         }
+        tau[t] = zero ? -1.0f : (tiny ? INFINITY : 0x1p-13f * smax * (float)sqrt(rn2[t]));
       }
-      static_assert(NRT * WMCT * 4 <= 32, "one bit per accumulator element in a 32-bit mask");
-      // pass 1: sign and "undecided" flag of every accumulator element, as per-lane bit masks
-      uint32_t bitm = 0u, ambm = 0u;
+      uint32_t sb[NV][NB];
+      // one 16-vector tile at a time: z for every sketch tile, r split into bf16 hi/lo one
+      // k-step at a time
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
+      for (int t = 0; t < NV; ++t) {
+        f32x4 z[NB][2];
 #pragma unroll
-        for (int mc = 0; mc < WMCT; ++mc)
+        for (int b = 0; b < NB; ++b) z[b][0] = z[b][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = (rt * WMCT + mc) * 4 + i;
-            const int row = 16 * rt + 4 * (lane >> 4) + i;
-            const float z = acc[rt][mc][i];
-            const float r2 = rn2[row];
-            const float tau = r2 < 1e-30f ? INFINITY : 0x1p-13f * snorm[mc] * sqrtf(r2);
-            bitm |= (z >= 0.0f ? 1u : 0u) << e;
-            ambm |= (fabsf(z) <= tau ? 1u : 0u) << e;
+        for (int u = 0; u < KS; ++u) {
+          bf16x8 rh, rl;
+          split8(yv[t][u], rh, rl);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const bf16x8 h0 = afrag(fsk, 2 * b, u, 0, KS), l0 = afrag(fsk, 2 * b, u, 1, KS);
+            const bf16x8 h1 = afrag(fsk, 2 * b + 1, u, 0, KS), l1 = afrag(fsk, 2 * b + 1, u, 1, KS);
+            z[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h0, rh, z[b][0], 0, 0, 0);
+            z[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h1, rh, z[b][1], 0, 0, 0);
+            z[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h0, rl, z[b][0], 0, 0, 0);
+            z[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h1, rl, z[b][1], 0, 0, 0);
+            z[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(l0, rh, z[b][0], 0, 0, 0);
+            z[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(l1, rh, z[b][1], 0, 0, 0);
           }
-      // pass 2: undecided elements, one at a time for the whole wavefront: fp64 dot product
-      // with its error bound, then the exact expansion if the bound still does not decide
-      uint64_t pend = __ballot(ambm != 0u);
-      while (pend) {
-        const int src = __ffsll((unsigned long long)pend) - 1;
-        const uint32_t sm = (uint32_t)__shfl((int)ambm, src, kWave);
-        const int e = __ffs(sm) - 1;
-        const int i = e & 3, mc = (e >> 2) % WMCT, rt = (e >> 2) / WMCT;
-        const int srow = 16 * rt + 4 * (src >> 4) + i;
-        const int j = 16 * (wid * WMCT + mc) + (src & 15);
-        double ps = 0.0, pa = 0.0;
-        for (int k = lane; k < D; k += kWave) {
-          const double p = (double)a.sketch[(int64_t)j * D + k] * (double)fv[srow * LDF + k];
-          ps += p;
-          pa += fabs(p);
         }
-        ps = wave_sum(ps);
-        pa = wave_sum(pa);
-        int sg;
-        if (fabs(ps) > 2.0 * (D + 2) * 0x1p-53 * pa) {
-          sg = ps > 0.0 ? 1 : -1;
-        } else {
-          for (int k = lane; k < D; k += kWave)
-            xterms[wid][k] = (double)a.sketch[(int64_t)j * D + k] * (double)fv[srow * LDF + k];
-          wave_lds_fence();
-          sg = 0;
-          if (lane == 0) sg = expansion_sign(xterms[wid], D, xbuf[wid]);
-          wave_lds_fence();
-          sg = __shfl(sg, 0, kWave);
+        if (t == NV - 1) load_pass(v0 + wstep);
+        // bit = 1 - sign bit of z (a z of either zero is undecided, so this is z >= 0 wherever
+        // it is used); undecided when |z| <= tau
+        uint32_t am[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          uint32_t neg = 0u, amb = 0u;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float zz = z[b][h][i];
+              neg |= (__float_as_uint(zz) >> 31) << (4 * h + i);
+              amb |= (fabsf(zz) <= tau[t] ? 1u : 0u) << (4 * h + i);
+            }
+          sb[t][b] = neg ^ 0xFFu;
+          am[b] = amb;
         }
-        if (lane == src) {
-          bitm = (bitm & ~(1u << e)) | ((sg >= 0 ? 1u : 0u) << e);
-          ambm &= ~(1u << e);
-        }
-        pend = __ballot(ambm != 0u);
-      }
-      // pass 3: 16-bit chunks of sketch rows per vector
+        // Undecided signs, all vectors of the tile at once: the four lanes of a vector agree on
+        // its lowest undecided sketch row q, each takes the fp64 products over its own 32
+        // coordinates, and two exchanges give the dot product and its error bound.
+        for (;;) {
+          int myq = 0xFF;
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
+          for (int b = NB - 1; b >= 0; --b)
+            if (am[b]) myq = 32 * b + 8 * g + (__ffs(am[b]) - 1);
+          int q = min(myq, __shfl_xor(myq, 16, kWave));
+          q = min(q, __shfl_xor(q, 32, kWave));
+          if (__ballot(q != 0xFF) == 0) break;
+          const bool act = q != 0xFF;
+          double ps = 0.0, pa = 0.0;
+          if (act) {
 #pragma unroll
-        for (int mc = 0; mc < WMCT; ++mc)
+            for (int u = 0; u < KS; ++u) {
+              const float4 *srow = reinterpret_cast<const float4 *>(a.sketch + (int64_t)q * D + 32 * u + 8 * g);
+              const float4 s0 = srow[0], s1 = srow[1];
+              const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = (rt * WMCT + mc) * 4 + i;
-            const uint64_t bm = __ballot((bitm >> e) & 1u);
-            if (lane < 4) {
-              const int rowg = 16 * rt + 4 * lane + i;
-              sbits[rowg * MCT + wid * WMCT + mc] = (uint16_t)((bm >> (16 * lane)) & 0xFFFFu);
+              for (int j = 0; j < 8; ++j) {
+                const double pr = (double)sv[j] * (double)yv[t][u][j];
+                ps += pr;
+                pa += fabs(pr);
+              }
             }
           }
-      __syncthreads();
-      for (int e = tid; e < T * sw_all; e += NTH) {
-        const int r = e / sw_all, w = e % sw_all;
-        const int64_t v = v0 + r;
-        if (v < a.n) {
-          uint32_t word = 0u;
-          if (2 * w < MCT) word = sbits[r * MCT + 2 * w];
-          if (2 * w + 1 < MCT) word |= (uint32_t)sbits[r * MCT + 2 * w + 1] << 16;
-          sgnw[v * sw_all + w] = word;
+          ps += __shfl_xor(ps, 16, kWave);
+          ps += __shfl_xor(ps, 32, kWave);
+          pa += __shfl_xor(pa, 16, kWave);
+          pa += __shfl_xor(pa, 32, kWave);
+          const bool dec = fabs(ps) > 2.0 * (D + 2) * 0x1p-53 * pa;
+          int sg = ps > 0.0 ? 1 : -1;
+          // where even fp64 cannot decide: the exact expansion, one vector at a time
+          uint64_t und = __ballot(act && !dec && g == 0);
+          while (und) {
+            const int n0 = __ffsll((unsigned long long)und) - 1;
+            const int q0 = __shfl(q, n0, kWave);
+            if (n == n0) {
+#pragma unroll
+              for (int u = 0; u < KS; ++u)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                  xt[8 * KS * g + 8 * u + j] = (double)a.sketch[(int64_t)q0 * D + 32 * u + 8 * g + j] * (double)yv[t][u][j];
+            }
+            wave_lds_fence();
+            int e = 0;
+            if (lane == n0) e = expansion_sign(xt, D, xb);
+            wave_lds_fence();
+            e = __shfl(e, n0, kWave);
+            if (n == n0) sg = e >= 0 ? 1 : -1;
+            und &= und - 1;
+          }
+          // the lane holding row q records the bit
+          if (act && g == ((q >> 3) & 3)) {
+            const int b0 = q >> 5, bit = q & 7;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+              if (b == b0) {
+                sb[t][b] = (sb[t][b] & ~(1u << bit)) | ((sg >= 0 ? 1u : 0u) << bit);
+                am[b] &= ~(1u << bit);
+              }
+          }
         }
       }
+      // sign byte b of lane g is byte 4b + g of the vector's sign record
+#pragma unroll
+      for (int t = 0; t < NV; ++t)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) stg[SB * (16 * t + n) + 4 * b + g] = (uint8_t)sb[t][b];
+      wave_lds_fence();
+      for (int e = lane; e < NV * 16 * SB / 8; e += kWave) {
+        const int vv = e / (SB / 8), w = e % (SB / 8);
+        const int64_t v = v0 + vv;
+        if (v < a.n)
+          *reinterpret_cast<uint2 *>(a.sign + v * a.sign_stride + 8 * w) =
+              *reinterpret_cast<const uint2 *>(stg + SB * vv + 8 * w);
+      }
+      wave_lds_fence();
+#pragma unroll
+      for (int t = 0; t < NV; ++t) {
+        const int64_t v = v0 + 16 * t + n;
+        if (v < a.n && g == 0)
+          for (int w = NB; w < sw_all; ++w) sgnw[v * sw_all + w] = 0u;
+      }
     }
-    for (int r = tid; r < T; r += NTH)
-      if (v0 + r < a.n) a.norms[v0 + r] = nws[r];
-    __syncthreads();
   }
 }
 
 template <int D, int BITS, int M, int TIN, bool PRE>
 static void launch_mfma(const EncArgs &a, hipStream_t st) {
-  constexpr int NTH = D == 128 ? 512 : 256;  // tiles of 128 vectors; 16 columns of y per wavefront
-  constexpr int T = NTH * 32 / D;
-  int64_t tiles = (a.n + T - 1) / T;
-  if (tiles > 256 * 2) tiles = 256 * 2;
-  hipLaunchKernelGGL((encode_mfma<D, BITS, M, TIN, PRE, NTH>), dim3((unsigned)tiles), dim3(NTH), 0, st, a);
+  constexpr int NW = 8;  // 2 per SIMD: the sign phase needs up to 256 VGPRs
+  constexpr int PER_BLOCK = NW * 32;
+  int64_t blocks = (a.n + PER_BLOCK - 1) / PER_BLOCK;
+  if (blocks > 256) blocks = 256;
+  hipLaunchKernelGGL((encode_mfma<D, BITS, M, TIN, PRE, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, a);
 }
 
 template <int D, int BITS, int M>
