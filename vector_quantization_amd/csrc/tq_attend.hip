@@ -83,18 +83,39 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   constexpr int RCAP = Lut<D, KB, KM, G>::BYTES / (NOUT * G * 4);  // slices per reduction round
   static_assert(RCAP >= 1, "final reduction reuses the table space");
 
-  __shared__ __align__(16) uint8_t tabs[CK::BYTES];
-  __shared__ float qt[G * D];
-  __shared__ float qh[G * (KM > 0 ? KM : 1)];
-  __shared__ float cbk[1 << KB];
-  __shared__ float cbv[LV];
-  __shared__ float2 cbv2[LP];  // (c[a], c[b]) for the two-code group (b << VB) | a
-  __shared__ float scm[G], scq[G];
-  __shared__ uint32_t vtile[NT * IWV];
-  __shared__ uint32_t vstile[VM > 0 ? NT * SWV : 1];
-  __shared__ __align__(16) float wt[NT * G];
-  __shared__ __align__(16) float wq[VM > 0 ? NT * G : 1];
-  __shared__ float red_max[NW * G], red_sum[NW * G];
+  // One LDS arena with fixed offsets: the value-phase arrays at the bottom, so that their
+  // addresses fit the 16-bit offset field of ds instructions; the lookup tables last.
+  constexpr int O_CBV2 = 0;
+  constexpr int O_VTILE = O_CBV2 + LP * 8;
+  constexpr int O_VSTILE = O_VTILE + NT * IWV * 4;
+  constexpr int O_WT = (O_VSTILE + (VM > 0 ? NT * SWV : 1) * 4 + 15) / 16 * 16;
+  constexpr int O_WQ = O_WT + NT * G * 4;
+  constexpr int O_RMAX = O_WQ + (VM > 0 ? NT * G : 4) * 4;
+  constexpr int O_RSUM = O_RMAX + NW * G * 4;
+  constexpr int O_CBK = O_RSUM + NW * G * 4;
+  constexpr int O_CBV = O_CBK + (1 << KB) * 4;
+  constexpr int O_SCM = O_CBV + LV * 4;
+  constexpr int O_SCQ = O_SCM + G * 4;
+  constexpr int O_QT = O_SCQ + G * 4;
+  constexpr int O_QH = O_QT + G * D * 4;
+  constexpr int O_TABS = (O_QH + G * (KM > 0 ? KM : 1) * 4 + 15) / 16 * 16;
+  constexpr int ARENA = O_TABS + CK::BYTES;
+  static_assert(ARENA <= 160 * 1024, "LDS arena");
+  __shared__ __align__(16) uint8_t arena[ARENA];
+  float2 *cbv2 = reinterpret_cast<float2 *>(arena + O_CBV2);  // (c[a], c[b]) for (b << VB) | a
+  uint32_t *vtile = reinterpret_cast<uint32_t *>(arena + O_VTILE);
+  uint32_t *vstile = reinterpret_cast<uint32_t *>(arena + O_VSTILE);
+  float *wt = reinterpret_cast<float *>(arena + O_WT);
+  float *wq = reinterpret_cast<float *>(arena + O_WQ);
+  float *red_max = reinterpret_cast<float *>(arena + O_RMAX);
+  float *red_sum = reinterpret_cast<float *>(arena + O_RSUM);
+  float *cbk = reinterpret_cast<float *>(arena + O_CBK);
+  float *cbv = reinterpret_cast<float *>(arena + O_CBV);
+  float *scm = reinterpret_cast<float *>(arena + O_SCM);
+  float *scq = reinterpret_cast<float *>(arena + O_SCQ);
+  float *qt = reinterpret_cast<float *>(arena + O_QT);
+  float *qh = reinterpret_cast<float *>(arena + O_QH);
+  uint8_t *tabs = arena + O_TABS;
 
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   const int64_t b = blockIdx.x;

@@ -293,7 +293,7 @@ static int launch_score_g(const ScoreArgs &a0, const ScoreShape &s, hipStream_t 
   constexpr int NT = (Lut<D, BITS, M, G>::BYTES > 48 * 1024) ? 1024 : 256;
   ScoreArgs a = a0;
   a.nsub = (s.hq / s.hkv) / G;
-  a.chunk = 16384;
+  a.chunk = 32768;
   if (s.n < a.chunk) a.chunk = (int)((s.n + NT - 1) / NT * NT);
   if (a.chunk < NT) a.chunk = NT;
   a.n_chunks = (int)((s.n + a.chunk - 1) / a.chunk);
