@@ -379,6 +379,14 @@ __device__ __forceinline__ uint32_t quantize_index(float y, const float (&t)[(1 
   }
 }
 
+// An opaque copy of x: conversions of it inside a rarely taken loop stay in that loop instead of
+// being hoisted in front of it, where they would hold two registers per element for the whole
+// pass.
+__device__ __forceinline__ float opaque(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Exact fp16 RNE of sqrt(sum of terms[0..cnt)), starting from candidate h: compares the exact
 // sum with squared fp16 midpoints (each exact in fp64).  terms needs cnt + 1 entries, buf
 // cnt + 1.  Run by one lane.
@@ -447,9 +455,11 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
   constexpr int KS = D / 32;   // k-steps; also 8-coordinate groups u per lane
   constexpr int CT = D / 16;   // 16-row tiles of y
   constexpr int MT = M / 16;   // 16-row tiles of z
-  constexpr int NV = 2;        // 16-vector tiles per pass
   constexpr int L = 1 << BITS;
   constexpr bool XLO = !PRE && TIN != TQ_BF16;            // input needs a lo part
+  // 16-vector tiles per pass: two share each Pi / S fragment read; one when the input's lo
+  // part would not fit the registers beside them (d = 128 fp16 / fp32 input)
+  constexpr int NV = (D == 128 && XLO) ? 1 : 2;
   constexpr int U4 = (PRE || TIN == TQ_F32) ? 2 : 1;      // 16-byte chunks per 8 elements
   constexpr int EB = (PRE || TIN == TQ_F32) ? 4 : 2;
   constexpr int IWV = D * BITS / 32;                       // index words per vector
@@ -561,7 +571,10 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
           float x[8];
           raw_to_f32<PRE ? TQ_F32 : TIN, U4>(raw[t][ks], x);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) s4[j & 3] = fma((double)x[j], (double)x[j], s4[j & 3]);
+          for (int j = 0; j < 8; ++j) {
+            const double xj = opaque(x[j]);
+            s4[j & 3] = fma(xj, xj, s4[j & 3]);
+          }
         }
         double s64 = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         s64 += __shfl_xor(s64, 16, kWave);
@@ -578,7 +591,10 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
               float x[8];
               raw_to_f32<PRE ? TQ_F32 : TIN, U4>(raw[t][ks], x);
 #pragma unroll
-              for (int j = 0; j < 8; ++j) xt[8 * KS * g + 8 * ks + j] = (double)x[j] * (double)x[j];
+              for (int j = 0; j < 8; ++j) {
+                const double xj = opaque(x[j]);
+                xt[8 * KS * g + 8 * ks + j] = xj * xj;
+              }
             }
           }
           wave_lds_fence();
@@ -717,7 +733,10 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
 #pragma unroll
         for (int u = 0; u < KS; ++u)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) s4[j & 3] = fma((double)yv[t][u][j], (double)yv[t][u][j], s4[j & 3]);
+          for (int j = 0; j < 8; ++j) {
+            const double rj = opaque(yv[t][u][j]);
+            s4[j & 3] = fma(rj, rj, s4[j & 3]);
+          }
         double s64 = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         s64 += __shfl_xor(s64, 16, kWave);
         s64 += __shfl_xor(s64, 32, kWave);
@@ -732,7 +751,10 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
 #pragma unroll
             for (int u = 0; u < KS; ++u)
 #pragma unroll
-              for (int j = 0; j < 8; ++j) xt[8 * KS * g + 8 * u + j] = (double)yv[t][u][j] * (double)yv[t][u][j];
+              for (int j = 0; j < 8; ++j) {
+                const double rj = opaque(yv[t][u][j]);
+                xt[8 * KS * g + 8 * u + j] = rj * rj;
+              }
           }
           wave_lds_fence();
           uint32_t h = 0;
@@ -832,7 +854,7 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
               const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
               for (int j = 0; j < 8; ++j) {
-                const double pr = (double)sv[j] * (double)yv[t][u][j];
+                const double pr = (double)sv[j] * (double)opaque(yv[t][u][j]);
                 ps += pr;
                 pa += fabs(pr);
               }
@@ -854,7 +876,8 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
               for (int u = 0; u < KS; ++u)
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                  xt[8 * KS * g + 8 * u + j] = (double)a.sketch[(int64_t)q0 * D + 32 * u + 8 * g + j] * (double)yv[t][u][j];
+                  xt[8 * KS * g + 8 * u + j] =
+                      (double)a.sketch[(int64_t)q0 * D + 32 * u + 8 * g + j] * (double)opaque(yv[t][u][j]);
             }
             wave_lds_fence();
             int e = 0;
@@ -902,8 +925,8 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
 
 template <int D, int BITS, int M, int TIN, bool PRE>
 static void launch_mfma(const EncArgs &a, hipStream_t st) {
-  constexpr int NW = 8;  // 2 per SIMD: the sign phase needs up to 256 VGPRs
-  constexpr int PER_BLOCK = NW * 32;
+  constexpr int NW = 8;  // 2 per SIMD: up to 256 VGPRs each
+  constexpr int PER_BLOCK = NW * 16 * ((D == 128 && !PRE && TIN != TQ_BF16) ? 1 : 2);
   int64_t blocks = (a.n + PER_BLOCK - 1) / PER_BLOCK;
   if (blocks > 256) blocks = 256;
   hipLaunchKernelGGL((encode_mfma<D, BITS, M, TIN, PRE, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, a);
