@@ -23,7 +23,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 SCORE_SOURCES = ("tq_scores.hip", "tq_lut.h", "tq_device.h", "tq_internal.h")
-SCORE_KERNELS = ("tq::qprep_tiled<128, 128>", "tq::score_kernel<128, 2, 128, 4, 1024>")
+SCORE_KERNELS = ("tq::score_kernel<128, 2, 128, 4, 1024>",)
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_kernel_gqa8b_decode_b8_32k_traffic.txt")
 METRIC = "compressed-KV decode scoring GB/s (% HBM peak) + keys/s; encode vectors/s"
 

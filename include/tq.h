@@ -129,7 +129,8 @@ int tq_encode(const tq_codec *codec, const void *x, tq_dtype dt, int64_t n, int6
  *   q       [n_seq][hq][d] fp32 queries (post-RoPE).  The cache k holds [n_seq][hkv][n_keys]
  *           vectors; query head h reads kv head h / (hq / hkv) (hq % hkv == 0).
  *   logits  [n_seq][hq][n_keys] fp32, unscaled (no 1/sqrt(d)).
- *   ws      workspace of tq_workspace_bytes(TQ_OP_SCORES, ...) bytes, 256-byte aligned.     */
+ *   ws      workspace of tq_workspace_bytes(TQ_OP_SCORES, ...) bytes, 256-byte aligned; that
+ *           size is 0 (each workgroup prepares Pi q and S Pi q itself), and ws may be NULL.   */
 int tq_scores(const tq_codec *kc, const float *q, int64_t n_seq, int32_t hq, int32_t hkv,
               int64_t n_keys, tq_codes k, float *logits, void *ws, size_t ws_bytes, void *stream);
 

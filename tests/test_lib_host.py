@@ -102,15 +102,20 @@ def test_device_call_argument_errors():
     assert L.tq_encode(ctypes.byref(cc), x, 0, 4, 100, 0, 0, _fake_codes(), None, S) == -1  # ld_x < d
     # n == 0 is a no-op
     assert L.tq_encode(ctypes.byref(cc), x, 0, 0, 128, 0, 0, _fake_codes(), None, S) == 0
-    # scores: GQA shape, workspace
+    # scores: GQA shape; no workspace (each workgroup prepares its own queries)
     q = ctypes.c_void_p(0x60000)
     lg = ctypes.c_void_p(0x70000)
     assert L.tq_scores(ctypes.byref(cc), q, 2, 6, 4, 16, _fake_codes(), lg, None, 0, S) == -1
-    need = L.tq_workspace_bytes(0, ctypes.byref(cc), None, 2, 8, 2, 16)
-    assert need == 2 * 8 * (128 + 128) * 4
-    assert L.tq_scores(ctypes.byref(cc), q, 2, 8, 2, 16, _fake_codes(), lg, None, 0, S) == -4
-    assert L.tq_scores(ctypes.byref(cc), q, 2, 8, 2, 16, _fake_codes(), lg, ctypes.c_void_p(0x80000), need - 1, S) == -4
-    assert L.tq_scores(ctypes.byref(cc), q, 2, 8, 2, 16, _fake_codes(), lg, ctypes.c_void_p(0x80010), need, S) == -3
+    assert L.tq_workspace_bytes(0, ctypes.byref(cc), None, 2, 8, 2, 16) == 0
+    # attend: workspace (query prep + per-chunk partial states), checked before any launch
+    vc = _fake_codec(bits=3, m=0)
+    need = L.tq_workspace_bytes(1, ctypes.byref(cc), ctypes.byref(vc), 2, 8, 2, 16)
+    assert need >= 2 * 8 * (128 + 128) * 4
+    vcodes = _fake_codes(idx_stride=48, sign=0, sign_stride=0)
+    args = (ctypes.byref(cc), ctypes.byref(vc), q, 2, 8, 2, 16, _fake_codes(), vcodes, ctypes.c_float(0.1), lg)
+    assert L.tq_attend_decode(*args, None, 0, S) == -4
+    assert L.tq_attend_decode(*args, ctypes.c_void_p(0x80000), need - 1, S) == -4
+    assert L.tq_attend_decode(*args, ctypes.c_void_p(0x80010), need, S) == -3
     # search: k range
     assert L.tq_search_topk(ctypes.byref(cc), q, 3, _fake_codes(), 100, 33, lg, lg, None, 0, S) == -1
     assert L.tq_search_topk(ctypes.byref(cc), q, 3, _fake_codes(), 5, 10, lg, lg, None, 0, S) == -1

@@ -80,8 +80,10 @@ extern "C" int tq_scores(const tq_codec *kc, const float *q, int64_t n_seq, int3
   if (rc != TQ_OK) return rc;
   const tq::ScoreShape s{n_seq, hq, hkv, n_keys};
   const size_t need = tq::scores_workspace(tq::view(*kc), s);
-  if (!ws || ws_bytes < need) return TQ_EWORKSPACE;
-  if (!aligned(ws, 256)) return TQ_EALIGN;
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return TQ_EWORKSPACE;
+    if (!aligned(ws, 256)) return TQ_EALIGN;
+  }
   return tq::launch_scores(tq::view(*kc), q, s, tq::view(k), logits, ws, ws_bytes, stream);
 }
 

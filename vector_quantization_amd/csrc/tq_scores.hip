@@ -6,10 +6,11 @@
 // "Cómo funciona PolarQuant" (norm times quantised direction).  The estimate is evaluated in
 // the rotated space: <q, k~> = nbar <Pi q, c[idx]> + rnbar sqrt(pi/2)/m <S Pi q, 2 bits - 1>.
 //
-// qprep: one wavefront per query head computes q~ = Pi_r q and q^ = S q~ in fp32.
-// score: one workgroup per (sequence, kv head, head subgroup, key chunk) builds the lookup
-// tables of its G query heads in LDS (tq_lut.h), then streams the chunk's code planes from
-// HBM, one key per thread per step, and writes fp32 logits for the G heads.
+// qprep (used by attention and search): q~ = Pi_r q and q^ = S q~ in fp32 for every query head.
+// score: one workgroup per (sequence, kv head, head subgroup, key chunk) computes q~ and q^ of
+// its G query heads itself (Pi and S come from L2), builds their lookup tables in LDS
+// (tq_lut.h), then streams the chunk's code planes from HBM, one key per thread per step, and
+// writes fp32 logits for the G heads.
 
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -156,7 +157,9 @@ __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
 }
 
 struct ScoreArgs {
-  const float *qt, *qh, *centroids;
+  const float *q, *rot, *sketch, *centroids;
+  int n_rot;
+  int64_t vecs_per_rot;
   int64_t n_seq, n_keys;
   int hq, hkv, nsub, n_chunks, chunk;
   const uint8_t *idx;
@@ -190,11 +193,58 @@ __device__ __forceinline__ void load_words(const uint8_t *p, uint32_t (&w)[W]) {
   }
 }
 
+// q~ = R q and q^ = S q~ for the G consecutive query heads at q (fp32, global), by the whole
+// workgroup: KSL threads per output row each sum KPER products, then combine by shuffles
+// (KSL is a power of two, so a row's threads are aligned lanes of one wavefront).  qs is LDS
+// scratch of G * D floats; qt [G][D] and qh [G][M] are LDS outputs.  Ends synchronised.
+template <int D, int M, int G, int NT>
+__device__ void block_prep_queries(const float *q, const float *R, const float *S, float *qs, float *qt, float *qh) {
+  constexpr int ROWS = D > M ? D : M;
+  constexpr int KSL = (NT / ROWS >= 16) ? 16 : (NT / ROWS >= 8) ? 8 : (NT / ROWS >= 4) ? 4 : (NT / ROWS >= 2) ? 2 : 1;
+  constexpr int KPER = (D + KSL - 1) / KSL;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < G * D; e += NT) qs[e] = q[e];
+  __syncthreads();
+  auto matvec = [&](const float *W, int rows, const float *in, float *out) {
+    for (int r0 = 0; r0 < rows; r0 += NT / KSL) {
+      const int r = r0 + tid / KSL, sl = tid % KSL;
+      float acc[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = 0.0f;
+      if (r < rows) {
+#pragma unroll 4
+        for (int kk = 0; kk < KPER; ++kk) {
+          const int k = sl * KPER + kk;
+          if (k < D) {
+            const float w = W[(int64_t)r * D + k];
+#pragma unroll
+            for (int h = 0; h < G; ++h) acc[h] = fmaf(w, in[h * D + k], acc[h]);
+          }
+        }
+      }
+#pragma unroll
+      for (int off = KSL / 2; off >= 1; off >>= 1)
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] += __shfl_xor(acc[h], off, kWave);
+      if (r < rows && sl == 0)
+#pragma unroll
+        for (int h = 0; h < G; ++h) out[h * rows + r] = acc[h];
+    }
+  };
+  matvec(R, D, qs, qt);
+  __syncthreads();
+  if constexpr (M > 0) {
+    matvec(S, M, qt, qh);
+    __syncthreads();
+  }
+}
+
 template <int D, int BITS, int M, int G, int NT>
 __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
   using C = Lut<D, BITS, M, G>;
   constexpr int SWN = C::SW > 0 ? C::SW : 1;
   __shared__ __align__(16) uint8_t tabs[C::BYTES];
+  __shared__ float qs[G * D];
   __shared__ float qt[G * D];
   __shared__ float qh[G * (M > 0 ? M : 1)];
   __shared__ float cb[C::L];
@@ -211,11 +261,13 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
   const int h0 = kvh * g + sub * G;  // first query head of this group
   const int64_t qrow = s * a.hq + h0;
 
-  for (int i = threadIdx.x; i < G * D; i += NT) qt[i] = a.qt[qrow * D + i];
-  if constexpr (M > 0)
-    for (int i = threadIdx.x; i < G * M; i += NT) qh[i] = a.qh[qrow * M + i];
   if (threadIdx.x < C::L) cb[threadIdx.x] = a.centroids[threadIdx.x];
-  __syncthreads();
+  int64_t rid = 0;  // the rotation of this kv block
+  if (a.n_rot > 1 && a.vecs_per_rot > 0) {
+    rid = (blk * a.n_keys) / a.vecs_per_rot;
+    if (rid > a.n_rot - 1) rid = a.n_rot - 1;
+  }
+  block_prep_queries<D, M, G, NT>(a.q + qrow * D, a.rot + rid * (int64_t)D * D, a.sketch, qs, qt, qh);
   HeadScales<G> hs;
   {
     const float cmax = fmaxf(fabsf(cb[0]), fabsf(cb[C::L - 1]));
@@ -255,9 +307,7 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
   }
 }
 
-size_t scores_workspace(const CodecView &kc, const ScoreShape &s) {
-  return (size_t)s.n_seq * s.hq * (size_t)(kc.d + kc.m) * sizeof(float);
-}
+size_t scores_workspace(const CodecView &, const ScoreShape &) { return 0; }
 
 template <int D, int M>
 static int launch_qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh,
@@ -304,7 +354,7 @@ static int launch_score_g(const ScoreArgs &a0, const ScoreShape &s, hipStream_t 
 
 template <int D, int BITS, int M, int G>
 constexpr bool lut_fits() {
-  return Lut<D, BITS, M, G>::BYTES + G * (D + M) * 4 + 512 <= 160 * 1024;
+  return Lut<D, BITS, M, G>::BYTES + G * (2 * D + M) * 4 + 512 <= 160 * 1024;
 }
 
 template <int D, int BITS, int M>
@@ -322,12 +372,10 @@ static int launch_score_dbm(const ScoreArgs &a, const ScoreShape &s, hipStream_t
 int launch_scores(const CodecView &kc, const float *q, const ScoreShape &s, const CodesView &k, float *logits,
                   void *ws, size_t ws_bytes, void *stream) {
   if (s.n == 0 || s.n_seq == 0) return TQ_OK;
+  (void)ws;
+  (void)ws_bytes;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  float *qt = reinterpret_cast<float *>(ws);
-  float *qh = qt + (size_t)s.n_seq * s.hq * kc.d;
-  int rc = qprep(kc, q, s, qt, qh, st);
-  if (rc != TQ_OK) return rc;
-  ScoreArgs a{qt, qh, kc.centroids, s.n_seq, s.n, s.hq, s.hkv, 1, 1, 1,
+  ScoreArgs a{q, kc.rot, kc.sketch, kc.centroids, kc.n_rot, kc.vecs_per_rot, s.n_seq, s.n, s.hq, s.hkv, 1, 1, 1,
               k.idx, k.idx_stride, k.sign, k.sign_stride, k.norms, logits};
   const int D = kc.d, B = kc.bits, M = kc.m;
 #define TQ_SC(DD, BB, MM) if (D == DD && B == BB && M == MM) return launch_score_dbm<DD, BB, MM>(a, s, st);
