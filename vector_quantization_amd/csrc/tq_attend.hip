@@ -72,43 +72,33 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   constexpr int IWV = (D * VB + 31) / 32;
   constexpr int SWV = (VM + 31) / 32;
   constexpr int NOUT = D + VM;
-  constexpr int CPT = 8;             // consecutive output coordinates per thread (value phase)
-  constexpr int NCG = NOUT / CPT;    // coordinate groups
-  constexpr int TPO = NT / NCG;      // threads sharing one coordinate group (token slices)
-  constexpr int TOK = NT / TPO;      // tokens of a tile handled by one thread in the value phase
   constexpr int NW = NT / kWave;
-  static_assert(D % CPT == 0 && VM % CPT == 0 && NT % NCG == 0, "threads must cover the outputs evenly");
+  constexpr int CPT = 8;             // consecutive output coordinates per lane (value phase)
+  constexpr int NCG = NOUT / CPT;    // coordinate groups
+  constexpr int TPO = kWave / NCG;   // lanes of a wavefront sharing one coordinate group
+  constexpr int TOK = kWave / TPO;   // tokens of a wavefront tile per lane in the value phase
+  static_assert(D % CPT == 0 && VM % CPT == 0 && kWave % NCG == 0, "lanes must cover the outputs evenly");
   constexpr int LV = 1 << VB;
   constexpr int LP = LV * LV;        // entries of the two-code value table
-  constexpr int RCAP = Lut<D, KB, KM, G>::BYTES / (NOUT * G * 4);  // slices per reduction round
-  static_assert(RCAP >= 1, "final reduction reuses the table space");
-
-  // One LDS arena with fixed offsets: the value-phase arrays at the bottom, so that their
-  // addresses fit the 16-bit offset field of ds instructions; the lookup tables last.
+  // One LDS arena with fixed offsets: the value table and the per-wavefront tiles at the bottom
+  // (immediate ds offsets), the lookup tables at the top; the final merge reuses the tables.
+  constexpr int WT_V = kWave * IWV;                 // words per wavefront: value index records
+  constexpr int WT_S = VM > 0 ? kWave * SWV : 0;    // value sign records
   constexpr int O_CBV2 = 0;
-  constexpr int O_VTILE = O_CBV2 + LP * 8;
-  constexpr int O_VSTILE = O_VTILE + NT * IWV * 4;
-  constexpr int O_WT = (O_VSTILE + (VM > 0 ? NT * SWV : 1) * 4 + 15) / 16 * 16;
-  constexpr int O_WQ = O_WT + NT * G * 4;
-  constexpr int O_RMAX = O_WQ + (VM > 0 ? NT * G : 4) * 4;
-  constexpr int O_RSUM = O_RMAX + NW * G * 4;
-  constexpr int O_CBK = O_RSUM + NW * G * 4;
+  constexpr int O_WAVE = O_CBV2 + LP * 8;
+  constexpr int WAVE_BYTES = ((WT_V + WT_S) * 4 + kWave * G * 4 * (VM > 0 ? 2 : 1) + 15) / 16 * 16;
+  constexpr int O_CBK = O_WAVE + NW * WAVE_BYTES;
   constexpr int O_CBV = O_CBK + (1 << KB) * 4;
   constexpr int O_SCM = O_CBV + LV * 4;
   constexpr int O_SCQ = O_SCM + G * 4;
   constexpr int O_QT = O_SCQ + G * 4;
   constexpr int O_QH = O_QT + G * D * 4;
   constexpr int O_TABS = (O_QH + G * (KM > 0 ? KM : 1) * 4 + 15) / 16 * 16;
-  constexpr int ARENA = O_TABS + CK::BYTES;
+  constexpr int MERGE_BYTES = NW * (NOUT + 2) * G * 4;
+  constexpr int ARENA = O_TABS + (CK::BYTES > MERGE_BYTES ? CK::BYTES : MERGE_BYTES);
   static_assert(ARENA <= 160 * 1024, "LDS arena");
   __shared__ __align__(16) uint8_t arena[ARENA];
   float2 *cbv2 = reinterpret_cast<float2 *>(arena + O_CBV2);  // (c[a], c[b]) for (b << VB) | a
-  uint32_t *vtile = reinterpret_cast<uint32_t *>(arena + O_VTILE);
-  uint32_t *vstile = reinterpret_cast<uint32_t *>(arena + O_VSTILE);
-  float *wt = reinterpret_cast<float *>(arena + O_WT);
-  float *wq = reinterpret_cast<float *>(arena + O_WQ);
-  float *red_max = reinterpret_cast<float *>(arena + O_RMAX);
-  float *red_sum = reinterpret_cast<float *>(arena + O_RSUM);
   float *cbk = reinterpret_cast<float *>(arena + O_CBK);
   float *cbv = reinterpret_cast<float *>(arena + O_CBV);
   float *scm = reinterpret_cast<float *>(arena + O_SCM);
@@ -118,6 +108,12 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   uint8_t *tabs = arena + O_TABS;
 
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  uint8_t *wbase = arena + O_WAVE + wid * WAVE_BYTES;
+  uint32_t *vtile = reinterpret_cast<uint32_t *>(wbase);             // [64][IWV]
+  uint32_t *vstile = vtile + WT_V;                                   // [64][SWV]
+  float *wt = reinterpret_cast<float *>(vtile + WT_V + WT_S);        // [64][G]: p * nbar_V
+  float *wq = wt + kWave * G;                                        // [64][G]: p * rnbar_V * kappa_V
+
   const int64_t b = blockIdx.x;
   const int chunk = (int)(b % a.n_chunks);
   const int64_t rest = b / a.n_chunks;
@@ -156,26 +152,27 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   if (t1 > a.n_ctx) t1 = a.n_ctx;
   const int64_t vbase = blk * a.n_ctx;
 
-  // value-phase role of this thread: coordinates o0 .. o0 + CPT - 1, tokens part*TOK ..
-  const int o0 = (tid % NCG) * CPT;
-  const int part = tid / NCG;
+  // value-phase role of this lane: outputs o0 .. o0 + CPT - 1 for tokens part*TOK .. + TOK - 1
+  // of the wavefront's tile
+  const int o0 = (lane % NCG) * CPT;
+  const int part = lane / NCG;
   const bool is_val = o0 < D;
   const int vw0 = is_val ? (o0 * VB) >> 5 : 0;
   const int vsh = is_val ? (o0 * VB) & 31 : 0;
   const int vw1i = (vw0 + 1 < IWV) ? vw0 + 1 : vw0;  // a clamped second word: its bits are masked off when unused
-  const int sj = is_val ? 0 : o0 - D;  // first sketch row (value QJL part)
+  const int sj = is_val ? 0 : o0 - D;                 // first sketch row (value QJL part)
 
-  float mrun[G], lrun[G], acc[CPT][G];
+  // Wavefront-local online softmax: mrun is uniform over the wavefront; lpart is this lane's
+  // share of the running sum (the tokens it scored), acc its share of the outputs.
+  float mrun[G], lpart[G], acc[CPT][G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     mrun[h] = -INFINITY;
-    lrun[h] = 0.0f;
+    lpart[h] = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) acc[c][h] = 0.0f;
   }
 
-  // Records of the next tile are loaded into registers before the current tile's value
-  // phase, so that HBM latency overlaps the arithmetic (the tile loop has barriers).
   struct Rec {
     uint32_t iw[CK::IW];
     uint32_t sw[KSW];
@@ -195,20 +192,22 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
       r.vnw = a.vnorms[v];
     }
   };
+  // Tiles of 64 tokens, wavefront w taking tiles w, w + NW, ...; no workgroup barrier until the
+  // final merge, so wavefronts in the lookup phase overlap wavefronts in the value phase.
   Rec cur;
-  load_rec(t0 + tid, cur);
-  for (int64_t tile = t0; tile < t1; tile += NT) {
-    // ---- phase A: one token per thread: logits, value codes to LDS
-    const int64_t t = tile + tid;
+  load_rec(t0 + (int64_t)wid * kWave + lane, cur);
+  for (int64_t tile = t0 + (int64_t)wid * kWave; tile < t1; tile += (int64_t)NW * kWave) {
+    // ---- phase A: one token per lane: logits, value records to the wavefront's tile
+    const int64_t t = tile + lane;
     const bool valid = t < t1;
     float lg[G];
     float vn = 0.0f, vr = 0.0f;
     if (valid) {
 #pragma unroll
-      for (int i = 0; i < IWV; ++i) vtile[tid * IWV + i] = cur.vw[i];
+      for (int i = 0; i < IWV; ++i) vtile[lane * IWV + i] = cur.vw[i];
       if constexpr (VM > 0) {
 #pragma unroll
-        for (int i = 0; i < SWV; ++i) vstile[tid * SWV + i] = cur.vs[i];
+        for (int i = 0; i < SWV; ++i) vstile[lane * SWV + i] = cur.vs[i];
       }
       vn = f16_bits_to_float(cur.vnw & 0xFFFFu);
       vr = f16_bits_to_float(cur.vnw >> 16) * kappa_v;
@@ -226,40 +225,28 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h) lg[h] = -INFINITY;
     }
-    load_rec(tile + NT + tid, cur);  // the next tile's records (registers of this tile are consumed)
+    load_rec(tile + (int64_t)NW * kWave + lane, cur);  // the next tile's records
+    bool rescale = false;
+    float alpha[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mx = wave_max(lg[h]);
-      if (lane == 0) red_max[wid * G + h] = mx;
+      const float mnew = fmaxf(mrun[h], wave_max(lg[h]));
+      alpha[h] = exp2f(mrun[h] - mnew);  // 0 on the first tile (mrun = -inf), 1 while the max holds
+      rescale |= mnew != mrun[h];
+      mrun[h] = mnew;
+      const float p = valid ? exp2f(lg[h] - mnew) : 0.0f;
+      lpart[h] = fmaf(lpart[h], alpha[h], p);
+      wt[lane * G + h] = p * vn;
+      if constexpr (VM > 0) wq[lane * G + h] = p * vr;
     }
-    __syncthreads();
-    float mnew[G], alpha[G];
+    if (rescale) {  // uniform over the wavefront
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = mrun[h];
-      for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red_max[w * G + h]);
-      mnew[h] = mx;
-      alpha[h] = exp2f(mrun[h] - mx);  // 0 on the first tile (mrun = -inf)
-    }
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float p = valid ? exp2f(lg[h] - mnew[h]) : 0.0f;
-      wt[tid * G + h] = p * vn;
-      if constexpr (VM > 0) wq[tid * G + h] = p * vr;
-      const float ps = wave_sumf(p);
-      if (lane == 0) red_sum[wid * G + h] = ps;
+        for (int c = 0; c < CPT; ++c) acc[c][h] *= alpha[h];
     }
-    __syncthreads();
+    wave_lds_fence();
     // ---- phase B: weighted values; tokens past the end carry weight 0
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float ps = 0.0f;
-      for (int w = 0; w < NW; ++w) ps += red_sum[w * G + h];
-      lrun[h] = fmaf(lrun[h], alpha[h], ps);
-      mrun[h] = mnew[h];
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) acc[c][h] *= alpha[h];
-    }
     const int n0 = part * TOK;
     if (is_val) {
 #pragma unroll 4
@@ -300,44 +287,54 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
         }
       }
     }
-    __syncthreads();
+    wave_lds_fence();  // the next tile overwrites this wavefront's records and weights
   }
 
-  // ---- reduce the TPO slices of each coordinate (in rounds of RCAP slices through the table
-  // space) and write this chunk's partial state
-  float *red = reinterpret_cast<float *>(tabs);  // tables are no longer needed
-  constexpr int OPT = (NOUT * G + NT - 1) / NT;  // outputs per thread
-  float osum[OPT];
+  // ---- merge: the lanes of a coordinate group, then the wavefronts, then write this chunk's
+  // partial state (max, sum, outputs) per query head
 #pragma unroll
-  for (int u = 0; u < OPT; ++u) osum[u] = 0.0f;
-  for (int r0 = 0; r0 < TPO; r0 += RCAP) {
-    __syncthreads();
-    if (part >= r0 && part < r0 + RCAP) {
+  for (int off = NCG; off < kWave; off *= 2)
 #pragma unroll
-      for (int c = 0; c < CPT; ++c)
+    for (int c = 0; c < CPT; ++c)
 #pragma unroll
-        for (int h = 0; h < G; ++h) red[((part - r0) * NOUT + o0 + c) * G + h] = acc[c][h];
-    }
-    __syncthreads();
-    const int nr = (TPO - r0) < RCAP ? (TPO - r0) : RCAP;
+      for (int h = 0; h < G; ++h) acc[c][h] += __shfl_xor(acc[c][h], off, kWave);
+  float lw[G];
 #pragma unroll
-    for (int u = 0; u < OPT; ++u) {
-      const int e = tid + u * NT;
-      if (e < NOUT * G)
-        for (int pp = 0; pp < nr; ++pp) osum[u] += red[pp * NOUT * G + e];
-    }
-  }
+  for (int h = 0; h < G; ++h) lw[h] = wave_sumf(lpart[h]);
+  __syncthreads();  // every wavefront is done with the tables
+  float *mg = reinterpret_cast<float *>(tabs);  // [NW][G] max, [NW][G] sum, [NW][NOUT][G] outputs
+  float *lsum = mg + NW * G;
+  float *outs = lsum + NW * G;
+  if (lane < G) {
 #pragma unroll
-  for (int u = 0; u < OPT; ++u) {
-    const int e = tid + u * NT;
-    if (e < NOUT * G) {
-      const int o = e / G, h = e % G;
-      float *dst = a.part + ((qrow + h) * a.n_chunks + chunk) * (int64_t)(2 + NOUT);
-      dst[2 + o] = osum[u];
-      if (o == 0) {
-        dst[0] = mrun[h];
-        dst[1] = lrun[h];
+    for (int h = 0; h < G; ++h)
+      if (h == lane) {
+        mg[wid * G + h] = mrun[h];
+        lsum[wid * G + h] = lw[h];
       }
+  }
+  if (part == 0) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int h = 0; h < G; ++h) outs[(wid * NOUT + o0 + c) * G + h] = acc[c][h];
+  }
+  __syncthreads();
+  for (int e = tid; e < NOUT * G; e += NT) {
+    const int o = e / G, h = e % G;
+    float m = -INFINITY;
+    for (int w = 0; w < NW; ++w) m = fmaxf(m, mg[w * G + h]);
+    float sacc = 0.0f, lt = 0.0f;
+    for (int w = 0; w < NW; ++w) {
+      const float sc = mg[w * G + h] == -INFINITY ? 0.0f : exp2f(mg[w * G + h] - m);
+      sacc = fmaf(sc, outs[(w * NOUT + o) * G + h], sacc);
+      lt = fmaf(sc, lsum[w * G + h], lt);
+    }
+    float *dst = a.part + ((qrow + h) * a.n_chunks + chunk) * (int64_t)(2 + NOUT);
+    dst[2 + o] = sacc;
+    if (o == 0) {
+      dst[0] = m;
+      dst[1] = lt;
     }
   }
 }
