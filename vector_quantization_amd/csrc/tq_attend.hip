@@ -400,10 +400,12 @@ __global__ __launch_bounds__(256) void attend_combine(CombArgs a) {
 
 // ------------------------------------------------------------------ host side
 
+// Tokens per workgroup: as many as possible (each workgroup builds the key tables once), as
+// long as there are at least 512 workgroups (two per CU) when the context allows it.
 static int att_chunk(const ScoreShape &s) {
   const int64_t pairs = s.n_seq * s.hkv;
-  int ch = pairs >= 2048 ? 8192 : 4096;
-  while (ch > 512 && pairs * ((s.n + ch - 1) / ch) < 1024) ch /= 2;
+  int ch = 16384;
+  while (ch > 512 && pairs * ((s.n + ch - 1) / ch) < 512) ch /= 2;
   return ch;
 }
 
