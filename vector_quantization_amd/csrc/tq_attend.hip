@@ -73,7 +73,9 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   constexpr int SWV = (VM + 31) / 32;
   constexpr int NOUT = D + VM;
   constexpr int NW = NT / kWave;
-  constexpr int CPT = 8;             // consecutive output coordinates per lane (value phase)
+  // consecutive output coordinates per lane in the value phase: 16 where their codes fit one
+  // 64-bit window of the record and the accumulators leave room (at most 128 outputs), else 8
+  constexpr int CPT = (D % 16 == 0 && VM % 16 == 0 && VB * 16 <= 48 && D + VM <= 128) ? 16 : 8;
   constexpr int NCG = NOUT / CPT;    // coordinate groups
   constexpr int TPO = kWave / NCG;   // lanes of a wavefront sharing one coordinate group
   constexpr int TOK = kWave / TPO;   // tokens of a wavefront tile per lane in the value phase
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
       for (int n = n0; n < n0 + TOK; ++n) {
         const uint32_t w0 = vtile[n * IWV + vw0];
         const uint32_t w1 = vtile[n * IWV + vw1i];
-        const uint32_t bits = (uint32_t)(((((uint64_t)w1) << 32) | w0) >> vsh);
+        const uint64_t bits = ((((uint64_t)w1) << 32) | w0) >> vsh;
         float wv[G];
         if constexpr (G == 4) {
           const float4 t4 = *reinterpret_cast<const float4 *>(&wt[n * G]);
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
         }
 #pragma unroll
         for (int c = 0; c < CPT; c += 2) {
-          const float2 cv = cbv2[(bits >> (VB * c)) & (LP - 1)];
+          const float2 cv = cbv2[(uint32_t)(bits >> (VB * c)) & (LP - 1)];
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             acc[c][h] = fmaf(wv[h], cv.x, acc[c][h]);
