@@ -450,6 +450,19 @@ __device__ __forceinline__ void raw_to_f32(const uint4 (&r)[U4], float (&x)[8]) 
   }
 }
 
+// 16-vector tiles per wavefront pass: two share each Pi / S fragment read from LDS.  At d = 128
+// an input that needs a lo part takes one (else the registers spill), and so does a codec
+// without sketch, whose one-tile passes fit 4 wavefronts per SIMD (latency is what bounds it).
+template <int D, int M, int TIN, bool PRE>
+constexpr int enc_tiles() {
+  return (D == 128 && (M == 0 || (!PRE && TIN != TQ_BF16))) ? 1 : 2;
+}
+// wavefronts per workgroup (one workgroup per CU): 16 where the one-tile pass fits 128 VGPRs
+template <int D, int BITS, int M, int TIN, bool PRE>
+constexpr int enc_waves() {
+  return (D == 128 && M == 0 && !PRE && TIN == TQ_BF16 && BITS <= 3) ? 16 : 8;
+}
+
 template <int D, int BITS, int M, int TIN, bool PRE, int NW>
 __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
   constexpr int KS = D / 32;   // k-steps; also 8-coordinate groups u per lane
@@ -457,9 +470,7 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
   constexpr int MT = M / 16;   // 16-row tiles of z
   constexpr int L = 1 << BITS;
   constexpr bool XLO = !PRE && TIN != TQ_BF16;            // input needs a lo part
-  // 16-vector tiles per pass: two share each Pi / S fragment read; one when the input's lo
-  // part would not fit the registers beside them (d = 128 fp16 / fp32 input)
-  constexpr int NV = (D == 128 && XLO) ? 1 : 2;
+  constexpr int NV = enc_tiles<D, M, TIN, PRE>();
   constexpr int U4 = (PRE || TIN == TQ_F32) ? 2 : 1;      // 16-byte chunks per 8 elements
   constexpr int EB = (PRE || TIN == TQ_F32) ? 4 : 2;
   constexpr int IWV = D * BITS / 32;                       // index words per vector
@@ -925,8 +936,8 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
 
 template <int D, int BITS, int M, int TIN, bool PRE>
 static void launch_mfma(const EncArgs &a, hipStream_t st) {
-  constexpr int NW = 8;  // 2 per SIMD: up to 256 VGPRs each
-  constexpr int PER_BLOCK = NW * 16 * ((D == 128 && !PRE && TIN != TQ_BF16) ? 1 : 2);
+  constexpr int NW = enc_waves<D, BITS, M, TIN, PRE>();
+  constexpr int PER_BLOCK = NW * 16 * enc_tiles<D, M, TIN, PRE>();
   int64_t blocks = (a.n + PER_BLOCK - 1) / PER_BLOCK;
   if (blocks > 256) blocks = 256;
   hipLaunchKernelGGL((encode_mfma<D, BITS, M, TIN, PRE, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, a);
