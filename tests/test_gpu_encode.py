@@ -180,6 +180,22 @@ def test_full_mode_per_head_rotations():
     _explained_mismatches(x, lib, ora, gpu, want)
 
 
+@pytest.mark.parametrize("d,bits,m,dtype", [(128, 2, 128, "bfloat16"), (128, 3, 0, "bfloat16"), (64, 3, 64, "float32")])
+def test_full_mode_rotation_blocks(d, bits, m, dtype):
+    # per-block rotations on the MFMA path: 300 blocks of 32 vectors (more blocks than
+    # workgroups), an offset first that skips two blocks, and 40 vectors past the last block
+    # (they take the last rotation)
+    n_rot, vpr, first = 300, 32, 64
+    seeds = [1000 + i for i in range(n_rot)]
+    lib, ora = _codecs(d, bits, m, basis=seeds, vpr=vpr)
+    n = n_rot * vpr - first + 40
+    x = (np.random.default_rng(d + bits).standard_normal((n, d)) * 3.0).astype(np.float32)
+    x = torch.from_numpy(x).to(getattr(torch, dtype)).float().numpy()  # exactly representable input
+    gpu = _gpu_encode(lib, x, pre=False, dtype=getattr(torch, dtype), first=first, tap=True)
+    want = oq.encode(x, ora, first=first, idx_stride=lib.idx_stride, sign_stride=lib.sign_stride, keep=True)
+    _explained_mismatches(x, lib, ora, gpu, want, first=first)
+
+
 def test_encode_offset_first_selects_rotation_block():
     d, bits, m, N = 64, 2, 64, 100
     seeds = [11, 12, 13, 14]

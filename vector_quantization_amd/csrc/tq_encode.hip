@@ -463,7 +463,7 @@ constexpr int enc_waves() {
   return (D == 128 && M == 0 && !PRE && TIN == TQ_BF16 && BITS <= 3) ? 16 : 8;
 }
 
-template <int D, int BITS, int M, int TIN, bool PRE, int NW>
+template <int D, int BITS, int M, int TIN, bool PRE, int NW, bool ROTS>
 __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
   constexpr int KS = D / 32;   // k-steps; also 8-coordinate groups u per lane
   constexpr int CT = D / 16;   // 16-row tiles of y
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
   constexpr int SB = M / 8;         // sign bytes per vector
   static_assert(NV * 16 * IB <= 2 * (D + 2) * 8 && NV * 16 * SB <= 2 * (D + 2) * 8, "staging fits");
   if (tid < L) cbs[tid] = a.centroids[tid];
-  if constexpr (!PRE) build_afrags<D>(a.rot, D, fpi, NW * 64);
+  if constexpr (!PRE && !ROTS) build_afrags<D>(a.rot, D, fpi, NW * 64);
   if constexpr (M > 0) {
     build_afrags<D>(a.sketch, M, fsk, NW * 64);
     if (wid == 0) {
@@ -537,9 +537,8 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
     }
   };
 
-  int64_t v0 = ((int64_t)blockIdx.x * NW + wid) * 16 * NV;
-  load_pass(v0);
-  for (; v0 < a.n; v0 += wstep) {
+  // One pass: vectors v0 .. v0 + 16 NV - 1; the input of the pass at vnext is loaded meanwhile.
+  auto pass = [&](const int64_t v0, const int64_t vnext) {
     // ---- 1. exact fp16 norm of the input (of y in pre-rotated mode)
     uint32_t n16[NV];
 #pragma unroll
@@ -671,7 +670,7 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
     }
     // the next pass's input is in flight while this one finishes (with a sketch, only once the
     // z products are issued: its registers are free then)
-    if constexpr (M == 0) load_pass(v0 + wstep);
+    if constexpr (M == 0) load_pass(vnext);
     if (a.y_tap) {
 #pragma unroll
       for (int t = 0; t < NV; ++t) {
@@ -826,7 +825,7 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
             z[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(l1, rh, z[b][1], 0, 0, 0);
           }
         }
-        if (t == NV - 1) load_pass(v0 + wstep);
+        if (t == NV - 1) load_pass(vnext);
         // bit = 1 - sign bit of z (a z of either zero is undecided, so this is z >= 0 wherever
         // it is used); undecided when |z| <= tau
         uint32_t am[NB];
@@ -931,16 +930,44 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
           for (int w = NB; w < sw_all; ++w) sgnw[v * sw_all + w] = 0u;
       }
     }
+  };
+
+  if constexpr (!ROTS) {
+    int64_t v0 = ((int64_t)blockIdx.x * NW + wid) * 16 * NV;
+    load_pass(v0);
+    for (; v0 < a.n; v0 += wstep) pass(v0, v0 + wstep);
+  } else {
+    // Per-block rotations: a workgroup takes whole rotation blocks (vectors v with
+    // (first + v) / vecs_per_rot = rb; the last rotation also takes everything beyond), rebuilds
+    // the Pi fragments for each, and its wavefronts split the block's passes.  The launcher
+    // guarantees that first and vecs_per_rot are multiples of 32, so no pass straddles blocks.
+    const int64_t vpr = a.vecs_per_rot;
+    const int64_t step = (int64_t)NW * 16 * NV;
+    for (int64_t rb = blockIdx.x;; rb += gridDim.x) {
+      int64_t bs = rb * vpr - a.first;
+      if (bs < 0) bs = 0;
+      if (bs >= a.n) break;
+      const bool last = rb >= a.n_rot - 1;
+      int64_t be = last ? a.n : (rb + 1) * vpr - a.first;
+      if (be > a.n) be = a.n;
+      __syncthreads();  // every wavefront is done with the previous block's fragments
+      build_afrags<D>(a.rot + (last ? a.n_rot - 1 : rb) * (int64_t)D * D, D, fpi, NW * 64);
+      __syncthreads();
+      int64_t v0 = bs + (int64_t)wid * 16 * NV;
+      load_pass(v0);
+      for (; v0 < be; v0 += step) pass(v0, v0 + step < be ? v0 + step : a.n);
+      if (last) break;
+    }
   }
 }
 
-template <int D, int BITS, int M, int TIN, bool PRE>
+template <int D, int BITS, int M, int TIN, bool PRE, bool ROTS = false>
 static void launch_mfma(const EncArgs &a, hipStream_t st) {
-  constexpr int NW = enc_waves<D, BITS, M, TIN, PRE>();
+  constexpr int NW = ROTS ? 8 : enc_waves<D, BITS, M, TIN, PRE>();
   constexpr int PER_BLOCK = NW * 16 * enc_tiles<D, M, TIN, PRE>();
-  int64_t blocks = (a.n + PER_BLOCK - 1) / PER_BLOCK;
+  int64_t blocks = ROTS ? a.n_rot : (a.n + PER_BLOCK - 1) / PER_BLOCK;
   if (blocks > 256) blocks = 256;
-  hipLaunchKernelGGL((encode_mfma<D, BITS, M, TIN, PRE, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((encode_mfma<D, BITS, M, TIN, PRE, NW, ROTS>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, a);
 }
 
 template <int D, int BITS, int M>
@@ -948,7 +975,21 @@ static int launch_enc_dm(const EncArgs &a, int dt, bool pre, hipStream_t st) {
   if constexpr (D == 64 || D == 128) {
     const int eb = dt == TQ_F32 ? 4 : 2;
     const bool vec_ok = ((uintptr_t)a.x % 16 == 0) && ((a.ld_x * eb) % 16 == 0);
-    if ((a.n_rot == 1 || a.vecs_per_rot == 0) && vec_ok) {
+    const bool rots = a.n_rot > 1 && a.vecs_per_rot > 0;
+    // per-block rotations on the MFMA path where the blocks align with passes (and, at d = 128,
+    // for bf16 input, whose registers leave room for the block loop)
+    if (rots && vec_ok && !pre && a.vecs_per_rot % 32 == 0 && a.first % 32 == 0 && (D == 64 || dt == TQ_BF16)) {
+      if constexpr (D == 64) {
+        if (dt == TQ_F32) launch_mfma<D, BITS, M, TQ_F32, false, true>(a, st);
+        else if (dt == TQ_F16) launch_mfma<D, BITS, M, TQ_F16, false, true>(a, st);
+        else if (dt == TQ_BF16) launch_mfma<D, BITS, M, TQ_BF16, false, true>(a, st);
+        else return TQ_EINVAL;
+      } else {
+        launch_mfma<D, BITS, M, TQ_BF16, false, true>(a, st);
+      }
+      return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+    }
+    if (!rots && vec_ok) {
       if (pre) {
         if (dt != TQ_F32) return TQ_EINVAL;
         launch_mfma<D, BITS, M, TQ_F32, true>(a, st);
