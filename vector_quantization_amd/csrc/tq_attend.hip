@@ -228,24 +228,38 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
       for (int h = 0; h < G; ++h) lg[h] = -INFINITY;
     }
     load_rec(tile + (int64_t)NW * kWave + lane, cur);  // the next tile's records
-    bool rescale = false;
+    // The running maxima change only when some lane's logit exceeds them, which is rare after
+    // the first tiles: the wavefront reductions and the rescale run only then (a ballot), and
+    // otherwise the maxima and alpha = 1 are exactly what the reductions would give.
     float alpha[G];
+    bool up = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mnew = fmaxf(mrun[h], wave_max(lg[h]));
-      alpha[h] = exp2f(mrun[h] - mnew);  // 0 on the first tile (mrun = -inf), 1 while the max holds
-      rescale |= mnew != mrun[h];
-      mrun[h] = mnew;
-      const float p = valid ? exp2f(lg[h] - mnew) : 0.0f;
+      alpha[h] = 1.0f;
+      up |= lg[h] > mrun[h];
+    }
+    if (__ballot(up) != 0ull) {  // uniform over the wavefront
+      bool rescale = false;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mnew = fmaxf(mrun[h], wave_max(lg[h]));
+        alpha[h] = exp2f(mrun[h] - mnew);  // 0 on the first tile (mrun = -inf)
+        rescale |= mnew != mrun[h];
+        mrun[h] = mnew;
+      }
+      if (rescale) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) acc[c][h] *= alpha[h];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p = valid ? exp2f(lg[h] - mrun[h]) : 0.0f;
       lpart[h] = fmaf(lpart[h], alpha[h], p);
       wt[lane * G + h] = p * vn;
       if constexpr (VM > 0) wq[lane * G + h] = p * vr;
-    }
-    if (rescale) {  // uniform over the wavefront
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[c][h] *= alpha[h];
     }
     wave_lds_fence();
     // ---- phase B: weighted values; tokens past the end carry weight 0
