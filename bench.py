@@ -79,6 +79,38 @@ def measured_traffic(kernel_names):
     return sum(vals[k] for k in kernel_names)
 
 
+def hbm_ceiling(dev):
+    """Practical HBM ceilings on this part, measured in the same run with plain torch kernels
+    (no code of this library): a read-only stream (sum over 4 GiB) and a device copy (2 GiB read
+    + 2 GiB written), best of three each."""
+    import torch
+
+    x = torch.empty(1 << 30, dtype=torch.float32, device=dev).fill_(1.0)
+    y = torch.empty(1 << 29, dtype=torch.float32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+
+    t_read = best(lambda: x.sum())
+    t_copy = best(lambda: y.copy_(x[: 1 << 29]))
+    res = {"read_stream_GBps": round(x.numel() * 4 / (t_read * 1e-3) / 1e9, 1),
+           "copy_GBps": round(2 * y.numel() * 4 / (t_copy * 1e-3) / 1e9, 1),
+           "kernels": "torch sum over 4 GiB fp32; torch copy of 2 GiB"}
+    del x, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, K, q, seed_rot, seed_sk):
     """Time the oracle's scoring of one (layer, batch) slice: all kv heads, full context."""
     import numpy as np
@@ -397,6 +429,7 @@ def main():
                      "kernel": " + ".join(SCORE_KERNELS) + " (one tq_scores call)"},
         "gpu": torch.cuda.get_device_name(0),
     }
+    res["hbm_ceiling"] = hbm_ceiling(dev)
     if a.calibrate:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
