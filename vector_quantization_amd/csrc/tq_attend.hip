@@ -91,9 +91,8 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   constexpr int WAVE_BYTES = ((WT_V + WT_S) * 4 + kWave * G * 4 * (VM > 0 ? 2 : 1) + 15) / 16 * 16;
   constexpr int O_CBK = O_WAVE + NW * WAVE_BYTES;
   constexpr int O_CBV = O_CBK + (1 << KB) * 4;
-  constexpr int O_SCM = O_CBV + LV * 4;
-  constexpr int O_SCQ = O_SCM + G * 4;
-  constexpr int O_QT = O_SCQ + G * 4;
+  constexpr int O_SC = O_CBV + LV * 4;
+  constexpr int O_QT = O_SC + 4 * G * 4;
   constexpr int O_QH = O_QT + G * D * 4;
   constexpr int O_TABS = (O_QH + G * (KM > 0 ? KM : 1) * 4 + 15) / 16 * 16;
   constexpr int MERGE_BYTES = NW * (NOUT + 2) * G * 4;
@@ -103,8 +102,7 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   float2 *cbv2 = reinterpret_cast<float2 *>(arena + O_CBV2);  // (c[a], c[b]) for (b << VB) | a
   float *cbk = reinterpret_cast<float *>(arena + O_CBK);
   float *cbv = reinterpret_cast<float *>(arena + O_CBV);
-  float *scm = reinterpret_cast<float *>(arena + O_SCM);
-  float *scq = reinterpret_cast<float *>(arena + O_SCQ);
+  float *sc = reinterpret_cast<float *>(arena + O_SC);  // table scales (block_table_scales)
   float *qt = reinterpret_cast<float *>(arena + O_QT);
   float *qh = reinterpret_cast<float *>(arena + O_QH);
   uint8_t *tabs = arena + O_TABS;
@@ -134,17 +132,11 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   for (int e = tid; e < LP; e += NT) cbv2[e] = make_float2(a.vcent[e & (LV - 1)], a.vcent[e >> VB]);
   __syncthreads();
   HeadScales<G> hs;
-  {
-    const float cmax = fmaxf(fabsf(cbk[0]), fabsf(cbk[(1 << KB) - 1]));
-    float sm[G], sq[G];
-    table_scales<D, KB, KM, G>(qt, qh, cmax, sm, sq, hs);
-    if (tid < G) {
-      scm[tid] = sm[tid];
-      scq[tid] = sq[tid];
-    }
-  }
-  __syncthreads();
-  build_luts<D, KB, KM, G, NT>(tabs, tabs + CK::MSE_BYTES, qt, qh, cbk, scm, scq);
+  block_table_scales<D, KB, KM, G>(qt, qh, cbk, sc, hs);
+  // the half-table builder's scratch aliases the wavefronts' tile area, unused until the tiles
+  constexpr bool HALF = lut_half_bytes<D, KB, KM, G>() <= NW * WAVE_BYTES;
+  build_luts<D, KB, KM, G, NT>(tabs, tabs + CK::MSE_BYTES, qt, qh, cbk, sc, sc + G,
+                               HALF ? reinterpret_cast<float *>(arena + O_WAVE) : nullptr);
   __syncthreads();
 
   const float kappa_k = KM > 0 ? 1.2533141373155003f / (float)(KM > 0 ? KM : 1) : 0.0f;

@@ -49,21 +49,112 @@ struct HeadScales {
   float inv_q[G];
 };
 
-// Four scaled values -> four 16-bit fixed-point integers (round to nearest), packed.
+// Four scaled values -> four 16-bit fixed-point integers (round to nearest, clamped to
+// [-32767, 32767]), packed: v_cvt_pk_i16_i32 saturates at 32767, the explicit lower clamp keeps
+// -32768 out.
 __device__ __forceinline__ uint2 pack_i16x4(const float (&v)[4]) {
-  uint32_t q[4];
+  int q[4];
 #pragma unroll
-  for (int h = 0; h < 4; ++h) q[h] = (uint32_t)(int)rintf(fminf(fmaxf(v[h], -32767.0f), 32767.0f)) & 0xFFFFu;
-  return make_uint2(q[0] | (q[1] << 16), q[2] | (q[3] << 16));
+  for (int h = 0; h < 4; ++h) q[h] = (int)__builtin_rintf(fmaxf(v[h], -32767.0f));
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(q[0], q[1])),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(q[2], q[3])));
+}
+
+// Store one table entry of G heads (already scaled) at index e.
+template <int G>
+__device__ __forceinline__ void store_entry(uint8_t *tab, int e, const float (&v)[G]) {
+  if constexpr (G == 1) {
+    reinterpret_cast<float *>(tab)[e] = v[0];
+  } else if constexpr (G == 2) {
+    reinterpret_cast<float2 *>(tab)[e] = make_float2(v[0], v[1]);
+  } else {
+    reinterpret_cast<uint2 *>(tab)[e] = pack_i16x4(v);
+  }
+}
+
+// LDS scratch of the half-table builder: for every index group and sign byte, the tables of its
+// low and high halves (HS = 2^(GB/2) entries for an index group, 16 for a sign byte), G floats
+// per entry.
+template <int D, int BITS, int M, int G>
+constexpr int lut_half_bytes() {
+  using C = Lut<D, BITS, M, G>;
+  return (C::NG * 2 * (1 << (C::GB / 2)) + C::NQ * 2 * 16) * G * 4;
 }
 
 // Build the tables of G query heads in LDS.  qt [G][D] and qh [G][M] (fp32) and the codebook
 // cb [L] are in LDS; scale_m/scale_q are the per-head table scales (1 for fp32 tables).
 // All threads of the block participate; the caller synchronises afterwards.
+//
+// With LDS scratch `half` (lut_half_bytes, 16-byte aligned), every entry is the sum of the
+// entries of its two half-groups -- T_p[beta] = Tlo_p[beta mod HS] + Thi_p[beta / HS], and the
+// same for the sign bytes -- which are built first.  This is the same sum of the same products,
+// grouped in two, and costs two reads and one add per head instead of CPG (or 8) products.
+// With half == nullptr each entry is summed directly.
 template <int D, int BITS, int M, int G, int NT>
 __device__ void build_luts(uint8_t *mse, uint8_t *qjl, const float *qt, const float *qh, const float *cb,
-                           const float *scale_m, const float *scale_q) {
+                           const float *scale_m, const float *scale_q, float *half = nullptr) {
   using C = Lut<D, BITS, M, G>;
+  if (half != nullptr) {
+    constexpr int HB = C::GB / 2;          // bits per half-group
+    constexpr int HS = 1 << HB;            // entries per half table
+    constexpr int HC = C::CPG / 2;         // coordinates per half-group
+    static_assert(C::CPG % 2 == 0, "index groups split into two halves");
+    constexpr int NHM = C::NG * 2 * HS;    // index half entries: [p][half][x]
+    constexpr int NHQ = C::NQ * 2 * 16;    // sign half entries: [p][half][x]
+    float *hm = half, *hq = half + NHM * G;
+    for (int e = threadIdx.x; e < NHM + NHQ; e += NT) {
+      float v[G];
+      if (e < NHM) {
+        const int p = e / (2 * HS), hf = (e / HS) & 1, x = e % HS;
+        const int i0 = C::CPG * p + HC * hf;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int t = 0; t < HC; ++t) acc = fmaf(qt[h * D + i0 + t], cb[(x >> (BITS * t)) & (C::L - 1)], acc);
+          v[h] = acc;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) hm[e * G + h] = v[h];
+      } else if constexpr (M > 0) {
+        const int f = e - NHM;
+        const int p = f >> 5, hf = (f >> 4) & 1, x = f & 15;
+        const int j0 = 8 * p + 4 * hf;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float y = qh[h * M + j0 + t];
+            acc += ((x >> t) & 1) ? y : -y;
+          }
+          hq[f * G + h] = acc;
+        }
+      }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < C::NG * C::TS; e += NT) {
+      const int p = e / C::TS, beta = e % C::TS;
+      const float *lo = hm + ((p * 2) * HS + (beta & (HS - 1))) * G;
+      const float *hi = hm + ((p * 2 + 1) * HS + (beta >> HB)) * G;
+      float v[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) v[h] = (lo[h] + hi[h]) * scale_m[h];
+      store_entry<G>(mse, e, v);
+    }
+    if constexpr (M > 0) {
+      for (int e = threadIdx.x; e < C::NQ * 256; e += NT) {
+        const int p = e >> 8, beta = e & 255;
+        const float *lo = hq + ((p * 2) * 16 + (beta & 15)) * G;
+        const float *hi = hq + ((p * 2 + 1) * 16 + (beta >> 4)) * G;
+        float v[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) v[h] = (lo[h] + hi[h]) * scale_q[h];
+        store_entry<G>(qjl, e, v);
+      }
+    }
+    return;
+  }
   for (int e = threadIdx.x; e < C::NG * C::TS; e += NT) {
     const int p = e / C::TS, beta = e % C::TS;
     float v[G];
@@ -119,31 +210,48 @@ __device__ void table_scales(const float *qt, const float *qh, float cmax, float
                              HeadScales<G> &hs) {
   using C = Lut<D, BITS, M, G>;
   const int lane = lane_id();
+  // per-lane partial maxima of every head first, then all 2G wavefront reductions interleaved
+  float pa[G], pb[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float sm = 1.0f, sq = 1.0f, im = 1.0f, iq = 1.0f;
+    pa[h] = pb[h] = 0.0f;
     if constexpr (C::I16) {
-      float a = 0.0f;
       for (int p = lane; p < C::NG; p += kWave) {
         float t = 0.0f;
 #pragma unroll
         for (int u = 0; u < C::CPG; ++u) t += fabsf(qt[h * D + C::CPG * p + u]);
-        a = fmaxf(a, t);
+        pa[h] = fmaxf(pa[h], t);
       }
-      a = wave_max(a) * cmax;
+      if constexpr (M > 0) {
+        for (int p = lane; p < C::NQ; p += kWave) {
+          float t = 0.0f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) t += fabsf(qh[h * M + 8 * p + u]);
+          pb[h] = fmaxf(pb[h], t);
+        }
+      }
+    }
+  }
+  if constexpr (C::I16) {
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        pa[h] = fmaxf(pa[h], __shfl_xor(pa[h], off, kWave));
+        if constexpr (M > 0) pb[h] = fmaxf(pb[h], __shfl_xor(pb[h], off, kWave));
+      }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float sm = 1.0f, sq = 1.0f, im = 1.0f, iq = 1.0f;
+    if constexpr (C::I16) {
+      const float a = pa[h] * cmax;
       if (a > 0.0f) {
         sm = 32767.0f / a;
         im = a / 32767.0f;
       }
       if constexpr (M > 0) {
-        float b = 0.0f;
-        for (int p = lane; p < C::NQ; p += kWave) {
-          float t = 0.0f;
-#pragma unroll
-          for (int u = 0; u < 8; ++u) t += fabsf(qh[h * M + 8 * p + u]);
-          b = fmaxf(b, t);
-        }
-        b = wave_max(b);
+        const float b = pb[h];
         if (b > 0.0f) {
           sq = 32767.0f / b;
           iq = b / 32767.0f;
@@ -154,6 +262,36 @@ __device__ void table_scales(const float *qt, const float *qh, float cmax, float
     scale_q[h] = sq;
     hs.inv_m[h] = im;
     hs.inv_q[h] = iq;
+  }
+}
+
+// The per-head scales for a workgroup: wavefront 0 computes them (table_scales) and publishes
+// them in LDS as sc[4G] = {scale_m[G], scale_q[G], inv_m[G], inv_q[G]}; after the barrier every
+// thread takes its HeadScales from there.  One wavefront instead of all of them keeps the LDS
+// reads and shuffles of the reductions off the other wavefronts.  Ends synchronised.
+template <int D, int BITS, int M, int G>
+__device__ void block_table_scales(const float *qt, const float *qh, const float *cb, float *sc, HeadScales<G> &hs) {
+  using C = Lut<D, BITS, M, G>;
+  if (threadIdx.x < kWave) {
+    const float cmax = fmaxf(fabsf(cb[0]), fabsf(cb[C::L - 1]));
+    float sm[G], sq[G];
+    HeadScales<G> h0;
+    table_scales<D, BITS, M, G>(qt, qh, cmax, sm, sq, h0);
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sc[h] = sm[h];
+        sc[G + h] = sq[h];
+        sc[2 * G + h] = h0.inv_m[h];
+        sc[3 * G + h] = h0.inv_q[h];
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    hs.inv_m[h] = sc[2 * G + h];
+    hs.inv_q[h] = sc[3 * G + h];
   }
 }
 

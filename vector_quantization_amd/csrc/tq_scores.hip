@@ -195,49 +195,101 @@ __device__ __forceinline__ void load_words(const uint8_t *p, uint32_t (&w)[W]) {
 
 // q~ = R q and q^ = S q~ for the G consecutive query heads at q (fp32, global), by the whole
 // workgroup: KSL threads per output row each sum KPER products, then combine by shuffles
-// (KSL is a power of two, so a row's threads are aligned lanes of one wavefront).  qs is LDS
-// scratch of G * D floats; qt [G][D] and qh [G][M] are LDS outputs.  Ends synchronised.
+// (KSL is a power of two, so a row's threads are aligned lanes of one wavefront).
+// issue() requests every global operand at once -- the queries and, where each thread owns one
+// (row, slice) of both products, its KPER weights of R and of S, kept in registers -- so that
+// the prologue waits for one memory latency instead of a chain of them.  finish() computes:
+// qs is LDS scratch of G * D floats; qt [G][D] and qh [G][M] are LDS outputs.  It ends
+// synchronised.
 template <int D, int M, int G, int NT>
-__device__ void block_prep_queries(const float *q, const float *R, const float *S, float *qs, float *qt, float *qh) {
-  constexpr int ROWS = D > M ? D : M;
-  constexpr int KSL = (NT / ROWS >= 16) ? 16 : (NT / ROWS >= 8) ? 8 : (NT / ROWS >= 4) ? 4 : (NT / ROWS >= 2) ? 2 : 1;
-  constexpr int KPER = (D + KSL - 1) / KSL;
-  const int tid = threadIdx.x;
-  for (int e = tid; e < G * D; e += NT) qs[e] = q[e];
-  __syncthreads();
-  auto matvec = [&](const float *W, int rows, const float *in, float *out) {
-    for (int r0 = 0; r0 < rows; r0 += NT / KSL) {
-      const int r = r0 + tid / KSL, sl = tid % KSL;
-      float acc[G];
+struct QueryPrep {
+  static constexpr int ROWS = D > M ? D : M;
+  static constexpr int KSL = (NT / ROWS >= 16) ? 16 : (NT / ROWS >= 8) ? 8 : (NT / ROWS >= 4) ? 4 : (NT / ROWS >= 2) ? 2 : 1;
+  static constexpr int KPER = (D + KSL - 1) / KSL;
+  static constexpr bool REG = NT / KSL >= ROWS && KPER * KSL == D && KPER <= 16;
+  static constexpr int NWR = REG ? KPER : 1;
+  static constexpr int QN = (G * D + NT - 1) / NT;
+  float qv[QN];
+  float wr[NWR], wsk[NWR];
+  const float *R, *S;
+
+  __device__ __forceinline__ void issue(const float *q, const float *R_, const float *S_) {
+    R = R_;
+    S = S_;
+    const int tid = threadIdx.x;
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = 0.0f;
-      if (r < rows) {
-#pragma unroll 4
-        for (int kk = 0; kk < KPER; ++kk) {
-          const int k = sl * KPER + kk;
-          if (k < D) {
-            const float w = W[(int64_t)r * D + k];
+    for (int i = 0; i < QN; ++i) {
+      const int e = tid + i * NT;
+      qv[i] = e < G * D ? q[e] : 0.0f;
+    }
+    if constexpr (REG) {
+      const int r = tid / KSL, sl = tid % KSL;
 #pragma unroll
-            for (int h = 0; h < G; ++h) acc[h] = fmaf(w, in[h * D + k], acc[h]);
-          }
-        }
+      for (int kk = 0; kk < KPER; ++kk) {
+        wr[kk] = r < D ? R[(int64_t)r * D + sl * KPER + kk] : 0.0f;
+        if constexpr (M > 0) wsk[kk] = r < M ? S[(int64_t)r * D + sl * KPER + kk] : 0.0f;
       }
+    }
+  }
+
+  __device__ void finish(float *qs, float *qt, float *qh) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < QN; ++i) {
+      const int e = tid + i * NT;
+      if (e < G * D) qs[e] = qv[i];
+    }
+    __syncthreads();
+    auto reduce_store = [&](float(&acc)[G], int r, int rows, float *out) {
 #pragma unroll
       for (int off = KSL / 2; off >= 1; off >>= 1)
 #pragma unroll
         for (int h = 0; h < G; ++h) acc[h] += __shfl_xor(acc[h], off, kWave);
-      if (r < rows && sl == 0)
+      if (r < rows && tid % KSL == 0)
 #pragma unroll
         for (int h = 0; h < G; ++h) out[h * rows + r] = acc[h];
-    }
-  };
-  matvec(R, D, qs, qt);
-  __syncthreads();
-  if constexpr (M > 0) {
-    matvec(S, M, qt, qh);
+    };
+    auto matvec_reg = [&](const float(&w)[NWR], int rows, const float *in, float *out) {
+      const int r = tid / KSL, sl = tid % KSL;
+      float acc[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < KPER; ++kk)
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = fmaf(w[kk], in[h * D + sl * KPER + kk], acc[h]);
+      reduce_store(acc, r, rows, out);
+    };
+    auto matvec = [&](const float *W, int rows, const float *in, float *out) {
+      for (int r0 = 0; r0 < rows; r0 += NT / KSL) {
+        const int r = r0 + tid / KSL, sl = tid % KSL;
+        float acc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = 0.0f;
+        if (r < rows) {
+#pragma unroll 4
+          for (int kk = 0; kk < KPER; ++kk) {
+            const int k = sl * KPER + kk;
+            if (k < D) {
+              const float w = W[(int64_t)r * D + k];
+#pragma unroll
+              for (int h = 0; h < G; ++h) acc[h] = fmaf(w, in[h * D + k], acc[h]);
+            }
+          }
+        }
+        reduce_store(acc, r, rows, out);
+      }
+    };
+    if constexpr (REG) matvec_reg(wr, D, qs, qt);
+    else matvec(R, D, qs, qt);
     __syncthreads();
+    if constexpr (M > 0) {
+      if constexpr (REG) matvec_reg(wsk, M, qt, qh);
+      else matvec(S, M, qt, qh);
+      __syncthreads();
+    }
   }
-}
+};
 
 template <int D, int BITS, int M, int G, int NT>
 __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
@@ -248,7 +300,10 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
   __shared__ float qt[G * D];
   __shared__ float qh[G * (M > 0 ? M : 1)];
   __shared__ float cb[C::L];
-  __shared__ float scm[G], scq[G];
+  __shared__ float sc[4 * G];
+  // scratch of the half-table builder where LDS has room for it
+  constexpr bool HALF = C::BYTES + lut_half_bytes<D, BITS, M, G>() + G * (2 * D + M) * 4 + 512 <= 160 * 1024;
+  __shared__ __align__(16) float halfs[HALF ? lut_half_bytes<D, BITS, M, G>() / 4 : 4];
 
   const int64_t b = blockIdx.x;
   const int chunk = (int)(b % a.n_chunks);
@@ -261,25 +316,18 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
   const int h0 = kvh * g + sub * G;  // first query head of this group
   const int64_t qrow = s * a.hq + h0;
 
-  if (threadIdx.x < C::L) cb[threadIdx.x] = a.centroids[threadIdx.x];
   int64_t rid = 0;  // the rotation of this kv block
   if (a.n_rot > 1 && a.vecs_per_rot > 0) {
     rid = (blk * a.n_keys) / a.vecs_per_rot;
     if (rid > a.n_rot - 1) rid = a.n_rot - 1;
   }
-  block_prep_queries<D, M, G, NT>(a.q + qrow * D, a.rot + rid * (int64_t)D * D, a.sketch, qs, qt, qh);
+  QueryPrep<D, M, G, NT> prep;
+  prep.issue(a.q + qrow * D, a.rot + rid * (int64_t)D * D, a.sketch);
+  if (threadIdx.x < C::L) cb[threadIdx.x] = a.centroids[threadIdx.x];
+  prep.finish(qs, qt, qh);
   HeadScales<G> hs;
-  {
-    const float cmax = fmaxf(fabsf(cb[0]), fabsf(cb[C::L - 1]));
-    float sm[G], sq[G];
-    table_scales<D, BITS, M, G>(qt, qh, cmax, sm, sq, hs);
-    if (threadIdx.x < G) {
-      scm[threadIdx.x] = sm[threadIdx.x];
-      scq[threadIdx.x] = sq[threadIdx.x];
-    }
-  }
-  __syncthreads();
-  build_luts<D, BITS, M, G, NT>(tabs, tabs + C::MSE_BYTES, qt, qh, cb, scm, scq);
+  block_table_scales<D, BITS, M, G>(qt, qh, cb, sc, hs);
+  build_luts<D, BITS, M, G, NT>(tabs, tabs + C::MSE_BYTES, qt, qh, cb, sc, sc + G, HALF ? halfs : nullptr);
   __syncthreads();
 
   const float kappa = M > 0 ? 1.2533141373155003f / (float)(M > 0 ? M : 1) : 0.0f;  // sqrt(pi/2)/m

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(NT) void search_scan(SearchArgs a) {
   __shared__ float qt[G * D];
   __shared__ float qh[G * (M > 0 ? M : 1)];
   __shared__ float cb[C::L];
-  __shared__ float scm[G], scq[G];
+  __shared__ float sc[4 * G];
 
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   const int slice = (int)(blockIdx.x % a.n_slices);
@@ -112,17 +112,8 @@ __global__ __launch_bounds__(NT) void search_scan(SearchArgs a) {
   if (tid < C::L) cb[tid] = a.centroids[tid];
   __syncthreads();
   HeadScales<G> hs;
-  {
-    const float cmax = fmaxf(fabsf(cb[0]), fabsf(cb[C::L - 1]));
-    float sm[G], sq[G];
-    table_scales<D, BITS, M, G>(qt, qh, cmax, sm, sq, hs);
-    if (tid < G) {
-      scm[tid] = sm[tid];
-      scq[tid] = sq[tid];
-    }
-  }
-  __syncthreads();
-  build_luts<D, BITS, M, G, NT>(tabs, tabs + C::MSE_BYTES, qt, qh, cb, scm, scq);
+  block_table_scales<D, BITS, M, G>(qt, qh, cb, sc, hs);
+  build_luts<D, BITS, M, G, NT>(tabs, tabs + C::MSE_BYTES, qt, qh, cb, sc, sc + G);
   __syncthreads();
 
   const int k = a.k;
