@@ -210,7 +210,7 @@ __device__ void table_scales(const float *qt, const float *qh, float cmax, float
                              HeadScales<G> &hs) {
   using C = Lut<D, BITS, M, G>;
   const int lane = lane_id();
-  // per-lane partial maxima of every head first, then all 2G wavefront reductions interleaved
+  // per-lane partial maxima of every head first, then the 2G wavefront reductions (DPP, no LDS)
   float pa[G], pb[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -234,12 +234,10 @@ __device__ void table_scales(const float *qt, const float *qh, float cmax, float
   }
   if constexpr (C::I16) {
 #pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1)
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        pa[h] = fmaxf(pa[h], __shfl_xor(pa[h], off, kWave));
-        if constexpr (M > 0) pb[h] = fmaxf(pb[h], __shfl_xor(pb[h], off, kWave));
-      }
+    for (int h = 0; h < G; ++h) {
+      pa[h] = wave_max_dpp(pa[h]);
+      if constexpr (M > 0) pb[h] = wave_max_dpp(pb[h]);
+    }
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {

@@ -242,9 +242,7 @@ struct QueryPrep {
     __syncthreads();
     auto reduce_store = [&](float(&acc)[G], int r, int rows, float *out) {
 #pragma unroll
-      for (int off = KSL / 2; off >= 1; off >>= 1)
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] += __shfl_xor(acc[h], off, kWave);
+      for (int h = 0; h < G; ++h) acc[h] = group_sum_dpp<KSL>(acc[h]);
       if (r < rows && tid % KSL == 0)
 #pragma unroll
         for (int h = 0; h < G; ++h) out[h * rows + r] = acc[h];
