@@ -52,6 +52,8 @@ def test_tiny_workload():
     (128, 3, 0, 8, 8, 2, 513),         # MSE only
     (200, 2, 200, 1, 1, 3, 3001),      # search shape
     (64, 4, 64, 8, 2, 1, 300),
+    (128, 3, 128, 8, 2, 1, 1500),      # four heads per lookup, 512-thread workgroups
+    (128, 2, 0, 4, 1, 2, 900),         # four heads per lookup without a sketch, 512 threads
 ])
 def test_scores_match_oracle(d, bits, m, hq, hkv, S, N):
     say("scores", d, bits, m, hq, hkv, S, N)

@@ -289,6 +289,31 @@ struct QueryPrep {
   }
 };
 
+// LDS of a score workgroup besides the tables: the queries, their two transforms, the
+// codebook and the scales.
+template <int D, int BITS, int M, int G>
+constexpr int score_lds_extra() {
+  return (G * (2 * D + (M > 0 ? M : 1)) + (1 << BITS) + 4 * G) * 4 + 256;
+}
+
+// Threads per workgroup: tables that leave room for one workgroup per CU take 1024 threads;
+// where two fit, 512 (the same 16 wavefronts per CU, twice the registers each); smaller
+// tables 256.
+template <int D, int BITS, int M, int G>
+constexpr int score_threads() {
+  constexpr int base = Lut<D, BITS, M, G>::BYTES + score_lds_extra<D, BITS, M, G>();
+  return base > 80 * 1024 ? 1024 : (Lut<D, BITS, M, G>::BYTES > 48 * 1024 ? 512 : 256);
+}
+
+// The half-table builder's scratch, where it costs no workgroups per CU.
+template <int D, int BITS, int M, int G>
+constexpr bool score_half_scratch() {
+  constexpr int base = Lut<D, BITS, M, G>::BYTES + score_lds_extra<D, BITS, M, G>();
+  constexpr int with = base + lut_half_bytes<D, BITS, M, G>();
+  constexpr int lds = 160 * 1024;
+  return with <= lds && lds / with == lds / base;
+}
+
 template <int D, int BITS, int M, int G, int NT>
 __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
   using C = Lut<D, BITS, M, G>;
@@ -300,7 +325,7 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
   __shared__ float cb[C::L];
   __shared__ float sc[4 * G];
   // scratch of the half-table builder where LDS has room for it
-  constexpr bool HALF = C::BYTES + lut_half_bytes<D, BITS, M, G>() + G * (2 * D + M) * 4 + 512 <= 160 * 1024;
+  constexpr bool HALF = score_half_scratch<D, BITS, M, G>();
   __shared__ __align__(16) float halfs[HALF ? lut_half_bytes<D, BITS, M, G>() / 4 : 4];
 
   const int64_t b = blockIdx.x;
@@ -386,7 +411,7 @@ static int pick_g(int g) {
 
 template <int D, int BITS, int M, int G>
 static int launch_score_g(const ScoreArgs &a0, const ScoreShape &s, hipStream_t st) {
-  constexpr int NT = (Lut<D, BITS, M, G>::BYTES > 48 * 1024) ? 1024 : 256;
+  constexpr int NT = score_threads<D, BITS, M, G>();
   ScoreArgs a = a0;
   a.nsub = (s.hq / s.hkv) / G;
   a.chunk = 32768;
