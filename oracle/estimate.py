@@ -26,7 +26,7 @@ import math
 import numpy as np
 
 from .codec import Codec
-from .quantize import Codes, unpack
+from .quantize import Codes, append, rope, unpack
 
 
 def qjl_scale(m: int) -> float:
@@ -110,6 +110,54 @@ def attend(q, kcodes, vcodes, kcodec, vcodec, n_ctx, hkv, scale):
             v = dequantize(_slice(vcodes, blk * n_ctx, (blk + 1) * n_ctx), vcodec, blk * n_ctx)
             out[s, kvh * g:(kvh + 1) * g] = p[s, kvh * g:(kvh + 1) * g] @ v
     return out
+
+
+def attend_lens(q, kcodes, vcodes, kcodec, vcodec, cap, lens, hkv, scale):
+    """Decode attention [S, Hq, d] over a cache of capacity ``cap`` per (sequence, kv head)
+    ([S][Hkv][cap]) in which sequence s holds its first lens[s] tokens: softmax over those
+    tokens only, times their dequantised V."""
+    S, hq, d = q.shape
+    g = hq // hkv
+    out = np.empty((S, hq, vcodec.d), dtype=np.float64)
+    for s in range(S):
+        n = int(lens[s])
+        for kvh in range(hkv):
+            blk = s * hkv + kvh
+            a, b = blk * cap, blk * cap + n
+            rot = int(kcodec.rot_index(1, a)[0])
+            kc = _slice(kcodes, a, b)
+            v = dequantize(_slice(vcodes, a, b), vcodec, a)
+            for h in range(kvh * g, (kvh + 1) * g):
+                p = softmax(scale * scores_one(q[s, h], kc, kcodec, rot))
+                out[s, h] = p @ v
+    return out
+
+
+def decode_step(q, k_new, v_new, kcodes, vcodes, kcodec, vcodec, cap, pos, rope_base, hkv, scale):
+    """One decode step over a growing cache [S][Hkv][cap]: sequence s appends its new key (RoPE
+    at pos[s]) and value at slot pos[s], then its queries (RoPE at pos[s]) attend over tokens
+    0 .. pos[s].  Returns (outputs [S, Hq, d], updated K codes, updated V codes); the inputs
+    are not modified."""
+    S, hq, d = q.shape
+    pos = np.asarray(pos, dtype=np.int64)
+    slots = ((np.arange(S)[:, None] * hkv + np.arange(hkv)[None, :]) * cap + pos[:, None]).reshape(-1)
+    kpos = np.repeat(pos, hkv)
+    out_codes = []
+    for codes, codec, x, base in ((kcodes, kcodec, k_new, rope_base), (vcodes, vcodec, v_new, 0.0)):
+        new = append(np.asarray(x).reshape(S * hkv, codec.d), codec, slots, kpos, base,
+                     idx_stride=codes.idx.shape[1],
+                     sign_stride=None if codes.sign is None else codes.sign.shape[1])
+        c2 = Codes(codes.idx.copy(), None if codes.sign is None else codes.sign.copy(), codes.norms.copy())
+        c2.idx[slots] = new.idx
+        if c2.sign is not None:
+            c2.sign[slots] = new.sign
+        c2.norms[slots] = new.norms
+        out_codes.append(c2)
+    qr = np.asarray(q, dtype=np.float64)
+    if rope_base > 0:
+        qr = rope(qr.reshape(S * hq, d), np.repeat(pos, hq), rope_base).reshape(S, hq, d)
+    out = attend_lens(qr, out_codes[0], out_codes[1], kcodec, vcodec, cap, pos + 1, hkv, scale)
+    return out, out_codes[0], out_codes[1]
 
 
 def attend_materialised(q, kcodes, vcodes, kcodec, vcodec, n_ctx, hkv, scale):

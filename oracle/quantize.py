@@ -203,14 +203,54 @@ def encode(x: np.ndarray, codec: Codec, pre_rotated: bool = False, first: int = 
     x = np.asarray(x)
     if x.ndim != 2 or x.shape[1] != codec.d:
         raise ValueError("x must be [n, d]")
-    n = x.shape[0]
     if pre_rotated:
         y = np.asarray(x, dtype=np.float32)
         norm_src = y
     else:
         y = rotate(x, codec, first)
         norm_src = x
-    n16 = f16_norm_bits(norm_src)
+    return encode_rotated(y, f16_norm_bits(norm_src), codec, idx_stride, sign_stride, keep)
+
+
+def rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """Rotary position embedding in fp64 (TurboESM summary, "Metodología" A: applied to the keys
+    (and queries) before the orthogonal rotation).  The pages do not spell out the pairing; the
+    reading taken is the half-split one: coordinate i < d/2 turns with coordinate i + d/2 by the
+    angle pos * base^(-2i/d)."""
+    x64 = np.asarray(x, dtype=np.float64)
+    d = x64.shape[-1]
+    half = d // 2
+    inv = np.power(float(base), -2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x64[:, :half], x64[:, half:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=1)
+
+
+def append(x: np.ndarray, codec: Codec, slots: np.ndarray, pos: np.ndarray, rope_base: float,
+           idx_stride: Optional[int] = None, sign_stride: Optional[int] = None, keep: bool = False) -> Codes:
+    """Codes of new vectors appended to a growing cache (7minutos.es walkthrough, "Etapa 1": the
+    indices stay in the cache until the token is evicted; TurboESM summary, "Metodología" A:
+    RoPE first, then the rotation).  Row k goes to cache slot ``slots[k]`` (which selects the
+    per-block rotation) at position ``pos[k]``; with rope_base > 0 the rotation sees
+    RoPE(x, pos) in fp64: y = fl32(Pi RoPE(x)).  The stored norm is that of x itself -- RoPE is
+    orthogonal, so this is the norm of the rotated input as well."""
+    x = np.asarray(x)
+    x64 = np.asarray(x, dtype=np.float64)
+    xr = rope(x64, pos, rope_base) if rope_base > 0 else x64
+    rid = np.array([codec.rot_index(1, int(sl))[0] for sl in slots], dtype=np.int64)
+    y = np.empty(x64.shape, dtype=np.float32)
+    for r in np.unique(rid):
+        sel = rid == r
+        y[sel] = (xr[sel] @ codec.rot[r].astype(np.float64).T).astype(np.float32)
+    return encode_rotated(y, f16_norm_bits(x), codec, idx_stride, sign_stride, keep)
+
+
+def encode_rotated(y: np.ndarray, n16: np.ndarray, codec: Codec, idx_stride: Optional[int] = None,
+                   sign_stride: Optional[int] = None, keep: bool = False) -> Codes:
+    """The steps after the rotation: indices against the thresholds scaled by the stored norm,
+    residual, its norm and the exact signs of S r; y is fp32, n16 the fp16 bits of the norm."""
+    y = np.asarray(y, dtype=np.float32)
     nbar = f16_value(n16).astype(np.float32)  # exact: fp16 values are fp32 values
 
     thr = nbar[:, None] * codec.thresholds[None, :].astype(np.float32)  # fp32 products
