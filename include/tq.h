@@ -143,6 +143,36 @@ int tq_attend_decode(const tq_codec *kc, const tq_codec *vc, const float *q, int
                      int32_t hq, int32_t hkv, int64_t n_ctx, tq_codes k, tq_codes v, float scale,
                      float *out, void *ws, size_t ws_bytes, void *stream);
 
+/* Append one new vector per (sequence, kv head) to a growing compressed cache laid out
+ * [n_seq][hkv][cap] (walkthrough "Etapa 1": the codes stay in the cache until the token is
+ * evicted; TurboESM summary, "Metodologia" A: RoPE first, then the orthogonal rotation, which
+ * keeps the attention scores).
+ *   x_new      [n_seq][hkv][d] device rows of type dt (contiguous).
+ *   pos        [n_seq] int32 device: the position of sequence s's new token, which is also its
+ *              slot: row (s, h) is encoded into record (s * hkv + h) * cap + pos[s].  Rows whose
+ *              position is outside [0, cap) are skipped (device data, not checked on the host).
+ *   rope_base  > 0: the rotation sees RoPE(x, pos[s]) -- coordinate i < d/2 turns with
+ *              i + d/2 by the angle pos * rope_base^(-2i/d), computed in fp64 -- while the
+ *              stored norm stays fp16(||x||) (RoPE keeps norms).  0: no RoPE (values).
+ * The codes are those of tq_encode otherwise (per-block rotations select the block of the
+ * record written).  Writes only the appended records.                                       */
+int tq_append(const tq_codec *c, const void *x_new, tq_dtype dt, int64_t n_seq, int32_t hkv,
+              const int32_t *pos, int64_t cap, float rope_base, tq_codes cache, void *stream);
+
+/* One decode step over growing caches of capacity cap per (sequence, kv head): tq_append of
+ * the new keys (RoPE at pos[s] when rope_base > 0) and values (no RoPE) into slot pos[s], then
+ * tq_attend_decode of the queries, turned by RoPE at pos[s] when rope_base > 0, over tokens
+ * 0 .. pos[s] of their sequence only.  A sequence whose pos[s] is outside [0, cap) appends
+ * nothing and gets a zero output.
+ *   q [n_seq][hq][d] fp32; k_new, v_new [n_seq][hkv][d] of type dt; out [n_seq][hq][d] fp32.
+ *   ws  workspace of tq_workspace_bytes(TQ_OP_DECODE_STEP, kc, vc, n_seq, hq, hkv, cap) bytes,
+ *       256-byte aligned.                                                                    */
+int tq_decode_step(const tq_codec *kc, const tq_codec *vc, const float *q, const void *k_new,
+                   const void *v_new, tq_dtype dt, int64_t n_seq, int32_t hq, int32_t hkv,
+                   int64_t cap, const int32_t *pos, float rope_base, tq_codes kcache,
+                   tq_codes vcache, float scale, float *out, void *ws, size_t ws_bytes,
+                   void *stream);
+
 /* Inner-product top-k search over an encoded database (one shared rotation):
  * for each query the k database rows with the largest estimated <q, x> (ties: smaller row
  * index first).  queries [n_q][d] fp32; out_idx [n_q][k] int64; out_score [n_q][k] fp32.
@@ -156,8 +186,10 @@ int tq_search_topk(const tq_codec *c, const float *queries, int64_t n_q, tq_code
 #define TQ_OP_SCORES 0
 #define TQ_OP_ATTEND 1
 #define TQ_OP_SEARCH 2
-/* Workspace bytes for `op` (0 when none).  SCORES/ATTEND: n_seq, hq, hkv, n = n_keys/n_ctx,
- * vc used by ATTEND only (may be NULL otherwise).  SEARCH: n_seq = n_q, hq = k, n = n_db.    */
+#define TQ_OP_DECODE_STEP 3
+/* Workspace bytes for `op` (0 when none).  SCORES/ATTEND/DECODE_STEP: n_seq, hq, hkv,
+ * n = n_keys/n_ctx/cap, vc used by ATTEND and DECODE_STEP only (may be NULL otherwise).
+ * SEARCH: n_seq = n_q, hq = k, n = n_db.                                                     */
 size_t tq_workspace_bytes(int op, const tq_codec *kc, const tq_codec *vc, int64_t n_seq,
                           int32_t hq, int32_t hkv, int64_t n);
 

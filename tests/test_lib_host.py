@@ -119,6 +119,31 @@ def test_device_call_argument_errors():
     # search: k range
     assert L.tq_search_topk(ctypes.byref(cc), q, 3, _fake_codes(), 100, 33, lg, lg, None, 0, S) == -1
     assert L.tq_search_topk(ctypes.byref(cc), q, 3, _fake_codes(), 5, 10, lg, lg, None, 0, S) == -1
+    # append: shape, rope base, positions, dtype and codes checked before any launch
+    pos = ctypes.c_void_p(0x90000)
+    F = ctypes.c_float
+    assert L.tq_append(ctypes.byref(cc), x, 0, 2, 0, pos, 100, F(1e4), _fake_codes(), S) == -1     # hkv < 1
+    assert L.tq_append(ctypes.byref(cc), x, 0, 2, 4, pos, 0, F(1e4), _fake_codes(), S) == -1       # cap < 1
+    assert L.tq_append(ctypes.byref(cc), x, 0, 2, 4, pos, 100, F(-1.0), _fake_codes(), S) == -1    # negative base
+    assert L.tq_append(ctypes.byref(cc), x, 0, 2, 4, pos, 100, F(float("nan")), _fake_codes(), S) == -1
+    assert L.tq_append(ctypes.byref(cc), x, 0, 2, 4, None, 100, F(1e4), _fake_codes(), S) == -1    # no positions
+    assert L.tq_append(ctypes.byref(cc), x, 5, 2, 4, pos, 100, F(1e4), _fake_codes(), S) == -1     # dtype
+    assert L.tq_append(ctypes.byref(cc), x, 0, 2, 4, pos, 100, F(1e4), _fake_codes(idx=0x20004), S) == -3
+    assert L.tq_append(ctypes.byref(cc), x, 0, 0, 4, pos, 100, F(1e4), _fake_codes(), S) == 0      # nothing to do
+    # decode step: the checks of append and attention, and the attention workspace at capacity cap
+    kv = ctypes.byref(vc)
+    step = (q, x, x, 0, 2, 8, 4, 100, pos, F(1e4), _fake_codes(), vcodes, F(0.1), lg)
+    assert L.tq_decode_step(ctypes.byref(cc), kv, *step, None, 0, S) == -4
+    need = L.tq_workspace_bytes(3, ctypes.byref(cc), kv, 2, 8, 4, 100)
+    assert need == L.tq_workspace_bytes(1, ctypes.byref(cc), kv, 2, 8, 4, 100) > 0
+    assert L.tq_decode_step(ctypes.byref(cc), kv, *step, ctypes.c_void_p(0x80000), need - 1, S) == -4
+    assert L.tq_decode_step(ctypes.byref(cc), kv, *step, ctypes.c_void_p(0x80010), need, S) == -3
+    bad = (q, x, x, 0, 2, 6, 4, 100, pos, F(1e4), _fake_codes(), vcodes, F(0.1), lg)  # hq % hkv
+    assert L.tq_decode_step(ctypes.byref(cc), kv, *bad, ctypes.c_void_p(0x80000), need, S) == -1
+    nopos = (q, x, x, 0, 2, 8, 4, 100, None, F(1e4), _fake_codes(), vcodes, F(0.1), lg)
+    assert L.tq_decode_step(ctypes.byref(cc), kv, *nopos, ctypes.c_void_p(0x80000), need, S) == -1
+    assert L.tq_decode_step(ctypes.byref(_fake_codec(d=64, m=64)), kv, *step, ctypes.c_void_p(0x80000), need,
+                            S) == -1  # key and value d differ
 
 
 def test_min_strides():

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libtq.so")
 
 TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
 TQ_ENC_PRE_ROTATED = 1
-TQ_OP_SCORES, TQ_OP_ATTEND, TQ_OP_SEARCH = 0, 1, 2
+TQ_OP_SCORES, TQ_OP_ATTEND, TQ_OP_SEARCH, TQ_OP_DECODE_STEP = 0, 1, 2, 3
 
 
 class TQError(RuntimeError):
@@ -54,6 +54,9 @@ def _load():
         "tq_scores": ([CP, P, I64, I32, I32, I64, _Codes, P, P, SZ, P], I32),
         "tq_attend_decode": ([CP, CP, P, I64, I32, I32, I64, _Codes, _Codes, ctypes.c_float, P, P, SZ, P], I32),
         "tq_search_topk": ([CP, P, I64, _Codes, I64, I32, P, P, P, SZ, P], I32),
+        "tq_append": ([CP, P, I32, I64, I32, P, I64, ctypes.c_float, _Codes, P], I32),
+        "tq_decode_step": ([CP, CP, P, P, P, I32, I64, I32, I32, I64, P, ctypes.c_float, _Codes, _Codes,
+                            ctypes.c_float, P, P, SZ, P], I32),
         "tq_workspace_bytes": ([ctypes.c_int, CP, CP, I64, I32, I32, I64], SZ),
         "tq_status_str": ([ctypes.c_int], ctypes.c_char_p),
         "tq_version": ([], ctypes.c_char_p),
@@ -67,8 +70,8 @@ def _load():
 
 lib = _load()
 EXPORTED = ("tq_make_rotation", "tq_make_head_rotations", "tq_make_sketch", "tq_make_codebook", "tq_encode",
-            "tq_scores", "tq_attend_decode", "tq_search_topk", "tq_workspace_bytes", "tq_status_str",
-            "tq_version")
+            "tq_scores", "tq_attend_decode", "tq_append", "tq_decode_step", "tq_search_topk",
+            "tq_workspace_bytes", "tq_status_str", "tq_version")
 
 
 def _check(rc):
@@ -281,6 +284,41 @@ def attend_decode(kcodec: Codec, vcodec: Codec, q, kcodes: Codes, vcodes: Codes,
     buf, ws, wsb = _workspace(need, q.device)
     _check(lib.tq_attend_decode(ctypes.byref(kc), ctypes.byref(vc), _ptr(q), n_seq, hq, hkv, n_ctx, kcodes.c(),
                                 vcodes.c(), ctypes.c_float(scale), _ptr(out), ws, wsb, _stream()))
+    return out
+
+
+def append(codec: Codec, x_new, pos, cap: int, rope_base: float, cache: Codes):
+    """Append x_new [n_seq, hkv, d] (one vector per sequence and kv head) into ``cache`` laid out
+    [n_seq][hkv][cap], at slot pos[s] (int32 [n_seq] on the device), RoPE'd at pos[s] before the
+    rotation when rope_base > 0."""
+    x = x_new.contiguous()
+    n_seq, hkv, d = x.shape
+    dt = _DT[str(x.dtype).replace("torch.", "")]
+    cc = codec.c()
+    _check(lib.tq_append(ctypes.byref(cc), _ptr(x), dt, n_seq, hkv, _ptr(pos), cap, ctypes.c_float(rope_base),
+                         cache.c(), _stream()))
+    return cache
+
+
+def decode_step(kcodec: Codec, vcodec: Codec, q, k_new, v_new, pos, cap: int, rope_base: float, kcache: Codes,
+                vcache: Codes, scale: float, out=None):
+    """One decode step: append k_new / v_new [n_seq, hkv, d] at slot pos[s] (keys RoPE'd), then
+    attention of q [n_seq, hq, d] (RoPE'd at pos[s]) over tokens 0 .. pos[s].  Returns out."""
+    torch = _torch()
+    q, kn, vn = q.contiguous(), k_new.contiguous(), v_new.contiguous()
+    n_seq, hq, d = q.shape
+    hkv = kn.shape[1]
+    if vn.dtype != kn.dtype:
+        raise ValueError("k_new and v_new must share a dtype")
+    dt = _DT[str(kn.dtype).replace("torch.", "")]
+    if out is None:
+        out = torch.empty((n_seq, hq, d), dtype=torch.float32, device=q.device)
+    kc, vc = kcodec.c(), vcodec.c()
+    need = lib.tq_workspace_bytes(TQ_OP_DECODE_STEP, ctypes.byref(kc), ctypes.byref(vc), n_seq, hq, hkv, cap)
+    buf, ws, wsb = _workspace(need, q.device)
+    _check(lib.tq_decode_step(ctypes.byref(kc), ctypes.byref(vc), _ptr(q), _ptr(kn), _ptr(vn), dt, n_seq, hq, hkv,
+                              cap, _ptr(pos), ctypes.c_float(rope_base), kcache.c(), vcache.c(),
+                              ctypes.c_float(scale), _ptr(out), ws, wsb, _stream()))
     return out
 
 

@@ -63,7 +63,8 @@ extern "C" size_t tq_workspace_bytes(int op, const tq_codec *kc, const tq_codec 
   const tq::ScoreShape s{n_seq, hq, hkv, n};
   switch (op) {
     case TQ_OP_SCORES: return tq::scores_workspace(tq::view(*kc), s);
-    case TQ_OP_ATTEND: return vc ? tq::attend_workspace(tq::view(*kc), tq::view(*vc), s) : 0;
+    case TQ_OP_ATTEND:
+    case TQ_OP_DECODE_STEP: return vc ? tq::attend_workspace(tq::view(*kc), tq::view(*vc), s) : 0;
     case TQ_OP_SEARCH: return tq::search_workspace(tq::view(*kc), n_seq, hq, n);
     default: return 0;
   }
@@ -108,6 +109,48 @@ extern "C" int tq_attend_decode(const tq_codec *kc, const tq_codec *vc, const fl
   if (!aligned(ws, 256)) return TQ_EALIGN;
   return tq::launch_attend(tq::view(*kc), tq::view(*vc), q, s, tq::view(k), tq::view(v), scale, out, ws,
                            ws_bytes, stream);
+}
+
+extern "C" int tq_append(const tq_codec *c, const void *x_new, tq_dtype dt, int64_t n_seq, int32_t hkv,
+                         const int32_t *pos, int64_t cap, float rope_base, tq_codes cache, void *stream) {
+  int rc = check_codec(c);
+  if (rc != TQ_OK) return rc;
+  if (n_seq < 0 || hkv < 1 || cap < 1 || !(rope_base >= 0.0f)) return TQ_EINVAL;
+  if (n_seq == 0) return TQ_OK;
+  if (!x_new || !pos) return TQ_EINVAL;
+  if (dt != TQ_F32 && dt != TQ_F16 && dt != TQ_BF16) return TQ_EINVAL;
+  rc = check_codes(c, cache);
+  if (rc != TQ_OK) return rc;
+  return tq::launch_append(tq::view(*c), x_new, (int)dt, n_seq, hkv, pos, cap, rope_base, tq::view(cache), stream);
+}
+
+extern "C" int tq_decode_step(const tq_codec *kc, const tq_codec *vc, const float *q, const void *k_new,
+                              const void *v_new, tq_dtype dt, int64_t n_seq, int32_t hq, int32_t hkv,
+                              int64_t cap, const int32_t *pos, float rope_base, tq_codes kcache, tq_codes vcache,
+                              float scale, float *out, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_codec(kc);
+  if (rc != TQ_OK) return rc;
+  rc = check_codec(vc);
+  if (rc != TQ_OK) return rc;
+  if (kc->d != vc->d) return TQ_EINVAL;
+  if (n_seq < 0 || cap < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || !(rope_base >= 0.0f)) return TQ_EINVAL;
+  if (n_seq == 0) return TQ_OK;
+  if (!q || !out || !k_new || !v_new || !pos) return TQ_EINVAL;
+  if (dt != TQ_F32 && dt != TQ_F16 && dt != TQ_BF16) return TQ_EINVAL;
+  rc = check_codes(kc, kcache);
+  if (rc != TQ_OK) return rc;
+  rc = check_codes(vc, vcache);
+  if (rc != TQ_OK) return rc;
+  const tq::ScoreShape s{n_seq, hq, hkv, cap};
+  const size_t need = tq::attend_workspace(tq::view(*kc), tq::view(*vc), s);
+  if (!ws || ws_bytes < need) return TQ_EWORKSPACE;
+  if (!aligned(ws, 256)) return TQ_EALIGN;
+  rc = tq::launch_append(tq::view(*kc), k_new, (int)dt, n_seq, hkv, pos, cap, rope_base, tq::view(kcache), stream);
+  if (rc != TQ_OK) return rc;
+  rc = tq::launch_append(tq::view(*vc), v_new, (int)dt, n_seq, hkv, pos, cap, 0.0f, tq::view(vcache), stream);
+  if (rc != TQ_OK) return rc;
+  return tq::launch_attend(tq::view(*kc), tq::view(*vc), q, s, tq::view(kcache), tq::view(vcache), scale, out, ws,
+                           ws_bytes, stream, pos, rope_base);
 }
 
 extern "C" int tq_search_topk(const tq_codec *c, const float *queries, int64_t n_q, tq_codes db, int64_t n_db,

@@ -20,7 +20,8 @@
 
 namespace tq {
 
-int qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh, hipStream_t st);
+int qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh, hipStream_t st,
+          const int32_t *pos = nullptr, float rope_base = 0.0f);
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -40,6 +41,7 @@ struct AttArgs {
   int64_t vsign_stride;
   const uint32_t *vnorms;
   float *part;  // [n_seq * hq][n_chunks][2 + d + m_V]
+  const int32_t *pos;  // decode step: sequence s attends over tokens 0 .. pos[s] (nullptr: all n_ctx)
 };
 
 template <int W>
@@ -124,6 +126,21 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   const int h0 = kvh * (a.hq / a.hkv) + sub * G;
   const int64_t qrow = s * a.hq + h0;
 
+  // Tokens of this sequence: all n_ctx, or 0 .. pos[s] in a decode step (none when pos[s] is
+  // outside the cache).  A chunk past them holds an empty state: max -inf, sum 0, outputs 0.
+  int64_t len = a.n_ctx;
+  if (a.pos != nullptr) {
+    const int64_t p = a.pos[s];
+    len = (p >= 0 && p < a.n_ctx) ? p + 1 : 0;
+  }
+  if ((int64_t)chunk * a.chunk >= len) {
+    for (int e = tid; e < G * (2 + NOUT); e += NT) {
+      const int h = e / (2 + NOUT), o = e % (2 + NOUT);
+      a.part[((qrow + h) * a.n_chunks + chunk) * (int64_t)(2 + NOUT) + o] = o == 0 ? -INFINITY : 0.0f;
+    }
+    return;  // uniform over the workgroup
+  }
+
   for (int i = tid; i < G * D; i += NT) qt[i] = a.qt[qrow * D + i];
   if constexpr (KM > 0)
     for (int i = tid; i < G * KM; i += NT) qh[i] = a.qh[qrow * KM + i];
@@ -143,7 +160,7 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   const float kappa_v = VM > 0 ? 1.2533141373155003f / (float)(VM > 0 ? VM : 1) : 0.0f;
   const int64_t t0 = (int64_t)chunk * a.chunk;
   int64_t t1 = t0 + a.chunk;
-  if (t1 > a.n_ctx) t1 = a.n_ctx;
+  if (t1 > len) t1 = len;
   const int64_t vbase = blk * a.n_ctx;
 
   // value-phase role of this lane: outputs o0 .. o0 + CPT - 1 for tokens part*TOK .. + TOK - 1
@@ -371,6 +388,10 @@ __global__ __launch_bounds__(256) void attend_combine(CombArgs a) {
   float m = -INFINITY;
   for (int c = lane; c < a.n_chunks; c += kWave) m = fmaxf(m, p[c * (2 + NOUT)]);
   m = wave_max(m);
+  if (m == -INFINITY) {  // no cached token for this sequence: zero output
+    for (int k = lane; k < D; k += kWave) a.out[hidx * D + k] = 0.0f;
+    return;  // uniform over the wavefront
+  }
   float l = 0.0f;
   for (int c = lane; c < a.n_chunks; c += kWave) l += exp2f(p[c * (2 + NOUT)] - m) * p[c * (2 + NOUT) + 1];
   l = wave_sumf(l);
@@ -453,7 +474,8 @@ static int launch_comb(const CombArgs &c, hipStream_t st) {
 }
 
 int launch_attend(const CodecView &kc, const CodecView &vc, const float *q, const ScoreShape &s, const CodesView &k,
-                  const CodesView &v, float scale, float *out, void *ws, size_t ws_bytes, void *stream) {
+                  const CodesView &v, float scale, float *out, void *ws, size_t ws_bytes, void *stream,
+                  const int32_t *pos, float rope_base) {
   if (s.n_seq == 0) return TQ_OK;
   (void)ws_bytes;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -461,13 +483,13 @@ int launch_attend(const CodecView &kc, const CodecView &vc, const float *q, cons
   float *qh = qt + (size_t)s.n_seq * s.hq * kc.d;
   const size_t qbytes = (size_t)s.n_seq * s.hq * (size_t)(kc.d + kc.m) * sizeof(float);
   float *part = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + (qbytes + 255) / 256 * 256);
-  int rc = qprep(kc, q, s, qt, qh, st);
+  int rc = qprep(kc, q, s, qt, qh, st, pos, rope_base);
   if (rc != TQ_OK) return rc;
   const int ch = att_chunk(s);
   const int nch = (int)((s.n + ch - 1) / ch);
   AttArgs a{qt, qh, kc.centroids, vc.centroids, s.n_seq, s.n, s.hq, s.hkv, 1, nch, ch, scale * kLog2e,
             k.idx, k.idx_stride, k.sign, k.sign_stride, k.norms, v.idx, v.idx_stride, v.sign, v.sign_stride,
-            v.norms, part};
+            v.norms, part, pos};
   const int D = kc.d, KB = kc.bits, KM = kc.m, VB = vc.bits, VM = vc.m;
   rc = TQ_EUNSUPPORTED;
 #define TQ_AT(DD, A, B, C, E) \

@@ -37,6 +37,13 @@ struct EncArgs {
   int64_t sign_stride;
   uint32_t *norms;
   float *y_tap;
+  // append mode (pos != nullptr, encode_kernel only): input row v = s * hkv + h is stored at
+  // record v * cap + pos[s] (rows whose position is outside [0, cap) are skipped), and with
+  // rope_base > 0 the rotation sees RoPE(x, pos[s])
+  const int32_t *pos;
+  int64_t cap;
+  int hkv;
+  float rope_base;
 };
 
 constexpr int kEncWaves = 4;
@@ -125,6 +132,13 @@ __global__ __launch_bounds__(kWave *kEncWaves) void encode_kernel(EncArgs a) {
   const int sw = M > 0 ? (int)(a.sign_stride >> 2) : 0;
 
   for (int64_t v = (int64_t)blockIdx.x * kEncWaves + wid; v < a.n; v += (int64_t)gridDim.x * kEncWaves) {
+    int64_t rec = v;  // the record written
+    int64_t p = 0;    // the position (append mode)
+    if (a.pos != nullptr) {
+      p = a.pos[v / a.hkv];
+      if (p < 0 || p >= a.cap) continue;  // uniform: one vector per wavefront
+      rec = v * a.cap + p;
+    }
     // ---- load and rotate
     float y[C], nsrc[C];
 #pragma unroll
@@ -140,9 +154,23 @@ __global__ __launch_bounds__(kWave *kEncWaves) void encode_kernel(EncArgs a) {
       for (int c = 0; c < C; ++c)
         if (lane + kWave * c < D) s.xs[lane + kWave * c] = nsrc[c];
       wave_lds_fence();
+      if (a.pos != nullptr && a.rope_base > 0.0f) {
+        // RoPE before the rotation: coordinate i < D/2 turns with i + D/2 by p * base^(-2i/D);
+        // angle, sine and cosine in fp64 (an fp32 angle would be off by ~p * 2^-24 radians)
+        const double lb = log2((double)a.rope_base);
+        for (int i = lane; i < D / 2; i += kWave) {
+          const double ang = (double)p * exp2(-2.0 * i / D * lb);
+          double sn, cs;
+          sincos(ang, &sn, &cs);
+          const double x0 = s.xs[i], x1 = s.xs[i + D / 2];
+          s.xs[i] = (float)(x0 * cs - x1 * sn);
+          s.xs[i + D / 2] = (float)(x0 * sn + x1 * cs);
+        }
+        wave_lds_fence();
+      }
       int64_t rid = 0;
       if (a.n_rot > 1 && a.vecs_per_rot > 0) {
-        rid = (a.first + v) / a.vecs_per_rot;
+        rid = (a.first + rec) / a.vecs_per_rot;
         if (rid > a.n_rot - 1) rid = a.n_rot - 1;
       }
       const float *R = a.rot + rid * (int64_t)D * D;
@@ -207,7 +235,7 @@ __global__ __launch_bounds__(kWave *kEncWaves) void encode_kernel(EncArgs a) {
           word |= off >= 0 ? (cv << off) : (cv >> (-off));
         }
       }
-      reinterpret_cast<uint32_t *>(a.idx + v * a.idx_stride)[w] = word;
+      reinterpret_cast<uint32_t *>(a.idx + rec * a.idx_stride)[w] = word;
     }
 
     if constexpr (M > 0) {
@@ -253,10 +281,10 @@ __global__ __launch_bounds__(kWave *kEncWaves) void encode_kernel(EncArgs a) {
         for (int c = 0; c < CM; ++c) {
           if ((w >> 1) == c) word = (w & 1) ? (uint32_t)(masks[c] >> 32) : (uint32_t)masks[c];
         }
-        reinterpret_cast<uint32_t *>(a.sign + v * a.sign_stride)[w] = word;
+        reinterpret_cast<uint32_t *>(a.sign + rec * a.sign_stride)[w] = word;
       }
     }
-    if (lane == 0) a.norms[v] = (rn16 << 16) | n16;
+    if (lane == 0) a.norms[rec] = (rn16 << 16) | n16;
     wave_lds_fence();
   }
 }
@@ -973,36 +1001,38 @@ static void launch_mfma(const EncArgs &a, hipStream_t st) {
 template <int D, int BITS, int M>
 static int launch_enc_dm(const EncArgs &a, int dt, bool pre, hipStream_t st) {
   if constexpr (D == 64 || D == 128) {
-    const int eb = dt == TQ_F32 ? 4 : 2;
-    const bool vec_ok = ((uintptr_t)a.x % 16 == 0) && ((a.ld_x * eb) % 16 == 0);
-    const bool rots = a.n_rot > 1 && a.vecs_per_rot > 0;
-    // per-block rotations on the MFMA path where the blocks align with passes (and, at d = 128,
-    // for bf16 input, whose registers leave room for the block loop)
-    if (rots && vec_ok && !pre && a.vecs_per_rot % 32 == 0 && a.first % 32 == 0 && (D == 64 || dt == TQ_BF16)) {
-      if constexpr (D == 64) {
-        if (dt == TQ_F32) launch_mfma<D, BITS, M, TQ_F32, false, true>(a, st);
-        else if (dt == TQ_F16) launch_mfma<D, BITS, M, TQ_F16, false, true>(a, st);
-        else if (dt == TQ_BF16) launch_mfma<D, BITS, M, TQ_BF16, false, true>(a, st);
-        else return TQ_EINVAL;
-      } else {
-        launch_mfma<D, BITS, M, TQ_BF16, false, true>(a, st);
+    if (a.pos == nullptr) {  // append mode takes encode_kernel below
+      const int eb = dt == TQ_F32 ? 4 : 2;
+      const bool vec_ok = ((uintptr_t)a.x % 16 == 0) && ((a.ld_x * eb) % 16 == 0);
+      const bool rots = a.n_rot > 1 && a.vecs_per_rot > 0;
+      // per-block rotations on the MFMA path where the blocks align with passes (and, at d = 128,
+      // for bf16 input, whose registers leave room for the block loop)
+      if (rots && vec_ok && !pre && a.vecs_per_rot % 32 == 0 && a.first % 32 == 0 && (D == 64 || dt == TQ_BF16)) {
+        if constexpr (D == 64) {
+          if (dt == TQ_F32) launch_mfma<D, BITS, M, TQ_F32, false, true>(a, st);
+          else if (dt == TQ_F16) launch_mfma<D, BITS, M, TQ_F16, false, true>(a, st);
+          else if (dt == TQ_BF16) launch_mfma<D, BITS, M, TQ_BF16, false, true>(a, st);
+          else return TQ_EINVAL;
+        } else {
+          launch_mfma<D, BITS, M, TQ_BF16, false, true>(a, st);
+        }
+        return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
       }
-      return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
-    }
-    if (!rots && vec_ok) {
-      if (pre) {
-        if (dt != TQ_F32) return TQ_EINVAL;
-        launch_mfma<D, BITS, M, TQ_F32, true>(a, st);
-      } else if (dt == TQ_F32) {
-        launch_mfma<D, BITS, M, TQ_F32, false>(a, st);
-      } else if (dt == TQ_F16) {
-        launch_mfma<D, BITS, M, TQ_F16, false>(a, st);
-      } else if (dt == TQ_BF16) {
-        launch_mfma<D, BITS, M, TQ_BF16, false>(a, st);
-      } else {
-        return TQ_EINVAL;
+      if (!rots && vec_ok) {
+        if (pre) {
+          if (dt != TQ_F32) return TQ_EINVAL;
+          launch_mfma<D, BITS, M, TQ_F32, true>(a, st);
+        } else if (dt == TQ_F32) {
+          launch_mfma<D, BITS, M, TQ_F32, false>(a, st);
+        } else if (dt == TQ_F16) {
+          launch_mfma<D, BITS, M, TQ_F16, false>(a, st);
+        } else if (dt == TQ_BF16) {
+          launch_mfma<D, BITS, M, TQ_BF16, false>(a, st);
+        } else {
+          return TQ_EINVAL;
+        }
+        return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
       }
-      return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
     }
   }
   int64_t blocks = (a.n + kEncWaves - 1) / kEncWaves;
@@ -1037,6 +1067,20 @@ static int launch_enc_bits(const EncArgs &a, int bits, int m, int dt, bool pre, 
     case 2: return launch_enc_d<D, 2>(a, m, dt, pre, st);
     case 3: return launch_enc_d<D, 3>(a, m, dt, pre, st);
     case 4: return launch_enc_d<D, 4>(a, m, dt, pre, st);
+    default: return TQ_EUNSUPPORTED;
+  }
+}
+
+int launch_append(const CodecView &c, const void *x, int dt, int64_t n_seq, int hkv, const int32_t *pos,
+                  int64_t cap, float rope_base, const CodesView &out, void *stream) {
+  if (n_seq == 0) return TQ_OK;
+  EncArgs a{x, c.d, n_seq * hkv, 0, c.rot, c.n_rot, c.vecs_per_rot, c.sketch, c.centroids, c.thresholds,
+            out.idx, out.idx_stride, out.sign, out.sign_stride, out.norms, nullptr, pos, cap, hkv, rope_base};
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  switch (c.d) {
+    case 64: return launch_enc_bits<64>(a, c.bits, c.m, dt, false, st);
+    case 128: return launch_enc_bits<128>(a, c.bits, c.m, dt, false, st);
+    case 200: return launch_enc_bits<200>(a, c.bits, c.m, dt, false, st);
     default: return TQ_EUNSUPPORTED;
   }
 }

@@ -39,6 +39,10 @@ inline CodesView view(const tq_codes &c) {
 // launchers (one per .hip translation unit); return a tq_status
 int launch_encode(const CodecView &c, const void *x, int dt, int64_t n, int64_t ld_x, bool pre_rotated,
                   int64_t first, const CodesView &out, float *y_tap, void *stream);
+// one new vector per (sequence, kv head) into record (s * hkv + h) * cap + pos[s]; RoPE at pos[s]
+// before the rotation when rope_base > 0
+int launch_append(const CodecView &c, const void *x, int dt, int64_t n_seq, int hkv, const int32_t *pos,
+                  int64_t cap, float rope_base, const CodesView &out, void *stream);
 
 struct ScoreShape {
   int64_t n_seq;
@@ -50,9 +54,11 @@ int launch_scores(const CodecView &kc, const float *q, const ScoreShape &s, cons
                   float *logits, void *ws, size_t ws_bytes, void *stream);
 
 size_t attend_workspace(const CodecView &kc, const CodecView &vc, const ScoreShape &s);
+// pos != nullptr: sequence s attends over tokens 0 .. pos[s] of its s.n slots, and its queries
+// are turned by RoPE at pos[s] first when rope_base > 0
 int launch_attend(const CodecView &kc, const CodecView &vc, const float *q, const ScoreShape &s,
                   const CodesView &k, const CodesView &v, float scale, float *out, void *ws,
-                  size_t ws_bytes, void *stream);
+                  size_t ws_bytes, void *stream, const int32_t *pos = nullptr, float rope_base = 0.0f);
 
 size_t search_workspace(const CodecView &c, int64_t n_q, int k, int64_t n_db);
 int launch_search(const CodecView &c, const float *queries, int64_t n_q, const CodesView &db,

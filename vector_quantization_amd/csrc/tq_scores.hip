@@ -28,7 +28,24 @@ struct QprepArgs {
   int64_t vecs_per_rot;
   const float *sketch;
   float *qt, *qh;
+  const int32_t *pos;  // with rope_base > 0: RoPE of the queries of sequence s at pos[s]
+  float rope_base;
 };
+
+// RoPE of the D-vector x (LDS) at position p: coordinate i < D/2 turns with i + D/2 by the angle
+// p * base^(-2i/D), in fp64; `first` and `step` spread the D/2 pairs over the calling threads.
+template <int D>
+__device__ __forceinline__ void rope_pairs(float *x, int64_t p, float base, int first, int step) {
+  const double lb = log2((double)base);
+  for (int i = first; i < D / 2; i += step) {
+    const double ang = (double)p * exp2(-2.0 * i / D * lb);
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    const double x0 = x[i], x1 = x[i + D / 2];
+    x[i] = (float)(x0 * cs - x1 * sn);
+    x[i + D / 2] = (float)(x0 * sn + x1 * cs);
+  }
+}
 
 template <int D, int M>
 __global__ __launch_bounds__(256) void qprep_kernel(QprepArgs a) {
@@ -50,6 +67,10 @@ __global__ __launch_bounds__(256) void qprep_kernel(QprepArgs a) {
   const float *R = a.rot + rid * (int64_t)D * D;
   for (int i = lane; i < D; i += kWave) qs[wid][i] = a.q[hidx * D + i];
   wave_lds_fence();
+  if (a.pos != nullptr && a.rope_base > 0.0f) {
+    rope_pairs<D>(qs[wid], a.pos[s], a.rope_base, lane, kWave);
+    wave_lds_fence();
+  }
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     const int i = lane + kWave * c;
@@ -93,6 +114,14 @@ __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
     int64_t h = h0 + e / D;
     if (h > a.n_heads - 1) h = a.n_heads - 1;
     qs[e / D][e % D] = a.q[h * D + e % D];
+  }
+  if (a.pos != nullptr && a.rope_base > 0.0f) {
+    __syncthreads();
+    // 16 threads per head
+    const int hh = tid / 16;
+    int64_t h = h0 + hh;
+    if (h > a.n_heads - 1) h = a.n_heads - 1;
+    rope_pairs<D>(qs[hh], a.pos[h / a.hq], a.rope_base, tid % 16, 16);
   }
   const int col = tid % NOUT;
   const int hs = tid / NOUT;
@@ -382,8 +411,9 @@ size_t scores_workspace(const CodecView &, const ScoreShape &) { return 0; }
 
 template <int D, int M>
 static int launch_qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh,
-                        hipStream_t st) {
-  QprepArgs a{q, s.n_seq * s.hq, s.hq, s.hkv, s.n, kc.rot, kc.n_rot, kc.vecs_per_rot, kc.sketch, qt, qh};
+                        hipStream_t st, const int32_t *pos, float rope_base) {
+  QprepArgs a{q, s.n_seq * s.hq, s.hq, s.hkv, s.n, kc.rot, kc.n_rot, kc.vecs_per_rot, kc.sketch, qt, qh, pos,
+              rope_base};
   if (kc.n_rot == 1 || kc.vecs_per_rot == 0) {
     const int64_t blocks = (a.n_heads + kQpHeads - 1) / kQpHeads;
     hipLaunchKernelGGL((qprep_tiled<D, M>), dim3((unsigned)blocks), dim3(256), 0, st, a);
@@ -394,9 +424,10 @@ static int launch_qprep(const CodecView &kc, const float *q, const ScoreShape &s
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 
-int qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh, hipStream_t st) {
+int qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh, hipStream_t st,
+          const int32_t *pos, float rope_base) {
   const int D = kc.d, M = kc.m;
-#define TQ_QP(DD, MM) if (D == DD && M == MM) return launch_qprep<DD, MM>(kc, q, s, qt, qh, st);
+#define TQ_QP(DD, MM) if (D == DD && M == MM) return launch_qprep<DD, MM>(kc, q, s, qt, qh, st, pos, rope_base);
   TQ_QP(64, 0) TQ_QP(64, 64) TQ_QP(128, 0) TQ_QP(128, 128) TQ_QP(200, 0) TQ_QP(200, 200)
 #undef TQ_QP
   return TQ_EUNSUPPORTED;

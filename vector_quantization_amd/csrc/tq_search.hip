@@ -19,7 +19,8 @@
 
 namespace tq {
 
-int qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh, hipStream_t st);
+int qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh, hipStream_t st,
+          const int32_t *pos = nullptr, float rope_base = 0.0f);
 
 struct SearchArgs {
   const float *qt, *qh, *centroids;
