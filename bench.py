@@ -37,10 +37,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["gqa", "long", "search", "esm2"], default="gqa",
+    ap.add_argument("--workload", choices=["gqa", "long", "search", "esm2", "decode_step"], default="gqa",
                     help="gqa (default, the headline line), long (single 131072-token sequence), "
                          "search (1M x d=200 database, 10k queries: pairs/s and recall), "
-                         "esm2 (33 layers x 20 heads x 1024 tokens, d=64, per-head rotations)")
+                         "esm2 (33 layers x 20 heads x 1024 tokens, d=64, per-head rotations), "
+                         "decode_step (the gqa cache growing: append one token per sequence, then attend)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attend", action="store_true")
     ap.add_argument("--encode-reps", type=int, default=3)
@@ -230,6 +231,83 @@ def search_main(a):
     print(json.dumps(res), flush=True)
 
 
+def decode_step_main(a):
+    """The 8B-class decode cache (capacity 32768 per sequence and kv head) growing by one token
+    per step: tq_decode_step appends each sequence's new K (RoPE) and V at the next position and
+    attends over the cache up to it.  The prefix is encoded once; the steps fill the last slots."""
+    import numpy as np
+    import torch
+
+    import synth
+    import vector_quantization_amd as tq
+
+    w = synth.GQA_DECODE
+    dev = "cuda"
+    torch.cuda.init()
+    log("decode step", w)
+    K, V, _ = synth.gqa_decode(w, seed=2, device=dev)
+    kc = tq.make_codec(w.d, w.k_bits, w.k_m, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
+    vc = tq.make_codec(w.d, w.v_bits, w.v_m, synth.SEED_ROT_V, synth.SEED_SKETCH_V)
+    cap = w.n_ctx
+    kcodes = tq.encode(kc, K.reshape(-1, w.d))
+    vcodes = tq.encode(vc, V.reshape(-1, w.d))
+    del K, V
+    torch.cuda.empty_cache()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31)
+    n = a.warmup + a.steps
+    qs = torch.randn((n, w.n_seq, w.hq, w.d), generator=gen, device=dev)
+    kn = torch.randn((n, w.n_seq, w.hkv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    vn = torch.randn((n, w.n_seq, w.hkv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    pos = [torch.full((w.n_seq,), cap - n + i, dtype=torch.int32, device=dev) for i in range(n)]
+    out = torch.empty((w.n_seq, w.hq, w.d), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(w.d)
+    base = 10000.0
+    step = lambda i: tq.decode_step(kc, vc, qs[i], kn[i], vn[i], pos[i], cap, base, kcodes, vcodes, scale, out=out)
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for j in range(a.steps):
+        ev[j][0].record()
+        step(a.warmup + j)
+        ev[j][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_step = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    # the appends alone (the same two encode launches the step makes), over the last slots again
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record()
+    for j in range(a.steps):
+        i = a.warmup + j
+        tq.append(kc, kn[i], pos[i], cap, base, kcodes)
+        tq.append(vc, vn[i], pos[i], cap, 0.0, vcodes)
+    eb.record()
+    torch.cuda.synchronize()
+    t_app = ea.elapsed_time(eb) / a.steps
+    mid = cap - n + a.warmup + a.steps // 2  # tokens attended at the middle step: 0 .. mid
+    code_b_k = (w.d * w.k_bits + 7) // 8 + (w.k_m + 7) // 8 + 4
+    code_b_v = (w.d * w.v_bits + 7) // 8 + (w.v_m + 7) // 8 + 4
+    step_bytes = (w.n_seq * w.hkv * (mid + 1) * (code_b_k + code_b_v) + 2 * w.n_seq * w.hq * w.d * 4
+                  + 2 * w.n_seq * w.hkv * w.d * 2)
+    res = {
+        "metric": "decode step over a growing compressed cache: tokens/s (append K/V with RoPE + attention)",
+        "value": w.n_seq / (t_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(wall * 1e3 / a.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (the gqa cache encoded from seeded bf16 K/V; new K/V bf16 N(0,1); fp32 queries)",
+        "config": {"workload": f"decode_step_{w.name}: {w.n_seq} sequences (32 layers x batch 8) x {w.hkv} kv heads, "
+                               f"{w.hq} q heads, d={w.d}, capacity {cap}, positions {cap - n}..{cap - 1}, "
+                               f"RoPE base {base:g}",
+                   "layers": w.layers, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "head_dim": w.d, "capacity": cap},
+        "step_ms": round(t_step, 4), "append_us": round(t_app * 1e3, 2),
+        "step_GBps": round(step_bytes / (t_step * 1e-3) / 1e9, 1), "step_algorithmic_bytes": step_bytes,
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def esm2_main(a):
     """ESM-2-650M-shaped cache: encode of all K/V (fp16, per-(layer, head) rotations) and one
     decode query per (layer, head) scored and attended over the 1024 cached tokens."""
@@ -307,6 +385,9 @@ def main():
         return
     if a.workload == "esm2":
         esm2_main(a)
+        return
+    if a.workload == "decode_step":
+        decode_step_main(a)
         return
     import numpy as np
     import torch
