@@ -26,6 +26,11 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-fno-gpu-rdc"]
 
 
+# per-source device flags: the bit-plane search keeps its int32 accumulators in VGPRs (no
+# AGPR copies in its epilogue)
+EXTRA = {"tq_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
@@ -34,7 +39,7 @@ def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, src + ".o")
     cmd = [HIPCC] + COMMON
     if src.endswith(".hip"):
-        cmd += DEVICE + ["-x", "hip"]
+        cmd += DEVICE + EXTRA.get(src, []) + ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
