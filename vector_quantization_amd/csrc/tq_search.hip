@@ -274,25 +274,25 @@ __global__ __launch_bounds__(256) void search_merge(SearchArgs a) {
 // (the Walsh expansion), so c[idx] = w_0 + sum_S w_S chi_S with w_S = 2^-bits sum_code c[code]
 // chi_S(code).  A codebook symmetric about zero (c[L-1-j] = -c[j], as for the Lloyd-Max levels
 // of the symmetric coordinate law) has w_S = 0 for every even |S|: two planes for 2 bits, four
-// for 3.  Other codebooks add the even planes (a uniform branch).  Then
+// for 3.  Other codebooks add the even planes (a second kernel variant).  Then
 //   sum_i c[idx_i] q~_i = w_0 Q + sum_S w_S (2 P_S - Q),  P_S = sum_i [chi_S,i = +1] q~_i,
-// with Q = sum_i q~_i.  Sign term likewise: sum_j (2 b_j - 1) q^_j = 2 P - Q^.
+// with Q = sum_i q~_i.  Sign term likewise: sum_j (2 b_j - 1) q^_j = 2 P - Q^.  For 2-bit codes
+// the planes taken are the b0 bits and the code values b0 + 2 b1 (2 P_b1 = P_code - P_b0), which
+// one shift of the index word serves with two masks.
 //
-// Products.  A plane's 0/1 bits, spread to bytes, are the int8 A operand of
+// Products.  A plane's bits (or code values) as bytes are the int8 A operand of
 // v_mfma_i32_16x16x64_i8; the query is the B operand as two int8 limbs,
 //   q~_i ~= sigma (L0_i + L1_i / 254),  sigma = max_i |q~_i| / 127,
 // (representation error <= sigma / 508 per coordinate), so every product sum is an exact
-// integer and 2 P_S - Q = sigma / 254 * (508 A0_S + 2 A1_S - (254 Q0 + Q1)), with A0/A1 the
-// limb sums and Q0/Q1 the limb totals; the bracket stays below 2^24 and converts exactly.  Per
-// 64 coordinates a plane costs two int8 products: 2-bit index + QJL signs at d = m = 200 take 24
-// per tile.
+// integer, P_S = sigma / 254 (254 A0_S + A1_S) with A0/A1 the limb sums, and 254 A0 + A1 stays
+// below 2^24 and converts exactly.  Per 64 coordinates a plane costs two products: 2-bit index +
+// QJL signs at d = m = 200 take 24 per tile.  The K order of the products is chosen so that a
+// lane's A bytes are its index or sign word shifted and masked (k_position).
 //
 // Rows.  A workgroup's four wavefronts hold 64 queries (16 each) and walk the same rows of a
-// database slice, so each row is fetched once per 64 queries; a lane decodes the planes of its
-// row's 16 coordinates per step with shifts, one 24-bit multiply and a mask per 4 coordinates,
-// and the next tile's words are loaded while this one is scored.  Each wavefront keeps its
-// queries' top-k lists in LDS as search_scan does, with the k-th best score of each query as
-// the entry threshold; the slices' lists are merged by search_merge.
+// database slice, so each row is fetched once per 64 queries; the next tile's words are loaded
+// while this one is scored.  Each wavefront keeps its queries' top-k lists in LDS, with the k-th
+// best score of each query as the entry threshold; the slices' lists are merged by search_merge.
 typedef int32_t si32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSpW = 4;  // wavefronts per workgroup (16 queries each)
