@@ -310,8 +310,9 @@ def decode_step_main(a):
 
 
 def esm2_main(a):
-    """ESM-2-650M-shaped cache: encode of all K/V (fp16, per-(layer, head) rotations) and one
-    decode query per (layer, head) scored and attended over the 1024 cached tokens."""
+    """ESM-2-650M-shaped cache: encode of all K/V (fp16, per-(layer, head) rotations), one decode
+    query per (layer, head) scored and attended over the 1024 cached tokens, and all-pairs scoring
+    (every token against every cached key of its (layer, head))."""
     import numpy as np
     import torch
 
@@ -350,12 +351,23 @@ def esm2_main(a):
     enc = lambda: (tq.encode(kc, Kd, out=kcodes), tq.encode(vc, Vd, out=vcodes))
     sco = lambda: tq.scores(kc, qd, kcodes, w.n_ctx, w.hkv, logits=logits)
     att = lambda: tq.attend_decode(kc, vc, qd, kcodes, vcodes, w.n_ctx, w.hkv, 1.0 / math.sqrt(w.d), out=out)
+    # all pairs: every token of the sequence queries every cached key of its (layer, head) -- 1024
+    # query heads per kv head, the matrix-core path of tq_scores (queries: the keys plus noise)
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(41)
+    qa = (Kd.view(w.layers, w.hkv, w.n_ctx, w.d).float()
+          + 0.1 * torch.randn((w.layers, w.hkv, w.n_ctx, w.d), generator=gq, device="cuda"))
+    qa = qa.reshape(w.layers, w.hkv * w.n_ctx, w.d).contiguous()
+    logits_all = torch.empty((w.layers, w.hkv * w.n_ctx, w.n_ctx), dtype=torch.float32, device="cuda")
+    allp = lambda: tq.scores(kc, qa, kcodes, w.n_ctx, w.hkv, logits=logits_all)
     for _ in range(a.warmup):
-        enc(); sco(); att()
+        enc(); sco(); att(); allp()
     torch.cuda.synchronize()
     t_enc = timed(enc, a.steps)
     t_sc = timed(sco, a.steps)
     t_at = timed(att, a.steps)
+    t_all = timed(allp, a.steps)
+    pairs_all = w.layers * w.hkv * w.n_ctx * w.n_ctx
     code_b = (w.d * w.k_bits + 7) // 8 + (w.k_m + 7) // 8 + 4
     sc_bytes = n_vec * code_b + w.n_seq * w.hq * w.n_ctx * 4 + w.n_seq * w.hq * w.d * 4
     res = {
@@ -369,6 +381,8 @@ def esm2_main(a):
                    "layers": w.layers, "heads": w.hkv, "n_ctx": w.n_ctx, "head_dim": w.d},
         "encode_ms": round(t_enc, 4), "scores_us": round(t_sc * 1e3, 2), "attend_us": round(t_at * 1e3, 2),
         "scores_GBps": round(sc_bytes / (t_sc * 1e-3) / 1e9, 1),
+        "allpairs_ms": round(t_all, 4), "allpairs_pairs_per_s": pairs_all / (t_all * 1e-3),
+        "allpairs_logits_GBps": round(pairs_all * 4 / (t_all * 1e-3) / 1e9, 1),
         "cache_bytes": 2 * n_vec * code_b,
         "gpu": torch.cuda.get_device_name(0),
     }

@@ -54,6 +54,13 @@ def test_tiny_workload():
     (64, 4, 64, 8, 2, 1, 300),
     (128, 3, 128, 8, 2, 1, 1500),      # four heads per lookup, 512-thread workgroups
     (128, 2, 0, 4, 1, 2, 900),         # four heads per lookup without a sketch, 512 threads
+    # from 32 query heads per kv head on: bit-plane products on the matrix cores
+    (64, 3, 64, 64, 2, 2, 300),        # 32 heads per kv head, ragged last tile
+    (128, 2, 128, 96, 1, 1, 1001),     # 64 + 32 heads, key count not a multiple of 4
+    (200, 3, 0, 40, 1, 2, 515),        # a partly filled wavefront of heads, no sketch
+    (128, 3, 128, 33, 1, 1, 4100),     # several key chunks
+    (64, 2, 0, 64, 4, 1, 2048),
+    (200, 2, 200, 32, 1, 1, 700),
 ])
 def test_scores_match_oracle(d, bits, m, hq, hkv, S, N):
     say("scores", d, bits, m, hq, hkv, S, N)
@@ -127,3 +134,41 @@ def test_scores_empty_and_tiny_n():
     assert out.shape == (1, 1, 1) and torch.isfinite(out).all()
     e = tq.scores(lib, torch.empty((0, 1, 64), device="cuda"), codes, 1, 1)
     assert e.shape == (0, 1, 1)
+
+
+def test_scores_many_heads_per_head_rotations():
+    """Every token of a short protein-like sequence querying every cached key, per (layer, head)
+    rotations: 64 queries per kv head on the bit-plane path."""
+    say("scores esm2-shaped all pairs")
+    d, bits, m, N, layers, heads = 64, 3, 64, 256, 1, 4
+    seeds = [synth.esm2_basis_seed(l, h) for l in range(layers) for h in range(heads)]
+    lib = tq.make_codec(d, bits, m, 1, 2, basis_seeds=seeds, vecs_per_rot=N)
+    ora = oc.make_codec(d, bits, m, 1, 2, basis_seeds=seeds, vecs_per_rot=N)
+    K, V, q = synth.esm2(layers=layers, heads=heads, seq=N)
+    g = np.random.default_rng(7)
+    qa = (K.reshape(layers, heads, N, d)[:, :, :64] + 0.1 * g.standard_normal((layers, heads, 64, d)))
+    qa = qa.reshape(layers, heads * 64, d).astype(np.float32)
+    got, want = _run(lib, ora, K.reshape(-1, d).astype(np.float32), qa, N, heads)
+    err = rel_err_rows(got, want)
+    say("  max rel err", err.max())
+    assert err.max() <= TOL
+
+
+def test_scores_many_heads_asymmetric_codebook():
+    """A codebook not symmetric about zero on the bit-plane path (its even Walsh planes)."""
+    import dataclasses
+    say("scores many heads, asymmetric codebook")
+    for d, bits, m in ((128, 2, 128), (64, 3, 0)):
+        ora0 = oc.make_codec(d, bits, m, 1, 2)
+        c = ora0.centroids.astype(np.float64)
+        c2 = (c + np.linspace(0.05, 0.3, len(c)) * (c.max() - c.min())).astype(np.float32)
+        t2 = (0.5 * (c2[:-1].astype(np.float64) + c2[1:])).astype(np.float32)
+        ora = dataclasses.replace(ora0, centroids=c2, thresholds=t2)
+        lib = tq.codec_from_arrays(d, bits, m, ora.rot, ora.sketch, c2, t2)
+        g = np.random.default_rng(d + bits)
+        K = g.standard_normal((2 * 600, d)).astype(np.float32)
+        q = g.standard_normal((1, 2 * 48, d)).astype(np.float32)
+        got, want = _run(lib, ora, K, q, 600, 2)
+        err = rel_err_rows(got, want)
+        say("  ", d, bits, m, "max rel err", err.max())
+        assert err.max() <= TOL

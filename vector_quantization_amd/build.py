@@ -26,9 +26,9 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-fno-gpu-rdc"]
 
 
-# per-source device flags: the bit-plane search keeps its int32 accumulators in VGPRs (no
-# AGPR copies in its epilogue)
-EXTRA = {"tq_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source device flags: the bit-plane scans keep their int32 accumulators in VGPRs (no AGPR
+# copies in their epilogues)
+EXTRA = {"tq_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "tq_scores.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

@@ -15,6 +15,7 @@
 #include "tq_device.h"
 #include "tq_internal.h"
 #include "tq_lut.h"
+#include "tq_planes.h"
 
 namespace tq {
 
@@ -30,6 +31,8 @@ struct QprepArgs {
   float *qt, *qh;
   const int32_t *pos;  // with rope_base > 0: RoPE of the queries of sequence s at pos[s]
   float rope_base;
+  uint8_t *limbs;      // qprep_tiled: when set, write the limb records (tq_planes.h) instead of q~, q^
+  int bits;            // their index-term K order
 };
 
 // RoPE of the D-vector x (LDS) at position p: coordinate i < D/2 turns with i + D/2 by the angle
@@ -95,22 +98,33 @@ __global__ __launch_bounds__(256) void qprep_kernel(QprepArgs a) {
   }
 }
 
-// Tiled variant for a codec with one shared rotation: a block takes 16 query heads and
-// computes q~ = q Pi^T, then q^ = q~ S^T, staging 8-column tiles of Pi (or S) transposed in
-// LDS so that the output columns are read without bank conflicts.
+// Tiled variant for 16 query heads that share one rotation (one shared rotation, or per-block
+// rotations with a multiple of 16 query heads per kv head): a block takes the 16 heads and
+// computes q~ = q Pi^T, then q^ = q~ S^T, staging 8-column tiles of Pi (or S) transposed in LDS
+// so that the output columns are read without bank conflicts.
 constexpr int kQpHeads = 16;
+constexpr int kQpHeadsMany = 64;
 constexpr int kQpKt = 8;
 
-template <int D, int M>
+template <int D, int M, int HEADS>
 __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
   constexpr int NOUT = D > M ? D : M;
   constexpr int TPC = (256 / NOUT) >= 1 ? 256 / NOUT : 1;  // threads per output column
-  constexpr int HPT = kQpHeads / TPC;                      // heads per thread
-  __shared__ float qs[kQpHeads][D + 1];
+  constexpr int HPT = HEADS / TPC;                         // heads per thread
+  __shared__ float qs[HEADS][D + 1];
+  __shared__ float qhs[HEADS][(M > 0 ? M : 1) + 1];
   __shared__ float rt[kQpKt][NOUT + 1];
   const int tid = threadIdx.x;
-  const int64_t h0 = (int64_t)blockIdx.x * kQpHeads;
-  for (int e = tid; e < kQpHeads * D; e += 256) {
+  const int64_t h0 = (int64_t)blockIdx.x * HEADS;
+  // the rotation of the key block that head h0 reads (the same for all HEADS heads)
+  const float *rot = a.rot;
+  if (a.n_rot > 1 && a.vecs_per_rot > 0) {
+    const int64_t kvb = (h0 / a.hq) * a.hkv + (h0 % a.hq) / (a.hq / a.hkv);
+    int64_t r = kvb * a.n_keys / a.vecs_per_rot;
+    if (r > a.n_rot - 1) r = a.n_rot - 1;
+    rot += r * D * D;
+  }
+  for (int e = tid; e < HEADS * D; e += 256) {
     int64_t h = h0 + e / D;
     if (h > a.n_heads - 1) h = a.n_heads - 1;
     qs[e / D][e % D] = a.q[h * D + e % D];
@@ -134,7 +148,7 @@ __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
     __syncthreads();
     for (int e = tid; e < D * kQpKt; e += 256) {
       const int i = e / kQpKt, kk = e % kQpKt;
-      rt[kk][i] = a.rot[(int64_t)i * D + k0 + kk];
+      rt[kk][i] = rot[(int64_t)i * D + k0 + kk];
     }
     __syncthreads();
     if (active && col < D) {
@@ -152,7 +166,7 @@ __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
     for (int j = 0; j < HPT; ++j) {
       const int64_t h = h0 + hs * HPT + j;
       qs[hs * HPT + j][col] = acc[j];
-      if (h < a.n_heads) a.qt[h * D + col] = acc[j];
+      if (h < a.n_heads && a.limbs == nullptr) a.qt[h * D + col] = acc[j];
     }
   }
   if constexpr (M > 0) {
@@ -179,8 +193,20 @@ __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
 #pragma unroll
       for (int j = 0; j < HPT; ++j) {
         const int64_t h = h0 + hs * HPT + j;
-        if (h < a.n_heads) a.qh[h * M + col] = acc[j];
+        qhs[hs * HPT + j][col] = acc[j];
+        if (h < a.n_heads && a.limbs == nullptr) a.qh[h * M + col] = acc[j];
       }
+    }
+  }
+  if (a.limbs != nullptr) {
+    // one wavefront per head: the limb records straight from LDS
+    __shared__ __align__(16) uint8_t stage[256 / kWave][limb_record_bytes(D, M)];
+    __syncthreads();
+    for (int hh = threadIdx.x / kWave; hh < HEADS; hh += 256 / kWave) {
+      const int64_t h = h0 + hh;
+      if (h < a.n_heads)
+        write_limb_record<D, M>(qs[hh], qhs[hh], a.bits, stage[threadIdx.x / kWave],
+                                a.limbs + h * limb_record_bytes(D, M));
     }
   }
 }
@@ -407,27 +433,136 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
   }
 }
 
-size_t scores_workspace(const CodecView &, const ScoreShape &) { return 0; }
+// ------------------------------------------------------------------ many query heads per kv head
+//
+// score_planes (tq_planes.h): with 32 or more query heads per kv head (every token of a sequence
+// querying every cached key, say), the logits of 64 query heads x a chunk of the kv head's keys
+// come from one workgroup whose four wavefronts walk the same keys.  Queries are prepared once
+// (qprep: q~, q^ with the key block's rotation; planes_limbs: int8 limbs) in the workspace.
+// Launched twice, ASYM false and true, as search_planes.
+struct ScorePlanesArgs {
+  const uint8_t *limbs;  // [n_seq * hq] limb records
+  const float *centroids;
+  int64_t n_seq, n;      // sequences; keys per (sequence, kv head)
+  int hq, hkv, q_groups, n_chunks;
+  int64_t chunk;         // keys per workgroup (a multiple of 16)
+  const uint8_t *idx;
+  int64_t idx_stride;
+  const uint8_t *sign;
+  int64_t sign_stride;
+  const uint32_t *norms;
+  float *logits;         // [n_seq][hq][n]
+};
+
+template <int D, int BITS, int M, bool ASYM>
+__global__ __launch_bounds__(kSpW * kWave) void score_planes(ScorePlanesArgs a) {
+  constexpr int NK = (D + 63) / 64;
+  constexpr int NKM = (M + 63) / 64;
+  constexpr int NKM1 = NKM > 0 ? NKM : 1;
+  constexpr int NP = n_planes<BITS, ASYM>();
+
+  double wd[1 << BITS];
+  if (walsh_weights<BITS>(a.centroids, wd) != ASYM) return;
+
+  const int lane = lane_id(), wid = threadIdx.x / kWave;
+  const int g = lane >> 4, col = lane & 15;
+  int64_t bid = blockIdx.x;
+  const int j = (int)(bid % a.q_groups);  // workgroups next to each other share the keys
+  bid /= a.q_groups;
+  const int c = (int)(bid % a.n_chunks);
+  const int64_t b = bid / a.n_chunks;     // key block: sequence * hkv + kv head
+  const int G = a.hq / a.hkv;
+  const int qg = 64 * j + 16 * wid;       // this wavefront's first query head within the group
+  if (qg >= G) return;
+  const int64_t rec = (b / a.hkv) * a.hq + (int64_t)(b % a.hkv) * G + qg + col;  // query head record
+  const bool ok = qg + col < G;
+
+  PlaneQuery<NK, NKM1, NP> pq;
+  load_plane_query<D, BITS, M, ASYM>(a.limbs, rec, ok, wd, pq);
+
+  const int64_t v0 = (int64_t)c * a.chunk;
+  const int64_t v1 = v0 + a.chunk < a.n ? v0 + a.chunk : a.n;
+  const RowPlanes rp{a.idx + b * a.n * a.idx_stride, a.idx_stride, M > 0 ? a.sign + b * a.n * a.sign_stride : a.idx,
+                     a.sign_stride, a.norms + b * a.n};
+  float *out = a.logits + (ok ? rec : 0) * a.n + 4 * g;
+  const bool vec4 = (a.n & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
+  planes_rows<D, BITS, M, ASYM>(rp, pq, v0, v1, [&](int64_t t0, int left, const float(&sc)[4]) {
+    if (!ok) return;
+    float *o = out + t0;
+    if (vec4 && left == 16) {
+      *reinterpret_cast<float4 *>(o) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * g + i < left) o[i] = sc[i];
+    }
+  });
+}
+
+// query heads per kv head from which the logits come from score_planes
+constexpr int kScorePlanesMinG = 32;
+
+static bool planes_config(const CodecView &kc) {
+  return (kc.d == 64 || kc.d == 128 || kc.d == 200) && (kc.bits == 2 || kc.bits == 3) && (kc.m == 0 || kc.m == kc.d);
+}
+
+static bool use_planes(const CodecView &kc, const ScoreShape &s) {
+  return s.hkv > 0 && s.hq / s.hkv >= kScorePlanesMinG && planes_config(kc);
+}
+
+size_t scores_workspace(const CodecView &kc, const ScoreShape &s) {
+  if (!use_planes(kc, s)) return 0;
+  const size_t heads = (size_t)s.n_seq * (size_t)s.hq;
+  const size_t qf = heads * (size_t)(kc.d + kc.m) * sizeof(float);
+  return (qf + 255) / 256 * 256 + heads * (size_t)limb_record_bytes(kc.d, kc.m);
+}
 
 template <int D, int M>
 static int launch_qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh,
-                        hipStream_t st, const int32_t *pos, float rope_base) {
+                        hipStream_t st, const int32_t *pos, float rope_base, uint8_t *limbs = nullptr) {
   QprepArgs a{q, s.n_seq * s.hq, s.hq, s.hkv, s.n, kc.rot, kc.n_rot, kc.vecs_per_rot, kc.sketch, qt, qh, pos,
-              rope_base};
-  if (kc.n_rot == 1 || kc.vecs_per_rot == 0) {
-    const int64_t blocks = (a.n_heads + kQpHeads - 1) / kQpHeads;
-    hipLaunchKernelGGL((qprep_tiled<D, M>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-  } else {
-    const int64_t blocks = (a.n_heads + 3) / 4;
-    hipLaunchKernelGGL((qprep_kernel<D, M>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+              rope_base, nullptr, kc.bits};
+  const bool one_rot = kc.n_rot == 1 || kc.vecs_per_rot == 0;
+  const int G = s.hq / s.hkv;
+  if (one_rot || G % kQpHeads == 0) {
+    a.limbs = limbs;  // the tiled kernel writes the limb records itself
+    // 64 heads per block when that still leaves a thousand blocks (each block reads Pi and S once)
+    // (d <= 128: at d = 200 the 64 heads a thread would carry do not fit its registers)
+    if (D <= 128 && (one_rot || G % kQpHeadsMany == 0) && a.n_heads >= 1024 * kQpHeadsMany) {
+      const int64_t blocks = (a.n_heads + kQpHeadsMany - 1) / kQpHeadsMany;
+      hipLaunchKernelGGL((qprep_tiled<D, M, D <= 128 ? kQpHeadsMany : kQpHeads>), dim3((unsigned)blocks), dim3(256),
+                         0, st, a);
+    } else {
+      const int64_t blocks = (a.n_heads + kQpHeads - 1) / kQpHeads;
+      hipLaunchKernelGGL((qprep_tiled<D, M, kQpHeads>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    }
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
   }
-  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+  const int64_t blocks = (a.n_heads + 3) / 4;
+  hipLaunchKernelGGL((qprep_kernel<D, M>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return TQ_EHIP;
+  if (limbs != nullptr) {
+    hipLaunchKernelGGL((planes_limbs<D, M>), dim3((unsigned)((a.n_heads + 3) / 4)), dim3(256), 0, st, qt, qh,
+                       a.n_heads, kc.bits, limbs);
+    if (hipGetLastError() != hipSuccess) return TQ_EHIP;
+  }
+  return TQ_OK;
 }
 
 int qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh, hipStream_t st,
           const int32_t *pos, float rope_base) {
   const int D = kc.d, M = kc.m;
 #define TQ_QP(DD, MM) if (D == DD && M == MM) return launch_qprep<DD, MM>(kc, q, s, qt, qh, st, pos, rope_base);
+  TQ_QP(64, 0) TQ_QP(64, 64) TQ_QP(128, 0) TQ_QP(128, 128) TQ_QP(200, 0) TQ_QP(200, 200)
+#undef TQ_QP
+  return TQ_EUNSUPPORTED;
+}
+
+int qprep_limbs(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, float *qh, uint8_t *limbs,
+                hipStream_t st) {
+  const int D = kc.d, M = kc.m;
+#define TQ_QP(DD, MM) \
+  if (D == DD && M == MM) return launch_qprep<DD, MM>(kc, q, s, qt, qh, st, nullptr, 0.0f, limbs);
   TQ_QP(64, 0) TQ_QP(64, 64) TQ_QP(128, 0) TQ_QP(128, 128) TQ_QP(200, 0) TQ_QP(200, 200)
 #undef TQ_QP
   return TQ_EUNSUPPORTED;
@@ -471,12 +606,55 @@ static int launch_score_dbm(const ScoreArgs &a, const ScoreShape &s, hipStream_t
   return launch_score_g<D, BITS, M, 1>(a, s, st);
 }
 
+template <int D, int BITS, int M>
+static int launch_score_planes(const CodecView &kc, const float *q, const ScoreShape &s, const CodesView &k,
+                               float *logits, void *ws, hipStream_t st) {
+  const size_t heads = (size_t)s.n_seq * (size_t)s.hq;
+  float *qt = reinterpret_cast<float *>(ws);
+  float *qh = qt + heads * D;
+  const size_t qf = heads * (size_t)(D + M) * sizeof(float);
+  uint8_t *limbs = reinterpret_cast<uint8_t *>(ws) + (qf + 255) / 256 * 256;
+  int rc = qprep_limbs(kc, q, s, qt, qh, limbs, st);
+  if (rc != TQ_OK) return rc;
+  ScorePlanesArgs a{limbs, kc.centroids, s.n_seq, s.n, s.hq, s.hkv, 0, 1, 0,
+                    k.idx, k.idx_stride, k.sign, k.sign_stride, k.norms, logits};
+  const int G = s.hq / s.hkv;
+  a.q_groups = (G + 16 * kSpW - 1) / (16 * kSpW);
+  // about 4096 workgroups, chunks of at least kSpMinRows keys (a multiple of 16), each chunk's
+  // bytes in every plane below 2^31 (32-bit buffer offsets)
+  const int64_t base = s.n_seq * s.hkv * a.q_groups;
+  int64_t want = (4096 + base - 1) / base;
+  const int64_t max_chunks = (s.n + kSpMinRows - 1) / kSpMinRows;
+  if (want > max_chunks) want = max_chunks;
+  if (want < 1) want = 1;
+  const int64_t stride = k.idx_stride > k.sign_stride ? k.idx_stride : k.sign_stride;
+  const int64_t max_rows = ((int64_t)0x7FFFFFFF - 64 * stride) / (stride > 4 ? stride : 4);
+  int64_t chunk = (s.n + want - 1) / want;
+  if (chunk > max_rows) chunk = max_rows;
+  chunk = (chunk + 15) / 16 * 16;
+  a.chunk = chunk;
+  a.n_chunks = (int)((s.n + chunk - 1) / chunk);
+  const unsigned blocks = (unsigned)(base * a.n_chunks);
+  hipLaunchKernelGGL((score_planes<D, BITS, M, false>), dim3(blocks), dim3(kSpW * kWave), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return TQ_EHIP;
+  hipLaunchKernelGGL((score_planes<D, BITS, M, true>), dim3(blocks), dim3(kSpW * kWave), 0, st, a);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
 int launch_scores(const CodecView &kc, const float *q, const ScoreShape &s, const CodesView &k, float *logits,
                   void *ws, size_t ws_bytes, void *stream) {
   if (s.n == 0 || s.n_seq == 0) return TQ_OK;
-  (void)ws;
   (void)ws_bytes;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (use_planes(kc, s)) {
+    const int D = kc.d, B = kc.bits, M = kc.m;
+#define TQ_SP(DD, BB, MM) if (D == DD && B == BB && M == MM) return launch_score_planes<DD, BB, MM>(kc, q, s, k, logits, ws, st);
+    TQ_SP(64, 2, 64) TQ_SP(64, 3, 64) TQ_SP(64, 2, 0) TQ_SP(64, 3, 0)
+    TQ_SP(128, 2, 128) TQ_SP(128, 3, 128) TQ_SP(128, 2, 0) TQ_SP(128, 3, 0)
+    TQ_SP(200, 2, 200) TQ_SP(200, 3, 200) TQ_SP(200, 2, 0) TQ_SP(200, 3, 0)
+#undef TQ_SP
+    return TQ_EUNSUPPORTED;
+  }
   ScoreArgs a{q, kc.rot, kc.sketch, kc.centroids, kc.n_rot, kc.vecs_per_rot, s.n_seq, s.n, s.hq, s.hkv, 1, 1, 1,
               k.idx, k.idx_stride, k.sign, k.sign_stride, k.norms, logits};
   const int D = kc.d, B = kc.bits, M = kc.m;
