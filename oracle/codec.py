@@ -230,6 +230,9 @@ class Codec:
     centroids: np.ndarray  # [2^bits] fp32 ascending
     thresholds: np.ndarray  # [2^bits - 1] fp32
     vecs_per_rot: int = 0  # consecutive vectors sharing one rotation (0: all share rot[0])
+    # > 0: the high half of a record's norm word holds fp16(nbar * resid_scale) instead of the
+    # residual norm (the TurboESM residual-sign correction, oracle/calibrate.py)
+    resid_scale: float = 0.0
     extra: dict = field(default_factory=dict)
 
     @property

@@ -79,6 +79,34 @@ def f16_rne_sqrt_exact(sumsq: Fraction) -> int:
     return lo if lo % 2 == 0 else lo + 1
 
 
+def f16_rne_exact(v: Fraction) -> int:
+    """fp16 bits of the non-negative rational v rounded to nearest, ties to even (>= 65520 -> inf)."""
+    lo, hi = 0, F16_INF_BITS  # invariant: value(lo) <= v
+    if Fraction(_f16_value_ext(hi)) <= v:
+        return F16_INF_BITS
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if Fraction(_f16_value_ext(mid)) <= v:
+            lo = mid
+        else:
+            hi = mid
+    mid = (Fraction(_f16_value_ext(lo)) + Fraction(_f16_value_ext(lo + 1))) / 2
+    if v < mid:
+        return lo
+    if v > mid:
+        return lo + 1
+    return lo if lo % 2 == 0 else lo + 1
+
+
+def f16_scaled_norm_bits(n16: np.ndarray, scale: float) -> np.ndarray:
+    """fp16 bits of nbar * scale (nbar the value of n16, scale an fp32 value), exactly rounded."""
+    s = Fraction(float(np.float32(scale)))
+    out = np.empty(len(n16), dtype=np.uint16)
+    for i, b in enumerate(np.asarray(n16, dtype=np.uint16)):
+        out[i] = f16_rne_exact(Fraction(float(f16_value(b))) * s)
+    return out
+
+
 def f16_norm_bits(v: np.ndarray) -> np.ndarray:
     """fp16 bits of the exactly rounded Euclidean norm of each row of ``v``.
 
@@ -257,7 +285,12 @@ def encode_rotated(y: np.ndarray, n16: np.ndarray, codec: Codec, idx_stride: Opt
     index = np.sum(y[:, :, None] >= thr[:, None, :], axis=2).astype(np.uint32)
     cval = nbar[:, None] * codec.centroids.astype(np.float32)[index]  # fp32 products
     resid = (y - cval).astype(np.float32)  # fp32 differences
-    rn16 = f16_norm_bits(resid)
+    if codec.resid_scale > 0:
+        # TurboESM residual-sign correction: the decoder adds nbar * ebar * sign per coordinate;
+        # the word carries nbar * ebar * m / sqrt(pi/2) so the QJL formula reads it unchanged
+        rn16 = f16_scaled_norm_bits(n16, codec.resid_scale)
+    else:
+        rn16 = f16_norm_bits(resid)
 
     idx = pack_bits(index, codec.bits, idx_stride)
     if codec.m > 0:
