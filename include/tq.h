@@ -55,7 +55,13 @@ typedef enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
  *   thresholds  [2^bits - 1] fp32 midpoints between adjacent centroids, ascending (the
  *               encoder finds #{j : y >= nbar t_j} by binary descent, which relies on it).
  *   vecs_per_rot  vector v of a cache uses rot[min(v / vecs_per_rot, n_rot - 1)]; 0 or
- *               n_rot == 1 means rot[0] for all.                                           */
+ *               n_rot == 1 means rot[0] for all.
+ *   resid_scale 0: the high half of a record's norm word is fp16(||r||) (walkthrough "Etapa 2").
+ *               > 0 (needs m > 0): it is fp16(nbar * resid_scale), exactly rounded -- the
+ *               TurboESM residual-sign correction (TurboESM summary, section 2.D): with S = I
+ *               (m = d) and resid_scale = e m / sqrt(pi/2), e the calibrated mean residual
+ *               magnitude (tq_calibrate_codebook), the QJL term of every estimator becomes
+ *               nbar e sign(r_i) per coordinate, x~ = x^ + sign * e.  Finite.              */
 typedef struct {
   int32_t d, bits, m;
   int32_t n_rot;
@@ -64,6 +70,7 @@ typedef struct {
   const float *sketch;
   const float *centroids;
   const float *thresholds;
+  float resid_scale;
 } tq_codec;
 
 /* Compressed vectors as three planes (structure of arrays), caller-allocated.
@@ -106,6 +113,24 @@ int tq_make_sketch(uint64_t seed, int32_t m, int32_t d, float *host_out);
  * Gauss-Legendre cell integrals, symmetrised, rounded to fp32.
  * host_centroids: [2^bits] ascending; host_thresholds: [2^bits - 1].  1 <= bits <= 8.       */
 int tq_make_codebook(int32_t d, int32_t bits, float *host_centroids, float *host_thresholds);
+
+/* A codebook calibrated on data (TurboESM summary, section 2.C: separate K and V tables fitted
+ * to each matrix's statistics; the Lloyd rule of walkthrough "Etapa 1" applied to a sample).
+ *   host_u        [n] samples of rotated directions u = Pi x / ||x|| (host memory).
+ *   host_init     [2^bits] ascending starting levels (e.g. tq_make_codebook's).
+ *   max_iter      rounds at most (>= 1); a round stops the loop when no level moved by more
+ *                 than 1e-12 of the largest.  Each round: midpoints t_j between the levels,
+ *                 cell of u = #{j : u >= t_j}, each level replaced by its cell's mean (in
+ *                 fp64; an empty cell keeps its level).
+ *   host_centroids [2^bits] out, fp32 of the final levels; host_thresholds [2^bits - 1] out,
+ *                 fp32 of their midpoints; host_ebar out: the mean over the samples of
+ *                 |u - level of its cell| (the TurboESM mean residual magnitude e);
+ *                 host_resid_scale out (may be NULL): fl32(e * m / sqrt(pi/2)), the
+ *                 tq_codec.resid_scale of a residual-sign codec with m = d sign bits.
+ * 1 <= bits <= 8, n >= 1, m >= 1.  Host only, no device work.                              */
+int tq_calibrate_codebook(const float *host_u, int64_t n, int32_t bits, const float *host_init, int32_t max_iter,
+                          int32_t m, float *host_centroids, float *host_thresholds, float *host_ebar,
+                          float *host_resid_scale);
 
 /* ---------------------------------------------------------------- device operations */
 

@@ -152,3 +152,59 @@ def test_min_strides():
     assert tq.min_stride(200 * 2) == 52
     assert tq.min_stride(200) == 28
     assert tq.min_stride(0) == 0
+
+
+@pytest.mark.parametrize("d,bits", [(64, 3), (128, 2), (200, 3)])
+def test_calibrated_codebook_matches_oracle(d, bits):
+    from oracle import calibrate
+    g = np.random.default_rng(d * bits)
+    # directions of a skewed mixture, as float32 samples (the library's input type)
+    x = g.standard_normal((3000, d)) * np.where(g.random(d) < 0.05, 6.0, 1.0) + 0.3
+    u = (x / np.linalg.norm(x, axis=1, keepdims=True)).astype(np.float32)
+    init, _ = tq.make_codebook(d, bits)
+    c, t, e, rs = tq.calibrate_codebook(u, init, m=d)
+    ora = calibrate.calibrate_codebook(u.astype(np.float64), init.astype(np.float64))
+    assert abs(rs - calibrate.resid_scale(ora.ebar, d)) <= 1e-6 * rs
+    scale = np.max(np.abs(ora.centroids))
+    assert np.max(np.abs(c - ora.centroids)) <= 1e-6 * scale
+    assert np.max(np.abs(t - ora.thresholds)) <= 1e-6 * scale
+    assert abs(e - ora.ebar) <= 1e-6 * ora.ebar
+    assert np.all(np.diff(c) > 0)
+
+
+def test_calibration_and_residual_scale_argument_errors():
+    L = tq.lib
+    u = np.zeros(8, np.float32)
+    init = np.array([-1.0, 1.0], np.float32)
+    out = np.empty(4, np.float32)
+    P = lambda a: a.ctypes.data
+    assert L.tq_calibrate_codebook(None, 8, 1, P(init), 10, 4, P(out), P(out), P(out), None) == -1
+    assert L.tq_calibrate_codebook(P(u), 0, 1, P(init), 10, 4, P(out), P(out), P(out), None) == -1
+    assert L.tq_calibrate_codebook(P(u), 8, 9, P(init), 10, 4, P(out), P(out), P(out), None) == -1
+    assert L.tq_calibrate_codebook(P(u), 8, 1, P(init), 0, 4, P(out), P(out), P(out), None) == -1
+    assert L.tq_calibrate_codebook(P(u), 8, 1, P(init), 10, 0, P(out), P(out), P(out), None) == -1
+    desc = np.array([1.0, -1.0], np.float32)
+    assert L.tq_calibrate_codebook(P(u), 8, 1, P(desc), 10, 4, P(out), P(out), P(out), None) == -1
+    assert L.tq_calibrate_codebook(P(u), 8, 1, P(init), 10, 4, P(out), P(out), P(out), None) == 0
+    # resid_scale: finite, not negative, and only with sign bits
+    S = ctypes.c_void_p(0)
+    x = ctypes.c_void_p(0x50000)
+    for bad, m in ((-1.0, 128), (float("nan"), 128), (float("inf"), 128), (0.5, 0)):
+        cc = _fake_codec(m=m)
+        cc.resid_scale = bad
+        assert L.tq_encode(ctypes.byref(cc), x, 0, 4, 128, 0, 0, _fake_codes(), None, S) == -1
+    cc = _fake_codec()
+    cc.resid_scale = 0.5
+    assert L.tq_encode(ctypes.byref(cc), x, 0, 0, 128, 0, 0, _fake_codes(), None, S) == 0
+
+
+def test_many_heads_per_kv_head_need_a_workspace():
+    # from 32 query heads per kv head tq_scores prepares the queries' int8 limbs in the workspace
+    L = tq.lib
+    cc = _fake_codec()
+    assert L.tq_workspace_bytes(0, ctypes.byref(cc), None, 2, 16, 2, 16) == 0
+    need = L.tq_workspace_bytes(0, ctypes.byref(cc), None, 2, 64, 2, 16)
+    assert need >= 2 * 64 * (128 + 128) * 4
+    q, lg, S = ctypes.c_void_p(0x60000), ctypes.c_void_p(0x70000), ctypes.c_void_p(0)
+    assert L.tq_scores(ctypes.byref(cc), q, 2, 64, 2, 16, _fake_codes(), lg, None, 0, S) == -4
+    assert L.tq_scores(ctypes.byref(cc), q, 2, 64, 2, 16, _fake_codes(), lg, ctypes.c_void_p(0x80010), need, S) == -3

@@ -29,7 +29,8 @@ class _Codec(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("bits", ctypes.c_int32), ("m", ctypes.c_int32),
                 ("n_rot", ctypes.c_int32), ("vecs_per_rot", ctypes.c_int64),
                 ("rot", ctypes.c_void_p), ("sketch", ctypes.c_void_p),
-                ("centroids", ctypes.c_void_p), ("thresholds", ctypes.c_void_p)]
+                ("centroids", ctypes.c_void_p), ("thresholds", ctypes.c_void_p),
+                ("resid_scale", ctypes.c_float)]
 
 
 class _Codes(ctypes.Structure):
@@ -50,6 +51,7 @@ def _load():
         "tq_make_head_rotations": ([U64, P, I32, I32, P], I32),
         "tq_make_sketch": ([U64, I32, I32, P], I32),
         "tq_make_codebook": ([I32, I32, P, P], I32),
+        "tq_calibrate_codebook": ([P, I64, I32, P, I32, I32, P, P, P, P], I32),
         "tq_encode": ([CP, P, I32, I64, I64, ctypes.c_uint32, I64, _Codes, P, P], I32),
         "tq_scores": ([CP, P, I64, I32, I32, I64, _Codes, P, P, SZ, P], I32),
         "tq_attend_decode": ([CP, CP, P, I64, I32, I32, I64, _Codes, _Codes, ctypes.c_float, P, P, SZ, P], I32),
@@ -69,7 +71,8 @@ def _load():
 
 
 lib = _load()
-EXPORTED = ("tq_make_rotation", "tq_make_head_rotations", "tq_make_sketch", "tq_make_codebook", "tq_encode",
+EXPORTED = ("tq_make_rotation", "tq_make_head_rotations", "tq_make_sketch", "tq_make_codebook",
+            "tq_calibrate_codebook", "tq_encode",
             "tq_scores", "tq_attend_decode", "tq_append", "tq_decode_step", "tq_search_topk",
             "tq_workspace_bytes", "tq_status_str", "tq_version")
 
@@ -112,6 +115,20 @@ def make_codebook(d: int, bits: int):
     return c, t
 
 
+def calibrate_codebook(u, init, m: int = 1, max_iter: int = 200):
+    """Levels, midpoints, mean residual magnitude e and resid_scale = fl32(e m / sqrt(pi/2))
+    fitted to the samples u (host, any shape)."""
+    u = np.ascontiguousarray(np.asarray(u, dtype=np.float32).ravel())
+    init = np.ascontiguousarray(init, dtype=np.float32)
+    bits = int(round(np.log2(len(init))))
+    c = np.empty(1 << bits, np.float32)
+    t = np.empty((1 << bits) - 1, np.float32)
+    e = np.empty(2, np.float32)
+    _check(lib.tq_calibrate_codebook(u.ctypes.data, u.size, bits, init.ctypes.data, max_iter, m, c.ctypes.data,
+                                     t.ctypes.data, e.ctypes.data, e[1:].ctypes.data))
+    return c, t, float(e[0]), float(e[1])
+
+
 # ------------------------------------------------------------------ device objects
 
 
@@ -149,6 +166,7 @@ class Codec:
     centroids: object
     thresholds: object
     vecs_per_rot: int = 0
+    resid_scale: float = 0.0  # > 0: residual-sign records (tq_codec.resid_scale)
 
     @property
     def n_rot(self) -> int:
@@ -157,7 +175,7 @@ class Codec:
     def c(self) -> _Codec:
         return _Codec(self.d, self.bits, self.m, self.n_rot, self.vecs_per_rot, self.rot.data_ptr(),
                       0 if self.sketch is None else self.sketch.data_ptr(), self.centroids.data_ptr(),
-                      self.thresholds.data_ptr())
+                      self.thresholds.data_ptr(), self.resid_scale)
 
     @property
     def idx_stride(self) -> int:
@@ -168,7 +186,8 @@ class Codec:
         return min_stride(self.m)
 
 
-def codec_from_arrays(d, bits, m, rot, sketch, centroids, thresholds, vecs_per_rot=0, device="cuda") -> Codec:
+def codec_from_arrays(d, bits, m, rot, sketch, centroids, thresholds, vecs_per_rot=0, device="cuda",
+                      resid_scale=0.0) -> Codec:
     torch = _torch()
     rot = np.asarray(rot, np.float32)
     if rot.ndim == 2:
@@ -177,7 +196,8 @@ def codec_from_arrays(d, bits, m, rot, sketch, centroids, thresholds, vecs_per_r
     def dev(a):
         return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
 
-    return Codec(d, bits, m, dev(rot), dev(sketch), dev(centroids), dev(thresholds), vecs_per_rot)
+    return Codec(d, bits, m, dev(rot), dev(sketch), dev(centroids), dev(thresholds), vecs_per_rot,
+                 float(np.float32(resid_scale)))
 
 
 def make_codec(d: int, bits: int, m: int, rot_seed: int, sketch_seed: int, basis_seeds=None,

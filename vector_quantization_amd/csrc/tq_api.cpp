@@ -1,6 +1,7 @@
 // C ABI entry points of libtq: argument validation, then the launchers of the .hip units.
 // Every check runs on the host before any launch; see include/tq.h for the contract.
 
+#include <cmath>
 #include <cstdint>
 
 #include "tq_internal.h"
@@ -21,6 +22,8 @@ int check_codec(const tq_codec *c) {
     return TQ_EUNSUPPORTED;
   if (!c->rot || !c->centroids || !c->thresholds || c->n_rot < 1 || c->vecs_per_rot < 0) return TQ_EINVAL;
   if (c->m > 0 && !c->sketch) return TQ_EINVAL;
+  if (!(c->resid_scale >= 0.0f) || c->resid_scale == INFINITY || (c->resid_scale > 0.0f && c->m == 0))
+    return TQ_EINVAL;
   if (!aligned(c->rot, 16) || (c->sketch && !aligned(c->sketch, 16))) return TQ_EALIGN;
   return TQ_OK;
 }

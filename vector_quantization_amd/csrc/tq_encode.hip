@@ -44,7 +44,15 @@ struct EncArgs {
   int64_t cap;
   int hkv;
   float rope_base;
+  // > 0: the norm word's high half is fp16(nbar * resid_scale) instead of fp16(||r||)
+  float resid_scale;
 };
+
+// The high half of the norm word: fp16(||r||), or with resid_scale > 0 fp16(nbar * resid_scale)
+// (the product of an fp16 and an fp32 value is exact in fp64; one rounding to fp16).
+__device__ __forceinline__ uint32_t hi_word(uint32_t rn16, float nbar, float resid_scale) {
+  return resid_scale > 0.0f ? f64_to_f16_rne((double)nbar * (double)resid_scale) : rn16;
+}
 
 constexpr int kEncWaves = 4;
 
@@ -284,7 +292,7 @@ __global__ __launch_bounds__(kWave *kEncWaves) void encode_kernel(EncArgs a) {
         reinterpret_cast<uint32_t *>(a.sign + rec * a.sign_stride)[w] = word;
       }
     }
-    if (lane == 0) a.norms[rec] = (rn16 << 16) | n16;
+    if (lane == 0) a.norms[rec] = (hi_word(rn16, nbar, a.resid_scale) << 16) | n16;
     wave_lds_fence();
   }
 }
@@ -804,7 +812,7 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
         }
       }
       rn2[t] = s2;
-      if (g == 0 && v < a.n) a.norms[v] = (rn16[t] << 16) | n16[t];
+      if (g == 0 && v < a.n) a.norms[v] = (hi_word(rn16[t], f16_bits_to_float(n16[t]), a.resid_scale) << 16) | n16[t];
     }
 
     // ---- 5. sign bits of z = S r
@@ -1075,7 +1083,8 @@ int launch_append(const CodecView &c, const void *x, int dt, int64_t n_seq, int 
                   int64_t cap, float rope_base, const CodesView &out, void *stream) {
   if (n_seq == 0) return TQ_OK;
   EncArgs a{x, c.d, n_seq * hkv, 0, c.rot, c.n_rot, c.vecs_per_rot, c.sketch, c.centroids, c.thresholds,
-            out.idx, out.idx_stride, out.sign, out.sign_stride, out.norms, nullptr, pos, cap, hkv, rope_base};
+            out.idx, out.idx_stride, out.sign, out.sign_stride, out.norms, nullptr, pos, cap, hkv, rope_base,
+            c.resid_scale};
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   switch (c.d) {
     case 64: return launch_enc_bits<64>(a, c.bits, c.m, dt, false, st);
@@ -1089,7 +1098,8 @@ int launch_encode(const CodecView &c, const void *x, int dt, int64_t n, int64_t 
                   int64_t first, const CodesView &out, float *y_tap, void *stream) {
   if (n == 0) return TQ_OK;
   EncArgs a{x, ld_x, n, first, c.rot, c.n_rot, c.vecs_per_rot, c.sketch, c.centroids, c.thresholds,
-            out.idx, out.idx_stride, out.sign, out.sign_stride, out.norms, y_tap};
+            out.idx, out.idx_stride, out.sign, out.sign_stride, out.norms, y_tap, nullptr, 0, 0, 0.0f,
+            c.resid_scale};
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   switch (c.d) {
     case 64: return launch_enc_bits<64>(a, c.bits, c.m, dt, pre_rotated, st);

@@ -14,6 +14,7 @@
 // u1 = 1 - (x >> 11) 2^-53 and u2 = (x >> 11) 2^-53.  Haar matrices: QR with the signs of
 // diag(R) folded into Q (Mezzadri 2007).
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -204,6 +205,63 @@ int lloyd_max_codebook(int d, int bits, std::vector<double> &c, std::vector<doub
 }  // namespace tq
 
 // ------------------------------------------------------------------------ C ABI
+
+extern "C" int tq_calibrate_codebook(const float *host_u, int64_t n, int32_t bits, const float *host_init,
+                                     int32_t max_iter, int32_t m, float *host_centroids, float *host_thresholds,
+                                     float *host_ebar, float *host_resid_scale) {
+  if (!host_u || !host_init || !host_centroids || !host_thresholds || !host_ebar) return TQ_EINVAL;
+  if (n < 1 || bits < 1 || bits > 8 || max_iter < 1 || m < 1) return TQ_EINVAL;
+  const int L = 1 << bits;
+  std::vector<double> lv(L), sum(L), t(L - 1);
+  std::vector<int64_t> cnt(L);
+  for (int j = 0; j < L; ++j) lv[j] = host_init[j];
+  for (int j = 0; j + 1 < L; ++j)
+    if (!(lv[j] <= lv[j + 1])) return TQ_EINVAL;  // ascending (and not NaN)
+  // the cell of u: the number of midpoints t_j with u >= t_j (binary search)
+  auto cell = [&](double u) {
+    int lo = 0, hi = L - 1;  // answer in [lo, hi]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;  // is u >= t[mid - 1]?
+      if (u >= t[mid - 1]) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  auto midpoints = [&]() {
+    for (int j = 0; j + 1 < L; ++j) t[j] = 0.5 * (lv[j] + lv[j + 1]);
+  };
+  for (int it = 0; it < max_iter; ++it) {
+    midpoints();
+    std::fill(sum.begin(), sum.end(), 0.0);
+    std::fill(cnt.begin(), cnt.end(), 0);
+    for (int64_t i = 0; i < n; ++i) {
+      const double u = host_u[i];
+      const int c = cell(u);
+      sum[c] += u;
+      ++cnt[c];
+    }
+    double moved = 0.0, big = 0.0;
+    for (int j = 0; j < L; ++j) {
+      const double nv = cnt[j] ? sum[j] / (double)cnt[j] : lv[j];
+      moved = std::fmax(moved, std::fabs(nv - lv[j]));
+      lv[j] = nv;
+      big = std::fmax(big, std::fabs(nv));
+    }
+    if (moved <= 1e-12 * big) break;
+  }
+  midpoints();
+  double e = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    const double u = host_u[i];
+    e += std::fabs(u - lv[cell(u)]);
+  }
+  for (int j = 0; j < L; ++j) host_centroids[j] = (float)lv[j];
+  for (int j = 0; j + 1 < L; ++j) host_thresholds[j] = (float)t[j];
+  const double ebar = e / (double)n;
+  *host_ebar = (float)ebar;
+  if (host_resid_scale) *host_resid_scale = (float)(ebar * (double)m / std::sqrt(M_PI / 2.0));
+  return TQ_OK;
+}
 
 extern "C" int tq_make_rotation(uint64_t seed, int32_t d, float *host_out) {
   if (!host_out) return TQ_EINVAL;

@@ -19,6 +19,7 @@ struct CodecView {
   int d, bits, m, n_rot;
   int64_t vecs_per_rot;
   const float *rot, *sketch, *centroids, *thresholds;
+  float resid_scale;
 };
 
 struct CodesView {
@@ -30,7 +31,8 @@ struct CodesView {
 };
 
 inline CodecView view(const tq_codec &c) {
-  return CodecView{c.d, c.bits, c.m, c.n_rot, c.vecs_per_rot, c.rot, c.sketch, c.centroids, c.thresholds};
+  return CodecView{c.d, c.bits, c.m, c.n_rot, c.vecs_per_rot, c.rot, c.sketch, c.centroids, c.thresholds,
+                   c.resid_scale};
 }
 inline CodesView view(const tq_codes &c) {
   return CodesView{c.idx, c.idx_stride, c.sign, c.sign_stride, c.norms};
