@@ -1,0 +1,252 @@
+"""Recursive polar stage 1 ("PolarQuant" proper): radius + angle tree.  Test infrastructure
+only: the tests, __graft_entry__.smoke() and bench.py's cpu_baseline use it; the library does
+not.
+
+Sources: hada.io TurboQuant page, "PolarQuant: um novo 'ângulo' para compressão": pairs of
+coordinates go to polar form, the radii are paired and turned to polar form again,
+recursively, until one radius and a set of angles remain; the angles' law is known and
+concentrated, so they are quantised on a fixed grid with known boundaries, with no
+per-vector normalisation.  sudonull.com, "Cómo funciona PolarQuant": a random rotation
+first; the radius carries the magnitude, the angles the direction; 3 to 4 bits per value.
+
+Readings (the pages leave these open):
+  * d = 2^L.  Level 1 pairs coordinates (2j, 2j+1) of y = Pi x; level l + 1 pairs the level-l
+    radii (2i, 2i+1).  A node's angle is psi = atan2(r_b, r_a) in [0, pi/2]; at level 1 the
+    pair (a, b) keeps its two signs (2 bits) and psi = atan2(|b|, |a|).
+  * Law of psi at level l, whose children hold k = 2^(l-1) coordinates each (direction uniform
+    on the sphere): density 2 / B(k/2, k/2) sin^(k-1) psi cos^(k-1) psi on [0, pi/2] (uniform
+    at level 1).  Each level's table: Lloyd-Max on that law with 2^ab levels, midpoint
+    thresholds, symmetrised about pi/4.  ab is one number for all levels.
+  * Decisions without angles: psi >= tau  <=>  r_b^2 cos^2 tau >= r_a^2 sin^2 tau, taken as
+    fl32(B * C) >= fl32(A * S) with A, B the children's sums of squares in fp32 (leaves
+    fl32(y^2), a node fl32(A + B)) and C = fl32(cos^2 tau), S = fl32(sin^2 tau).  The index is
+    the number of thresholds passed (a tie goes up).
+  * Radius: n16 = fp16(||x||), exactly rounded, as in the standard stage 1.
+  * Reconstruction: from the root (value 1) down, child a = parent cos psi^, child b =
+    parent sin psi^ (psi^ the level's level for the node's index, as fp32 cos and sin); a
+    level-1 pair gives (sign a * r cos psi^, sign b * r sin psi^); y^ = nbar u^.  Scores:
+    nbar <Pi q, u^>.
+  * Record: one bitstream, LSB first: pair j at bit (2 + ab) j as [sign of a (1 = negative),
+    sign of b, angle index]; then the node indices of levels 2, 3, ..., L in order, ab bits
+    each; pad bits zero.  Norm word: n16 in the low half, 0 in the high half.
+"""
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+from scipy import special
+
+from . import codec as oc
+from .quantize import f16_norm_bits, f16_value, pack_bits, unpack_bits
+
+
+def angle_density(k: int):
+    """Density of psi at a level whose children hold k coordinates each."""
+    c = 2.0 / special.beta(k / 2.0, k / 2.0)
+    return lambda p: c * np.sin(p) ** (k - 1) * np.cos(p) ** (k - 1)
+
+
+@dataclass
+class PolarLevel:
+    k: int
+    centroids64: np.ndarray   # psi^ (2^ab, ascending in [0, pi/2])
+    thresholds64: np.ndarray  # tau (2^ab - 1)
+    cos: np.ndarray           # fp32 cos psi^
+    sin: np.ndarray           # fp32 sin psi^
+    c2: np.ndarray            # fp32 cos^2 tau
+    s2: np.ndarray            # fp32 sin^2 tau
+
+
+def angle_table(k: int, ab: int) -> PolarLevel:
+    """Lloyd-Max levels of the level law with children of k coordinates."""
+    L = 1 << ab
+    half = math.pi / 2.0
+    f = angle_density(k)
+
+    def mass(a, b):
+        return special.betainc(k / 2.0, k / 2.0, np.sin(b) ** 2) - special.betainc(k / 2.0, k / 2.0, np.sin(a) ** 2)
+
+    gx, gw = np.polynomial.legendre.leggauss(64)
+
+    def moment(a, b):
+        # 64-point Gauss-Legendre per cell (the density is smooth on [0, pi/2])
+        a = np.atleast_1d(a)[:, None]
+        b = np.atleast_1d(b)[:, None]
+        p = 0.5 * (b - a) * gx[None, :] + 0.5 * (a + b)
+        return 0.5 * (b - a)[:, 0] * np.sum(gw[None, :] * p * f(p), axis=1)
+
+    if k == 1:
+        c64 = (np.arange(L) + 0.5) * half / L  # uniform law: equal cells, centred levels
+    else:
+        # start from the law's quantiles (every cell holds mass, however concentrated the law)
+        init = np.arcsin(np.sqrt(special.betaincinv(k / 2.0, k / 2.0, (np.arange(L) + 0.5) / L)))
+        c64, _ = oc.lloyd_max(mass, moment, 0.0, half, init, rel_tol=1e-13, floor_tol=1e-11)
+    c64 = 0.5 * (c64 + (half - c64[::-1]))  # symmetric about pi/4
+    t64 = 0.5 * (c64[:-1] + c64[1:])
+    return PolarLevel(k, c64, t64, np.cos(c64).astype(np.float32), np.sin(c64).astype(np.float32),
+                      (np.cos(t64) ** 2).astype(np.float32), (np.sin(t64) ** 2).astype(np.float32))
+
+
+@dataclass
+class PolarCodec:
+    d: int
+    ab: int
+    rot: np.ndarray                  # [n_rot, d, d] fp32
+    levels: List[PolarLevel]         # levels[l - 1] for l = 1..L
+    vecs_per_rot: int = 0
+
+    @property
+    def L(self) -> int:
+        return int(round(math.log2(self.d)))
+
+    @property
+    def n_bits(self) -> int:
+        return (self.d // 2) * (2 + self.ab) + (self.d // 2 - 1) * self.ab
+
+    def rot_index(self, n_vec: int, first: int = 0) -> np.ndarray:
+        ids = np.arange(first, first + n_vec, dtype=np.int64)
+        if self.rot.shape[0] == 1 or self.vecs_per_rot <= 0:
+            return np.zeros(n_vec, dtype=np.int64)
+        return np.minimum(ids // self.vecs_per_rot, self.rot.shape[0] - 1)
+
+
+def make_polar_codec(d: int, ab: int, rot_seed: int, basis_seeds=None, vecs_per_rot: int = 0) -> PolarCodec:
+    L = int(round(math.log2(d)))
+    assert 1 << L == d, "d must be a power of two"
+    rot = oc.haar_rotation(rot_seed, d)[None] if basis_seeds is None else oc.head_rotations(rot_seed, basis_seeds, d)
+    return PolarCodec(d, ab, rot, [angle_table(1 << (l - 1), ab) for l in range(1, L + 1)], vecs_per_rot)
+
+
+@dataclass
+class PolarCodes:
+    bits: np.ndarray   # [n][stride] u8
+    norms: np.ndarray  # [n] u32
+    extra: dict = field(default_factory=dict)
+
+
+def _decide(A, B, lv: PolarLevel):
+    """Index per node: thresholds passed, fl32(B C_j) >= fl32(A S_j)."""
+    A = A.astype(np.float32)
+    B = B.astype(np.float32)
+    return np.sum((B[..., None] * lv.c2) >= (A[..., None] * lv.s2), axis=-1).astype(np.uint32)
+
+
+def encode_rotated(y: np.ndarray, n16: np.ndarray, pc: PolarCodec, stride: Optional[int] = None) -> PolarCodes:
+    y = np.asarray(y, dtype=np.float32)
+    n, d = y.shape
+    a, b = y[:, 0::2], y[:, 1::2]
+    A = (a * a).astype(np.float32)
+    B = (b * b).astype(np.float32)
+    sa = (a < 0).astype(np.uint32)
+    sb = (b < 0).astype(np.uint32)
+    k1 = _decide(A, B, pc.levels[0])
+    pair = sa | (sb << 1) | (k1 << 2)                         # [n, d/2], 2 + ab bits each
+    s = (A + B).astype(np.float32)                              # level-1 radii squared
+    nodes = []
+    for lvl in range(2, pc.L + 1):
+        A, B = s[:, 0::2], s[:, 1::2]
+        nodes.append(_decide(A, B, pc.levels[lvl - 1]))
+        s = (A + B).astype(np.float32)
+    # one bitstream: pairs, then nodes of levels 2..L
+    fields = [(pair, 2 + pc.ab)] + [(c, pc.ab) for c in nodes]
+    nb = pc.n_bits
+    stride = stride or 4 * ((nb + 31) // 32)
+    out = np.zeros((n, stride), dtype=np.uint8)
+    bitpos = 0
+    words = np.zeros((n, (stride + 3) // 4 * 32), dtype=np.uint8)  # one byte per bit
+    for vals, w in fields:
+        for j in range(vals.shape[1]):
+            for t in range(w):
+                words[:, bitpos + t] = (vals[:, j] >> t) & 1
+            bitpos += w
+    assert bitpos == nb
+    packed = np.packbits(words[:, :stride * 8].reshape(n, stride, 8)[:, :, ::-1], axis=-1).reshape(n, stride)
+    out[:] = packed
+    norms = n16.astype(np.uint32)
+    return PolarCodes(out, norms, {"pair": pair, "nodes": nodes, "y": y})
+
+
+def encode(x: np.ndarray, pc: PolarCodec, pre_rotated: bool = False, first: int = 0,
+           stride: Optional[int] = None) -> PolarCodes:
+    x32 = np.asarray(x, dtype=np.float32)
+    n16 = f16_norm_bits(x32)
+    if pre_rotated:
+        y = x32
+    else:
+        rid = pc.rot_index(x32.shape[0], first)
+        y = np.empty_like(x32)
+        for r in np.unique(rid):
+            sel = rid == r
+            y[sel] = (x32[sel].astype(np.float64) @ pc.rot[r].astype(np.float64).T).astype(np.float32)
+    return encode_rotated(y, n16, pc, stride)
+
+
+def decode_fields(codes: PolarCodes, pc: PolarCodec):
+    """Record -> (pair fields [n, d/2], node indices per level 2..L)."""
+    n = codes.bits.shape[0]
+    bits = np.unpackbits(codes.bits, axis=-1, bitorder="little")
+    pos = 0
+
+    def take(cnt, w):
+        nonlocal pos
+        v = np.zeros((n, cnt), dtype=np.uint32)
+        for j in range(cnt):
+            for t in range(w):
+                v[:, j] |= bits[:, pos + t].astype(np.uint32) << t
+            pos += w
+        return v
+    pair = take(pc.d // 2, 2 + pc.ab)
+    nodes = [take(pc.d >> lvl, pc.ab) for lvl in range(2, pc.L + 1)]
+    return pair, nodes
+
+
+def unit_directions(codes: PolarCodes, pc: PolarCodec) -> np.ndarray:
+    """u^ [n, d] in the rotated space (fp64), from the root down."""
+    pair, nodes = decode_fields(codes, pc)
+    n = pair.shape[0]
+    r = np.ones((n, 1))
+    for lvl in range(pc.L, 1, -1):          # nodes of level lvl: children radii
+        lv = pc.levels[lvl - 1]
+        idx = nodes[lvl - 2]
+        c = lv.cos.astype(np.float64)[idx]
+        s = lv.sin.astype(np.float64)[idx]
+        r = np.stack([r * c, r * s], axis=-1).reshape(n, -1)
+    lv = pc.levels[0]
+    k = pair >> 2
+    sa = np.where(pair & 1, -1.0, 1.0)
+    sb = np.where(pair & 2, -1.0, 1.0)
+    u = np.stack([r * sa * lv.cos.astype(np.float64)[k], r * sb * lv.sin.astype(np.float64)[k]], axis=-1)
+    return u.reshape(n, pc.d)
+
+
+def scores(q: np.ndarray, codes: PolarCodes, pc: PolarCodec, n_keys: int, hkv: int) -> np.ndarray:
+    """Logits [S, hq, n_keys] = nbar <Pi_b q, u^> for queries [S, hq, d] (fp64)."""
+    S, hq, d = q.shape
+    G = hq // hkv
+    u = unit_directions(codes, pc)
+    nbar = f16_value((codes.norms & 0xFFFF).astype(np.uint16))
+    out = np.empty((S, hq, n_keys))
+    for s_ in range(S):
+        for h in range(hkv):
+            blk = s_ * hkv + h
+            sl = slice(blk * n_keys, (blk + 1) * n_keys)
+            rid = pc.rot_index(1, blk * n_keys)[0]
+            qt = q[s_, h * G:(h + 1) * G].astype(np.float64) @ pc.rot[rid].astype(np.float64).T
+            out[s_, h * G:(h + 1) * G] = (qt @ u[sl].T) * nbar[sl][None, :]
+    return out
+
+
+def exact_polar(y: np.ndarray):
+    """The unquantised transform of y (fp64): (radius, level-1 signs and angles, node angles)."""
+    y = np.asarray(y, dtype=np.float64)
+    a, b = y[:, 0::2], y[:, 1::2]
+    psi1 = np.arctan2(np.abs(b), np.abs(a))
+    r = np.hypot(a, b)
+    ang = []
+    while r.shape[1] > 1:
+        ra, rb = r[:, 0::2], r[:, 1::2]
+        ang.append(np.arctan2(rb, ra))
+        r = np.hypot(ra, rb)
+    return r[:, 0], (a < 0, b < 0, psi1), ang
