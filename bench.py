@@ -37,11 +37,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["gqa", "long", "search", "esm2", "decode_step"], default="gqa",
+    ap.add_argument("--workload", choices=["gqa", "long", "search", "esm2", "decode_step", "polar"], default="gqa",
                     help="gqa (default, the headline line), long (single 131072-token sequence), "
                          "search (1M x d=200 database, 10k queries: pairs/s and recall), "
                          "esm2 (33 layers x 20 heads x 1024 tokens, d=64, per-head rotations), "
-                         "decode_step (the gqa cache growing: append one token per sequence, then attend)")
+                         "decode_step (the gqa cache growing: append one token per sequence, then attend), "
+                         "polar (the gqa keys under the recursive polar stage, 2 angle bits: 52 B per key)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attend", action="store_true")
     ap.add_argument("--encode-reps", type=int, default=3)
@@ -420,6 +421,126 @@ def esm2_main(a):
     print(json.dumps(res), flush=True)
 
 
+def polar_main(a):
+    """The 8B-class key cache (32 layers x batch 8 x 8 kv heads x 32768 tokens, d = 128) under the
+    recursive polar stage with 2 angle bits per node: 48 B of bitstream + 4 B norm per key, the
+    size of the 2-bit + QJL record.  Timed: tq_polar_scores over every layer (the score stream);
+    the bulk encode on its own.  Quality on layer 0, batch 0 against exact fp32 logits, beside
+    the two-stage codec at the same record size (and both at 68 B: 3 angle bits / 3-bit + QJL)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import vector_quantization_amd as tq
+
+    w = synth.GQA_DECODE
+    ab = 2
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    log("workload", w, "polar ab", ab)
+    K, V, q = synth.gqa_decode(w, seed=2, device="cuda")
+    del V
+    pc = tq.make_polar_codec(w.d, ab, synth.SEED_ROT_K)
+    n_vec = w.n_seq * w.hkv * w.n_ctx
+    codes = tq.alloc_polar_codes(pc, n_vec)
+    Kf = K.reshape(-1, w.d)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    tq.polar_encode(pc, Kf, out=codes)
+    torch.cuda.synchronize()
+    enc = []
+    for _ in range(a.encode_reps):
+        ev[0].record(stream)
+        tq.polar_encode(pc, Kf, out=codes)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        enc.append(ev[0].elapsed_time(ev[1]))
+    t_enc = float(np.median(enc))
+    log(f"polar encode {t_enc:.2f} ms")
+    qf = q.reshape(w.n_seq, w.hq, w.d).contiguous()
+    logits = torch.empty((w.n_seq, w.hq, w.n_ctx), dtype=torch.float32, device="cuda")
+    for _ in range(a.warmup):
+        tq.polar_scores(pc, qf, codes, w.n_ctx, w.hkv, logits=logits)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        tq.polar_scores(pc, qf, codes, w.n_ctx, w.hkv, logits=logits)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_sc = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    rec_b = tq.polar_record_bytes(w.d, ab) + 4
+    keys = n_vec
+    q_bytes = w.n_seq * w.hq * w.d * 4
+    score_bytes = keys * rec_b + w.n_seq * w.hq * w.n_ctx * 4 + q_bytes
+    gbps = score_bytes / (t_sc * 1e-3) / 1e9
+
+    # quality on layer 0, batch 0 (8 kv heads x 32768 keys, 32 query heads) vs exact fp32 logits
+    k0 = K[0, 0].float()                                   # [hkv, n_ctx, d]
+    q0 = q[0, 0].float()                                   # [hq, d]
+    exact = torch.matmul(q0.view(w.hkv, w.group, w.d), k0.transpose(1, 2).contiguous()).reshape(1, w.hq, w.n_ctx)
+    qs0 = q0.view(1, w.hq, w.d).contiguous()
+
+    def quality(est):
+        est = est.reshape(w.hq, w.n_ctx).double()
+        ex = exact.reshape(w.hq, w.n_ctx).double()
+        cos = torch.nn.functional.cosine_similarity(est, ex, dim=1).mean().item()
+        rel = (torch.linalg.norm(est - ex, dim=1) / torch.linalg.norm(ex, dim=1)).mean().item()
+        return {"logit_cos_vs_exact": round(cos, 5), "logit_rel_l2_err": round(rel, 5)}
+
+    comp = {}
+    for bits_, abits in ((2, 2), (3, 3)):
+        pcb = tq.make_polar_codec(w.d, abits, synth.SEED_ROT_K)
+        pcodes = tq.polar_encode(pcb, k0.reshape(-1, w.d))
+        pq = quality(tq.polar_scores(pcb, qs0, pcodes, w.n_ctx, w.hkv))
+        kc = tq.make_codec(w.d, bits_, w.d, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
+        tcodes = tq.encode(kc, k0.reshape(-1, w.d))
+        tqq = quality(tq.scores(kc, qs0, tcodes, w.n_ctx, w.hkv))
+        comp[f"{tq.polar_record_bytes(w.d, abits) + 4}B_per_key"] = {
+            f"polar_ab{abits}": pq, f"two_stage_{bits_}bit_qjl{w.d}": tqq}
+    torch.cuda.synchronize()
+    res = {
+        "metric": "recursive-polar decode scoring GB/s (% HBM peak) + keys/s",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(wall * 1e3 / a.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded bf16 K, N(0,1) with 2% channels x10; fp32 queries)",
+        "config": {"workload": f"polar_{w.name}: {w.layers} layers x batch {w.batch}, {w.hq} q / {w.hkv} kv heads, "
+                               f"d={w.d}, {w.n_ctx} cached tokens; K recursive polar, {ab} angle bits per node, "
+                               f"{rec_b} B per key",
+                   "layers": w.layers, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "head_dim": w.d,
+                   "n_ctx": w.n_ctx, "angle_bits": ab},
+        "scores_ms": round(t_sc, 4), "keys_per_s": keys / (t_sc * 1e-3),
+        "qk_pairs_per_s": keys * w.group / (t_sc * 1e-3), "scores_algorithmic_bytes": score_bytes,
+        "encode_ms": round(t_enc, 3), "encode_vectors_per_s": round(n_vec / (t_enc * 1e-3)),
+        "quality_layer0_batch0": comp,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": f"tq::polar_score_kernel<{w.d}, {ab}, 4, 256> (one tq_polar_scores call)"},
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not a.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import polar as op
+        ora = op.make_polar_codec(w.d, ab, synth.SEED_ROT_K)
+        kx = k0.reshape(-1, w.d).cpu().numpy()
+        t0 = time.perf_counter()
+        ocodes = op.encode(kx, ora)
+        t_oe = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        op.scores(q0.cpu().numpy()[None], ocodes, ora, w.n_ctx, w.hkv)
+        tc = time.perf_counter() - t0
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        nk = w.hkv * w.n_ctx
+        res["cpu_baseline"] = {"value": nk / tc, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+                               "sample": (f"layer 0, batch 0: {w.hkv} kv heads x {w.n_ctx} keys scored for "
+                                          f"{w.hq} query heads ({tc:.1f} s); oracle encode of the same {nk} keys "
+                                          f"took {t_oe:.1f} s")}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -434,6 +555,9 @@ def main():
         return
     if a.workload == "decode_step":
         decode_step_main(a)
+        return
+    if a.workload == "polar":
+        polar_main(a)
         return
     import numpy as np
     import torch

@@ -206,6 +206,72 @@ int tq_search_topk(const tq_codec *c, const float *queries, int64_t n_q, tq_code
                    int64_t n_db, int32_t k, int64_t *out_idx, float *out_score, void *ws,
                    size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------- recursive polar stage 1
+ *
+ * The recursive form of the polar stage (hada.io TurboQuant page, "PolarQuant: um novo
+ * 'ângulo' para compressão"; sudonull.com "Cómo funciona PolarQuant"): after the rotation
+ * y = Pi x (d = 2^L), coordinate pairs (y_2j, y_2j+1) become (radius, angle), the radii are
+ * paired and turned to polar form again, level by level, until one radius remains.  Every
+ * angle psi = atan2(r_b, r_a) lies in [0, pi/2] with a known law (children of k = 2^(l-1)
+ * coordinates at level l: density proportional to sin^(k-1) psi cos^(k-1) psi), so each level
+ * has a fixed Lloyd-Max table and no vector carries a scale besides its radius fp16(||x||).
+ * Decode: u^ from the root (value 1) down, child a = parent cos psi^, child b = parent sin psi^;
+ * a level-1 pair gives (sign_a r cos psi^, sign_b r sin psi^); x^ = ||x|| Pi^T u^.  No
+ * residual stage.
+ *
+ * Tables [L][4][2^ab] fp32, level l = 1..L at (l-1) * 4 * 2^ab:
+ *   [0, n)    cos psi^_j      [n, 2n)   sin psi^_j      (psi^_j ascending, n = 2^ab)
+ *   [2n, 3n)  cos^2 tau_j     [3n, 4n)  sin^2 tau_j     (tau_j = (psi^_j + psi^_j+1)/2, j < n-1;
+ *                                                        the last entry of each is 0 padding)  */
+typedef struct {
+  int32_t d;  /* 64, 128 or 256 on the device */
+  int32_t ab; /* angle bits per node: 2, 3 or 4 on the device */
+  int32_t n_rot;
+  int64_t vecs_per_rot; /* as tq_codec.vecs_per_rot */
+  const float *rot;     /* [n_rot][d][d] fp32, 16-byte aligned */
+  const float *tables;  /* [L][4][2^ab] fp32 as above */
+} tq_polar_codec;
+
+/* Compressed vectors of the polar stage.
+ *   bits   [n][stride] bytes, one bitstream per vector, least significant bit first: pair j at
+ *          bit (2 + ab) j as [sign of y_2j (1 = negative), sign of y_2j+1, angle index (ab
+ *          bits)], then the node indices of levels 2, 3, ..., L in order, ab bits each; pad
+ *          bits and bytes zero.  stride >= tq_polar_record_bytes(d, ab), a multiple of 16 when
+ *          that size is a multiple of 16 (else of 8, else of 4); 16-byte aligned base.
+ *   norms  [n] uint32: fp16 ||x|| (round to nearest even of the exact norm) in the low half, 0
+ *          in the high half.                                                                 */
+typedef struct {
+  uint8_t *bits;
+  int64_t stride;
+  uint32_t *norms;
+} tq_polar_codes;
+
+/* Per-level angle tables (layout above) for d = 2^L (4 <= d <= 1024) and ab angle bits
+ * (1 <= ab <= 8): Lloyd-Max on each level's law in fp64 (Gauss-Legendre cell integrals, the
+ * law's quantiles as the start; level 1, the uniform law, in closed form), symmetrised about
+ * pi/4, rounded to fp32.  host_tables: L * 4 * 2^ab floats.  Host only.                      */
+int tq_make_polar_tables(int32_t d, int32_t ab, float *host_tables);
+
+/* Bytes of one record's bitstream: 4 * ceil(((d/2)(2 + ab) + (d/2 - 1) ab) / 32); 0 for
+ * d or ab out of range.                                                                      */
+size_t tq_polar_record_bytes(int32_t d, int32_t ab);
+
+/* Encode n vectors with the recursive polar stage.
+ *   x, dt, ld_x, flags, first, y_tap as tq_encode (TQ_ENC_PRE_ROTATED: x holds y as fp32).
+ * Per vector: n16 = fp16(||x||).  Level 1: A = fl32(y_2j^2), B = fl32(y_2j+1^2); level l > 1: A,
+ * B the children's fl32(A + B).  A node's index is #{ j : fl32(B cos^2 tau_j) >= fl32(A sin^2
+ * tau_j) } with the level's table -- the number of thresholds below psi, decided without
+ * computing an angle.                                                                        */
+int tq_polar_encode(const tq_polar_codec *pc, const void *x, tq_dtype dt, int64_t n, int64_t ld_x,
+                    uint32_t flags, int64_t first, tq_polar_codes out, float *y_tap, void *stream);
+
+/* Logits of every (query head, key) pair: nbar <Pi q, u^> (the query stays in fp32).
+ *   q [n_seq][hq][d] fp32, keys [n_seq][hkv][n_keys] records, logits [n_seq][hq][n_keys] fp32
+ *   (unscaled); query head h reads kv head h / (hq / hkv).  The rotation of kv block
+ *   (s, h) is that of record (s hkv + h) n_keys, as in tq_scores.  No workspace.              */
+int tq_polar_scores(const tq_polar_codec *pc, const float *q, int64_t n_seq, int32_t hq, int32_t hkv,
+                    int64_t n_keys, tq_polar_codes k, float *logits, void *stream);
+
 /* ---------------------------------------------------------------- helpers */
 
 #define TQ_OP_SCORES 0

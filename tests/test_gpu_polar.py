@@ -1,0 +1,247 @@
+"""GPU parity of the recursive polar stage (tq_polar_encode, tq_polar_scores) against the oracle.
+
+Encode, pre-rotated: from identical fp32 rotated inputs the bitstream and the norm word must be
+bit-identical (every decision is a single-rounding fp32 comparison on both sides, and the
+norm is the exactly rounded fp16 of the exact norm).  Full mode: the device rotation (fp32
+FMA) is checked against the exact rotation within ROT_BOUND through the y tap, and the
+record must be bit-identical to the oracle's encoding of that tap with the oracle's norm of
+the input.  Scores: records written by the oracle's encoder (or uniform random bits), logits
+within score_tol(d) of the oracle's fp64 nbar <Pi q, u^>.  The tables are the oracle's, uploaded.
+"""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import polar as op
+from oracle import quantize as oq
+from tests._util import say
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+tq = pytest.importorskip("vector_quantization_amd")
+
+# fp32 FMA rotation: (d + 2) 2^-24 of sum_k |Pi_ik x_k| at most, below 2^-13 for d <= 256
+ROT_BOUND = 2.0 ** -13
+# Logit error bound relative to nbar ||q||.  The rotated query in fp32 is off by at most
+# d 2^-24 ||q|| per coordinate (the rows of Pi are unit vectors), which moves <Pi q, u^> by at
+# most sqrt(d) times that (||u^||_1 <= sqrt(d)); the radii (products of at most L fp32
+# factors), the leaf terms and the fp32 sum of d/2 terms add at most (L + 4 + d/2) 2^-24
+# sqrt(d) more.  With L + 4 <= 12 <= 16: (1.5 d + 16) sqrt(d) 2^-24.
+def score_tol(d):
+    return (1.5 * d + 16) * np.sqrt(d) * 2.0 ** -24
+
+
+def _tables(pc):
+    n = 1 << pc.ab
+    t = np.zeros((pc.L, 4, n), np.float32)
+    for l, lv in enumerate(pc.levels):
+        t[l, 0], t[l, 1] = lv.cos, lv.sin
+        t[l, 2, :n - 1], t[l, 3, :n - 1] = lv.c2, lv.s2
+    return t
+
+
+def _codecs(d, ab, rot_seed=1, basis=None, vpr=0):
+    ora = op.make_polar_codec(d, ab, rot_seed, basis_seeds=basis, vecs_per_rot=vpr)
+    lib = tq.polar_codec_from_arrays(d, ab, ora.rot, _tables(ora), vecs_per_rot=vpr)
+    return lib, ora
+
+
+def _edge_rows(d):
+    rows = np.zeros((8, d), np.float32)
+    rows[1, 0] = 1.0                       # one coordinate: every other pair and node is 0 / 0
+    rows[2, :] = np.float32(0.25)          # a == b everywhere: psi = pi/4 at every node
+    rows[3, 1::2] = np.float32(-2.0)       # even coordinates zero, odd negative
+    rows[4, ::2] = np.float32(-0.0)        # negative zeros keep a clear sign bit
+    rows[4, 1::2] = np.float32(3.0)
+    rows[5, :d // 2] = np.float32(1e-20)   # squares and sums in the fp32 subnormal range
+    rows[6, :] = np.float32(2000.0)        # large norm, below 65520
+    rows[7, ::4] = np.float32(1.5)
+    rows[7, 1::4] = np.float32(-1.5)
+    return rows
+
+
+def _gpu_encode(lib, x_np, pre, dtype=None, first=0, tap=False, stride=None):
+    x = torch.from_numpy(x_np).to("cuda")
+    if dtype is not None:
+        x = x.to(dtype)
+    ytap = torch.empty((x.shape[0], lib.d), dtype=torch.float32, device="cuda") if tap else None
+    out = tq.alloc_polar_codes(lib, x.shape[0], stride=stride)
+    tq.polar_encode(lib, x, pre_rotated=pre, first=first, out=out, y_tap=ytap)
+    torch.cuda.synchronize()
+    bits, norms = out.numpy()
+    return bits, norms, (None if ytap is None else ytap.cpu().numpy())
+
+
+@pytest.mark.parametrize("d,ab", [(64, 2), (64, 3), (128, 2), (128, 3), (128, 4), (256, 2), (256, 4)])
+def test_pre_rotated_bit_exact(d, ab):
+    say("polar encode pre-rotated", d, ab)
+    lib, ora = _codecs(d, ab)
+    y = np.concatenate([_edge_rows(d), synth.pre_rotated(2053, d, seed=d * 10 + ab)])
+    y[100:200] *= np.float32(1e-3)
+    y[200:300] *= np.float32(300.0)
+    bits, norms, _ = _gpu_encode(lib, y, pre=True)
+    want = op.encode(y, ora, pre_rotated=True, stride=lib.stride)
+    assert np.array_equal(norms, want.norms)
+    assert np.array_equal(bits, want.bits)
+    assert norms[0] == 0
+    # the pi/4 row: the level-1 index passes every threshold below pi/4 and the tie at pi/4
+    pair, nodes = op.decode_fields(want, ora)
+    assert np.all(pair[2] >> 2 == (1 << ab) // 2)
+
+
+def test_pre_rotated_padded_stride():
+    d, ab = 128, 2
+    lib, ora = _codecs(d, ab)
+    y = synth.pre_rotated(515, d, seed=3)
+    stride = lib.stride + 32
+    bits, norms, _ = _gpu_encode(lib, y, pre=True, stride=stride)
+    want = op.encode(y, ora, pre_rotated=True, stride=stride)
+    assert np.array_equal(bits, want.bits) and np.array_equal(norms, want.norms)
+    assert not bits[:, lib.stride:].any()
+
+
+def _check_full(x_seen, lib, ora, gpu, first=0):
+    bits, norms, ytap = gpu
+    x64 = x_seen.astype(np.float64)
+    rid = ora.rot_index(x64.shape[0], first)
+    for r in np.unique(rid):
+        sel = rid == r
+        P = ora.rot[r].astype(np.float64)
+        bound = ROT_BOUND * (np.abs(x64[sel]) @ np.abs(P).T) + 1e-45
+        assert np.all(np.abs(ytap[sel].astype(np.float64) - x64[sel] @ P.T) <= bound)
+    want = op.encode_rotated(ytap, oq.f16_norm_bits(x_seen), ora, stride=lib.stride)
+    assert np.array_equal(norms, want.norms)
+    assert np.array_equal(bits, want.bits)
+
+
+@pytest.mark.parametrize("d,ab,dtype", [(64, 3, "float32"), (128, 2, "bfloat16"), (128, 4, "float16"),
+                                        (256, 3, "float32")])
+def test_full_mode_codes_of_the_tap(d, ab, dtype):
+    say("polar encode full", d, ab, dtype)
+    lib, ora = _codecs(d, ab)
+    g = np.random.default_rng(d + ab)
+    x = (g.standard_normal((1501, d)) * np.where(g.random(d) < 0.05, 10.0, 1.0)).astype(np.float32)
+    tdt = getattr(torch, dtype)
+    x_seen = torch.from_numpy(x).to(tdt).to(torch.float32).numpy()
+    _check_full(x_seen, lib, ora, _gpu_encode(lib, x, pre=False, dtype=tdt, tap=True))
+
+
+def test_full_mode_rotation_blocks():
+    d, ab, n_rot, vpr, first = 128, 2, 40, 32, 64
+    lib, ora = _codecs(d, ab, basis=[500 + i for i in range(n_rot)], vpr=vpr)
+    n = n_rot * vpr - first + 40
+    x = (np.random.default_rng(9).standard_normal((n, d)) * 3.0).astype(np.float32)
+    _check_full(x, lib, ora, _gpu_encode(lib, x, pre=False, first=first, tap=True), first=first)
+
+
+def _score_case(lib, ora, q, codes_bits, norms, n_keys, hkv):
+    n_seq, hq, d = q.shape
+    k = tq.PolarCodes(torch.from_numpy(np.ascontiguousarray(codes_bits)).cuda(),
+                      torch.from_numpy(np.ascontiguousarray(norms).view(np.int32)).cuda())
+    got = tq.polar_scores(lib, torch.from_numpy(q).cuda(), k, n_keys, hkv).cpu().numpy()
+    want = op.scores(q, op.PolarCodes(codes_bits, norms), ora, n_keys, hkv)
+    nbar = oq.f16_value((norms & 0xFFFF).astype(np.uint16)).reshape(n_seq, hkv, 1, n_keys)
+    qn = np.linalg.norm(q.astype(np.float64), axis=-1).reshape(n_seq, hkv, hq // hkv, 1)
+    tol = (score_tol(d) * nbar * qn).reshape(n_seq, hq, n_keys) + 1e-30
+    err = np.abs(got.astype(np.float64) - want)
+    assert np.all(err <= tol), float(np.max(err / tol))
+    return float(np.max(err / tol))
+
+
+@pytest.mark.parametrize("d,ab,n_seq,hq,hkv,n_keys", [
+    (128, 2, 2, 8, 2, 1000),    # 4 heads per table
+    (128, 3, 1, 3, 3, 777),     # one head per table
+    (64, 3, 2, 6, 3, 515),      # two
+    (64, 2, 1, 16, 2, 300),     # eight
+    (256, 4, 1, 4, 2, 400),     # two (the table limit)
+    (128, 2, 1, 4, 1, 1),       # a single key
+])
+def test_scores_match_oracle(d, ab, n_seq, hq, hkv, n_keys):
+    say("polar scores", d, ab, n_seq, hq, hkv, n_keys)
+    lib, ora = _codecs(d, ab)
+    g = np.random.default_rng(d * ab + n_keys)
+    x = (g.standard_normal((n_seq * hkv * n_keys, d)) * np.where(g.random(d) < 0.05, 10.0, 1.0)).astype(np.float32)
+    enc = op.encode(x, ora, stride=lib.stride)
+    q = g.standard_normal((n_seq, hq, d)).astype(np.float32)
+    r = _score_case(lib, ora, q, enc.bits, enc.norms, n_keys, hkv)
+    say("  max err / tol", r)
+
+
+def _random_records(n, d, ab, stride, seed):
+    g = np.random.default_rng(seed)
+    nb = (d // 2) * (2 + ab) + (d // 2 - 1) * ab
+    bitsarr = g.integers(0, 2, (n, stride * 8), dtype=np.uint8)
+    bitsarr[:, nb:] = 0
+    rec = np.packbits(bitsarr, axis=-1, bitorder="little")
+    norms = np.abs(g.standard_normal(n) * np.sqrt(d)).astype(np.float16).view(np.uint16).astype(np.uint32)
+    return rec, norms
+
+
+@pytest.mark.parametrize("d,ab", [(64, 4), (128, 2), (256, 3)])
+def test_scores_random_records(d, ab):
+    # uniform bits reach every field value of every pair and node
+    lib, ora = _codecs(d, ab)
+    n_seq, hq, hkv, n_keys = 1, 4, 2, 600
+    rec, norms = _random_records(n_seq * hkv * n_keys, d, ab, lib.stride, seed=d + ab)
+    q = np.random.default_rng(1).standard_normal((n_seq, hq, d)).astype(np.float32)
+    _score_case(lib, ora, q, rec, norms, n_keys, hkv)
+
+
+def test_scores_per_block_rotations():
+    d, ab, n_seq, hq, hkv, n_keys = 64, 2, 2, 6, 3, 200
+    seeds = [700 + i for i in range(n_seq * hkv)]
+    lib, ora = _codecs(d, ab, basis=seeds, vpr=n_keys)
+    x = np.random.default_rng(4).standard_normal((n_seq * hkv * n_keys, d)).astype(np.float32)
+    enc = op.encode(x, ora, stride=lib.stride)
+    q = np.random.default_rng(5).standard_normal((n_seq, hq, d)).astype(np.float32)
+    _score_case(lib, ora, q, enc.bits, enc.norms, n_keys, hkv)
+
+
+def test_full_size_sampled():
+    # the 8B decode shape of one layer-batch slice at full context (8 sequences x 8 kv heads x
+    # 32768 keys, 32 query heads): device encode, device scores, and oracle logits on sampled keys
+    w = synth.GQA_DECODE
+    d, ab, n_seq = w.d, 2, w.batch
+    lib, ora = _codecs(d, ab)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    K = torch.randn((n_seq * w.hkv * w.n_ctx, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    q = torch.randn((n_seq, w.hq, d), generator=gen, device="cuda", dtype=torch.float32)
+    codes = tq.polar_encode(lib, K)
+    logits = tq.polar_scores(lib, q, codes, w.n_ctx, w.hkv)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(0)
+    keys = np.sort(g.choice(K.shape[0], 512, replace=False))
+    sel = torch.from_numpy(keys).cuda()
+    bits = codes.bits[sel].cpu().numpy()
+    norms = codes.norms[sel].cpu().numpy().view(np.uint32)
+    x_seen = K[sel].float().cpu().numpy()
+    # the records equal the oracle's encoding of the same keys up to rotation-bound decisions:
+    # their norms are exact, and their decoded directions are close
+    assert np.array_equal(norms, oq.f16_norm_bits(x_seen))
+    u = op.unit_directions(op.PolarCodes(bits, norms), ora)
+    qn = q.cpu().numpy().astype(np.float64)
+    nbar = oq.f16_value((norms & 0xFFFF).astype(np.uint16))
+    blk = keys // w.n_ctx
+    s_idx, h_idx, t_idx = blk // w.hkv, blk % w.hkv, keys % w.n_ctx
+    G = w.hq // w.hkv
+    P = ora.rot[0].astype(np.float64)
+    got = logits.cpu().numpy()
+    for i in range(len(keys)):
+        heads = np.arange(h_idx[i] * G, (h_idx[i] + 1) * G)
+        want = (qn[s_idx[i], heads] @ P.T) @ u[i] * nbar[i]
+        tol = score_tol(d) * nbar[i] * np.linalg.norm(qn[s_idx[i], heads], axis=-1)
+        assert np.all(np.abs(got[s_idx[i], heads, t_idx[i]] - want) <= tol)
+
+
+def test_zero_sizes_and_errors():
+    lib, _ = _codecs(64, 2)
+    empty = tq.alloc_polar_codes(lib, 0)
+    x = torch.zeros((0, 64), device="cuda")
+    tq.polar_encode(lib, x, out=empty)
+    q = torch.zeros((1, 2, 64), device="cuda")
+    tq.polar_scores(lib, q, empty, 0, 1, logits=torch.zeros((1, 2, 0), device="cuda"))
+    bad = tq.alloc_polar_codes(lib, 4, stride=lib.stride - 4)
+    with pytest.raises(tq.TQError):
+        tq.polar_encode(lib, torch.zeros((4, 64), device="cuda"), out=bad)

@@ -208,3 +208,58 @@ def test_many_heads_per_kv_head_need_a_workspace():
     q, lg, S = ctypes.c_void_p(0x60000), ctypes.c_void_p(0x70000), ctypes.c_void_p(0)
     assert L.tq_scores(ctypes.byref(cc), q, 2, 64, 2, 16, _fake_codes(), lg, None, 0, S) == -4
     assert L.tq_scores(ctypes.byref(cc), q, 2, 64, 2, 16, _fake_codes(), lg, ctypes.c_void_p(0x80010), need, S) == -3
+
+
+# ------------------------------------------------------------------ recursive polar stage
+
+
+@pytest.mark.parametrize("d,ab", [(64, 2), (128, 2), (128, 3), (256, 4), (16, 1)])
+def test_polar_tables_match_oracle(d, ab):
+    # the library integrates each level's law with Gauss-Legendre panels and starts from
+    # quantiles found by bisection; the oracle uses the regularised incomplete beta function
+    from oracle import polar as op
+
+    t = tq.make_polar_tables(d, ab)
+    pc = op.make_polar_codec(d, ab, 1)
+    n = 1 << ab
+    for l, lv in enumerate(pc.levels):
+        ref = np.stack([lv.cos, lv.sin, np.r_[lv.c2, 0.0], np.r_[lv.s2, 0.0]]).astype(np.float32)
+        assert np.max(np.abs(t[l].astype(np.float64) - ref)) <= 1e-6, (l, t[l], ref)
+        assert t[l, 2, n - 1] == 0 and t[l, 3, n - 1] == 0
+
+
+def test_polar_record_bytes_and_errors():
+    L = tq.lib
+    for d, ab in ((64, 2), (128, 2), (128, 3), (256, 4), (1024, 8)):
+        nb = (d // 2) * (2 + ab) + (d // 2 - 1) * ab
+        assert tq.polar_record_bytes(d, ab) == 4 * ((nb + 31) // 32)
+    assert tq.polar_record_bytes(128, 2) == 48  # + 4-byte norm word: 52 bytes per key
+    assert L.tq_polar_record_bytes(96, 2) == 0 and L.tq_polar_record_bytes(128, 0) == 0
+    out = np.empty(4 * 7 * 4, np.float32)
+    assert L.tq_make_polar_tables(96, 2, out.ctypes.data) == -1
+    assert L.tq_make_polar_tables(128, 9, out.ctypes.data) == -1
+    assert L.tq_make_polar_tables(128, 2, None) == -1
+
+    fake = 0x10000
+    S = ctypes.c_void_p(0)
+    x, q, lg = ctypes.c_void_p(0x50000), ctypes.c_void_p(0x60000), ctypes.c_void_p(0x70000)
+    pc = tq._PolarCodec(128, 2, 1, 0, fake, fake)
+    codes = tq._PolarCodes(0x20000, 48, 0x40000)
+    E = L.tq_polar_encode
+    assert E(None, x, 0, 4, 128, 0, 0, codes, None, S) == -1
+    assert E(ctypes.byref(tq._PolarCodec(96, 2, 1, 0, fake, fake)), x, 0, 4, 96, 0, 0, codes, None, S) == -2
+    assert E(ctypes.byref(tq._PolarCodec(128, 5, 1, 0, fake, fake)), x, 0, 4, 128, 0, 0, codes, None, S) == -2
+    assert E(ctypes.byref(tq._PolarCodec(128, 2, 1, 0, fake, 0)), x, 0, 4, 128, 0, 0, codes, None, S) == -1
+    assert E(ctypes.byref(tq._PolarCodec(128, 2, 1, 0, fake + 4, fake)), x, 0, 4, 128, 0, 0, codes, None, S) == -3
+    assert E(ctypes.byref(pc), x, 0, 4, 100, 0, 0, codes, None, S) == -1       # ld_x < d
+    assert E(ctypes.byref(pc), x, 1, 4, 128, 1, 0, codes, None, S) == -1       # pre-rotated needs fp32
+    assert E(ctypes.byref(pc), x, 0, 4, 128, 2, 0, codes, None, S) == -1       # unknown flag
+    assert E(ctypes.byref(pc), x, 0, 4, 128, 0, 0, tq._PolarCodes(0x20000, 44, 0x40000), None, S) == -1
+    assert E(ctypes.byref(pc), x, 0, 4, 128, 0, 0, tq._PolarCodes(0x20000, 52, 0x40000), None, S) == -3
+    assert E(ctypes.byref(pc), x, 0, 4, 128, 0, 0, tq._PolarCodes(0x20008, 48, 0x40000), None, S) == -3
+    assert E(ctypes.byref(pc), x, 0, 0, 128, 0, 0, codes, None, S) == 0        # nothing to do
+    P = L.tq_polar_scores
+    assert P(ctypes.byref(pc), q, 1, 6, 4, 16, codes, lg, S) == -1              # hq % hkv != 0
+    assert P(ctypes.byref(pc), q, 1, 8, 2, 16, tq._PolarCodes(0x20000, 40, 0x40000), lg, S) == -1
+    assert P(ctypes.byref(pc), None, 1, 8, 2, 16, codes, lg, S) == -1
+    assert P(ctypes.byref(pc), q, 0, 8, 2, 16, codes, lg, S) == 0

@@ -39,6 +39,15 @@ class _Codes(ctypes.Structure):
                 ("norms", ctypes.c_void_p)]
 
 
+class _PolarCodec(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("ab", ctypes.c_int32), ("n_rot", ctypes.c_int32),
+                ("vecs_per_rot", ctypes.c_int64), ("rot", ctypes.c_void_p), ("tables", ctypes.c_void_p)]
+
+
+class _PolarCodes(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_void_p), ("stride", ctypes.c_int64), ("norms", ctypes.c_void_p)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libtq.so not built: {LIB_PATH} is missing "
@@ -46,6 +55,7 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
     CP = ctypes.POINTER(_Codec)
+    PP = ctypes.POINTER(_PolarCodec)
     sig = {
         "tq_make_rotation": ([U64, I32, P], I32),
         "tq_make_head_rotations": ([U64, P, I32, I32, P], I32),
@@ -60,6 +70,10 @@ def _load():
         "tq_decode_step": ([CP, CP, P, P, P, I32, I64, I32, I32, I64, P, ctypes.c_float, _Codes, _Codes,
                             ctypes.c_float, P, P, SZ, P], I32),
         "tq_workspace_bytes": ([ctypes.c_int, CP, CP, I64, I32, I32, I64], SZ),
+        "tq_make_polar_tables": ([I32, I32, P], I32),
+        "tq_polar_record_bytes": ([I32, I32], SZ),
+        "tq_polar_encode": ([PP, P, I32, I64, I64, ctypes.c_uint32, I64, _PolarCodes, P, P], I32),
+        "tq_polar_scores": ([PP, P, I64, I32, I32, I64, _PolarCodes, P, P], I32),
         "tq_status_str": ([ctypes.c_int], ctypes.c_char_p),
         "tq_version": ([], ctypes.c_char_p),
     }
@@ -74,7 +88,8 @@ lib = _load()
 EXPORTED = ("tq_make_rotation", "tq_make_head_rotations", "tq_make_sketch", "tq_make_codebook",
             "tq_calibrate_codebook", "tq_encode",
             "tq_scores", "tq_attend_decode", "tq_append", "tq_decode_step", "tq_search_topk",
-            "tq_workspace_bytes", "tq_status_str", "tq_version")
+            "tq_workspace_bytes", "tq_status_str", "tq_version", "tq_make_polar_tables",
+            "tq_polar_record_bytes", "tq_polar_encode", "tq_polar_scores")
 
 
 def _check(rc):
@@ -355,3 +370,111 @@ def search_topk(codec: Codec, queries, db: Codes, n_db: int, k: int):
     _check(lib.tq_search_topk(ctypes.byref(cc), _ptr(queries), n_q, db.c(), n_db, k, _ptr(idx), _ptr(sc), ws, wsb,
                               _stream()))
     return idx, sc
+
+
+# ------------------------------------------------------------------ recursive polar stage 1
+
+
+def make_polar_tables(d: int, ab: int) -> np.ndarray:
+    """Per-level angle tables [L, 4, 2^ab] fp32 (cos, sin of the levels; cos^2, sin^2 of the
+    thresholds, zero-padded)."""
+    L = int(d).bit_length() - 1
+    out = np.empty((L, 4, 1 << ab), np.float32)
+    _check(lib.tq_make_polar_tables(d, ab, out.ctypes.data))
+    return out
+
+
+def polar_record_bytes(d: int, ab: int) -> int:
+    return int(lib.tq_polar_record_bytes(d, ab))
+
+
+@dataclass
+class PolarCodec:
+    d: int
+    ab: int
+    rot: object     # torch [n_rot, d, d] fp32 on device
+    tables: object  # torch [L, 4, 2^ab] fp32 on device
+    vecs_per_rot: int = 0
+
+    @property
+    def n_rot(self) -> int:
+        return int(self.rot.shape[0])
+
+    def c(self) -> _PolarCodec:
+        return _PolarCodec(self.d, self.ab, self.n_rot, self.vecs_per_rot, self.rot.data_ptr(),
+                           self.tables.data_ptr())
+
+    @property
+    def stride(self) -> int:
+        return polar_record_bytes(self.d, self.ab)
+
+
+def polar_codec_from_arrays(d, ab, rot, tables, vecs_per_rot=0, device="cuda") -> PolarCodec:
+    torch = _torch()
+    rot = np.asarray(rot, np.float32)
+    if rot.ndim == 2:
+        rot = rot[None]
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+
+    return PolarCodec(d, ab, dev(rot), dev(tables), vecs_per_rot)
+
+
+def make_polar_codec(d: int, ab: int, rot_seed: int, basis_seeds=None, vecs_per_rot: int = 0,
+                     device="cuda") -> PolarCodec:
+    """A polar codec from the library's own host constructors."""
+    rot = make_rotation(rot_seed, d) if basis_seeds is None else make_head_rotations(rot_seed, basis_seeds, d)
+    return polar_codec_from_arrays(d, ab, rot, make_polar_tables(d, ab), vecs_per_rot, device)
+
+
+@dataclass
+class PolarCodes:
+    bits: object   # torch uint8 [n, stride]
+    norms: object  # torch int32 [n] (uint32 bit patterns)
+
+    def c(self) -> _PolarCodes:
+        return _PolarCodes(self.bits.data_ptr(), int(self.bits.shape[1]), self.norms.data_ptr())
+
+    @property
+    def n(self) -> int:
+        return int(self.bits.shape[0])
+
+    def numpy(self):
+        return self.bits.cpu().numpy(), self.norms.cpu().numpy().view(np.uint32)
+
+
+def alloc_polar_codes(pc: PolarCodec, n: int, device="cuda", stride: Optional[int] = None) -> PolarCodes:
+    torch = _torch()
+    bits = torch.empty((n, stride or pc.stride), dtype=torch.uint8, device=device)
+    norms = torch.empty((n,), dtype=torch.int32, device=device)
+    return PolarCodes(bits, norms)
+
+
+def polar_encode(pc: PolarCodec, x, pre_rotated: bool = False, first: int = 0, out: Optional[PolarCodes] = None,
+                 y_tap=None) -> PolarCodes:
+    """Encode rows of ``x`` ([n, d] or [..., d], contiguous rows) with the recursive polar stage."""
+    x2 = x.reshape(-1, x.shape[-1])
+    if x2.stride(-1) != 1:
+        raise ValueError("x rows must be contiguous")
+    n = x2.shape[0]
+    out = out or alloc_polar_codes(pc, n, x.device)
+    dt = _DT[str(x.dtype).replace("torch.", "")]
+    flags = TQ_ENC_PRE_ROTATED if pre_rotated else 0
+    cc = pc.c()
+    _check(lib.tq_polar_encode(ctypes.byref(cc), _ptr(x2), dt, n, x2.stride(0), flags, first, out.c(),
+                               _ptr(y_tap), _stream()))
+    return out
+
+
+def polar_scores(pc: PolarCodec, q, codes: PolarCodes, n_keys: int, hkv: int, logits=None):
+    """Logits [n_seq, hq, n_keys] = nbar <Pi q, u^> over polar codes [n_seq][hkv][n_keys]."""
+    torch = _torch()
+    n_seq, hq, d = q.shape
+    q = q.contiguous()
+    if logits is None:
+        logits = torch.empty((n_seq, hq, n_keys), dtype=torch.float32, device=q.device)
+    cc = pc.c()
+    _check(lib.tq_polar_scores(ctypes.byref(cc), _ptr(q), n_seq, hq, hkv, n_keys, codes.c(), _ptr(logits),
+                               _stream()))
+    return logits

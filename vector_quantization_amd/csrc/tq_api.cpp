@@ -173,3 +173,57 @@ extern "C" int tq_search_topk(const tq_codec *c, const float *queries, int64_t n
   return tq::launch_search(tq::view(*c), queries, n_q, tq::view(db), n_db, k, out_idx, out_score, ws, ws_bytes,
                            stream);
 }
+
+namespace {
+
+int check_polar(const tq_polar_codec *pc) {
+  if (!pc) return TQ_EINVAL;
+  if (!tq::supported_polar(pc->d, pc->ab)) return TQ_EUNSUPPORTED;
+  if (!pc->rot || !pc->tables || pc->n_rot < 1 || pc->vecs_per_rot < 0) return TQ_EINVAL;
+  if (!aligned(pc->rot, 16) || !aligned(pc->tables, 4)) return TQ_EALIGN;
+  return TQ_OK;
+}
+
+int check_polar_codes(const tq_polar_codec *pc, const tq_polar_codes &k) {
+  if (!k.bits || !k.norms) return TQ_EINVAL;
+  const int64_t words = (tq::polar_record_bits(pc->d, pc->ab) + 31) / 32;
+  if (k.stride < 4 * words) return TQ_EINVAL;
+  if (k.stride % vec_bytes(words) != 0 || !aligned(k.bits, 16) || !aligned(k.norms, 4)) return TQ_EALIGN;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" size_t tq_polar_record_bytes(int32_t d, int32_t ab) {
+  if (d < 4 || d > 1024 || (d & (d - 1)) != 0 || ab < 1 || ab > 8) return 0;
+  return (size_t)(4 * ((tq::polar_record_bits(d, ab) + 31) / 32));
+}
+
+extern "C" int tq_polar_encode(const tq_polar_codec *pc, const void *x, tq_dtype dt, int64_t n, int64_t ld_x,
+                               uint32_t flags, int64_t first, tq_polar_codes out, float *y_tap, void *stream) {
+  int rc = check_polar(pc);
+  if (rc != TQ_OK) return rc;
+  if (n < 0 || first < 0) return TQ_EINVAL;
+  if (n == 0) return TQ_OK;
+  if (!x || ld_x < pc->d) return TQ_EINVAL;
+  if (dt != TQ_F32 && dt != TQ_F16 && dt != TQ_BF16) return TQ_EINVAL;
+  const bool pre = (flags & TQ_ENC_PRE_ROTATED) != 0;
+  if ((flags & ~TQ_ENC_PRE_ROTATED) != 0) return TQ_EINVAL;
+  if (pre && dt != TQ_F32) return TQ_EINVAL;
+  rc = check_polar_codes(pc, out);
+  if (rc != TQ_OK) return rc;
+  return tq::launch_polar_encode(tq::view(*pc), x, (int)dt, n, ld_x, pre, first, tq::view(out), y_tap, stream);
+}
+
+extern "C" int tq_polar_scores(const tq_polar_codec *pc, const float *q, int64_t n_seq, int32_t hq, int32_t hkv,
+                               int64_t n_keys, tq_polar_codes k, float *logits, void *stream) {
+  int rc = check_polar(pc);
+  if (rc != TQ_OK) return rc;
+  if (n_seq < 0 || n_keys < 0 || hq < 1 || hkv < 1 || hq % hkv != 0) return TQ_EINVAL;
+  if (n_seq == 0 || n_keys == 0) return TQ_OK;
+  if (!q || !logits) return TQ_EINVAL;
+  rc = check_polar_codes(pc, k);
+  if (rc != TQ_OK) return rc;
+  const tq::ScoreShape s{n_seq, hq, hkv, n_keys};
+  return tq::launch_polar_scores(tq::view(*pc), q, s, tq::view(k), logits, stream);
+}

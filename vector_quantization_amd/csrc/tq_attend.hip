@@ -44,29 +44,6 @@ struct AttArgs {
   const int32_t *pos;  // decode step: sequence s attends over tokens 0 .. pos[s] (nullptr: all n_ctx)
 };
 
-template <int W>
-__device__ __forceinline__ void load_words_a(const uint8_t *p, uint32_t (&w)[W]) {
-  if constexpr (W % 4 == 0) {
-    const uint4 *p4 = reinterpret_cast<const uint4 *>(p);
-#pragma unroll
-    for (int i = 0; i < W / 4; ++i) {
-      const uint4 v = p4[i];
-      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-    }
-  } else if constexpr (W % 2 == 0) {
-    const uint2 *p2 = reinterpret_cast<const uint2 *>(p);
-#pragma unroll
-    for (int i = 0; i < W / 2; ++i) {
-      const uint2 v = p2[i];
-      w[2 * i] = v.x; w[2 * i + 1] = v.y;
-    }
-  } else {
-    const uint32_t *p1 = reinterpret_cast<const uint32_t *>(p);
-#pragma unroll
-    for (int i = 0; i < W; ++i) w[i] = p1[i];
-  }
-}
-
 template <int D, int KB, int KM, int VB, int VM, int G, int NT>
 __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   using CK = Lut<D, KB, KM, G>;
@@ -195,11 +172,11 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   auto load_rec = [&](int64_t t, Rec &r) {
     if (t < t1) {
       const int64_t v = vbase + t;
-      load_words_a<CK::IW>(a.kidx + v * a.kidx_stride, r.iw);
-      if constexpr (KM > 0) load_words_a<CK::SW>(a.ksign + v * a.ksign_stride, r.sw);
+      load_words<CK::IW>(a.kidx + v * a.kidx_stride, r.iw);
+      if constexpr (KM > 0) load_words<CK::SW>(a.ksign + v * a.ksign_stride, r.sw);
       r.nw = a.knorms[v];
-      load_words_a<IWV>(a.vidx + v * a.vidx_stride, r.vw);
-      if constexpr (VM > 0) load_words_a<SWV>(a.vsign + v * a.vsign_stride, r.vs);
+      load_words<IWV>(a.vidx + v * a.vidx_stride, r.vw);
+      if constexpr (VM > 0) load_words<SWV>(a.vsign + v * a.vsign_stride, r.vs);
       r.vnw = a.vnorms[v];
     }
   };

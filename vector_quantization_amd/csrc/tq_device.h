@@ -5,6 +5,8 @@
 #include <hip/hip_fp16.h>
 #include <cstdint>
 
+#include "../../include/tq.h"
+
 namespace tq {
 
 constexpr int kWave = 64;
@@ -129,6 +131,88 @@ __device__ inline int expansion_sign(const double *terms, int n, double *buf) {
   }
   if (len == 0) return 0;
   return buf[len - 1] > 0.0 ? 1 : -1;
+}
+
+// ---------------------------------------------------------------- encoder helpers
+
+template <int TIN>
+__device__ __forceinline__ float load_in(const void *p, int64_t off) {
+  if constexpr (TIN == TQ_F32) return reinterpret_cast<const float *>(p)[off];
+  else if constexpr (TIN == TQ_F16) return __half2float(reinterpret_cast<const __half *>(p)[off]);
+  else return bf16_bits_to_float(reinterpret_cast<const uint16_t *>(p)[off]);
+}
+
+// fp16 bits of the exactly rounded norm of the D values held C per lane.
+template <int D, int C>
+__device__ uint32_t wave_norm_f16(const float (&v)[C], double *terms, double *buf) {
+  const int lane = lane_id();
+  double s = 0.0;
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+    if (lane + kWave * c < D) s += (double)v[c] * (double)v[c];
+  s = wave_sum(s);  // every lane holds the same value (the butterfly is symmetric)
+  const double slack = 4.0 * (D + 2) * 0x1p-53;
+  uint32_t h = f64_to_f16_rne(sqrt(s));
+  bool ok = h < 0x7C00u;
+  if (ok) {
+    const double vh = f16_bits_to_double_ext(h);
+    const double up = 0.5 * (vh + f16_bits_to_double_ext(h + 1));
+    if (!(s < up * up * (1.0 - slack))) ok = false;
+    if (h > 0) {
+      const double dn = 0.5 * (vh + f16_bits_to_double_ext(h - 1));
+      if (!(s > dn * dn * (1.0 + slack))) ok = false;
+    }
+  }
+  if (ok) return h;
+  // Exact decision: compare the exact sum of squares with squared midpoints.
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+    if (lane + kWave * c < D) terms[lane + kWave * c] = (double)v[c] * (double)v[c];
+  wave_lds_fence();
+  uint32_t hh = h >= 0x7C00u ? 0x7BFFu : h;
+  if (lane == 0) {
+    while (hh < 0x7C00u) {
+      const double mu = 0.5 * (f16_bits_to_double_ext(hh) + f16_bits_to_double_ext(hh + 1));
+      terms[D] = -(mu * mu);
+      const int cmp = expansion_sign(terms, D + 1, buf);
+      if (cmp > 0 || (cmp == 0 && ((hh + 1) & 1u) == 0)) ++hh;
+      else break;
+    }
+    while (hh > 0) {
+      const double mu = 0.5 * (f16_bits_to_double_ext(hh - 1) + f16_bits_to_double_ext(hh));
+      terms[D] = -(mu * mu);
+      const int cmp = expansion_sign(terms, D + 1, buf);
+      if (cmp < 0 || (cmp == 0 && ((hh - 1) & 1u) == 0)) --hh;
+      else break;
+    }
+  }
+  wave_lds_fence();
+  return (uint32_t)__shfl((int)hh, 0, kWave);
+}
+
+// The W 32-bit words of one record at p, in 16-, 8- or 4-byte loads by W (record strides
+// and base pointers aligned to that width).
+template <int W>
+__device__ __forceinline__ void load_words(const uint8_t *p, uint32_t (&w)[W]) {
+  if constexpr (W % 4 == 0) {
+    const uint4 *p4 = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const uint4 v = p4[i];
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (W % 2 == 0) {
+    const uint2 *p2 = reinterpret_cast<const uint2 *>(p);
+#pragma unroll
+    for (int i = 0; i < W / 2; ++i) {
+      const uint2 v = p2[i];
+      w[2 * i] = v.x; w[2 * i + 1] = v.y;
+    }
+  } else {
+    const uint32_t *p1 = reinterpret_cast<const uint32_t *>(p);
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = p1[i];
+  }
 }
 
 }  // namespace tq

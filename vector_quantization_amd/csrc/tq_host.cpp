@@ -202,6 +202,98 @@ int lloyd_max_codebook(int d, int bits, std::vector<double> &c, std::vector<doub
   return TQ_OK;
 }
 
+// Law of a polar node's angle psi = atan2(r_b, r_a) on [0, pi/2] when each child holds k
+// coordinates of a uniform unit vector (hada.io TurboQuant page, "PolarQuant: um novo 'ângulo'
+// para compressão": the angles' law is known and concentrated): r_a^2 / (r_a^2 + r_b^2) is
+// Beta(k/2, k/2), so psi has density 2 / B(k/2, k/2) sin^(k-1) psi cos^(k-1) psi (uniform for
+// k = 1).
+struct AngleLaw {
+  int k;
+  double logc;
+  std::vector<double> gx, gw;
+  explicit AngleLaw(int k_) : k(k_) {
+    logc = std::log(2.0) + std::lgamma((double)k) - 2.0 * std::lgamma(0.5 * k);
+    gauss_legendre(48, gx, gw);
+  }
+  double density(double p) const {
+    if (k == 1) return 2.0 / M_PI;
+    const double sc = std::sin(p) * std::cos(p);
+    if (sc <= 0.0) return 0.0;
+    return std::exp(logc + (k - 1) * std::log(sc));
+  }
+  void cell(double a, double b, double &mass, double &mom) const {
+    const int panels = 16;
+    mass = 0.0;
+    mom = 0.0;
+    const double h = (b - a) / panels;
+    for (int p = 0; p < panels; ++p) {
+      const double lo = a + p * h, hi = (p + 1 == panels) ? b : a + (p + 1) * h;
+      const double half = 0.5 * (hi - lo), mid = 0.5 * (hi + lo);
+      double pm = 0.0, pq = 0.0;
+      for (size_t i = 0; i < gx.size(); ++i) {
+        const double x = mid + half * gx[i];
+        const double f = density(x) * gw[i];
+        pm += f;
+        pq += f * x;
+      }
+      mass += pm * half;
+      mom += pq * half;
+    }
+  }
+};
+
+// Lloyd-Max levels of AngleLaw(k) with L levels, ascending in [0, pi/2], symmetric about pi/4.
+// k = 1: the uniform law's equal cells.  Otherwise the law's quantiles (j + 1/2) / L start the
+// iteration, so every cell holds mass however concentrated the law is.
+int polar_angle_levels(int k, int L, std::vector<double> &c) {
+  const double half = 0.5 * M_PI;
+  c.resize(L);
+  if (k == 1) {
+    for (int j = 0; j < L; ++j) c[j] = (j + 0.5) * half / L;
+    return TQ_OK;
+  }
+  AngleLaw law(k);
+  for (int j = 0; j < L; ++j) {
+    const double target = (j + 0.5) / L;
+    double lo = 0.0, hi = half;
+    for (int it = 0; it < 64; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      double mass, mom;
+      law.cell(0.0, mid, mass, mom);
+      (mass < target ? lo : hi) = mid;
+    }
+    c[j] = 0.5 * (lo + hi);
+  }
+  std::vector<double> nc(L);
+  double best = INFINITY;
+  int since = 0;
+  bool done = false;
+  for (int it = 0; it < 400000 && !done; ++it) {
+    double maxc = 0.0, step = 0.0;
+    for (int j = 0; j < L; ++j) {
+      const double a = (j == 0) ? 0.0 : 0.5 * (c[j - 1] + c[j]);
+      const double b = (j == L - 1) ? half : 0.5 * (c[j] + c[j + 1]);
+      double mass, mom;
+      law.cell(a, b, mass, mom);
+      nc[j] = mass > 0.0 ? mom / mass : c[j];
+    }
+    for (int j = 0; j < L; ++j) {
+      maxc = std::fmax(maxc, std::fabs(nc[j]));
+      step = std::fmax(step, std::fabs(nc[j] - c[j]));
+    }
+    c = nc;
+    step /= maxc;
+    if (step <= 1e-13) done = true;
+    else if (step < best) { best = step; since = 0; }
+    else if (best <= 1e-11 && ++since >= 200) done = true;
+  }
+  if (!done) return TQ_EINVAL;
+  std::vector<double> sym(L);
+  for (int j = 0; j < L; ++j) sym[j] = 0.5 * (c[j] + (half - c[L - 1 - j]));
+  c = sym;
+  return TQ_OK;
+}
+
 }  // namespace tq
 
 // ------------------------------------------------------------------------ C ABI
@@ -308,6 +400,32 @@ extern "C" int tq_make_codebook(int32_t d, int32_t bits, float *host_centroids,
   if (st != TQ_OK) return st;
   for (size_t j = 0; j < c.size(); ++j) host_centroids[j] = (float)c[j];
   for (size_t j = 0; j < t.size(); ++j) host_thresholds[j] = (float)t[j];
+  return TQ_OK;
+}
+
+extern "C" int tq_make_polar_tables(int32_t d, int32_t ab, float *host_tables) {
+  if (!host_tables) return TQ_EINVAL;
+  int levels = 0;
+  while ((1 << levels) < d) ++levels;
+  if (d < 4 || (1 << levels) != d || d > 1024 || ab < 1 || ab > 8) return TQ_EINVAL;
+  const int n = 1 << ab;
+  for (int l = 1; l <= levels; ++l) {
+    std::vector<double> c;
+    const int st = tq::polar_angle_levels(1 << (l - 1), n, c);
+    if (st != TQ_OK) return st;
+    float *tab = host_tables + (int64_t)(l - 1) * 4 * n;
+    for (int j = 0; j < 4 * n; ++j) tab[j] = 0.0f;
+    for (int j = 0; j < n; ++j) {
+      tab[j] = (float)std::cos(c[j]);
+      tab[n + j] = (float)std::sin(c[j]);
+    }
+    for (int j = 0; j + 1 < n; ++j) {
+      const double t = 0.5 * (c[j] + c[j + 1]);
+      const double ct = std::cos(t), sn = std::sin(t);
+      tab[2 * n + j] = (float)(ct * ct);
+      tab[3 * n + j] = (float)(sn * sn);
+    }
+  }
   return TQ_OK;
 }
 

@@ -67,6 +67,30 @@ int launch_search(const CodecView &c, const float *queries, int64_t n_q, const C
                   int64_t n_db, int k, int64_t *out_idx, float *out_score, void *ws, size_t ws_bytes,
                   void *stream);
 
+// recursive polar stage 1 (tq_polar.hip)
+struct PolarView {
+  int d, ab, n_rot;
+  int64_t vecs_per_rot;
+  const float *rot, *tables;
+};
+struct PolarCodesView {
+  uint8_t *bits;
+  int64_t stride;
+  uint32_t *norms;
+};
+inline PolarView view(const tq_polar_codec &c) {
+  return PolarView{c.d, c.ab, c.n_rot, c.vecs_per_rot, c.rot, c.tables};
+}
+inline PolarCodesView view(const tq_polar_codes &c) { return PolarCodesView{c.bits, c.stride, c.norms}; }
+// bits of one record: (d/2)(2 + ab) pair fields and (d/2 - 1) ab node fields
+inline int64_t polar_record_bits(int d, int ab) { return (int64_t)(d / 2) * (2 + ab) + (int64_t)(d / 2 - 1) * ab; }
+int polar_angle_levels(int k, int L, std::vector<double> &c);
+int launch_polar_encode(const PolarView &pc, const void *x, int dt, int64_t n, int64_t ld_x, bool pre_rotated,
+                        int64_t first, const PolarCodesView &out, float *y_tap, void *stream);
+int launch_polar_scores(const PolarView &pc, const float *q, const ScoreShape &s, const PolarCodesView &k,
+                        float *logits, void *stream);
+inline bool supported_polar(int d, int ab) { return (d == 64 || d == 128 || d == 256) && ab >= 2 && ab <= 4; }
+
 // supported device configurations
 inline bool supported_d(int d) { return d == 64 || d == 128 || d == 200; }
 inline bool supported_bits(int b) { return b >= 2 && b <= 4; }

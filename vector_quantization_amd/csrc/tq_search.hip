@@ -95,29 +95,6 @@ __device__ __forceinline__ float list_insert_lds(float *lsp, int32_t *lip, float
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), k - 1));
 }
 
-template <int W>
-__device__ __forceinline__ void load_words_s(const uint8_t *p, uint32_t (&w)[W]) {
-  if constexpr (W % 4 == 0) {
-    const uint4 *p4 = reinterpret_cast<const uint4 *>(p);
-#pragma unroll
-    for (int i = 0; i < W / 4; ++i) {
-      const uint4 v = p4[i];
-      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-    }
-  } else if constexpr (W % 2 == 0) {
-    const uint2 *p2 = reinterpret_cast<const uint2 *>(p);
-#pragma unroll
-    for (int i = 0; i < W / 2; ++i) {
-      const uint2 v = p2[i];
-      w[2 * i] = v.x; w[2 * i + 1] = v.y;
-    }
-  } else {
-    const uint32_t *p1 = reinterpret_cast<const uint32_t *>(p);
-#pragma unroll
-    for (int i = 0; i < W; ++i) w[i] = p1[i];
-  }
-}
-
 template <int D, int BITS, int M, int G, int NT>
 __global__ __launch_bounds__(NT) void search_scan(SearchArgs a) {
   using C = Lut<D, BITS, M, G>;
@@ -172,8 +149,8 @@ __global__ __launch_bounds__(NT) void search_scan(SearchArgs a) {
     if (valid) {
       uint32_t iw[C::IW];
       uint32_t sw[SWN];
-      load_words_s<C::IW>(a.idx + v * a.idx_stride, iw);
-      if constexpr (M > 0) load_words_s<C::SW>(a.sign + v * a.sign_stride, sw);
+      load_words<C::IW>(a.idx + v * a.idx_stride, iw);
+      if constexpr (M > 0) load_words<C::SW>(a.sign + v * a.sign_stride, sw);
       const uint32_t nw = a.norms[v];
       float am[G], aq[G];
       lut_score<D, BITS, M, G>(iw, sw, tabs, tabs + C::MSE_BYTES, hs, am, aq);
