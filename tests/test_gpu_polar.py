@@ -21,7 +21,9 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 tq = pytest.importorskip("vector_quantization_amd")
 
-# fp32 FMA rotation: (d + 2) 2^-24 of sum_k |Pi_ik x_k| at most, below 2^-13 for d <= 256
+# Rotation error relative to sum_k |Pi_ik x_k|: the MFMA encoder (d = 64, 128, aligned rows) splits
+# each operand into bf16 hi + lo (3 * 2^-16 missed) and accumulates 3d products in fp32
+# (3d 2^-24); the FMA kernel (d = 256, or unaligned rows) (d + 2) 2^-24.  All below 2^-13.
 ROT_BOUND = 2.0 ** -13
 # Logit error bound relative to nbar ||q||.  The rotated query in fp32 is off by at most
 # d 2^-24 ||q|| per coordinate (the rows of Pi are unit vectors), which moves <Pi q, u^> by at
@@ -127,12 +129,31 @@ def test_full_mode_codes_of_the_tap(d, ab, dtype):
     _check_full(x_seen, lib, ora, _gpu_encode(lib, x, pre=False, dtype=tdt, tap=True))
 
 
-def test_full_mode_rotation_blocks():
-    d, ab, n_rot, vpr, first = 128, 2, 40, 32, 64
+@pytest.mark.parametrize("d,dtype", [(128, "float32"), (128, "bfloat16"), (64, "float32")])
+def test_full_mode_rotation_blocks(d, dtype):
+    # 40 blocks of 32 vectors from an offset of two blocks, 40 vectors past the last block (they
+    # take the last rotation); bf16 at d = 128 and d = 64 run the MFMA encoder's block loop,
+    # fp32 at d = 128 the FMA kernel
+    ab, n_rot, vpr, first = 2, 40, 32, 64
     lib, ora = _codecs(d, ab, basis=[500 + i for i in range(n_rot)], vpr=vpr)
     n = n_rot * vpr - first + 40
     x = (np.random.default_rng(9).standard_normal((n, d)) * 3.0).astype(np.float32)
-    _check_full(x, lib, ora, _gpu_encode(lib, x, pre=False, first=first, tap=True), first=first)
+    tdt = getattr(torch, dtype)
+    x_seen = torch.from_numpy(x).to(tdt).to(torch.float32).numpy()
+    _check_full(x_seen, lib, ora, _gpu_encode(lib, x, pre=False, dtype=tdt, first=first, tap=True), first=first)
+
+
+@pytest.mark.parametrize("d,ab", [(64, 3), (128, 2)])
+def test_full_mode_unaligned_rows(d, ab):
+    # rows d + 1 floats apart: not 16-byte aligned, so the FMA kernel encodes them
+    lib, ora = _codecs(d, ab)
+    x = (np.random.default_rng(d).standard_normal((777, d + 1)) * 2.0).astype(np.float32)
+    xt = torch.from_numpy(x).cuda()[:, :d]
+    ytap = torch.empty((x.shape[0], d), dtype=torch.float32, device="cuda")
+    out = tq.polar_encode(lib, xt, y_tap=ytap)
+    torch.cuda.synchronize()
+    bits, norms = out.numpy()
+    _check_full(np.ascontiguousarray(x[:, :d]), lib, ora, (bits, norms, ytap.cpu().numpy()))
 
 
 def _score_case(lib, ora, q, codes_bits, norms, n_keys, hkv):

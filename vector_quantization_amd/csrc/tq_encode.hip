@@ -434,6 +434,158 @@ __device__ __forceinline__ void raw_to_f32(const uint4 (&r)[U4], float (&x)[8]) 
 // 16-vector tiles per wavefront pass: two share each Pi / S fragment read from LDS.  At d = 128
 // an input that needs a lo part takes one (else the registers spill), and so does a codec
 // without sketch, whose one-tile passes fit 4 wavefronts per SIMD (latency is what bounds it).
+// ---- recursive polar stage as the MFMA encoder's epilogue (tq_polar_encode, d = 64, 128)
+//
+// Same record and decisions as polar_encode_kernel: A, B the children's fp32 sums of squares,
+// index #{ j : fl32(B cos^2 tau_j) >= fl32(A sin^2 tau_j) } with the level's table.  Lane
+// (n, g) holds coordinates 32u + 8g + 0..7 of vector n, so levels 1-3 (pairs, quads, octets)
+// stay in the lane; level 4 pairs lanes g, g ^ 1 (one shuffle), level 5 lanes g, g ^ 2, and the
+// levels above combine the lane's own octet groups u.  A node's field goes into the staged
+// record (LDS, zeroed per tile) by an LDS OR; every lane of a vector computes the shared nodes
+// with the same operands, and one of them stores each.
+
+template <int D>
+constexpr int log2_d() { return D == 64 ? 6 : D == 128 ? 7 : 8; }
+
+// OR `width` (<= 32) bits of val into the LDS record at bit p.
+__device__ __forceinline__ void or_field(uint32_t *rec, int p, uint32_t val, int width) {
+  const int w = p >> 5, o = p & 31;
+  atomicOr(&rec[w], val << o);
+  if (o + width > 32) atomicOr(&rec[w + 1], val >> (32 - o));
+}
+
+// Thresholds of one level (cos^2 tau, sin^2 tau) from the LDS copy of the tables.
+template <int NA>
+struct PolarLevelTh {
+  float c2[NA - 1], s2[NA - 1];
+  __device__ __forceinline__ void load(const float *ptab, int level) {
+#pragma unroll
+    for (int j = 0; j < NA - 1; ++j) {
+      c2[j] = ptab[(2 * level) * NA + j];
+      s2[j] = ptab[(2 * level + 1) * NA + j];
+    }
+  }
+  __device__ __forceinline__ uint32_t decide(float A, float B) const {
+    uint32_t k = 0;
+#pragma unroll
+    for (int j = 0; j < NA - 1; ++j) k += (__fmul_rn(B, c2[j]) >= __fmul_rn(A, s2[j])) ? 1u : 0u;
+    return k;
+  }
+};
+
+template <int D, int AB, int NV, int KS>
+__device__ void polar_tail(const float (&yv)[NV][KS][8], const uint32_t (&n16)[NV], int64_t v0, const EncArgs &a,
+                           uint32_t *stg, const float *ptab) {
+  constexpr int NA = 1 << AB, WP = 2 + AB, NP = D / 2, P0 = NP * WP;
+  constexpr int NWD = (P0 + (NP - 1) * AB + 31) / 32;  // record words
+  constexpr int LV = log2_d<D>();
+  static_assert(KS == D / 32 && (D == 64 || D == 128), "lane layout");
+  const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+  const int sw = (int)(a.idx_stride >> 2);
+  uint32_t *bitsw = reinterpret_cast<uint32_t *>(a.idx);
+  auto node_bit = [](int l, int i) { return P0 + AB * (NP - (D >> (l - 1)) + i); };
+#pragma unroll
+  for (int t = 0; t < NV; ++t) {
+    for (int e = lane; e < 16 * NWD; e += kWave) stg[e] = 0u;
+    wave_lds_fence();
+    uint32_t *rec = stg + n * NWD;
+    // level 1: pairs 16u + 4g + p (p < 4), one run of 4 fields per octet
+    float s1[KS][4];
+    {
+      PolarLevelTh<NA> th;
+      th.load(ptab, 0);
+#pragma unroll
+      for (int u = 0; u < KS; ++u) {
+        uint32_t run = 0u;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float ya = yv[t][u][2 * p], yb = yv[t][u][2 * p + 1];
+          const float A = __fmul_rn(ya, ya), B = __fmul_rn(yb, yb);
+          const uint32_t f = (ya < 0.0f ? 1u : 0u) | (yb < 0.0f ? 2u : 0u) | (th.decide(A, B) << 2);
+          run |= f << (WP * p);
+          s1[u][p] = __fadd_rn(A, B);
+        }
+        or_field(rec, WP * (16 * u + 4 * g), run, 4 * WP);
+      }
+    }
+    // level 2: nodes 8u + 2g + {0, 1}
+    float s2[KS][2];
+    {
+      PolarLevelTh<NA> th;
+      th.load(ptab, 1);
+#pragma unroll
+      for (int u = 0; u < KS; ++u) {
+        const uint32_t k0 = th.decide(s1[u][0], s1[u][1]), k1 = th.decide(s1[u][2], s1[u][3]);
+        s2[u][0] = __fadd_rn(s1[u][0], s1[u][1]);
+        s2[u][1] = __fadd_rn(s1[u][2], s1[u][3]);
+        or_field(rec, node_bit(2, 8 * u + 2 * g), k0 | (k1 << AB), 2 * AB);
+      }
+    }
+    // level 3: node 4u + g
+    float s3[KS];
+    {
+      PolarLevelTh<NA> th;
+      th.load(ptab, 2);
+#pragma unroll
+      for (int u = 0; u < KS; ++u) {
+        or_field(rec, node_bit(3, 4 * u + g), th.decide(s2[u][0], s2[u][1]), AB);
+        s3[u] = __fadd_rn(s2[u][0], s2[u][1]);
+      }
+    }
+    // level 4: node 2u + (g >> 1) from the level-3 nodes of lanes g & ~1 (A) and g | 1 (B)
+    float s4[KS];
+    {
+      PolarLevelTh<NA> th;
+      th.load(ptab, 3);
+#pragma unroll
+      for (int u = 0; u < KS; ++u) {
+        const float o = __shfl_xor(s3[u], 16, kWave);
+        const float A = (g & 1) ? o : s3[u], B = (g & 1) ? s3[u] : o;
+        const uint32_t k = th.decide(A, B);
+        if ((g & 1) == 0) or_field(rec, node_bit(4, 2 * u + (g >> 1)), k, AB);
+        s4[u] = __fadd_rn(A, B);
+      }
+    }
+    // level 5: node u from the level-4 nodes of lanes g & ~2 (A) and g | 2 (B)
+    float cur[KS];
+    {
+      PolarLevelTh<NA> th;
+      th.load(ptab, 4);
+#pragma unroll
+      for (int u = 0; u < KS; ++u) {
+        const float o = __shfl_xor(s4[u], 32, kWave);
+        const float A = (g & 2) ? o : s4[u], B = (g & 2) ? s4[u] : o;
+        const uint32_t k = th.decide(A, B);
+        if (g == 0) or_field(rec, node_bit(5, u), k, AB);
+        cur[u] = __fadd_rn(A, B);
+      }
+    }
+    // levels 6 .. L: the octet groups u within the lane (every lane holds the same values)
+#pragma unroll
+    for (int l = 6; l <= LV; ++l) {
+      PolarLevelTh<NA> th;
+      th.load(ptab, l - 1);
+      const int cnt = D >> l;
+#pragma unroll
+      for (int i = 0; i < cnt; ++i) {
+        const uint32_t k = th.decide(cur[2 * i], cur[2 * i + 1]);
+        if (g == 0) or_field(rec, node_bit(l, i), k, AB);
+        cur[i] = __fadd_rn(cur[2 * i], cur[2 * i + 1]);
+      }
+    }
+    wave_lds_fence();
+    // the tile's 16 records -> HBM (pad words zero), then the norm words
+    for (int e = lane; e < 16 * sw; e += kWave) {
+      const int vv = e / sw, w = e % sw;
+      const int64_t v = v0 + 16 * t + vv;
+      if (v < a.n) bitsw[v * sw + w] = w < NWD ? stg[vv * NWD + w] : 0u;
+    }
+    wave_lds_fence();
+    const int64_t v = v0 + 16 * t + n;
+    if (g == 0 && v < a.n) a.norms[v] = n16[t];
+  }
+}
+
 template <int D, int M, int TIN, bool PRE>
 constexpr int enc_tiles() {
   return (D == 128 && (M == 0 || (!PRE && TIN != TQ_BF16))) ? 1 : 2;
@@ -444,7 +596,9 @@ constexpr int enc_waves() {
   return (D == 128 && M == 0 && !PRE && TIN == TQ_BF16 && BITS <= 3) ? 16 : 8;
 }
 
-template <int D, int BITS, int M, int TIN, bool PRE, int NW, bool ROTS>
+// AB > 0: the recursive polar stage with AB angle bits (M = 0; a.thresholds holds the polar
+// tables, a.idx / a.idx_stride the records) in place of steps 3-5.
+template <int D, int BITS, int M, int TIN, bool PRE, int NW, bool ROTS, int AB = 0>
 __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
   constexpr int KS = D / 32;   // k-steps; also 8-coordinate groups u per lane
   constexpr int CT = D / 16;   // 16-row tiles of y
@@ -463,6 +617,10 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
   __shared__ __align__(16) double wscr[NW][2 * (D + 2)];
   __shared__ float cbs[L];
   __shared__ float smax_s;
+  // polar: cos^2 tau and sin^2 tau of every level, [level][2][2^AB]
+  __shared__ float ptab[AB > 0 ? log2_d<D>() * 2 * (1 << AB) : 1];
+  static_assert(AB == 0 || (M == 0 && 16 * ((D / 2 * (2 + AB) + (D / 2 - 1) * AB + 31) / 32) * 4 <= 2 * (D + 2) * 8),
+                "polar records of a tile fit the staging");
 
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   const int n = lane & 15, g = lane >> 4;
@@ -471,7 +629,15 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
   constexpr int IB = D * BITS / 8;  // index bytes per vector
   constexpr int SB = M / 8;         // sign bytes per vector
   static_assert(NV * 16 * IB <= 2 * (D + 2) * 8 && NV * 16 * SB <= 2 * (D + 2) * 8, "staging fits");
-  if (tid < L) cbs[tid] = a.centroids[tid];
+  if constexpr (AB == 0) {
+    if (tid < L) cbs[tid] = a.centroids[tid];
+  } else {
+    constexpr int NA = 1 << AB;
+    for (int e = tid; e < log2_d<D>() * 2 * NA; e += NW * 64) {
+      const int l = e / (2 * NA), r = e % (2 * NA);  // r < NA: cos^2 tau, else sin^2 tau
+      ptab[e] = a.thresholds[(l * 4 + 2) * NA + r];
+    }
+  }
   if constexpr (!PRE && !ROTS) build_afrags<D>(a.rot, D, fpi, NW * 64);
   if constexpr (M > 0) {
     build_afrags<D>(a.sketch, M, fsk, NW * 64);
@@ -491,7 +657,7 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
   }
   float th[L - 1];
 #pragma unroll
-  for (int j = 0; j < L - 1; ++j) th[j] = a.thresholds[j];
+  for (int j = 0; j < L - 1; ++j) th[j] = AB == 0 ? a.thresholds[j] : 0.0f;
   __syncthreads();
   const float smax = M > 0 ? smax_s : 0.0f;
 
@@ -663,6 +829,10 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
             for (int j = 0; j < 8; ++j) a.y_tap[v * D + 32 * u + 8 * g + j] = yv[t][u][j];
         }
       }
+    }
+    if constexpr (AB > 0) {
+      polar_tail<D, AB, NV, KS>(yv, n16, v0, a, reinterpret_cast<uint32_t *>(wscr[wid]), ptab);
+      return;
     }
 
     // ---- 3. indices and residual; 4. residual norm
@@ -942,13 +1112,52 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
   }
 }
 
-template <int D, int BITS, int M, int TIN, bool PRE, bool ROTS = false>
+template <int D, int BITS, int M, int TIN, bool PRE, bool ROTS = false, int AB = 0>
 static void launch_mfma(const EncArgs &a, hipStream_t st) {
   constexpr int NW = ROTS ? 8 : enc_waves<D, BITS, M, TIN, PRE>();
   constexpr int PER_BLOCK = NW * 16 * enc_tiles<D, M, TIN, PRE>();
   int64_t blocks = ROTS ? a.n_rot : (a.n + PER_BLOCK - 1) / PER_BLOCK;
   if (blocks > 256) blocks = 256;
-  hipLaunchKernelGGL((encode_mfma<D, BITS, M, TIN, PRE, NW, ROTS>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((encode_mfma<D, BITS, M, TIN, PRE, NW, ROTS, AB>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, a);
+}
+
+// The recursive polar stage on the MFMA encoder (d = 64, 128; input rows 16-byte aligned; with
+// per-block rotations, blocks and first multiples of 32 and, at d = 128, bf16 input).  Returns
+// TQ_EUNSUPPORTED where these do not hold (the caller then takes polar_encode_kernel).
+template <int D, int AB>
+static int launch_polar_mfma_da(const EncArgs &a, int dt, bool pre, hipStream_t st) {
+  const int eb = dt == TQ_F32 ? 4 : 2;
+  const bool vec_ok = ((uintptr_t)a.x % 16 == 0) && ((a.ld_x * eb) % 16 == 0);
+  const bool rots = a.n_rot > 1 && a.vecs_per_rot > 0;
+  if (!vec_ok) return TQ_EUNSUPPORTED;
+  if (rots) {
+    if (pre || a.vecs_per_rot % 32 != 0 || a.first % 32 != 0 || (D == 128 && dt != TQ_BF16)) return TQ_EUNSUPPORTED;
+    if (dt == TQ_BF16) launch_mfma<D, 2, 0, TQ_BF16, false, true, AB>(a, st);
+    else if constexpr (D == 64) {
+      if (dt == TQ_F32) launch_mfma<D, 2, 0, TQ_F32, false, true, AB>(a, st);
+      else launch_mfma<D, 2, 0, TQ_F16, false, true, AB>(a, st);
+    }
+  } else if (pre) {
+    launch_mfma<D, 2, 0, TQ_F32, true, false, AB>(a, st);
+  } else if (dt == TQ_F32) {
+    launch_mfma<D, 2, 0, TQ_F32, false, false, AB>(a, st);
+  } else if (dt == TQ_F16) {
+    launch_mfma<D, 2, 0, TQ_F16, false, false, AB>(a, st);
+  } else {
+    launch_mfma<D, 2, 0, TQ_BF16, false, false, AB>(a, st);
+  }
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+int launch_polar_mfma(const PolarView &pc, const void *x, int dt, int64_t n, int64_t ld_x, bool pre, int64_t first,
+                      const PolarCodesView &out, float *y_tap, void *stream) {
+  EncArgs a{x, ld_x, n, first, pc.rot, pc.n_rot, pc.vecs_per_rot, nullptr, nullptr, pc.tables,
+            out.bits, out.stride, nullptr, 0, out.norms, y_tap, nullptr, 0, 0, 0.0f, 0.0f};
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+#define TQ_PM(DD, AA) if (pc.d == DD && pc.ab == AA) return launch_polar_mfma_da<DD, AA>(a, dt, pre, st);
+  TQ_PM(64, 2) TQ_PM(64, 3) TQ_PM(64, 4) TQ_PM(128, 2) TQ_PM(128, 3) TQ_PM(128, 4)
+#undef TQ_PM
+  return TQ_EUNSUPPORTED;
 }
 
 template <int D, int BITS, int M>

@@ -87,6 +87,9 @@ inline int64_t polar_record_bits(int d, int ab) { return (int64_t)(d / 2) * (2 +
 int polar_angle_levels(int k, int L, std::vector<double> &c);
 int launch_polar_encode(const PolarView &pc, const void *x, int dt, int64_t n, int64_t ld_x, bool pre_rotated,
                         int64_t first, const PolarCodesView &out, float *y_tap, void *stream);
+// the MFMA encoder with the polar epilogue; TQ_EUNSUPPORTED where it does not apply
+int launch_polar_mfma(const PolarView &pc, const void *x, int dt, int64_t n, int64_t ld_x, bool pre_rotated,
+                      int64_t first, const PolarCodesView &out, float *y_tap, void *stream);
 int launch_polar_scores(const PolarView &pc, const float *q, const ScoreShape &s, const PolarCodesView &k,
                         float *logits, void *stream);
 inline bool supported_polar(int d, int ab) { return (d == 64 || d == 128 || d == 256) && ab >= 2 && ab <= 4; }

@@ -223,6 +223,8 @@ static int launch_polar_encode_da(const PolarEncArgs &a, int dt, bool pre, hipSt
 int launch_polar_encode(const PolarView &pc, const void *x, int dt, int64_t n, int64_t ld_x, bool pre_rotated,
                         int64_t first, const PolarCodesView &out, float *y_tap, void *stream) {
   if (n == 0) return TQ_OK;
+  const int rc = launch_polar_mfma(pc, x, dt, n, ld_x, pre_rotated, first, out, y_tap, stream);
+  if (rc != TQ_EUNSUPPORTED) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   PolarEncArgs a{x, ld_x, n, first, pc.rot, pc.n_rot, pc.vecs_per_rot, pc.tables, out.bits, out.stride,
                  out.norms, y_tap};
