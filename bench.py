@@ -22,7 +22,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-SCORE_SOURCES = ("tq_scores.hip", "tq_lut.h", "tq_device.h", "tq_internal.h")
+SCORE_SOURCES = ("vector_quantization_amd/csrc/tq_scores.hip", "vector_quantization_amd/csrc/tq_lut.h",
+                 "vector_quantization_amd/csrc/tq_qprep.h", "vector_quantization_amd/csrc/tq_planes.h",
+                 "vector_quantization_amd/csrc/tq_device.h", "vector_quantization_amd/csrc/tq_internal.h",
+                 "include/tq.h")
 SCORE_KERNELS = ("tq::score_kernel<128, 2, 128, 4, 1024>",)
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_kernel_gqa8b_decode_b8_32k_traffic.txt")
 METRIC = "compressed-KV decode scoring GB/s (% HBM peak) + keys/s; encode vectors/s"
@@ -56,7 +59,7 @@ def score_source_hash():
     import hashlib
     h = hashlib.sha256()
     for name in SCORE_SOURCES:
-        with open(os.path.join(ROOT, "vector_quantization_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(ROOT, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
