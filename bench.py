@@ -84,6 +84,18 @@ def measured_traffic(kernel_names):
     return sum(vals[k] for k in kernel_names)
 
 
+def gpu_clocks():
+    """Current clocks as rocm-smi reports them (sclk, mclk, fclk ...) for GPU 0, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout)
+        card = next(iter(sorted(k for k in data if k.startswith("card"))))
+        return {k: v for k, v in data[card].items() if "clock" in k.lower() or "clk" in k.lower()}
+    except Exception:
+        return None
+
+
 def hbm_ceiling(dev):
     """Practical HBM ceilings on this part, measured in the same run with plain torch kernels
     (no code of this library): a read-only stream (row sums over 4 GiB) and a device copy (2 GiB
@@ -215,7 +227,7 @@ def search_main(a):
                      "frac": round(ops_s / 1e12 / INT8_PEAK_TOPS, 4), "traffic": None,
                      "kernel": "tq::search_planes (v_mfma_i32_16x16x64_i8 over index/sign bit planes, "
                                "two int8 query limbs, 64 queries per workgroup)"},
-        "gpu": torch.cuda.get_device_name(0),
+        "gpu": torch.cuda.get_device_name(0), "clocks": gpu_clocks(),
     }
     if not a.no_cpu_baseline:
         from threadpoolctl import threadpool_info
@@ -308,7 +320,7 @@ def decode_step_main(a):
                    "layers": w.layers, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "head_dim": w.d, "capacity": cap},
         "step_ms": round(t_step, 4), "append_us": round(t_app * 1e3, 2),
         "step_GBps": round(step_bytes / (t_step * 1e-3) / 1e9, 1), "step_algorithmic_bytes": step_bytes,
-        "gpu": torch.cuda.get_device_name(0),
+        "gpu": torch.cuda.get_device_name(0), "clocks": gpu_clocks(),
     }
     print(json.dumps(res), flush=True)
 
@@ -419,7 +431,7 @@ def esm2_main(a):
                      "codec": "K and V tables calibrated on the cache (library Lloyd on rotated directions), "
                               "3-bit index + one residual sign per coordinate"},
         "cache_bytes": 2 * n_vec * code_b,
-        "gpu": torch.cuda.get_device_name(0),
+        "gpu": torch.cuda.get_device_name(0), "clocks": gpu_clocks(),
     }
     print(json.dumps(res), flush=True)
 
@@ -521,7 +533,7 @@ def polar_main(a):
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": f"tq::polar_score_kernel<{w.d}, {ab}, 4, 256> (one tq_polar_scores call)"},
-        "gpu": torch.cuda.get_device_name(0),
+        "gpu": torch.cuda.get_device_name(0), "clocks": gpu_clocks(),
     }
     if not a.no_cpu_baseline:
         from threadpoolctl import threadpool_info
@@ -681,7 +693,7 @@ def main():
                      "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(SCORE_KERNELS) if a.workload == "gqa" else None,
                      "kernel": " + ".join(SCORE_KERNELS) + " (one tq_scores call)"},
-        "gpu": torch.cuda.get_device_name(0),
+        "gpu": torch.cuda.get_device_name(0), "clocks": gpu_clocks(),
     }
     res["hbm_ceiling"] = hbm_ceiling(dev)
     if a.calibrate:
