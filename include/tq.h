@@ -247,9 +247,10 @@ typedef struct {
 } tq_polar_codes;
 
 /* Per-level angle tables (layout above) for d = 2^L (4 <= d <= 1024) and ab angle bits
- * (1 <= ab <= 8): Lloyd-Max on each level's law in fp64 (Gauss-Legendre cell integrals, the
+ * (1 <= ab <= 4): Lloyd-Max on each level's law in fp64 (Gauss-Legendre cell integrals, the
  * law's quantiles as the start; level 1, the uniform law, in closed form), symmetrised about
- * pi/4, rounded to fp32.  host_tables: L * 4 * 2^ab floats.  Host only.                      */
+ * pi/4, rounded to fp32.  host_tables: L * 4 * 2^ab floats.  Host only; up to a few seconds
+ * at d = 1024, ab = 4.                                                                       */
 int tq_make_polar_tables(int32_t d, int32_t ab, float *host_tables);
 
 /* Bytes of one record's bitstream: 4 * ceil(((d/2)(2 + ab) + (d/2 - 1) ab) / 32); 0 for

@@ -237,7 +237,8 @@ def test_polar_record_bytes_and_errors():
     assert L.tq_polar_record_bytes(96, 2) == 0 and L.tq_polar_record_bytes(128, 0) == 0
     out = np.empty(4 * 7 * 4, np.float32)
     assert L.tq_make_polar_tables(96, 2, out.ctypes.data) == -1
-    assert L.tq_make_polar_tables(128, 9, out.ctypes.data) == -1
+    assert L.tq_make_polar_tables(128, 5, out.ctypes.data) == -1  # more than 4 angle bits: not built
+    assert L.tq_make_polar_tables(128, 0, out.ctypes.data) == -1
     assert L.tq_make_polar_tables(128, 2, None) == -1
 
     fake = 0x10000

@@ -407,7 +407,9 @@ extern "C" int tq_make_polar_tables(int32_t d, int32_t ab, float *host_tables) {
   if (!host_tables) return TQ_EINVAL;
   int levels = 0;
   while ((1 << levels) < d) ++levels;
-  if (d < 4 || (1 << levels) != d || d > 1024 || ab < 1 || ab > 8) return TQ_EINVAL;
+  // more than 16 levels per table would make the Lloyd iteration (linear convergence, many
+  // levels) take minutes; the device codec uses 2 to 4 angle bits
+  if (d < 4 || (1 << levels) != d || d > 1024 || ab < 1 || ab > 4) return TQ_EINVAL;
   const int n = 1 << ab;
   for (int l = 1; l <= levels; ++l) {
     std::vector<double> c;
