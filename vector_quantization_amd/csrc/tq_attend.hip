@@ -430,6 +430,7 @@ static int launch_att(const AttArgs &a0, const ScoreShape &s, hipStream_t st) {
   constexpr int NT = (G == 4) ? 512 : (NOUT > 256 ? 512 : 256);
   AttArgs a = a0;
   a.nsub = (s.hq / s.hkv) / G;
+  if (!grid_fits(s.n_seq * s.hkv * a.nsub * a.n_chunks)) return TQ_EUNSUPPORTED;
   hipLaunchKernelGGL((attend_partial<D, KB, KM, VB, VM, G, NT>), dim3((unsigned)(s.n_seq * s.hkv * a.nsub * a.n_chunks)),
                      dim3(NT), 0, st, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;

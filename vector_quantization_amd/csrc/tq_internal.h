@@ -94,6 +94,10 @@ int launch_polar_scores(const PolarView &pc, const float *q, const ScoreShape &s
                         float *logits, void *stream);
 inline bool supported_polar(int d, int ab) { return (d == 64 || d == 128 || d == 256) && ab >= 2 && ab <= 4; }
 
+// A 1-D grid of `blocks` workgroups is within the launch limit (2^31 - 1); launchers return
+// TQ_EUNSUPPORTED for shapes beyond it instead of truncating the count.
+inline bool grid_fits(int64_t blocks) { return blocks >= 0 && blocks <= 0x7FFFFFFF; }
+
 // supported device configurations
 inline bool supported_d(int d) { return d == 64 || d == 128 || d == 200; }
 inline bool supported_bits(int b) { return b >= 2 && b <= 4; }

@@ -357,6 +357,7 @@ static int launch_polar_score_g(const PolarScoreArgs &a0, int64_t n_seq, int hq,
   if (n < a.chunk) a.chunk = (int)((n + NT - 1) / NT * NT);
   a.n_chunks = (int)((n + a.chunk - 1) / a.chunk);
   const int64_t blocks = n_seq * hkv * a.nsub * a.n_chunks;
+  if (!grid_fits(blocks)) return TQ_EUNSUPPORTED;
   hipLaunchKernelGGL((polar_score_kernel<D, AB, G, NT>), dim3((unsigned)blocks), dim3(NT), 0, st, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }

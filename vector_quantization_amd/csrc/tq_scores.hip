@@ -412,15 +412,18 @@ static int launch_qprep(const CodecView &kc, const float *q, const ScoreShape &s
     // (d <= 128: at d = 200 the 64 heads a thread would carry do not fit its registers)
     if (D <= 128 && (one_rot || G % kQpHeadsMany == 0) && a.n_heads >= 1024 * kQpHeadsMany) {
       const int64_t blocks = (a.n_heads + kQpHeadsMany - 1) / kQpHeadsMany;
+      if (!grid_fits(blocks)) return TQ_EUNSUPPORTED;
       hipLaunchKernelGGL((qprep_tiled<D, M, D <= 128 ? kQpHeadsMany : kQpHeads>), dim3((unsigned)blocks), dim3(256),
                          0, st, a);
     } else {
       const int64_t blocks = (a.n_heads + kQpHeads - 1) / kQpHeads;
+      if (!grid_fits(blocks)) return TQ_EUNSUPPORTED;
       hipLaunchKernelGGL((qprep_tiled<D, M, kQpHeads>), dim3((unsigned)blocks), dim3(256), 0, st, a);
     }
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
   }
   const int64_t blocks = (a.n_heads + 3) / 4;
+  if (!grid_fits(blocks)) return TQ_EUNSUPPORTED;
   hipLaunchKernelGGL((qprep_kernel<D, M>), dim3((unsigned)blocks), dim3(256), 0, st, a);
   if (hipGetLastError() != hipSuccess) return TQ_EHIP;
   if (limbs != nullptr) {
@@ -467,6 +470,7 @@ static int launch_score_g(const ScoreArgs &a0, const ScoreShape &s, hipStream_t 
   if (a.chunk < NT) a.chunk = NT;
   a.n_chunks = (int)((s.n + a.chunk - 1) / a.chunk);
   const int64_t blocks = s.n_seq * s.hkv * a.nsub * a.n_chunks;
+  if (!grid_fits(blocks)) return TQ_EUNSUPPORTED;
   hipLaunchKernelGGL((score_kernel<D, BITS, M, G, NT>), dim3((unsigned)blocks), dim3(NT), 0, st, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }
@@ -516,6 +520,7 @@ static int launch_score_planes(const CodecView &kc, const float *q, const ScoreS
   chunk = (chunk + 15) / 16 * 16;
   a.chunk = chunk;
   a.n_chunks = (int)((s.n + chunk - 1) / chunk);
+  if (!grid_fits(base * a.n_chunks)) return TQ_EUNSUPPORTED;
   const unsigned blocks = (unsigned)(base * a.n_chunks);
   hipLaunchKernelGGL((score_planes<D, BITS, M, false>), dim3(blocks), dim3(kSpW * kWave), 0, st, a);
   if (hipGetLastError() != hipSuccess) return TQ_EHIP;

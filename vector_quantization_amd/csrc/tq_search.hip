@@ -376,6 +376,7 @@ template <int D, int BITS, int M>
 static int launch_scan(const SearchArgs &a, hipStream_t st) {
   if (a.limbs != nullptr) {
     const int64_t groups = (a.n_q + 16 * kSpW - 1) / (16 * kSpW);
+    if (!grid_fits(groups * a.n_slices)) return TQ_EUNSUPPORTED;
     hipLaunchKernelGGL((search_planes<D, BITS, M, false>), dim3((unsigned)(groups * a.n_slices)),
                        dim3(kSpW * kWave), 0, st, a);
     if (hipGetLastError() != hipSuccess) return TQ_EHIP;
@@ -384,6 +385,7 @@ static int launch_scan(const SearchArgs &a, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
   }
   const int64_t groups = (a.n_q + kSearchG - 1) / kSearchG;
+  if (!grid_fits(groups * a.n_slices)) return TQ_EUNSUPPORTED;
   hipLaunchKernelGGL((search_scan<D, BITS, M, kSearchG, kSearchNT>), dim3((unsigned)(groups * a.n_slices)),
                      dim3(kSearchNT), 0, st, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
