@@ -129,7 +129,8 @@ def hbm_ceiling(dev):
 
 
 def cpu_baseline(w, K, q, seed_rot, seed_sk):
-    """Time the oracle's scoring of one (layer, batch) slice: all kv heads, full context."""
+    """Time the oracle's encode and scoring of four (layer, batch) slices -- layers {0, L-1} x
+    batches {0, B-1}, all kv heads, full context -- on the host cores."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -138,23 +139,26 @@ def cpu_baseline(w, K, q, seed_rot, seed_sk):
     from oracle import quantize as oq
 
     ora = oc.make_codec(w.d, w.k_bits, w.k_m, seed_rot, seed_sk)
-    kx = K[0, 0].float().cpu().numpy().reshape(-1, w.d)  # [hkv * n_ctx, d]
-    qx = q[0, 0].cpu().numpy().astype(np.float64)  # [hq, d]
-    t0 = time.perf_counter()
-    codes = oq.encode(kx, ora)
-    t_enc = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    for h in range(w.hq):
-        kvh = h // w.group
-        sl = slice(kvh * w.n_ctx, (kvh + 1) * w.n_ctx)
-        oe.scores_one(qx[h], oq.Codes(codes.idx[sl], codes.sign[sl], codes.norms[sl]), ora)
-    t_sc = time.perf_counter() - t0
+    slices = sorted({(0, 0), (0, w.batch - 1), (w.layers - 1, 0), (w.layers - 1, w.batch - 1)})
+    t_enc = t_sc = 0.0
+    for l, b in slices:
+        kx = K[l, b].float().cpu().numpy().reshape(-1, w.d)  # [hkv * n_ctx, d]
+        qx = q[l, b].cpu().numpy().astype(np.float64)  # [hq, d]
+        t0 = time.perf_counter()
+        codes = oq.encode(kx, ora)
+        t_enc += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for h in range(w.hq):
+            kvh = h // w.group
+            sl = slice(kvh * w.n_ctx, (kvh + 1) * w.n_ctx)
+            oe.scores_one(qx[h], oq.Codes(codes.idx[sl], codes.sign[sl], codes.norms[sl]), ora)
+        t_sc += time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    keys = w.hkv * w.n_ctx
+    keys = len(slices) * w.hkv * w.n_ctx
     return {
         "value": keys / t_sc, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"layer 0, batch 0: {w.hkv} kv heads x {w.n_ctx} keys scored for {w.hq} query heads "
-                   f"({t_sc:.1f} s); oracle encode of the same {keys} keys took {t_enc:.1f} s "
+        "sample": (f"(layer, batch) in {slices}: {w.hkv} kv heads x {w.n_ctx} keys each, scored for {w.hq} query "
+                   f"heads ({t_sc:.1f} s); oracle encode of the same {keys} keys took {t_enc:.1f} s "
                    f"({keys / t_enc:.3g} vectors/s)"),
         "encode_vectors_per_s": keys / t_enc,
         "affinity_cores": len(os.sched_getaffinity(0)),
