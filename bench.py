@@ -548,19 +548,22 @@ def polar_main(a):
 
         from oracle import polar as op
         ora = op.make_polar_codec(w.d, ab, synth.SEED_ROT_K)
-        kx = k0.reshape(-1, w.d).cpu().numpy()
-        t0 = time.perf_counter()
-        ocodes = op.encode(kx, ora)
-        t_oe = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        op.scores(q0.cpu().numpy()[None], ocodes, ora, w.n_ctx, w.hkv)
-        tc = time.perf_counter() - t0
+        slices = sorted({(0, 0), (0, w.batch - 1), (w.layers - 1, 0), (w.layers - 1, w.batch - 1)})
+        t_oe = tc = 0.0
+        for l, b in slices:
+            kx = K[l, b].float().reshape(-1, w.d).cpu().numpy()
+            t0 = time.perf_counter()
+            ocodes = op.encode(kx, ora)
+            t_oe += time.perf_counter() - t0
+            t0 = time.perf_counter()
+            op.scores(q[l, b].float().cpu().numpy()[None], ocodes, ora, w.n_ctx, w.hkv)
+            tc += time.perf_counter() - t0
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        nk = w.hkv * w.n_ctx
+        nk = len(slices) * w.hkv * w.n_ctx
         res["cpu_baseline"] = {"value": nk / tc, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
-                               "sample": (f"layer 0, batch 0: {w.hkv} kv heads x {w.n_ctx} keys scored for "
-                                          f"{w.hq} query heads ({tc:.1f} s); oracle encode of the same {nk} keys "
-                                          f"took {t_oe:.1f} s")}
+                               "sample": (f"(layer, batch) in {slices}: {w.hkv} kv heads x {w.n_ctx} keys each, "
+                                          f"scored for {w.hq} query heads ({tc:.1f} s); oracle encode of the same "
+                                          f"{nk} keys took {t_oe:.1f} s")}
     print(json.dumps(res), flush=True)
 
 
