@@ -115,3 +115,21 @@ def test_more_angle_bits_less_error():
         u = polar.unit_directions(polar.encode(y, pc, pre_rotated=True), pc)
         errs.append(np.mean(np.sum((u - yn) ** 2, axis=1)))
     assert errs[0] > errs[1] > errs[2]
+
+
+def test_each_level_table_fits_that_levels_angles():
+    # a codec's table at level l is the Lloyd-Max table of the angles that level actually sees:
+    # cell means of exact angles of Gaussian vectors sit on the table's levels (within 5 standard
+    # errors), which a table built for another level's law would miss
+    pc = polar.make_polar_codec(64, 2, 1)
+    y = np.random.default_rng(7).standard_normal((40000, 64))
+    _, (_, _, psi1), ang = polar.exact_polar(y)
+    for lvl, psi in enumerate([psi1] + ang, start=1):
+        lv = pc.levels[lvl - 1]
+        assert lv.k == 1 << (lvl - 1)
+        x = psi.ravel()
+        cell = np.searchsorted(lv.thresholds64, x, side="right")
+        for j in range(len(lv.centroids64)):
+            s = x[cell == j]
+            se = s.std() / math.sqrt(len(s))
+            assert abs(s.mean() - lv.centroids64[j]) < 5 * se + 1e-12, (lvl, j, s.mean(), lv.centroids64[j], se)
