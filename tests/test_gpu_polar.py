@@ -129,12 +129,13 @@ def test_full_mode_codes_of_the_tap(d, ab, dtype):
     _check_full(x_seen, lib, ora, _gpu_encode(lib, x, pre=False, dtype=tdt, tap=True))
 
 
-@pytest.mark.parametrize("d,dtype", [(128, "float32"), (128, "bfloat16"), (64, "float32")])
-def test_full_mode_rotation_blocks(d, dtype):
-    # 40 blocks of 32 vectors from an offset of two blocks, 40 vectors past the last block (they
-    # take the last rotation); bf16 at d = 128 and d = 64 run the MFMA encoder's block loop,
-    # fp32 at d = 128 the FMA kernel
-    ab, n_rot, vpr, first = 2, 40, 32, 64
+@pytest.mark.parametrize("d,dtype,first", [(128, "float32", 64), (128, "bfloat16", 64), (64, "float32", 64),
+                                           (64, "float16", 64), (64, "float16", 40)])
+def test_full_mode_rotation_blocks(d, dtype, first):
+    # 40 blocks of 32 vectors from an offset, 40 vectors past the last block (they take the last
+    # rotation); bf16 at d = 128 and every type at d = 64 run the MFMA encoder's block loop when
+    # the offset is a multiple of 32, the FMA kernel otherwise (and for fp32 at d = 128)
+    ab, n_rot, vpr = 2, 40, 32
     lib, ora = _codecs(d, ab, basis=[500 + i for i in range(n_rot)], vpr=vpr)
     n = n_rot * vpr - first + 40
     x = (np.random.default_rng(9).standard_normal((n, d)) * 3.0).astype(np.float32)
