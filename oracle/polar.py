@@ -250,3 +250,24 @@ def exact_polar(y: np.ndarray):
         ang.append(np.arctan2(rb, ra))
         r = np.hypot(ra, rb)
     return r[:, 0], (a < 0, b < 0, psi1), ang
+
+
+def attend(q: np.ndarray, kcodes: PolarCodes, vcodes, pc: PolarCodec, vcodec, n_ctx: int, hkv: int,
+           scale: float) -> np.ndarray:
+    """Decode attention [S, Hq, d] with polar keys and two-stage values (fp64): softmax over the
+    keys of scale * nbar <Pi q, u^>, times the values dequantised as the two-stage decoder does
+    (TurboESM summary, section 2.E: scores, softmax, weighted sum of the values)."""
+    from . import estimate as oe
+
+    S, hq, d = q.shape
+    g = hq // hkv
+    p = oe.softmax(scale * scores(q, kcodes, pc, n_ctx, hkv))
+    out = np.empty((S, hq, vcodec.d))
+    for s_ in range(S):
+        for h in range(hkv):
+            blk = s_ * hkv + h
+            sl = slice(blk * n_ctx, (blk + 1) * n_ctx)
+            v = oe.dequantize(oe.Codes(vcodes.idx[sl], None if vcodes.sign is None else vcodes.sign[sl],
+                                       vcodes.norms[sl]), vcodec, blk * n_ctx)
+            out[s_, h * g:(h + 1) * g] = p[s_, h * g:(h + 1) * g] @ v
+    return out

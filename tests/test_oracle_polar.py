@@ -133,3 +133,51 @@ def test_each_level_table_fits_that_levels_angles():
             s = x[cell == j]
             se = s.std() / math.sqrt(len(s))
             assert abs(s.mean() - lv.centroids64[j]) < 5 * se + 1e-12, (lvl, j, s.mean(), lv.centroids64[j], se)
+
+
+def _two_stage_values(n, d, seed):
+    from oracle import codec as oc
+
+    vo = oc.make_codec(d, 3, 0, 3, 4)
+    x = np.random.default_rng(seed).standard_normal((n, d)).astype(np.float32)
+    return vo, quantize.encode(x, vo)
+
+
+def test_attention_matches_textbook_route_over_reconstructed_keys():
+    # second route: keys rebuilt in the original space (nbar Pi^T u^), logits q . k^ there, a
+    # textbook softmax per (sequence, query head), grouped-query mapping h -> h // (hq / hkv)
+    d, S, hq, hkv, n = 64, 2, 4, 2, 50
+    pc = polar.make_polar_codec(d, 2, 1)
+    g = np.random.default_rng(3)
+    x = g.standard_normal((S * hkv * n, d)).astype(np.float32)
+    kc = polar.encode(x, pc)
+    vo, vc = _two_stage_values(S * hkv * n, d, 4)
+    q = g.standard_normal((S, hq, d))
+    scale = 0.125
+    got = polar.attend(q, kc, vc, pc, vo, n, hkv, scale)
+    from oracle import estimate as oe
+
+    u = polar.unit_directions(kc, pc)
+    nbar = quantize.f16_value((kc.norms & 0xFFFF).astype(np.uint16))
+    khat = (u @ pc.rot[0].astype(np.float64)) * nbar[:, None]  # rows: nbar Pi^T u^
+    vt = oe.dequantize(vc, vo)
+    for s in range(S):
+        for h in range(hq):
+            blk = s * hkv + h // (hq // hkv)
+            sl = slice(blk * n, (blk + 1) * n)
+            lg = scale * (khat[sl] @ q[s, h])
+            p = np.exp(lg - lg.max())
+            p /= p.sum()
+            want = p @ vt[sl]
+            assert np.allclose(got[s, h], want, rtol=1e-10, atol=1e-12)
+
+
+def test_attention_with_zero_scale_is_the_mean_value():
+    d, n = 64, 33
+    pc = polar.make_polar_codec(d, 2, 1)
+    x = np.random.default_rng(5).standard_normal((n, d)).astype(np.float32)
+    vo, vc = _two_stage_values(n, d, 6)
+    from oracle import estimate as oe
+
+    got = polar.attend(np.ones((1, 1, d)), polar.encode(x, pc), vc, pc, vo, n, 1, 0.0)
+    assert np.allclose(got[0, 0], oe.dequantize(vc, vo).mean(axis=0), rtol=1e-12, atol=1e-14)
