@@ -273,6 +273,20 @@ int tq_polar_encode(const tq_polar_codec *pc, const void *x, tq_dtype dt, int64_
 int tq_polar_scores(const tq_polar_codec *pc, const float *q, int64_t n_seq, int32_t hq, int32_t hkv,
                     int64_t n_keys, tq_polar_codes k, float *logits, void *stream);
 
+/* One decode step of attention with polar-coded keys and two-stage-coded values: the logits of
+ * tq_polar_scores, then the online softmax and the value sum of tq_attend_decode (TurboESM
+ * summary, section 2.E) over vc's codes:
+ * out[s][h] = sum_n softmax_n(scale * nbar_n <Pi q, u^_n>) * v~_n.
+ *   pc, vc of the same d (vc: 2 or 3 bits, m in {0, d}); q [n_seq][hq][d] fp32; keys k and values v
+ *   [n_seq][hkv][n_ctx]; out [n_seq][hq][d] fp32.
+ *   ws  workspace of tq_polar_attend_workspace_bytes bytes, 256-byte aligned: the logits
+ *       [n_seq][hq][n_ctx] fp32, then the per-chunk partial states.                          */
+size_t tq_polar_attend_workspace_bytes(const tq_polar_codec *pc, const tq_codec *vc, int64_t n_seq, int32_t hq,
+                                       int32_t hkv, int64_t n_ctx);
+int tq_polar_attend_decode(const tq_polar_codec *pc, const tq_codec *vc, const float *q, int64_t n_seq,
+                           int32_t hq, int32_t hkv, int64_t n_ctx, tq_polar_codes k, tq_codes v, float scale,
+                           float *out, void *ws, size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------- helpers */
 
 #define TQ_OP_SCORES 0

@@ -267,3 +267,50 @@ def test_zero_sizes_and_errors():
     bad = tq.alloc_polar_codes(lib, 4, stride=lib.stride - 4)
     with pytest.raises(tq.TQError):
         tq.polar_encode(lib, torch.zeros((4, 64), device="cuda"), out=bad)
+
+
+@pytest.mark.parametrize("d,ab,vbits,vm,n_seq,hq,hkv,n_ctx", [
+    (128, 2, 3, 0, 2, 8, 2, 1000),     # 4 heads per kv head, 3-bit values (the 8B value codec)
+    (64, 3, 3, 64, 1, 6, 3, 515),      # 2 heads, values with QJL
+    (128, 2, 2, 128, 1, 2, 2, 2000),   # 1 head; several context chunks
+])
+def test_attention_with_polar_keys(d, ab, vbits, vm, n_seq, hq, hkv, n_ctx):
+    from oracle import codec as oc
+
+    say("polar attention", d, ab, vbits, vm, n_seq, hq, hkv, n_ctx)
+    lib, ora = _codecs(d, ab)
+    vl = tq.make_codec(d, vbits, vm, 3, 4)
+    vo = oc.make_codec(d, vbits, vm, 3, 4)
+    g = np.random.default_rng(d + n_ctx)
+    n = n_seq * hkv * n_ctx
+    x = (g.standard_normal((n, d)) * np.where(g.random(d) < 0.05, 10.0, 1.0)).astype(np.float32)
+    kc = op.encode(x, ora, stride=lib.stride)
+    vc = oq.encode(g.standard_normal((n, d)).astype(np.float32), vo, idx_stride=vl.idx_stride,
+                   sign_stride=vl.sign_stride)
+    q = g.standard_normal((n_seq, hq, d)).astype(np.float32)
+    scale = 1.0 / np.sqrt(d)
+    kd = tq.PolarCodes(torch.from_numpy(kc.bits).cuda(), torch.from_numpy(kc.norms.view(np.int32)).cuda())
+    vd = tq.Codes(torch.from_numpy(vc.idx).cuda(), None if vc.sign is None else torch.from_numpy(vc.sign).cuda(),
+                  torch.from_numpy(vc.norms.view(np.int32)).cuda())
+    got = tq.polar_attend_decode(lib, vl, torch.from_numpy(q).cuda(), kd, vd, n_ctx, hkv, scale).cpu().numpy()
+    want = op.attend(q.astype(np.float64), kc, vc, ora, vo, n_ctx, hkv, scale)
+    err = np.max(np.abs(got - want), axis=-1) / np.max(np.abs(want), axis=-1)
+    say("  max rel err", float(err.max()))
+    assert np.all(err <= 1e-3)
+
+
+def test_attention_with_polar_keys_argument_errors():
+    lib, _ = _codecs(64, 2)
+    vl = tq.make_codec(128, 3, 0, 3, 4)  # another d
+    k = tq.alloc_polar_codes(lib, 8)
+    v = tq.alloc_codes(vl, 8)
+    q = torch.zeros((1, 2, 64), device="cuda")
+    with pytest.raises(tq.TQError):
+        tq.polar_attend_decode(lib, vl, q, k, v, 4, 2, 1.0)
+    vl64 = tq.make_codec(64, 3, 0, 3, 4)
+    cc, vc = lib.c(), vl64.c()
+    need = tq.lib.tq_polar_attend_workspace_bytes(tq.ctypes.byref(cc), tq.ctypes.byref(vc), 1, 2, 2, 4)
+    assert need >= 2 * 4 * 4
+    rc = tq.lib.tq_polar_attend_decode(tq.ctypes.byref(cc), tq.ctypes.byref(vc), tq._ptr(q), 1, 2, 2, 4, k.c(),
+                                       tq.alloc_codes(vl64, 8).c(), 1.0, tq._ptr(q), None, 0, tq._stream())
+    assert rc == -4

@@ -74,6 +74,9 @@ def _load():
         "tq_polar_record_bytes": ([I32, I32], SZ),
         "tq_polar_encode": ([PP, P, I32, I64, I64, ctypes.c_uint32, I64, _PolarCodes, P, P], I32),
         "tq_polar_scores": ([PP, P, I64, I32, I32, I64, _PolarCodes, P, P], I32),
+        "tq_polar_attend_workspace_bytes": ([PP, CP, I64, I32, I32, I64], SZ),
+        "tq_polar_attend_decode": ([PP, CP, P, I64, I32, I32, I64, _PolarCodes, _Codes, ctypes.c_float, P, P, SZ,
+                                    P], I32),
         "tq_status_str": ([ctypes.c_int], ctypes.c_char_p),
         "tq_version": ([], ctypes.c_char_p),
     }
@@ -89,7 +92,8 @@ EXPORTED = ("tq_make_rotation", "tq_make_head_rotations", "tq_make_sketch", "tq_
             "tq_calibrate_codebook", "tq_encode",
             "tq_scores", "tq_attend_decode", "tq_append", "tq_decode_step", "tq_search_topk",
             "tq_workspace_bytes", "tq_status_str", "tq_version", "tq_make_polar_tables",
-            "tq_polar_record_bytes", "tq_polar_encode", "tq_polar_scores")
+            "tq_polar_record_bytes", "tq_polar_encode", "tq_polar_scores", "tq_polar_attend_workspace_bytes",
+            "tq_polar_attend_decode")
 
 
 def _check(rc):
@@ -478,3 +482,19 @@ def polar_scores(pc: PolarCodec, q, codes: PolarCodes, n_keys: int, hkv: int, lo
     _check(lib.tq_polar_scores(ctypes.byref(cc), _ptr(q), n_seq, hq, hkv, n_keys, codes.c(), _ptr(logits),
                                _stream()))
     return logits
+
+
+def polar_attend_decode(pc: PolarCodec, vcodec: Codec, q, kcodes: PolarCodes, vcodes: Codes, n_ctx: int, hkv: int,
+                        scale: float, out=None):
+    """Attention outputs [n_seq, hq, d] with polar-coded keys and two-stage-coded values."""
+    torch = _torch()
+    n_seq, hq, d = q.shape
+    q = q.contiguous()
+    if out is None:
+        out = torch.empty((n_seq, hq, d), dtype=torch.float32, device=q.device)
+    pcc, vcc = pc.c(), vcodec.c()
+    need = lib.tq_polar_attend_workspace_bytes(ctypes.byref(pcc), ctypes.byref(vcc), n_seq, hq, hkv, n_ctx)
+    buf, ws, wsb = _workspace(need, q.device)
+    _check(lib.tq_polar_attend_decode(ctypes.byref(pcc), ctypes.byref(vcc), _ptr(q), n_seq, hq, hkv, n_ctx,
+                                      kcodes.c(), vcodes.c(), float(scale), _ptr(out), ws, wsb, _stream()))
+    return out

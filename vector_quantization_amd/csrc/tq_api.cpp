@@ -215,6 +215,51 @@ extern "C" int tq_polar_encode(const tq_polar_codec *pc, const void *x, tq_dtype
   return tq::launch_polar_encode(tq::view(*pc), x, (int)dt, n, ld_x, pre, first, tq::view(out), y_tap, stream);
 }
 
+namespace {
+
+size_t polar_attend_ws(const tq_polar_codec *pc, const tq_codec *vc, int64_t n_seq, int32_t hq, int32_t hkv,
+                       int64_t n_ctx) {
+  const tq::ScoreShape s{n_seq, hq, hkv, n_ctx};
+  const size_t lg = (size_t)n_seq * (size_t)hq * (size_t)n_ctx * sizeof(float);
+  (void)pc;
+  return (lg + 255) / 256 * 256 + tq::attend_logits_workspace(tq::view(*vc), s);
+}
+
+}  // namespace
+
+extern "C" size_t tq_polar_attend_workspace_bytes(const tq_polar_codec *pc, const tq_codec *vc, int64_t n_seq,
+                                                  int32_t hq, int32_t hkv, int64_t n_ctx) {
+  if (!pc || !vc || n_seq < 0 || n_ctx < 1 || hq < 1 || hkv < 1 || hq % hkv != 0) return 0;
+  return polar_attend_ws(pc, vc, n_seq, hq, hkv, n_ctx);
+}
+
+extern "C" int tq_polar_attend_decode(const tq_polar_codec *pc, const tq_codec *vc, const float *q, int64_t n_seq,
+                                      int32_t hq, int32_t hkv, int64_t n_ctx, tq_polar_codes k, tq_codes v,
+                                      float scale, float *out, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_polar(pc);
+  if (rc != TQ_OK) return rc;
+  rc = check_codec(vc);
+  if (rc != TQ_OK) return rc;
+  if (pc->d != vc->d) return TQ_EINVAL;
+  if (n_seq < 0 || n_ctx < 1 || hq < 1 || hkv < 1 || hq % hkv != 0) return TQ_EINVAL;
+  if (n_seq == 0) return TQ_OK;
+  if (!q || !out) return TQ_EINVAL;
+  rc = check_polar_codes(pc, k);
+  if (rc != TQ_OK) return rc;
+  rc = check_codes(vc, v);
+  if (rc != TQ_OK) return rc;
+  const size_t need = polar_attend_ws(pc, vc, n_seq, hq, hkv, n_ctx);
+  if (!ws || ws_bytes < need) return TQ_EWORKSPACE;
+  if (!aligned(ws, 256)) return TQ_EALIGN;
+  const tq::ScoreShape s{n_seq, hq, hkv, n_ctx};
+  float *lg = reinterpret_cast<float *>(ws);
+  const size_t lg_bytes = (size_t)n_seq * (size_t)hq * (size_t)n_ctx * sizeof(float);
+  void *part = reinterpret_cast<uint8_t *>(ws) + (lg_bytes + 255) / 256 * 256;
+  rc = tq::launch_polar_scores(tq::view(*pc), q, s, tq::view(k), lg, stream);
+  if (rc != TQ_OK) return rc;
+  return tq::launch_attend_logits(tq::view(*vc), lg, s, tq::view(v), scale, out, part, stream);
+}
+
 extern "C" int tq_polar_scores(const tq_polar_codec *pc, const float *q, int64_t n_seq, int32_t hq, int32_t hkv,
                                int64_t n_keys, tq_polar_codes k, float *logits, void *stream) {
   int rc = check_polar(pc);

@@ -42,9 +42,14 @@ struct AttArgs {
   const uint32_t *vnorms;
   float *part;  // [n_seq * hq][n_chunks][2 + d + m_V]
   const int32_t *pos;  // decode step: sequence s attends over tokens 0 .. pos[s] (nullptr: all n_ctx)
+  // logits given (attend_partial with LIN): [n_seq][hq][n_ctx] fp32, unscaled, in place of the
+  // key codes (keys of another codec, scored by their own kernel)
+  const float *lg_in;
 };
 
-template <int D, int KB, int KM, int VB, int VM, int G, int NT>
+// LIN: the logits come from a.lg_in (no key tables, no key records); KB and KM then only size
+// unused parts.
+template <int D, int KB, int KM, int VB, int VM, int G, int NT, bool LIN = false>
 __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   using CK = Lut<D, KB, KM, G>;
   constexpr int KSW = CK::SW > 0 ? CK::SW : 1;
@@ -75,7 +80,8 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   constexpr int O_QH = O_QT + G * D * 4;
   constexpr int O_TABS = (O_QH + G * (KM > 0 ? KM : 1) * 4 + 15) / 16 * 16;
   constexpr int MERGE_BYTES = NW * (NOUT + 2) * G * 4;
-  constexpr int ARENA = O_TABS + (CK::BYTES > MERGE_BYTES ? CK::BYTES : MERGE_BYTES);
+  constexpr int TAB_BYTES = LIN ? 0 : CK::BYTES;
+  constexpr int ARENA = O_TABS + (TAB_BYTES > MERGE_BYTES ? TAB_BYTES : MERGE_BYTES);
   static_assert(ARENA <= 160 * 1024, "LDS arena");
   __shared__ __align__(16) uint8_t arena[ARENA];
   float2 *cbv2 = reinterpret_cast<float2 *>(arena + O_CBV2);  // (c[a], c[b]) for (b << VB) | a
@@ -118,20 +124,24 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
     return;  // uniform over the workgroup
   }
 
-  for (int i = tid; i < G * D; i += NT) qt[i] = a.qt[qrow * D + i];
-  if constexpr (KM > 0)
-    for (int i = tid; i < G * KM; i += NT) qh[i] = a.qh[qrow * KM + i];
-  if (tid < (1 << KB)) cbk[tid] = a.kcent[tid];
+  if constexpr (!LIN) {
+    for (int i = tid; i < G * D; i += NT) qt[i] = a.qt[qrow * D + i];
+    if constexpr (KM > 0)
+      for (int i = tid; i < G * KM; i += NT) qh[i] = a.qh[qrow * KM + i];
+    if (tid < (1 << KB)) cbk[tid] = a.kcent[tid];
+  }
   if (tid < LV) cbv[tid] = a.vcent[tid];
   for (int e = tid; e < LP; e += NT) cbv2[e] = make_float2(a.vcent[e & (LV - 1)], a.vcent[e >> VB]);
   __syncthreads();
   HeadScales<G> hs;
-  block_table_scales<D, KB, KM, G>(qt, qh, cbk, sc, hs);
-  // the half-table builder's scratch aliases the wavefronts' tile area, unused until the tiles
-  constexpr bool HALF = lut_half_bytes<D, KB, KM, G>() <= NW * WAVE_BYTES;
-  build_luts<D, KB, KM, G, NT>(tabs, tabs + CK::MSE_BYTES, qt, qh, cbk, sc, sc + G,
-                               HALF ? reinterpret_cast<float *>(arena + O_WAVE) : nullptr);
-  __syncthreads();
+  if constexpr (!LIN) {
+    block_table_scales<D, KB, KM, G>(qt, qh, cbk, sc, hs);
+    // the half-table builder's scratch aliases the wavefronts' tile area, unused until the tiles
+    constexpr bool HALF = lut_half_bytes<D, KB, KM, G>() <= NW * WAVE_BYTES;
+    build_luts<D, KB, KM, G, NT>(tabs, tabs + CK::MSE_BYTES, qt, qh, cbk, sc, sc + G,
+                                 HALF ? reinterpret_cast<float *>(arena + O_WAVE) : nullptr);
+    __syncthreads();
+  }
 
   const float kappa_k = KM > 0 ? 1.2533141373155003f / (float)(KM > 0 ? KM : 1) : 0.0f;
   const float kappa_v = VM > 0 ? 1.2533141373155003f / (float)(VM > 0 ? VM : 1) : 0.0f;
@@ -172,9 +182,11 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   auto load_rec = [&](int64_t t, Rec &r) {
     if (t < t1) {
       const int64_t v = vbase + t;
-      load_words<CK::IW>(a.kidx + v * a.kidx_stride, r.iw);
-      if constexpr (KM > 0) load_words<CK::SW>(a.ksign + v * a.ksign_stride, r.sw);
-      r.nw = a.knorms[v];
+      if constexpr (!LIN) {
+        load_words<CK::IW>(a.kidx + v * a.kidx_stride, r.iw);
+        if constexpr (KM > 0) load_words<CK::SW>(a.ksign + v * a.ksign_stride, r.sw);
+        r.nw = a.knorms[v];
+      }
       load_words<IWV>(a.vidx + v * a.vidx_stride, r.vw);
       if constexpr (VM > 0) load_words<SWV>(a.vsign + v * a.vsign_stride, r.vs);
       r.vnw = a.vnorms[v];
@@ -199,15 +211,20 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
       }
       vn = f16_bits_to_float(cur.vnw & 0xFFFFu);
       vr = f16_bits_to_float(cur.vnw >> 16) * kappa_v;
-      float am[G], aq[G];
-      lut_score<D, KB, KM, G>(cur.iw, cur.sw, tabs, tabs + CK::MSE_BYTES, hs, am, aq);
-      const float nbar = f16_bits_to_float(cur.nw & 0xFFFFu);
-      const float rq = f16_bits_to_float(cur.nw >> 16) * kappa_k;
+      if constexpr (LIN) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float sc = nbar * am[h];
-        if constexpr (KM > 0) sc = fmaf(rq, aq[h], sc);
-        lg[h] = sc * a.scale_log2;
+        for (int h = 0; h < G; ++h) lg[h] = a.lg_in[(qrow + h) * a.n_ctx + t] * a.scale_log2;
+      } else {
+        float am[G], aq[G];
+        lut_score<D, KB, KM, G>(cur.iw, cur.sw, tabs, tabs + CK::MSE_BYTES, hs, am, aq);
+        const float nbar = f16_bits_to_float(cur.nw & 0xFFFFu);
+        const float rq = f16_bits_to_float(cur.nw >> 16) * kappa_k;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float sc = nbar * am[h];
+          if constexpr (KM > 0) sc = fmaf(rq, aq[h], sc);
+          lg[h] = sc * a.scale_log2;
+        }
       }
     } else {
 #pragma unroll
@@ -424,24 +441,24 @@ size_t attend_workspace(const CodecView &kc, const CodecView &vc, const ScoreSha
   return q_al + (size_t)s.n_seq * s.hq * nch * (size_t)(2 + vc.d + vc.m) * sizeof(float);
 }
 
-template <int D, int KB, int KM, int VB, int VM, int G>
+template <int D, int KB, int KM, int VB, int VM, int G, bool LIN = false>
 static int launch_att(const AttArgs &a0, const ScoreShape &s, hipStream_t st) {
   constexpr int NOUT = D + VM;
   constexpr int NT = (G == 4) ? 512 : (NOUT > 256 ? 512 : 256);
   AttArgs a = a0;
   a.nsub = (s.hq / s.hkv) / G;
   if (!grid_fits(s.n_seq * s.hkv * a.nsub * a.n_chunks)) return TQ_EUNSUPPORTED;
-  hipLaunchKernelGGL((attend_partial<D, KB, KM, VB, VM, G, NT>), dim3((unsigned)(s.n_seq * s.hkv * a.nsub * a.n_chunks)),
+  hipLaunchKernelGGL((attend_partial<D, KB, KM, VB, VM, G, NT, LIN>), dim3((unsigned)(s.n_seq * s.hkv * a.nsub * a.n_chunks)),
                      dim3(NT), 0, st, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 
-template <int D, int KB, int KM, int VB, int VM>
+template <int D, int KB, int KM, int VB, int VM, bool LIN = false>
 static int launch_att_g(const AttArgs &a, const ScoreShape &s, hipStream_t st) {
   switch (att_g(s.hq / s.hkv)) {
-    case 4: return launch_att<D, KB, KM, VB, VM, 4>(a, s, st);
-    case 2: return launch_att<D, KB, KM, VB, VM, 2>(a, s, st);
-    default: return launch_att<D, KB, KM, VB, VM, 1>(a, s, st);
+    case 4: return launch_att<D, KB, KM, VB, VM, 4, LIN>(a, s, st);
+    case 2: return launch_att<D, KB, KM, VB, VM, 2, LIN>(a, s, st);
+    default: return launch_att<D, KB, KM, VB, VM, 1, LIN>(a, s, st);
   }
 }
 
@@ -475,6 +492,38 @@ int launch_attend(const CodecView &kc, const CodecView &vc, const float *q, cons
   TQ_AT(64, 2, 64, 2, 64) TQ_AT(64, 3, 64, 3, 64) TQ_AT(64, 2, 64, 3, 0) TQ_AT(128, 2, 128, 3, 0)
   TQ_AT(128, 3, 0, 3, 0) TQ_AT(128, 2, 128, 2, 128) TQ_AT(128, 3, 128, 3, 128) {}
 #undef TQ_AT
+  if (rc != TQ_OK) return rc;
+  CombArgs c{part, s.n_seq * s.hq, s.hq, s.hkv, nch, s.n, vc.rot, vc.n_rot, vc.vecs_per_rot, vc.sketch, out};
+  if (D == 64 && VM == 64) return launch_comb<64, 64>(c, st);
+  if (D == 64 && VM == 0) return launch_comb<64, 0>(c, st);
+  if (D == 128 && VM == 0) return launch_comb<128, 0>(c, st);
+  if (D == 128 && VM == 128) return launch_comb<128, 128>(c, st);
+  return TQ_EUNSUPPORTED;
+}
+
+size_t attend_logits_workspace(const CodecView &vc, const ScoreShape &s) {
+  const int64_t nch = (s.n + att_chunk(s) - 1) / att_chunk(s);
+  return (size_t)s.n_seq * s.hq * nch * (size_t)(2 + vc.d + vc.m) * sizeof(float);
+}
+
+// Attention from given logits: the same chunked pass (online softmax, values in the rotated
+// space) and chunk merge, with the logits read instead of computed from key codes.
+int launch_attend_logits(const CodecView &vc, const float *logits, const ScoreShape &s, const CodesView &v,
+                         float scale, float *out, void *ws, void *stream) {
+  if (s.n_seq == 0) return TQ_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float *part = reinterpret_cast<float *>(ws);
+  const int ch = att_chunk(s);
+  const int nch = (int)((s.n + ch - 1) / ch);
+  AttArgs a{nullptr, nullptr, nullptr, vc.centroids, s.n_seq, s.n, s.hq, s.hkv, 1, nch, ch, scale * kLog2e,
+            nullptr, 0, nullptr, 0, nullptr, v.idx, v.idx_stride, v.sign, v.sign_stride, v.norms, part, nullptr,
+            logits};
+  const int D = vc.d, VB = vc.bits, VM = vc.m;
+  int rc = TQ_EUNSUPPORTED;
+#define TQ_AL(DD, C, E) \
+  if (D == DD && VB == C && VM == E) rc = launch_att_g<DD, 2, 0, C, E, true>(a, s, st); else
+  TQ_AL(64, 2, 64) TQ_AL(64, 3, 64) TQ_AL(64, 3, 0) TQ_AL(128, 3, 0) TQ_AL(128, 2, 128) TQ_AL(128, 3, 128) {}
+#undef TQ_AL
   if (rc != TQ_OK) return rc;
   CombArgs c{part, s.n_seq * s.hq, s.hq, s.hkv, nch, s.n, vc.rot, vc.n_rot, vc.vecs_per_rot, vc.sketch, out};
   if (D == 64 && VM == 64) return launch_comb<64, 64>(c, st);

@@ -62,6 +62,11 @@ int launch_attend(const CodecView &kc, const CodecView &vc, const float *q, cons
                   const CodesView &k, const CodesView &v, float scale, float *out, void *ws,
                   size_t ws_bytes, void *stream, const int32_t *pos = nullptr, float rope_base = 0.0f);
 
+// attention from given logits [n_seq][hq][n] (keys scored elsewhere) over value codes
+size_t attend_logits_workspace(const CodecView &vc, const ScoreShape &s);
+int launch_attend_logits(const CodecView &vc, const float *logits, const ScoreShape &s, const CodesView &v,
+                         float scale, float *out, void *ws, void *stream);
+
 size_t search_workspace(const CodecView &c, int64_t n_q, int k, int64_t n_db);
 int launch_search(const CodecView &c, const float *queries, int64_t n_q, const CodesView &db,
                   int64_t n_db, int k, int64_t *out_idx, float *out_score, void *ws, size_t ws_bytes,
