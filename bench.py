@@ -462,6 +462,10 @@ def polar_main(a):
     stream = torch.cuda.current_stream()
     log("workload", w, "polar ab", ab)
     K, V, q = synth.gqa_decode(w, seed=2, device="cuda")
+    # values: the decode workload's 3-bit two-stage codec, for attention with polar keys
+    vc = tq.make_codec(w.d, w.v_bits, w.v_m, synth.SEED_ROT_V, synth.SEED_SKETCH_V)
+    vcodes = tq.encode(vc, V.reshape(-1, w.d))
+    v0 = V[0, 0].float()  # layer 0, batch 0 for the quality comparison
     del V
     pc = tq.make_polar_codec(w.d, ab, synth.SEED_ROT_K)
     n_vec = w.n_seq * w.hkv * w.n_ctx
@@ -493,6 +497,19 @@ def polar_main(a):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     t_sc = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    # attention: polar-key logits, then the online softmax and value pass over the 3-bit values
+    scale = 1.0 / math.sqrt(w.d)
+    aout = torch.empty((w.n_seq, w.hq, w.d), dtype=torch.float32, device="cuda")
+    for _ in range(a.warmup):
+        tq.polar_attend_decode(pc, vc, qf, codes, vcodes, w.n_ctx, w.hkv, scale, out=aout)
+    torch.cuda.synchronize()
+    aev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
+    for e in aev:
+        e[0].record(stream)
+        tq.polar_attend_decode(pc, vc, qf, codes, vcodes, w.n_ctx, w.hkv, scale, out=aout)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    t_att = float(np.mean([e[0].elapsed_time(e[1]) for e in aev]))
     rec_b = tq.polar_record_bytes(w.d, ab) + 4
     keys = n_vec
     q_bytes = w.n_seq * w.hq * w.d * 4
@@ -512,6 +529,16 @@ def polar_main(a):
         rel = (torch.linalg.norm(est - ex, dim=1) / torch.linalg.norm(ex, dim=1)).mean().item()
         return {"logit_cos_vs_exact": round(cos, 5), "logit_rel_l2_err": round(rel, 5)}
 
+    # exact fp32 attention on the slice, against which both key codecs' outputs are compared (the
+    # values through the same 3-bit codec in both)
+    p_ex = torch.softmax(exact.view(w.hkv, w.group, w.n_ctx) * scale, dim=-1)
+    o_ex = torch.matmul(p_ex, v0).reshape(w.hq, w.d)
+    vslice = vcodes.slice(0, w.hkv * w.n_ctx)
+
+    def out_cos(o):
+        return round(torch.nn.functional.cosine_similarity(o.reshape(w.hq, w.d).double(), o_ex.double(),
+                                                           dim=1).mean().item(), 5)
+
     comp = {}
     for bits_, abits in ((2, 2), (3, 3)):
         pcb = tq.make_polar_codec(w.d, abits, synth.SEED_ROT_K)
@@ -520,6 +547,11 @@ def polar_main(a):
         kc = tq.make_codec(w.d, bits_, w.d, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
         tcodes = tq.encode(kc, k0.reshape(-1, w.d))
         tqq = quality(tq.scores(kc, qs0, tcodes, w.n_ctx, w.hkv))
+        if bits_ == w.k_bits:  # attention at the workload's own key size (52 B), 3-bit values for both
+            pq["attention_cos_vs_exact"] = out_cos(tq.polar_attend_decode(pcb, vc, qs0, pcodes, vslice, w.n_ctx,
+                                                                          w.hkv, scale))
+            tqq["attention_cos_vs_exact"] = out_cos(tq.attend_decode(kc, vc, qs0, tcodes, vslice, w.n_ctx, w.hkv,
+                                                                     scale))
         comp[f"{tq.polar_record_bytes(w.d, abits) + 4}B_per_key"] = {
             f"polar_ab{abits}": pq, f"two_stage_{bits_}bit_qjl{w.d}": tqq}
     torch.cuda.synchronize()
@@ -537,6 +569,8 @@ def polar_main(a):
         "scores_ms": round(t_sc, 4), "keys_per_s": keys / (t_sc * 1e-3),
         "qk_pairs_per_s": keys * w.group / (t_sc * 1e-3), "scores_algorithmic_bytes": score_bytes,
         "encode_ms": round(t_enc, 3), "encode_vectors_per_s": round(n_vec / (t_enc * 1e-3)),
+        "attend_ms": round(t_att, 4),
+        "attend_note": f"polar keys + {w.v_bits}-bit values: tq_polar_scores into the workspace, then the value pass",
         "quality_layer0_batch0": comp,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
