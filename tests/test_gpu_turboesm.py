@@ -1,11 +1,11 @@
 """The TurboESM variant on the GPU against the oracle: codebooks calibrated separately for K
-and V (the library's calibration, fed to both sides), per-coordinate residual signs (S = I,
+and V (the oracle's calibration, uploaded to the library; the library's own calibration is
+checked against it on the CPU), per-coordinate residual signs (S = I,
 m = d) and the norm word's high half fp16(nbar * resid_scale).  Encode: bit-exact in
 pre-rotated mode, every difference explained by the rotation bound in full mode.  Scores and
 attention: within 1e-3 relative per row from identical codes, on the table path and on the
 many-heads (bit-plane) path, whose calibrated tables are not symmetric about zero."""
 
-import dataclasses
 import math
 
 import numpy as np
@@ -27,15 +27,14 @@ TOL = 1e-3
 
 
 def _turbo(d, bits, samples, rot_seed, basis=None, vpr=0):
-    """The library's calibrated table for these sample vectors, as (library, oracle) codecs."""
+    """The oracle's calibrated table for these sample vectors (its Lloyd rule from its own
+    codebook), uploaded to the library: (library, oracle) codecs of the same table."""
     ora0 = oc.make_codec(d, bits, 0, rot_seed, 2, basis_seeds=basis, vecs_per_rot=vpr)
-    u = calibrate.rotated_directions(samples, ora0).astype(np.float32)
-    init, _ = tq.make_codebook(d, bits)
-    c, t, e, rs = tq.calibrate_codebook(u, init, m=d)
-    assert abs(rs - calibrate.resid_scale(e, d)) <= 1e-6 * rs
-    ora = dataclasses.replace(ora0, m=d, sketch=np.eye(d, dtype=np.float32), centroids=c, thresholds=t,
-                              resid_scale=rs)
-    lib = tq.codec_from_arrays(d, bits, d, ora.rot, ora.sketch, c, t, vecs_per_rot=vpr, resid_scale=rs)
+    u = calibrate.rotated_directions(samples, ora0)
+    cal = calibrate.calibrate_codebook(u, oc.lloyd_max_beta(d, bits).centroids64)
+    ora = calibrate.turboesm_codec(ora0, cal)
+    lib = tq.codec_from_arrays(d, bits, d, ora.rot, ora.sketch, ora.centroids, ora.thresholds, vecs_per_rot=vpr,
+                               resid_scale=ora.resid_scale)
     return lib, ora
 
 
