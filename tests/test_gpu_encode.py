@@ -93,9 +93,8 @@ def test_exact_sign_fallback_with_crafted_sketch():
     S[3] = 0
     S[3, 4], S[3, 5], S[3, 6] = 2.0 ** 30, 1.0, -(2.0 ** 30)
     rot = np.eye(d, dtype=np.float32)
-    c, t = tq.make_codebook(d, bits)
-    lib = tq.codec_from_arrays(d, bits, m, rot, S, c, t)
     cb = oc.lloyd_max_beta(d, bits)
+    lib = tq.codec_from_arrays(d, bits, m, rot, S, cb.centroids, cb.thresholds)
     ora = oc.Codec(d, bits, m, rot[None], S, cb.centroids, cb.thresholds)
     y = synth.pre_rotated(512, d, seed=77)
     y[:, 1] = y[:, 0]  # r_0 == r_1: row 1 sums to exactly 0
