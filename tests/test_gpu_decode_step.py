@@ -12,7 +12,7 @@ import synth
 from oracle import codec as oc
 from oracle import estimate as oe
 from oracle import quantize as oq
-from tests._util import oracle_codes, rel_err_rows, say
+from tests._util import oracle_codes, rel_err_rows, say, to_device_codes
 from tests.test_gpu_encode import _explained_mismatches
 
 pytestmark = pytest.mark.gpu
@@ -33,7 +33,9 @@ def _host_codes(c, sl=slice(None)):
 
 
 def _check_appended(lib, ora, x, pos, cap, hkv, rope_base, before, after):
-    """The records at the appended slots against the oracle; every other record unchanged."""
+    """The records at the appended slots against the oracle; every other record unchanged.
+    Returns the oracle's cache after the append: ``before`` with the oracle's own records at the
+    appended slots (the attention reference reads it, never the device's records)."""
     S = x.shape[0]
     valid = [(s, h) for s in range(S) for h in range(hkv) if 0 <= pos[s] < cap]
     slots = np.array([(s * hkv + h) * cap + pos[s] for s, h in valid], dtype=np.int64)
@@ -50,6 +52,20 @@ def _check_appended(lib, ora, x, pos, cap, hkv, rope_base, before, after):
     assert np.array_equal(after.idx[keep], before.idx[keep])
     if after.sign is not None:
         assert np.array_equal(after.sign[keep], before.sign[keep])
+    return _with_records(before, slots, want)
+
+
+def _with_records(base, slots, recs):
+    """A host copy of the codes ``base`` with the records ``recs`` written at ``slots``."""
+    idx = base.idx.copy()
+    idx[slots] = recs.idx
+    sign = None
+    if base.sign is not None:
+        sign = base.sign.copy()
+        sign[slots] = recs.sign
+    norms = base.norms.copy()
+    norms[slots] = recs.norms
+    return oracle_codes(idx, sign, norms)
 
 
 @pytest.mark.parametrize("d,bits,m,rope,dtype", [(128, 2, 128, True, "bfloat16"), (128, 3, 0, False, "float32"),
@@ -75,11 +91,12 @@ def test_append_matches_oracle(d, bits, m, rope, dtype):
 
 
 def _prefix_cache(lib, ora, S, hkv, cap, seed):
-    """A cache whose every slot holds an encoded random vector (slots past a sequence's length
-    must not matter)."""
+    """A cache whose every slot holds a random vector encoded by the oracle (slots past a
+    sequence's length must not matter): (device codes, the same codes on the host)."""
     g = np.random.default_rng(seed)
     x = (g.standard_normal((S * hkv * cap, lib.d)) * np.where(g.random(lib.d) < 0.03, 8.0, 1.0)).astype(np.float32)
-    return tq.encode(lib, torch.from_numpy(x).cuda())
+    host = oq.encode(x, ora, idx_stride=lib.idx_stride, sign_stride=lib.sign_stride)
+    return to_device_codes(tq, host.idx, host.sign, host.norms), oracle_codes(host.idx, host.sign, host.norms)
 
 
 @pytest.mark.parametrize("hq,hkv,S,cap,pos", [
@@ -92,9 +109,8 @@ def test_decode_step_matches_oracle(hq, hkv, S, cap, pos):
     d = 128
     kl, ko = _codecs(d, 2, 128, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
     vl, vo = _codecs(d, 3, 0, synth.SEED_ROT_V, synth.SEED_SKETCH_V)
-    kc = _prefix_cache(kl, ko, S, hkv, cap, 1)
-    vc = _prefix_cache(vl, vo, S, hkv, cap, 2)
-    kb, vb = _host_codes(kc), _host_codes(vc)
+    kc, kb = _prefix_cache(kl, ko, S, hkv, cap, 1)
+    vc, vb = _prefix_cache(vl, vo, S, hkv, cap, 2)
     g = np.random.default_rng(cap + hq)
     q = g.standard_normal((S, hq, d)).astype(np.float32)
     kn = g.standard_normal((S, hkv, d)).astype(np.float32)
@@ -104,9 +120,8 @@ def test_decode_step_matches_oracle(hq, hkv, S, cap, pos):
     out = tq.decode_step(kl, vl, torch.from_numpy(q).cuda(), torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(),
                          torch.from_numpy(p).cuda(), cap, BASE, kc, vc, scale)
     torch.cuda.synchronize()
-    ka, va = _host_codes(kc), _host_codes(vc)
-    _check_appended(kl, ko, kn, p, cap, hkv, BASE, kb, ka)
-    _check_appended(vl, vo, vn, p, cap, hkv, 0.0, vb, va)
+    ka = _check_appended(kl, ko, kn, p, cap, hkv, BASE, kb, _host_codes(kc))
+    va = _check_appended(vl, vo, vn, p, cap, hkv, 0.0, vb, _host_codes(vc))
     qr = oq.rope(q.reshape(S * hq, d), np.repeat(p, hq), BASE).reshape(S, hq, d)
     want = oe.attend_lens(qr, ka, va, ko, vo, cap, p.astype(np.int64) + 1, hkv, scale)
     err = rel_err_rows(out.cpu().numpy(), want)
@@ -120,8 +135,8 @@ def test_decode_loop_and_out_of_range_sequence():
     d, hq, hkv, S, cap = 64, 4, 1, 3, 600
     kl, ko = _codecs(d, 3, 64, 1, 2)
     vl, vo = _codecs(d, 3, 64, 3, 4)
-    kc = _prefix_cache(kl, ko, S, hkv, cap, 3)
-    vc = _prefix_cache(vl, vo, S, hkv, cap, 4)
+    kc, ko_cache = _prefix_cache(kl, ko, S, hkv, cap, 3)
+    vc, vo_cache = _prefix_cache(vl, vo, S, hkv, cap, 4)
     g = np.random.default_rng(9)
     start = np.array([100, 599 - 2, cap], dtype=np.int32)  # the third is outside the cache
     for step in range(3):
@@ -129,17 +144,16 @@ def test_decode_loop_and_out_of_range_sequence():
         q = g.standard_normal((S, hq, d)).astype(np.float32)
         kn = g.standard_normal((S, hkv, d)).astype(np.float16)
         vn = g.standard_normal((S, hkv, d)).astype(np.float16)
-        kb, vb = _host_codes(kc), _host_codes(vc)
         out = tq.decode_step(kl, vl, torch.from_numpy(q).cuda(), torch.from_numpy(kn).cuda(),
                              torch.from_numpy(vn).cuda(), torch.from_numpy(p).cuda(), cap, BASE, kc, vc, 0.125)
         torch.cuda.synchronize()
-        ka, va = _host_codes(kc), _host_codes(vc)
-        _check_appended(kl, ko, kn.astype(np.float32), p, cap, hkv, BASE, kb, ka)
-        _check_appended(vl, vo, vn.astype(np.float32), p, cap, hkv, 0.0, vb, va)
+        # the device's records against the oracle's; the oracle's caches advance with its own
+        ko_cache = _check_appended(kl, ko, kn.astype(np.float32), p, cap, hkv, BASE, ko_cache, _host_codes(kc))
+        vo_cache = _check_appended(vl, vo, vn.astype(np.float32), p, cap, hkv, 0.0, vo_cache, _host_codes(vc))
         o = out.cpu().numpy()
         assert np.all(o[2] == 0.0)
         qr = oq.rope(q[:2].reshape(2 * hq, d), np.repeat(p[:2], hq), BASE).reshape(2, hq, d)
-        want = oe.attend_lens(qr, ka, va, ko, vo, cap, p[:2].astype(np.int64) + 1, hkv, 0.125)
+        want = oe.attend_lens(qr, ko_cache, vo_cache, ko, vo, cap, p[:2].astype(np.int64) + 1, hkv, 0.125)
         err = rel_err_rows(o[:2], want)
         say("  step", step, "max rel err", err.max())
         assert err.max() <= TOL
@@ -176,14 +190,30 @@ def test_full_size_decode_step_sampled_heads():
     kn = torch.randn((w.n_seq, w.hkv, w.d), generator=gen, device="cuda").to(torch.bfloat16)
     vn = torch.randn((w.n_seq, w.hkv, w.d), generator=gen, device="cuda").to(torch.bfloat16)
     scale = 1.0 / math.sqrt(w.d)
+    heads = [(0, 0), (w.n_seq - 1, w.hq - 1), (w.n_seq // 2, 9), (77, 30)]
+    # the sampled blocks as they are before the step (inputs of the oracle)
+    before = {}
+    for s, h in heads:
+        blk = s * w.hkv + h // w.group
+        sl = slice(blk * cap, (blk + 1) * cap)
+        before[(s, h)] = (_host_codes(kc, sl), _host_codes(vc, sl))
     out = tq.decode_step(kl, vl, q, kn, vn, pos, cap, BASE, kc, vc, scale)
     torch.cuda.synchronize()
     p = pos.cpu().numpy().astype(np.int64)
     qn = q.cpu().numpy().astype(np.float64)
-    for s, h in [(0, 0), (w.n_seq - 1, w.hq - 1), (w.n_seq // 2, 9), (77, 30)]:
+    kn_h, vn_h = kn.float().cpu().numpy(), vn.float().cpu().numpy()
+    for s, h in heads:
         blk = s * w.hkv + h // w.group
-        sl = slice(blk * cap, (blk + 1) * cap)
-        k1, v1 = _host_codes(kc, sl), _host_codes(vc, sl)
+        kvh = h // w.group
+        kb1, vb1 = before[(s, h)]
+        slot = np.array([blk * cap + p[s]])
+        # the oracle's own records of the new key and value at slot pos[s] of this block
+        kr = oq.append(kn_h[s, kvh][None], ko, slot, np.array([p[s]]), BASE, idx_stride=kl.idx_stride,
+                       sign_stride=kl.sign_stride)
+        vr = oq.append(vn_h[s, kvh][None], vo, slot, np.array([p[s]]), 0.0, idx_stride=vl.idx_stride,
+                       sign_stride=vl.sign_stride)
+        k1 = _with_records(kb1, np.array([p[s]]), kr)
+        v1 = _with_records(vb1, np.array([p[s]]), vr)
         qr = oq.rope(qn[s, h][None], [p[s]], BASE)
         want = oe.attend_lens(qr[None], k1, v1, ko, vo, cap, [p[s] + 1], 1, scale)[0, 0]
         err = rel_err_rows(out[s, h].cpu().numpy()[None], want[None])[0]
