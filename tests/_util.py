@@ -28,3 +28,19 @@ def rel_err_rows(got, want):
 
 def say(*a):
     print("[gpu-test]", *a, flush=True)
+
+
+def sampled_heads(w, n_rows, seed):
+    """About n_rows (sequence, query head) rows of a workload, spread over its layers, batches and
+    kv heads: [(kv block, [query heads of that block])], two heads per sampled block, the first and
+    last blocks always included."""
+    g = np.random.default_rng(seed)
+    n_blk = w.n_seq * w.hkv
+    k = max(2, (n_rows + 1) // 2)
+    blks = np.unique(np.concatenate([[0, n_blk - 1], g.choice(n_blk, size=min(n_blk, k) - 2, replace=False)]))
+    out = []
+    for b in blks:
+        kvh = int(b % w.hkv)
+        hs = sorted(set(int(kvh * w.group + x) for x in g.choice(w.group, size=min(2, w.group), replace=False)))
+        out.append((int(b), hs))
+    return out

@@ -10,7 +10,7 @@ import synth
 from oracle import codec as oc
 from oracle import estimate as oe
 from oracle import quantize as oq
-from tests._util import oracle_codes, rel_err_rows, say, to_device_codes
+from tests._util import oracle_codes, rel_err_rows, sampled_heads, say, to_device_codes
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -125,13 +125,35 @@ def test_full_size_sampled_heads(wname):
     out = tq.attend_decode(kl, vl, q, kcodes, vcodes, w.n_ctx, w.hkv, scale)
     torch.cuda.synchronize()
     qn = q.cpu().numpy().astype(np.float64)
-    for s, h in [(0, 0), (w.n_seq - 1, w.hq - 1), (w.n_seq // 2, 9)]:
-        blk = s * w.hkv + h // w.group
+    worst, n_heads = 0.0, 0
+    for blk, heads in sampled_heads(w, 64 if wname == "gqa" else 32, seed=6):
+        s = blk // w.hkv
         sl = slice(blk * w.n_ctx, (blk + 1) * w.n_ctx)
         kc = oracle_codes(kcodes.idx[sl].cpu().numpy(), kcodes.sign[sl].cpu().numpy(),
                           kcodes.norms[sl].cpu().numpy().view(np.uint32))
         vc = oracle_codes(vcodes.idx[sl].cpu().numpy(), None, vcodes.norms[sl].cpu().numpy().view(np.uint32))
-        want = oe.attend(qn[s:s + 1, h:h + 1], kc, vc, ko, vo, w.n_ctx, 1, scale)[0, 0]
-        err = rel_err_rows(out[s, h].cpu().numpy()[None], want[None])[0]
-        say("  head", s, h, "rel err", err)
-        assert err <= TOL
+        want = oe.attend(qn[s:s + 1, heads], kc, vc, ko, vo, w.n_ctx, 1, scale)[0]
+        err = rel_err_rows(out[s, heads].cpu().numpy(), want)
+        worst, n_heads = max(worst, err.max()), n_heads + len(heads)
+        assert err.max() <= TOL, (s, heads, err)
+    say("  heads", n_heads, "max rel err", worst)
+
+
+@pytest.mark.parametrize("kb,km,vb,vm,N", [(2, 128, 3, 0, 1), (2, 128, 3, 0, 2), (2, 128, 3, 0, 3),
+                                           (2, 128, 3, 0, 17), (3, 128, 3, 128, 3), (3, 0, 3, 0, 17)])
+def test_four_heads_per_kv_head_tiny_n(kb, km, vb, vm, N):
+    """Four query heads per kv head (16-bit fixed-point key tables) over a handful of tokens, half
+    the queries nearly orthogonal to every key of their block (logits near zero, weights near
+    uniform)."""
+    from tests.test_gpu_scores import _orthogonal_queries
+
+    say("attend G=4 tiny N", kb, km, vb, vm, N)
+    d, S, hkv, hq = 128, 64, 2, 8
+    g = np.random.default_rng(77 * N + kb + vb)
+    K = (g.standard_normal((S * hkv * N, d)) * np.where(g.random(d) < 0.03, 10.0, 1.0)).astype(np.float32)
+    V = g.standard_normal((S * hkv * N, d)).astype(np.float32)
+    q = _orthogonal_queries(K, g.standard_normal((S, hq, d)).astype(np.float32), N, hkv, 0.5, g)
+    got, want = _case(d, kb, km, vb, vm, hq, hkv, S, N, 0, K=K, V=V, q=q)
+    err = rel_err_rows(got, want)
+    say("  max rel err", err.max())
+    assert err.max() <= TOL

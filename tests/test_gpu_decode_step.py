@@ -3,6 +3,7 @@ the oracle.  Appended records: the norm word's low half exact, every other diffe
 by the rotation bound (the rotation sees RoPE(x), computed in fp64 on both sides).  Outputs:
 within 1e-3 relative per (sequence, head), the oracle reading the GPU's own updated caches."""
 
+import dataclasses
 import math
 
 import numpy as np
@@ -23,8 +24,9 @@ TOL = 1e-3
 BASE = 10000.0
 
 
-def _codecs(d, bits, m, rs, ss):
-    return tq.make_codec(d, bits, m, rs, ss), oc.make_codec(d, bits, m, rs, ss)
+def _codecs(d, bits, m, rs, ss, basis=None, vpr=0):
+    return (tq.make_codec(d, bits, m, rs, ss, basis_seeds=basis, vecs_per_rot=vpr),
+            oc.make_codec(d, bits, m, rs, ss, basis_seeds=basis, vecs_per_rot=vpr))
 
 
 def _host_codes(c, sl=slice(None)):
@@ -45,7 +47,12 @@ def _check_appended(lib, ora, x, pos, cap, hkv, rope_base, before, after):
                      keep=True)
     got = (after.idx[slots], None if after.sign is None else after.sign[slots], after.norms[slots], None)
     xr = oq.rope(rows, p, rope_base) if rope_base > 0 else rows.astype(np.float64)
-    _explained_mismatches(xr, lib, ora, got, want, rates=False)
+    # each appended record's rotation is the one of its cache slot
+    rid = np.array([ora.rot_index(1, int(sl))[0] for sl in slots], dtype=np.int64)
+    flips, rns, n_rows = _explained_mismatches(xr, lib, ora, got, want, rates=False, rid=rid)
+    # every difference is bound-explained (checked above); index flips stay rare: at most one
+    # row, or 2% of the rows, as in the full-mode encode tests
+    assert flips <= max(1, int(0.02 * n_rows)), (flips, rns, n_rows)
     keep = np.ones(len(before.norms), bool)
     keep[slots] = False
     assert np.array_equal(after.norms[keep], before.norms[keep])
@@ -88,6 +95,37 @@ def test_append_matches_oracle(d, bits, m, rope, dtype):
               BASE if rope else 0.0, cache)
     torch.cuda.synchronize()
     _check_appended(lib, ora, x, pos, cap, hkv, BASE if rope else 0.0, before, _host_codes(cache))
+
+
+@pytest.mark.parametrize("d,bits,m,dtype", [(128, 2, 128, "bfloat16"), (64, 3, 64, "float32"),
+                                            (128, 3, 0, "float16")])
+def test_append_per_block_rotations(d, bits, m, dtype):
+    """One rotation per (sequence, kv head) block (vecs_per_rot = cap): each appended record must
+    use its slot's rotation, on the MFMA-free append kernel and in the oracle alike."""
+    say("append per-block rotations", d, bits, m, dtype)
+    S, hkv, cap = 3, 4, 40
+    seeds = [500 + i for i in range(S * hkv)]
+    lib, ora = _codecs(d, bits, m, 1, 2, basis=seeds, vpr=cap)
+    pos = np.array([0, 17, 39], dtype=np.int32)
+    g = np.random.default_rng(3 * d + bits)
+    x = (g.standard_normal((S, hkv, d)) * 2.0).astype(np.float32)
+    x = torch.from_numpy(x).to(getattr(torch, dtype)).float().numpy()
+    cache = tq.alloc_codes(lib, S * hkv * cap)
+    cache.idx.fill_(0x3C)
+    if cache.sign is not None:
+        cache.sign.fill_(0xC3)
+    cache.norms.fill_(0x0BADBEEF)
+    before = _host_codes(cache)
+    tq.append(lib, torch.from_numpy(x).to(getattr(torch, dtype)).cuda(), torch.from_numpy(pos).cuda(), cap,
+              BASE, cache)
+    torch.cuda.synchronize()
+    _check_appended(lib, ora, x, pos, cap, hkv, BASE, before, _host_codes(cache))
+    # the rotation used is the block's own: encoding with the first block's rotation instead would
+    # give other indices for the other blocks
+    slots = np.array([(s * hkv + h) * cap + pos[s] for s in range(S) for h in range(hkv)])
+    wrong = oq.append(x.reshape(-1, d), dataclasses.replace(ora, rot=ora.rot[:1], vecs_per_rot=0), slots,
+                      np.repeat(pos, hkv), BASE, idx_stride=lib.idx_stride, sign_stride=lib.sign_stride)
+    assert not np.array_equal(wrong.idx[hkv:], _host_codes(cache).idx[slots][hkv:])
 
 
 def _prefix_cache(lib, ora, S, hkv, cap, seed):

@@ -264,3 +264,60 @@ def test_polar_record_bytes_and_errors():
     assert P(ctypes.byref(pc), q, 1, 8, 2, 16, tq._PolarCodes(0x20000, 40, 0x40000), lg, S) == -1
     assert P(ctypes.byref(pc), None, 1, 8, 2, 16, codes, lg, S) == -1
     assert P(ctypes.byref(pc), q, 0, 8, 2, 16, codes, lg, S) == 0
+
+
+def test_unsupported_attention_combination_changes_nothing():
+    """Combinations that pass every per-codec check but have no attention kernel return
+    TQ_EUNSUPPORTED before any launch: a decode step must not have appended into its caches."""
+    L = tq.lib
+    S = ctypes.c_void_p(0)
+    n_seq, hq, hkv, cap = 2, 4, 1, 8
+
+    def planes(stride, n):
+        a = np.full((n, stride), 0xA7, np.uint8)
+        return a
+
+    kidx, ksign, knorm = planes(48, n_seq * cap), planes(16, n_seq * cap), np.full(n_seq * cap, 0x1234, np.uint32)
+    vidx, vnorm = planes(32, n_seq * cap), np.full(n_seq * cap, 0x5678, np.uint32)
+    before = [a.copy() for a in (kidx, ksign, knorm, vidx, vnorm)]
+    rot = np.zeros((128, 128), np.float32)
+    sk = np.zeros((128, 128), np.float32)
+    cb = np.zeros(8, np.float32)
+    kc = tq._Codec(128, 3, 128, 1, 0, rot.ctypes.data, sk.ctypes.data, cb.ctypes.data, cb.ctypes.data)
+    vc = tq._Codec(128, 2, 0, 1, 0, rot.ctypes.data, 0, cb.ctypes.data, cb.ctypes.data)
+    kcodes = tq._Codes(kidx.ctypes.data, 48, ksign.ctypes.data, 16, knorm.ctypes.data)
+    vcodes = tq._Codes(vidx.ctypes.data, 32, 0, 0, vnorm.ctypes.data)
+    q = np.zeros((n_seq, hq, 128), np.float32)
+    kn = np.zeros((n_seq, hkv, 128), np.float32)
+    pos = np.zeros(n_seq, np.int32)
+    out = np.zeros((n_seq, hq, 128), np.float32)
+    ws = np.zeros(1 << 16, np.uint8)
+    wsp = (ws.ctypes.data + 255) // 256 * 256
+    rc = L.tq_decode_step(ctypes.byref(kc), ctypes.byref(vc), q.ctypes.data, kn.ctypes.data, kn.ctypes.data, 0,
+                          n_seq, hq, hkv, cap, pos.ctypes.data, ctypes.c_float(10000.0), kcodes, vcodes,
+                          ctypes.c_float(0.1), out.ctypes.data, ctypes.c_void_p(wsp), 1 << 15, S)
+    assert rc == -2
+    for a, b in zip(before, (kidx, ksign, knorm, vidx, vnorm)):
+        assert np.array_equal(a, b)
+    assert L.tq_attend_decode(ctypes.byref(kc), ctypes.byref(vc), q.ctypes.data, n_seq, hq, hkv, cap, kcodes,
+                              vcodes, ctypes.c_float(0.1), out.ctypes.data, None, 0, S) == -2
+    # d = 200 has encode, scores and search, no attention
+    rot2 = np.zeros((200, 200), np.float32)
+    k200 = tq._Codec(200, 2, 200, 1, 0, rot2.ctypes.data, rot2.ctypes.data, cb.ctypes.data, cb.ctypes.data)
+    v200 = tq._Codec(200, 3, 0, 1, 0, rot2.ctypes.data, 0, cb.ctypes.data, cb.ctypes.data)
+    assert L.tq_attend_decode(ctypes.byref(k200), ctypes.byref(v200), q.ctypes.data, n_seq, hq, hkv, cap,
+                              tq._Codes(kidx.ctypes.data, 64, ksign.ctypes.data, 32, knorm.ctypes.data),
+                              tq._Codes(vidx.ctypes.data, 80, 0, 0, vnorm.ctypes.data), ctypes.c_float(0.1),
+                              out.ctypes.data, None, 0, S) == -2
+    # polar keys with 4-bit values: the value pass is not built, checked before the score launch
+    tabs = np.zeros(7 * 4 * 4, np.float32)
+    pc = tq._PolarCodec(128, 2, 1, 0, rot.ctypes.data, tabs.ctypes.data)
+    v4 = tq._Codec(128, 4, 0, 1, 0, rot.ctypes.data, 0, cb.ctypes.data, cb.ctypes.data)
+    pbits = np.full((n_seq * cap, 48), 0x5A, np.uint8)
+    pb0 = pbits.copy()
+    rc = L.tq_polar_attend_decode(ctypes.byref(pc), ctypes.byref(v4), q.ctypes.data, n_seq, hq, hkv, cap,
+                                  tq._PolarCodes(pbits.ctypes.data, 48, knorm.ctypes.data),
+                                  tq._Codes(vidx.ctypes.data, 64, 0, 0, vnorm.ctypes.data), ctypes.c_float(0.1),
+                                  out.ctypes.data, ctypes.c_void_p(wsp), 1 << 15, S)
+    assert rc == -2
+    assert np.array_equal(pbits, pb0)

@@ -2,8 +2,10 @@
 
 Thin ctypes marshalling over the C ABI declared in include/tq.h: every step of encode,
 scoring, attention and search runs in the library's HIP kernels.  PyTorch provides device
-memory and the stream.  Importing this package loads ``lib/libtq.so`` and fails loudly when
-it is missing (build it with ``python -m vector_quantization_amd.build``).
+memory and the stream.  ``lib/libtq.so`` is loaded at the first use of ``lib`` (any call of
+this module that reaches the library), which raises ImportError when it is missing -- there is
+no other code path.  Build it with ``python -m vector_quantization_amd.build``; importing the
+package itself needs no built library, so that this command works on a fresh checkout.
 """
 
 import ctypes
@@ -87,7 +89,18 @@ def _load():
     return lib
 
 
-lib = _load()
+class _Lib:
+    """libtq's ctypes handle, loaded (and its signatures set) at the first attribute access."""
+
+    _cdll = None
+
+    def __getattr__(self, name):
+        if _Lib._cdll is None:
+            _Lib._cdll = _load()
+        return getattr(_Lib._cdll, name)
+
+
+lib = _Lib()
 EXPORTED = ("tq_make_rotation", "tq_make_head_rotations", "tq_make_sketch", "tq_make_codebook",
             "tq_calibrate_codebook", "tq_encode",
             "tq_scores", "tq_attend_decode", "tq_append", "tq_decode_step", "tq_search_topk",
@@ -164,6 +177,110 @@ def _stream():
 
 def _ptr(t):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+# ------------------------------------------------------------------ argument checks
+#
+# The C ABI takes raw pointers and cannot see tensor sizes, dtypes or devices: every wrapper
+# below checks them first and raises ValueError, so that a wrong tensor never reaches a kernel
+# as an out-of-bounds or host address.  Sizes and dtypes are checked first, devices last
+# (_check_devices: every tensor of the call on one CUDA device).
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensor(t, name, dtype=None, shape=None, rows_contiguous=False):
+    torch = _torch()
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None:
+        _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if rows_contiguous:
+        _need(t.dim() == 2 and (t.shape[0] <= 1 or t.stride(0) == t.shape[1]) and (t.shape[1] <= 1 or t.stride(1) == 1),
+              f"{name} must be a contiguous [n, bytes] plane")
+    else:
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    return [(name, t)]
+
+
+def _check_devices(named):
+    """Every tensor of ``named`` ((name, tensor) pairs, None skipped) on one CUDA device."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        _need(t.device.type == "cuda", f"{name} must be on a CUDA device, got {t.device}")
+        if dev is None:
+            dev = t.device
+        _need(t.device == dev, f"{name} is on {t.device}, the call's other tensors on {dev}")
+
+
+def _check_codec(codec, name="codec"):
+    out = []
+    for f in ("rot", "sketch", "centroids", "thresholds", "tables"):
+        t = getattr(codec, f, None)
+        if t is not None:
+            out += _check_tensor(t, f"{name}.{f}", dtype=_torch().float32)
+    return out
+
+
+def _check_codes(codes, codec, n_min, name="codes"):
+    """Code planes of ``codec`` holding at least n_min records."""
+    torch = _torch()
+    _need(isinstance(codes, Codes), f"{name} must be Codes")
+    n = codes.n
+    _need(n >= n_min, f"{name} holds {n} records, the call addresses {n_min}")
+    out = _check_tensor(codes.idx, f"{name}.idx", dtype=torch.uint8, rows_contiguous=True)
+    _need(codes.idx.shape[1] >= codec.idx_stride, f"{name}.idx rows must hold >= {codec.idx_stride} bytes")
+    out += _check_tensor(codes.norms, f"{name}.norms", dtype=torch.int32, shape=(n,))
+    if codec.m > 0:
+        _need(codes.sign is not None, f"{name}.sign is required (m = {codec.m})")
+        out += _check_tensor(codes.sign, f"{name}.sign", dtype=torch.uint8, rows_contiguous=True)
+        _need(codes.sign.shape[0] == n, f"{name}.sign must have {n} rows")
+        _need(codes.sign.shape[1] >= codec.sign_stride, f"{name}.sign rows must hold >= {codec.sign_stride} bytes")
+    return out
+
+
+def _check_polar_codes(codes, pc, n_min, name="codes"):
+    torch = _torch()
+    _need(isinstance(codes, PolarCodes), f"{name} must be PolarCodes")
+    n = codes.n
+    _need(n >= n_min, f"{name} holds {n} records, the call addresses {n_min}")
+    out = _check_tensor(codes.bits, f"{name}.bits", dtype=torch.uint8, rows_contiguous=True)
+    _need(codes.bits.shape[1] >= pc.stride, f"{name}.bits rows must hold >= {pc.stride} bytes")
+    return out + _check_tensor(codes.norms, f"{name}.norms", dtype=torch.int32, shape=(n,))
+
+
+def _check_queries(q, d, name="q"):
+    """fp32 [n_seq, hq, d], contiguous."""
+    torch = _torch()
+    _need(isinstance(q, torch.Tensor) and q.dim() == 3 and q.shape[2] == d, f"{name} must be [n_seq, hq, {d}]")
+    return _check_tensor(q, name, dtype=torch.float32)
+
+
+def _check_heads(hq, hkv):
+    _need(hkv >= 1 and hq >= 1 and hq % hkv == 0, f"hq ({hq}) must be a positive multiple of hkv ({hkv})")
+
+
+def _check_rows(x, d, name="x"):
+    """Rows [..., d] of fp32 / fp16 / bf16, each row contiguous."""
+    torch = _torch()
+    _need(isinstance(x, torch.Tensor) and x.dim() >= 1 and x.shape[-1] == d, f"{name} must be [..., {d}]")
+    _need(str(x.dtype).replace("torch.", "") in _DT, f"{name} must be float32, float16 or bfloat16, got {x.dtype}")
+    _need(x.stride(-1) == 1 or x.shape[-1] == 1, f"{name} rows must be contiguous")
+    return [(name, x)]
+
+
+def _out(t, name, shape, like):
+    """A caller-given fp32 output of exactly ``shape``, or a new one on ``like``'s device."""
+    torch = _torch()
+    if t is None:
+        return torch.empty(shape, dtype=torch.float32, device=like.device), []
+    return t, _check_tensor(t, name, dtype=torch.float32, shape=shape)
 
 
 def _record_words(bits: int) -> int:
@@ -282,10 +399,19 @@ _DT = {"float32": TQ_F32, "float16": TQ_F16, "bfloat16": TQ_BF16}
 def encode(codec: Codec, x, pre_rotated: bool = False, first: int = 0, out: Optional[Codes] = None,
            y_tap=None) -> Codes:
     """Encode rows of ``x`` ([n, d] or [..., d], contiguous rows) into ``out`` (allocated if None)."""
+    named = _check_rows(x, codec.d)
     x2 = x.reshape(-1, x.shape[-1])
     if x2.stride(-1) != 1:
         raise ValueError("x rows must be contiguous")
     n = x2.shape[0]
+    _need(first >= 0, "first must be >= 0")
+    _need(not pre_rotated or x.dtype == _torch().float32, "pre-rotated input must be float32")
+    named += _check_codec(codec)
+    if out is not None:
+        named += _check_codes(out, codec, n, "out")
+    if y_tap is not None:
+        named += _check_tensor(y_tap, "y_tap", dtype=_torch().float32, shape=(n, codec.d))
+    _check_devices(named)
     out = out or alloc_codes(codec, n, x.device)
     dt = _DT[str(x.dtype).replace("torch.", "")]
     flags = TQ_ENC_PRE_ROTATED if pre_rotated else 0
@@ -297,11 +423,13 @@ def encode(codec: Codec, x, pre_rotated: bool = False, first: int = 0, out: Opti
 
 def scores(codec: Codec, q, codes: Codes, n_keys: int, hkv: int, logits=None):
     """Logits [n_seq, hq, n_keys] for fp32 queries q [n_seq, hq, d] over codes [n_seq][hkv][n_keys]."""
-    torch = _torch()
+    named = _check_queries(q, codec.d)
     n_seq, hq, d = q.shape
-    q = q.contiguous()
-    if logits is None:
-        logits = torch.empty((n_seq, hq, n_keys), dtype=torch.float32, device=q.device)
+    _check_heads(hq, hkv)
+    _need(n_keys >= 0, "n_keys must be >= 0")
+    named += _check_codec(codec) + _check_codes(codes, codec, n_seq * hkv * n_keys)
+    logits, o = _out(logits, "logits", (n_seq, hq, n_keys), q)
+    _check_devices(named + o)
     cc = codec.c()
     need = lib.tq_workspace_bytes(TQ_OP_SCORES, ctypes.byref(cc), None, n_seq, hq, hkv, n_keys)
     buf, ws, wsb = _workspace(need, q.device)
@@ -313,11 +441,16 @@ def scores(codec: Codec, q, codes: Codes, n_keys: int, hkv: int, logits=None):
 def attend_decode(kcodec: Codec, vcodec: Codec, q, kcodes: Codes, vcodes: Codes, n_ctx: int, hkv: int,
                   scale: float, out=None):
     """Attention outputs [n_seq, hq, d] for fp32 queries q [n_seq, hq, d]."""
-    torch = _torch()
+    named = _check_queries(q, kcodec.d)
     n_seq, hq, d = q.shape
-    q = q.contiguous()
-    if out is None:
-        out = torch.empty((n_seq, hq, d), dtype=torch.float32, device=q.device)
+    _check_heads(hq, hkv)
+    _need(vcodec.d == d, "kcodec and vcodec must share d")
+    _need(n_ctx >= 1, "n_ctx must be >= 1")
+    named += _check_codec(kcodec, "kcodec") + _check_codec(vcodec, "vcodec")
+    named += _check_codes(kcodes, kcodec, n_seq * hkv * n_ctx, "kcodes")
+    named += _check_codes(vcodes, vcodec, n_seq * hkv * n_ctx, "vcodes")
+    out, o = _out(out, "out", (n_seq, hq, d), q)
+    _check_devices(named + o)
     kc, vc = kcodec.c(), vcodec.c()
     need = lib.tq_workspace_bytes(TQ_OP_ATTEND, ctypes.byref(kc), ctypes.byref(vc), n_seq, hq, hkv, n_ctx)
     buf, ws, wsb = _workspace(need, q.device)
@@ -330,8 +463,14 @@ def append(codec: Codec, x_new, pos, cap: int, rope_base: float, cache: Codes):
     """Append x_new [n_seq, hkv, d] (one vector per sequence and kv head) into ``cache`` laid out
     [n_seq][hkv][cap], at slot pos[s] (int32 [n_seq] on the device), RoPE'd at pos[s] before the
     rotation when rope_base > 0."""
+    named = _check_rows(x_new, codec.d, "x_new")
+    _need(x_new.dim() == 3, "x_new must be [n_seq, hkv, d]")
     x = x_new.contiguous()
     n_seq, hkv, d = x.shape
+    _need(cap >= 1, "cap must be >= 1")
+    named += _check_tensor(pos, "pos", dtype=_torch().int32, shape=(n_seq,))
+    named += _check_codec(codec) + _check_codes(cache, codec, n_seq * hkv * cap, "cache")
+    _check_devices(named)
     dt = _DT[str(x.dtype).replace("torch.", "")]
     cc = codec.c()
     _check(lib.tq_append(ctypes.byref(cc), _ptr(x), dt, n_seq, hkv, _ptr(pos), cap, ctypes.c_float(rope_base),
@@ -343,15 +482,25 @@ def decode_step(kcodec: Codec, vcodec: Codec, q, k_new, v_new, pos, cap: int, ro
                 vcache: Codes, scale: float, out=None):
     """One decode step: append k_new / v_new [n_seq, hkv, d] at slot pos[s] (keys RoPE'd), then
     attention of q [n_seq, hq, d] (RoPE'd at pos[s]) over tokens 0 .. pos[s].  Returns out."""
-    torch = _torch()
-    q, kn, vn = q.contiguous(), k_new.contiguous(), v_new.contiguous()
+    named = _check_queries(q, kcodec.d)
     n_seq, hq, d = q.shape
+    named += _check_rows(k_new, d, "k_new") + _check_rows(v_new, d, "v_new")
+    _need(k_new.dim() == 3 and k_new.shape[0] == n_seq, "k_new must be [n_seq, hkv, d]")
+    kn, vn = k_new.contiguous(), v_new.contiguous()
     hkv = kn.shape[1]
+    _need(tuple(vn.shape) == tuple(kn.shape), "v_new must have k_new's shape")
     if vn.dtype != kn.dtype:
         raise ValueError("k_new and v_new must share a dtype")
+    _check_heads(hq, hkv)
+    _need(vcodec.d == d, "kcodec and vcodec must share d")
+    _need(cap >= 1, "cap must be >= 1")
+    named += _check_tensor(pos, "pos", dtype=_torch().int32, shape=(n_seq,))
+    named += _check_codec(kcodec, "kcodec") + _check_codec(vcodec, "vcodec")
+    named += _check_codes(kcache, kcodec, n_seq * hkv * cap, "kcache")
+    named += _check_codes(vcache, vcodec, n_seq * hkv * cap, "vcache")
     dt = _DT[str(kn.dtype).replace("torch.", "")]
-    if out is None:
-        out = torch.empty((n_seq, hq, d), dtype=torch.float32, device=q.device)
+    out, o = _out(out, "out", (n_seq, hq, d), q)
+    _check_devices(named + o)
     kc, vc = kcodec.c(), vcodec.c()
     need = lib.tq_workspace_bytes(TQ_OP_DECODE_STEP, ctypes.byref(kc), ctypes.byref(vc), n_seq, hq, hkv, cap)
     buf, ws, wsb = _workspace(need, q.device)
@@ -364,8 +513,13 @@ def decode_step(kcodec: Codec, vcodec: Codec, q, k_new, v_new, pos, cap: int, ro
 def search_topk(codec: Codec, queries, db: Codes, n_db: int, k: int):
     """Top-k (index int64, score fp32) per query by estimated inner product."""
     torch = _torch()
-    queries = queries.contiguous()
+    _need(isinstance(queries, torch.Tensor) and queries.dim() == 2 and queries.shape[1] == codec.d,
+          f"queries must be [n_q, {codec.d}]")
+    named = _check_tensor(queries, "queries", dtype=torch.float32)
     n_q = queries.shape[0]
+    _need(1 <= k <= 32 and k <= n_db, "k must be in 1 .. min(32, n_db)")
+    named += _check_codec(codec) + _check_codes(db, codec, n_db, "db")
+    _check_devices(named)
     idx = torch.empty((n_q, k), dtype=torch.int64, device=queries.device)
     sc = torch.empty((n_q, k), dtype=torch.float32, device=queries.device)
     cc = codec.c()
@@ -458,10 +612,19 @@ def alloc_polar_codes(pc: PolarCodec, n: int, device="cuda", stride: Optional[in
 def polar_encode(pc: PolarCodec, x, pre_rotated: bool = False, first: int = 0, out: Optional[PolarCodes] = None,
                  y_tap=None) -> PolarCodes:
     """Encode rows of ``x`` ([n, d] or [..., d], contiguous rows) with the recursive polar stage."""
+    named = _check_rows(x, pc.d)
     x2 = x.reshape(-1, x.shape[-1])
     if x2.stride(-1) != 1:
         raise ValueError("x rows must be contiguous")
     n = x2.shape[0]
+    _need(first >= 0, "first must be >= 0")
+    _need(not pre_rotated or x.dtype == _torch().float32, "pre-rotated input must be float32")
+    named += _check_codec(pc)
+    if out is not None:
+        named += _check_polar_codes(out, pc, n, "out")
+    if y_tap is not None:
+        named += _check_tensor(y_tap, "y_tap", dtype=_torch().float32, shape=(n, pc.d))
+    _check_devices(named)
     out = out or alloc_polar_codes(pc, n, x.device)
     dt = _DT[str(x.dtype).replace("torch.", "")]
     flags = TQ_ENC_PRE_ROTATED if pre_rotated else 0
@@ -473,11 +636,13 @@ def polar_encode(pc: PolarCodec, x, pre_rotated: bool = False, first: int = 0, o
 
 def polar_scores(pc: PolarCodec, q, codes: PolarCodes, n_keys: int, hkv: int, logits=None):
     """Logits [n_seq, hq, n_keys] = nbar <Pi q, u^> over polar codes [n_seq][hkv][n_keys]."""
-    torch = _torch()
+    named = _check_queries(q, pc.d)
     n_seq, hq, d = q.shape
-    q = q.contiguous()
-    if logits is None:
-        logits = torch.empty((n_seq, hq, n_keys), dtype=torch.float32, device=q.device)
+    _check_heads(hq, hkv)
+    _need(n_keys >= 0, "n_keys must be >= 0")
+    named += _check_codec(pc) + _check_polar_codes(codes, pc, n_seq * hkv * n_keys)
+    logits, o = _out(logits, "logits", (n_seq, hq, n_keys), q)
+    _check_devices(named + o)
     cc = pc.c()
     _check(lib.tq_polar_scores(ctypes.byref(cc), _ptr(q), n_seq, hq, hkv, n_keys, codes.c(), _ptr(logits),
                                _stream()))
@@ -487,11 +652,16 @@ def polar_scores(pc: PolarCodec, q, codes: PolarCodes, n_keys: int, hkv: int, lo
 def polar_attend_decode(pc: PolarCodec, vcodec: Codec, q, kcodes: PolarCodes, vcodes: Codes, n_ctx: int, hkv: int,
                         scale: float, out=None):
     """Attention outputs [n_seq, hq, d] with polar-coded keys and two-stage-coded values."""
-    torch = _torch()
+    named = _check_queries(q, pc.d)
     n_seq, hq, d = q.shape
-    q = q.contiguous()
-    if out is None:
-        out = torch.empty((n_seq, hq, d), dtype=torch.float32, device=q.device)
+    _check_heads(hq, hkv)
+    _need(vcodec.d == d, "the polar codec and vcodec must share d")
+    _need(n_ctx >= 1, "n_ctx must be >= 1")
+    named += _check_codec(pc, "pc") + _check_codec(vcodec, "vcodec")
+    named += _check_polar_codes(kcodes, pc, n_seq * hkv * n_ctx, "kcodes")
+    named += _check_codes(vcodes, vcodec, n_seq * hkv * n_ctx, "vcodes")
+    out, o = _out(out, "out", (n_seq, hq, d), q)
+    _check_devices(named + o)
     pcc, vcc = pc.c(), vcodec.c()
     need = lib.tq_polar_attend_workspace_bytes(ctypes.byref(pcc), ctypes.byref(vcc), n_seq, hq, hkv, n_ctx)
     buf, ws, wsb = _workspace(need, q.device)

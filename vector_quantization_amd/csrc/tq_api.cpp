@@ -107,6 +107,8 @@ extern "C" int tq_attend_decode(const tq_codec *kc, const tq_codec *vc, const fl
   rc = check_codes(vc, v);
   if (rc != TQ_OK) return rc;
   const tq::ScoreShape s{n_seq, hq, hkv, n_ctx};
+  rc = tq::attend_preflight(tq::view(*kc), tq::view(*vc), s);
+  if (rc != TQ_OK) return rc;
   const size_t need = tq::attend_workspace(tq::view(*kc), tq::view(*vc), s);
   if (!ws || ws_bytes < need) return TQ_EWORKSPACE;
   if (!aligned(ws, 256)) return TQ_EALIGN;
@@ -145,6 +147,10 @@ extern "C" int tq_decode_step(const tq_codec *kc, const tq_codec *vc, const floa
   rc = check_codes(vc, vcache);
   if (rc != TQ_OK) return rc;
   const tq::ScoreShape s{n_seq, hq, hkv, cap};
+  // every check of the attention, and of both appends, before the first launch: an unsupported
+  // combination must leave the caches untouched
+  rc = tq::attend_preflight(tq::view(*kc), tq::view(*vc), s);
+  if (rc != TQ_OK) return rc;
   const size_t need = tq::attend_workspace(tq::view(*kc), tq::view(*vc), s);
   if (!ws || ws_bytes < need) return TQ_EWORKSPACE;
   if (!aligned(ws, 256)) return TQ_EALIGN;
@@ -248,10 +254,12 @@ extern "C" int tq_polar_attend_decode(const tq_polar_codec *pc, const tq_codec *
   if (rc != TQ_OK) return rc;
   rc = check_codes(vc, v);
   if (rc != TQ_OK) return rc;
+  const tq::ScoreShape s{n_seq, hq, hkv, n_ctx};
+  rc = tq::attend_logits_preflight(tq::view(*vc), s);  // before the score launch
+  if (rc != TQ_OK) return rc;
   const size_t need = polar_attend_ws(pc, vc, n_seq, hq, hkv, n_ctx);
   if (!ws || ws_bytes < need) return TQ_EWORKSPACE;
   if (!aligned(ws, 256)) return TQ_EALIGN;
-  const tq::ScoreShape s{n_seq, hq, hkv, n_ctx};
   float *lg = reinterpret_cast<float *>(ws);
   const size_t lg_bytes = (size_t)n_seq * (size_t)hq * (size_t)n_ctx * sizeof(float);
   void *part = reinterpret_cast<uint8_t *>(ws) + (lg_bytes + 255) / 256 * 256;

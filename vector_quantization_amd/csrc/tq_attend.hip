@@ -468,11 +468,43 @@ static int launch_comb(const CombArgs &c, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 
+// The (d, key bits, key m, value bits, value m) combinations built for attention over key codes,
+// and the (d, value bits, value m) ones built for attention from given logits.
+#define TQ_ATTEND_CONFIGS(X) \
+  X(64, 2, 64, 2, 64) X(64, 3, 64, 3, 64) X(64, 2, 64, 3, 0) X(128, 2, 128, 3, 0) X(128, 3, 0, 3, 0) \
+  X(128, 2, 128, 2, 128) X(128, 3, 128, 3, 128)
+#define TQ_ATTEND_LOGITS_CONFIGS(X) X(64, 2, 64) X(64, 3, 64) X(64, 3, 0) X(128, 3, 0) X(128, 2, 128) X(128, 3, 128)
+
+// Grids of the attention launches within the launch limit.
+static bool attend_grids_fit(const ScoreShape &s) {
+  const int64_t nch = (s.n + att_chunk(s) - 1) / att_chunk(s);
+  const int g = s.hq / s.hkv;
+  // attend_partial; the query prep and attend_combine take at most one workgroup per 4 heads
+  return grid_fits(s.n_seq * s.hkv * (g / att_g(g)) * nch) && grid_fits((s.n_seq * s.hq + 3) / 4);
+}
+
+int attend_preflight(const CodecView &kc, const CodecView &vc, const ScoreShape &s) {
+  bool ok = false;
+#define TQ_AT_OK(DD, A, B, C, E) ok = ok || (kc.d == DD && kc.bits == A && kc.m == B && vc.bits == C && vc.m == E);
+  TQ_ATTEND_CONFIGS(TQ_AT_OK)
+#undef TQ_AT_OK
+  return ok && attend_grids_fit(s) ? TQ_OK : TQ_EUNSUPPORTED;
+}
+
+int attend_logits_preflight(const CodecView &vc, const ScoreShape &s) {
+  bool ok = false;
+#define TQ_AL_OK(DD, C, E) ok = ok || (vc.d == DD && vc.bits == C && vc.m == E);
+  TQ_ATTEND_LOGITS_CONFIGS(TQ_AL_OK)
+#undef TQ_AL_OK
+  return ok && attend_grids_fit(s) ? TQ_OK : TQ_EUNSUPPORTED;
+}
+
 int launch_attend(const CodecView &kc, const CodecView &vc, const float *q, const ScoreShape &s, const CodesView &k,
                   const CodesView &v, float scale, float *out, void *ws, size_t ws_bytes, void *stream,
                   const int32_t *pos, float rope_base) {
   if (s.n_seq == 0) return TQ_OK;
   (void)ws_bytes;
+  if (attend_preflight(kc, vc, s) != TQ_OK) return TQ_EUNSUPPORTED;  // before any launch
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   float *qt = reinterpret_cast<float *>(ws);
   float *qh = qt + (size_t)s.n_seq * s.hq * kc.d;
@@ -489,8 +521,7 @@ int launch_attend(const CodecView &kc, const CodecView &vc, const float *q, cons
   rc = TQ_EUNSUPPORTED;
 #define TQ_AT(DD, A, B, C, E) \
   if (D == DD && KB == A && KM == B && VB == C && VM == E) rc = launch_att_g<DD, A, B, C, E>(a, s, st); else
-  TQ_AT(64, 2, 64, 2, 64) TQ_AT(64, 3, 64, 3, 64) TQ_AT(64, 2, 64, 3, 0) TQ_AT(128, 2, 128, 3, 0)
-  TQ_AT(128, 3, 0, 3, 0) TQ_AT(128, 2, 128, 2, 128) TQ_AT(128, 3, 128, 3, 128) {}
+  TQ_ATTEND_CONFIGS(TQ_AT) {}
 #undef TQ_AT
   if (rc != TQ_OK) return rc;
   CombArgs c{part, s.n_seq * s.hq, s.hq, s.hkv, nch, s.n, vc.rot, vc.n_rot, vc.vecs_per_rot, vc.sketch, out};
@@ -511,6 +542,7 @@ size_t attend_logits_workspace(const CodecView &vc, const ScoreShape &s) {
 int launch_attend_logits(const CodecView &vc, const float *logits, const ScoreShape &s, const CodesView &v,
                          float scale, float *out, void *ws, void *stream) {
   if (s.n_seq == 0) return TQ_OK;
+  if (attend_logits_preflight(vc, s) != TQ_OK) return TQ_EUNSUPPORTED;  // before any launch
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   float *part = reinterpret_cast<float *>(ws);
   const int ch = att_chunk(s);
@@ -522,7 +554,7 @@ int launch_attend_logits(const CodecView &vc, const float *logits, const ScoreSh
   int rc = TQ_EUNSUPPORTED;
 #define TQ_AL(DD, C, E) \
   if (D == DD && VB == C && VM == E) rc = launch_att_g<DD, 2, 0, C, E, true>(a, s, st); else
-  TQ_AL(64, 2, 64) TQ_AL(64, 3, 64) TQ_AL(64, 3, 0) TQ_AL(128, 3, 0) TQ_AL(128, 2, 128) TQ_AL(128, 3, 128) {}
+  TQ_ATTEND_LOGITS_CONFIGS(TQ_AL) {}
 #undef TQ_AL
   if (rc != TQ_OK) return rc;
   CombArgs c{part, s.n_seq * s.hq, s.hq, s.hkv, nch, s.n, vc.rot, vc.n_rot, vc.vecs_per_rot, vc.sketch, out};

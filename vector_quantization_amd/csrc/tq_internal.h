@@ -62,6 +62,12 @@ int launch_attend(const CodecView &kc, const CodecView &vc, const float *q, cons
                   const CodesView &k, const CodesView &v, float scale, float *out, void *ws,
                   size_t ws_bytes, void *stream, const int32_t *pos = nullptr, float rope_base = 0.0f);
 
+// TQ_OK when launch_attend (resp. launch_attend_logits) builds the codecs' combination and its
+// grids fit the launch limits, TQ_EUNSUPPORTED otherwise; host only, launches nothing -- the
+// entry points call them before any launch, so that an unsupported call changes no memory
+int attend_preflight(const CodecView &kc, const CodecView &vc, const ScoreShape &s);
+int attend_logits_preflight(const CodecView &vc, const ScoreShape &s);
+
 // attention from given logits [n_seq][hq][n] (keys scored elsewhere) over value codes
 size_t attend_logits_workspace(const CodecView &vc, const ScoreShape &s);
 int launch_attend_logits(const CodecView &vc, const float *logits, const ScoreShape &s, const CodesView &v,

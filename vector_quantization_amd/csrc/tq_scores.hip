@@ -251,6 +251,49 @@ constexpr bool score_half_scratch() {
   return with <= lds && lds / with == lds / base;
 }
 
+// Error units of a 16-bit-table score (tq_lut.h): em per unit of nbar, eq per unit of rq =
+// rnbar sqrt(pi/2)/m.  Each of the NG index entries and NQ sign entries is rounded to the
+// nearest multiple of its table's unit (inv_m, inv_q), at most half a unit off; the integer sums
+// are exact and convert to fp32 exactly (|sum| < NG 32767 < 2^24), and the fp32 conversion by
+// the unit, the products with the norms and the final sum add at most 2^-21 of the largest
+// possible |sum| (NG 32767 units, NQ 32767 units) -- 0.0157 units per entry.
+template <int D, int BITS, int M>
+__device__ __forceinline__ void i16_error_units(float inv_m, float inv_q, float &em, float &eq) {
+  using C = Lut<D, BITS, M, 4>;
+  em = (float)C::NG * inv_m * 0.5157f;
+  eq = (float)C::NQ * inv_q * 0.5157f;
+}
+
+// Score keys t0 .. t1 - 1 of a kv block again for one query head with fp32 tables (the G = 1
+// layout, built over the 16-bit tables' LDS) and overwrite its logits: the 16-bit tables' error
+// guard's way back to fp32 accuracy.  qt [D] and qh [M] are the head's rotated query and sketch
+// in LDS; one points to {1, 1} in LDS (the fp32 tables' scales).  All threads call it; it ends
+// synchronised.
+template <int D, int BITS, int M, int NT>
+__device__ void rescore_fp32(const ScoreArgs &a, uint8_t *tabs, const float *qt, const float *qh, const float *cb,
+                             const float *one, int64_t row, int64_t vbase, int64_t t0, int64_t t1, float kappa) {
+  using C1 = Lut<D, BITS, M, 1>;
+  constexpr int SWN = C1::SW > 0 ? C1::SW : 1;
+  build_luts<D, BITS, M, 1, NT>(tabs, tabs + C1::MSE_BYTES, qt, qh, cb, one, one, nullptr);
+  __syncthreads();
+  HeadScales<1> hs1;
+  hs1.inv_m[0] = hs1.inv_q[0] = 1.0f;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += NT) {
+    const int64_t v = vbase + t;
+    uint32_t iw[C1::IW];
+    uint32_t sw[SWN];
+    load_words<C1::IW>(a.idx + v * a.idx_stride, iw);
+    if constexpr (M > 0) load_words<C1::SW>(a.sign + v * a.sign_stride, sw);
+    const uint32_t nw = a.norms[v];
+    float am[1], aq[1];
+    lut_score<D, BITS, M, 1>(iw, sw, tabs, tabs + C1::MSE_BYTES, hs1, am, aq);
+    float sc = f16_bits_to_float(nw & 0xFFFFu) * am[0];
+    if constexpr (M > 0) sc = fmaf(f16_bits_to_float(nw >> 16) * kappa, aq[0], sc);
+    a.logits[row * a.n_keys + t] = sc;
+  }
+  __syncthreads();  // the tables are rebuilt by the next call
+}
+
 template <int D, int BITS, int M, int G, int NT>
 __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
   using C = Lut<D, BITS, M, G>;
@@ -260,7 +303,7 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
   __shared__ float qt[G * D];
   __shared__ float qh[G * (M > 0 ? M : 1)];
   __shared__ float cb[C::L];
-  __shared__ float sc[4 * G];
+  __shared__ float sc[4 * G + 2];  // table scales (block_table_scales), then {1, 1} for fp32 tables
   // scratch of the half-table builder where LDS has room for it
   constexpr bool HALF = score_half_scratch<D, BITS, M, G>();
   __shared__ __align__(16) float halfs[HALF ? lut_half_bytes<D, BITS, M, G>() / 4 : 4];
@@ -284,6 +327,7 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
   QueryPrep<D, M, G, NT> prep;
   prep.issue(a.q + qrow * D, a.rot + rid * (int64_t)D * D, a.sketch);
   if (threadIdx.x < C::L) cb[threadIdx.x] = a.centroids[threadIdx.x];
+  if (threadIdx.x < 2) sc[4 * G + threadIdx.x] = 1.0f;
   prep.finish(qs, qt, qh);
   HeadScales<G> hs;
   block_table_scales<D, BITS, M, G>(qt, qh, cb, sc, hs);
@@ -295,6 +339,10 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
   int64_t t1 = t0 + a.chunk;
   if (t1 > a.n_keys) t1 = a.n_keys;
   const int64_t vbase = blk * a.n_keys;
+  // 16-bit tables: the chunk's largest |logit| per head and largest norms, for the error guard
+  float smax[G], nmax = 0.0f, rmax = 0.0f;
+#pragma unroll
+  for (int h = 0; h < G; ++h) smax[h] = 0.0f;
   for (int64_t t = t0 + threadIdx.x; t < t1; t += NT) {
     const int64_t v = vbase + t;
     uint32_t iw[C::IW];
@@ -311,6 +359,55 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
       float sc = nbar * am[h];
       if constexpr (M > 0) sc = fmaf(rq, aq[h], sc);
       a.logits[(qrow + h) * a.n_keys + t] = sc;
+      if constexpr (C::I16) smax[h] = fmaxf(smax[h], fabsf(sc));
+    }
+    if constexpr (C::I16) {
+      nmax = fmaxf(nmax, nbar);
+      rmax = fmaxf(rmax, rq);
+    }
+  }
+  if constexpr (C::I16) {
+    // Error guard of the 16-bit tables.  A key's logit misses the exact table sums by at most
+    // E = nbar Em + rq Eq (i16_error_units), so every logit of the chunk is within
+    // Emax = nmax Em + rmax Eq of its fp32-table value.  The row's largest |logit| is at least
+    // the chunk's, so Emax <= tau (max |logit| - Emax) with tau = 5e-4 keeps the chunk's errors
+    // within half the 1e-3 row-relative tolerance; a head of the chunk that fails it (a short
+    // row, or a query nearly orthogonal to every key) is scored again with fp32 tables.
+    float *red = reinterpret_cast<float *>(tabs);  // [NT / kWave][G + 2], after the barrier below
+    constexpr int NW = NT / kWave;
+#pragma unroll
+    for (int h = 0; h < G; ++h) smax[h] = wave_max_dpp(smax[h]);
+    nmax = wave_max_dpp(nmax);
+    rmax = wave_max_dpp(rmax);
+    __syncthreads();  // every wavefront is done with the tables
+    const int wid = threadIdx.x / kWave;
+    if (lane_id() == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) red[wid * (G + 2) + h] = smax[h];
+      red[wid * (G + 2) + G] = nmax;
+      red[wid * (G + 2) + G + 1] = rmax;
+    }
+    __syncthreads();
+    float mx[G + 2];
+#pragma unroll
+    for (int k = 0; k < G + 2; ++k) {
+      mx[k] = 0.0f;
+      for (int w = 0; w < NW; ++w) mx[k] = fmaxf(mx[k], red[w * (G + 2) + k]);
+    }
+    unsigned redo = 0;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float em, eq;
+      i16_error_units<D, BITS, M>(hs.inv_m[h], hs.inv_q[h], em, eq);
+      const float emax = mx[G] * em + mx[G + 1] * eq;
+      if (!(emax <= 5e-4f * (mx[h] - emax))) redo |= 1u << h;
+    }
+    __syncthreads();  // every thread has read red (it aliases the tables rebuilt below)
+    if (redo != 0u) {  // uniform: every thread computed it from the same LDS values
+      for (int h = 0; h < G; ++h)
+        if (redo & (1u << h))
+          rescore_fp32<D, BITS, M, NT>(a, tabs, qt + h * D, qh + h * (M > 0 ? M : 1), cb, sc + 4 * G,
+                                       qrow + h, vbase, t0, t1, kappa);
     }
   }
 }
