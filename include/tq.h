@@ -22,7 +22,8 @@
  *   - Argument checks run on the host before any launch and return a negative status; a
  *     failed launch returns TQ_EHIP.  Faults inside kernels surface at the caller's next
  *     synchronisation.  No C++ exception crosses this interface.
- *   - Calls are reentrant: the library keeps no mutable global state.
+ *   - Calls are reentrant: the library keeps no mutable global state (one exception:
+ *     tq_decode_step_noalloc shares one static scratch array per GPU between its calls).
  *   - Inputs must be finite.  A vector norm of 65520 or more does not fit fp16 and is out of
  *     contract (it is stored as +inf).
  */
@@ -42,7 +43,8 @@ typedef enum {
   TQ_EUNSUPPORTED = -2, /* (d, bits, m, heads-per-group, dtype) not built            */
   TQ_EALIGN = -3,       /* plane stride or pointer alignment violated                */
   TQ_EWORKSPACE = -4,   /* workspace NULL or smaller than tq_workspace_bytes         */
-  TQ_EHIP = -5          /* a HIP launch failed                                       */
+  TQ_EHIP = -5,         /* a HIP launch failed                                       */
+  TQ_ESCRATCH = -6      /* the call needs more than the static scratch maximum        */
 } tq_status;
 
 typedef enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
@@ -197,6 +199,23 @@ int tq_decode_step(const tq_codec *kc, const tq_codec *vc, const float *q, const
                    int64_t cap, const int32_t *pos, float rope_base, tq_codes kcache,
                    tq_codes vcache, float scale, float *out, void *ws, size_t ws_bytes,
                    void *stream);
+
+/* tq_decode_step for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same checks, kernels and results,
+ * with no workspace argument.  The workspace is the library's own scratch array, a static device
+ * array of TQ_NOALLOC_SCRATCH_BYTES per GPU (reserved when the library's code is loaded on that
+ * GPU, held until the process ends); this call allocates and frees nothing.  A call whose
+ * tq_workspace_bytes(TQ_OP_DECODE_STEP, ...) exceeds it returns TQ_ESCRATCH before any launch
+ * (the 8B-class step at batch 256 x capacity 32768 needs about 16 MiB).  Every call on one GPU
+ * uses that GPU's array: calls that overlap on one GPU (other streams, other threads) race and
+ * must be serialised by the caller.  Nothing in the array needs clearing between calls (each
+ * call writes every scratch value it reads).  The first call on a device looks up that device's
+ * copy of the array (the calling thread's current device).                                 */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int tq_decode_step_noalloc(const tq_codec *kc, const tq_codec *vc, const float *q, const void *k_new,
+                           const void *v_new, tq_dtype dt, int64_t n_seq, int32_t hq, int32_t hkv,
+                           int64_t cap, const int32_t *pos, float rope_base, tq_codes kcache,
+                           tq_codes vcache, float scale, float *out, void *stream);
 
 /* Inner-product top-k search over an encoded database (one shared rotation):
  * for each query the k database rows with the largest estimated <q, x> (ties: smaller row

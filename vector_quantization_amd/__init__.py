@@ -71,6 +71,8 @@ def _load():
         "tq_append": ([CP, P, I32, I64, I32, P, I64, ctypes.c_float, _Codes, P], I32),
         "tq_decode_step": ([CP, CP, P, P, P, I32, I64, I32, I32, I64, P, ctypes.c_float, _Codes, _Codes,
                             ctypes.c_float, P, P, SZ, P], I32),
+        "tq_decode_step_noalloc": ([CP, CP, P, P, P, I32, I64, I32, I32, I64, P, ctypes.c_float, _Codes, _Codes,
+                                    ctypes.c_float, P, P], I32),
         "tq_workspace_bytes": ([ctypes.c_int, CP, CP, I64, I32, I32, I64], SZ),
         "tq_make_polar_tables": ([I32, I32, P], I32),
         "tq_polar_record_bytes": ([I32, I32], SZ),
@@ -103,7 +105,8 @@ class _Lib:
 lib = _Lib()
 EXPORTED = ("tq_make_rotation", "tq_make_head_rotations", "tq_make_sketch", "tq_make_codebook",
             "tq_calibrate_codebook", "tq_encode",
-            "tq_scores", "tq_attend_decode", "tq_append", "tq_decode_step", "tq_search_topk",
+            "tq_scores", "tq_attend_decode", "tq_append", "tq_decode_step", "tq_decode_step_noalloc",
+            "tq_search_topk",
             "tq_workspace_bytes", "tq_status_str", "tq_version", "tq_make_polar_tables",
             "tq_polar_record_bytes", "tq_polar_encode", "tq_polar_scores", "tq_polar_attend_workspace_bytes",
             "tq_polar_attend_decode")
@@ -507,6 +510,34 @@ def decode_step(kcodec: Codec, vcodec: Codec, q, k_new, v_new, pos, cap: int, ro
     _check(lib.tq_decode_step(ctypes.byref(kc), ctypes.byref(vc), _ptr(q), _ptr(kn), _ptr(vn), dt, n_seq, hq, hkv,
                               cap, _ptr(pos), ctypes.c_float(rope_base), kcache.c(), vcache.c(),
                               ctypes.c_float(scale), _ptr(out), ws, wsb, _stream()))
+    return out
+
+
+def decode_step_noalloc(kcodec: Codec, vcodec: Codec, q, k_new, v_new, pos, cap: int, rope_base: float,
+                        kcache: Codes, vcache: Codes, scale: float, out):
+    """decode_step with the library's static scratch array as its workspace (tq_decode_step_noalloc):
+    nothing is allocated, ``out`` [n_seq, hq, d] fp32 is the caller's.  Calls that overlap on one
+    GPU race on that array."""
+    named = _check_queries(q, kcodec.d)
+    n_seq, hq, d = q.shape
+    named += _check_rows(k_new, d, "k_new") + _check_rows(v_new, d, "v_new")
+    _need(k_new.dim() == 3 and k_new.shape[0] == n_seq and k_new.is_contiguous() and v_new.is_contiguous(),
+          "k_new, v_new must be contiguous [n_seq, hkv, d]")
+    hkv = k_new.shape[1]
+    _need(tuple(v_new.shape) == tuple(k_new.shape) and v_new.dtype == k_new.dtype, "v_new must match k_new")
+    _check_heads(hq, hkv)
+    _need(vcodec.d == d and cap >= 1, "kcodec and vcodec must share d; cap >= 1")
+    named += _check_tensor(pos, "pos", dtype=_torch().int32, shape=(n_seq,))
+    named += _check_codec(kcodec, "kcodec") + _check_codec(vcodec, "vcodec")
+    named += _check_codes(kcache, kcodec, n_seq * hkv * cap, "kcache")
+    named += _check_codes(vcache, vcodec, n_seq * hkv * cap, "vcache")
+    named += _check_tensor(out, "out", dtype=_torch().float32, shape=(n_seq, hq, d))
+    _check_devices(named)
+    kc, vc = kcodec.c(), vcodec.c()
+    _check(lib.tq_decode_step_noalloc(ctypes.byref(kc), ctypes.byref(vc), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                      _DT[str(k_new.dtype).replace("torch.", "")], n_seq, hq, hkv, cap, _ptr(pos),
+                                      ctypes.c_float(rope_base), kcache.c(), vcache.c(), ctypes.c_float(scale),
+                                      _ptr(out), _stream()))
     return out
 
 

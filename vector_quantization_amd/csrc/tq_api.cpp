@@ -129,10 +129,15 @@ extern "C" int tq_append(const tq_codec *c, const void *x_new, tq_dtype dt, int6
   return tq::launch_append(tq::view(*c), x_new, (int)dt, n_seq, hkv, pos, cap, rope_base, tq::view(cache), stream);
 }
 
-extern "C" int tq_decode_step(const tq_codec *kc, const tq_codec *vc, const float *q, const void *k_new,
-                              const void *v_new, tq_dtype dt, int64_t n_seq, int32_t hq, int32_t hkv,
-                              int64_t cap, const int32_t *pos, float rope_base, tq_codes kcache, tq_codes vcache,
-                              float scale, float *out, void *ws, size_t ws_bytes, void *stream) {
+namespace tq {
+
+// tq_decode_step; every check before the first launch.  With `scratch` set, the workspace is
+// not an argument: once the arguments are checked, scratch() gives the library's own buffer and
+// its size, and a call that needs more returns TQ_ESCRATCH.
+int decode_step_impl(const tq_codec *kc, const tq_codec *vc, const float *q, const void *k_new, const void *v_new,
+                     tq_dtype dt, int64_t n_seq, int32_t hq, int32_t hkv, int64_t cap, const int32_t *pos,
+                     float rope_base, tq_codes kcache, tq_codes vcache, float scale, float *out, void *ws,
+                     size_t ws_bytes, void *stream, int (*scratch)(void **ws, size_t *bytes)) {
   int rc = check_codec(kc);
   if (rc != TQ_OK) return rc;
   rc = check_codec(vc);
@@ -146,20 +151,35 @@ extern "C" int tq_decode_step(const tq_codec *kc, const tq_codec *vc, const floa
   if (rc != TQ_OK) return rc;
   rc = check_codes(vc, vcache);
   if (rc != TQ_OK) return rc;
-  const tq::ScoreShape s{n_seq, hq, hkv, cap};
+  const ScoreShape s{n_seq, hq, hkv, cap};
   // every check of the attention, and of both appends, before the first launch: an unsupported
   // combination must leave the caches untouched
-  rc = tq::attend_preflight(tq::view(*kc), tq::view(*vc), s);
+  rc = attend_preflight(view(*kc), view(*vc), s);
   if (rc != TQ_OK) return rc;
-  const size_t need = tq::attend_workspace(tq::view(*kc), tq::view(*vc), s);
+  const size_t need = attend_workspace(view(*kc), view(*vc), s);
+  if (scratch != nullptr) {
+    rc = scratch(&ws, &ws_bytes);
+    if (rc != TQ_OK) return rc;
+    if (need > ws_bytes) return TQ_ESCRATCH;
+  }
   if (!ws || ws_bytes < need) return TQ_EWORKSPACE;
   if (!aligned(ws, 256)) return TQ_EALIGN;
-  rc = tq::launch_append(tq::view(*kc), k_new, (int)dt, n_seq, hkv, pos, cap, rope_base, tq::view(kcache), stream);
+  rc = launch_append(view(*kc), k_new, (int)dt, n_seq, hkv, pos, cap, rope_base, view(kcache), stream);
   if (rc != TQ_OK) return rc;
-  rc = tq::launch_append(tq::view(*vc), v_new, (int)dt, n_seq, hkv, pos, cap, 0.0f, tq::view(vcache), stream);
+  rc = launch_append(view(*vc), v_new, (int)dt, n_seq, hkv, pos, cap, 0.0f, view(vcache), stream);
   if (rc != TQ_OK) return rc;
-  return tq::launch_attend(tq::view(*kc), tq::view(*vc), q, s, tq::view(kcache), tq::view(vcache), scale, out, ws,
-                           ws_bytes, stream, pos, rope_base);
+  return launch_attend(view(*kc), view(*vc), q, s, view(kcache), view(vcache), scale, out, ws, ws_bytes, stream,
+                       pos, rope_base);
+}
+
+}  // namespace tq
+
+extern "C" int tq_decode_step(const tq_codec *kc, const tq_codec *vc, const float *q, const void *k_new,
+                              const void *v_new, tq_dtype dt, int64_t n_seq, int32_t hq, int32_t hkv,
+                              int64_t cap, const int32_t *pos, float rope_base, tq_codes kcache, tq_codes vcache,
+                              float scale, float *out, void *ws, size_t ws_bytes, void *stream) {
+  return tq::decode_step_impl(kc, vc, q, k_new, v_new, dt, n_seq, hq, hkv, cap, pos, rope_base, kcache, vcache,
+                              scale, out, ws, ws_bytes, stream, nullptr);
 }
 
 extern "C" int tq_search_topk(const tq_codec *c, const float *queries, int64_t n_q, tq_codes db, int64_t n_db,

@@ -439,6 +439,7 @@ extern "C" const char *tq_status_str(int status) {
     case TQ_EALIGN: return "misaligned pointer or stride";
     case TQ_EWORKSPACE: return "workspace missing or too small";
     case TQ_EHIP: return "HIP launch failed";
+    case TQ_ESCRATCH: return "the call needs more scratch memory than the library's static maximum";
     default: return "unknown status";
   }
 }

@@ -73,6 +73,14 @@ size_t attend_logits_workspace(const CodecView &vc, const ScoreShape &s);
 int launch_attend_logits(const CodecView &vc, const float *logits, const ScoreShape &s, const CodesView &v,
                          float scale, float *out, void *ws, void *stream);
 
+// tq_decode_step behind its C entry point (all argument checks, then the launches), shared with
+// the entry point that takes its workspace from the library's static scratch array: with
+// `scratch` set, ws and ws_bytes come from scratch() once the arguments are checked
+int decode_step_impl(const tq_codec *kc, const tq_codec *vc, const float *q, const void *k_new, const void *v_new,
+                     tq_dtype dt, int64_t n_seq, int32_t hq, int32_t hkv, int64_t cap, const int32_t *pos,
+                     float rope_base, tq_codes kcache, tq_codes vcache, float scale, float *out, void *ws,
+                     size_t ws_bytes, void *stream, int (*scratch)(void **ws, size_t *bytes));
+
 size_t search_workspace(const CodecView &c, int64_t n_q, int k, int64_t n_db);
 int launch_search(const CodecView &c, const float *queries, int64_t n_q, const CodesView &db,
                   int64_t n_db, int k, int64_t *out_idx, float *out_score, void *ws, size_t ws_bytes,
