@@ -8,7 +8,9 @@ is one decode step over the resident compressed cache for all layers: the score 
 
 Prints one JSON line.  value = decode-scoring GB/s: algorithmic bytes of one tq_scores call
 (the key code planes, unpadded, + the fp32 logits written + the queries read) divided by the
-call's average duration measured with HIP events on the launch stream.
+call's median duration measured with HIP events on the launch stream.  The same line carries the
+other workloads under "configs" (the tiny case, the ESM-2-shaped cache, the 131072-token
+sequence and the 1M-vector search), each timed by its own medians in the same run.
 """
 
 import argparse
@@ -51,6 +53,8 @@ def parse():
     ap.add_argument("--encode-reps", type=int, default=3)
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for hardware byte counters)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="default workload only: skip the other workloads' sub-objects (profiling runs)")
     return ap.parse_args()
 
 
@@ -82,6 +86,40 @@ def measured_traffic(kernel_names):
     if src != score_source_hash() or not all(k in vals for k in kernel_names):
         return None
     return sum(vals[k] for k in kernel_names)
+
+
+ENCODE_SOURCES = ("vector_quantization_amd/csrc/tq_encode.hip", "vector_quantization_amd/csrc/tq_device.h")
+ENCODE_PROFILE = os.path.join(ROOT, "profiles", "encode_mfma_gqa8b_decode_b8_32k_counters.txt")
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def source_hash(names):
+    import hashlib
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def encode_counters():
+    """MFMA busy fractions of the two encode launches of the decode workload from the committed
+    counter summary (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 1024 SIMDs), or None when
+    the encoder's sources have changed since the counters were taken."""
+    try:
+        lines = open(ENCODE_PROFILE).read().splitlines()
+    except OSError:
+        return None
+    vals, src = {}, None
+    for ln in lines:
+        if ln.startswith("source_sha256:"):
+            src = ln.split(":", 1)[1].strip()
+        elif ln.startswith("mfma_busy_frac["):
+            k, v = ln[len("mfma_busy_frac["):].split("]:", 1)
+            vals[k] = float(v)
+    if src != source_hash(ENCODE_SOURCES) or not vals:
+        return None
+    return vals
 
 
 def gpu_clocks():
@@ -120,17 +158,26 @@ def hbm_ceiling(dev):
 
     t_read = best(lambda: x.view(-1, 4096).sum(1))  # row sums: the fastest torch read stream here
     t_copy = best(lambda: y.copy_(x[: 1 << 29]))
+    # three read streams and one write stream of 768 MiB each: the 3.3 : 1 read : write mix of the
+    # score stream (52 B of codes read and 16 B of logits written per key) is closest to this
+    n = 3 << 26
+    a3, b3, c3 = x[:n], x[n:2 * n], x[2 * n:3 * n]
+    d3 = torch.empty(n, dtype=torch.float32, device=dev)
+    t_mix = best(lambda: torch.addcmul(a3, b3, c3, out=d3))
     res = {"read_stream_GBps": round(x.numel() * 4 / (t_read * 1e-3) / 1e9, 1),
            "copy_GBps": round(2 * y.numel() * 4 / (t_copy * 1e-3) / 1e9, 1),
-           "kernels": "torch row sums over 4 GiB fp32 (rows of 4096); torch copy of 2 GiB"}
-    del x, y
+           "mixed_3r1w_GBps": round(4 * n * 4 / (t_mix * 1e-3) / 1e9, 1),
+           "kernels": "torch row sums over 4 GiB fp32 (rows of 4096); torch copy of 2 GiB; torch addcmul "
+                      "(3 x 768 MiB read, 768 MiB written)"}
+    del x, y, d3
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(w, K, q, seed_rot, seed_sk):
+def cpu_baseline(w, K, q, seed_rot, seed_sk, V=None):
     """Time the oracle's encode and scoring of four (layer, batch) slices -- layers {0, L-1} x
-    batches {0, B-1}, all kv heads, full context -- on the host cores."""
+    batches {0, B-1}, all kv heads, full context -- on the host cores; with V, also the oracle's
+    attention over the first slice (its values encoded by the oracle as well)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -155,14 +202,31 @@ def cpu_baseline(w, K, q, seed_rot, seed_sk):
         t_sc += time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     keys = len(slices) * w.hkv * w.n_ctx
-    return {
+    code_b = (w.d * w.k_bits + 7) // 8 + (w.k_m + 7) // 8 + 4
+    res = {
         "value": keys / t_sc, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
         "sample": (f"(layer, batch) in {slices}: {w.hkv} kv heads x {w.n_ctx} keys each, scored for {w.hq} query "
                    f"heads ({t_sc:.1f} s); oracle encode of the same {keys} keys took {t_enc:.1f} s "
                    f"({keys / t_enc:.3g} vectors/s)"),
+        "GBps": keys * (code_b + 4 * w.group) / t_sc / 1e9,
         "encode_vectors_per_s": keys / t_enc,
         "affinity_cores": len(os.sched_getaffinity(0)),
     }
+    if V is not None:
+        import synth
+
+        vora = oc.make_codec(w.d, w.v_bits, w.v_m, synth.SEED_ROT_V, synth.SEED_SKETCH_V)
+        kx = K[0, 0].float().cpu().numpy().reshape(-1, w.d)
+        vx = V[0, 0].float().cpu().numpy().reshape(-1, w.d)
+        kcodes, vcodes = oq.encode(kx, ora), oq.encode(vx, vora)
+        qx = q[0, 0].cpu().numpy().astype(np.float64)[None]  # [1, hq, d]
+        t0 = time.perf_counter()
+        oe.attend(qx, kcodes, vcodes, ora, vora, w.n_ctx, w.hkv, 1.0 / math.sqrt(w.d))
+        t_at = time.perf_counter() - t0
+        res["attend_tokens_per_s"] = w.hkv * w.n_ctx / t_at
+        res["attend_sample"] = (f"(layer, batch) (0, 0): {w.hq} query heads over {w.hkv} kv heads x {w.n_ctx} "
+                                f"tokens ({t_at:.1f} s)")
+    return res
 
 
 INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix peak
@@ -172,6 +236,12 @@ N_CU = 256
 
 def search_main(a):
     """Top-10 inner-product search over 1M encoded d=200 vectors for 10k queries."""
+    print(json.dumps(search_line(a)), flush=True)
+
+
+def search_line(a, cpu=None):
+    """The search workload's line (dict); cpu: run the oracle leg (default: unless
+    --no-cpu-baseline)."""
     import numpy as np
     import torch
 
@@ -237,7 +307,7 @@ def search_main(a):
                                "two int8 query limbs, 64 queries per workgroup)"},
         "gpu": torch.cuda.get_device_name(0), "clocks": gpu_clocks(),
     }
-    if not a.no_cpu_baseline:
+    if cpu if cpu is not None else not a.no_cpu_baseline:
         from threadpoolctl import threadpool_info
 
         from oracle import codec as oc
@@ -253,7 +323,9 @@ def search_main(a):
         res["cpu_baseline"] = {"value": nq * db.shape[0] / tc, "unit": "pairs/s", "cores": int(threads),
                                "kind": "oracle",
                                "sample": f"{nq} queries against the full {db.shape[0]}-row database ({tc:.1f} s)"}
-    print(json.dumps(res), flush=True)
+    del db, qs, codes, truth, flush
+    torch.cuda.empty_cache()
+    return res
 
 
 def decode_step_main(a):
@@ -337,6 +409,10 @@ def esm2_main(a):
     """ESM-2-650M-shaped cache: encode of all K/V (fp16, per-(layer, head) rotations), one decode
     query per (layer, head) scored and attended over the 1024 cached tokens, and all-pairs scoring
     (every token against every cached key of its (layer, head))."""
+    print(json.dumps(esm2_line(a)), flush=True)
+
+
+def esm2_line(a):
     import numpy as np
     import torch
 
@@ -441,7 +517,9 @@ def esm2_main(a):
         "cache_bytes": 2 * n_vec * code_b,
         "gpu": torch.cuda.get_device_name(0), "clocks": gpu_clocks(),
     }
-    print(json.dumps(res), flush=True)
+    del Kd, Vd, kcodes, vcodes, tkcodes, tvcodes, logits_all, qa, flush
+    torch.cuda.empty_cache()
+    return res
 
 
 def polar_main(a):
@@ -601,36 +679,63 @@ def polar_main(a):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (got --gpus {a.gpus}); the multi-GPU split of this "
-              "path is a design note, not a measured configuration.", file=sys.stderr)
-        sys.exit(2)
-    if a.workload == "search":
-        search_main(a)
-        return
-    if a.workload == "esm2":
-        esm2_main(a)
-        return
-    if a.workload == "decode_step":
-        decode_step_main(a)
-        return
-    if a.workload == "polar":
-        polar_main(a)
-        return
+def tiny_line(a):
+    """The tiny case (1 head, d = 64, 256 keys and values, 2-bit + QJL m = 64 for both): encode of
+    K and V, scores and attention of one query, each the median of a.steps calls (launch-bound)."""
     import numpy as np
     import torch
 
     import synth
     import vector_quantization_amd as tq
 
-    w = synth.GQA_DECODE if a.workload == "gqa" else synth.LONG_CTX
+    w = synth.TINY
+    K, V, q = synth.tiny()
+    kc = tq.make_codec(w.d, w.k_bits, w.k_m, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
+    vc = tq.make_codec(w.d, w.v_bits, w.v_m, synth.SEED_ROT_V, synth.SEED_SKETCH_V)
+    Kd, Vd = torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda()
+    qd = torch.from_numpy(q.reshape(1, 1, -1)).cuda()
+    kcodes, vcodes = tq.alloc_codes(kc, w.n_ctx), tq.alloc_codes(vc, w.n_ctx)
+    logits = torch.empty((1, 1, w.n_ctx), dtype=torch.float32, device="cuda")
+    out = torch.empty((1, 1, w.d), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(w.d)
+    calls = {
+        "encode_kv": lambda: (tq.encode(kc, Kd, out=kcodes), tq.encode(vc, Vd, out=vcodes)),
+        "scores": lambda: tq.scores(kc, qd, kcodes, w.n_ctx, 1, logits=logits),
+        "attend": lambda: tq.attend_decode(kc, vc, qd, kcodes, vcodes, w.n_ctx, 1, scale, out=out),
+    }
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    res = {"workload": f"tiny: 1 head, d={w.d}, {w.n_ctx} keys and values, 2-bit + QJL m={w.k_m} (K and V), "
+                       "1 query", "unit": "us (median per call, HIP events)"}
+    for name, fn in calls.items():
+        for _ in range(a.warmup):
+            fn()
+        ts = []
+        for _ in range(max(a.steps, 20)):
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        res[f"{name}_us"] = round(float(np.median(ts)), 2)
+    res["step_us"] = round(res["encode_kv_us"] + res["scores_us"] + res["attend_us"], 2)
+    return res
+
+
+def kv_line(a, w, seed, cpu):
+    """The decode workload w (8B-class GQA, or the 131072-token sequence): bulk encode of the whole
+    K/V prefix (timed on its own), then a.steps decode steps over the resident compressed cache --
+    tq_scores then tq_attend_decode, each timed by HIP events on the launch stream; medians."""
+    import numpy as np
+    import torch
+
+    import synth
+    import vector_quantization_amd as tq
+
     dev = "cuda"
     torch.cuda.init()
     stream = torch.cuda.current_stream()
     log("workload", w)
-    K, V, q = synth.gqa_decode(w, seed=2 if a.workload == "gqa" else 3, device=dev)
+    K, V, q = synth.gqa_decode(w, seed=seed, device=dev)
     kc = tq.make_codec(w.d, w.k_bits, w.k_m, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
     vc = tq.make_codec(w.d, w.v_bits, w.v_m, synth.SEED_ROT_V, synth.SEED_SKETCH_V)
     n_vec = w.n_seq * w.hkv * w.n_ctx
@@ -660,12 +765,6 @@ def main():
     out = torch.empty((w.n_seq, w.hq, w.d), dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(w.d)
     do_attend = not a.no_attend
-    if do_attend:
-        try:
-            tq.attend_decode(kc, vc, qf, kcodes, vcodes, w.n_ctx, w.hkv, scale, out=out)
-        except tq.TQError as e:
-            log("attend unavailable:", e)
-            do_attend = False
 
     def step(evs=None):
         if evs:
@@ -690,8 +789,8 @@ def main():
     wall = time.perf_counter() - t0
     sc_ms = [e[0].elapsed_time(e[1]) for e in evs]
     at_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    t_sc = float(np.mean(sc_ms))
-    t_at = float(np.mean(at_ms)) if do_attend else None
+    t_sc = float(np.median(sc_ms))
+    t_at = float(np.median(at_ms)) if do_attend else None
     ms_step = wall * 1e3 / a.steps
 
     keys = w.n_seq * w.hkv * w.n_ctx
@@ -704,6 +803,9 @@ def main():
     enc_in = n_vec * w.d * 2
     enc_out_k = n_vec * code_b_k
     enc_out_v = n_vec * code_b_v
+    # the encoder's matrix products, algorithmic: y = Pi x (2 d^2 flop per vector) and, for keys,
+    # z = S r (2 m d)
+    fl_k, fl_v = n_vec * (2 * w.d * w.d + 2 * w.k_m * w.d), n_vec * (2 * w.d * w.d + 2 * w.v_m * w.d)
     res = {
         "metric": METRIC,
         "value": round(gbps, 1),
@@ -716,6 +818,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "dtype_note": ("fp32 queries and accumulation; with 4 query heads per kv head the lookup entries are "
+                       "16-bit fixed point, and a chunk whose error bound is not below 5e-4 of its largest "
+                       "|logit| is scored again with fp32 entries"),
         "data": "synthetic (seeded bf16 K/V, N(0,1) with 2% channels x10; fp32 queries)",
         "config": {
             "workload": f"{w.name}: {w.layers} layers x batch {w.batch}, {w.hq} q / {w.hkv} kv heads, d={w.d}, "
@@ -723,34 +828,117 @@ def main():
             "layers": w.layers, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "head_dim": w.d, "n_ctx": w.n_ctx,
             "k_bits": w.k_bits, "k_qjl_m": w.k_m, "v_bits": w.v_bits, "v_qjl_m": w.v_m,
         },
+        "timing": "medians of the timed steps (HIP events on the launch stream); ms_per_step is wall time",
         "scores_ms": round(t_sc, 4),
+        "scores_ms_min_max": [round(min(sc_ms), 4), round(max(sc_ms), 4)],
         "scores_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "keys_per_s": keys / (t_sc * 1e-3),
         "qk_pairs_per_s": keys * w.group / (t_sc * 1e-3),
         "scores_algorithmic_bytes": score_bytes,
         "attend_ms": None if t_at is None else round(t_at, 4),
         "attend_GBps": None if t_at is None else round(attend_bytes / (t_at * 1e-3) / 1e9, 1),
+        "attend_hbm_frac": None if t_at is None else round(attend_bytes / (t_at * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "attend_algorithmic_bytes": attend_bytes,
         "encode_ms": {"K": round(t_enc_k, 3), "V": round(t_enc_v, 3)},
         "encode_vectors_per_s": round(2 * n_vec / ((t_enc_k + t_enc_v) * 1e-3)),
         "encode_GBps": round((2 * enc_in + enc_out_k + enc_out_v) / ((t_enc_k + t_enc_v) * 1e-3) / 1e9, 1),
+        "encode_mfma": {"K_algorithmic_TFLOPs": round(fl_k / (t_enc_k * 1e-3) / 1e12, 1),
+                        "V_algorithmic_TFLOPs": round(fl_v / (t_enc_v * 1e-3) / 1e12, 1),
+                        "peak_TFLOPs": BF16_PEAK_TFLOPS,
+                        "K_frac_of_bf16_peak": round(fl_k / (t_enc_k * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                        "busy_frac_counters": encode_counters() if w.name == "gqa8b_decode_b8_32k" else None,
+                        "note": "algorithmic flops: y = Pi x (2 d^2) and z = S r (2 m d) per vector; the "
+                                "kernel issues them as bf16 hi/lo split products (2 for bf16 input, 3 for "
+                                "the sketch).  busy_frac: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x "
+                                "1024 SIMDs) from the committed counter summary (null when the encoder "
+                                "changed since)"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(SCORE_KERNELS) if a.workload == "gqa" else None,
+                     "traffic": measured_traffic(SCORE_KERNELS) if w.name == "gqa8b_decode_b8_32k" else None,
                      "kernel": " + ".join(SCORE_KERNELS) + " (one tq_scores call)"},
         "gpu": torch.cuda.get_device_name(0), "clocks": gpu_clocks(),
     }
-    res["hbm_ceiling"] = hbm_ceiling(dev)
+    host = None
+    if cpu:
+        # the oracle's inputs on the host before the device memory is released
+        sl = sorted({(0, 0), (0, w.batch - 1), (w.layers - 1, 0), (w.layers - 1, w.batch - 1)})
+        host = ({k: K[k].cpu() for k in sl}, {(0, 0): V[0, 0].cpu()}, {k: q[k].cpu() for k in sl})
+    del K, V, q, kcodes, vcodes, logits, Kf, Vf
+    torch.cuda.empty_cache()
+    return res, host
+
+
+class _Slices:
+    """K / V / q restricted to the (layer, batch) slices copied to the host; indexed like them."""
+
+    def __init__(self, d):
+        self.d = d
+
+    def __getitem__(self, lb):
+        return self.d[lb]
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {a.gpus}); the multi-GPU split of this "
+              "path is a design note, not a measured configuration.", file=sys.stderr)
+        sys.exit(2)
+    if a.workload == "search":
+        search_main(a)
+        return
+    if a.workload == "esm2":
+        esm2_main(a)
+        return
+    if a.workload == "decode_step":
+        decode_step_main(a)
+        return
+    if a.workload == "polar":
+        polar_main(a)
+        return
+    import synth
+
+    w = synth.GQA_DECODE if a.workload == "gqa" else synth.LONG_CTX
+    cpu = not a.no_cpu_baseline
+    res, host = kv_line(a, w, 2 if a.workload == "gqa" else 3, cpu)
+    res["hbm_ceiling"] = hbm_ceiling("cuda")
     if a.calibrate:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        import torch
+
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
         res["calibration_copy_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
-    if not a.no_cpu_baseline:
+        del src, dst
+    if a.workload == "gqa" and not a.no_configs:
+        # every other workload under the same clock: the tiny case, the ESM-2-shaped cache, the
+        # 131072-token sequence and the 1M-vector search (its oracle leg stays in --workload search)
+        cfg = {}
+        log("config 1: tiny")
+        cfg["1_tiny"] = tiny_line(a)
+        log("config 2: esm2")
+        e = esm2_line(a)
+        cfg["2_esm2"] = {k: e[k] for k in ("config", "encode_ms", "scores_us", "attend_us", "scores_GBps",
+                                           "allpairs_ms", "allpairs_pairs_per_s", "attend_cos_vs_exact",
+                                           "turboesm", "cache_bytes")}
+        cfg["2_esm2"]["encode_vectors_per_s"] = e["value"]
+        log("config 4: long context")
+        lr, _ = kv_line(a, synth.LONG_CTX, 3, False)
+        cfg["4_long"] = {k: lr[k] for k in ("config", "scores_ms", "scores_hbm_frac", "keys_per_s", "attend_ms",
+                                            "attend_GBps", "encode_ms", "encode_vectors_per_s")}
+        cfg["4_long"]["scores_GBps"] = lr["value"]
+        log("config 5: search")
+        sr = search_line(a, cpu=False)
+        cfg["5_search"] = {k: sr[k] for k in ("config", "ms_per_step", "recall_at_10", "one_at_10", "encode_ms",
+                                              "encode_vectors_per_s", "roofline")}
+        cfg["5_search"]["pairs_per_s"] = sr["value"]
+        res["configs"] = cfg
+    if cpu:
         log("cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(w, K, q, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
+        K, V, q = (_Slices(h) for h in host)
+        res["cpu_baseline"] = cpu_baseline(w, K, q, synth.SEED_ROT_K, synth.SEED_SKETCH_K, V=V)
     print(json.dumps(res), flush=True)
 
 
