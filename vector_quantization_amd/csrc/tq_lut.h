@@ -339,16 +339,52 @@ __device__ __forceinline__ void lut_score(const uint32_t (&iw)[Lut<D, BITS, M, G
     am[h] = aq[h] = 0.0f;
     im[h] = iq[h] = 0;
   }
+  if constexpr (C::I16) {
+    // 16-bit entries: the reads of a batch of groups are all issued before any is summed, so
+    // that many table reads are in flight at once whatever else the caller keeps in registers
+    constexpr int NT_ = C::NG + C::NQ;
+    constexpr int B = 16;
 #pragma unroll
-  for (int p = 0; p < C::NG; ++p) {
-    const int code = group_code<BITS, C::IW, C::GB>(iw, p);
-    lut_accumulate<G>(mse, p * C::TS + code, am, im);
-  }
-  if constexpr (M > 0) {
+    for (int p0 = 0; p0 < NT_; p0 += B) {
+      uint2 e[B];
 #pragma unroll
-    for (int p = 0; p < C::NQ; ++p) {
-      const int byte = (sw[p >> 2] >> (8 * (p & 3))) & 0xFF;
-      lut_accumulate<G>(qjl, p * 256 + byte, aq, iq);
+      for (int k = 0; k < B; ++k) {
+        const int p = p0 + k;
+        if (p < C::NG) {
+          e[k] = reinterpret_cast<const uint2 *>(mse)[p * C::TS + group_code<BITS, C::IW, C::GB>(iw, p)];
+        } else if constexpr (M > 0) {
+          if (p < NT_) {
+            const int q = p - C::NG;
+            e[k] = reinterpret_cast<const uint2 *>(qjl)[q * 256 + ((sw[q >> 2] >> (8 * (q & 3))) & 0xFF)];
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < B; ++k) {
+        const int p = p0 + k;
+        if (p >= NT_) continue;
+        typedef short s2 __attribute__((ext_vector_type(2)));
+        const s2 lo = {1, 0}, hi = {0, 1};
+        const s2 x = __builtin_bit_cast(s2, e[k].x), y = __builtin_bit_cast(s2, e[k].y);
+        int *acc = p < C::NG ? im : iq;
+        acc[0] = __builtin_amdgcn_sdot2(x, lo, acc[0], false);
+        acc[1] = __builtin_amdgcn_sdot2(x, hi, acc[1], false);
+        acc[2] = __builtin_amdgcn_sdot2(y, lo, acc[2], false);
+        acc[3] = __builtin_amdgcn_sdot2(y, hi, acc[3], false);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < C::NG; ++p) {
+      const int code = group_code<BITS, C::IW, C::GB>(iw, p);
+      lut_accumulate<G>(mse, p * C::TS + code, am, im);
+    }
+    if constexpr (M > 0) {
+#pragma unroll
+      for (int p = 0; p < C::NQ; ++p) {
+        const int byte = (sw[p >> 2] >> (8 * (p & 3))) & 0xFF;
+        lut_accumulate<G>(qjl, p * 256 + byte, aq, iq);
+      }
     }
   }
   if constexpr (C::I16) {
