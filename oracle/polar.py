@@ -29,6 +29,17 @@ Readings (the pages leave these open):
   * Record: one bitstream, LSB first: pair j at bit (2 + ab) j as [sign of a (1 = negative),
     sign of b, angle index]; then the node indices of levels 2, 3, ..., L in order, ab bits
     each; pad bits zero.  Norm word: n16 in the low half, 0 in the high half.
+
+Stage 2 on the polar residual (hada.io TurboQuant page, "Estrutura de compressão em 2 etapas"
+and "Etapa 2: eliminação do erro oculto": the polar stage first, then the 1-bit QJL correction
+of the error it leaves), when the codec carries a sketch S (m x d):
+  * the stage-1 reconstruction in fp32, from the root down: the root is 1; a node's children
+    are fl32(parent * cos psi^) and fl32(parent * sin psi^) with the level's fp32 table values;
+    a pair gives +-fl32(r * cos psi^), +-fl32(r * sin psi^) (the recorded signs);
+  * residual in the rotated space r_i = fl32(y_i - fl32(nbar * u^_i)), rn16 = fp16 of the exact
+    norm of r, sign bit j = [ (S r)_j >= 0 ] exact -- the two-stage codec's stage 2 with the
+    polar reconstruction in place of the codebook levels;
+  * norm word: n16 low, rn16 high; scores nbar <Pi q, u^> + rnbar sqrt(pi/2)/m <S Pi q, 2 b - 1>.
 """
 
 import math
@@ -96,6 +107,8 @@ class PolarCodec:
     rot: np.ndarray                  # [n_rot, d, d] fp32
     levels: List[PolarLevel]         # levels[l - 1] for l = 1..L
     vecs_per_rot: int = 0
+    m: int = 0                       # > 0: QJL stage on the polar residual
+    sketch: Optional[np.ndarray] = None  # [m, d] fp32
 
     @property
     def L(self) -> int:
@@ -112,11 +125,13 @@ class PolarCodec:
         return np.minimum(ids // self.vecs_per_rot, self.rot.shape[0] - 1)
 
 
-def make_polar_codec(d: int, ab: int, rot_seed: int, basis_seeds=None, vecs_per_rot: int = 0) -> PolarCodec:
+def make_polar_codec(d: int, ab: int, rot_seed: int, basis_seeds=None, vecs_per_rot: int = 0, m: int = 0,
+                     sketch_seed: Optional[int] = None) -> PolarCodec:
     L = int(round(math.log2(d)))
     assert 1 << L == d, "d must be a power of two"
     rot = oc.haar_rotation(rot_seed, d)[None] if basis_seeds is None else oc.head_rotations(rot_seed, basis_seeds, d)
-    return PolarCodec(d, ab, rot, [angle_table(1 << (l - 1), ab) for l in range(1, L + 1)], vecs_per_rot)
+    sk = oc.gaussian_sketch(sketch_seed, m, d) if m > 0 else None
+    return PolarCodec(d, ab, rot, [angle_table(1 << (l - 1), ab) for l in range(1, L + 1)], vecs_per_rot, m, sk)
 
 
 @dataclass
@@ -124,6 +139,7 @@ class PolarCodes:
     bits: np.ndarray   # [n][stride] u8
     norms: np.ndarray  # [n] u32
     extra: dict = field(default_factory=dict)
+    sign: Optional[np.ndarray] = None  # [n][sign_stride] u8 (QJL stage), else None
 
 
 def _decide(A, B, lv: PolarLevel):
@@ -133,7 +149,8 @@ def _decide(A, B, lv: PolarLevel):
     return np.sum((B[..., None] * lv.c2) >= (A[..., None] * lv.s2), axis=-1).astype(np.uint32)
 
 
-def encode_rotated(y: np.ndarray, n16: np.ndarray, pc: PolarCodec, stride: Optional[int] = None) -> PolarCodes:
+def encode_rotated(y: np.ndarray, n16: np.ndarray, pc: PolarCodec, stride: Optional[int] = None,
+                   sign_stride: Optional[int] = None) -> PolarCodes:
     y = np.asarray(y, dtype=np.float32)
     n, d = y.shape
     a, b = y[:, 0::2], y[:, 1::2]
@@ -165,11 +182,46 @@ def encode_rotated(y: np.ndarray, n16: np.ndarray, pc: PolarCodec, stride: Optio
     packed = np.packbits(words[:, :stride * 8].reshape(n, stride, 8)[:, :, ::-1], axis=-1).reshape(n, stride)
     out[:] = packed
     norms = n16.astype(np.uint32)
-    return PolarCodes(out, norms, {"pair": pair, "nodes": nodes, "y": y})
+    codes = PolarCodes(out, norms, {"pair": pair, "nodes": nodes, "y": y})
+    if pc.m > 0:
+        _residual_stage(codes, y, n16, pc, sign_stride)
+    return codes
+
+
+def unit_directions32(pair: np.ndarray, nodes, pc: PolarCodec) -> np.ndarray:
+    """The stage-1 reconstruction u^ [n, d] in fp32, one rounding per product, from the root down
+    (the order the residual of the QJL stage is defined in)."""
+    n = pair.shape[0]
+    r = np.ones((n, 1), dtype=np.float32)
+    for lvl in range(pc.L, 1, -1):
+        lv = pc.levels[lvl - 1]
+        idx = nodes[lvl - 2]
+        r = np.stack([r * lv.cos[idx], r * lv.sin[idx]], axis=-1).reshape(n, -1).astype(np.float32)
+    lv = pc.levels[0]
+    k = pair >> 2
+    ua = (r * lv.cos[k]).astype(np.float32)
+    ub = (r * lv.sin[k]).astype(np.float32)
+    ua = np.where(pair & 1, -ua, ua)
+    ub = np.where(pair & 2, -ub, ub)
+    return np.stack([ua, ub], axis=-1).reshape(n, pc.d).astype(np.float32)
+
+
+def _residual_stage(codes: PolarCodes, y: np.ndarray, n16: np.ndarray, pc: PolarCodec, sign_stride):
+    """QJL on the polar residual: r = fl32(y - fl32(nbar u^)), rn16, exact signs of S r."""
+    from .quantize import exact_sign_bits
+
+    u32 = unit_directions32(codes.extra["pair"], codes.extra["nodes"], pc)
+    nbar = f16_value(n16).astype(np.float32)
+    resid = (y - (nbar[:, None] * u32).astype(np.float32)).astype(np.float32)
+    rn16 = f16_norm_bits(resid)
+    bits = exact_sign_bits(pc.sketch, resid)
+    codes.sign = pack_bits(bits, 1, sign_stride)
+    codes.norms = (rn16.astype(np.uint32) << 16) | n16.astype(np.uint32)
+    codes.extra.update({"u32": u32, "resid": resid, "sign_bits": bits})
 
 
 def encode(x: np.ndarray, pc: PolarCodec, pre_rotated: bool = False, first: int = 0,
-           stride: Optional[int] = None) -> PolarCodes:
+           stride: Optional[int] = None, sign_stride: Optional[int] = None) -> PolarCodes:
     x32 = np.asarray(x, dtype=np.float32)
     n16 = f16_norm_bits(x32)
     if pre_rotated:
@@ -180,7 +232,7 @@ def encode(x: np.ndarray, pc: PolarCodec, pre_rotated: bool = False, first: int 
         for r in np.unique(rid):
             sel = rid == r
             y[sel] = (x32[sel].astype(np.float64) @ pc.rot[r].astype(np.float64).T).astype(np.float32)
-    return encode_rotated(y, n16, pc, stride)
+    return encode_rotated(y, n16, pc, stride, sign_stride)
 
 
 def decode_fields(codes: PolarCodes, pc: PolarCodec):
@@ -222,11 +274,17 @@ def unit_directions(codes: PolarCodes, pc: PolarCodec) -> np.ndarray:
 
 
 def scores(q: np.ndarray, codes: PolarCodes, pc: PolarCodec, n_keys: int, hkv: int) -> np.ndarray:
-    """Logits [S, hq, n_keys] = nbar <Pi_b q, u^> for queries [S, hq, d] (fp64)."""
+    """Logits [S, hq, n_keys] = nbar <Pi_b q, u^> (+ rnbar sqrt(pi/2)/m <S Pi_b q, 2 b - 1> with the
+    QJL stage) for queries [S, hq, d] (fp64)."""
+    from .estimate import qjl_scale
+
     S, hq, d = q.shape
     G = hq // hkv
     u = unit_directions(codes, pc)
     nbar = f16_value((codes.norms & 0xFFFF).astype(np.uint16))
+    if pc.m > 0:
+        signs = 2.0 * unpack_bits(codes.sign, 1, pc.m).astype(np.float64) - 1.0
+        rnbar = f16_value((codes.norms >> 16).astype(np.uint16))
     out = np.empty((S, hq, n_keys))
     for s_ in range(S):
         for h in range(hkv):
@@ -235,6 +293,29 @@ def scores(q: np.ndarray, codes: PolarCodes, pc: PolarCodec, n_keys: int, hkv: i
             rid = pc.rot_index(1, blk * n_keys)[0]
             qt = q[s_, h * G:(h + 1) * G].astype(np.float64) @ pc.rot[rid].astype(np.float64).T
             out[s_, h * G:(h + 1) * G] = (qt @ u[sl].T) * nbar[sl][None, :]
+            if pc.m > 0:
+                qh = qt @ pc.sketch.astype(np.float64).T
+                out[s_, h * G:(h + 1) * G] += (qh @ signs[sl].T) * (rnbar[sl] * qjl_scale(pc.m))[None, :]
+    return out
+
+
+def dequantize(codes: PolarCodes, pc: PolarCodec, first: int = 0) -> np.ndarray:
+    """Explicit reconstruction in the original space (fp64): Pi^T (nbar u^ + [m > 0]
+    rnbar sqrt(pi/2)/m S^T (2 b - 1))."""
+    from .estimate import qjl_scale
+
+    u = unit_directions(codes, pc)
+    nbar = f16_value((codes.norms & 0xFFFF).astype(np.uint16))
+    rot_space = nbar[:, None] * u
+    if pc.m > 0:
+        signs = 2.0 * unpack_bits(codes.sign, 1, pc.m).astype(np.float64) - 1.0
+        rnbar = f16_value((codes.norms >> 16).astype(np.uint16))
+        rot_space = rot_space + (rnbar * qjl_scale(pc.m))[:, None] * (signs @ pc.sketch.astype(np.float64))
+    rid = pc.rot_index(u.shape[0], first)
+    out = np.empty_like(rot_space)
+    for r in np.unique(rid):
+        sel = rid == r
+        out[sel] = rot_space[sel] @ pc.rot[r].astype(np.float64)
     return out
 
 

@@ -181,3 +181,99 @@ def test_attention_with_zero_scale_is_the_mean_value():
 
     got = polar.attend(np.ones((1, 1, d)), polar.encode(x, pc), vc, pc, vo, n, 1, 0.0)
     assert np.allclose(got[0, 0], oe.dequantize(vc, vo).mean(axis=0), rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------- QJL stage on the residual
+
+
+def _with_sketch(pc, S):
+    import dataclasses
+
+    return dataclasses.replace(pc, m=S.shape[0], sketch=np.asarray(S, np.float32))
+
+
+def test_qjl_on_polar_residual_is_unbiased_where_polar_alone_is_not():
+    """hada.io TurboQuant page, "Etapa 2: eliminação do erro oculto": the 1-bit stage on the
+    polar stage's error removes its bias.  Over many Gaussian sketches the two-stage estimate's
+    mean is the exact <Pi q, y>, within its own sampling error (plus the fp16 rounding of the
+    residual norm and fp32 reconstruction rounding), while the polar stage alone stays off by
+    many of those errors."""
+    d, ab, T = 64, 2, 600
+    base = polar.make_polar_codec(d, ab, 1)
+    g = np.random.default_rng(11)
+    y = g.standard_normal((3, d)).astype(np.float32)
+    q = g.standard_normal(d)
+    y64 = y.astype(np.float64)
+    exact = y64 @ q
+    est = np.empty((T, 3))
+    rel_rn = None
+    for t in range(T):
+        S = np.random.default_rng(1000 + t).standard_normal((d, d)).astype(np.float32)
+        pc = _with_sketch(base, S)
+        c = polar.encode(y, pc, pre_rotated=True)
+        # scores in the rotated space: the rotation applied to q is the identity here
+        pc_id = _with_sketch(polar.PolarCodec(d, ab, np.eye(d, dtype=np.float32)[None], base.levels), S)
+        est[t] = polar.scores(q[None, None, :], c, pc_id, 3, 1)[0, 0]
+        if rel_rn is None:
+            r = c.extra["resid"].astype(np.float64)
+            rn = quantize.f16_value((c.norms >> 16).astype(np.uint16))
+            rel_rn = np.abs(rn / np.linalg.norm(r, axis=1) - 1.0) * np.abs(r @ q)
+            polar_only = polar.scores(q[None, None, :], polar.PolarCodes(c.bits, c.norms & 0xFFFF), 
+                                      polar.PolarCodec(d, ab, np.eye(d, dtype=np.float32)[None], base.levels),
+                                      3, 1)[0, 0]
+    mean, se = est.mean(axis=0), est.std(axis=0, ddof=1) / np.sqrt(T)
+    assert np.all(np.abs(mean - exact) <= 4.0 * se + rel_rn + 1e-5 * np.abs(exact).max())
+    # the polar stage alone: biased by far more than the two-stage estimate's sampling error
+    assert np.max(np.abs(polar_only - exact) / se) > 10.0
+
+
+def test_qjl_residual_is_the_stage_one_error_and_matches_explicit_dequantisation():
+    d, ab, m = 128, 3, 128
+    pc = polar.make_polar_codec(d, ab, 1, m=m, sketch_seed=2)
+    g = np.random.default_rng(4)
+    x = (g.standard_normal((40, d)) * np.where(g.random(d) < 0.05, 8.0, 1.0)).astype(np.float32)
+    c = polar.encode(x, pc)
+    y = c.extra["y"].astype(np.float64)
+    nbar = quantize.f16_value((c.norms & 0xFFFF).astype(np.uint16))
+    u32 = c.extra["u32"].astype(np.float64)
+    rec = (nbar[:, None] * u32).astype(np.float32).astype(np.float64)
+    r = c.extra["resid"].astype(np.float64)
+    # r = fl32(y - fl32(nbar u^)): the residual is the stage-1 error up to one fp32 rounding
+    assert np.all(np.abs(y - rec - r) <= 2.0 ** -24 * np.abs(y - rec))
+    # the fp32 reconstruction is the fp64 one of the same record within the product chain's rounding
+    u64 = polar.unit_directions(c, pc)
+    assert np.max(np.abs(u32 - u64)) <= (pc.L + 1) * 2.0 ** -24
+    # the residual norm word: fp16 of the exact norm; the signs: exact signs of S r
+    assert np.array_equal(c.norms >> 16, quantize.f16_norm_bits(c.extra["resid"]).astype(np.uint32))
+    want_bits = (r @ pc.sketch.astype(np.float64).T >= 0).astype(np.uint32)
+    got_bits = quantize.unpack_bits(c.sign, 1, m)
+    z = r @ pc.sketch.astype(np.float64).T
+    clear = np.abs(z) > 1e-9 * (np.abs(r) @ np.abs(pc.sketch.astype(np.float64)).T)
+    assert np.array_equal(got_bits[clear], want_bits[clear])
+    # scores equal the inner products with the explicitly dequantised keys
+    q = g.standard_normal((1, 2, d))
+    sc = polar.scores(q, c, pc, 40, 1)[0]
+    xt = polar.dequantize(c, pc)
+    assert np.max(np.abs(sc - q[0] @ xt.T)) <= 1e-12 * np.max(np.abs(sc))
+
+
+def test_qjl_on_polar_zero_residual():
+    """A vector that is exactly its own stage-1 reconstruction: residual 0, every sign bit 1
+    (a zero dot product counts as +), rn16 = 0, and the QJL term vanishes."""
+    d, ab, m = 64, 2, 64
+    pc = polar.make_polar_codec(d, ab, 1, m=m, sketch_seed=5)
+    g = np.random.default_rng(9)
+    c0 = polar.encode(g.standard_normal((8, d)).astype(np.float32), pc, pre_rotated=True)
+    nbar = quantize.f16_value((c0.norms & 0xFFFF).astype(np.uint16)).astype(np.float32)
+    y = (nbar[:, None] * c0.extra["u32"]).astype(np.float32)  # on the grid
+    c = polar.encode(y, pc, pre_rotated=True)
+    same = np.all(c.bits == c0.bits, axis=1) & ((c.norms & 0xFFFF) == (c0.norms & 0xFFFF))
+    assert same.sum() >= 6  # re-encoding a grid point gives back its record (norm rounding aside)
+    assert np.all(c.extra["resid"][same] == 0.0)
+    assert np.all((c.norms[same] >> 16) == 0)
+    assert np.all(quantize.unpack_bits(c.sign[same], 1, m) == 1)
+    q = g.standard_normal((1, 1, d))
+    plain = polar.PolarCodec(d, ab, pc.rot, pc.levels)
+    a = polar.scores(q, c, pc, 8, 1)[0, 0]
+    b = polar.scores(q, polar.PolarCodes(c.bits, c.norms & 0xFFFF), plain, 8, 1)[0, 0]
+    assert np.array_equal(a[same], b[same])
