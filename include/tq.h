@@ -235,8 +235,14 @@ int tq_search_topk(const tq_codec *c, const float *queries, int64_t n_q, tq_code
  * coordinates at level l: density proportional to sin^(k-1) psi cos^(k-1) psi), so each level
  * has a fixed Lloyd-Max table and no vector carries a scale besides its radius fp16(||x||).
  * Decode: u^ from the root (value 1) down, child a = parent cos psi^, child b = parent sin psi^;
- * a level-1 pair gives (sign_a r cos psi^, sign_b r sin psi^); x^ = ||x|| Pi^T u^.  No
- * residual stage.
+ * a level-1 pair gives (sign_a r cos psi^, sign_b r sin psi^); x^ = ||x|| Pi^T u^.
+ *
+ * With a sketch (m > 0) the codec is the pages' two-stage composition with this polar stage
+ * first (hada.io page, "Estrutura de compressão em 2 etapas" and "Etapa 2: eliminação do erro
+ * oculto"): the QJL stage of tq_encode on the polar stage's residual in the rotated space,
+ * r_i = fl32(y_i - fl32(nbar u^_i)) with u^ computed in fp32 from the root down (one rounding
+ * per product, in the order above), rn16 = fp16(||r||) exactly rounded, and the exact sign bits
+ * of S r; scores add rnbar sqrt(pi/2)/m <S Pi q, 2 bits - 1> as in tq_scores.
  *
  * Tables [L][4][2^ab] fp32, level l = 1..L at (l-1) * 4 * 2^ab:
  *   [0, n)    cos psi^_j      [n, 2n)   sin psi^_j      (psi^_j ascending, n = 2^ab)
@@ -249,6 +255,8 @@ typedef struct {
   int64_t vecs_per_rot; /* as tq_codec.vecs_per_rot */
   const float *rot;     /* [n_rot][d][d] fp32, 16-byte aligned */
   const float *tables;  /* [L][4][2^ab] fp32 as above */
+  int32_t m;            /* 0: polar stage only; d: QJL stage on the residual (d = 64, 128) */
+  const float *sketch;  /* [m][d] fp32 Gaussian S, 16-byte aligned (NULL when m == 0) */
 } tq_polar_codec;
 
 /* Compressed vectors of the polar stage.
@@ -257,12 +265,17 @@ typedef struct {
  *          bits)], then the node indices of levels 2, 3, ..., L in order, ab bits each; pad
  *          bits and bytes zero.  stride >= tq_polar_record_bytes(d, ab), a multiple of 16 when
  *          that size is a multiple of 16 (else of 8, else of 4); 16-byte aligned base.
- *   norms  [n] uint32: fp16 ||x|| (round to nearest even of the exact norm) in the low half, 0
- *          in the high half.                                                                 */
+ *   norms  [n] uint32: fp16 ||x|| (round to nearest even of the exact norm) in the low half; the
+ *          high half 0, or with m > 0 fp16 ||r|| (round to nearest even of the exact norm).
+ *   sign   [n][sign_stride] bytes with m > 0: bit j = [ (S r)_j >= 0 ], LSB first, pad bytes
+ *          zero; sign_stride >= m/8, a multiple of 16 (m = 128) or 8 (m = 64); 16-byte aligned.
+ *          NULL when m == 0.                                                                   */
 typedef struct {
   uint8_t *bits;
   int64_t stride;
   uint32_t *norms;
+  uint8_t *sign;
+  int64_t sign_stride;
 } tq_polar_codes;
 
 /* Per-level angle tables (layout above) for d = 2^L (4 <= d <= 1024) and ab angle bits
@@ -276,7 +289,8 @@ int tq_make_polar_tables(int32_t d, int32_t ab, float *host_tables);
  * d or ab out of range.                                                                      */
 size_t tq_polar_record_bytes(int32_t d, int32_t ab);
 
-/* Encode n vectors with the recursive polar stage.
+/* Encode n vectors with the recursive polar stage (and, with m > 0, the QJL stage on its
+ * residual).
  *   x, dt, ld_x, flags, first, y_tap as tq_encode (TQ_ENC_PRE_ROTATED: x holds y as fp32).
  * Per vector: n16 = fp16(||x||).  Level 1: A = fl32(y_2j^2), B = fl32(y_2j+1^2); level l > 1: A,
  * B the children's fl32(A + B).  A node's index is #{ j : fl32(B cos^2 tau_j) >= fl32(A sin^2

@@ -43,9 +43,10 @@ def _tables(pc):
     return t
 
 
-def _codecs(d, ab, rot_seed=1, basis=None, vpr=0):
-    ora = op.make_polar_codec(d, ab, rot_seed, basis_seeds=basis, vecs_per_rot=vpr)
-    lib = tq.polar_codec_from_arrays(d, ab, ora.rot, _tables(ora), vecs_per_rot=vpr)
+def _codecs(d, ab, rot_seed=1, basis=None, vpr=0, m=0, sketch_seed=5):
+    ora = op.make_polar_codec(d, ab, rot_seed, basis_seeds=basis, vecs_per_rot=vpr, m=m,
+                              sketch_seed=sketch_seed if m else None)
+    lib = tq.polar_codec_from_arrays(d, ab, ora.rot, _tables(ora), vecs_per_rot=vpr, sketch=ora.sketch)
     return lib, ora
 
 
@@ -71,8 +72,9 @@ def _gpu_encode(lib, x_np, pre, dtype=None, first=0, tap=False, stride=None):
     out = tq.alloc_polar_codes(lib, x.shape[0], stride=stride)
     tq.polar_encode(lib, x, pre_rotated=pre, first=first, out=out, y_tap=ytap)
     torch.cuda.synchronize()
-    bits, norms = out.numpy()
-    return bits, norms, (None if ytap is None else ytap.cpu().numpy())
+    got = out.numpy()
+    res = (got[0], got[1], None if ytap is None else ytap.cpu().numpy())
+    return res if lib.m == 0 else res + (got[2],)
 
 
 @pytest.mark.parametrize("d,ab", [(64, 2), (64, 3), (128, 2), (128, 3), (128, 4), (256, 2), (256, 4)])
@@ -113,7 +115,7 @@ def _near_nodes(A, B, dA, dB, lv):
     return np.any(margin <= 2.0 * slack + 1e-300, axis=-1)
 
 
-def _check_full(x_seen, lib, ora, gpu, first=0, max_rows=0.02):
+def _check_full(x_seen, lib, ora, gpu, first=0, max_rows=0.02, low_norms_only=False):
     """Full-mode records against the oracle's own encoding (its fp64 rotation rounded to fp32):
     the rotation within ROT_BOUND of the exact one (through the y tap, where the call wrote one),
     the norm words exact, and every other difference explained by that bound: a sign only where
@@ -133,7 +135,7 @@ def _check_full(x_seen, lib, ora, gpu, first=0, max_rows=0.02):
     if ytap is not None:
         assert np.all(np.abs(ytap.astype(np.float64) - y_ex) <= bound)
     want = op.encode(x_seen, ora, first=first, stride=lib.stride)
-    assert np.array_equal(norms, want.norms)
+    assert np.array_equal(norms, want.norms & 0xFFFF if low_norms_only else want.norms)
     y_o = want.extra["y"].astype(np.float64)
     dy = bound + np.abs(y_o - y_ex)  # |y_gpu - y_oracle|
     gp, gn = op.decode_fields(op.PolarCodes(bits, norms), ora)
@@ -406,3 +408,186 @@ def test_attention_with_polar_keys_argument_errors():
     rc = tq.lib.tq_polar_attend_decode(tq.ctypes.byref(cc), tq.ctypes.byref(vc), tq._ptr(q), 1, 2, 2, 4, k.c(),
                                        tq.alloc_codes(vl64, 8).c(), 1.0, tq._ptr(q), None, 0, tq._stream())
     assert rc == -4
+
+
+# ------------------------------------------------------------------ the QJL stage on the polar residual
+
+
+def _qjl_score_tol(lib, ora, q, norms, n_keys, hkv):
+    """Bound on the QJL term's error, per logit: the sketched query S q~ in fp32 is off by at most
+    2^-24 (d + 1) sum_k |S_jk| (|q~_k| + sum_i |Pi_ki| |q_i|) per row (its own fp32 sum plus the
+    rotated query's), each byte table entry sums 8 of them and each logit 16 entries (24 more
+    roundings of sum_j |S q~|_j), and the fma with rnbar sqrt(pi/2)/m rounds once more."""
+    n_seq, hq, d = q.shape
+    G = hq // hkv
+    S = np.abs(ora.sketch.astype(np.float64))
+    tol = np.empty((n_seq, hq, n_keys))
+    rq = oq.f16_value((norms >> 16).astype(np.uint16)) * np.sqrt(np.pi / 2) / ora.m
+    for s_ in range(n_seq):
+        for h in range(hkv):
+            blk = s_ * hkv + h
+            P = ora.rot[ora.rot_index(1, blk * n_keys)[0]].astype(np.float64)
+            qq = q[s_, h * G:(h + 1) * G].astype(np.float64)
+            qt = qq @ P.T
+            base = (np.abs(qt) + np.abs(qq) @ np.abs(P).T) @ S.T  # [G, m]
+            e = 2.0 ** -24 * ((d + 1) * base.sum(-1) + 26 * np.abs(qt @ ora.sketch.astype(np.float64).T).sum(-1))
+            tol[s_, h * G:(h + 1) * G] = e[:, None] * rq[blk * n_keys:(blk + 1) * n_keys][None, :]
+    return tol
+
+
+def _qjl_score_case(lib, ora, q, codes, n_keys, hkv):
+    n_seq, hq, d = q.shape
+    k = tq.PolarCodes(torch.from_numpy(np.ascontiguousarray(codes.bits)).cuda(),
+                      torch.from_numpy(np.ascontiguousarray(codes.norms).view(np.int32)).cuda(),
+                      torch.from_numpy(np.ascontiguousarray(codes.sign)).cuda())
+    got = tq.polar_scores(lib, torch.from_numpy(q).cuda(), k, n_keys, hkv).cpu().numpy()
+    want = op.scores(q, codes, ora, n_keys, hkv)
+    nbar = oq.f16_value((codes.norms & 0xFFFF).astype(np.uint16)).reshape(n_seq, hkv, 1, n_keys)
+    qn = np.linalg.norm(q.astype(np.float64), axis=-1).reshape(n_seq, hkv, hq // hkv, 1)
+    tol = (score_tol(d) * nbar * qn).reshape(n_seq, hq, n_keys)
+    tol = tol + _qjl_score_tol(lib, ora, q, codes.norms, n_keys, hkv) + 2.0 ** -24 * np.abs(want) + 1e-30
+    err = np.abs(got.astype(np.float64) - want)
+    assert np.all(err <= tol), float(np.max(err / tol))
+    return float(np.max(err / tol))
+
+
+@pytest.mark.parametrize("d,ab", [(64, 2), (64, 4), (128, 2), (128, 3)])
+def test_qjl_pre_rotated_bit_exact(d, ab):
+    # from identical rotated inputs the whole record is bit-identical: the polar fields, fp16 ||x||,
+    # the fp32 reconstruction from the root down and its residual, fp16 ||r|| and the exact signs
+    say("polar+qjl encode pre-rotated", d, ab)
+    lib, ora = _codecs(d, ab, m=d)
+    y = np.concatenate([_edge_rows(d), synth.pre_rotated(1027, d, seed=d * 10 + ab + 1)])
+    y[100:200] *= np.float32(1e-3)
+    y[200:300] *= np.float32(300.0)
+    bits, norms, _, sign = _gpu_encode(lib, y, pre=True)
+    want = op.encode(y, ora, pre_rotated=True, stride=lib.stride, sign_stride=lib.sign_stride)
+    assert np.array_equal(bits, want.bits)
+    assert np.array_equal(norms, want.norms)
+    assert np.array_equal(sign, want.sign)
+    assert norms[0] == 0 and np.all(sign[0] == 0xFF)  # zero vector: zero residual, (S 0)_j = 0 >= 0
+    assert np.any(norms[8:] >> 16)
+
+
+def test_qjl_pre_rotated_padded_sign_stride():
+    d, ab = 64, 3
+    lib, ora = _codecs(d, ab, m=d)
+    y = synth.pre_rotated(300, d, seed=8)
+    out = tq.alloc_polar_codes(lib, y.shape[0])
+    out.sign = torch.full((y.shape[0], lib.sign_stride + 16), 0xAB, dtype=torch.uint8, device="cuda")
+    tq.polar_encode(lib, torch.from_numpy(y).cuda(), pre_rotated=True, out=out)
+    bits, norms, sign = out.numpy()
+    want = op.encode(y, ora, pre_rotated=True, stride=lib.stride, sign_stride=lib.sign_stride)
+    assert np.array_equal(bits, want.bits) and np.array_equal(norms, want.norms)
+    assert np.array_equal(sign[:, :lib.sign_stride], want.sign)
+    assert not sign[:, lib.sign_stride:].any()  # the whole row is written, pad bytes zero
+
+
+@pytest.mark.parametrize("d,ab,dtype", [(64, 3, "float32"), (128, 2, "bfloat16"), (128, 3, "float16")])
+def test_qjl_full_mode_explained(d, ab, dtype):
+    # full mode: the rotation is the FMA kernel's (the MFMA encoder has no residual stage); the
+    # polar fields as _check_full, and on rows whose fields agree the residual differs from the
+    # oracle's by at most dr = dy (1 + 2^-23) + 2^-22 |r|, which bounds fp16 ||r|| and any sign flip
+    say("polar+qjl encode full", d, ab, dtype)
+    lib, ora = _codecs(d, ab, m=d)
+    g = np.random.default_rng(d + ab + 7)
+    x = (g.standard_normal((1201, d)) * np.where(g.random(d) < 0.05, 10.0, 1.0)).astype(np.float32)
+    tdt = getattr(torch, dtype)
+    x_seen = torch.from_numpy(x).to(tdt).to(torch.float32).numpy()
+    bits, norms, ytap, sign = _gpu_encode(lib, x, pre=False, dtype=tdt, tap=True)
+    _check_full(x_seen, lib, ora, (bits, norms & 0xFFFF, ytap), low_norms_only=True)
+    want = op.encode(x_seen, ora, stride=lib.stride, sign_stride=lib.sign_stride)
+    same = np.all(bits == want.bits, axis=1)
+    # the device's y (the tap) against the oracle's
+    dy = np.abs(ytap.astype(np.float64) - want.extra["y"].astype(np.float64))
+    r_o = want.extra["resid"].astype(np.float64)
+    dr = dy * (1.0 + 2.0 ** -23) + 2.0 ** -22 * np.abs(r_o) + 1e-45
+    rn_gpu = oq.f16_value((norms >> 16).astype(np.uint16))
+    half_ulp = np.abs(np.spacing(np.linalg.norm(r_o, axis=1).astype(np.float16)).astype(np.float64)) / 2
+    slack = np.linalg.norm(dr, axis=1) + half_ulp
+    assert np.all(np.abs(rn_gpu - np.linalg.norm(r_o, axis=1))[same] <= slack[same])
+    Sk = ora.sketch.astype(np.float64)
+    z = r_o @ Sk.T
+    zb = dr @ np.abs(Sk).T
+    gb = np.unpackbits(sign, axis=1, bitorder="little")[:, :d].astype(bool)
+    wb = want.extra["sign_bits"].astype(bool)
+    flip = (gb != wb) & same[:, None]
+    assert not (flip & (np.abs(z) > zb)).any()
+    assert np.mean(same) >= 0.98
+
+
+@pytest.mark.parametrize("d,ab,n_seq,hq,hkv,n_keys", [
+    (128, 2, 2, 8, 2, 700),   # 4 heads per kv head: two heads per table (the table limit)
+    (128, 3, 1, 3, 3, 333),   # one head per table
+    (64, 2, 1, 16, 2, 300),   # eight heads per kv head: four per table
+    (64, 4, 2, 6, 3, 257),    # two
+    (128, 2, 1, 4, 1, 1),     # a single key
+])
+def test_qjl_scores_match_oracle(d, ab, n_seq, hq, hkv, n_keys):
+    say("polar+qjl scores", d, ab, n_seq, hq, hkv, n_keys)
+    lib, ora = _codecs(d, ab, m=d)
+    g = np.random.default_rng(d * ab + n_keys + 1)
+    x = (g.standard_normal((n_seq * hkv * n_keys, d)) * np.where(g.random(d) < 0.05, 10.0, 1.0)).astype(np.float32)
+    enc = op.encode(x, ora, stride=lib.stride, sign_stride=lib.sign_stride)
+    q = g.standard_normal((n_seq, hq, d)).astype(np.float32)
+    say("  max err / tol", _qjl_score_case(lib, ora, q, enc, n_keys, hkv))
+
+
+def test_qjl_scores_random_records_and_rotations():
+    # uniform bits reach every polar field value and every sign byte of every position;
+    # per-block rotations
+    d, ab, n_seq, hq, hkv, n_keys = 64, 3, 2, 4, 2, 400
+    lib, ora = _codecs(d, ab, basis=[900 + i for i in range(n_seq * hkv)], vpr=n_keys, m=d)
+    rec, norms = _random_records(n_seq * hkv * n_keys, d, ab, lib.stride, seed=77)
+    g = np.random.default_rng(78)
+    rn = np.abs(g.standard_normal(norms.shape[0]) * 2.0).astype(np.float16).view(np.uint16).astype(np.uint32)
+    sign = g.integers(0, 256, (norms.shape[0], lib.sign_stride), dtype=np.uint8)
+    codes = op.PolarCodes(rec, norms | (rn << 16), sign=sign)
+    q = g.standard_normal((n_seq, hq, d)).astype(np.float32)
+    _qjl_score_case(lib, ora, q, codes, n_keys, hkv)
+
+
+@pytest.mark.parametrize("d,ab,vbits,vm,n_seq,hq,hkv,n_ctx", [
+    (128, 2, 3, 0, 2, 8, 2, 1000),
+    (64, 3, 3, 64, 1, 6, 3, 515),
+])
+def test_qjl_attention_with_polar_keys(d, ab, vbits, vm, n_seq, hq, hkv, n_ctx):
+    from oracle import codec as oc
+
+    say("polar+qjl attention", d, ab, vbits, vm, n_seq, hq, hkv, n_ctx)
+    lib, ora = _codecs(d, ab, m=d)
+    vl = tq.make_codec(d, vbits, vm, 3, 4)
+    vo = oc.make_codec(d, vbits, vm, 3, 4)
+    g = np.random.default_rng(d + n_ctx + 5)
+    n = n_seq * hkv * n_ctx
+    x = (g.standard_normal((n, d)) * np.where(g.random(d) < 0.05, 10.0, 1.0)).astype(np.float32)
+    kc = op.encode(x, ora, stride=lib.stride, sign_stride=lib.sign_stride)
+    vc = oq.encode(g.standard_normal((n, d)).astype(np.float32), vo, idx_stride=vl.idx_stride,
+                   sign_stride=vl.sign_stride)
+    q = g.standard_normal((n_seq, hq, d)).astype(np.float32)
+    scale = 1.0 / np.sqrt(d)
+    kd = tq.PolarCodes(torch.from_numpy(kc.bits).cuda(), torch.from_numpy(kc.norms.view(np.int32)).cuda(),
+                       torch.from_numpy(kc.sign).cuda())
+    vd = tq.Codes(torch.from_numpy(vc.idx).cuda(), None if vc.sign is None else torch.from_numpy(vc.sign).cuda(),
+                  torch.from_numpy(vc.norms.view(np.int32)).cuda())
+    got = tq.polar_attend_decode(lib, vl, torch.from_numpy(q).cuda(), kd, vd, n_ctx, hkv, scale).cpu().numpy()
+    want = op.attend(q.astype(np.float64), kc, vc, ora, vo, n_ctx, hkv, scale)
+    err = np.max(np.abs(got - want), axis=-1) / np.max(np.abs(want), axis=-1)
+    say("  max rel err", float(err.max()))
+    assert np.all(err <= 1e-3)
+
+
+def test_qjl_codec_errors():
+    lib, _ = _codecs(64, 2, m=64)
+    x = torch.zeros((4, 64), device="cuda")
+    nosign = tq.alloc_polar_codes(lib, 4)
+    nosign.sign = None
+    with pytest.raises(ValueError):  # the binding's check
+        tq.polar_encode(lib, x, out=nosign)
+    cc = lib.c()  # the library's own check: m > 0 needs a sign plane
+    assert tq.lib.tq_polar_encode(tq.ctypes.byref(cc), tq._ptr(x), 0, 4, 64, 0, 0, nosign.c(), None,
+                                  tq._stream()) == -1
+    bad = tq._PolarCodec(64, 2, 1, 0, lib.rot.data_ptr(), lib.tables.data_ptr(), 32, lib.sketch.data_ptr())
+    ok = tq.alloc_polar_codes(lib, 4)
+    assert tq.lib.tq_polar_encode(tq.ctypes.byref(bad), tq._ptr(x), 0, 4, 64, 0, 0, ok.c(), None,
+                                  tq._stream()) == -2  # m other than 0 or d

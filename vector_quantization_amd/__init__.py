@@ -43,11 +43,13 @@ class _Codes(ctypes.Structure):
 
 class _PolarCodec(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("ab", ctypes.c_int32), ("n_rot", ctypes.c_int32),
-                ("vecs_per_rot", ctypes.c_int64), ("rot", ctypes.c_void_p), ("tables", ctypes.c_void_p)]
+                ("vecs_per_rot", ctypes.c_int64), ("rot", ctypes.c_void_p), ("tables", ctypes.c_void_p),
+                ("m", ctypes.c_int32), ("sketch", ctypes.c_void_p)]
 
 
 class _PolarCodes(ctypes.Structure):
-    _fields_ = [("bits", ctypes.c_void_p), ("stride", ctypes.c_int64), ("norms", ctypes.c_void_p)]
+    _fields_ = [("bits", ctypes.c_void_p), ("stride", ctypes.c_int64), ("norms", ctypes.c_void_p),
+                ("sign", ctypes.c_void_p), ("sign_stride", ctypes.c_int64)]
 
 
 def _load():
@@ -255,7 +257,13 @@ def _check_polar_codes(codes, pc, n_min, name="codes"):
     _need(n >= n_min, f"{name} holds {n} records, the call addresses {n_min}")
     out = _check_tensor(codes.bits, f"{name}.bits", dtype=torch.uint8, rows_contiguous=True)
     _need(codes.bits.shape[1] >= pc.stride, f"{name}.bits rows must hold >= {pc.stride} bytes")
-    return out + _check_tensor(codes.norms, f"{name}.norms", dtype=torch.int32, shape=(n,))
+    out += _check_tensor(codes.norms, f"{name}.norms", dtype=torch.int32, shape=(n,))
+    if pc.m > 0:
+        _need(codes.sign is not None, f"{name}.sign is required (m = {pc.m})")
+        out += _check_tensor(codes.sign, f"{name}.sign", dtype=torch.uint8, rows_contiguous=True)
+        _need(codes.sign.shape[0] == n, f"{name}.sign must have {n} rows")
+        _need(codes.sign.shape[1] >= pc.sign_stride, f"{name}.sign rows must hold >= {pc.sign_stride} bytes")
+    return out
 
 
 def _check_queries(q, d, name="q"):
@@ -584,6 +592,8 @@ class PolarCodec:
     rot: object     # torch [n_rot, d, d] fp32 on device
     tables: object  # torch [L, 4, 2^ab] fp32 on device
     vecs_per_rot: int = 0
+    m: int = 0                       # d: the QJL stage on the polar residual
+    sketch: Optional[object] = None  # torch [m, d] fp32 on device when m > 0
 
     @property
     def n_rot(self) -> int:
@@ -591,53 +601,67 @@ class PolarCodec:
 
     def c(self) -> _PolarCodec:
         return _PolarCodec(self.d, self.ab, self.n_rot, self.vecs_per_rot, self.rot.data_ptr(),
-                           self.tables.data_ptr())
+                           self.tables.data_ptr(), self.m,
+                           0 if self.sketch is None else self.sketch.data_ptr())
 
     @property
     def stride(self) -> int:
         return polar_record_bytes(self.d, self.ab)
 
+    @property
+    def sign_stride(self) -> int:
+        return min_stride(self.m)
 
-def polar_codec_from_arrays(d, ab, rot, tables, vecs_per_rot=0, device="cuda") -> PolarCodec:
+
+def polar_codec_from_arrays(d, ab, rot, tables, vecs_per_rot=0, device="cuda", sketch=None) -> PolarCodec:
     torch = _torch()
     rot = np.asarray(rot, np.float32)
     if rot.ndim == 2:
         rot = rot[None]
 
     def dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
 
-    return PolarCodec(d, ab, dev(rot), dev(tables), vecs_per_rot)
+    m = 0 if sketch is None else int(np.asarray(sketch).shape[0])
+    return PolarCodec(d, ab, dev(rot), dev(tables), vecs_per_rot, m, dev(sketch))
 
 
 def make_polar_codec(d: int, ab: int, rot_seed: int, basis_seeds=None, vecs_per_rot: int = 0,
-                     device="cuda") -> PolarCodec:
-    """A polar codec from the library's own host constructors."""
+                     device="cuda", m: int = 0, sketch_seed: int = 0) -> PolarCodec:
+    """A polar codec from the library's own host constructors; m = d adds the QJL stage on the
+    polar residual with the sketch of ``sketch_seed``."""
     rot = make_rotation(rot_seed, d) if basis_seeds is None else make_head_rotations(rot_seed, basis_seeds, d)
-    return polar_codec_from_arrays(d, ab, rot, make_polar_tables(d, ab), vecs_per_rot, device)
+    sk = make_sketch(sketch_seed, m, d) if m > 0 else None
+    return polar_codec_from_arrays(d, ab, rot, make_polar_tables(d, ab), vecs_per_rot, device, sk)
 
 
 @dataclass
 class PolarCodes:
     bits: object   # torch uint8 [n, stride]
     norms: object  # torch int32 [n] (uint32 bit patterns)
+    sign: Optional[object] = None  # torch uint8 [n, sign_stride] with the QJL stage
 
     def c(self) -> _PolarCodes:
-        return _PolarCodes(self.bits.data_ptr(), int(self.bits.shape[1]), self.norms.data_ptr())
+        return _PolarCodes(self.bits.data_ptr(), int(self.bits.shape[1]), self.norms.data_ptr(),
+                           0 if self.sign is None else self.sign.data_ptr(),
+                           0 if self.sign is None else int(self.sign.shape[1]))
 
     @property
     def n(self) -> int:
         return int(self.bits.shape[0])
 
     def numpy(self):
-        return self.bits.cpu().numpy(), self.norms.cpu().numpy().view(np.uint32)
+        """(bits uint8, norms uint32), and sign uint8 as a third item when the codes have one."""
+        out = (self.bits.cpu().numpy(), self.norms.cpu().numpy().view(np.uint32))
+        return out if self.sign is None else out + (self.sign.cpu().numpy(),)
 
 
 def alloc_polar_codes(pc: PolarCodec, n: int, device="cuda", stride: Optional[int] = None) -> PolarCodes:
     torch = _torch()
     bits = torch.empty((n, stride or pc.stride), dtype=torch.uint8, device=device)
     norms = torch.empty((n,), dtype=torch.int32, device=device)
-    return PolarCodes(bits, norms)
+    sign = torch.empty((n, pc.sign_stride), dtype=torch.uint8, device=device) if pc.m > 0 else None
+    return PolarCodes(bits, norms, sign)
 
 
 def polar_encode(pc: PolarCodec, x, pre_rotated: bool = False, first: int = 0, out: Optional[PolarCodes] = None,

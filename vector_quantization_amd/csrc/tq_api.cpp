@@ -204,9 +204,10 @@ namespace {
 
 int check_polar(const tq_polar_codec *pc) {
   if (!pc) return TQ_EINVAL;
-  if (!tq::supported_polar(pc->d, pc->ab)) return TQ_EUNSUPPORTED;
+  if (!tq::supported_polar(pc->d, pc->ab) || !tq::supported_polar_m(pc->d, pc->m)) return TQ_EUNSUPPORTED;
   if (!pc->rot || !pc->tables || pc->n_rot < 1 || pc->vecs_per_rot < 0) return TQ_EINVAL;
-  if (!aligned(pc->rot, 16) || !aligned(pc->tables, 4)) return TQ_EALIGN;
+  if (pc->m > 0 && !pc->sketch) return TQ_EINVAL;
+  if (!aligned(pc->rot, 16) || !aligned(pc->tables, 4) || (pc->sketch && !aligned(pc->sketch, 16))) return TQ_EALIGN;
   return TQ_OK;
 }
 
@@ -215,6 +216,12 @@ int check_polar_codes(const tq_polar_codec *pc, const tq_polar_codes &k) {
   const int64_t words = (tq::polar_record_bits(pc->d, pc->ab) + 31) / 32;
   if (k.stride < 4 * words) return TQ_EINVAL;
   if (k.stride % vec_bytes(words) != 0 || !aligned(k.bits, 16) || !aligned(k.norms, 4)) return TQ_EALIGN;
+  if (pc->m > 0) {
+    const int64_t sw = ((int64_t)pc->m + 31) / 32;
+    if (!k.sign) return TQ_EINVAL;
+    if (k.sign_stride < 4 * sw) return TQ_EINVAL;
+    if (k.sign_stride % vec_bytes(sw) != 0 || !aligned(k.sign, 16)) return TQ_EALIGN;
+  }
   return TQ_OK;
 }
 

@@ -190,6 +190,61 @@ __device__ uint32_t wave_norm_f16(const float (&v)[C], double *terms, double *bu
   return (uint32_t)__shfl((int)hh, 0, kWave);
 }
 
+// The sign words of one vector's QJL stage, by one wavefront: bit j (lane j + 64c's row) is
+// [ sum_k S_jk r_k >= 0 ] of the exact real dot product, for r in LDS (rs[D], fp32).  Lane j
+// sums its rows' fp64 products (each exact) with an error bound; rows whose sum the bound cannot
+// decide are settled one at a time by the exact expansion (terms and buf: LDS scratch of D + 2
+// doubles).  The sign stream (sw words) is written to out, pad bits zero.
+template <int D, int M>
+__device__ void wave_sign_words(const float *sketch, const float *rs, double *terms, double *buf, uint32_t *out,
+                                int sw) {
+  constexpr int CM = (M + kWave - 1) / kWave;
+  const int lane = lane_id();
+  uint64_t masks[CM > 0 ? CM : 1];
+#pragma unroll
+  for (int c = 0; c < CM; ++c) {
+    const int j = lane + kWave * c;
+    double z = 0.0, bound = 0.0;
+    if (j < M) {
+      const float4 *row = reinterpret_cast<const float4 *>(sketch + (int64_t)j * D);
+      for (int k4 = 0; k4 < D / 4; ++k4) {
+        const float4 p = row[k4];
+        const double t0 = (double)p.x * (double)rs[4 * k4 + 0];
+        const double t1 = (double)p.y * (double)rs[4 * k4 + 1];
+        const double t2 = (double)p.z * (double)rs[4 * k4 + 2];
+        const double t3 = (double)p.w * (double)rs[4 * k4 + 3];
+        z += t0; z += t1; z += t2; z += t3;
+        bound += fabs(t0) + fabs(t1) + fabs(t2) + fabs(t3);
+      }
+    }
+    bool bit = z >= 0.0;
+    bool amb = (j < M) && (fabs(z) <= 2.0 * (D + 2) * 0x1p-53 * bound);
+    // rows whose fp64 sum cannot decide the sign: exact expansion, one row at a time
+    uint64_t am = __ballot(amb);
+    while (am) {
+      const int src = __ffsll((unsigned long long)am) - 1;
+      const int j0 = src + kWave * c;
+      for (int k = lane; k < D; k += kWave) terms[k] = (double)sketch[(int64_t)j0 * D + k] * (double)rs[k];
+      wave_lds_fence();
+      int sg = 0;
+      if (lane == 0) sg = expansion_sign(terms, D, buf);
+      wave_lds_fence();
+      sg = __shfl(sg, 0, kWave);
+      if (lane == src) bit = sg >= 0;
+      am &= am - 1;
+    }
+    masks[c] = __ballot((j < M) && bit);
+  }
+  for (int w = lane; w < sw; w += kWave) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int c = 0; c < CM; ++c) {
+      if ((w >> 1) == c) word = (w & 1) ? (uint32_t)(masks[c] >> 32) : (uint32_t)masks[c];
+    }
+    out[w] = word;
+  }
+}
+
 // The W 32-bit words of one record at p, in 16-, 8- or 4-byte loads by W (record strides
 // and base pointers aligned to that width).
 template <int W>

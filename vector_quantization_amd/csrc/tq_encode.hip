@@ -68,7 +68,6 @@ struct EncLds {
 template <int D, int BITS, int M, int TIN, bool PRE>
 __global__ __launch_bounds__(kWave *kEncWaves) void encode_kernel(EncArgs a) {
   constexpr int C = (D + kWave - 1) / kWave;
-  constexpr int CM = (M + kWave - 1) / kWave;
   constexpr int L = 1 << BITS;
   __shared__ EncLds<D> lds_all[kEncWaves];
   __shared__ float cbs[L];
@@ -191,52 +190,9 @@ __global__ __launch_bounds__(kWave *kEncWaves) void encode_kernel(EncArgs a) {
       reinterpret_cast<uint32_t *>(a.idx + rec * a.idx_stride)[w] = word;
     }
 
-    if constexpr (M > 0) {
-      uint64_t masks[CM > 0 ? CM : 1];
-#pragma unroll
-      for (int c = 0; c < CM; ++c) {
-        const int j = lane + kWave * c;
-        double z = 0.0, bound = 0.0;
-        if (j < M) {
-          const float4 *row = reinterpret_cast<const float4 *>(a.sketch + (int64_t)j * D);
-          for (int k4 = 0; k4 < D / 4; ++k4) {
-            const float4 p = row[k4];
-            const double t0 = (double)p.x * (double)s.rs[4 * k4 + 0];
-            const double t1 = (double)p.y * (double)s.rs[4 * k4 + 1];
-            const double t2 = (double)p.z * (double)s.rs[4 * k4 + 2];
-            const double t3 = (double)p.w * (double)s.rs[4 * k4 + 3];
-            z += t0; z += t1; z += t2; z += t3;
-            bound += fabs(t0) + fabs(t1) + fabs(t2) + fabs(t3);
-          }
-        }
-        bool bit = z >= 0.0;
-        bool amb = (j < M) && (fabs(z) <= 2.0 * (D + 2) * 0x1p-53 * bound);
-        // rows whose fp64 sum cannot decide the sign: exact expansion, one row at a time
-        uint64_t am = __ballot(amb);
-        while (am) {
-          const int src = __ffsll((unsigned long long)am) - 1;
-          const int j0 = src + kWave * c;
-          for (int k = lane; k < D; k += kWave)
-            s.terms[k] = (double)a.sketch[(int64_t)j0 * D + k] * (double)s.rs[k];
-          wave_lds_fence();
-          int sg = 0;
-          if (lane == 0) sg = expansion_sign(s.terms, D, s.buf);
-          wave_lds_fence();
-          sg = __shfl(sg, 0, kWave);
-          if (lane == src) bit = sg >= 0;
-          am &= am - 1;
-        }
-        masks[c] = __ballot((j < M) && bit);
-      }
-      for (int w = lane; w < sw; w += kWave) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int c = 0; c < CM; ++c) {
-          if ((w >> 1) == c) word = (w & 1) ? (uint32_t)(masks[c] >> 32) : (uint32_t)masks[c];
-        }
-        reinterpret_cast<uint32_t *>(a.sign + rec * a.sign_stride)[w] = word;
-      }
-    }
+    if constexpr (M > 0)
+      wave_sign_words<D, M>(a.sketch, s.rs, s.terms, s.buf, reinterpret_cast<uint32_t *>(a.sign + rec * a.sign_stride),
+                            sw);
     if (lane == 0) a.norms[rec] = (hi_word(rn16, nbar, a.resid_scale) << 16) | n16;
     wave_lds_fence();
   }

@@ -91,16 +91,22 @@ struct PolarView {
   int d, ab, n_rot;
   int64_t vecs_per_rot;
   const float *rot, *tables;
+  int m;
+  const float *sketch;
 };
 struct PolarCodesView {
   uint8_t *bits;
   int64_t stride;
   uint32_t *norms;
+  uint8_t *sign;
+  int64_t sign_stride;
 };
 inline PolarView view(const tq_polar_codec &c) {
-  return PolarView{c.d, c.ab, c.n_rot, c.vecs_per_rot, c.rot, c.tables};
+  return PolarView{c.d, c.ab, c.n_rot, c.vecs_per_rot, c.rot, c.tables, c.m, c.sketch};
 }
-inline PolarCodesView view(const tq_polar_codes &c) { return PolarCodesView{c.bits, c.stride, c.norms}; }
+inline PolarCodesView view(const tq_polar_codes &c) {
+  return PolarCodesView{c.bits, c.stride, c.norms, c.sign, c.sign_stride};
+}
 // bits of one record: (d/2)(2 + ab) pair fields and (d/2 - 1) ab node fields
 inline int64_t polar_record_bits(int d, int ab) { return (int64_t)(d / 2) * (2 + ab) + (int64_t)(d / 2 - 1) * ab; }
 int polar_angle_levels(int k, int L, std::vector<double> &c);
@@ -112,6 +118,8 @@ int launch_polar_mfma(const PolarView &pc, const void *x, int dt, int64_t n, int
 int launch_polar_scores(const PolarView &pc, const float *q, const ScoreShape &s, const PolarCodesView &k,
                         float *logits, void *stream);
 inline bool supported_polar(int d, int ab) { return (d == 64 || d == 128 || d == 256) && ab >= 2 && ab <= 4; }
+// the QJL stage on the polar residual: m = d at d = 64, 128
+inline bool supported_polar_m(int d, int m) { return m == 0 || (m == d && (d == 64 || d == 128)); }
 
 // A 1-D grid of `blocks` workgroups is within the launch limit (2^31 - 1); launchers return
 // TQ_EUNSUPPORTED for shapes beyond it instead of truncating the count.

@@ -19,7 +19,10 @@
 // pad bits zero.  Norm word: fp16 ||x|| in the low half, 0 in the high half.
 //
 // polar_encode_kernel: one wavefront per vector (rotation as the standard encoder's); the
-// levels are decided in LDS, one node per lane, and lane w packs word w of the record.
+// levels are decided in LDS, one node per lane, and lane w packs word w of the record.  With a
+// sketch (M = D), the QJL stage follows on the residual: the reconstruction u^ is expanded from
+// the root down in LDS (one node per lane, fp32 products), r = fl32(y - fl32(nbar u^)), its exact
+// fp16 norm and the exact signs of S r as in the two-stage encoder.
 // polar_score_kernel: one workgroup per (sequence, kv head, head subgroup, key chunk).  It
 // rotates its G query heads, then tabulates for every pair j and every value f of the pair
 // field the leaf term (+-cos psi^ q_2j +- sin psi^ q_2j+1) of each head, G floats per (j, f).  A
@@ -68,6 +71,9 @@ struct PolarEncArgs {
   int64_t stride;
   uint32_t *norms;
   float *y_tap;
+  const float *sketch;  // [M][D] with the QJL stage
+  uint8_t *sign;
+  int64_t sign_stride;
 };
 
 constexpr int kPolarEncWaves = 4;
@@ -76,8 +82,9 @@ template <int D>
 struct PolarEncLds {
   float xs[D];
   float ys[D];
-  float sum[2][D / 2];
+  float sum[2][D / 2];  // children's sums of squares; then the node values of the reconstruction
   uint32_t field[D];  // pair fields [0, D/2), node fields of levels 2.. from D/2
+  float rs[D];        // the residual of the QJL stage
   double terms[D + 2];
   double buf[D + 2];
 };
@@ -91,12 +98,14 @@ __device__ __forceinline__ uint32_t polar_decide(float A, float B, const float *
   return k;
 }
 
-template <int D, int AB, int TIN, bool PRE>
+template <int D, int AB, int M, int TIN, bool PRE>
 __global__ __launch_bounds__(kWave *kPolarEncWaves) void polar_encode_kernel(PolarEncArgs a) {
   using P = PolarLayout<D, AB>;
   constexpr int C = D / kWave;
+  static_assert(M == 0 || M == D, "the QJL stage takes m = d");
   __shared__ PolarEncLds<D> lds_all[kPolarEncWaves];
   __shared__ float tc2[P::LV][P::NA], ts2[P::LV][P::NA];
+  __shared__ float tco[M > 0 ? P::LV : 1][P::NA], tsi[M > 0 ? P::LV : 1][P::NA];  // cos, sin of the levels
   const int lane = lane_id();
   const int wid = threadIdx.x / kWave;
   PolarEncLds<D> &s = lds_all[wid];
@@ -104,6 +113,10 @@ __global__ __launch_bounds__(kWave *kPolarEncWaves) void polar_encode_kernel(Pol
     const int l = e / P::NA, j = e % P::NA;
     tc2[l][j] = a.tables[(l * 4 + 2) * P::NA + j];
     ts2[l][j] = a.tables[(l * 4 + 3) * P::NA + j];
+    if constexpr (M > 0) {
+      tco[l][j] = a.tables[(l * 4) * P::NA + j];
+      tsi[l][j] = a.tables[(l * 4 + 1) * P::NA + j];
+    }
   }
   __syncthreads();
   const int sw = (int)(a.stride >> 2);
@@ -199,36 +212,87 @@ __global__ __launch_bounds__(kWave *kPolarEncWaves) void polar_encode_kernel(Pol
       }
       reinterpret_cast<uint32_t *>(a.bits + v * a.stride)[w] = word;
     }
-    if (lane == 0) a.norms[v] = n16;
+    uint32_t hi = 0u;
+    if constexpr (M > 0) {
+      // ---- the reconstruction u^ from the root down: node values in s.sum (ping-pong)
+      if (lane == 0) s.sum[0][0] = 1.0f;
+      wave_lds_fence();
+      int cur = 0;
+#pragma unroll
+      for (int l = P::LV; l >= 2; --l) {
+        const int nn = D >> l;  // nodes of level l
+        const int f0 = P::NP + (P::NP - (D >> (l - 1)));  // first field of level l
+        for (int i = lane; i < nn; i += kWave) {
+          const uint32_t k = s.field[f0 + i];
+          const float pv = s.sum[cur][i];
+          s.sum[cur ^ 1][2 * i] = __fmul_rn(pv, tco[l - 1][k]);
+          s.sum[cur ^ 1][2 * i + 1] = __fmul_rn(pv, tsi[l - 1][k]);
+        }
+        cur ^= 1;
+        wave_lds_fence();
+      }
+      // ---- residual r_i = fl32(y_i - fl32(nbar u^_i)) on the lane's coordinates
+      const float nbar = f16_bits_to_float(n16);
+      float r[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int i = lane + kWave * c;
+        const uint32_t f = s.field[i >> 1];
+        const uint32_t k = f >> 2;
+        const float rad = s.sum[cur][i >> 1];
+        float u = (i & 1) ? __fmul_rn(rad, tsi[0][k]) : __fmul_rn(rad, tco[0][k]);
+        if (f & ((i & 1) ? 2u : 1u)) u = -u;
+        r[c] = __fsub_rn(s.ys[i], __fmul_rn(nbar, u));
+        s.rs[i] = r[c];
+      }
+      const uint32_t rn16 = wave_norm_f16<D, C>(r, s.terms, s.buf);
+      wave_lds_fence();
+      wave_sign_words<D, M>(a.sketch, s.rs, s.terms, s.buf, reinterpret_cast<uint32_t *>(a.sign + v * a.sign_stride),
+                            (int)(a.sign_stride >> 2));
+      hi = rn16;
+    }
+    if (lane == 0) a.norms[v] = (hi << 16) | n16;
     wave_lds_fence();
   }
 }
 
-template <int D, int AB, int TIN, bool PRE>
+template <int D, int AB, int M, int TIN, bool PRE>
 static int launch_polar_encode_t(const PolarEncArgs &a, hipStream_t st) {
   const int64_t want = (a.n + kPolarEncWaves - 1) / kPolarEncWaves;
   const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
-  hipLaunchKernelGGL((polar_encode_kernel<D, AB, TIN, PRE>), dim3(blocks), dim3(kWave * kPolarEncWaves), 0, st, a);
+  hipLaunchKernelGGL((polar_encode_kernel<D, AB, M, TIN, PRE>), dim3(blocks), dim3(kWave * kPolarEncWaves), 0, st, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 
+template <int D, int AB, int M>
+static int launch_polar_encode_dam(const PolarEncArgs &a, int dt, bool pre, hipStream_t st) {
+  if (pre) return launch_polar_encode_t<D, AB, M, TQ_F32, true>(a, st);
+  if (dt == TQ_F32) return launch_polar_encode_t<D, AB, M, TQ_F32, false>(a, st);
+  if (dt == TQ_F16) return launch_polar_encode_t<D, AB, M, TQ_F16, false>(a, st);
+  return launch_polar_encode_t<D, AB, M, TQ_BF16, false>(a, st);
+}
+
 template <int D, int AB>
-static int launch_polar_encode_da(const PolarEncArgs &a, int dt, bool pre, hipStream_t st) {
-  if (pre) return launch_polar_encode_t<D, AB, TQ_F32, true>(a, st);
-  if (dt == TQ_F32) return launch_polar_encode_t<D, AB, TQ_F32, false>(a, st);
-  if (dt == TQ_F16) return launch_polar_encode_t<D, AB, TQ_F16, false>(a, st);
-  return launch_polar_encode_t<D, AB, TQ_BF16, false>(a, st);
+static int launch_polar_encode_da(const PolarEncArgs &a, int m, int dt, bool pre, hipStream_t st) {
+  if (m == 0) return launch_polar_encode_dam<D, AB, 0>(a, dt, pre, st);
+  if constexpr (D == 64 || D == 128) {
+    if (m == D) return launch_polar_encode_dam<D, AB, D>(a, dt, pre, st);
+  }
+  return TQ_EUNSUPPORTED;
 }
 
 int launch_polar_encode(const PolarView &pc, const void *x, int dt, int64_t n, int64_t ld_x, bool pre_rotated,
                         int64_t first, const PolarCodesView &out, float *y_tap, void *stream) {
   if (n == 0) return TQ_OK;
-  const int rc = launch_polar_mfma(pc, x, dt, n, ld_x, pre_rotated, first, out, y_tap, stream);
-  if (rc != TQ_EUNSUPPORTED) return rc;
+  if (pc.m == 0) {  // the MFMA encoder has no residual stage
+    const int rc = launch_polar_mfma(pc, x, dt, n, ld_x, pre_rotated, first, out, y_tap, stream);
+    if (rc != TQ_EUNSUPPORTED) return rc;
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   PolarEncArgs a{x, ld_x, n, first, pc.rot, pc.n_rot, pc.vecs_per_rot, pc.tables, out.bits, out.stride,
-                 out.norms, y_tap};
-#define TQ_PE(DD, AA) if (pc.d == DD && pc.ab == AA) return launch_polar_encode_da<DD, AA>(a, dt, pre_rotated, st);
+                 out.norms, y_tap, pc.sketch, out.sign, out.sign_stride};
+#define TQ_PE(DD, AA) \
+  if (pc.d == DD && pc.ab == AA) return launch_polar_encode_da<DD, AA>(a, pc.m, dt, pre_rotated, st);
   TQ_PE(64, 2) TQ_PE(64, 3) TQ_PE(64, 4) TQ_PE(128, 2) TQ_PE(128, 3) TQ_PE(128, 4)
   TQ_PE(256, 2) TQ_PE(256, 3) TQ_PE(256, 4)
 #undef TQ_PE
@@ -247,21 +311,29 @@ struct PolarScoreArgs {
   int64_t stride;
   const uint32_t *norms;
   float *logits;
+  const float *sketch;  // the QJL stage (M > 0): S [M][D], sign planes
+  const uint8_t *sign;
+  int64_t sign_stride;
 };
 
-template <int D, int AB, int G>
+// LDS tables of G heads: the leaf terms, and with the QJL stage the sign-byte tables
+// U_p[beta] = sum_t q^_{8p+t} (2 bit_t(beta) - 1), G floats per entry
+template <int D, int AB, int M, int G>
 constexpr int polar_lut_bytes() {
-  return PolarLayout<D, AB>::NP * PolarLayout<D, AB>::NF * G * 4;
+  return PolarLayout<D, AB>::NP * PolarLayout<D, AB>::NF * G * 4 + (M / 8) * 256 * G * 4;
 }
 
-template <int D, int AB, int G, int NT>
+template <int D, int AB, int M, int G, int NT>
 __global__ __launch_bounds__(NT) void polar_score_kernel(PolarScoreArgs a) {
   using P = PolarLayout<D, AB>;
+  constexpr int NQ = M / 8;
+  constexpr int SW = (M + 31) / 32;
   __shared__ __align__(16) float lut[P::NP * P::NF * G];
+  __shared__ __align__(16) float qlut[M > 0 ? NQ * 256 * G : 4];
   __shared__ float2 cs[P::LV][P::NA];
   __shared__ float qs[G * D];
   __shared__ float qt[G * D];
-  __shared__ float qh_unused[1];
+  __shared__ float qh[G * (M > 0 ? M : 1)];
 
   const int64_t b = blockIdx.x;
   const int chunk = (int)(b % a.n_chunks);
@@ -278,13 +350,25 @@ __global__ __launch_bounds__(NT) void polar_score_kernel(PolarScoreArgs a) {
     rid = (blk * a.n_keys) / a.vecs_per_rot;
     if (rid > a.n_rot - 1) rid = a.n_rot - 1;
   }
-  QueryPrep<D, 0, G, NT> prep;
-  prep.issue(a.q + qrow * D, a.rot + rid * (int64_t)D * D, nullptr);
+  QueryPrep<D, M, G, NT> prep;
+  prep.issue(a.q + qrow * D, a.rot + rid * (int64_t)D * D, a.sketch);
   for (int e = threadIdx.x; e < P::LV * P::NA; e += NT) {
     const int l = e / P::NA, j = e % P::NA;
     cs[l][j] = make_float2(a.tables[l * 4 * P::NA + j], a.tables[(l * 4 + 1) * P::NA + j]);
   }
-  prep.finish(qs, qt, qh_unused);  // ends synchronised
+  prep.finish(qs, qt, qh);  // ends synchronised
+  if constexpr (M > 0) {
+    for (int e = threadIdx.x; e < NQ * 256 * G; e += NT) {
+      const int g = e % G, beta = (e / G) & 255, p = e / (G * 256);
+      float acc = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float y = qh[g * M + 8 * p + t];
+        acc += ((beta >> t) & 1) ? y : -y;
+      }
+      qlut[e] = acc;
+    }
+  }
   // leaf terms: entry (j, f, g) = (+-cos psi^_k) q_2j + (+-sin psi^_k) q_2j+1, f = sa | sb << 1 | k << 2
   for (int e = threadIdx.x; e < P::NP * P::NF * G; e += NT) {
     const int g = e % G, f = (e / G) % P::NF, j = e / (G * P::NF);
@@ -342,12 +426,31 @@ __global__ __launch_bounds__(NT) void polar_score_kernel(PolarScoreArgs a) {
       }
     }
     const float nbar = f16_bits_to_float(nw & 0xFFFFu);
+    if constexpr (M > 0) {
+      // the QJL term: rnbar sqrt(pi/2)/m sum_p U_p[sign byte p]
+      uint32_t sw[SW];
+      load_words<SW>(a.sign + v * a.sign_stride, sw);
+      float aq[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) a.logits[(qrow + h) * a.n_keys + t] = nbar * acc[h];
+      for (int g = 0; g < G; ++g) aq[g] = 0.0f;
+#pragma unroll
+      for (int p = 0; p < NQ; ++p) {
+        const int byte = (sw[p >> 2] >> (8 * (p & 3))) & 0xFF;
+        const float *e = qlut + (p * 256 + byte) * G;
+#pragma unroll
+        for (int g = 0; g < G; ++g) aq[g] += e[g];
+      }
+      const float rq = f16_bits_to_float(nw >> 16) * (1.2533141373155003f / (float)(M > 0 ? M : 1));
+#pragma unroll
+      for (int h = 0; h < G; ++h) a.logits[(qrow + h) * a.n_keys + t] = fmaf(rq, aq[h], nbar * acc[h]);
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) a.logits[(qrow + h) * a.n_keys + t] = nbar * acc[h];
+    }
   }
 }
 
-template <int D, int AB, int G>
+template <int D, int AB, int M, int G>
 static int launch_polar_score_g(const PolarScoreArgs &a0, int64_t n_seq, int hq, int hkv, int64_t n,
                                 hipStream_t st) {
   constexpr int NT = 256;
@@ -358,24 +461,36 @@ static int launch_polar_score_g(const PolarScoreArgs &a0, int64_t n_seq, int hq,
   a.n_chunks = (int)((n + a.chunk - 1) / a.chunk);
   const int64_t blocks = n_seq * hkv * a.nsub * a.n_chunks;
   if (!grid_fits(blocks)) return TQ_EUNSUPPORTED;
-  hipLaunchKernelGGL((polar_score_kernel<D, AB, G, NT>), dim3((unsigned)blocks), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((polar_score_kernel<D, AB, M, G, NT>), dim3((unsigned)blocks), dim3(NT), 0, st, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 
-// query heads per table: the largest of 8, 4, 2, 1 dividing the group whose table fits 64 KiB
-template <int D, int AB>
-static int launch_polar_score_da(const PolarScoreArgs &a, int64_t n_seq, int hq, int hkv, int64_t n,
-                                 hipStream_t st) {
+// query heads per table: the largest of 8, 4, 2, 1 dividing the group whose tables fit 64 KiB
+template <int D, int AB, int M>
+static int launch_polar_score_dam(const PolarScoreArgs &a, int64_t n_seq, int hq, int hkv, int64_t n,
+                                  hipStream_t st) {
   const int g = hq / hkv;
   constexpr int kMax = 64 * 1024;
-  if (g % 8 == 0 && polar_lut_bytes<D, AB, 8>() <= kMax) {
-    if constexpr (polar_lut_bytes<D, AB, 8>() <= kMax) return launch_polar_score_g<D, AB, 8>(a, n_seq, hq, hkv, n, st);
+  if constexpr (polar_lut_bytes<D, AB, M, 8>() <= kMax) {
+    if (g % 8 == 0) return launch_polar_score_g<D, AB, M, 8>(a, n_seq, hq, hkv, n, st);
   }
-  if (g % 4 == 0 && polar_lut_bytes<D, AB, 4>() <= kMax) {
-    if constexpr (polar_lut_bytes<D, AB, 4>() <= kMax) return launch_polar_score_g<D, AB, 4>(a, n_seq, hq, hkv, n, st);
+  if constexpr (polar_lut_bytes<D, AB, M, 4>() <= kMax) {
+    if (g % 4 == 0) return launch_polar_score_g<D, AB, M, 4>(a, n_seq, hq, hkv, n, st);
   }
-  if (g % 2 == 0) return launch_polar_score_g<D, AB, 2>(a, n_seq, hq, hkv, n, st);
-  return launch_polar_score_g<D, AB, 1>(a, n_seq, hq, hkv, n, st);
+  if constexpr (polar_lut_bytes<D, AB, M, 2>() <= kMax) {
+    if (g % 2 == 0) return launch_polar_score_g<D, AB, M, 2>(a, n_seq, hq, hkv, n, st);
+  }
+  return launch_polar_score_g<D, AB, M, 1>(a, n_seq, hq, hkv, n, st);
+}
+
+template <int D, int AB>
+static int launch_polar_score_da(const PolarScoreArgs &a, int m, int64_t n_seq, int hq, int hkv, int64_t n,
+                                 hipStream_t st) {
+  if (m == 0) return launch_polar_score_dam<D, AB, 0>(a, n_seq, hq, hkv, n, st);
+  if constexpr (D == 64 || D == 128) {
+    if (m == D) return launch_polar_score_dam<D, AB, D>(a, n_seq, hq, hkv, n, st);
+  }
+  return TQ_EUNSUPPORTED;
 }
 
 int launch_polar_scores(const PolarView &pc, const float *q, const ScoreShape &s, const PolarCodesView &k,
@@ -383,8 +498,9 @@ int launch_polar_scores(const PolarView &pc, const float *q, const ScoreShape &s
   if (s.n == 0 || s.n_seq == 0) return TQ_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   PolarScoreArgs a{q, pc.rot, pc.tables, pc.n_rot, pc.vecs_per_rot, s.n_seq, s.n, s.hq, s.hkv, 0, 1, 0,
-                   k.bits, k.stride, k.norms, logits};
-#define TQ_PS(DD, AA) if (pc.d == DD && pc.ab == AA) return launch_polar_score_da<DD, AA>(a, s.n_seq, s.hq, s.hkv, s.n, st);
+                   k.bits, k.stride, k.norms, logits, pc.sketch, k.sign, k.sign_stride};
+#define TQ_PS(DD, AA) \
+  if (pc.d == DD && pc.ab == AA) return launch_polar_score_da<DD, AA>(a, pc.m, s.n_seq, s.hq, s.hkv, s.n, st);
   TQ_PS(64, 2) TQ_PS(64, 3) TQ_PS(64, 4) TQ_PS(128, 2) TQ_PS(128, 3) TQ_PS(128, 4)
   TQ_PS(256, 2) TQ_PS(256, 3) TQ_PS(256, 4)
 #undef TQ_PS
