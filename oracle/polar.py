@@ -319,6 +319,48 @@ def dequantize(codes: PolarCodes, pc: PolarCodec, first: int = 0) -> np.ndarray:
     return out
 
 
+def append(x: np.ndarray, pc: PolarCodec, slots, pos, rope_base: float, stride: Optional[int] = None,
+           sign_stride: Optional[int] = None) -> PolarCodes:
+    """Polar codes of new vectors appended to a growing cache, the two-stage append's steps with
+    the polar stage (TurboESM summary, "Metodologia" A: RoPE first, then the orthogonal rotation;
+    7minutos.es walkthrough, "Etapa 1": the codes stay in the cache): row k goes to cache slot
+    slots[k], whose block selects the rotation, at position pos[k]; with rope_base > 0 the
+    rotation sees RoPE(x, pos) in fp64, y = fl32(Pi_b RoPE(x)); the stored radius is fp16(||x||)
+    (RoPE keeps norms)."""
+    from .quantize import rope
+
+    x32 = np.asarray(x, dtype=np.float32)
+    x64 = x32.astype(np.float64)
+    xr = rope(x64, np.asarray(pos), rope_base) if rope_base > 0 else x64
+    rid = np.array([pc.rot_index(1, int(sl))[0] for sl in slots], dtype=np.int64)
+    y = np.empty(x64.shape, dtype=np.float32)
+    for r in np.unique(rid):
+        sel = rid == r
+        y[sel] = (xr[sel] @ pc.rot[r].astype(np.float64).T).astype(np.float32)
+    return encode_rotated(y, f16_norm_bits(x32), pc, stride, sign_stride)
+
+
+def search_scores(queries: np.ndarray, db: PolarCodes, pc: PolarCodec, chunk: int = 65536) -> np.ndarray:
+    """Estimated <q, x_n> [Q, n_db] of every query against every database record (one shared
+    rotation): the logits of scores() with the database as one block of keys."""
+    qs = np.asarray(queries, dtype=np.float64)
+    n = db.norms.shape[0]
+    out = np.empty((qs.shape[0], n))
+    for a in range(0, n, chunk):
+        b = min(n, a + chunk)
+        part = PolarCodes(db.bits[a:b], db.norms[a:b], sign=None if db.sign is None else db.sign[a:b])
+        out[:, a:b] = scores(qs[None], part, pc, b - a, 1)[0]
+    return out
+
+
+def search_topk(queries: np.ndarray, db: PolarCodes, pc: PolarCodec, k: int):
+    """Top-k database records per query by estimated inner product (hada.io TurboQuant page,
+    "Desempenho em busca vetorial"): score descending, then row ascending."""
+    from .estimate import topk_rows
+
+    return topk_rows(search_scores(queries, db, pc), k)
+
+
 def exact_polar(y: np.ndarray):
     """The unquantised transform of y (fp64): (radius, level-1 signs and angles, node angles)."""
     y = np.asarray(y, dtype=np.float64)

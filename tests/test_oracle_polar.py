@@ -277,3 +277,107 @@ def test_qjl_on_polar_zero_residual():
     a = polar.scores(q, c, pc, 8, 1)[0, 0]
     b = polar.scores(q, polar.PolarCodes(c.bits, c.norms & 0xFFFF), plain, 8, 1)[0, 0]
     assert np.array_equal(a[same], b[same])
+
+
+# ------------------------------------------------------------------ append into a growing cache
+
+
+@pytest.mark.parametrize("m", [0, 32])
+def test_polar_append_reduces_to_encode(m):
+    # no RoPE, or RoPE at position 0 (the identity): append is the encoder with the slots' rotations
+    pc = polar.make_polar_codec(32, 3, 4, m=m, sketch_seed=6 if m else None)
+    x = np.random.default_rng(1).standard_normal((40, 32)).astype(np.float32)
+    want = polar.encode(x, pc)
+    for base, pos in ((0.0, np.arange(40) * 7), (10000.0, np.zeros(40, np.int64))):
+        got = polar.append(x, pc, np.arange(40), pos, base)
+        assert np.array_equal(got.bits, want.bits) and np.array_equal(got.norms, want.norms)
+        if m:
+            assert np.array_equal(got.sign, want.sign)
+
+
+def test_polar_append_slot_selects_the_rotation_block():
+    # per-block rotations: a row appended at slot t is the encoder's record of that row at offset t
+    pc = polar.make_polar_codec(32, 2, 4, basis_seeds=[10, 11, 12], vecs_per_rot=8)
+    x = np.random.default_rng(2).standard_normal((6, 32)).astype(np.float32)
+    slots = np.array([0, 7, 8, 15, 16, 40])  # blocks 0, 0, 1, 1, 2, 2 (past the last block: the last)
+    got = polar.append(x, pc, slots, np.zeros(6, np.int64), 0.0)
+    for i, t in enumerate(slots):
+        one = polar.encode(x[i:i + 1], pc, first=int(t))
+        assert np.array_equal(got.bits[i], one.bits[0])
+    # and the rotation matters: block 0's record of the row at slot 40 differs
+    assert not np.array_equal(got.bits[5], polar.encode(x[5:6], pc).bits[0])
+
+
+def test_polar_append_keeps_the_norm_and_encodes_the_turned_vector():
+    # RoPE keeps the norm, so the radius is fp16(||x||); the record is the direction of RoPE(x, p):
+    # its reconstruction is as close to RoPE(x, p) as an encoding of RoPE(x, p) itself is, and far
+    # from x (the turn is large at these positions)
+    d, base = 64, 10000.0
+    pc = polar.make_polar_codec(d, 4, 4)
+    g = np.random.default_rng(3)
+    x = g.standard_normal((400, d)).astype(np.float32)
+    pos = g.integers(50, 5000, 400)
+    got = polar.append(x, pc, np.arange(400), pos, base)
+    assert np.array_equal(got.norms, quantize.f16_norm_bits(x))
+    xr = quantize.rope(x, pos, base)
+    rec = polar.dequantize(got, pc)
+    direct = polar.dequantize(polar.encode(xr.astype(np.float32), pc), pc)
+
+    def rel(a, b):
+        return float(np.mean(np.sum((a - b) ** 2, 1) / np.sum(b * b, 1)))
+
+    assert rel(rec, xr) < 1.1 * rel(direct, xr) + 1e-6
+    assert rel(rec, xr) < 0.01
+    assert rel(rec, x.astype(np.float64)) > 0.5
+
+
+# ------------------------------------------------------------------ search
+
+
+@pytest.mark.parametrize("m", [0, 64])
+def test_polar_search_ranks_the_explicit_reconstructions(m):
+    # the estimated score is the inner product with the dequantised record (the polar stage's
+    # reconstruction plus the QJL term), so the top-k by score is the top-k of q . x^ computed
+    # from the explicit reconstruction
+    d = 64
+    pc = polar.make_polar_codec(d, 3, 7, m=m, sketch_seed=8 if m else None)
+    g = np.random.default_rng(4)
+    db = polar.encode(g.standard_normal((3000, d)).astype(np.float32), pc)
+    q = g.standard_normal((7, d))
+    idx, sc = polar.search_topk(q, db, pc, 10)
+    xhat = polar.dequantize(db, pc)
+    ip = q @ xhat.T
+    for i in range(7):
+        order = np.argsort(-ip[i], kind="stable")[:10]
+        assert np.array_equal(idx[i], order)
+        assert np.allclose(sc[i], ip[i][order], rtol=1e-10, atol=1e-10)
+
+
+def test_polar_search_ties_take_the_smaller_row_and_k_n_is_a_sorted_permutation():
+    d = 32
+    pc = polar.make_polar_codec(d, 2, 9)
+    x = np.random.default_rng(5).standard_normal((50, d)).astype(np.float32)
+    x[30] = x[3]  # identical records score identically
+    x[41] = x[3]
+    db = polar.encode(x, pc)
+    q = x[3:4].astype(np.float64)
+    idx, sc = polar.search_topk(q, db, pc, 3)
+    assert list(idx[0]) == [3, 30, 41] and sc[0, 0] == sc[0, 1] == sc[0, 2]
+    idx, sc = polar.search_topk(np.random.default_rng(6).standard_normal((2, d)), db, pc, 50)
+    for i in range(2):
+        assert sorted(idx[i]) == list(range(50))
+        assert np.all(np.diff(sc[i]) <= 0)
+
+
+def test_polar_search_recall_against_exact_top_k():
+    # the codec serves search: with 4 angle bits most of the exact top 10 is found in the top 10
+    from oracle import estimate
+
+    d = 64
+    pc = polar.make_polar_codec(d, 4, 11)
+    g = np.random.default_rng(7)
+    x = g.standard_normal((4000, d)).astype(np.float32)
+    q = g.standard_normal((20, d))
+    found, _ = polar.search_topk(q, polar.encode(x, pc), pc, 10)
+    truth, _ = estimate.exact_topk(q, x, 10)
+    assert estimate.recall_at_k(found, truth) > 0.8
