@@ -299,7 +299,32 @@ size_t tq_polar_record_bytes(int32_t d, int32_t ab);
 int tq_polar_encode(const tq_polar_codec *pc, const void *x, tq_dtype dt, int64_t n, int64_t ld_x,
                     uint32_t flags, int64_t first, tq_polar_codes out, float *y_tap, void *stream);
 
-/* Logits of every (query head, key) pair: nbar <Pi q, u^> (the query stays in fp32).
+/* Append one new vector per (sequence, kv head) to a growing cache of polar records laid out
+ * [n_seq][hkv][cap]: the steps of tq_append with the polar stage (TurboESM summary,
+ * "Metodologia" A: RoPE first, then the orthogonal rotation; walkthrough "Etapa 1": the codes
+ * stay in the cache).  x_new [n_seq][hkv][d] device rows of type dt (contiguous); pos [n_seq]
+ * int32 device, the position and slot of sequence s's token (row (s, h) goes to record
+ * (s hkv + h) cap + pos[s], whose block selects the rotation; positions outside [0, cap) are
+ * skipped); rope_base > 0 turns x by RoPE at pos[s] in fp64 before the rotation (as tq_append),
+ * 0 for none.  The stored radius is fp16(||x||).  With m > 0 the QJL stage follows as in
+ * tq_polar_encode.  Writes only the appended records.                                       */
+int tq_polar_append(const tq_polar_codec *pc, const void *x_new, tq_dtype dt, int64_t n_seq, int32_t hkv,
+                    const int32_t *pos, int64_t cap, float rope_base, tq_polar_codes cache, void *stream);
+
+/* Inner-product top-k search over a database of polar records (hada.io TurboQuant page,
+ * "Desempenho em busca vetorial"): per query the k records with the largest estimate of
+ * tq_polar_scores (ties: smaller row first).  One shared rotation (n_rot = 1).
+ *   queries [n_q][d] fp32; db [n_db] records; out_idx [n_q][k] int64; out_score [n_q][k] fp32;
+ *   1 <= k <= min(32, n_db), n_db < 2^31 - 1.
+ *   ws  workspace of tq_polar_search_workspace_bytes bytes (may be 0: then ws may be NULL),
+ *       256-byte aligned: the per-slice lists when the database is split.                   */
+size_t tq_polar_search_workspace_bytes(const tq_polar_codec *pc, int64_t n_q, int32_t k, int64_t n_db);
+int tq_polar_search_topk(const tq_polar_codec *pc, const float *queries, int64_t n_q, tq_polar_codes db,
+                         int64_t n_db, int32_t k, int64_t *out_idx, float *out_score, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* Logits of every (query head, key) pair: nbar <Pi q, u^> (the query stays in fp32), plus
+ * rnbar sqrt(pi/2)/m <S Pi q, 2 bits - 1> with the QJL stage.
  *   q [n_seq][hq][d] fp32, keys [n_seq][hkv][n_keys] records, logits [n_seq][hq][n_keys] fp32
  *   (unscaled); query head h reads kv head h / (hq / hkv).  The rotation of kv block
  *   (s, h) is that of record (s hkv + h) n_keys, as in tq_scores.  No workspace.              */
@@ -309,7 +334,7 @@ int tq_polar_scores(const tq_polar_codec *pc, const float *q, int64_t n_seq, int
 /* One decode step of attention with polar-coded keys and two-stage-coded values: the logits of
  * tq_polar_scores, then the online softmax and the value sum of tq_attend_decode (TurboESM
  * summary, section 2.E) over vc's codes:
- * out[s][h] = sum_n softmax_n(scale * nbar_n <Pi q, u^_n>) * v~_n.
+ * out[s][h] = sum_n softmax_n(scale * s_n) * v~_n, s_n the logit of tq_polar_scores.
  *   pc, vc of the same d (vc: 2 or 3 bits, m in {0, d}); q [n_seq][hq][d] fp32; keys k and values v
  *   [n_seq][hkv][n_ctx]; out [n_seq][hq][d] fp32.
  *   ws  workspace of tq_polar_attend_workspace_bytes bytes, 256-byte aligned: the logits

@@ -118,13 +118,19 @@ def _near_nodes(A, B, dA, dB, lv):
 def _check_full(x_seen, lib, ora, gpu, first=0, max_rows=0.02, low_norms_only=False):
     """Full-mode records against the oracle's own encoding (its fp64 rotation rounded to fp32):
     the rotation within ROT_BOUND of the exact one (through the y tap, where the call wrote one),
-    the norm words exact, and every other difference explained by that bound: a sign only where
-    |y| is within it, a node index only where the bound, carried into the node's sums of squares,
-    reaches one of its thresholds (each node's index depends on its own subtree's sums alone)."""
+    the norm words exact, and every other difference explained by that bound (_explain_fields)."""
     bits, norms, ytap = gpu
     n, d = x_seen.shape
-    x64 = x_seen.astype(np.float64)
-    rid = ora.rot_index(n, first)
+    y_ex, bound = _exact_rotation(x_seen.astype(np.float64), ora, ora.rot_index(n, first))
+    if ytap is not None:
+        assert np.all(np.abs(ytap.astype(np.float64) - y_ex) <= bound)
+    want = op.encode(x_seen, ora, first=first, stride=lib.stride)
+    assert np.array_equal(norms, want.norms & 0xFFFF if low_norms_only else want.norms)
+    _explain_fields(bits, norms, want, bound + np.abs(want.extra["y"].astype(np.float64) - y_ex), ora, max_rows)
+
+
+def _exact_rotation(x64, ora, rid):
+    """The exact fp64 rotation of each row by its block's Pi, and ROT_BOUND carried to each y_i."""
     y_ex = np.empty_like(x64)
     bound = np.empty_like(x64)
     for r in np.unique(rid):
@@ -132,12 +138,16 @@ def _check_full(x_seen, lib, ora, gpu, first=0, max_rows=0.02, low_norms_only=Fa
         P = ora.rot[r].astype(np.float64)
         y_ex[sel] = x64[sel] @ P.T
         bound[sel] = ROT_BOUND * (np.abs(x64[sel]) @ np.abs(P).T) + 1e-45
-    if ytap is not None:
-        assert np.all(np.abs(ytap.astype(np.float64) - y_ex) <= bound)
-    want = op.encode(x_seen, ora, first=first, stride=lib.stride)
-    assert np.array_equal(norms, want.norms & 0xFFFF if low_norms_only else want.norms)
+    return y_ex, bound
+
+
+def _explain_fields(bits, norms, want, dy, ora, max_rows):
+    """Device records against the oracle's, given dy >= |y_device - y_oracle| per coordinate: a
+    sign differs only where |y| is within dy, a node index only where dy, carried into the node's
+    sums of squares, reaches one of its thresholds (each node's index depends on its own subtree's
+    sums alone).  Returns the rows whose fields all agree."""
+    n, d = dy.shape
     y_o = want.extra["y"].astype(np.float64)
-    dy = bound + np.abs(y_o - y_ex)  # |y_gpu - y_oracle|
     gp, gn = op.decode_fields(op.PolarCodes(bits, norms), ora)
     wp, wn = op.decode_fields(want, ora)
     # signs
@@ -145,10 +155,10 @@ def _check_full(x_seen, lib, ora, gpu, first=0, max_rows=0.02, low_norms_only=Fa
     ok_sa = ((gp & 1) == (wp & 1)) | (np.abs(a) <= dy[:, 0::2])
     ok_sb = (((gp >> 1) & 1) == ((wp >> 1) & 1)) | (np.abs(b) <= dy[:, 1::2])
     assert ok_sa.all() and ok_sb.all()
+    bad_rows = ((gp & 3) != (wp & 3)).any(axis=1)
     # node indices, level by level: sums of squares of each child's coordinates and their bounds
     sq = y_o * y_o
     dsq = 2.0 * np.abs(y_o) * dy + dy * dy
-    bad_rows = np.zeros(n, bool)
     for lvl in range(1, ora.L + 1):
         half = 1 << (lvl - 1)
         S = sq.reshape(n, d >> lvl, 2, half).sum(-1)
@@ -160,6 +170,30 @@ def _check_full(x_seen, lib, ora, gpu, first=0, max_rows=0.02, low_norms_only=Fa
         assert not (diff & ~near).any(), (lvl, np.argwhere(diff & ~near)[:5])
         bad_rows |= diff.any(axis=1)
     assert np.mean(bad_rows) <= max_rows, np.mean(bad_rows)
+    return ~bad_rows
+
+
+def _explain_qjl(norms, sign, want, dy, same, ora):
+    """The QJL half of device records whose polar fields agree with the oracle's (rows `same`):
+    the residual then differs by at most dr = dy (1 + 2^-23) + 2^-22 |r| per coordinate, which
+    bounds fp16 ||r|| (within ||dr|| plus half an fp16 ulp) and any sign flip (only where
+    |(S r)_j| <= sum_i |S_ji| dr_i)."""
+    d = dy.shape[1]
+    r_o = want.extra["resid"].astype(np.float64)
+    dr = dy * (1.0 + 2.0 ** -23) + 2.0 ** -22 * np.abs(r_o) + 1e-45
+    rn_gpu = oq.f16_value((norms >> 16).astype(np.uint16))
+    rn_o = np.linalg.norm(r_o, axis=1)
+    half_ulp = np.abs(np.spacing(rn_o.astype(np.float16)).astype(np.float64)) / 2
+    slack = np.linalg.norm(dr, axis=1) + half_ulp
+    assert np.all(np.abs(rn_gpu - rn_o)[same] <= slack[same])
+    Sk = ora.sketch.astype(np.float64)
+    z = r_o @ Sk.T
+    zb = dr @ np.abs(Sk).T
+    gb = np.unpackbits(sign, axis=1, bitorder="little")[:, :ora.m].astype(bool)
+    wb = want.extra["sign_bits"].astype(bool)
+    flip = (gb != wb) & same[:, None]
+    assert not (flip & (np.abs(z) > zb)).any()
+    return int(flip.sum())
 
 
 @pytest.mark.parametrize("d,ab,dtype", [(64, 3, "float32"), (128, 2, "bfloat16"), (128, 4, "float16"),
@@ -495,25 +529,15 @@ def test_qjl_full_mode_explained(d, ab, dtype):
     tdt = getattr(torch, dtype)
     x_seen = torch.from_numpy(x).to(tdt).to(torch.float32).numpy()
     bits, norms, ytap, sign = _gpu_encode(lib, x, pre=False, dtype=tdt, tap=True)
-    _check_full(x_seen, lib, ora, (bits, norms & 0xFFFF, ytap), low_norms_only=True)
+    y_ex, bound = _exact_rotation(x_seen.astype(np.float64), ora, ora.rot_index(x.shape[0]))
+    assert np.all(np.abs(ytap.astype(np.float64) - y_ex) <= bound)
     want = op.encode(x_seen, ora, stride=lib.stride, sign_stride=lib.sign_stride)
-    same = np.all(bits == want.bits, axis=1)
+    assert np.array_equal(norms & 0xFFFF, want.norms & 0xFFFF)
     # the device's y (the tap) against the oracle's
     dy = np.abs(ytap.astype(np.float64) - want.extra["y"].astype(np.float64))
-    r_o = want.extra["resid"].astype(np.float64)
-    dr = dy * (1.0 + 2.0 ** -23) + 2.0 ** -22 * np.abs(r_o) + 1e-45
-    rn_gpu = oq.f16_value((norms >> 16).astype(np.uint16))
-    half_ulp = np.abs(np.spacing(np.linalg.norm(r_o, axis=1).astype(np.float16)).astype(np.float64)) / 2
-    slack = np.linalg.norm(dr, axis=1) + half_ulp
-    assert np.all(np.abs(rn_gpu - np.linalg.norm(r_o, axis=1))[same] <= slack[same])
-    Sk = ora.sketch.astype(np.float64)
-    z = r_o @ Sk.T
-    zb = dr @ np.abs(Sk).T
-    gb = np.unpackbits(sign, axis=1, bitorder="little")[:, :d].astype(bool)
-    wb = want.extra["sign_bits"].astype(bool)
-    flip = (gb != wb) & same[:, None]
-    assert not (flip & (np.abs(z) > zb)).any()
-    assert np.mean(same) >= 0.98
+    same = _explain_fields(bits, norms, want, dy, ora, 0.02)
+    flips = _explain_qjl(norms, sign, want, dy, same, ora)
+    assert flips <= max(1, int(0.02 * x.shape[0]))
 
 
 @pytest.mark.parametrize("d,ab,n_seq,hq,hkv,n_keys", [
@@ -591,3 +615,171 @@ def test_qjl_codec_errors():
     ok = tq.alloc_polar_codes(lib, 4)
     assert tq.lib.tq_polar_encode(tq.ctypes.byref(bad), tq._ptr(x), 0, 4, 64, 0, 0, ok.c(), None,
                                   tq._stream()) == -2  # m other than 0 or d
+
+
+# ------------------------------------------------------------------ append
+
+
+@pytest.mark.parametrize("d,ab,m,dtype,rope_base,per_block", [
+    (128, 2, 0, "bfloat16", 10000.0, False),  # the 8B key shape, RoPE
+    (64, 3, 64, "float32", 10000.0, True),    # QJL stage, a rotation per cache block
+    (128, 3, 128, "float16", 0.0, False),     # values: no RoPE
+    (256, 2, 0, "float32", 500000.0, False),
+])
+def test_polar_append_matches_oracle(d, ab, m, dtype, rope_base, per_block):
+    # ragged positions over a [n_seq][hkv][cap] cache, one below 0 and one at cap (skipped); the
+    # appended records against the oracle's append (RoPE in fp64, then the slot block's rotation):
+    # the radius word exact, every other difference explained by the rotation bound (the device
+    # rounds RoPE(x) to fp32 before its fp32 rotation: (d + 3) 2^-24, within ROT_BOUND); every
+    # other record untouched
+    n_seq, hkv, cap = 6, 3, 40
+    basis = [300 + i for i in range(n_seq * hkv)] if per_block else None
+    lib, ora = _codecs(d, ab, basis=basis, vpr=cap if per_block else 0, m=m)
+    say("polar append", d, ab, m, dtype, rope_base, per_block)
+    g = np.random.default_rng(d + ab + m)
+    x = (g.standard_normal((n_seq, hkv, d)) * np.where(g.random(d) < 0.05, 10.0, 1.0)).astype(np.float32)
+    pos = np.array([0, 17, cap - 1, -1, cap, 5], np.int32)
+    tdt = getattr(torch, dtype)
+    xt = torch.from_numpy(x).cuda().to(tdt)
+    x_seen = xt.float().cpu().numpy().reshape(-1, d)
+    n_rec = n_seq * hkv * cap
+    cache = tq.alloc_polar_codes(lib, n_rec)
+    cache.bits.fill_(0xAB)
+    cache.norms.fill_(0x1234567)
+    if m:
+        cache.sign.fill_(0xCD)
+    tq.polar_append(lib, xt, torch.from_numpy(pos).cuda(), cap, rope_base, cache)
+    torch.cuda.synchronize()
+    got = cache.numpy()
+    rows = np.array([r for r in range(n_seq * hkv) if 0 <= pos[r // hkv] < cap])
+    slots = rows * cap + pos[rows // hkv]
+    want = op.append(x_seen[rows], ora, slots, pos[rows // hkv], rope_base, stride=lib.stride,
+                     sign_stride=lib.sign_stride if m else None)
+    assert np.array_equal(got[1][slots] & 0xFFFF, oq.f16_norm_bits(x_seen[rows]))  # the radius of x itself
+    if not m:
+        assert np.array_equal(got[1][slots], want.norms)
+    xr = oq.rope(x_seen[rows], pos[rows // hkv], rope_base) if rope_base > 0 else x_seen[rows].astype(np.float64)
+    rid = np.array([ora.rot_index(1, int(t))[0] for t in slots])
+    y_ex, bound = _exact_rotation(xr, ora, rid)
+    dy = bound + np.abs(want.extra["y"].astype(np.float64) - y_ex)
+    same = _explain_fields(got[0][slots], got[1][slots], want, dy, ora, 0.1)
+    if m:
+        flips = _explain_qjl(got[1][slots], got[2][slots], want, dy, same, ora)
+        assert flips <= 2
+    other = np.setdiff1d(np.arange(n_rec), slots)
+    assert np.all(got[0][other] == 0xAB) and np.all(got[1][other] == 0x1234567)
+    if m:
+        assert np.all(got[2][other] == 0xCD)
+
+
+def test_polar_append_then_scores_see_the_turned_keys():
+    # keys appended with RoPE at their positions score against a query turned by RoPE at the
+    # query's position like the unturned pair at the relative offset (RoPE then the rotation keeps
+    # inner products): the logits of the appended cache within the codec's error of q . k
+    d, ab, cap, base = 128, 4, 64, 10000.0
+    lib, ora = _codecs(d, ab)
+    g = np.random.default_rng(41)
+    keys = g.standard_normal((cap, d)).astype(np.float32)
+    cache = tq.alloc_polar_codes(lib, cap)
+    for t in range(cap):
+        tq.polar_append(lib, torch.from_numpy(keys[t][None, None]).cuda(), torch.tensor([t], dtype=torch.int32,
+                        device="cuda"), cap, base, cache)
+    q = g.standard_normal((1, 1, d)).astype(np.float32)
+    qpos = cap - 1
+    qr = oq.rope(q[0], np.array([qpos]), base).astype(np.float32)[None]
+    got = tq.polar_scores(lib, torch.from_numpy(qr).cuda(), cache, cap, 1).cpu().numpy()[0, 0]
+    exact = np.array([(oq.rope(q[0], [qpos], base) @ oq.rope(keys[t:t + 1], [t], base).T).item() for t in range(cap)])
+    bits, norms = cache.numpy()
+    want = op.scores(qr.astype(np.float64), op.PolarCodes(bits, norms), ora, cap, 1)[0, 0]
+    nbar = oq.f16_value((norms & 0xFFFF).astype(np.uint16))
+    assert np.all(np.abs(got - want) <= score_tol(d) * np.linalg.norm(qr) * nbar + 1e-30)
+    # and the estimate tracks the exact RoPE'd inner product (4 angle bits: about 1% of |q||k|)
+    rel = np.abs(got - exact) / (np.linalg.norm(q) * np.linalg.norm(keys, axis=1))
+    assert np.mean(rel) < 0.02
+
+
+# ------------------------------------------------------------------ search
+
+
+def _check_polar_topk(gi, gs, osc, tol, k):
+    """gi/gs the device's lists [Q, k]; osc the oracle's estimates [Q, n_db] (fp64), tol the
+    bound on the device's score error per entry [Q, n_db].  Every returned score within its bound
+    of the oracle's, the list in the device's score order, and a row in one top-k but not the
+    other only where its score is within the bounds of the oracle's k-th."""
+    oi, os_ = topk_rows_np(osc, k)
+    for q in range(gi.shape[0]):
+        assert len(set(gi[q].tolist())) == k
+        assert np.all(np.abs(gs[q] - osc[q, gi[q]]) <= tol[q, gi[q]])
+        assert np.all(np.diff(gs[q]) <= 0)  # ordered by the device's own scores
+        kth = os_[q, -1]
+        tk = tol[q].max()
+        for r in set(gi[q].tolist()) ^ set(oi[q].tolist()):
+            assert abs(osc[q, r] - kth) <= 2 * tk, (q, r, osc[q, r], kth)
+
+
+def topk_rows_np(rows, k):
+    from oracle import estimate as oe
+
+    return oe.topk_rows(rows, k)
+
+
+def _search_tol(lib, ora, qs, codes):
+    """Per-entry bound on the device's search scores: score_tol on the polar term, the QJL term's
+    bound as for tq_polar_scores."""
+    nbar = oq.f16_value((codes.norms & 0xFFFF).astype(np.uint16))
+    qn = np.linalg.norm(qs.astype(np.float64), axis=1)
+    tol = score_tol(lib.d) * qn[:, None] * nbar[None, :]
+    if ora.m:
+        tol = tol + _qjl_score_tol(lib, ora, qs[None], codes.norms, codes.norms.shape[0], 1)[0]
+    return tol + 1e-30
+
+
+@pytest.mark.parametrize("d,ab,m,n_db,n_q,k", [
+    (128, 2, 0, 5000, 7, 10),       # one query group of 4 and a ragged one
+    (64, 3, 64, 40000, 3, 32),      # several slices and the merge, k = 32
+    (256, 4, 0, 3000, 5, 1),        # one query per group (the table limit)
+    (128, 3, 128, 9000, 9, 16),     # QJL: two queries per group
+    (64, 2, 0, 20, 2, 20),          # tiny database: k = n_db
+])
+def test_polar_search_matches_oracle(d, ab, m, n_db, n_q, k):
+    say("polar search", d, ab, m, n_db, n_q, k)
+    lib, ora = _codecs(d, ab, m=m)
+    db, qs = synth.search_data(n_db=n_db, n_q=n_q, d=d, clusters=50)
+    codes = op.encode(db, ora, stride=lib.stride, sign_stride=lib.sign_stride if m else None)
+    dcodes = tq.PolarCodes(torch.from_numpy(codes.bits).cuda(), torch.from_numpy(codes.norms.view(np.int32)).cuda(),
+                           None if codes.sign is None else torch.from_numpy(codes.sign).cuda())
+    gi, gs = tq.polar_search_topk(lib, torch.from_numpy(qs).cuda(), dcodes, n_db, k)
+    torch.cuda.synchronize()
+    osc = op.search_scores(qs, codes, ora)
+    _check_polar_topk(gi.cpu().numpy(), gs.cpu().numpy(), osc, _search_tol(lib, ora, qs, codes), k)
+
+
+def test_polar_search_ties_take_the_smaller_row():
+    # duplicated records score identically on the device too; the earlier row comes first
+    d, ab = 64, 2
+    lib, ora = _codecs(d, ab)
+    x = np.random.default_rng(51).standard_normal((5000, d)).astype(np.float32)
+    x[4000] = x[123]
+    x[2500] = x[123]
+    codes = op.encode(x, ora, stride=lib.stride)
+    dcodes = tq.PolarCodes(torch.from_numpy(codes.bits).cuda(), torch.from_numpy(codes.norms.view(np.int32)).cuda())
+    gi, gs = tq.polar_search_topk(lib, torch.from_numpy(x[123:124] * 3.0).cuda(), dcodes, 5000, 3)
+    gi, gs = gi.cpu().numpy()[0], gs.cpu().numpy()[0]
+    assert list(gi) == [123, 2500, 4000] and gs[0] == gs[1] == gs[2]
+
+
+def test_polar_search_errors():
+    lib, _ = _codecs(64, 2, basis=[1, 2], vpr=10)  # two rotations: search takes one
+    db = tq.alloc_polar_codes(lib, 20)
+    q = torch.zeros((2, 64), device="cuda")
+    cc = lib.c()
+    i = torch.empty((2, 4), dtype=torch.int64, device="cuda")
+    s = torch.empty((2, 4), device="cuda")
+    assert tq.lib.tq_polar_search_topk(tq.ctypes.byref(cc), tq._ptr(q), 2, db.c(), 20, 4, tq._ptr(i), tq._ptr(s),
+                                       None, 0, tq._stream()) == -1
+    lib1, _ = _codecs(64, 2)
+    cc1 = lib1.c()
+    with pytest.raises(ValueError):
+        tq.polar_search_topk(lib1, q, db, 20, 21)  # k > n_db
+    assert tq.lib.tq_polar_search_topk(tq.ctypes.byref(cc1), tq._ptr(q), 2, db.c(), 20, 33, tq._ptr(i), tq._ptr(s),
+                                       None, 0, tq._stream()) == -1  # k > 32

@@ -80,6 +80,9 @@ def _load():
         "tq_polar_record_bytes": ([I32, I32], SZ),
         "tq_polar_encode": ([PP, P, I32, I64, I64, ctypes.c_uint32, I64, _PolarCodes, P, P], I32),
         "tq_polar_scores": ([PP, P, I64, I32, I32, I64, _PolarCodes, P, P], I32),
+        "tq_polar_append": ([PP, P, I32, I64, I32, P, I64, ctypes.c_float, _PolarCodes, P], I32),
+        "tq_polar_search_workspace_bytes": ([PP, I64, I32, I64], SZ),
+        "tq_polar_search_topk": ([PP, P, I64, _PolarCodes, I64, I32, P, P, P, SZ, P], I32),
         "tq_polar_attend_workspace_bytes": ([PP, CP, I64, I32, I32, I64], SZ),
         "tq_polar_attend_decode": ([PP, CP, P, I64, I32, I32, I64, _PolarCodes, _Codes, ctypes.c_float, P, P, SZ,
                                     P], I32),
@@ -111,7 +114,7 @@ EXPORTED = ("tq_make_rotation", "tq_make_head_rotations", "tq_make_sketch", "tq_
             "tq_search_topk",
             "tq_workspace_bytes", "tq_status_str", "tq_version", "tq_make_polar_tables",
             "tq_polar_record_bytes", "tq_polar_encode", "tq_polar_scores", "tq_polar_attend_workspace_bytes",
-            "tq_polar_attend_decode")
+            "tq_polar_attend_decode", "tq_polar_append", "tq_polar_search_workspace_bytes", "tq_polar_search_topk")
 
 
 def _check(rc):
@@ -687,6 +690,44 @@ def polar_encode(pc: PolarCodec, x, pre_rotated: bool = False, first: int = 0, o
     _check(lib.tq_polar_encode(ctypes.byref(cc), _ptr(x2), dt, n, x2.stride(0), flags, first, out.c(),
                                _ptr(y_tap), _stream()))
     return out
+
+
+def polar_append(pc: PolarCodec, x_new, pos, cap: int, rope_base: float, cache: PolarCodes):
+    """Append x_new [n_seq, hkv, d] into the polar ``cache`` laid out [n_seq][hkv][cap], at slot
+    pos[s] (int32 [n_seq] on the device), RoPE'd at pos[s] before the rotation when rope_base > 0."""
+    named = _check_rows(x_new, pc.d, "x_new")
+    _need(x_new.dim() == 3, "x_new must be [n_seq, hkv, d]")
+    x = x_new.contiguous()
+    n_seq, hkv, d = x.shape
+    _need(cap >= 1, "cap must be >= 1")
+    named += _check_tensor(pos, "pos", dtype=_torch().int32, shape=(n_seq,))
+    named += _check_codec(pc) + _check_polar_codes(cache, pc, n_seq * hkv * cap, "cache")
+    _check_devices(named)
+    dt = _DT[str(x.dtype).replace("torch.", "")]
+    cc = pc.c()
+    _check(lib.tq_polar_append(ctypes.byref(cc), _ptr(x), dt, n_seq, hkv, _ptr(pos), cap, ctypes.c_float(rope_base),
+                               cache.c(), _stream()))
+    return cache
+
+
+def polar_search_topk(pc: PolarCodec, queries, db: PolarCodes, n_db: int, k: int):
+    """Top-k (index int64, score fp32) per query by the polar estimate of <q, x>."""
+    torch = _torch()
+    _need(isinstance(queries, torch.Tensor) and queries.dim() == 2 and queries.shape[1] == pc.d,
+          f"queries must be [n_q, {pc.d}]")
+    named = _check_tensor(queries, "queries", dtype=torch.float32)
+    n_q = queries.shape[0]
+    _need(1 <= k <= 32 and k <= n_db, "k must be in 1 .. min(32, n_db)")
+    named += _check_codec(pc) + _check_polar_codes(db, pc, n_db, "db")
+    _check_devices(named)
+    idx = torch.empty((n_q, k), dtype=torch.int64, device=queries.device)
+    sc = torch.empty((n_q, k), dtype=torch.float32, device=queries.device)
+    cc = pc.c()
+    need = lib.tq_polar_search_workspace_bytes(ctypes.byref(cc), n_q, k, n_db)
+    buf, ws, wsb = _workspace(need, queries.device)
+    _check(lib.tq_polar_search_topk(ctypes.byref(cc), _ptr(queries), n_q, db.c(), n_db, k, _ptr(idx), _ptr(sc),
+                                    ws, wsb, _stream()))
+    return idx, sc
 
 
 def polar_scores(pc: PolarCodec, q, codes: PolarCodes, n_keys: int, hkv: int, logits=None):

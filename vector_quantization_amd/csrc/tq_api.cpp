@@ -295,6 +295,43 @@ extern "C" int tq_polar_attend_decode(const tq_polar_codec *pc, const tq_codec *
   return tq::launch_attend_logits(tq::view(*vc), lg, s, tq::view(v), scale, out, part, stream);
 }
 
+extern "C" int tq_polar_append(const tq_polar_codec *pc, const void *x_new, tq_dtype dt, int64_t n_seq, int32_t hkv,
+                               const int32_t *pos, int64_t cap, float rope_base, tq_polar_codes cache, void *stream) {
+  int rc = check_polar(pc);
+  if (rc != TQ_OK) return rc;
+  if (n_seq < 0 || hkv < 1 || cap < 1 || !(rope_base >= 0.0f)) return TQ_EINVAL;
+  if (n_seq == 0) return TQ_OK;
+  if (!x_new || !pos) return TQ_EINVAL;
+  if (dt != TQ_F32 && dt != TQ_F16 && dt != TQ_BF16) return TQ_EINVAL;
+  rc = check_polar_codes(pc, cache);
+  if (rc != TQ_OK) return rc;
+  return tq::launch_polar_append(tq::view(*pc), x_new, (int)dt, n_seq, hkv, pos, cap, rope_base, tq::view(cache),
+                                 stream);
+}
+
+extern "C" size_t tq_polar_search_workspace_bytes(const tq_polar_codec *pc, int64_t n_q, int32_t k, int64_t n_db) {
+  if (check_polar(pc) != TQ_OK || n_q < 0 || n_db < 1 || k < 1 || k > 32) return 0;
+  return tq::polar_search_workspace(tq::view(*pc), n_q, k, n_db);
+}
+
+extern "C" int tq_polar_search_topk(const tq_polar_codec *pc, const float *queries, int64_t n_q, tq_polar_codes db,
+                                    int64_t n_db, int32_t k, int64_t *out_idx, float *out_score, void *ws,
+                                    size_t ws_bytes, void *stream) {
+  int rc = check_polar(pc);
+  if (rc != TQ_OK) return rc;
+  if (pc->n_rot != 1) return TQ_EINVAL;
+  if (n_q < 0 || n_db < 1 || k < 1 || k > 32 || k > n_db) return TQ_EINVAL;
+  if (n_q == 0) return TQ_OK;
+  if (!queries || !out_idx || !out_score) return TQ_EINVAL;
+  rc = check_polar_codes(pc, db);
+  if (rc != TQ_OK) return rc;
+  const size_t need = tq::polar_search_workspace(tq::view(*pc), n_q, k, n_db);
+  if (need > 0 && (!ws || ws_bytes < need)) return TQ_EWORKSPACE;
+  if (ws && !aligned(ws, 256)) return TQ_EALIGN;
+  return tq::launch_polar_search(tq::view(*pc), queries, n_q, tq::view(db), n_db, k, out_idx, out_score, ws,
+                                 stream);
+}
+
 extern "C" int tq_polar_scores(const tq_polar_codec *pc, const float *q, int64_t n_seq, int32_t hq, int32_t hkv,
                                int64_t n_keys, tq_polar_codes k, float *logits, void *stream) {
   int rc = check_polar(pc);

@@ -106,20 +106,7 @@ __global__ __launch_bounds__(kWave *kEncWaves) void encode_kernel(EncArgs a) {
       for (int c = 0; c < C; ++c)
         if (lane + kWave * c < D) s.xs[lane + kWave * c] = nsrc[c];
       wave_lds_fence();
-      if (a.pos != nullptr && a.rope_base > 0.0f) {
-        // RoPE before the rotation: coordinate i < D/2 turns with i + D/2 by p * base^(-2i/D);
-        // angle, sine and cosine in fp64 (an fp32 angle would be off by ~p * 2^-24 radians)
-        const double lb = log2((double)a.rope_base);
-        for (int i = lane; i < D / 2; i += kWave) {
-          const double ang = (double)p * exp2(-2.0 * i / D * lb);
-          double sn, cs;
-          sincos(ang, &sn, &cs);
-          const double x0 = s.xs[i], x1 = s.xs[i + D / 2];
-          s.xs[i] = (float)(x0 * cs - x1 * sn);
-          s.xs[i + D / 2] = (float)(x0 * sn + x1 * cs);
-        }
-        wave_lds_fence();
-      }
+      if (a.pos != nullptr && a.rope_base > 0.0f) wave_rope_lds<D>(s.xs, p, a.rope_base);
       int64_t rid = 0;
       if (a.n_rot > 1 && a.vecs_per_rot > 0) {
         rid = (a.first + rec) / a.vecs_per_rot;

@@ -117,6 +117,14 @@ int launch_polar_mfma(const PolarView &pc, const void *x, int dt, int64_t n, int
                       int64_t first, const PolarCodesView &out, float *y_tap, void *stream);
 int launch_polar_scores(const PolarView &pc, const float *q, const ScoreShape &s, const PolarCodesView &k,
                         float *logits, void *stream);
+int launch_polar_append(const PolarView &pc, const void *x, int dt, int64_t n_seq, int hkv, const int32_t *pos,
+                        int64_t cap, float rope_base, const PolarCodesView &out, void *stream);
+size_t polar_search_workspace(const PolarView &pc, int64_t n_q, int k, int64_t n_db);
+int launch_polar_search(const PolarView &pc, const float *queries, int64_t n_q, const PolarCodesView &db,
+                        int64_t n_db, int k, int64_t *out_idx, float *out_score, void *ws, void *stream);
+// merge of per-slice top-k lists part_s/part_i [n_q][n_slices][k] into out [n_q][k] (tq_search.hip)
+int launch_topk_merge(const float *part_s, const int32_t *part_i, int64_t n_q, int n_slices, int k,
+                      int64_t *out_idx, float *out_score, void *stream);
 inline bool supported_polar(int d, int ab) { return (d == 64 || d == 128 || d == 256) && ab >= 2 && ab <= 4; }
 // the QJL stage on the polar residual: m = d at d = 64, 128
 inline bool supported_polar_m(int d, int m) { return m == 0 || (m == d && (d == 64 || d == 128)); }

@@ -27,11 +27,16 @@
 // rotates its G query heads, then tabulates for every pair j and every value f of the pair
 // field the leaf term (+-cos psi^ q_2j +- sin psi^ q_2j+1) of each head, G floats per (j, f).  A
 // key's logit is nbar sum_j r_j T[j][f_j], with r_j the product of the node cos/sin factors on
-// the path to pair j, expanded from the root down in registers (one thread per key).
+// the path to pair j, expanded from the root down in registers (one thread per key).  With the
+// QJL stage, byte tables U_p[beta] = sum_t q^_8p+t (2 bit_t(beta) - 1) of the sketched query add
+// rnbar sqrt(pi/2)/m sum_p U_p[sign byte p].
+// polar_search_scan: the same tables for G queries of a search, one workgroup per (query group,
+// database slice), a top-k list per wave and query as in the two-stage search.
 
 #include "tq_device.h"
 #include "tq_internal.h"
 #include "tq_qprep.h"
+#include "tq_topk.h"
 
 namespace tq {
 
@@ -74,6 +79,13 @@ struct PolarEncArgs {
   const float *sketch;  // [M][D] with the QJL stage
   uint8_t *sign;
   int64_t sign_stride;
+  // append mode (pos != nullptr): input row v = s * hkv + h goes to record v * cap + pos[s]
+  // (skipped when pos[s] is outside [0, cap)), whose block selects the rotation; with
+  // rope_base > 0 the rotation sees RoPE(x, pos[s])
+  const int32_t *pos;
+  int64_t cap;
+  int hkv;
+  float rope_base;
 };
 
 constexpr int kPolarEncWaves = 4;
@@ -122,6 +134,13 @@ __global__ __launch_bounds__(kWave *kPolarEncWaves) void polar_encode_kernel(Pol
   const int sw = (int)(a.stride >> 2);
 
   for (int64_t v = (int64_t)blockIdx.x * kPolarEncWaves + wid; v < a.n; v += (int64_t)gridDim.x * kPolarEncWaves) {
+    int64_t rec = v;  // the record written
+    int64_t p = 0;    // the position (append mode)
+    if (a.pos != nullptr) {
+      p = a.pos[v / a.hkv];
+      if (p < 0 || p >= a.cap) continue;  // uniform: one vector per wavefront
+      rec = v * a.cap + p;
+    }
     // ---- load and rotate
     float y[C], nsrc[C];
 #pragma unroll
@@ -133,9 +152,10 @@ __global__ __launch_bounds__(kWave *kPolarEncWaves) void polar_encode_kernel(Pol
 #pragma unroll
       for (int c = 0; c < C; ++c) s.xs[lane + kWave * c] = nsrc[c];
       wave_lds_fence();
+      if (a.pos != nullptr && a.rope_base > 0.0f) wave_rope_lds<D>(s.xs, p, a.rope_base);
       int64_t rid = 0;
       if (a.n_rot > 1 && a.vecs_per_rot > 0) {
-        rid = (a.first + v) / a.vecs_per_rot;
+        rid = (a.first + rec) / a.vecs_per_rot;
         if (rid > a.n_rot - 1) rid = a.n_rot - 1;
       }
       const float *R = a.rot + rid * (int64_t)D * D;
@@ -210,7 +230,7 @@ __global__ __launch_bounds__(kWave *kPolarEncWaves) void polar_encode_kernel(Pol
           word |= off >= 0 ? (f << off) : (f >> (-off));
         }
       }
-      reinterpret_cast<uint32_t *>(a.bits + v * a.stride)[w] = word;
+      reinterpret_cast<uint32_t *>(a.bits + rec * a.stride)[w] = word;
     }
     uint32_t hi = 0u;
     if constexpr (M > 0) {
@@ -247,11 +267,11 @@ __global__ __launch_bounds__(kWave *kPolarEncWaves) void polar_encode_kernel(Pol
       }
       const uint32_t rn16 = wave_norm_f16<D, C>(r, s.terms, s.buf);
       wave_lds_fence();
-      wave_sign_words<D, M>(a.sketch, s.rs, s.terms, s.buf, reinterpret_cast<uint32_t *>(a.sign + v * a.sign_stride),
-                            (int)(a.sign_stride >> 2));
+      wave_sign_words<D, M>(a.sketch, s.rs, s.terms, s.buf,
+                            reinterpret_cast<uint32_t *>(a.sign + rec * a.sign_stride), (int)(a.sign_stride >> 2));
       hi = rn16;
     }
-    if (lane == 0) a.norms[v] = (hi << 16) | n16;
+    if (lane == 0) a.norms[rec] = (hi << 16) | n16;
     wave_lds_fence();
   }
 }
@@ -299,6 +319,21 @@ int launch_polar_encode(const PolarView &pc, const void *x, int dt, int64_t n, i
   return TQ_EUNSUPPORTED;
 }
 
+int launch_polar_append(const PolarView &pc, const void *x, int dt, int64_t n_seq, int hkv, const int32_t *pos,
+                        int64_t cap, float rope_base, const PolarCodesView &out, void *stream) {
+  const int64_t n = n_seq * hkv;
+  if (n == 0) return TQ_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  PolarEncArgs a{x, pc.d, n, 0, pc.rot, pc.n_rot, pc.vecs_per_rot, pc.tables, out.bits, out.stride,
+                 out.norms, nullptr, pc.sketch, out.sign, out.sign_stride, pos, cap, hkv, rope_base};
+#define TQ_PE(DD, AA) \
+  if (pc.d == DD && pc.ab == AA) return launch_polar_encode_da<DD, AA>(a, pc.m, dt, false, st);
+  TQ_PE(64, 2) TQ_PE(64, 3) TQ_PE(64, 4) TQ_PE(128, 2) TQ_PE(128, 3) TQ_PE(128, 4)
+  TQ_PE(256, 2) TQ_PE(256, 3) TQ_PE(256, 4)
+#undef TQ_PE
+  return TQ_EUNSUPPORTED;
+}
+
 // ------------------------------------------------------------------ scores
 
 struct PolarScoreArgs {
@@ -316,6 +351,108 @@ struct PolarScoreArgs {
   int64_t sign_stride;
 };
 
+// Logits of record v for G query heads from the LDS tables (layouts as polar_score_kernel's):
+// nbar sum_j r_j T[j][f_j], plus rnbar sqrt(pi/2)/m sum_p U_p[sign byte p] with the QJL stage.
+template <int D, int AB, int M, int G>
+__device__ __forceinline__ void polar_record_logits(const uint8_t *bits, int64_t stride, const uint32_t *norms,
+                                                    const uint8_t *sign, int64_t sign_stride, int64_t v,
+                                                    const float *lut, const float *qlut,
+                                                    const float2 (*cs)[PolarLayout<D, AB>::NA], float (&out)[G]) {
+  using P = PolarLayout<D, AB>;
+  uint32_t w[P::NW];
+  load_words<P::NW>(bits + v * stride, w);
+  const uint32_t nw = norms[v];
+  // radii of the level-1 pairs, expanded from the root (radius 1) down; r[i] holds node i of
+  // the current level, children written in place from the back
+  float r[P::NP];
+  r[0] = 1.0f;
+#pragma unroll
+  for (int l = P::LV; l >= 2; --l) {
+#pragma unroll
+    for (int i = (D >> l) - 1; i >= 0; --i) {
+      const float2 c = cs[l - 1][bit_field<P::NW>(w, P::node_bit(l, i), AB)];
+      const float ri = r[i];
+      r[2 * i] = ri * c.x;
+      r[2 * i + 1] = ri * c.y;
+    }
+  }
+  float acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < P::NP; ++j) {
+    const uint32_t f = bit_field<P::NW>(w, P::WP * j, P::WP);
+    const float *e = lut + (j * P::NF + (int)f) * G;
+    if constexpr (G % 4 == 0) {
+#pragma unroll
+      for (int g = 0; g < G; g += 4) {
+        const float4 tv = *reinterpret_cast<const float4 *>(e + g);
+        acc[g] = fmaf(r[j], tv.x, acc[g]);
+        acc[g + 1] = fmaf(r[j], tv.y, acc[g + 1]);
+        acc[g + 2] = fmaf(r[j], tv.z, acc[g + 2]);
+        acc[g + 3] = fmaf(r[j], tv.w, acc[g + 3]);
+      }
+    } else if constexpr (G == 2) {
+      const float2 tv = *reinterpret_cast<const float2 *>(e);
+      acc[0] = fmaf(r[j], tv.x, acc[0]);
+      acc[1] = fmaf(r[j], tv.y, acc[1]);
+    } else {
+      acc[0] = fmaf(r[j], e[0], acc[0]);
+    }
+  }
+  const float nbar = f16_bits_to_float(nw & 0xFFFFu);
+  if constexpr (M > 0) {
+    constexpr int NQ = M / 8;
+    constexpr int SW = (M + 31) / 32;
+    uint32_t sw[SW];
+    load_words<SW>(sign + v * sign_stride, sw);
+    float aq[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) aq[g] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NQ; ++p) {
+      const int byte = (sw[p >> 2] >> (8 * (p & 3))) & 0xFF;
+      const float *e = qlut + (p * 256 + byte) * G;
+#pragma unroll
+      for (int g = 0; g < G; ++g) aq[g] += e[g];
+    }
+    const float rq = f16_bits_to_float(nw >> 16) * (1.2533141373155003f / (float)(M > 0 ? M : 1));
+#pragma unroll
+    for (int h = 0; h < G; ++h) out[h] = fmaf(rq, aq[h], nbar * acc[h]);
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) out[h] = nbar * acc[h];
+  }
+}
+
+// The LDS tables of G query heads from their rotated (qt [G][D]) and sketched (qh [G][M])
+// forms: leaf terms (j, f, g) = (+-cos psi^_k) q_2j + (+-sin psi^_k) q_2j+1 with f = sa | sb << 1
+// | k << 2, and the sign-byte tables.  Ends synchronised.
+template <int D, int AB, int M, int G, int NT>
+__device__ void build_polar_tables(float *lut, float *qlut, const float2 (*cs)[PolarLayout<D, AB>::NA],
+                                   const float *qt, const float *qh) {
+  using P = PolarLayout<D, AB>;
+  if constexpr (M > 0) {
+    for (int e = threadIdx.x; e < (M / 8) * 256 * G; e += NT) {
+      const int g = e % G, beta = (e / G) & 255, p = e / (G * 256);
+      float acc = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float y = qh[g * M + 8 * p + t];
+        acc += ((beta >> t) & 1) ? y : -y;
+      }
+      qlut[e] = acc;
+    }
+  }
+  for (int e = threadIdx.x; e < P::NP * P::NF * G; e += NT) {
+    const int g = e % G, f = (e / G) % P::NF, j = e / (G * P::NF);
+    const float2 t = cs[0][f >> 2];
+    const float c = (f & 1) ? -t.x : t.x, sn = (f & 2) ? -t.y : t.y;
+    lut[e] = fmaf(sn, qt[g * D + 2 * j + 1], c * qt[g * D + 2 * j]);
+  }
+  __syncthreads();
+}
+
 // LDS tables of G heads: the leaf terms, and with the QJL stage the sign-byte tables
 // U_p[beta] = sum_t q^_{8p+t} (2 bit_t(beta) - 1), G floats per entry
 template <int D, int AB, int M, int G>
@@ -327,7 +464,6 @@ template <int D, int AB, int M, int G, int NT>
 __global__ __launch_bounds__(NT) void polar_score_kernel(PolarScoreArgs a) {
   using P = PolarLayout<D, AB>;
   constexpr int NQ = M / 8;
-  constexpr int SW = (M + 31) / 32;
   __shared__ __align__(16) float lut[P::NP * P::NF * G];
   __shared__ __align__(16) float qlut[M > 0 ? NQ * 256 * G : 4];
   __shared__ float2 cs[P::LV][P::NA];
@@ -357,96 +493,17 @@ __global__ __launch_bounds__(NT) void polar_score_kernel(PolarScoreArgs a) {
     cs[l][j] = make_float2(a.tables[l * 4 * P::NA + j], a.tables[(l * 4 + 1) * P::NA + j]);
   }
   prep.finish(qs, qt, qh);  // ends synchronised
-  if constexpr (M > 0) {
-    for (int e = threadIdx.x; e < NQ * 256 * G; e += NT) {
-      const int g = e % G, beta = (e / G) & 255, p = e / (G * 256);
-      float acc = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float y = qh[g * M + 8 * p + t];
-        acc += ((beta >> t) & 1) ? y : -y;
-      }
-      qlut[e] = acc;
-    }
-  }
-  // leaf terms: entry (j, f, g) = (+-cos psi^_k) q_2j + (+-sin psi^_k) q_2j+1, f = sa | sb << 1 | k << 2
-  for (int e = threadIdx.x; e < P::NP * P::NF * G; e += NT) {
-    const int g = e % G, f = (e / G) % P::NF, j = e / (G * P::NF);
-    const float2 t = cs[0][f >> 2];
-    const float c = (f & 1) ? -t.x : t.x, sn = (f & 2) ? -t.y : t.y;
-    lut[e] = fmaf(sn, qt[g * D + 2 * j + 1], c * qt[g * D + 2 * j]);
-  }
-  __syncthreads();
+  build_polar_tables<D, AB, M, G, NT>(lut, qlut, cs, qt, qh);
 
   const int64_t t0 = (int64_t)chunk * a.chunk;
   int64_t t1 = t0 + a.chunk;
   if (t1 > a.n_keys) t1 = a.n_keys;
   const int64_t vbase = blk * a.n_keys;
   for (int64_t t = t0 + threadIdx.x; t < t1; t += NT) {
-    const int64_t v = vbase + t;
-    uint32_t w[P::NW];
-    load_words<P::NW>(a.bits + v * a.stride, w);
-    const uint32_t nw = a.norms[v];
-    // radii of the level-1 pairs, expanded from the root (radius 1) down; r[i] holds node i of
-    // the current level, children written in place from the back
-    float r[P::NP];
-    r[0] = 1.0f;
+    float lg[G];
+    polar_record_logits<D, AB, M, G>(a.bits, a.stride, a.norms, a.sign, a.sign_stride, vbase + t, lut, qlut, cs, lg);
 #pragma unroll
-    for (int l = P::LV; l >= 2; --l) {
-#pragma unroll
-      for (int i = (D >> l) - 1; i >= 0; --i) {
-        const float2 c = cs[l - 1][bit_field<P::NW>(w, P::node_bit(l, i), AB)];
-        const float ri = r[i];
-        r[2 * i] = ri * c.x;
-        r[2 * i + 1] = ri * c.y;
-      }
-    }
-    float acc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < P::NP; ++j) {
-      const uint32_t f = bit_field<P::NW>(w, P::WP * j, P::WP);
-      const float *e = lut + (j * P::NF + (int)f) * G;
-      if constexpr (G % 4 == 0) {
-#pragma unroll
-        for (int g = 0; g < G; g += 4) {
-          const float4 tv = *reinterpret_cast<const float4 *>(e + g);
-          acc[g] = fmaf(r[j], tv.x, acc[g]);
-          acc[g + 1] = fmaf(r[j], tv.y, acc[g + 1]);
-          acc[g + 2] = fmaf(r[j], tv.z, acc[g + 2]);
-          acc[g + 3] = fmaf(r[j], tv.w, acc[g + 3]);
-        }
-      } else if constexpr (G == 2) {
-        const float2 tv = *reinterpret_cast<const float2 *>(e);
-        acc[0] = fmaf(r[j], tv.x, acc[0]);
-        acc[1] = fmaf(r[j], tv.y, acc[1]);
-      } else {
-        acc[0] = fmaf(r[j], e[0], acc[0]);
-      }
-    }
-    const float nbar = f16_bits_to_float(nw & 0xFFFFu);
-    if constexpr (M > 0) {
-      // the QJL term: rnbar sqrt(pi/2)/m sum_p U_p[sign byte p]
-      uint32_t sw[SW];
-      load_words<SW>(a.sign + v * a.sign_stride, sw);
-      float aq[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) aq[g] = 0.0f;
-#pragma unroll
-      for (int p = 0; p < NQ; ++p) {
-        const int byte = (sw[p >> 2] >> (8 * (p & 3))) & 0xFF;
-        const float *e = qlut + (p * 256 + byte) * G;
-#pragma unroll
-        for (int g = 0; g < G; ++g) aq[g] += e[g];
-      }
-      const float rq = f16_bits_to_float(nw >> 16) * (1.2533141373155003f / (float)(M > 0 ? M : 1));
-#pragma unroll
-      for (int h = 0; h < G; ++h) a.logits[(qrow + h) * a.n_keys + t] = fmaf(rq, aq[h], nbar * acc[h]);
-    } else {
-#pragma unroll
-      for (int h = 0; h < G; ++h) a.logits[(qrow + h) * a.n_keys + t] = nbar * acc[h];
-    }
+    for (int h = 0; h < G; ++h) a.logits[(qrow + h) * a.n_keys + t] = lg[h];
   }
 }
 
@@ -505,6 +562,194 @@ int launch_polar_scores(const PolarView &pc, const float *q, const ScoreShape &s
   TQ_PS(256, 2) TQ_PS(256, 3) TQ_PS(256, 4)
 #undef TQ_PS
   return TQ_EUNSUPPORTED;
+}
+
+// ------------------------------------------------------------------ search
+
+struct PolarSearchArgs {
+  const float *q, *rot, *tables, *sketch;
+  int64_t n_q, n_db;
+  int k, n_slices;
+  int64_t slice;
+  const uint8_t *bits;
+  int64_t stride;
+  const uint32_t *norms;
+  const uint8_t *sign;
+  int64_t sign_stride;
+  float *part_s;     // [n_q][n_slices][k] when n_slices > 1
+  int32_t *part_i;
+  int64_t *out_idx;  // [n_q][k] when n_slices == 1
+  float *out_score;
+};
+
+constexpr int kPolarSearchNT = 512;
+
+template <int D, int AB, int M, int G, int NT>
+__global__ __launch_bounds__(NT) void polar_search_scan(PolarSearchArgs a) {
+  using P = PolarLayout<D, AB>;
+  constexpr int NW = NT / kWave;
+  static_assert(NW >= G, "one wave per query merges the lists");
+  __shared__ __align__(16) float lut[P::NP * P::NF * G];
+  __shared__ __align__(16) float qlut[M > 0 ? (M / 8) * 256 * G : 4];
+  __shared__ float2 cs[P::LV][P::NA];
+  __shared__ float qs[G * D];
+  __shared__ float qt[G * D];
+  __shared__ float qh[G * (M > 0 ? M : 1)];
+  __shared__ float wls[NW * G * 32];
+  __shared__ int32_t wli[NW * G * 32];
+
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  const int slice = (int)(blockIdx.x % a.n_slices);
+  const int64_t q0 = (int64_t)(blockIdx.x / a.n_slices) * G;
+  const int rows = a.n_q - q0 < G ? (int)(a.n_q - q0) : G;  // the last group may be partial
+  QueryPrep<D, M, G, NT> prep;
+  prep.issue(a.q + q0 * D, a.rot, a.sketch, rows);
+  for (int e = tid; e < P::LV * P::NA; e += NT) {
+    const int l = e / P::NA, j = e % P::NA;
+    cs[l][j] = make_float2(a.tables[l * 4 * P::NA + j], a.tables[(l * 4 + 1) * P::NA + j]);
+  }
+  prep.finish(qs, qt, qh);  // ends synchronised
+  build_polar_tables<D, AB, M, G, NT>(lut, qlut, cs, qt, qh);
+
+  const int k = a.k;
+  float ls[G], tau[G];
+  int32_t li[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    ls[h] = -INFINITY;
+    li[h] = 0x7FFFFFFF;
+    tau[h] = -INFINITY;
+  }
+  const int64_t v0 = (int64_t)slice * a.slice;
+  int64_t v1 = v0 + a.slice;
+  if (v1 > a.n_db) v1 = a.n_db;
+  for (int64_t base = v0; base < v1; base += NT) {
+    const int64_t v = base + tid;
+    const bool valid = v < v1;
+    float sc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) sc[h] = -INFINITY;
+    if (valid) polar_record_logits<D, AB, M, G>(a.bits, a.stride, a.norms, a.sign, a.sign_stride, v, lut, qlut, cs, sc);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      uint64_t m = __ballot(valid && sc[h] >= tau[h]);
+      while (m) {
+        const int j = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        const float c = __shfl(sc[h], j, kWave);
+        list_insert(ls[h], li[h], c, (int32_t)(base + wid * kWave + j), k);
+        tau[h] = __shfl(ls[h], k - 1, kWave);
+      }
+    }
+  }
+
+  // merge the waves' lists: wave h (< G) merges query h
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    if (lane < k) {
+      wls[(wid * G + h) * 32 + lane] = ls[h];
+      wli[(wid * G + h) * 32 + lane] = li[h];
+    }
+  __syncthreads();
+  if (wid < G && wid < rows) {
+    const int h = wid;
+    float ms = lane < k ? wls[h * 32 + lane] : -INFINITY;
+    int32_t mi = lane < k ? wli[h * 32 + lane] : 0x7FFFFFFF;
+    for (int w = 1; w < NW; ++w)
+      for (int i = 0; i < k; ++i) list_insert(ms, mi, wls[(w * G + h) * 32 + i], wli[(w * G + h) * 32 + i], k);
+    const int64_t qi = q0 + h;
+    if (lane < k) {
+      if (a.n_slices == 1) {
+        a.out_idx[qi * k + lane] = mi;
+        a.out_score[qi * k + lane] = ms;
+      } else {
+        a.part_s[(qi * a.n_slices + slice) * k + lane] = ms;
+        a.part_i[(qi * a.n_slices + slice) * k + lane] = mi;
+      }
+    }
+  }
+}
+
+// queries per workgroup: the largest of 4, 2, 1 whose tables fit 64 KiB
+static int polar_search_group(const PolarView &pc) {
+  const int64_t per = (int64_t)(pc.d / 2) * (1 << (2 + pc.ab)) * 4 + (int64_t)(pc.m / 8) * 256 * 4;
+  for (int g = 4; g > 1; g /= 2)
+    if (per * g <= 64 * 1024) return g;
+  return 1;
+}
+
+// about 2048 workgroups over (query group, slice); slices of at least 4 NT rows
+static void polar_search_split(int64_t n_q, int g, int64_t n_db, int &n_slices, int64_t &slice) {
+  const int64_t groups = (n_q + g - 1) / g;
+  int64_t want = (2048 + groups - 1) / groups;
+  const int64_t max_slices = (n_db + 4 * kPolarSearchNT - 1) / (4 * kPolarSearchNT);
+  if (want > max_slices) want = max_slices;
+  if (want < 1) want = 1;
+  slice = (n_db + want - 1) / want;
+  n_slices = (int)((n_db + slice - 1) / slice);
+}
+
+size_t polar_search_workspace(const PolarView &pc, int64_t n_q, int k, int64_t n_db) {
+  int ns;
+  int64_t sl;
+  polar_search_split(n_q, polar_search_group(pc), n_db, ns, sl);
+  return ns > 1 ? (size_t)n_q * ns * k * (sizeof(float) + sizeof(int32_t)) : 0;
+}
+
+template <int D, int AB, int M>
+static int launch_polar_search_dam(const PolarSearchArgs &a, int g, hipStream_t st) {
+  constexpr int NT = kPolarSearchNT;
+  const int64_t blocks = (a.n_q + g - 1) / g * a.n_slices;
+  if (!grid_fits(blocks)) return TQ_EUNSUPPORTED;
+  if (g == 4) {
+    if constexpr (polar_lut_bytes<D, AB, M, 4>() <= 64 * 1024) {
+      hipLaunchKernelGGL((polar_search_scan<D, AB, M, 4, NT>), dim3((unsigned)blocks), dim3(NT), 0, st, a);
+      return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+    }
+    return TQ_EUNSUPPORTED;
+  }
+  if (g == 2) {
+    if constexpr (polar_lut_bytes<D, AB, M, 2>() <= 64 * 1024) {
+      hipLaunchKernelGGL((polar_search_scan<D, AB, M, 2, NT>), dim3((unsigned)blocks), dim3(NT), 0, st, a);
+      return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+    }
+    return TQ_EUNSUPPORTED;
+  }
+  hipLaunchKernelGGL((polar_search_scan<D, AB, M, 1, NT>), dim3((unsigned)blocks), dim3(NT), 0, st, a);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+template <int D, int AB>
+static int launch_polar_search_da(const PolarSearchArgs &a, int m, int g, hipStream_t st) {
+  if (m == 0) return launch_polar_search_dam<D, AB, 0>(a, g, st);
+  if constexpr (D == 64 || D == 128) {
+    if (m == D) return launch_polar_search_dam<D, AB, D>(a, g, st);
+  }
+  return TQ_EUNSUPPORTED;
+}
+
+int launch_polar_search(const PolarView &pc, const float *queries, int64_t n_q, const PolarCodesView &db,
+                        int64_t n_db, int k, int64_t *out_idx, float *out_score, void *ws, void *stream) {
+  if (n_q == 0) return TQ_OK;
+  if (n_db > 0x7FFFFFFELL) return TQ_EUNSUPPORTED;  // rows are int32 in the lists
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int g = polar_search_group(pc);
+  int ns;
+  int64_t sl;
+  polar_search_split(n_q, g, n_db, ns, sl);
+  float *part_s = reinterpret_cast<float *>(ws);
+  int32_t *part_i = ns > 1 ? reinterpret_cast<int32_t *>(part_s + (size_t)n_q * ns * k) : nullptr;
+  PolarSearchArgs a{queries, pc.rot, pc.tables, pc.sketch, n_q, n_db, k, ns, sl, db.bits, db.stride, db.norms,
+                    db.sign, db.sign_stride, part_s, part_i, out_idx, out_score};
+  int rc = TQ_EUNSUPPORTED;
+#define TQ_PQ(DD, AA) \
+  if (pc.d == DD && pc.ab == AA) rc = launch_polar_search_da<DD, AA>(a, pc.m, g, st); else
+  TQ_PQ(64, 2) TQ_PQ(64, 3) TQ_PQ(64, 4) TQ_PQ(128, 2) TQ_PQ(128, 3) TQ_PQ(128, 4)
+  TQ_PQ(256, 2) TQ_PQ(256, 3) TQ_PQ(256, 4) {}
+#undef TQ_PQ
+  if (rc != TQ_OK) return rc;
+  if (ns > 1) return launch_topk_merge(part_s, part_i, n_q, ns, k, out_idx, out_score, stream);
+  return TQ_OK;
 }
 
 }  // namespace tq

@@ -26,14 +26,15 @@ struct QueryPrep {
   float wr[NWR], wsk[NWR];
   const float *R, *S;
 
-  __device__ __forceinline__ void issue(const float *q, const float *R_, const float *S_) {
+  // rows < G: only the first `rows` query rows are read, the others taken as zero
+  __device__ __forceinline__ void issue(const float *q, const float *R_, const float *S_, int rows = G) {
     R = R_;
     S = S_;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < QN; ++i) {
       const int e = tid + i * NT;
-      qv[i] = e < G * D ? q[e] : 0.0f;
+      qv[i] = e < rows * D ? q[e] : 0.0f;
     }
     if constexpr (REG) {
       const int r = tid / KSL, sl = tid % KSL;

@@ -17,6 +17,7 @@
 #include "tq_internal.h"
 #include "tq_lut.h"
 #include "tq_planes.h"
+#include "tq_topk.h"
 
 namespace tq {
 
@@ -41,59 +42,6 @@ struct SearchArgs {
   float *out_score;
   const uint8_t *limbs;  // search_planes: per query, its int8 limbs and constants (planes_limbs)
 };
-
-// a better than b: higher score, then smaller row
-__device__ __forceinline__ bool better(float as, int32_t ai, float bs, int32_t bi) {
-  return as > bs || (as == bs && ai < bi);
-}
-
-// Shift a value up by one lane across the wavefront (DPP wave_shr:1; lane 0 gets 0).
-__device__ __forceinline__ int32_t wave_shr1(int32_t x) {
-  return __builtin_amdgcn_update_dpp(0, x, 0x138, 0xF, 0xF, false);
-}
-
-// Insert the wave-uniform candidate (cs, ci) into the lane-distributed sorted list (ls, li)
-// of length k (lanes >= k are unused).
-__device__ __forceinline__ void list_insert(float &ls, int32_t &li, float cs, int32_t ci, int k) {
-  const int lane = lane_id();
-  const bool b = lane < k && better(ls, li, cs, ci);
-  const int pos = __popcll(__ballot(b));
-  if (pos >= k) return;
-  const float us = __int_as_float(wave_shr1(__float_as_int(ls)));
-  const int32_t ui = wave_shr1(li);
-  if (lane > pos) {
-    ls = us;
-    li = ui;
-  } else if (lane == pos) {
-    ls = cs;
-    li = ci;
-  }
-}
-
-// Insert the wave-uniform candidate (cs, ci) into the sorted list of length k held in LDS
-// (entry i at ls[i], li[i]); returns the list's k-th score afterwards.
-__device__ __forceinline__ float list_insert_lds(float *lsp, int32_t *lip, float cs, int32_t ci, int k) {
-  const int lane = lane_id();
-  float ls = lane < k ? lsp[lane] : -INFINITY;
-  int32_t li = lane < k ? lip[lane] : 0x7FFFFFFF;
-  const int pos = __popcll(__ballot(lane < k && better(ls, li, cs, ci)));
-  if (pos < k) {
-    const float us = __int_as_float(wave_shr1(__float_as_int(ls)));
-    const int32_t ui = wave_shr1(li);
-    if (lane > pos) {
-      ls = us;
-      li = ui;
-    } else if (lane == pos) {
-      ls = cs;
-      li = ci;
-    }
-    if (lane >= pos && lane < k) {
-      lsp[lane] = ls;
-      lip[lane] = li;
-    }
-  }
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), k - 1));
-}
 
 template <int D, int BITS, int M, int G, int NT>
 __global__ __launch_bounds__(NT) void search_scan(SearchArgs a) {
@@ -422,11 +370,23 @@ int launch_search(const CodecView &c, const float *queries, int64_t n_q, const C
   TQ_SR(64, 2, 64) TQ_SR(64, 3, 64) TQ_SR(128, 2, 128) TQ_SR(128, 3, 0) TQ_SR(200, 2, 200) TQ_SR(200, 3, 0) {}
 #undef TQ_SR
   if (rc != TQ_OK) return rc;
-  if (ns > 1) {
-    hipLaunchKernelGGL(search_merge, dim3((unsigned)((n_q + 3) / 4)), dim3(256), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return TQ_EHIP;
-  }
+  if (ns > 1) return launch_topk_merge(part_s, part_i, n_q, ns, k, out_idx, out_score, stream);
   return TQ_OK;
+}
+
+int launch_topk_merge(const float *part_s, const int32_t *part_i, int64_t n_q, int n_slices, int k,
+                      int64_t *out_idx, float *out_score, void *stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  SearchArgs a{};
+  a.n_q = n_q;
+  a.k = k;
+  a.n_slices = n_slices;
+  a.part_s = const_cast<float *>(part_s);
+  a.part_i = const_cast<int32_t *>(part_i);
+  a.out_idx = out_idx;
+  a.out_score = out_score;
+  hipLaunchKernelGGL(search_merge, dim3((unsigned)((n_q + 3) / 4)), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 
 }  // namespace tq
