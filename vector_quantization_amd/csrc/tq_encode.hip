@@ -877,6 +877,7 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
     if constexpr (M > 0) {
       constexpr int NB = M / 32;  // sign bytes per lane per tile: sketch rows 32b + 8g + 0..7
       float tau[NV];
+      double rbound[NV];
 #pragma unroll
       for (int t = 0; t < NV; ++t) {
         // A tiny r (products near the fp32 underflow) leaves every sign to the fp64 path,
@@ -894,6 +895,10 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
           zero = rmax == 0.0f;
         }
         tau[t] = zero ? -1.0f : (tiny ? INFINITY : 0x1p-13f * smax * (float)sqrt(rn2[t]));
+        // an upper bound on smax ||r|| for the fp64 test: rn2 is the sum of squares within
+        // relative 2^-19 (fp32 partial sums of 8 squares; squares below the fp32 range add at
+        // most 2^-19 of a sum >= 1e-30); a tiny r leaves every undecided row to the expansion
+        rbound[t] = tiny ? INFINITY : (double)smax * sqrt(rn2[t]) * (1.0 + 0x1p-16);
       }
       uint32_t sb[NV][NB];
       // one 16-vector tile at a time: z for every sketch tile, r split into bf16 hi/lo one
@@ -926,14 +931,13 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           uint32_t neg = 0u, amb = 0u;
+          // rows 4h + i from the top down: each step shifts one bit in
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float zz = z[b][h][i];
-              neg |= (__float_as_uint(zz) >> 31) << (4 * h + i);
-              amb |= (fabsf(zz) <= tau[t] ? 1u : 0u) << (4 * h + i);
-            }
+          for (int k = 7; k >= 0; --k) {
+            const float zz = z[b][k >> 2][k & 3];
+            neg = __builtin_amdgcn_alignbit(neg, __float_as_uint(zz), 31);
+            amb = 2u * amb + (fabsf(zz) <= tau[t] ? 1u : 0u);
+          }
           sb[t][b] = neg ^ 0xFFu;
           am[b] = amb;
         }
@@ -949,7 +953,7 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
           q = min(q, __shfl_xor(q, 32, kWave));
           if (__ballot(q != 0xFF) == 0) break;
           const bool act = q != 0xFF;
-          double ps = 0.0, pa = 0.0;
+          double ps = 0.0;
           if (act) {
 #pragma unroll
             for (int u = 0; u < KS; ++u) {
@@ -957,18 +961,15 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
               const float4 s0 = srow[0], s1 = srow[1];
               const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                const double pr = (double)sv[j] * (double)opaque(yv[t][u][j]);
-                ps += pr;
-                pa += fabs(pr);
-              }
+              for (int j = 0; j < 8; ++j) ps = fma((double)sv[j], (double)opaque(yv[t][u][j]), ps);
             }
           }
           ps += __shfl_xor(ps, 16, kWave);
           ps += __shfl_xor(ps, 32, kWave);
-          pa += __shfl_xor(pa, 16, kWave);
-          pa += __shfl_xor(pa, 32, kWave);
-          const bool dec = fabs(ps) > 2.0 * (D + 2) * 0x1p-53 * pa;
+          // D/4 fused steps per lane and two exchanges, each rounding once: error <= (D/4 + 2)
+          // 2^-53 sum_k |S_qk r_k| <= (D/4 + 2) 2^-53 ||S_q|| ||r||, with smax >= ||S_q|| and
+          // rbound >= ||r|| (the test below allows 2 (D + 2) 2^-53 of it)
+          const bool dec = fabs(ps) > 2.0 * (D + 2) * 0x1p-53 * rbound[t];
           int sg = ps > 0.0 ? 1 : -1;
           // where even fp64 cannot decide: the exact expansion, one vector at a time
           uint64_t und = __ballot(act && !dec && g == 0);
