@@ -650,6 +650,14 @@ def polar_main(a):
         "attend_ms": round(t_att, 4),
         "attend_note": f"polar keys + {w.v_bits}-bit values: tq_polar_scores into the workspace, then the value pass",
         "quality_layer0_batch0": comp,
+        "score_traffic_twin": None if twin is None else {
+            "ms": round(twin[0], 4), "scores_ms_same_run": round(twin[1], 4),
+            "GBps": round(score_bytes / (twin[0] * 1e-3) / 1e9, 1),
+            "scores_frac_of_twin": round(twin[0] / twin[1], 4),
+            "kernel": "score_traffic (lib/libtq_traffic.so): the score stream's grid, loads and logit "
+                      "stores with no table work",
+            "note": "the practical HBM ceiling of the score stream's own access pattern; medians of "
+                    "alternating calls"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": f"tq::polar_score_kernel<{w.d}, {ab}, 4, 256> (one tq_polar_scores call)"},
@@ -792,6 +800,8 @@ def kv_line(a, w, seed, cpu):
     t_sc = float(np.median(sc_ms))
     t_at = float(np.median(at_ms)) if do_attend else None
     ms_step = wall * 1e3 / a.steps
+    twin = score_traffic_twin(w, kc, kcodes, logits, stream, lambda: tq.scores(kc, qf, kcodes, w.n_ctx, w.hkv,
+                                                                                 logits=logits))
 
     keys = w.n_seq * w.hkv * w.n_ctx
     code_b_k = (w.d * w.k_bits + 7) // 8 + (w.k_m + 7) // 8 + 4
@@ -819,7 +829,7 @@ def kv_line(a, w, seed, cpu):
         "vs_baseline": None,
         "dtype": "f32",
         "dtype_note": ("fp32 queries and accumulation; with 4 query heads per kv head the lookup entries are "
-                       "16-bit fixed point, and a chunk whose error bound is not below 5e-4 of its largest "
+                       "16-bit fixed point, and a chunk whose error bound is not below 8e-4 of its largest "
                        "|logit| is scored again with fp32 entries"),
         "data": "synthetic (seeded bf16 K/V, N(0,1) with 2% channels x10; fp32 queries)",
         "config": {
@@ -852,6 +862,14 @@ def kv_line(a, w, seed, cpu):
                                 "the sketch).  busy_frac: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x "
                                 "1024 SIMDs) from the committed counter summary (null when the encoder "
                                 "changed since)"},
+        "score_traffic_twin": None if twin is None else {
+            "ms": round(twin[0], 4), "scores_ms_same_run": round(twin[1], 4),
+            "GBps": round(score_bytes / (twin[0] * 1e-3) / 1e9, 1),
+            "scores_frac_of_twin": round(twin[0] / twin[1], 4),
+            "kernel": "score_traffic (lib/libtq_traffic.so): the score stream's grid, loads and logit "
+                      "stores with no table work",
+            "note": "the practical HBM ceiling of the score stream's own access pattern; medians of "
+                    "alternating calls"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(SCORE_KERNELS) if w.name == "gqa8b_decode_b8_32k" else None,
@@ -866,6 +884,47 @@ def kv_line(a, w, seed, cpu):
     del K, V, q, kcodes, vcodes, logits, Kf, Vf
     torch.cuda.empty_cache()
     return res, host
+
+
+def score_traffic_twin(w, kc, kcodes, logits, stream, scores_call, reps=10):
+    """Median times of the traffic twin of the score stream and of the score call itself,
+    alternating on the same codes and logits (ms, ms); None where the twin does not apply."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    import vector_quantization_amd as tq
+
+    path = os.path.join(os.path.dirname(tq.LIB_PATH), "libtq_traffic.so")
+    if not (os.path.exists(path) and kc.d == 128 and kc.bits == 2 and kc.m == 128 and w.hq == 4 * w.hkv):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.tq_traffic_score_twin.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tq_traffic_score_twin.restype = ctypes.c_int
+    st = ctypes.c_void_p(stream.cuda_stream)
+
+    def twin():
+        rc = lib.tq_traffic_score_twin(kcodes.idx.data_ptr(), kcodes.idx.shape[1], kcodes.sign.data_ptr(),
+                                       kcodes.sign.shape[1], kcodes.norms.data_ptr(), w.n_seq, w.hq, w.hkv,
+                                       w.n_ctx, logits.data_ptr(), st)
+        if rc != 0:
+            raise RuntimeError(f"traffic twin launch: {rc}")
+
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tw, sc = [], []
+    for i in range(reps + 2):
+        e[0].record(stream)
+        twin()
+        e[1].record(stream)
+        scores_call()
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            tw.append(e[0].elapsed_time(e[1]))
+            sc.append(e[1].elapsed_time(e[2]))
+    return float(np.median(tw)), float(np.median(sc))
 
 
 class _Slices:

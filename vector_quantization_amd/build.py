@@ -1,7 +1,8 @@
 """Build libtq.so for gfx950 in-tree with hipcc (one object per source, compiled in parallel).
 
 Usage: python -m vector_quantization_amd.build [--jobs N] [--verbose]
-The library lands in vector_quantization_amd/lib/libtq.so.
+The library lands in vector_quantization_amd/lib/libtq.so (and bench.py's measurement aid in
+lib/libtq_traffic.so).
 """
 
 import argparse
@@ -16,6 +17,9 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "lib")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libtq.so")
+# measurement aid for bench.py (csrc/probe): the score stream's traffic without its arithmetic
+TRAFFIC_SRC = os.path.join(CSRC, "probe", "tq_traffic.hip")
+TRAFFIC_LIB = os.path.join(OUT_DIR, "libtq_traffic.so")
 
 ARCH = "gfx950"
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -65,6 +69,12 @@ def build(jobs=None, verbose=False):
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
     os.replace(tmp, LIB)
+    tmp = TRAFFIC_LIB + ".tmp"
+    cmd = [HIPCC] + COMMON + DEVICE + ["-shared", "-x", "hip", TRAFFIC_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on the traffic probe:\n" + r.stderr)
+    os.replace(tmp, TRAFFIC_LIB)
     return LIB
 
 

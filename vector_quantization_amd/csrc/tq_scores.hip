@@ -370,9 +370,10 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
     // Error guard of the 16-bit tables.  A key's logit misses the exact table sums by at most
     // E = nbar Em + rq Eq (i16_error_units), so every logit of the chunk is within
     // Emax = nmax Em + rmax Eq of its fp32-table value.  The row's largest |logit| is at least
-    // the chunk's, so Emax <= tau (max |logit| - Emax) with tau = 5e-4 keeps the chunk's errors
-    // within half the 1e-3 row-relative tolerance; a head of the chunk that fails it (a short
-    // row, or a query nearly orthogonal to every key) is scored again with fp32 tables.
+    // the chunk's, so Emax <= tau (max |logit| - Emax) with tau = 8e-4 keeps the chunk's errors
+    // within 8e-4 of the row's largest |logit| (the fp32 parts add below 1e-5 of it, inside the
+    // 1e-3 row-relative tolerance); a head of the chunk that fails it (a short row, or a query
+    // nearly orthogonal to every key) is scored again with fp32 tables.
     float *red = reinterpret_cast<float *>(tabs);  // [NT / kWave][G + 2], after the barrier below
     constexpr int NW = NT / kWave;
 #pragma unroll
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
       float em, eq;
       i16_error_units<D, BITS, M>(hs.inv_m[h], hs.inv_q[h], em, eq);
       const float emax = mx[G] * em + mx[G + 1] * eq;
-      if (!(emax <= 5e-4f * (mx[h] - emax))) redo |= 1u << h;
+      if (!(emax <= 8e-4f * (mx[h] - emax))) redo |= 1u << h;
     }
     __syncthreads();  // every thread has read red (it aliases the tables rebuilt below)
     if (redo != 0u) {  // uniform: every thread computed it from the same LDS values
