@@ -196,6 +196,7 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   // final merge, so wavefronts in the lookup phase overlap wavefronts in the value phase.
   Rec cur;
   load_rec(t0 + (int64_t)wid * kWave + lane, cur);
+  const uint8_t *qjl_tabs = tabs + opaque_offset(CK::MSE_BYTES);
   for (int64_t tile = t0 + (int64_t)wid * kWave; tile < t1; tile += (int64_t)NW * kWave) {
     // ---- phase A: one token per lane: logits, value records to the wavefront's tile
     const int64_t t = tile + lane;
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
         for (int h = 0; h < G; ++h) lg[h] = a.lg_in[(qrow + h) * a.n_ctx + t] * a.scale_log2;
       } else {
         float am[G], aq[G];
-        lut_score<D, KB, KM, G>(cur.iw, cur.sw, tabs, tabs + CK::MSE_BYTES, hs, am, aq);
+        lut_score<D, KB, KM, G>(cur.iw, cur.sw, tabs, qjl_tabs, hs, am, aq);
         const float nbar = f16_bits_to_float(cur.nw & 0xFFFFu);
         const float rq = f16_bits_to_float(cur.nw >> 16) * kappa_k;
 #pragma unroll

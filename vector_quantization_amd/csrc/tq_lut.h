@@ -286,11 +286,21 @@ __device__ void block_table_scales(const float *qt, const float *qh, const float
     }
   }
   __syncthreads();
+  // block-uniform: read into scalar registers, which keeps them out of the key loops' VGPRs
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    hs.inv_m[h] = sc[2 * G + h];
-    hs.inv_q[h] = sc[3 * G + h];
+    hs.inv_m[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc[2 * G + h])));
+    hs.inv_q[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc[3 * G + h])));
   }
+}
+
+// A block-uniform byte offset the compiler cannot treat as a constant.  The sign tables start at
+// the index tables' size, 64 KB for 2-bit keys at d = 128: with a constant base every sign
+// group's address (beyond the 16-bit immediate offset of an LDS read) would take a register of
+// its own; with this one base register each group's offset fits the reads' immediate field.
+__device__ __forceinline__ int opaque_offset(int off) {
+  asm volatile("" : "+s"(off));
+  return off;
 }
 
 // acc[h] += entry[h] for fp32 tables (G = 1, 2); iacc[h] += entry[h] for 16-bit tables

@@ -335,6 +335,7 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
   __syncthreads();
 
   const float kappa = M > 0 ? 1.2533141373155003f / (float)(M > 0 ? M : 1) : 0.0f;  // sqrt(pi/2)/m
+  const uint8_t *qjl_tabs = tabs + opaque_offset(C::MSE_BYTES);
   const int64_t t0 = (int64_t)chunk * a.chunk;
   int64_t t1 = t0 + a.chunk;
   if (t1 > a.n_keys) t1 = a.n_keys;
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs a) {
     if constexpr (M > 0) load_words<C::SW>(a.sign + v * a.sign_stride, sw);
     const uint32_t nw = a.norms[v];
     float am[G], aq[G];
-    lut_score<D, BITS, M, G>(iw, sw, tabs, tabs + C::MSE_BYTES, hs, am, aq);
+    lut_score<D, BITS, M, G>(iw, sw, tabs, qjl_tabs, hs, am, aq);
     const float nbar = f16_bits_to_float(nw & 0xFFFFu);
     const float rq = f16_bits_to_float(nw >> 16) * kappa;
 #pragma unroll

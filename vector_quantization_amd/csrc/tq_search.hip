@@ -78,6 +78,7 @@ __global__ __launch_bounds__(NT) void search_scan(SearchArgs a) {
 
   const int k = a.k;
   const float kappa = M > 0 ? 1.2533141373155003f / (float)(M > 0 ? M : 1) : 0.0f;
+  const uint8_t *qjl_tabs = tabs + opaque_offset(C::MSE_BYTES);
   float ls[G];
   int32_t li[G];
   float tau[G];
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(NT) void search_scan(SearchArgs a) {
       if constexpr (M > 0) load_words<C::SW>(a.sign + v * a.sign_stride, sw);
       const uint32_t nw = a.norms[v];
       float am[G], aq[G];
-      lut_score<D, BITS, M, G>(iw, sw, tabs, tabs + C::MSE_BYTES, hs, am, aq);
+      lut_score<D, BITS, M, G>(iw, sw, tabs, qjl_tabs, hs, am, aq);
       const float nbar = f16_bits_to_float(nw & 0xFFFFu);
       const float rq = f16_bits_to_float(nw >> 16) * kappa;
 #pragma unroll
