@@ -125,6 +125,11 @@ def encode_counters():
 def gpu_clocks():
     """Current clocks as rocm-smi reports them (sclk, mclk, fclk ...) for GPU 0, or None."""
     import subprocess
+
+    # under a profiler every child process is instrumented too; rocm-smi (a script that starts
+    # its interpreter through env) is then better left out
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
         data = json.loads(r.stdout)
