@@ -637,6 +637,60 @@ def polar_main(a):
                                                                      scale))
         comp[f"{tq.polar_record_bytes(w.d, abits) + 4}B_per_key"] = {
             f"polar_ab{abits}": pq, f"two_stage_{bits_}bit_qjl{w.d}": tqq}
+    # the QJL stage on the polar residual (m = d, 48 + 16 + 4 = 68 B per key) over every layer:
+    # the residual stage runs in the one-wavefront-per-vector encoder (timed once)
+    pcq = tq.make_polar_codec(w.d, ab, synth.SEED_ROT_K, m=w.d, sketch_seed=synth.SEED_SKETCH_K)
+    n0 = w.batch * w.hkv * w.n_ctx
+    k_l0 = K[0].reshape(-1, w.d)
+    qcodes = tq.alloc_polar_codes(pcq, n_vec)
+    tq.polar_encode(pcq, k_l0, out=qcodes.slice(0, n0))
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    tq.polar_encode(pcq, Kf, out=qcodes)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t_qenc = ev[0].elapsed_time(ev[1])
+    qt = []
+    for i in range(a.warmup + a.steps):
+        ev[0].record(stream)
+        tq.polar_scores(pcq, qf, qcodes, w.n_ctx, w.hkv, logits=logits)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if i >= a.warmup:
+            qt.append(ev[0].elapsed_time(ev[1]))
+    t_qsc = float(np.median(qt))
+    qrec_b = tq.polar_record_bytes(w.d, ab) + w.d // 8 + 4
+    q_score_bytes = keys * qrec_b + w.n_seq * w.hq * w.n_ctx * 4 + q_bytes
+    qjl_line = {"record_bytes": qrec_b, "encode_ms": round(t_qenc, 2),
+                "encode_vectors_per_s": round(n_vec / (t_qenc * 1e-3)),
+                "scores_ms": round(t_qsc, 4), "scores_GBps": round(q_score_bytes / (t_qsc * 1e-3) / 1e9, 1),
+                "scores_hbm_frac": round(q_score_bytes / (t_qsc * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "keys_per_s": keys / (t_qsc * 1e-3)}
+    # search over polar records: the layer-0 keys (2.1M, d = 128) as a database, 1024 queries,
+    # top-10, recall@10 against exact fp32 search
+    n_qs = 1024
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(41)
+    qs = torch.randn((n_qs, w.d), generator=gq, device="cuda")
+    db = codes.slice(0, n0)
+    tq.polar_search_topk(pc, qs, db, n0, 10)
+    torch.cuda.synchronize()
+    st_ = []
+    for _ in range(3):
+        ev[0].record(stream)
+        idx, _sc = tq.polar_search_topk(pc, qs, db, n0, 10)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        st_.append(ev[0].elapsed_time(ev[1]))
+    t_srch = float(np.median(st_))
+    exact_top = torch.topk(qs @ k_l0.float().T, 10, dim=1).indices
+    rec10 = float(np.mean([len(set(a_.tolist()) & set(b_.tolist())) / 10.0
+                           for a_, b_ in zip(idx.cpu(), exact_top.cpu())]))
+    search_line_p = {"database": f"layer-0 keys, {n0} x {w.d}, polar ab = {ab} ({rec_b} B per record)",
+                     "queries": n_qs, "k": 10, "ms": round(t_srch, 3),
+                     "pairs_per_s": n_qs * n0 / (t_srch * 1e-3), "recall_at_10_vs_exact_fp32": round(rec10, 4)}
+    comp.setdefault(f"{qrec_b}B_per_key", {})[f"polar_ab{ab}_qjl{w.d}"] = quality(
+        tq.polar_scores(pcq, qs0, qcodes.slice(0, w.hkv * w.n_ctx), w.n_ctx, w.hkv))
     torch.cuda.synchronize()
     res = {
         "metric": "recursive-polar decode scoring GB/s (% HBM peak) + keys/s",
@@ -655,14 +709,8 @@ def polar_main(a):
         "attend_ms": round(t_att, 4),
         "attend_note": f"polar keys + {w.v_bits}-bit values: tq_polar_scores into the workspace, then the value pass",
         "quality_layer0_batch0": comp,
-        "score_traffic_twin": None if twin is None else {
-            "ms": round(twin[0], 4), "scores_ms_same_run": round(twin[1], 4),
-            "GBps": round(score_bytes / (twin[0] * 1e-3) / 1e9, 1),
-            "scores_frac_of_twin": round(twin[0] / twin[1], 4),
-            "kernel": "score_traffic (lib/libtq_traffic.so): the score stream's grid, loads and logit "
-                      "stores with no table work",
-            "note": "the practical HBM ceiling of the score stream's own access pattern; medians of "
-                    "alternating calls"},
+        "polar_qjl": qjl_line,
+        "polar_search": search_line_p,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": f"tq::polar_score_kernel<{w.d}, {ab}, 4, 256> (one tq_polar_scores call)"},

@@ -450,8 +450,9 @@ def test_attention_with_polar_keys_argument_errors():
 def _qjl_score_tol(lib, ora, q, norms, n_keys, hkv):
     """Bound on the QJL term's error, per logit: the sketched query S q~ in fp32 is off by at most
     2^-24 (d + 1) sum_k |S_jk| (|q~_k| + sum_i |Pi_ki| |q_i|) per row (its own fp32 sum plus the
-    rotated query's), each byte table entry sums 8 of them and each logit 16 entries (24 more
-    roundings of sum_j |S q~|_j), and the fma with rnbar sqrt(pi/2)/m rounds once more."""
+    rotated query's), each table entry sums 4 of them and each logit m/4 entries (m/4 + 3 more
+    roundings of sum_j |S q~|_j, taken as m/4 + 8), and the fma with rnbar sqrt(pi/2)/m rounds
+    once more."""
     n_seq, hq, d = q.shape
     G = hq // hkv
     S = np.abs(ora.sketch.astype(np.float64))
@@ -464,7 +465,7 @@ def _qjl_score_tol(lib, ora, q, norms, n_keys, hkv):
             qq = q[s_, h * G:(h + 1) * G].astype(np.float64)
             qt = qq @ P.T
             base = (np.abs(qt) + np.abs(qq) @ np.abs(P).T) @ S.T  # [G, m]
-            e = 2.0 ** -24 * ((d + 1) * base.sum(-1) + 26 * np.abs(qt @ ora.sketch.astype(np.float64).T).sum(-1))
+            e = 2.0 ** -24 * ((d + 1) * base.sum(-1) + (ora.m // 4 + 8) * np.abs(qt @ ora.sketch.astype(np.float64).T).sum(-1))
             tol[s_, h * G:(h + 1) * G] = e[:, None] * rq[blk * n_keys:(blk + 1) * n_keys][None, :]
     return tol
 
@@ -558,7 +559,7 @@ def test_qjl_scores_match_oracle(d, ab, n_seq, hq, hkv, n_keys):
 
 
 def test_qjl_scores_random_records_and_rotations():
-    # uniform bits reach every polar field value and every sign byte of every position;
+    # uniform bits reach every polar field value and every sign group value of every position;
     # per-block rotations
     d, ab, n_seq, hq, hkv, n_keys = 64, 3, 2, 4, 2, 400
     lib, ora = _codecs(d, ab, basis=[900 + i for i in range(n_seq * hkv)], vpr=n_keys, m=d)

@@ -653,6 +653,9 @@ class PolarCodes:
     def n(self) -> int:
         return int(self.bits.shape[0])
 
+    def slice(self, a: int, b: int) -> "PolarCodes":
+        return PolarCodes(self.bits[a:b], self.norms[a:b], None if self.sign is None else self.sign[a:b])
+
     def numpy(self):
         """(bits uint8, norms uint32), and sign uint8 as a third item when the codes have one."""
         out = (self.bits.cpu().numpy(), self.norms.cpu().numpy().view(np.uint32))

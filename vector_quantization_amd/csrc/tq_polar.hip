@@ -28,8 +28,9 @@
 // field the leaf term (+-cos psi^ q_2j +- sin psi^ q_2j+1) of each head, G floats per (j, f).  A
 // key's logit is nbar sum_j r_j T[j][f_j], with r_j the product of the node cos/sin factors on
 // the path to pair j, expanded from the root down in registers (one thread per key).  With the
-// QJL stage, byte tables U_p[beta] = sum_t q^_8p+t (2 bit_t(beta) - 1) of the sketched query add
-// rnbar sqrt(pi/2)/m sum_p U_p[sign byte p].
+// QJL stage, tables of 4-bit sign groups U_p[beta] = sum_t q^_4p+t (2 bit_t(beta) - 1) of the
+// sketched query add rnbar sqrt(pi/2)/m sum_p U_p[sign nibble p] (16 entries per group keep four
+// heads' tables small enough for several workgroups per CU).
 // polar_search_scan: the same tables for G queries of a search, one workgroup per (query group,
 // database slice), a top-k list per wave and query as in the two-stage search.
 
@@ -352,7 +353,11 @@ struct PolarScoreArgs {
 };
 
 // Logits of record v for G query heads from the LDS tables (layouts as polar_score_kernel's):
-// nbar sum_j r_j T[j][f_j], plus rnbar sqrt(pi/2)/m sum_p U_p[sign byte p] with the QJL stage.
+// nbar sum_j r_j T[j][f_j], plus rnbar sqrt(pi/2)/m sum_p U_p[sign nibble p] with the QJL stage.
+// sign bits per lookup of the QJL term's tables, and entries per table
+constexpr int kPolarSB = 4;
+constexpr int kPolarSE = 1 << kPolarSB;
+
 template <int D, int AB, int M, int G>
 __device__ __forceinline__ void polar_record_logits(const uint8_t *bits, int64_t stride, const uint32_t *norms,
                                                     const uint8_t *sign, int64_t sign_stride, int64_t v,
@@ -402,7 +407,8 @@ __device__ __forceinline__ void polar_record_logits(const uint8_t *bits, int64_t
   }
   const float nbar = f16_bits_to_float(nw & 0xFFFFu);
   if constexpr (M > 0) {
-    constexpr int NQ = M / 8;
+    constexpr int NQ = M / kPolarSB;
+    constexpr int PW = 32 / kPolarSB;  // groups per sign word
     constexpr int SW = (M + 31) / 32;
     uint32_t sw[SW];
     load_words<SW>(sign + v * sign_stride, sw);
@@ -411,10 +417,21 @@ __device__ __forceinline__ void polar_record_logits(const uint8_t *bits, int64_t
     for (int g = 0; g < G; ++g) aq[g] = 0.0f;
 #pragma unroll
     for (int p = 0; p < NQ; ++p) {
-      const int byte = (sw[p >> 2] >> (8 * (p & 3))) & 0xFF;
-      const float *e = qlut + (p * 256 + byte) * G;
+      const int code = (sw[p / PW] >> (kPolarSB * (p % PW))) & (kPolarSE - 1);
+      const float *e = qlut + (p * kPolarSE + code) * G;
+      if constexpr (G % 4 == 0) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) aq[g] += e[g];
+        for (int g = 0; g < G; g += 4) {
+          const float4 tv = *reinterpret_cast<const float4 *>(e + g);
+          aq[g] += tv.x;
+          aq[g + 1] += tv.y;
+          aq[g + 2] += tv.z;
+          aq[g + 3] += tv.w;
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) aq[g] += e[g];
+      }
     }
     const float rq = f16_bits_to_float(nw >> 16) * (1.2533141373155003f / (float)(M > 0 ? M : 1));
 #pragma unroll
@@ -433,12 +450,12 @@ __device__ void build_polar_tables(float *lut, float *qlut, const float2 (*cs)[P
                                    const float *qt, const float *qh) {
   using P = PolarLayout<D, AB>;
   if constexpr (M > 0) {
-    for (int e = threadIdx.x; e < (M / 8) * 256 * G; e += NT) {
-      const int g = e % G, beta = (e / G) & 255, p = e / (G * 256);
+    for (int e = threadIdx.x; e < (M / kPolarSB) * kPolarSE * G; e += NT) {
+      const int g = e % G, beta = (e / G) % kPolarSE, p = e / (G * kPolarSE);
       float acc = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float y = qh[g * M + 8 * p + t];
+      for (int t = 0; t < kPolarSB; ++t) {
+        const float y = qh[g * M + kPolarSB * p + t];
         acc += ((beta >> t) & 1) ? y : -y;
       }
       qlut[e] = acc;
@@ -453,19 +470,19 @@ __device__ void build_polar_tables(float *lut, float *qlut, const float2 (*cs)[P
   __syncthreads();
 }
 
-// LDS tables of G heads: the leaf terms, and with the QJL stage the sign-byte tables
-// U_p[beta] = sum_t q^_{8p+t} (2 bit_t(beta) - 1), G floats per entry
+// LDS tables of G heads: the leaf terms, and with the QJL stage the sign-group tables
+// U_p[beta] = sum_t q^_{4p+t} (2 bit_t(beta) - 1), G floats per entry
 template <int D, int AB, int M, int G>
 constexpr int polar_lut_bytes() {
-  return PolarLayout<D, AB>::NP * PolarLayout<D, AB>::NF * G * 4 + (M / 8) * 256 * G * 4;
+  return PolarLayout<D, AB>::NP * PolarLayout<D, AB>::NF * G * 4 + (M / kPolarSB) * kPolarSE * G * 4;
 }
 
 template <int D, int AB, int M, int G, int NT>
 __global__ __launch_bounds__(NT) void polar_score_kernel(PolarScoreArgs a) {
   using P = PolarLayout<D, AB>;
-  constexpr int NQ = M / 8;
+  constexpr int NQ = M / kPolarSB;
   __shared__ __align__(16) float lut[P::NP * P::NF * G];
-  __shared__ __align__(16) float qlut[M > 0 ? NQ * 256 * G : 4];
+  __shared__ __align__(16) float qlut[M > 0 ? NQ * kPolarSE * G : 4];
   __shared__ float2 cs[P::LV][P::NA];
   __shared__ float qs[G * D];
   __shared__ float qt[G * D];
@@ -590,7 +607,7 @@ __global__ __launch_bounds__(NT) void polar_search_scan(PolarSearchArgs a) {
   constexpr int NW = NT / kWave;
   static_assert(NW >= G, "one wave per query merges the lists");
   __shared__ __align__(16) float lut[P::NP * P::NF * G];
-  __shared__ __align__(16) float qlut[M > 0 ? (M / 8) * 256 * G : 4];
+  __shared__ __align__(16) float qlut[M > 0 ? (M / kPolarSB) * kPolarSE * G : 4];
   __shared__ float2 cs[P::LV][P::NA];
   __shared__ float qs[G * D];
   __shared__ float qt[G * D];
@@ -672,7 +689,7 @@ __global__ __launch_bounds__(NT) void polar_search_scan(PolarSearchArgs a) {
 
 // queries per workgroup: the largest of 4, 2, 1 whose tables fit 64 KiB
 static int polar_search_group(const PolarView &pc) {
-  const int64_t per = (int64_t)(pc.d / 2) * (1 << (2 + pc.ab)) * 4 + (int64_t)(pc.m / 8) * 256 * 4;
+  const int64_t per = (int64_t)(pc.d / 2) * (1 << (2 + pc.ab)) * 4 + (int64_t)(pc.m / kPolarSB) * kPolarSE * 4;
   for (int g = 4; g > 1; g /= 2)
     if (per * g <= 64 * 1024) return g;
   return 1;
