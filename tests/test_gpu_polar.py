@@ -784,3 +784,53 @@ def test_polar_search_errors():
         tq.polar_search_topk(lib1, q, db, 20, 21)  # k > n_db
     assert tq.lib.tq_polar_search_topk(tq.ctypes.byref(cc1), tq._ptr(q), 2, db.c(), 20, 33, tq._ptr(i), tq._ptr(s),
                                        None, 0, tq._stream()) == -1  # k > 32
+
+
+@pytest.mark.parametrize("d,dtype,first", [(128, "bfloat16", 64), (64, "float32", 64), (64, "float16", 40)])
+def test_qjl_full_mode_rotation_blocks(d, dtype, first):
+    # per-block rotations with the QJL stage: the MFMA encoder's block loop (offsets that are
+    # multiples of 32; bf16 at d = 128) and the FMA kernel (offset 40); fields, rn16 and signs
+    # explained by the rotation bound as in the single-rotation case
+    ab, n_rot, vpr = 2, 24, 32
+    lib, ora = _codecs(d, ab, basis=[800 + i for i in range(n_rot)], vpr=vpr, m=d)
+    n = n_rot * vpr - first + 40
+    x = (np.random.default_rng(d + first).standard_normal((n, d)) * 3.0).astype(np.float32)
+    tdt = getattr(torch, dtype)
+    x_seen = torch.from_numpy(x).to(tdt).to(torch.float32).numpy()
+    bits, norms, ytap, sign = _gpu_encode(lib, x, pre=False, dtype=tdt, first=first, tap=True)
+    y_ex, bound = _exact_rotation(x_seen.astype(np.float64), ora, ora.rot_index(n, first))
+    assert np.all(np.abs(ytap.astype(np.float64) - y_ex) <= bound)
+    want = op.encode(x_seen, ora, first=first, stride=lib.stride, sign_stride=lib.sign_stride)
+    assert np.array_equal(norms & 0xFFFF, want.norms & 0xFFFF)
+    dy = np.abs(ytap.astype(np.float64) - want.extra["y"].astype(np.float64))
+    same = _explain_fields(bits, norms, want, dy, ora, 0.02)
+    assert _explain_qjl(norms, sign, want, dy, same, ora) <= max(1, int(0.02 * n))
+
+
+def test_qjl_full_size_sampled():
+    # the 8B decode shape's 2.1M bf16 keys (one layer) encoded with the QJL stage in one call (the
+    # MFMA encoder's multi-pass loop): norm words' low halves on 65536 sampled keys, and the
+    # records, rn16 and signs of 2048 sampled keys explained against the oracle with the bound
+    # taken from the exact fp64 rotation (no y tap)
+    w = synth.GQA_DECODE
+    d, ab = w.d, 2
+    lib, ora = _codecs(d, ab, m=d)
+    n = w.batch * w.hkv * w.n_ctx
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(13)
+    K = torch.randn((n, d), generator=gen, device="cuda", dtype=torch.bfloat16)
+    codes = tq.polar_encode(lib, K)
+    torch.cuda.synchronize()
+    x_seen = K.float().cpu().numpy()
+    g = np.random.default_rng(14)
+    rows = np.sort(g.choice(n, 65536, replace=False))
+    nw = codes.norms.cpu().numpy().view(np.uint32)
+    assert np.array_equal(nw[rows] & 0xFFFF, oq.f16_norm_bits(x_seen[rows]))
+    sub = np.sort(g.choice(n, 2048, replace=False))
+    y_ex, bound = _exact_rotation(x_seen[sub].astype(np.float64), ora, ora.rot_index(len(sub)))
+    want = op.encode(x_seen[sub], ora, stride=lib.stride, sign_stride=lib.sign_stride)
+    dy = bound + np.abs(want.extra["y"].astype(np.float64) - y_ex)
+    bits = codes.bits.cpu().numpy()[sub]
+    sign = codes.sign.cpu().numpy()[sub]
+    same = _explain_fields(bits, nw[sub], want, dy, ora, 0.02)
+    assert _explain_qjl(nw[sub], sign, want, dy, same, ora) <= max(1, int(0.02 * len(sub)))

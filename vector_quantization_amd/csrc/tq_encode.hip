@@ -416,9 +416,14 @@ struct PolarLevelTh {
   }
 };
 
-template <int D, int AB, int NV, int KS>
-__device__ void polar_tail(const float (&yv)[NV][KS][8], const uint32_t (&n16)[NV], int64_t v0, const EncArgs &a,
-                           uint32_t *stg, const float *ptab) {
+// QJL: the records are followed by the stage-1 residual on the lane's own coordinates, which
+// replaces yv: u^ from the root down (fp32 products in the order of the decoder: a node's value
+// times its level's cos or sin, the children of the lane's own nodes only), r = fl32(y -
+// fl32(nbar u^)); the norm words are then left to the caller.  pcs: cos and sin of every
+// level, [level][2][2^AB].
+template <int D, int AB, int NV, int KS, bool QJL>
+__device__ void polar_tail(float (&yv)[NV][KS][8], const uint32_t (&n16)[NV], int64_t v0, const EncArgs &a,
+                           uint32_t *stg, const float *ptab, const float *pcs) {
   constexpr int NA = 1 << AB, WP = 2 + AB, NP = D / 2, P0 = NP * WP;
   constexpr int NWD = (P0 + (NP - 1) * AB + 31) / 32;  // record words
   constexpr int LV = log2_d<D>();
@@ -434,6 +439,7 @@ __device__ void polar_tail(const float (&yv)[NV][KS][8], const uint32_t (&n16)[N
     uint32_t *rec = stg + n * NWD;
     // level 1: pairs 16u + 4g + p (p < 4), one run of 4 fields per octet
     float s1[KS][4];
+    uint32_t f1[KS][4], k2s[KS][2], k3s[KS], k4s[KS], k5s[KS], khs[LV + 1][(D >> 6) > 0 ? (D >> 6) : 1];
     {
       PolarLevelTh<NA> th;
       th.load(ptab, 0);
@@ -445,6 +451,7 @@ __device__ void polar_tail(const float (&yv)[NV][KS][8], const uint32_t (&n16)[N
           const float ya = yv[t][u][2 * p], yb = yv[t][u][2 * p + 1];
           const float A = __fmul_rn(ya, ya), B = __fmul_rn(yb, yb);
           const uint32_t f = (ya < 0.0f ? 1u : 0u) | (yb < 0.0f ? 2u : 0u) | (th.decide(A, B) << 2);
+          f1[u][p] = f;
           run |= f << (WP * p);
           s1[u][p] = __fadd_rn(A, B);
         }
@@ -459,6 +466,8 @@ __device__ void polar_tail(const float (&yv)[NV][KS][8], const uint32_t (&n16)[N
 #pragma unroll
       for (int u = 0; u < KS; ++u) {
         const uint32_t k0 = th.decide(s1[u][0], s1[u][1]), k1 = th.decide(s1[u][2], s1[u][3]);
+        k2s[u][0] = k0;
+        k2s[u][1] = k1;
         s2[u][0] = __fadd_rn(s1[u][0], s1[u][1]);
         s2[u][1] = __fadd_rn(s1[u][2], s1[u][3]);
         or_field(rec, node_bit(2, 8 * u + 2 * g), k0 | (k1 << AB), 2 * AB);
@@ -471,7 +480,8 @@ __device__ void polar_tail(const float (&yv)[NV][KS][8], const uint32_t (&n16)[N
       th.load(ptab, 2);
 #pragma unroll
       for (int u = 0; u < KS; ++u) {
-        or_field(rec, node_bit(3, 4 * u + g), th.decide(s2[u][0], s2[u][1]), AB);
+        k3s[u] = th.decide(s2[u][0], s2[u][1]);
+        or_field(rec, node_bit(3, 4 * u + g), k3s[u], AB);
         s3[u] = __fadd_rn(s2[u][0], s2[u][1]);
       }
     }
@@ -485,6 +495,7 @@ __device__ void polar_tail(const float (&yv)[NV][KS][8], const uint32_t (&n16)[N
         const float o = __shfl_xor(s3[u], 16, kWave);
         const float A = (g & 1) ? o : s3[u], B = (g & 1) ? s3[u] : o;
         const uint32_t k = th.decide(A, B);
+        k4s[u] = k;
         if ((g & 1) == 0) or_field(rec, node_bit(4, 2 * u + (g >> 1)), k, AB);
         s4[u] = __fadd_rn(A, B);
       }
@@ -499,6 +510,7 @@ __device__ void polar_tail(const float (&yv)[NV][KS][8], const uint32_t (&n16)[N
         const float o = __shfl_xor(s4[u], 32, kWave);
         const float A = (g & 2) ? o : s4[u], B = (g & 2) ? s4[u] : o;
         const uint32_t k = th.decide(A, B);
+        k5s[u] = k;
         if (g == 0) or_field(rec, node_bit(5, u), k, AB);
         cur[u] = __fadd_rn(A, B);
       }
@@ -512,6 +524,7 @@ __device__ void polar_tail(const float (&yv)[NV][KS][8], const uint32_t (&n16)[N
 #pragma unroll
       for (int i = 0; i < cnt; ++i) {
         const uint32_t k = th.decide(cur[2 * i], cur[2 * i + 1]);
+        khs[l][i] = k;
         if (g == 0) or_field(rec, node_bit(l, i), k, AB);
         cur[i] = __fadd_rn(cur[2 * i], cur[2 * i + 1]);
       }
@@ -524,8 +537,46 @@ __device__ void polar_tail(const float (&yv)[NV][KS][8], const uint32_t (&n16)[N
       if (v < a.n) bitsw[v * sw + w] = w < NWD ? stg[vv * NWD + w] : 0u;
     }
     wave_lds_fence();
-    const int64_t v = v0 + 16 * t + n;
-    if (g == 0 && v < a.n) a.norms[v] = n16[t];
+    if constexpr (QJL) {
+      constexpr int NA2 = 2 * NA;
+      auto cs = [&](int level, bool sn, uint32_t k) { return pcs[(level - 1) * NA2 + (sn ? NA : 0) + k]; };
+      // level-5 node values from the root (every lane the same), then the lane's own subtree
+      float v5[KS];
+      v5[0] = 1.0f;
+#pragma unroll
+      for (int l = LV; l >= 6; --l) {
+#pragma unroll
+        for (int i = (D >> l) - 1; i >= 0; --i) {
+          const float pv = v5[i];
+          v5[2 * i] = __fmul_rn(pv, cs(l, false, khs[l][i]));
+          v5[2 * i + 1] = __fmul_rn(pv, cs(l, true, khs[l][i]));
+        }
+      }
+      const float nbar = f16_bits_to_float(n16[t]);
+#pragma unroll
+      for (int u = 0; u < KS; ++u) {
+        const float v4 = __fmul_rn(v5[u], cs(5, ((g >> 1) & 1) != 0, k5s[u]));
+        const float v3 = __fmul_rn(v4, cs(4, (g & 1) != 0, k4s[u]));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float v2 = __fmul_rn(v3, cs(3, c != 0, k3s[u]));
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float rp = __fmul_rn(v2, cs(2, e != 0, k2s[u][c]));
+            const int p = 2 * c + e;
+            const uint32_t f = f1[u][p], k = f >> 2;
+            float ua = __fmul_rn(rp, cs(1, false, k)), ub = __fmul_rn(rp, cs(1, true, k));
+            if (f & 1u) ua = -ua;
+            if (f & 2u) ub = -ub;
+            yv[t][u][2 * p] = __fsub_rn(yv[t][u][2 * p], __fmul_rn(nbar, ua));
+            yv[t][u][2 * p + 1] = __fsub_rn(yv[t][u][2 * p + 1], __fmul_rn(nbar, ub));
+          }
+        }
+      }
+    } else {
+      const int64_t v = v0 + 16 * t + n;
+      if (g == 0 && v < a.n) a.norms[v] = n16[t];
+    }
   }
 }
 
@@ -562,8 +613,11 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
   __shared__ float smax_s;
   // polar: cos^2 tau and sin^2 tau of every level, [level][2][2^AB]
   __shared__ float ptab[AB > 0 ? log2_d<D>() * 2 * (1 << AB) : 1];
-  static_assert(AB == 0 || (M == 0 && 16 * ((D / 2 * (2 + AB) + (D / 2 - 1) * AB + 31) / 32) * 4 <= 2 * (D + 2) * 8),
+  static_assert(AB == 0 || ((M == 0 || M == D) && 16 * ((D / 2 * (2 + AB) + (D / 2 - 1) * AB + 31) / 32) * 4 <=
+                                                       2 * (D + 2) * 8),
                 "polar records of a tile fit the staging");
+  // polar with the QJL stage: cos and sin of every level, [level][2][2^AB]
+  __shared__ float pcs[AB > 0 && M > 0 ? log2_d<D>() * 2 * (1 << AB) : 1];
 
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   const int n = lane & 15, g = lane >> 4;
@@ -579,6 +633,7 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
     for (int e = tid; e < log2_d<D>() * 2 * NA; e += NW * 64) {
       const int l = e / (2 * NA), r = e % (2 * NA);  // r < NA: cos^2 tau, else sin^2 tau
       ptab[e] = a.thresholds[(l * 4 + 2) * NA + r];
+      if constexpr (M > 0) pcs[e] = a.thresholds[(l * 4) * NA + r];  // r < NA: cos, else sin
     }
   }
   if constexpr (!PRE && !ROTS) build_afrags<D>(a.rot, D, fpi, NW * 64);
@@ -774,60 +829,15 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
       }
     }
     if constexpr (AB > 0) {
-      polar_tail<D, AB, NV, KS>(yv, n16, v0, a, reinterpret_cast<uint32_t *>(wscr[wid]), ptab);
-      return;
+      polar_tail<D, AB, NV, KS, (M > 0)>(yv, n16, v0, a, reinterpret_cast<uint32_t *>(wscr[wid]), ptab, pcs);
+      if constexpr (M == 0) return;
     }
-
-    // ---- 3. indices and residual; 4. residual norm
+    // ---- 4. exact fp16 norm of the residual of tile t from s2, the fp64 sum of the lanes' fp32
+    // partial sums of 8 squares (within 8u of the exact sum): the fp64 sum where that cannot
+    // decide, then the exact expansion (one vector at a time)
     uint32_t rn16[NV];
     double rn2[NV];
-#pragma unroll
-    for (int t = 0; t < NV; ++t) {
-      const float nbar = f16_bits_to_float(n16[t]);
-      float thr[L - 1];
-#pragma unroll
-      for (int j = 0; j < L - 1; ++j) thr[j] = __fmul_rn(nbar, th[j]);
-      double s2 = 0.0;
-#pragma unroll
-      for (int u = 0; u < KS; ++u) {
-        uint32_t qv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) qv[j] = quantize_index<BITS>(yv[t][u][j], thr);
-        uint32_t field = 0u;  // 8 * BITS bits: coordinates 32u + 8g + 0..7
-        float p = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float r = __fsub_rn(yv[t][u][j], __fmul_rn(nbar, cbs[qv[j]]));
-          yv[t][u][j] = r;
-          p = fmaf(r, r, p);
-          field |= qv[j] << (BITS * j);
-        }
-        s2 += (double)p;
-        // the field is bytes BITS (4u + g) .. + BITS - 1 of the vector's index record
-        uint8_t *dst = stg + IB * (16 * t + n) + BITS * (4 * u + g);
-        if constexpr (BITS == 2) {
-          *reinterpret_cast<uint16_t *>(dst) = (uint16_t)field;
-        } else if constexpr (BITS == 4) {
-          *reinterpret_cast<uint32_t *>(dst) = field;
-        } else {
-          dst[0] = (uint8_t)field;
-          dst[1] = (uint8_t)(field >> 8);
-          dst[2] = (uint8_t)(field >> 16);
-        }
-      }
-      // staged index records of tile t -> HBM, 8 bytes per lane and step
-      wave_lds_fence();
-      for (int e = lane; e < 16 * IB / 8; e += kWave) {
-        const int vv = e / (IB / 8), w = e % (IB / 8);
-        const int64_t v = v0 + 16 * t + vv;
-        if (v < a.n)
-          *reinterpret_cast<uint2 *>(a.idx + v * a.idx_stride + 8 * w) =
-              *reinterpret_cast<const uint2 *>(stg + IB * (16 * t + vv) + 8 * w);
-      }
-      wave_lds_fence();
-      const int64_t v = v0 + 16 * t + n;
-      if (g == 0 && v < a.n)
-        for (int w = IWV; w < iw_all; ++w) idxw[v * iw_all + w] = 0u;
+    auto resid_norm = [&](const int t, double s2) {
       s2 += __shfl_xor(s2, 16, kWave);
       s2 += __shfl_xor(s2, 32, kWave);
       bool ok;
@@ -870,7 +880,75 @@ __global__ __launch_bounds__(NW * 64) void encode_mfma(EncArgs a) {
         }
       }
       rn2[t] = s2;
-      if (g == 0 && v < a.n) a.norms[v] = (hi_word(rn16[t], f16_bits_to_float(n16[t]), a.resid_scale) << 16) | n16[t];
+    };
+    if constexpr (AB > 0) {
+      // the QJL stage on the polar residual (yv): its norm, then the signs below
+#pragma unroll
+      for (int t = 0; t < NV; ++t) {
+        double s2 = 0.0;
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+          float p = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) p = fmaf(yv[t][u][j], yv[t][u][j], p);
+          s2 += (double)p;
+        }
+        resid_norm(t, s2);
+        const int64_t v = v0 + 16 * t + n;
+        if (g == 0 && v < a.n) a.norms[v] = (rn16[t] << 16) | n16[t];
+      }
+    } else {
+      // ---- 3. indices and residual (their norm by resid_norm)
+#pragma unroll
+      for (int t = 0; t < NV; ++t) {
+        const float nbar = f16_bits_to_float(n16[t]);
+        float thr[L - 1];
+#pragma unroll
+        for (int j = 0; j < L - 1; ++j) thr[j] = __fmul_rn(nbar, th[j]);
+        double s2 = 0.0;
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+          uint32_t qv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) qv[j] = quantize_index<BITS>(yv[t][u][j], thr);
+          uint32_t field = 0u;  // 8 * BITS bits: coordinates 32u + 8g + 0..7
+          float p = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float r = __fsub_rn(yv[t][u][j], __fmul_rn(nbar, cbs[qv[j]]));
+            yv[t][u][j] = r;
+            p = fmaf(r, r, p);
+            field |= qv[j] << (BITS * j);
+          }
+          s2 += (double)p;
+          // the field is bytes BITS (4u + g) .. + BITS - 1 of the vector's index record
+          uint8_t *dst = stg + IB * (16 * t + n) + BITS * (4 * u + g);
+          if constexpr (BITS == 2) {
+            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)field;
+          } else if constexpr (BITS == 4) {
+            *reinterpret_cast<uint32_t *>(dst) = field;
+          } else {
+            dst[0] = (uint8_t)field;
+            dst[1] = (uint8_t)(field >> 8);
+            dst[2] = (uint8_t)(field >> 16);
+          }
+        }
+        // staged index records of tile t -> HBM, 8 bytes per lane and step
+        wave_lds_fence();
+        for (int e = lane; e < 16 * IB / 8; e += kWave) {
+          const int vv = e / (IB / 8), w = e % (IB / 8);
+          const int64_t v = v0 + 16 * t + vv;
+          if (v < a.n)
+            *reinterpret_cast<uint2 *>(a.idx + v * a.idx_stride + 8 * w) =
+                *reinterpret_cast<const uint2 *>(stg + IB * (16 * t + vv) + 8 * w);
+        }
+        wave_lds_fence();
+        const int64_t v = v0 + 16 * t + n;
+        if (g == 0 && v < a.n)
+          for (int w = IWV; w < iw_all; ++w) idxw[v * iw_all + w] = 0u;
+        resid_norm(t, s2);
+        if (g == 0 && v < a.n) a.norms[v] = (hi_word(rn16[t], f16_bits_to_float(n16[t]), a.resid_scale) << 16) | n16[t];
+      }
     }
 
     // ---- 5. sign bits of z = S r
@@ -1066,9 +1144,10 @@ static void launch_mfma(const EncArgs &a, hipStream_t st) {
 }
 
 // The recursive polar stage on the MFMA encoder (d = 64, 128; input rows 16-byte aligned; with
-// per-block rotations, blocks and first multiples of 32 and, at d = 128, bf16 input).  Returns
-// TQ_EUNSUPPORTED where these do not hold (the caller then takes polar_encode_kernel).
-template <int D, int AB>
+// per-block rotations, blocks and first multiples of 32 and, at d = 128, bf16 input), with or
+// without the QJL stage on its residual (M = D).  Returns TQ_EUNSUPPORTED where these do not
+// hold (the caller then takes polar_encode_kernel).
+template <int D, int AB, int M>
 static int launch_polar_mfma_da(const EncArgs &a, int dt, bool pre, hipStream_t st) {
   const int eb = dt == TQ_F32 ? 4 : 2;
   const bool vec_ok = ((uintptr_t)a.x % 16 == 0) && ((a.ld_x * eb) % 16 == 0);
@@ -1076,29 +1155,34 @@ static int launch_polar_mfma_da(const EncArgs &a, int dt, bool pre, hipStream_t 
   if (!vec_ok) return TQ_EUNSUPPORTED;
   if (rots) {
     if (pre || a.vecs_per_rot % 32 != 0 || a.first % 32 != 0 || (D == 128 && dt != TQ_BF16)) return TQ_EUNSUPPORTED;
-    if (dt == TQ_BF16) launch_mfma<D, 2, 0, TQ_BF16, false, true, AB>(a, st);
+    if (dt == TQ_BF16) launch_mfma<D, 2, M, TQ_BF16, false, true, AB>(a, st);
     else if constexpr (D == 64) {
-      if (dt == TQ_F32) launch_mfma<D, 2, 0, TQ_F32, false, true, AB>(a, st);
-      else launch_mfma<D, 2, 0, TQ_F16, false, true, AB>(a, st);
+      if (dt == TQ_F32) launch_mfma<D, 2, M, TQ_F32, false, true, AB>(a, st);
+      else launch_mfma<D, 2, M, TQ_F16, false, true, AB>(a, st);
     }
   } else if (pre) {
-    launch_mfma<D, 2, 0, TQ_F32, true, false, AB>(a, st);
+    launch_mfma<D, 2, M, TQ_F32, true, false, AB>(a, st);
   } else if (dt == TQ_F32) {
-    launch_mfma<D, 2, 0, TQ_F32, false, false, AB>(a, st);
+    launch_mfma<D, 2, M, TQ_F32, false, false, AB>(a, st);
   } else if (dt == TQ_F16) {
-    launch_mfma<D, 2, 0, TQ_F16, false, false, AB>(a, st);
+    launch_mfma<D, 2, M, TQ_F16, false, false, AB>(a, st);
   } else {
-    launch_mfma<D, 2, 0, TQ_BF16, false, false, AB>(a, st);
+    launch_mfma<D, 2, M, TQ_BF16, false, false, AB>(a, st);
   }
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 
 int launch_polar_mfma(const PolarView &pc, const void *x, int dt, int64_t n, int64_t ld_x, bool pre, int64_t first,
                       const PolarCodesView &out, float *y_tap, void *stream) {
-  EncArgs a{x, ld_x, n, first, pc.rot, pc.n_rot, pc.vecs_per_rot, nullptr, nullptr, pc.tables,
-            out.bits, out.stride, nullptr, 0, out.norms, y_tap, nullptr, 0, 0, 0.0f, 0.0f};
+  EncArgs a{x, ld_x, n, first, pc.rot, pc.n_rot, pc.vecs_per_rot, pc.sketch, nullptr, pc.tables,
+            out.bits, out.stride, out.sign, out.sign_stride, out.norms, y_tap, nullptr, 0, 0, 0.0f, 0.0f};
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-#define TQ_PM(DD, AA) if (pc.d == DD && pc.ab == AA) return launch_polar_mfma_da<DD, AA>(a, dt, pre, st);
+#define TQ_PM(DD, AA)                                                              \
+  if (pc.d == DD && pc.ab == AA) {                                                 \
+    if (pc.m == 0) return launch_polar_mfma_da<DD, AA, 0>(a, dt, pre, st);         \
+    if (pc.m == DD) return launch_polar_mfma_da<DD, AA, DD>(a, dt, pre, st);       \
+    return TQ_EUNSUPPORTED;                                                        \
+  }
   TQ_PM(64, 2) TQ_PM(64, 3) TQ_PM(64, 4) TQ_PM(128, 2) TQ_PM(128, 3) TQ_PM(128, 4)
 #undef TQ_PM
   return TQ_EUNSUPPORTED;

@@ -305,7 +305,7 @@ static int launch_polar_encode_da(const PolarEncArgs &a, int m, int dt, bool pre
 int launch_polar_encode(const PolarView &pc, const void *x, int dt, int64_t n, int64_t ld_x, bool pre_rotated,
                         int64_t first, const PolarCodesView &out, float *y_tap, void *stream) {
   if (n == 0) return TQ_OK;
-  if (pc.m == 0) {  // the MFMA encoder has no residual stage
+  {
     const int rc = launch_polar_mfma(pc, x, dt, n, ld_x, pre_rotated, first, out, y_tap, stream);
     if (rc != TQ_EUNSUPPORTED) return rc;
   }
