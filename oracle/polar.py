@@ -340,6 +340,82 @@ def append(x: np.ndarray, pc: PolarCodec, slots, pos, rope_base: float, stride: 
     return encode_rotated(y, f16_norm_bits(x32), pc, stride, sign_stride)
 
 
+def _slice(codes: PolarCodes, a: int, b: int) -> PolarCodes:
+    return PolarCodes(codes.bits[a:b], codes.norms[a:b], sign=None if codes.sign is None else codes.sign[a:b])
+
+
+def attend_lens(q: np.ndarray, kcodes: PolarCodes, vcodes, pc: PolarCodec, vcodec, cap: int, lens, hkv: int,
+                scale: float) -> np.ndarray:
+    """Decode attention [S, Hq, d] over caches of capacity ``cap`` per (sequence, kv head) in which
+    sequence s holds its first lens[s] tokens (none: a zero output): softmax over those tokens of
+    scale times the polar estimate (with the rotation of the block's first record), times their
+    values dequantised as the two-stage decoder does (fp64)."""
+    from . import estimate as oe
+
+    S, hq, d = q.shape
+    g = hq // hkv
+    out = np.zeros((S, hq, vcodec.d))
+    for s_ in range(S):
+        n = int(lens[s_])
+        if n <= 0:
+            continue
+        for h in range(hkv):
+            a = (s_ * hkv + h) * cap
+            kc = _slice(kcodes, a, a + n)
+            rid = pc.rot_index(1, a)[0]
+            qt = q[s_, h * g:(h + 1) * g].astype(np.float64) @ pc.rot[rid].astype(np.float64).T
+            lg = (qt @ unit_directions(kc, pc).T) * f16_value((kc.norms & 0xFFFF).astype(np.uint16))[None, :]
+            if pc.m > 0:
+                from .estimate import qjl_scale
+
+                signs = 2.0 * unpack_bits(kc.sign, 1, pc.m).astype(np.float64) - 1.0
+                rn = f16_value((kc.norms >> 16).astype(np.uint16))
+                lg = lg + ((qt @ pc.sketch.astype(np.float64).T) @ signs.T) * (rn * qjl_scale(pc.m))[None, :]
+            v = oe.dequantize(oe.Codes(vcodes.idx[a:a + n], None if vcodes.sign is None else vcodes.sign[a:a + n],
+                                       vcodes.norms[a:a + n]), vcodec, a)
+            out[s_, h * g:(h + 1) * g] = oe.softmax(scale * lg) @ v
+    return out
+
+
+def decode_step(q, k_new, v_new, kcodes: PolarCodes, vcodes, pc: PolarCodec, vcodec, cap: int, pos, rope_base: float,
+                hkv: int, scale: float):
+    """One decode step over growing caches [S][Hkv][cap] with polar keys and two-stage values:
+    sequence s appends its new key (RoPE at pos[s], then the slot block's rotation) and value at
+    slot pos[s], then its queries, turned by RoPE at pos[s], attend over tokens 0 .. pos[s]; a
+    sequence whose position is outside [0, cap) appends nothing and gets a zero output.  Returns
+    (outputs [S, Hq, d], updated key codes, updated value codes); the inputs are not modified."""
+    from . import quantize as oq
+
+    S, hq, d = q.shape
+    pos = np.asarray(pos, dtype=np.int64)
+    ok = (pos >= 0) & (pos < cap)
+    slots = ((np.arange(S)[:, None] * hkv + np.arange(hkv)[None, :]) * cap + np.where(ok, pos, 0)[:, None]).reshape(-1)
+    rows = np.repeat(ok, hkv)
+    kpos = np.repeat(pos, hkv)
+    k2 = PolarCodes(kcodes.bits.copy(), kcodes.norms.copy(), sign=None if kcodes.sign is None else kcodes.sign.copy())
+    v2 = oq.Codes(vcodes.idx.copy(), None if vcodes.sign is None else vcodes.sign.copy(), vcodes.norms.copy())
+    if rows.any():
+        kn = np.asarray(k_new, dtype=np.float32).reshape(S * hkv, d)[rows]
+        vn = np.asarray(v_new, dtype=np.float32).reshape(S * hkv, vcodec.d)[rows]
+        nk = append(kn, pc, slots[rows], kpos[rows], rope_base, stride=k2.bits.shape[1],
+                    sign_stride=None if k2.sign is None else k2.sign.shape[1])
+        k2.bits[slots[rows]] = nk.bits
+        k2.norms[slots[rows]] = nk.norms
+        if k2.sign is not None:
+            k2.sign[slots[rows]] = nk.sign
+        nv = oq.append(vn, vcodec, slots[rows], kpos[rows], 0.0, idx_stride=v2.idx.shape[1],
+                       sign_stride=None if v2.sign is None else v2.sign.shape[1])
+        v2.idx[slots[rows]] = nv.idx
+        v2.norms[slots[rows]] = nv.norms
+        if v2.sign is not None:
+            v2.sign[slots[rows]] = nv.sign
+    qr = np.asarray(q, dtype=np.float64)
+    if rope_base > 0:
+        qr = oq.rope(qr.reshape(S * hq, d), np.repeat(pos, hq), rope_base).reshape(S, hq, d)
+    out = attend_lens(qr, k2, v2, pc, vcodec, cap, np.where(ok, pos + 1, 0), hkv, scale)
+    return out, k2, v2
+
+
 def search_scores(queries: np.ndarray, db: PolarCodes, pc: PolarCodec, chunk: int = 65536) -> np.ndarray:
     """Estimated <q, x_n> [Q, n_db] of every query against every database record (one shared
     rotation): the logits of scores() with the database as one block of keys."""

@@ -381,3 +381,69 @@ def test_polar_search_recall_against_exact_top_k():
     found, _ = polar.search_topk(q, polar.encode(x, pc), pc, 10)
     truth, _ = estimate.exact_topk(q, x, 10)
     assert estimate.recall_at_k(found, truth) > 0.8
+
+
+# ------------------------------------------------------------------ decode step over growing caches
+
+
+def _polar_caches(S, hkv, cap, d, pc, vc, seed):
+    g = np.random.default_rng(seed)
+    kx = g.standard_normal((S * hkv * cap, d)).astype(np.float32)
+    vx = g.standard_normal((S * hkv * cap, d)).astype(np.float32)
+    return polar.encode(kx, pc), quantize.encode(vx, vc)
+
+
+def test_polar_attend_lens_reduces_to_attend_and_to_one_token():
+    from oracle import codec as oc
+    from oracle import estimate
+
+    S, hkv, hq, cap, d = 2, 2, 4, 24, 32
+    pc = polar.make_polar_codec(d, 3, 1, m=d, sketch_seed=2)
+    vc = oc.make_codec(d, 3, 0, 3, 4)
+    kc, vcodes = _polar_caches(S, hkv, cap, d, pc, vc, 5)
+    q = np.random.default_rng(6).standard_normal((S, hq, d))
+    full = polar.attend_lens(q, kc, vcodes, pc, vc, cap, [cap, cap], hkv, 0.3)
+    assert np.allclose(full, polar.attend(q, kc, vcodes, pc, vc, cap, hkv, 0.3), rtol=0, atol=1e-12)
+    # one token: the softmax of one logit is 1, so the output is that token's dequantised value
+    one = polar.attend_lens(q, kc, vcodes, pc, vc, cap, [1, 0], hkv, 0.3)
+    v = estimate.dequantize(vcodes, vc)
+    for h in range(hq):
+        assert np.allclose(one[0, h], v[(h // 2) * cap], rtol=0, atol=1e-12)
+    assert not one[1].any()  # no token: zero output
+
+
+def test_polar_decode_step_appends_then_attends_over_the_prefix():
+    from oracle import codec as oc
+
+    S, hkv, hq, cap, d = 3, 2, 4, 16, 32
+    pc = polar.make_polar_codec(d, 2, 1, basis_seeds=[7, 8, 9, 10, 11, 12], vecs_per_rot=cap, m=d, sketch_seed=2)
+    vc = oc.make_codec(d, 3, d, 3, 4)
+    kc, vcodes = _polar_caches(S, hkv, cap, d, pc, vc, 9)
+    g = np.random.default_rng(10)
+    kn, vn = g.standard_normal((S, hkv, d)), g.standard_normal((S, hkv, d))
+    q = g.standard_normal((S, hq, d))
+    pos = np.array([5, cap, cap - 1])  # the second sequence is past its capacity
+    out, k2, v2 = polar.decode_step(q, kn, vn, kc, vcodes, pc, vc, cap, pos, 10000.0, hkv, 0.25)
+    # sequence 1: nothing appended, zero output
+    assert not out[1].any()
+    for h in range(hkv):
+        a = (1 * hkv + h) * cap
+        assert np.array_equal(k2.bits[a:a + cap], kc.bits[a:a + cap])
+        assert np.array_equal(v2.idx[a:a + cap], vcodes.idx[a:a + cap])
+    # the appended records are the append of the same rows, every other record unchanged
+    for s_ in (0, 2):
+        for h in range(hkv):
+            slot = (s_ * hkv + h) * cap + pos[s_]
+            want = polar.append(kn[s_, h][None].astype(np.float32), pc, [slot], [pos[s_]], 10000.0)
+            assert np.array_equal(k2.bits[slot], want.bits[0]) and k2.norms[slot] == want.norms[0]
+            assert np.array_equal(k2.sign[slot], want.sign[0])
+    changed = np.nonzero(np.any(k2.bits != kc.bits, axis=1))[0]
+    assert set(changed) <= {(s_ * hkv + h) * cap + pos[s_] for s_ in (0, 2) for h in range(hkv)}
+    # attention over the prefix: tokens past pos[s] do not matter (scramble them)
+    k3 = polar.PolarCodes(k2.bits.copy(), k2.norms.copy(), sign=k2.sign.copy())
+    for h in range(hkv):
+        a = (0 * hkv + h) * cap
+        k3.bits[a + pos[0] + 1:a + cap] ^= 0x5A
+    qr = quantize.rope(q.reshape(S * hq, d), np.repeat(pos, hq), 10000.0).reshape(S, hq, d)
+    again = polar.attend_lens(qr, k3, v2, pc, vc, cap, [pos[0] + 1, 0, pos[2] + 1], hkv, 0.25)
+    assert np.allclose(again, out, rtol=0, atol=1e-12)
