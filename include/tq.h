@@ -311,6 +311,25 @@ int tq_polar_encode(const tq_polar_codec *pc, const void *x, tq_dtype dt, int64_
 int tq_polar_append(const tq_polar_codec *pc, const void *x_new, tq_dtype dt, int64_t n_seq, int32_t hkv,
                     const int32_t *pos, int64_t cap, float rope_base, tq_polar_codes cache, void *stream);
 
+/* One decode step with polar-coded keys and two-stage-coded values over growing caches of
+ * capacity cap per (sequence, kv head): tq_polar_append of the new keys (RoPE at pos[s] when
+ * rope_base > 0) and tq_append of the new values (no RoPE) into slot pos[s], then attention of
+ * the queries, turned by RoPE at pos[s] when rope_base > 0, over tokens 0 .. pos[s] of their
+ * sequence only: softmax of scale times the estimate of tq_polar_scores, times the values as
+ * tq_polar_attend_decode.  A sequence whose pos[s] is outside [0, cap) appends nothing and gets
+ * a zero output (TurboESM summary, "Metodologia" A and section 2.E; walkthrough "Etapa 1").
+ *   q [n_seq][hq][d] fp32; k_new, v_new [n_seq][hkv][d] of type dt; pos [n_seq] int32 device;
+ *   kcache [n_seq][hkv][cap] polar records, vcache [n_seq][hkv][cap] codes; out [n_seq][hq][d].
+ *   ws  workspace of tq_polar_decode_step_workspace_bytes bytes, 256-byte aligned: logits
+ *       [n_seq][hq][cap] fp32 (only tokens 0 .. pos[s] written), then the per-chunk states.
+ * Every check runs before the first launch; an unsupported call changes no memory.          */
+size_t tq_polar_decode_step_workspace_bytes(const tq_polar_codec *pc, const tq_codec *vc, int64_t n_seq,
+                                            int32_t hq, int32_t hkv, int64_t cap);
+int tq_polar_decode_step(const tq_polar_codec *pc, const tq_codec *vc, const float *q, const void *k_new,
+                         const void *v_new, tq_dtype dt, int64_t n_seq, int32_t hq, int32_t hkv, int64_t cap,
+                         const int32_t *pos, float rope_base, tq_polar_codes kcache, tq_codes vcache, float scale,
+                         float *out, void *ws, size_t ws_bytes, void *stream);
+
 /* Inner-product top-k search over a database of polar records (hada.io TurboQuant page,
  * "Desempenho em busca vetorial"): per query the k records with the largest estimate of
  * tq_polar_scores (ties: smaller row first).  One shared rotation (n_rot = 1).

@@ -834,3 +834,105 @@ def test_qjl_full_size_sampled():
     sign = codes.sign.cpu().numpy()[sub]
     same = _explain_fields(bits, nw[sub], want, dy, ora, 0.02)
     assert _explain_qjl(nw[sub], sign, want, dy, same, ora) <= max(1, int(0.02 * len(sub)))
+
+
+# ------------------------------------------------------------------ decode step
+
+
+def _polar_appended(lib, ora, x, pos, cap, hkv, rope_base, before, after):
+    """Device records at the appended slots against the oracle's append (explained by the rotation
+    bound, as test_polar_append_matches_oracle); every other record unchanged.  Returns the
+    oracle's cache after the append (its own records at the slots)."""
+    S, _, d = x.shape
+    valid = [(s, h) for s in range(S) for h in range(hkv) if 0 <= pos[s] < cap]
+    slots = np.array([(s * hkv + h) * cap + pos[s] for s, h in valid], dtype=np.int64)
+    rows = np.array([x[s, h] for s, h in valid], dtype=np.float32)
+    p = np.array([pos[s] for s, _ in valid], dtype=np.int64)
+    want = op.append(rows, ora, slots, p, rope_base, stride=lib.stride,
+                     sign_stride=lib.sign_stride if ora.m else None)
+    bits, norms = after[0], after[1]
+    assert np.array_equal(norms[slots] & 0xFFFF, oq.f16_norm_bits(rows))
+    xr = oq.rope(rows, p, rope_base) if rope_base > 0 else rows.astype(np.float64)
+    rid = np.array([ora.rot_index(1, int(t))[0] for t in slots])
+    y_ex, bound = _exact_rotation(xr, ora, rid)
+    dy = bound + np.abs(want.extra["y"].astype(np.float64) - y_ex)
+    same = _explain_fields(bits[slots], norms[slots], want, dy, ora, 0.2)
+    if ora.m:
+        assert _explain_qjl(norms[slots], after[2][slots], want, dy, same, ora) <= 2
+    other = np.setdiff1d(np.arange(bits.shape[0]), slots)
+    assert np.array_equal(bits[other], before.bits[other]) and np.array_equal(norms[other], before.norms[other])
+    cache = op.PolarCodes(before.bits.copy(), before.norms.copy(),
+                          sign=None if before.sign is None else before.sign.copy())
+    cache.bits[slots], cache.norms[slots] = want.bits, want.norms
+    if ora.m:
+        cache.sign[slots] = want.sign
+    return cache
+
+
+@pytest.mark.parametrize("m,hq,hkv,S,cap,pos", [
+    (0, 8, 2, 3, 5000, [4999, 1234, -1]),     # several chunks; ragged lengths; one sequence appends nothing
+    (128, 4, 4, 2, 700, [699, 350]),          # the QJL stage; one head per kv head
+    (128, 16, 4, 2, 20000, [17000, 20000]),   # four heads per kv head, long; one past its capacity
+])
+def test_polar_decode_step_matches_oracle(m, hq, hkv, S, cap, pos):
+    from oracle import codec as oc
+
+    say("polar decode step", m, hq, hkv, S, cap, pos)
+    d, ab, base = 128, 2, 10000.0
+    lib, ora = _codecs(d, ab, m=m)
+    vl = tq.make_codec(d, 3, 0, 3, 4)
+    vo = oc.make_codec(d, 3, 0, 3, 4)
+    g = np.random.default_rng(cap + hq + m)
+    n = S * hkv * cap
+    kx = (g.standard_normal((n, d)) * np.where(g.random(d) < 0.03, 8.0, 1.0)).astype(np.float32)
+    kb = op.encode(kx, ora, stride=lib.stride, sign_stride=lib.sign_stride if m else None)
+    vb = oq.encode(g.standard_normal((n, d)).astype(np.float32), vo, idx_stride=vl.idx_stride,
+                   sign_stride=vl.sign_stride)
+    kc = tq.PolarCodes(torch.from_numpy(kb.bits.copy()).cuda(), torch.from_numpy(kb.norms.view(np.int32).copy()).cuda(),
+                       None if kb.sign is None else torch.from_numpy(kb.sign.copy()).cuda())
+    vc = tq.Codes(torch.from_numpy(vb.idx.copy()).cuda(), None, torch.from_numpy(vb.norms.view(np.int32).copy()).cuda())
+    q = g.standard_normal((S, hq, d)).astype(np.float32)
+    kn = g.standard_normal((S, hkv, d)).astype(np.float32)
+    vn = g.standard_normal((S, hkv, d)).astype(np.float32)
+    p = np.array(pos, dtype=np.int32)
+    scale = 1.0 / np.sqrt(d)
+    out = tq.polar_decode_step(lib, vl, torch.from_numpy(q).cuda(), torch.from_numpy(kn).cuda(),
+                               torch.from_numpy(vn).cuda(), torch.from_numpy(p).cuda(), cap, base, kc, vc,
+                               scale).cpu().numpy()
+    ka = _polar_appended(lib, ora, kn, p, cap, hkv, base, kb, kc.numpy())
+    # values: the two-stage append (tested on its own); the reference reads the oracle's records
+    _, _, va = op.decode_step(q, kn, vn, kb, vb, ora, vo, cap, p, base, hkv, scale)
+    vidx = vc.idx.cpu().numpy()
+    ok = (p >= 0) & (p < cap)
+    vslots = {(s * hkv + h) * cap + p[s] for s in range(S) for h in range(hkv) if ok[s]}
+    other = np.array(sorted(set(range(n)) - vslots))
+    assert np.array_equal(vidx[other], vb.idx[other])
+    qr = oq.rope(q.reshape(S * hq, d), np.repeat(p, hq), base).reshape(S, hq, d)
+    want = op.attend_lens(qr, ka, va, ora, vo, cap, np.where(ok, p + 1, 0), hkv, scale)
+    for s in range(S):
+        if not ok[s]:
+            assert not out[s].any()
+    rows = [s for s in range(S) if ok[s]]
+    err = np.max(np.abs(out[rows] - want[rows]), axis=-1) / np.max(np.abs(want[rows]), axis=-1)
+    say("  max rel err", float(err.max()))
+    assert np.all(err <= 1e-3)
+
+
+def test_polar_decode_step_unsupported_changes_nothing():
+    # 4-bit values are not a value codec of the logits-in attention: refused before any launch
+    from oracle import codec as oc  # noqa: F401
+
+    d, hq, hkv, S, cap = 64, 2, 1, 1, 16
+    lib, _ = _codecs(d, 2)
+    vl = tq.make_codec(d, 4, 0, 3, 4)
+    kc = tq.alloc_polar_codes(lib, S * hkv * cap)
+    vc = tq.alloc_codes(vl, S * hkv * cap)
+    kc.bits.fill_(7)
+    vc.idx.fill_(9)
+    q = torch.zeros((S, hq, d), device="cuda")
+    kn = torch.ones((S, hkv, d), device="cuda")
+    p = torch.zeros((S,), dtype=torch.int32, device="cuda")
+    with pytest.raises(tq.TQError):
+        tq.polar_decode_step(lib, vl, q, kn, kn, p, cap, 0.0, kc, vc, 1.0)
+    torch.cuda.synchronize()
+    assert bool((kc.bits == 7).all()) and bool((vc.idx == 9).all())

@@ -81,6 +81,9 @@ def _load():
         "tq_polar_encode": ([PP, P, I32, I64, I64, ctypes.c_uint32, I64, _PolarCodes, P, P], I32),
         "tq_polar_scores": ([PP, P, I64, I32, I32, I64, _PolarCodes, P, P], I32),
         "tq_polar_append": ([PP, P, I32, I64, I32, P, I64, ctypes.c_float, _PolarCodes, P], I32),
+        "tq_polar_decode_step_workspace_bytes": ([PP, CP, I64, I32, I32, I64], SZ),
+        "tq_polar_decode_step": ([PP, CP, P, P, P, I32, I64, I32, I32, I64, P, ctypes.c_float, _PolarCodes, _Codes,
+                                  ctypes.c_float, P, P, SZ, P], I32),
         "tq_polar_search_workspace_bytes": ([PP, I64, I32, I64], SZ),
         "tq_polar_search_topk": ([PP, P, I64, _PolarCodes, I64, I32, P, P, P, SZ, P], I32),
         "tq_polar_attend_workspace_bytes": ([PP, CP, I64, I32, I32, I64], SZ),
@@ -114,7 +117,8 @@ EXPORTED = ("tq_make_rotation", "tq_make_head_rotations", "tq_make_sketch", "tq_
             "tq_search_topk",
             "tq_workspace_bytes", "tq_status_str", "tq_version", "tq_make_polar_tables",
             "tq_polar_record_bytes", "tq_polar_encode", "tq_polar_scores", "tq_polar_attend_workspace_bytes",
-            "tq_polar_attend_decode", "tq_polar_append", "tq_polar_search_workspace_bytes", "tq_polar_search_topk")
+            "tq_polar_attend_decode", "tq_polar_append", "tq_polar_search_workspace_bytes", "tq_polar_search_topk",
+            "tq_polar_decode_step_workspace_bytes", "tq_polar_decode_step")
 
 
 def _check(rc):
@@ -711,6 +715,38 @@ def polar_append(pc: PolarCodec, x_new, pos, cap: int, rope_base: float, cache: 
     _check(lib.tq_polar_append(ctypes.byref(cc), _ptr(x), dt, n_seq, hkv, _ptr(pos), cap, ctypes.c_float(rope_base),
                                cache.c(), _stream()))
     return cache
+
+
+def polar_decode_step(pc: PolarCodec, vcodec: Codec, q, k_new, v_new, pos, cap: int, rope_base: float,
+                      kcache: PolarCodes, vcache: Codes, scale: float, out=None):
+    """One decode step with polar keys: append k_new (polar, RoPE'd at pos[s]) and v_new [n_seq,
+    hkv, d] at slot pos[s], then attention of q [n_seq, hq, d] (RoPE'd at pos[s]) over tokens
+    0 .. pos[s].  Returns out."""
+    named = _check_queries(q, pc.d)
+    n_seq, hq, d = q.shape
+    named += _check_rows(k_new, d, "k_new") + _check_rows(v_new, d, "v_new")
+    _need(k_new.dim() == 3 and k_new.shape[0] == n_seq, "k_new must be [n_seq, hkv, d]")
+    kn, vn = k_new.contiguous(), v_new.contiguous()
+    hkv = kn.shape[1]
+    _need(tuple(vn.shape) == tuple(kn.shape), "v_new must have k_new's shape")
+    _need(vn.dtype == kn.dtype, "k_new and v_new must share a dtype")
+    _check_heads(hq, hkv)
+    _need(vcodec.d == d, "the polar codec and vcodec must share d")
+    _need(cap >= 1, "cap must be >= 1")
+    named += _check_tensor(pos, "pos", dtype=_torch().int32, shape=(n_seq,))
+    named += _check_codec(pc, "pc") + _check_codec(vcodec, "vcodec")
+    named += _check_polar_codes(kcache, pc, n_seq * hkv * cap, "kcache")
+    named += _check_codes(vcache, vcodec, n_seq * hkv * cap, "vcache")
+    dt = _DT[str(kn.dtype).replace("torch.", "")]
+    out, o = _out(out, "out", (n_seq, hq, d), q)
+    _check_devices(named + o)
+    pcc, vc = pc.c(), vcodec.c()
+    need = lib.tq_polar_decode_step_workspace_bytes(ctypes.byref(pcc), ctypes.byref(vc), n_seq, hq, hkv, cap)
+    buf, ws, wsb = _workspace(need, q.device)
+    _check(lib.tq_polar_decode_step(ctypes.byref(pcc), ctypes.byref(vc), _ptr(q), _ptr(kn), _ptr(vn), dt, n_seq, hq,
+                                    hkv, cap, _ptr(pos), ctypes.c_float(rope_base), kcache.c(), vcache.c(),
+                                    ctypes.c_float(scale), _ptr(out), ws, wsb, _stream()))
+    return out
 
 
 def polar_search_topk(pc: PolarCodec, queries, db: PolarCodes, n_db: int, k: int):

@@ -332,6 +332,61 @@ extern "C" int tq_polar_search_topk(const tq_polar_codec *pc, const float *queri
                                  stream);
 }
 
+namespace {
+
+size_t polar_step_ws(const tq_polar_codec *pc, const tq_codec *vc, int64_t n_seq, int32_t hq, int32_t hkv,
+                     int64_t cap) {
+  return polar_attend_ws(pc, vc, n_seq, hq, hkv, cap);
+}
+
+}  // namespace
+
+extern "C" size_t tq_polar_decode_step_workspace_bytes(const tq_polar_codec *pc, const tq_codec *vc, int64_t n_seq,
+                                                       int32_t hq, int32_t hkv, int64_t cap) {
+  if (!pc || !vc || n_seq < 0 || cap < 1 || hq < 1 || hkv < 1 || hq % hkv != 0) return 0;
+  return polar_step_ws(pc, vc, n_seq, hq, hkv, cap);
+}
+
+extern "C" int tq_polar_decode_step(const tq_polar_codec *pc, const tq_codec *vc, const float *q, const void *k_new,
+                                    const void *v_new, tq_dtype dt, int64_t n_seq, int32_t hq, int32_t hkv,
+                                    int64_t cap, const int32_t *pos, float rope_base, tq_polar_codes kcache,
+                                    tq_codes vcache, float scale, float *out, void *ws, size_t ws_bytes,
+                                    void *stream) {
+  int rc = check_polar(pc);
+  if (rc != TQ_OK) return rc;
+  rc = check_codec(vc);
+  if (rc != TQ_OK) return rc;
+  if (pc->d != vc->d) return TQ_EINVAL;
+  if (n_seq < 0 || cap < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || !(rope_base >= 0.0f)) return TQ_EINVAL;
+  if (n_seq == 0) return TQ_OK;
+  if (!q || !out || !k_new || !v_new || !pos) return TQ_EINVAL;
+  if (dt != TQ_F32 && dt != TQ_F16 && dt != TQ_BF16) return TQ_EINVAL;
+  rc = check_polar_codes(pc, kcache);
+  if (rc != TQ_OK) return rc;
+  rc = check_codes(vc, vcache);
+  if (rc != TQ_OK) return rc;
+  const tq::ScoreShape s{n_seq, hq, hkv, cap};
+  // every check before the first launch: an unsupported call leaves the caches untouched (the
+  // score grid is at most n_seq * hq * ceil(cap / 256) workgroups)
+  rc = tq::attend_logits_preflight(tq::view(*vc), s);
+  if (rc != TQ_OK) return rc;
+  if (!tq::grid_fits(n_seq * hq * ((cap + 255) / 256))) return TQ_EUNSUPPORTED;
+  const size_t need = polar_step_ws(pc, vc, n_seq, hq, hkv, cap);
+  if (!ws || ws_bytes < need) return TQ_EWORKSPACE;
+  if (!aligned(ws, 256)) return TQ_EALIGN;
+  rc = tq::launch_polar_append(tq::view(*pc), k_new, (int)dt, n_seq, hkv, pos, cap, rope_base, tq::view(kcache),
+                               stream);
+  if (rc != TQ_OK) return rc;
+  rc = tq::launch_append(tq::view(*vc), v_new, (int)dt, n_seq, hkv, pos, cap, 0.0f, tq::view(vcache), stream);
+  if (rc != TQ_OK) return rc;
+  float *lg = reinterpret_cast<float *>(ws);
+  const size_t lg_bytes = (size_t)n_seq * (size_t)hq * (size_t)cap * sizeof(float);
+  void *part = reinterpret_cast<uint8_t *>(ws) + (lg_bytes + 255) / 256 * 256;
+  rc = tq::launch_polar_scores(tq::view(*pc), q, s, tq::view(kcache), lg, stream, pos, rope_base);
+  if (rc != TQ_OK) return rc;
+  return tq::launch_attend_logits(tq::view(*vc), lg, s, tq::view(vcache), scale, out, part, stream, pos);
+}
+
 extern "C" int tq_polar_scores(const tq_polar_codec *pc, const float *q, int64_t n_seq, int32_t hq, int32_t hkv,
                                int64_t n_keys, tq_polar_codes k, float *logits, void *stream) {
   int rc = check_polar(pc);

@@ -541,7 +541,7 @@ size_t attend_logits_workspace(const CodecView &vc, const ScoreShape &s) {
 // Attention from given logits: the same chunked pass (online softmax, values in the rotated
 // space) and chunk merge, with the logits read instead of computed from key codes.
 int launch_attend_logits(const CodecView &vc, const float *logits, const ScoreShape &s, const CodesView &v,
-                         float scale, float *out, void *ws, void *stream) {
+                         float scale, float *out, void *ws, void *stream, const int32_t *pos) {
   if (s.n_seq == 0) return TQ_OK;
   if (attend_logits_preflight(vc, s) != TQ_OK) return TQ_EUNSUPPORTED;  // before any launch
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -549,7 +549,7 @@ int launch_attend_logits(const CodecView &vc, const float *logits, const ScoreSh
   const int ch = att_chunk(s);
   const int nch = (int)((s.n + ch - 1) / ch);
   AttArgs a{nullptr, nullptr, nullptr, vc.centroids, s.n_seq, s.n, s.hq, s.hkv, 1, nch, ch, scale * kLog2e,
-            nullptr, 0, nullptr, 0, nullptr, v.idx, v.idx_stride, v.sign, v.sign_stride, v.norms, part, nullptr,
+            nullptr, 0, nullptr, 0, nullptr, v.idx, v.idx_stride, v.sign, v.sign_stride, v.norms, part, pos,
             logits};
   const int D = vc.d, VB = vc.bits, VM = vc.m;
   int rc = TQ_EUNSUPPORTED;

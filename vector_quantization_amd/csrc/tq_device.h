@@ -190,21 +190,26 @@ __device__ uint32_t wave_norm_f16(const float (&v)[C], double *terms, double *bu
   return (uint32_t)__shfl((int)hh, 0, kWave);
 }
 
-// RoPE of one vector held in LDS, by one wavefront (TurboESM summary, "Metodologia" A: the
-// positional rotation comes before the orthogonal one): coordinate i < D/2 turns with i + D/2 by
-// the angle p * base^(-2i/D); angle, sine, cosine and the turn in fp64, each result rounded once
-// to fp32 (an fp32 angle would be off by about p 2^-24 radians).  Ends with the wave's LDS fence.
+// RoPE of the D-vector x (LDS) at position p: coordinate i < D/2 turns with i + D/2 by the angle
+// p * base^(-2i/D), in fp64; `first` and `step` spread the D/2 pairs over the calling threads.
 template <int D>
-__device__ void wave_rope_lds(float *xs, int64_t p, float rope_base) {
-  const double lb = log2((double)rope_base);
-  for (int i = lane_id(); i < D / 2; i += kWave) {
+__device__ __forceinline__ void rope_pairs(float *x, int64_t p, float base, int first, int step) {
+  const double lb = log2((double)base);
+  for (int i = first; i < D / 2; i += step) {
     const double ang = (double)p * exp2(-2.0 * i / D * lb);
     double sn, cs;
     sincos(ang, &sn, &cs);
-    const double x0 = xs[i], x1 = xs[i + D / 2];
-    xs[i] = (float)(x0 * cs - x1 * sn);
-    xs[i + D / 2] = (float)(x0 * sn + x1 * cs);
+    const double x0 = x[i], x1 = x[i + D / 2];
+    x[i] = (float)(x0 * cs - x1 * sn);
+    x[i + D / 2] = (float)(x0 * sn + x1 * cs);
   }
+}
+
+// RoPE of one vector held in LDS, by one wavefront (TurboESM summary, "Metodologia" A: the
+// positional rotation comes before the orthogonal one); ends with the wave's LDS fence.
+template <int D>
+__device__ void wave_rope_lds(float *xs, int64_t p, float rope_base) {
+  rope_pairs<D>(xs, p, rope_base, lane_id(), kWave);
   wave_lds_fence();
 }
 

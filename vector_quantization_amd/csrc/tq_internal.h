@@ -70,8 +70,10 @@ int attend_logits_preflight(const CodecView &vc, const ScoreShape &s);
 
 // attention from given logits [n_seq][hq][n] (keys scored elsewhere) over value codes
 size_t attend_logits_workspace(const CodecView &vc, const ScoreShape &s);
+// pos != nullptr: sequence s attends over tokens 0 .. pos[s] (none, a zero output, when pos[s] is
+// outside [0, s.n)); logits past them are not read
 int launch_attend_logits(const CodecView &vc, const float *logits, const ScoreShape &s, const CodesView &v,
-                         float scale, float *out, void *ws, void *stream);
+                         float scale, float *out, void *ws, void *stream, const int32_t *pos = nullptr);
 
 // tq_decode_step behind its C entry point (all argument checks, then the launches), shared with
 // the entry point that takes its workspace from the library's static scratch array: with
@@ -115,8 +117,10 @@ int launch_polar_encode(const PolarView &pc, const void *x, int dt, int64_t n, i
 // the MFMA encoder with the polar epilogue; TQ_EUNSUPPORTED where it does not apply
 int launch_polar_mfma(const PolarView &pc, const void *x, int dt, int64_t n, int64_t ld_x, bool pre_rotated,
                       int64_t first, const PolarCodesView &out, float *y_tap, void *stream);
+// pos != nullptr: sequence s scores keys 0 .. pos[s] only (RoPE of its queries at pos[s] with
+// rope_base > 0); the other logits of the row are left unwritten
 int launch_polar_scores(const PolarView &pc, const float *q, const ScoreShape &s, const PolarCodesView &k,
-                        float *logits, void *stream);
+                        float *logits, void *stream, const int32_t *pos = nullptr, float rope_base = 0.0f);
 int launch_polar_append(const PolarView &pc, const void *x, int dt, int64_t n_seq, int hkv, const int32_t *pos,
                         int64_t cap, float rope_base, const PolarCodesView &out, void *stream);
 size_t polar_search_workspace(const PolarView &pc, int64_t n_q, int k, int64_t n_db);

@@ -350,6 +350,10 @@ struct PolarScoreArgs {
   const float *sketch;  // the QJL stage (M > 0): S [M][D], sign planes
   const uint8_t *sign;
   int64_t sign_stride;
+  // decode step (pos != nullptr): sequence s scores its keys 0 .. pos[s] only (none when pos[s]
+  // is outside [0, n_keys)), with its queries turned by RoPE at pos[s] when rope_base > 0
+  const int32_t *pos;
+  float rope_base;
 };
 
 // Logits of record v for G query heads from the LDS tables (layouts as polar_score_kernel's):
@@ -498,6 +502,16 @@ __global__ __launch_bounds__(NT) void polar_score_kernel(PolarScoreArgs a) {
   const int h0 = kvh * (a.hq / a.hkv) + sub * G;
   const int64_t qrow = s * a.hq + h0;
 
+  int64_t len = a.n_keys, p = -1;
+  if (a.pos != nullptr) {
+    p = a.pos[s];
+    len = (p >= 0 && p < a.n_keys) ? p + 1 : 0;
+  }
+  const int64_t t0 = (int64_t)chunk * a.chunk;
+  int64_t t1 = t0 + a.chunk;
+  if (t1 > len) t1 = len;
+  if (t0 >= t1) return;  // uniform over the workgroup: no key of this chunk is scored
+
   int64_t rid = 0;  // the rotation of this kv block
   if (a.n_rot > 1 && a.vecs_per_rot > 0) {
     rid = (blk * a.n_keys) / a.vecs_per_rot;
@@ -509,12 +523,9 @@ __global__ __launch_bounds__(NT) void polar_score_kernel(PolarScoreArgs a) {
     const int l = e / P::NA, j = e % P::NA;
     cs[l][j] = make_float2(a.tables[l * 4 * P::NA + j], a.tables[(l * 4 + 1) * P::NA + j]);
   }
-  prep.finish(qs, qt, qh);  // ends synchronised
+  prep.finish(qs, qt, qh, p, a.rope_base);  // ends synchronised
   build_polar_tables<D, AB, M, G, NT>(lut, qlut, cs, qt, qh);
 
-  const int64_t t0 = (int64_t)chunk * a.chunk;
-  int64_t t1 = t0 + a.chunk;
-  if (t1 > a.n_keys) t1 = a.n_keys;
   const int64_t vbase = blk * a.n_keys;
   for (int64_t t = t0 + threadIdx.x; t < t1; t += NT) {
     float lg[G];
@@ -568,11 +579,11 @@ static int launch_polar_score_da(const PolarScoreArgs &a, int m, int64_t n_seq, 
 }
 
 int launch_polar_scores(const PolarView &pc, const float *q, const ScoreShape &s, const PolarCodesView &k,
-                        float *logits, void *stream) {
+                        float *logits, void *stream, const int32_t *pos, float rope_base) {
   if (s.n == 0 || s.n_seq == 0) return TQ_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   PolarScoreArgs a{q, pc.rot, pc.tables, pc.n_rot, pc.vecs_per_rot, s.n_seq, s.n, s.hq, s.hkv, 0, 1, 0,
-                   k.bits, k.stride, k.norms, logits, pc.sketch, k.sign, k.sign_stride};
+                   k.bits, k.stride, k.norms, logits, pc.sketch, k.sign, k.sign_stride, pos, rope_base};
 #define TQ_PS(DD, AA) \
   if (pc.d == DD && pc.ab == AA) return launch_polar_score_da<DD, AA>(a, pc.m, s.n_seq, s.hq, s.hkv, s.n, st);
   TQ_PS(64, 2) TQ_PS(64, 3) TQ_PS(64, 4) TQ_PS(128, 2) TQ_PS(128, 3) TQ_PS(128, 4)

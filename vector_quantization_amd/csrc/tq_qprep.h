@@ -12,7 +12,8 @@ namespace tq {
 // issue() requests every global operand at once -- the queries and, where each thread owns one
 // (row, slice) of both products, its KPER weights of R and of S, kept in registers -- so that
 // the prologue waits for one memory latency instead of a chain of them.  finish() computes:
-// qs is LDS scratch of G * D floats; qt [G][D] and qh [G][M] are LDS outputs.  It ends
+// qs is LDS scratch of G * D floats; qt [G][D] and qh [G][M] are LDS outputs.  With rope_base > 0
+// and rope_p >= 0 the queries are first turned by RoPE at position rope_p (rope_pairs).  It ends
 // synchronised.
 template <int D, int M, int G, int NT>
 struct QueryPrep {
@@ -46,7 +47,7 @@ struct QueryPrep {
     }
   }
 
-  __device__ void finish(float *qs, float *qt, float *qh) {
+  __device__ void finish(float *qs, float *qt, float *qh, int64_t rope_p = -1, float rope_base = 0.0f) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < QN; ++i) {
@@ -54,6 +55,10 @@ struct QueryPrep {
       if (e < G * D) qs[e] = qv[i];
     }
     __syncthreads();
+    if (rope_base > 0.0f && rope_p >= 0) {  // uniform over the workgroup
+      for (int e = tid; e < G * (D / 2); e += NT) rope_pairs<D>(qs + (e / (D / 2)) * D, rope_p, rope_base, e % (D / 2), D / 2);
+      __syncthreads();
+    }
     auto reduce_store = [&](float(&acc)[G], int r, int rows, float *out) {
 #pragma unroll
       for (int h = 0; h < G; ++h) acc[h] = group_sum_dpp<KSL>(acc[h]);

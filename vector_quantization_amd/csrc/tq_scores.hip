@@ -36,21 +36,6 @@ struct QprepArgs {
   int bits;            // their index-term K order
 };
 
-// RoPE of the D-vector x (LDS) at position p: coordinate i < D/2 turns with i + D/2 by the angle
-// p * base^(-2i/D), in fp64; `first` and `step` spread the D/2 pairs over the calling threads.
-template <int D>
-__device__ __forceinline__ void rope_pairs(float *x, int64_t p, float base, int first, int step) {
-  const double lb = log2((double)base);
-  for (int i = first; i < D / 2; i += step) {
-    const double ang = (double)p * exp2(-2.0 * i / D * lb);
-    double sn, cs;
-    sincos(ang, &sn, &cs);
-    const double x0 = x[i], x1 = x[i + D / 2];
-    x[i] = (float)(x0 * cs - x1 * sn);
-    x[i + D / 2] = (float)(x0 * sn + x1 * cs);
-  }
-}
-
 template <int D, int M>
 __global__ __launch_bounds__(256) void qprep_kernel(QprepArgs a) {
   constexpr int C = (D + kWave - 1) / kWave;
