@@ -689,6 +689,26 @@ def polar_main(a):
     search_line_p = {"database": f"layer-0 keys, {n0} x {w.d}, polar ab = {ab} ({rec_b} B per record)",
                      "queries": n_qs, "k": 10, "ms": round(t_srch, 3),
                      "pairs_per_s": n_qs * n0 / (t_srch * 1e-3), "recall_at_10_vs_exact_fp32": round(rec10, 4)}
+    # one decode step over the whole cache: every sequence appends its token at the last slot
+    # (polar key with RoPE, 3-bit value), then attends over all 32768 tokens
+    gs = torch.Generator(device="cuda")
+    gs.manual_seed(31)
+    k_new = torch.randn((w.n_seq, w.hkv, w.d), generator=gs, device="cuda", dtype=torch.bfloat16)
+    v_new = torch.randn((w.n_seq, w.hkv, w.d), generator=gs, device="cuda", dtype=torch.bfloat16)
+    pos_t = torch.full((w.n_seq,), w.n_ctx - 1, dtype=torch.int32, device="cuda")
+    st_out = torch.empty((w.n_seq, w.hq, w.d), dtype=torch.float32, device="cuda")
+    dsteps = []
+    for i in range(a.warmup + a.steps):
+        ev[0].record(stream)
+        tq.polar_decode_step(pc, vc, qf, k_new, v_new, pos_t, w.n_ctx, 10000.0, codes, vcodes, scale, out=st_out)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if i >= a.warmup:
+            dsteps.append(ev[0].elapsed_time(ev[1]))
+    t_step = float(np.median(dsteps))
+    step_line = {"ms": round(t_step, 4), "tokens_per_s": round(w.n_seq / (t_step * 1e-3)),
+                 "note": f"{w.n_seq} sequences x {w.hkv} kv heads append one token at position {w.n_ctx - 1} "
+                         f"(polar keys with RoPE, 3-bit values), then attention over {w.n_ctx} tokens"}
     comp.setdefault(f"{qrec_b}B_per_key", {})[f"polar_ab{ab}_qjl{w.d}"] = quality(
         tq.polar_scores(pcq, qs0, qcodes.slice(0, w.hkv * w.n_ctx), w.n_ctx, w.hkv))
     torch.cuda.synchronize()
@@ -711,6 +731,7 @@ def polar_main(a):
         "quality_layer0_batch0": comp,
         "polar_qjl": qjl_line,
         "polar_search": search_line_p,
+        "polar_decode_step": step_line,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": f"tq::polar_score_kernel<{w.d}, {ab}, 4, 256> (one tq_polar_scores call)"},
