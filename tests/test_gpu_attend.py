@@ -91,6 +91,57 @@ def test_attend_esm2_per_head_rotations():
     assert err.max() <= TOL
 
 
+def test_running_max_moves_in_most_tiles():
+    """Key norms growing along the context, so that the running maxima move in most tiles, at a
+    size where every wavefront takes several tiles of its chunk (the accumulators are rescaled
+    between tiles); four query heads per kv head; sampled heads against the oracle."""
+    d, S, hkv, hq, N = 128, 2, 8, 32, 65536
+    say("attend growing key norms", S, hkv, hq, N)
+    kl = tq.make_codec(d, 2, 128, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
+    vl = tq.make_codec(d, 3, 0, synth.SEED_ROT_V, synth.SEED_SKETCH_V)
+    ko = oc.make_codec(d, 2, 128, synth.SEED_ROT_K, synth.SEED_SKETCH_K)
+    vo = oc.make_codec(d, 3, 0, synth.SEED_ROT_V, synth.SEED_SKETCH_V)
+    n_vec = S * hkv * N
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(21)
+    ramp = (1.0 + 4.0 * torch.arange(N, device="cuda", dtype=torch.float32) / N).repeat(S * hkv)
+
+    def fill(codes, grow):
+        codes.idx.copy_(torch.randint(0, 256, codes.idx.shape, generator=gen, device="cuda", dtype=torch.uint8))
+        if codes.sign is not None:
+            codes.sign.copy_(torch.randint(0, 256, codes.sign.shape, generator=gen, device="cuda", dtype=torch.uint8))
+        nrm = torch.randn(n_vec, generator=gen, device="cuda").abs() * math.sqrt(d)
+        if grow:
+            nrm = nrm * ramp
+        rn = torch.randn(n_vec, generator=gen, device="cuda").abs() * (0.35 * math.sqrt(d))
+        lo = nrm.half().view(torch.int16).to(torch.int32) & 0xFFFF
+        hi = rn.half().view(torch.int16).to(torch.int32) & 0xFFFF
+        codes.norms.copy_(lo | (hi << 16))
+
+    kcodes, vcodes = tq.alloc_codes(kl, n_vec), tq.alloc_codes(vl, n_vec)
+    fill(kcodes, True)
+    fill(vcodes, False)
+    q = torch.randn((S, hq, d), generator=gen, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    out = tq.attend_decode(kl, vl, q, kcodes, vcodes, N, hkv, scale)
+    torch.cuda.synchronize()
+    qn = q.cpu().numpy().astype(np.float64)
+    g = hq // hkv
+    worst = 0.0
+    for blk in (0, 5, 11, 15):
+        s, kvh = blk // hkv, blk % hkv
+        heads = list(range(kvh * g, (kvh + 1) * g))
+        sl = slice(blk * N, (blk + 1) * N)
+        kc = oracle_codes(kcodes.idx[sl].cpu().numpy(), kcodes.sign[sl].cpu().numpy(),
+                          kcodes.norms[sl].cpu().numpy().view(np.uint32))
+        vc = oracle_codes(vcodes.idx[sl].cpu().numpy(), None, vcodes.norms[sl].cpu().numpy().view(np.uint32))
+        want = oe.attend(qn[s:s + 1, heads], kc, vc, ko, vo, N, 1, scale)[0]
+        err = rel_err_rows(out[s, heads].cpu().numpy(), want)
+        worst = max(worst, err.max())
+        assert err.max() <= TOL, (blk, err)
+    say("  max rel err", worst)
+
+
 @pytest.mark.parametrize("wname", ["gqa", "long"])
 def test_full_size_sampled_heads(wname):
     """Full decode step in the bench's launch configuration; sampled query heads recomputed by

@@ -24,6 +24,7 @@ int qprep(const CodecView &kc, const float *q, const ScoreShape &s, float *qt, f
           const int32_t *pos = nullptr, float rope_base = 0.0f);
 
 constexpr float kLog2e = 1.4426950408889634f;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct AttArgs {
   const float *qt, *qh, *kcent, *vcent;
@@ -47,6 +48,14 @@ struct AttArgs {
   const float *lg_in;
 };
 
+// The value sum runs on the matrix cores (attend_partial, MV) for four query heads per kv head,
+// d = 128, value codes of at most 3 bits and no value sketch, with keys that carry a sketch or
+// logits given (3-bit keys without one keep the VALU value sum, which needs fewer registers
+// beside their larger key tables).
+constexpr bool att_mv(int d, int km, int vb, int vm, int g, bool lin) {
+  return g == 4 && vm == 0 && d == 128 && vb <= 3 && (lin || km > 0);
+}
+
 // LIN: the logits come from a.lg_in (no key tables, no key records); KB and KM then only size
 // unused parts.
 template <int D, int KB, int KM, int VB, int VM, int G, int NT, bool LIN = false>
@@ -64,6 +73,17 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   constexpr int TPO = kWave / NCG;   // lanes of a wavefront sharing one coordinate group
   constexpr int TOK = kWave / TPO;   // tokens of a wavefront tile per lane in the value phase
   static_assert(D % CPT == 0 && VM % CPT == 0 && kWave % NCG == 0, "lanes must cover the outputs evenly");
+  // MV: the value sum on the matrix cores.  With four query heads, no value sketch and d = 128,
+  // the weighted sum over a tile's tokens is a [4 heads x 64 tokens] x [64 tokens x 128] product,
+  // run as fp32 4x4x1 blocks.  Block b (lanes 4b .. 4b + 3) takes token TS q + (b mod TS) of the
+  // tile and coordinate part b / TS (of 16 / TS): lane 4b + j supplies the weight of head j as
+  // its A operand and, for g = 0 .. CPL - 1, the centroid of coordinate (4 (b / TS) + j) CPL + g
+  // as its B operand, so a lane's value operands are one contiguous CPL-code slice of the
+  // record.  Each block keeps its own partial sums (head i in element i of a lane's
+  // accumulator), which the lanes add up once at the end of the chunk.
+  constexpr bool MV = att_mv(D, KM, VB, VM, G, LIN);
+  constexpr int TS = 8;                  // token slots per block instruction
+  constexpr int CPL = D * TS / 64;       // coordinates per lane
   constexpr int LV = 1 << VB;
   constexpr int LP = LV * LV;        // entries of the two-code value table
   // One LDS arena with fixed offsets: the value table and the per-wavefront tiles at the bottom
@@ -162,14 +182,24 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
 
   // Wavefront-local online softmax: mrun is uniform over the wavefront; lpart is this lane's
   // share of the running sum (the tokens it scored), acc its share of the outputs.
-  float mrun[G], lpart[G], acc[CPT][G];
+  float mrun[G], lpart[G], acc[MV ? 1 : CPT][G];
+  f32x4 macc[MV ? CPL : 1];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     mrun[h] = -INFINITY;
     lpart[h] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) acc[c][h] = 0.0f;
+    for (int c = 0; c < (MV ? 1 : CPT); ++c) acc[c][h] = 0.0f;
   }
+#pragma unroll
+  for (int g = 0; g < (MV ? CPL : 1); ++g) macc[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // MV: the lane's slice (coordinates mc0 .. mc0 + CPL - 1) starts at bit mbit of the record:
+  // word mw0, bit msh of that word
+  const int mslot = (lane >> 2) % TS;             // token slot
+  const int mc0 = (4 * (lane / (4 * TS)) + (lane & 3)) * CPL;
+  const int mbit = VB * mc0;
+  const int mw0 = mbit >> 5, msh = mbit & 31;
+  const int mw1 = mw0 + 1 < IWV ? mw0 + 1 : mw0;  // a clamped second word (its bits unused when past the slice)
 
   struct Rec {
     uint32_t iw[CK::IW];
@@ -196,7 +226,11 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   // final merge, so wavefronts in the lookup phase overlap wavefronts in the value phase.
   Rec cur;
   load_rec(t0 + (int64_t)wid * kWave + lane, cur);
-  const uint8_t *qjl_tabs = tabs + opaque_offset(CK::MSE_BYTES);
+  // both table bases opaque (one scalar register each): the group offsets within them fit the
+  // 16-bit immediate of the LDS reads, with no per-group base held in a vector register
+  const uint8_t *mse_tabs = arena + opaque_offset(O_TABS);
+  const uint8_t *qjl_tabs = arena + opaque_offset(O_TABS + CK::MSE_BYTES);
+
   for (int64_t tile = t0 + (int64_t)wid * kWave; tile < t1; tile += (int64_t)NW * kWave) {
     // ---- phase A: one token per lane: logits, value records to the wavefront's tile
     const int64_t t = tile + lane;
@@ -217,7 +251,7 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
         for (int h = 0; h < G; ++h) lg[h] = a.lg_in[(qrow + h) * a.n_ctx + t] * a.scale_log2;
       } else {
         float am[G], aq[G];
-        lut_score<D, KB, KM, G>(cur.iw, cur.sw, tabs, qjl_tabs, hs, am, aq);
+        lut_score<D, KB, KM, G>(cur.iw, cur.sw, mse_tabs, qjl_tabs, hs, am, aq);
         const float nbar = f16_bits_to_float(cur.nw & 0xFFFFu);
         const float rq = f16_bits_to_float(cur.nw >> 16) * kappa_k;
 #pragma unroll
@@ -252,10 +286,17 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
         mrun[h] = mnew;
       }
       if (rescale) {
+        if constexpr (MV) {
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+          for (int g = 0; g < CPL; ++g)
 #pragma unroll
-          for (int c = 0; c < CPT; ++c) acc[c][h] *= alpha[h];
+            for (int h = 0; h < 4; ++h) macc[g][h] *= alpha[h];
+        } else {
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) acc[c][h] *= alpha[h];
+        }
       }
     }
 #pragma unroll
@@ -268,7 +309,27 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
     wave_lds_fence();
     // ---- phase B: weighted values; tokens past the end carry weight 0
     const int n0 = part * TOK;
-    if (is_val) {
+    if constexpr (MV) {
+      constexpr int PB = 2 * VB;  // bits of a code pair
+      static_assert(VB * CPL <= 64, "a lane's slice within two realigned words");
+#pragma unroll 2
+      for (int q = 0; q < kWave / TS; ++q) {
+        const int n = TS * q + mslot;
+        const float w = wt[4 * TS * q + (lane & (4 * TS - 1))];  // p * nbar_V of token n, head lane mod 4
+        const uint32_t x0 = __builtin_amdgcn_alignbit(vtile[n * IWV + mw1], vtile[n * IWV + mw0], msh);
+        const uint32_t x1 = vtile[n * IWV + mw1] >> msh;  // bits 32 .. of the slice
+#pragma unroll
+        for (int k = 0; k < CPL / 2; ++k) {  // coordinates 2k, 2k + 1 of the slice
+          const int bit = PB * k;
+          const uint32_t code =
+              (bit + PB <= 32 ? x0 >> bit : (bit >= 32 ? x1 >> (bit - 32) : __builtin_amdgcn_alignbit(x1, x0, bit))) &
+              (LP - 1);
+          const float2 cv = cbv2[code];
+          macc[2 * k] = __builtin_amdgcn_mfma_f32_4x4x1f32(w, cv.x, macc[2 * k], 0, 0, 0);
+          macc[2 * k + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(w, cv.y, macc[2 * k + 1], 0, 0, 0);
+        }
+      }
+    } else if (is_val) {
 #pragma unroll 4
       for (int n = n0; n < n0 + TOK; ++n) {
         const uint32_t w0 = vtile[n * IWV + vw0];
@@ -312,12 +373,35 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
 
   // ---- merge: the lanes of a coordinate group, then the wavefronts, then write this chunk's
   // partial state (max, sum, outputs) per query head
+  // MV: the TS token slots' partial sums, halved at each exchange over lane bits log2(TS) + 1
+  // .. 2 (a lane keeps the half its bit selects and adds its partner's copy of it), end with
+  // lane 4b + j holding e = 4g + i for e in [MR (b mod TS), MR (b mod TS) + MR)
+  constexpr int MR = MV ? 4 * CPL / TS : 1;
+  float mred[MV ? 4 * CPL : 1];
+  if constexpr (MV) {
 #pragma unroll
-  for (int off = NCG; off < kWave; off *= 2)
+    for (int g = 0; g < CPL; ++g)
 #pragma unroll
-    for (int c = 0; c < CPT; ++c)
+      for (int i = 0; i < 4; ++i) mred[4 * g + i] = macc[g][i];
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[c][h] += __shfl_xor(acc[c][h], off, kWave);
+    for (int m = 2 * TS; m >= 4; m >>= 1) {
+      const int hlf = CPL * m / TS;  // values kept after this exchange
+      const bool up = (lane & m) != 0;
+#pragma unroll
+      for (int e = 0; e < hlf; ++e) {
+        const float keep = up ? mred[e + hlf] : mred[e];
+        const float send = up ? mred[e] : mred[e + hlf];
+        mred[e] = keep + __shfl_xor(send, m, kWave);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int off = NCG; off < kWave; off *= 2)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[c][h] += __shfl_xor(acc[c][h], off, kWave);
+  }
   float lw[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) lw[h] = wave_sumf(lpart[h]);
@@ -333,7 +417,13 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
         lsum[wid * G + h] = lw[h];
       }
   }
-  if (part == 0) {
+  if constexpr (MV) {
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      const int e = MR * mslot + r;
+      outs[(wid * NOUT + mc0 + (e >> 2)) * G + (e & 3)] = mred[r];
+    }
+  } else if (part == 0) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
 #pragma unroll
