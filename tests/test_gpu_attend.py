@@ -52,6 +52,7 @@ def test_tiny_workload():
     (128, 2, 128, 3, 0, 32, 8, 2, 5000),    # 8B GQA decode shape, ragged last tile, several chunks
     (128, 2, 128, 3, 0, 8, 8, 1, 20000),    # one head per kv head, many chunks
     (128, 2, 128, 3, 0, 16, 8, 1, 3000),    # two heads per kv head
+    (128, 2, 128, 3, 0, 16, 2, 2, 2500),    # eight heads per kv head: two groups of four
     (64, 3, 64, 3, 64, 20, 20, 1, 1024),    # ESM-2 shape with V QJL
     (64, 2, 64, 2, 64, 4, 1, 2, 700),
     (128, 3, 128, 3, 128, 4, 2, 1, 1000),

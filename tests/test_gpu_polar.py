@@ -396,6 +396,7 @@ def test_zero_sizes_and_errors():
 
 @pytest.mark.parametrize("d,ab,vbits,vm,n_seq,hq,hkv,n_ctx", [
     (128, 2, 3, 0, 2, 8, 2, 1000),     # 4 heads per kv head, 3-bit values (the 8B value codec)
+    (128, 2, 3, 0, 1, 16, 2, 3000),    # 8 heads per kv head: two groups of four
     (64, 3, 3, 64, 1, 6, 3, 515),      # 2 heads, values with QJL
     (128, 2, 2, 128, 1, 2, 2, 2000),   # 1 head; several context chunks
 ])
