@@ -580,14 +580,20 @@ __device__ void polar_tail(float (&yv)[NV][KS][8], const uint32_t (&n16)[NV], in
   }
 }
 
+// 16-vector tiles per wavefront pass: one at d = 128 (the registers of a second tile cost more
+// occupancy than its shared work saves), two at d = 64
 template <int D, int M, int TIN, bool PRE>
 constexpr int enc_tiles() {
-  return (D == 128 && (M == 0 || (!PRE && TIN != TQ_BF16))) ? 1 : 2;
+  return (D == 128) ? 1 : 2;
 }
-// wavefronts per workgroup (one workgroup per CU): 16 where the one-tile pass fits 128 VGPRs
+// wavefronts per workgroup (one workgroup per CU, the A fragments in LDS): 16 where the pass
+// fits 128 VGPRs, 12 where it fits 168 and the fragments of Pi and S leave room for 12
+// wavefronts' staging (bf16 2-bit keys with a sketch)
 template <int D, int BITS, int M, int TIN, bool PRE>
 constexpr int enc_waves() {
-  return (D == 128 && M == 0 && !PRE && TIN == TQ_BF16 && BITS <= 3) ? 16 : 8;
+  return (D == 128 && M == 0 && !PRE && TIN == TQ_BF16 && BITS <= 3)   ? 16
+         : (D == 128 && M == D && !PRE && TIN == TQ_BF16 && BITS == 2) ? 12
+                                                                        : 8;
 }
 
 // AB > 0: the recursive polar stage with AB angle bits (M = 0; a.thresholds holds the polar
