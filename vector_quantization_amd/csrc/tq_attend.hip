@@ -201,6 +201,7 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
   const int mw0 = mbit >> 5, msh = mbit & 31;
   const int mw1 = mw0 + 1 < IWV ? mw0 + 1 : mw0;  // a clamped second word (its bits unused when past the slice)
 
+  // the records of the lane's token (LIN: its logits in place of its key record)
   struct Rec {
     uint32_t iw[CK::IW];
     uint32_t sw[KSW];
@@ -208,11 +209,15 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
     uint32_t vw[IWV];
     uint32_t vs[VM > 0 ? SWV : 1];
     uint32_t vnw;
+    float lgi[LIN ? G : 1];
   };
   auto load_rec = [&](int64_t t, Rec &r) {
     if (t < t1) {
       const int64_t v = vbase + t;
-      if constexpr (!LIN) {
+      if constexpr (LIN) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) r.lgi[h] = a.lg_in[(qrow + h) * a.n_ctx + t];
+      } else {
         load_words<CK::IW>(a.kidx + v * a.kidx_stride, r.iw);
         if constexpr (KM > 0) load_words<CK::SW>(a.ksign + v * a.ksign_stride, r.sw);
         r.nw = a.knorms[v];
@@ -248,7 +253,7 @@ __global__ __launch_bounds__(NT) void attend_partial(AttArgs a) {
       vr = f16_bits_to_float(cur.vnw >> 16) * kappa_v;
       if constexpr (LIN) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) lg[h] = a.lg_in[(qrow + h) * a.n_ctx + t] * a.scale_log2;
+        for (int h = 0; h < G; ++h) lg[h] = cur.lgi[h] * a.scale_log2;
       } else {
         float am[G], aq[G];
         lut_score<D, KB, KM, G>(cur.iw, cur.sw, mse_tabs, qjl_tabs, hs, am, aq);
