@@ -90,14 +90,17 @@ __global__ __launch_bounds__(256) void qprep_kernel(QprepArgs a) {
 // so that the output columns are read without bank conflicts.
 constexpr int kQpHeads = 16;
 constexpr int kQpHeadsMany = 64;
-constexpr int kQpKt = 8;
+constexpr int kQpKt = 8;  // a multiple of 4 dividing every supported d
 
 template <int D, int M, int HEADS>
 __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
   constexpr int NOUT = D > M ? D : M;
   constexpr int TPC = (256 / NOUT) >= 1 ? 256 / NOUT : 1;  // threads per output column
   constexpr int HPT = HEADS / TPC;                         // heads per thread
-  __shared__ float qs[HEADS][D + 1];
+  // rows padded to a multiple of 4 floats: a thread reads four consecutive k of a head at once
+  // (every lane of a wavefront the same head, one broadcast read)
+  constexpr int QSW = (D + 4) / 4 * 4;
+  __shared__ __align__(16) float qs[HEADS][QSW];
   __shared__ float qhs[HEADS][(M > 0 ? M : 1) + 1];
   __shared__ float rt[kQpKt][NOUT + 1];
   const int tid = threadIdx.x;
@@ -139,10 +142,18 @@ __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
     __syncthreads();
     if (active && col < D) {
 #pragma unroll
-      for (int kk = 0; kk < kQpKt; ++kk) {
-        const float r = rt[kk][col];
+      for (int k4 = 0; k4 < kQpKt; k4 += 4) {
+        float r[4];
 #pragma unroll
-        for (int j = 0; j < HPT; ++j) acc[j] = fmaf(r, qs[hs * HPT + j][k0 + kk], acc[j]);
+        for (int t = 0; t < 4; ++t) r[t] = rt[k4 + t][col];
+#pragma unroll
+        for (int j = 0; j < HPT; ++j) {
+          const float4 x = *reinterpret_cast<const float4 *>(&qs[hs * HPT + j][k0 + k4]);
+          acc[j] = fmaf(r[0], x.x, acc[j]);
+          acc[j] = fmaf(r[1], x.y, acc[j]);
+          acc[j] = fmaf(r[2], x.z, acc[j]);
+          acc[j] = fmaf(r[3], x.w, acc[j]);
+        }
       }
     }
   }
@@ -168,10 +179,18 @@ __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
       __syncthreads();
       if (active && col < M) {
 #pragma unroll
-        for (int kk = 0; kk < kQpKt; ++kk) {
-          const float r = rt[kk][col];
+        for (int k4 = 0; k4 < kQpKt; k4 += 4) {
+          float r[4];
 #pragma unroll
-          for (int j = 0; j < HPT; ++j) acc[j] = fmaf(r, qs[hs * HPT + j][k0 + kk], acc[j]);
+          for (int t = 0; t < 4; ++t) r[t] = rt[k4 + t][col];
+#pragma unroll
+          for (int j = 0; j < HPT; ++j) {
+            const float4 x = *reinterpret_cast<const float4 *>(&qs[hs * HPT + j][k0 + k4]);
+            acc[j] = fmaf(r[0], x.x, acc[j]);
+            acc[j] = fmaf(r[1], x.y, acc[j]);
+            acc[j] = fmaf(r[2], x.z, acc[j]);
+            acc[j] = fmaf(r[3], x.w, acc[j]);
+          }
         }
       }
     }
