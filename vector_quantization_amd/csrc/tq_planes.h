@@ -145,6 +145,73 @@ __device__ __forceinline__ void write_limb_record(const float *qt_row, const flo
   wave_lds_fence();  // the stage is reused by the wavefront's next record
 }
 
+// limbs_of for four queries at once, one per 16-lane group of the wavefront: lane 16 g + s
+// takes coordinates s, s + 16, ... of query g's row, and the maximum and the limb sums are
+// reduced over the group's 16 lanes.  The same values as limbs_of, byte for byte.
+template <int LEN, int NK>
+__device__ __forceinline__ void limbs_of16(const float *row, int layout, uint8_t *l0, uint8_t *l1, float &sigma,
+                                           int32_t &qc) {
+  const int sl = lane_id() & 15;
+  constexpr int NC = 4 * NK;  // coordinates per lane
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = sl + 16 * i;
+    if (c < LEN) mx = fmaxf(mx, fabsf(row[c]));
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+  sigma = mx / 127.0f;
+  const float inv = mx > 0.0f ? 127.0f / mx : 0.0f;
+  int32_t s0 = 0, s1 = 0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = sl + 16 * i;
+    const float u = c < LEN ? row[c] * inv : 0.0f;
+    const float r0 = fminf(fmaxf(__builtin_rintf(u), -127.0f), 127.0f);
+    const float r1 = fminf(fmaxf(__builtin_rintf((u - r0) * 254.0f), -127.0f), 127.0f);
+    const int b = 64 * (i >> 2) + k_position(layout, sl + 16 * (i & 3));
+    l0[b] = (uint8_t)(int8_t)r0;
+    l1[b] = (uint8_t)(int8_t)r1;
+    s0 += (int32_t)r0;
+    s1 += (int32_t)r1;
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) {
+    s0 += __shfl_xor(s0, o, 16);
+    s1 += __shfl_xor(s1, o, 16);
+  }
+  qc = 254 * s0 + s1;
+}
+
+// The limb records of four consecutive queries, rows qt0 + g qt_stride and qh0 + g qh_stride
+// (LDS), one per 16-lane group; assembled in `stage` (4 records) and written to rec0 (the
+// first of four consecutive records) for the first n_valid of them.
+template <int D, int M>
+__device__ __forceinline__ void write_limb_records4(const float *qt0, int qt_stride, const float *qh0, int qh_stride,
+                                                    int n_valid, int bits, uint8_t *stage, uint8_t *rec0) {
+  constexpr int NK = (D + 63) / 64, NKM = (M + 63) / 64;
+  constexpr int R = limb_record_bytes(D, M);
+  static_assert(R % 16 == 0, "records in 16-byte words");
+  const int lane = lane_id(), g = lane >> 4;
+  uint8_t *st = stage + g * R;
+  float sig, sigh = 0.0f;
+  int32_t qc, qch = 0;
+  limbs_of16<D, NK>(qt0 + g * qt_stride, bits == 2 ? KL_CODE2 : KL_CONTIG, st, st + 64 * NK, sig, qc);
+  if constexpr (M > 0) limbs_of16<M, NKM>(qh0 + g * qh_stride, KL_SIGN, st + 128 * NK, st + 128 * NK + 64 * NKM, sigh, qch);
+  if ((lane & 15) == 0) {
+    float *cf = reinterpret_cast<float *>(st + 128 * (NK + NKM));
+    cf[0] = sig;
+    cf[1] = sigh;
+    reinterpret_cast<int32_t *>(cf)[2] = qc;
+    reinterpret_cast<int32_t *>(cf)[3] = qch;
+  }
+  wave_lds_fence();
+  for (int e = lane; e < 4 * (R / 16); e += kWave)
+    if (e / (R / 16) < n_valid) reinterpret_cast<uint4 *>(rec0)[e] = reinterpret_cast<const uint4 *>(stage)[e];
+  wave_lds_fence();  // the stage is reused by the wavefront's next records
+}
+
 // The limb records of n_q queries from q~ [n_q][D] and q^ [n_q][M]; one wavefront per query.
 template <int D, int M>
 __global__ __launch_bounds__(256) void planes_limbs(const float *qt, const float *qh, int64_t n_q, int bits,

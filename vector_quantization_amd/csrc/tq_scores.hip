@@ -204,14 +204,17 @@ __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
     }
   }
   if (a.limbs != nullptr) {
-    // one wavefront per head: the limb records straight from LDS
-    __shared__ __align__(16) uint8_t stage[256 / kWave][limb_record_bytes(D, M)];
+    // four heads per wavefront (16 lanes each): the limb records straight from LDS
+    static_assert(HEADS % 4 == 0, "heads in groups of four");
+    __shared__ __align__(16) uint8_t stage[256 / kWave][4 * limb_record_bytes(D, M)];
     __syncthreads();
-    for (int hh = threadIdx.x / kWave; hh < HEADS; hh += 256 / kWave) {
+    for (int hh = 4 * (threadIdx.x / kWave); hh < HEADS; hh += 4 * (256 / kWave)) {
       const int64_t h = h0 + hh;
-      if (h < a.n_heads)
-        write_limb_record<D, M>(qs[hh], qhs[hh], a.bits, stage[threadIdx.x / kWave],
-                                a.limbs + h * limb_record_bytes(D, M));
+      const int64_t left = a.n_heads - h;
+      if (left > 0)
+        write_limb_records4<D, M>(qs[hh], QSW, M > 0 ? qhs[hh] : nullptr, (M > 0 ? M : 1) + 1,
+                                  left < 4 ? (int)left : 4, a.bits, stage[threadIdx.x / kWave],
+                                  a.limbs + h * limb_record_bytes(D, M));
     }
   }
 }
