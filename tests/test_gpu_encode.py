@@ -80,9 +80,12 @@ def test_pre_rotated_bit_exact(d, bits, m):
     assert norms[0] == 0
 
 
-def test_exact_sign_fallback_with_crafted_sketch():
-    # rows of S whose dot product with r is exactly zero force the exact expansion path
-    d, bits, m = 64, 2, 64
+@pytest.mark.parametrize("d", [64, 200])
+def test_exact_sign_fallback_with_crafted_sketch(d):
+    # rows of S whose dot product with r is exactly zero force the exact expansion path (d = 64:
+    # the MFMA encoder's band; d = 200: the several-vectors-per-wavefront encoder's fp32 band;
+    # 509 rows there, so that its last group of 8 vectors is a partial one)
+    bits, m = 2, d
     g = np.random.default_rng(5)
     S = g.standard_normal((m, d)).astype(np.float32)
     S[0] = 0
@@ -96,7 +99,7 @@ def test_exact_sign_fallback_with_crafted_sketch():
     cb = oc.lloyd_max_beta(d, bits)
     lib = tq.codec_from_arrays(d, bits, m, rot, S, cb.centroids, cb.thresholds)
     ora = oc.Codec(d, bits, m, rot[None], S, cb.centroids, cb.thresholds)
-    y = synth.pre_rotated(512, d, seed=77)
+    y = synth.pre_rotated(512 if d == 64 else 509, d, seed=77)
     y[:, 1] = y[:, 0]  # r_0 == r_1: row 1 sums to exactly 0
     y[:, 3] = -y[:, 2]  # r_3 == -r_2: row 2 sums to exactly 0
     y[:, 6] = y[:, 4]  # row 3: 2^30 r_4 + r_5 - 2^30 r_4 == r_5

@@ -185,6 +185,266 @@ __global__ __launch_bounds__(kWave *kEncWaves) void encode_kernel(EncArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ several vectors per wavefront
+//
+// encode_multi: the encoder of encode_kernel for one shared rotation outside append mode, with
+// each wavefront taking EV vectors at a time, so that every element of Pi and S it reads from
+// cache serves EV vectors (encode_kernel reads the whole of both per vector: at d = 200 that is
+// 320 KB of cache traffic per 200-coordinate vector).  Lane l owns rotation rows and sketch rows
+// l + 64c for all EV vectors; the vectors themselves sit in LDS, read as broadcast float4s.
+//   - y: the same fp32 FMA chain per row as encode_kernel (k ascending), so the rotated values,
+//     and with them the records, are those encode_kernel writes;
+//   - norms, indices and residual: encode_kernel's steps, one vector after the other;
+//   - signs: z = S r by an fp32 FMA chain, whose error is at most gamma_D sum_k |S_jk r_k| <=
+//     2 (D + 2) 2^-24 ||S_j|| ||r|| (Cauchy-Schwarz), with ||S_j|| computed once per wavefront and
+//     ||r|| bounded from its exact fp16 norm; outside that band the sign of z is the sign of the
+//     exact dot product.  Inside it (or where r = 0) the wavefront takes the exact products in
+//     fp64 and decides from their fp64 sum and its error bound, or else by the exact expansion.
+
+constexpr int kMultiWaves = 4;
+constexpr int kMultiVec = 8;
+
+template <int D>
+struct MultiLds {
+  float xs[kMultiVec][D];  // the inputs; after the rotation, the residuals
+  uint8_t code[kMultiVec][D + 4];
+  double terms[D + 2];
+  double buf[D + 2];
+};
+
+template <int D, int BITS, int M, int TIN, bool PRE>
+__global__ __launch_bounds__(kWave *kMultiWaves) void encode_multi(EncArgs a) {
+  constexpr int C = (D + kWave - 1) / kWave;
+  constexpr int CM = (M + kWave - 1) / kWave;
+  constexpr int EV = kMultiVec;
+  constexpr int L = 1 << BITS;
+  static_assert(D % 4 == 0, "float4 rows");
+  __shared__ MultiLds<D> lds_all[kMultiWaves];
+  __shared__ float cbs[L];
+  const int lane = lane_id();
+  const int wid = threadIdx.x / kWave;
+  MultiLds<D> &s = lds_all[wid];
+  if (threadIdx.x < L) cbs[threadIdx.x] = a.centroids[threadIdx.x];
+  float th[L - 1];
+#pragma unroll
+  for (int j = 0; j < L - 1; ++j) th[j] = a.thresholds[j];
+  __syncthreads();
+
+  // ||S_j|| of the lane's sketch rows, rounded up: 2 (D + 2) 2^-24 ||S_j|| (1 + 2^-16) per row
+  float band[CM > 0 ? CM : 1];
+#pragma unroll
+  for (int c = 0; c < (CM > 0 ? CM : 1); ++c) {
+    band[c] = 0.0f;
+    if constexpr (M > 0) {
+      const int j = lane + kWave * c;
+      if (j < M) {
+        double ss = 0.0;
+        for (int k = 0; k < D; ++k) {
+          const double v = a.sketch[(int64_t)j * D + k];
+          ss += v * v;
+        }
+        band[c] = (float)(sqrt(ss) * (2.0 * (D + 2) * 0x1p-24) * (1.0 + 0x1p-16));
+      }
+    }
+  }
+
+  const int iw = (int)(a.idx_stride >> 2);
+  const int sw = M > 0 ? (int)(a.sign_stride >> 2) : 0;
+  const int64_t groups = (a.n + EV - 1) / EV;
+
+  for (int64_t grp = (int64_t)blockIdx.x * kMultiWaves + wid; grp < groups; grp += (int64_t)gridDim.x * kMultiWaves) {
+    const int64_t v0 = grp * EV;
+    // ---- load, the exact norms of the inputs, and the inputs staged for the rotation
+    float y[EV][C];
+    uint32_t n16[EV];
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+      float xin[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int i = lane + kWave * c;
+        xin[c] = (i < D && v0 + e < a.n) ? load_in<TIN>(a.x, (v0 + e) * a.ld_x + i) : 0.0f;
+        if (!PRE && i < D) s.xs[e][i] = xin[c];
+        y[e][c] = xin[c];
+      }
+      n16[e] = wave_norm_f16<D, C>(xin, s.terms, s.buf);
+    }
+    if constexpr (!PRE) {
+      wave_lds_fence();
+#pragma unroll
+      for (int e = 0; e < EV; ++e)
+#pragma unroll
+        for (int c = 0; c < C; ++c) y[e][c] = 0.0f;
+      const float4 *rows[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int i = lane + kWave * c;
+        rows[c] = reinterpret_cast<const float4 *>(a.rot + (int64_t)(i < D ? i : 0) * D);
+      }
+      for (int k4 = 0; k4 < D / 4; ++k4) {
+        float4 p[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) p[c] = rows[c][k4];
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+          const float4 xv = *reinterpret_cast<const float4 *>(&s.xs[e][4 * k4]);
+#pragma unroll
+          for (int c = 0; c < C; ++c) {
+            float acc = y[e][c];
+            acc = fmaf(p[c].x, xv.x, acc);
+            acc = fmaf(p[c].y, xv.y, acc);
+            acc = fmaf(p[c].z, xv.z, acc);
+            acc = fmaf(p[c].w, xv.w, acc);
+            y[e][c] = acc;
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EV; ++e)
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+          if (lane + kWave * c >= D) y[e][c] = 0.0f;
+      wave_lds_fence();  // every lane is done with the inputs before the residuals replace them
+    }
+    if (a.y_tap) {
+#pragma unroll
+      for (int e = 0; e < EV; ++e)
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+          if (lane + kWave * c < D && v0 + e < a.n) a.y_tap[(v0 + e) * D + lane + kWave * c] = y[e][c];
+    }
+
+    // ---- stage 1 and the residual, one vector after the other
+    uint32_t nw[EV];
+    float rbound[EV];
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+      const float nbar = f16_bits_to_float(n16[e]);
+      float thr[L - 1];
+#pragma unroll
+      for (int j = 0; j < L - 1; ++j) thr[j] = __fmul_rn(nbar, th[j]);
+      float r[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int i = lane + kWave * c;
+        int q = 0;
+#pragma unroll
+        for (int j = 0; j < L - 1; ++j) q += (y[e][c] >= thr[j]) ? 1 : 0;
+        r[c] = 0.0f;
+        if (i < D) {
+          s.code[e][i] = (uint8_t)q;
+          r[c] = __fsub_rn(y[e][c], __fmul_rn(nbar, cbs[q]));
+          s.xs[e][i] = r[c];
+        }
+      }
+      const uint32_t rn16 = wave_norm_f16<D, C>(r, s.terms, s.buf);
+      nw[e] = (hi_word(rn16, nbar, a.resid_scale) << 16) | n16[e];
+      // ||r|| <= fp16(||r||) + max(2^-11 ||r||, 2^-25) < fp16(||r||) * 1.001 + 2^-25 (the fp16 word
+      // is the correctly rounded norm: half a spacing, relative for normal values, 2^-25 below)
+      rbound[e] = fmaf(f16_bits_to_float(rn16), 1.001f, 0x1p-25f);
+    }
+    wave_lds_fence();
+
+    // ---- index words
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+      if (v0 + e >= a.n) break;  // uniform
+      for (int w = lane; w < iw; w += kWave) {
+        uint32_t word = 0;
+        const int b0 = 32 * w;
+        if (b0 < D * BITS) {
+          const int i0 = b0 / BITS;
+          int i1 = (b0 + 31) / BITS;
+          if (i1 > D - 1) i1 = D - 1;
+          for (int i = i0; i <= i1; ++i) {
+            const int off = BITS * i - b0;
+            const uint32_t cv = s.code[e][i];
+            word |= off >= 0 ? (cv << off) : (cv >> (-off));
+          }
+        }
+        reinterpret_cast<uint32_t *>(a.idx + (v0 + e) * a.idx_stride)[w] = word;
+      }
+      if (lane == 0) a.norms[v0 + e] = nw[e];
+    }
+
+    // ---- stage 2: sign words
+    if constexpr (M > 0) {
+      float z[EV][CM];
+#pragma unroll
+      for (int e = 0; e < EV; ++e)
+#pragma unroll
+        for (int c = 0; c < CM; ++c) z[e][c] = 0.0f;
+      const float4 *srow[CM];
+#pragma unroll
+      for (int c = 0; c < CM; ++c) {
+        const int j = lane + kWave * c;
+        srow[c] = reinterpret_cast<const float4 *>(a.sketch + (int64_t)(j < M ? j : 0) * D);
+      }
+      for (int k4 = 0; k4 < D / 4; ++k4) {
+        float4 p[CM];
+#pragma unroll
+        for (int c = 0; c < CM; ++c) p[c] = srow[c][k4];
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+          const float4 rv = *reinterpret_cast<const float4 *>(&s.xs[e][4 * k4]);
+#pragma unroll
+          for (int c = 0; c < CM; ++c) {
+            float acc = z[e][c];
+            acc = fmaf(p[c].x, rv.x, acc);
+            acc = fmaf(p[c].y, rv.y, acc);
+            acc = fmaf(p[c].z, rv.z, acc);
+            acc = fmaf(p[c].w, rv.w, acc);
+            z[e][c] = acc;
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EV; ++e) {
+        if (v0 + e >= a.n) break;  // uniform
+        uint64_t masks[CM];
+#pragma unroll
+        for (int c = 0; c < CM; ++c) {
+          const int j = lane + kWave * c;
+          bool bit = z[e][c] >= 0.0f;
+          const bool amb = (j < M) && !(fabsf(z[e][c]) > band[c] * rbound[e]);
+          uint64_t am = __ballot(amb);
+          while (am) {  // rows the fp32 band cannot decide, one at a time
+            const int src = __ffsll((unsigned long long)am) - 1;
+            const int j0 = src + kWave * c;
+            for (int k = lane; k < D; k += kWave) s.terms[k] = (double)a.sketch[(int64_t)j0 * D + k] * (double)s.xs[e][k];
+            wave_lds_fence();
+            int sg = 0;
+            if (lane == 0) {
+              double zz = 0.0, bb = 0.0;
+              for (int k = 0; k < D; ++k) {
+                zz += s.terms[k];
+                bb += fabs(s.terms[k]);
+              }
+              if (fabs(zz) > 2.0 * (D + 2) * 0x1p-53 * bb) sg = zz > 0.0 ? 1 : -1;
+              else if (bb == 0.0) sg = 0;
+              else sg = expansion_sign(s.terms, D, s.buf);
+            }
+            wave_lds_fence();
+            sg = __shfl(sg, 0, kWave);
+            if (lane == src) bit = sg >= 0;
+            am &= am - 1;
+          }
+          masks[c] = __ballot((j < M) && bit);
+        }
+        uint32_t *out = reinterpret_cast<uint32_t *>(a.sign + (v0 + e) * a.sign_stride);
+        for (int w = lane; w < sw; w += kWave) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int c = 0; c < CM; ++c)
+            if ((w >> 1) == c) word = (w & 1) ? (uint32_t)(masks[c] >> 32) : (uint32_t)masks[c];
+          out[w] = word;
+        }
+      }
+    }
+    wave_lds_fence();  // the next group overwrites this wavefront's LDS
+  }
+}
+
 // ------------------------------------------------------------------ MFMA encode (d = 64, 128)
 //
 // Persistent workgroups of NW wavefronts; every wavefront runs its own passes of 32 vectors
@@ -1229,6 +1489,27 @@ static int launch_enc_dm(const EncArgs &a, int dt, bool pre, hipStream_t st) {
         }
         return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
       }
+    }
+  }
+  if constexpr (D % 32 != 0) {
+    // one shared rotation outside append mode: several vectors per wavefront
+    if (a.pos == nullptr && !(a.n_rot > 1 && a.vecs_per_rot > 0)) {
+      int64_t blocks = (a.n + kMultiVec * kMultiWaves - 1) / (kMultiVec * kMultiWaves);
+      if (blocks > 256 * 8) blocks = 256 * 8;
+      dim3 grid((unsigned)blocks), block(kWave * kMultiWaves);
+      if (pre) {
+        if (dt != TQ_F32) return TQ_EINVAL;
+        hipLaunchKernelGGL((encode_multi<D, BITS, M, TQ_F32, true>), grid, block, 0, st, a);
+      } else if (dt == TQ_F32) {
+        hipLaunchKernelGGL((encode_multi<D, BITS, M, TQ_F32, false>), grid, block, 0, st, a);
+      } else if (dt == TQ_F16) {
+        hipLaunchKernelGGL((encode_multi<D, BITS, M, TQ_F16, false>), grid, block, 0, st, a);
+      } else if (dt == TQ_BF16) {
+        hipLaunchKernelGGL((encode_multi<D, BITS, M, TQ_BF16, false>), grid, block, 0, st, a);
+      } else {
+        return TQ_EINVAL;
+      }
+      return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
     }
   }
   int64_t blocks = (a.n + kEncWaves - 1) / kEncWaves;
