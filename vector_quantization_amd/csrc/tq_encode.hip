@@ -188,10 +188,13 @@ __global__ __launch_bounds__(kWave *kEncWaves) void encode_kernel(EncArgs a) {
 // ------------------------------------------------------------------ several vectors per wavefront
 //
 // encode_multi: the encoder of encode_kernel for one shared rotation outside append mode, with
-// each wavefront taking EV vectors at a time, so that every element of Pi and S it reads from
-// cache serves EV vectors (encode_kernel reads the whole of both per vector: at d = 200 that is
-// 320 KB of cache traffic per 200-coordinate vector).  Lane l owns rotation rows and sketch rows
-// l + 64c for all EV vectors; the vectors themselves sit in LDS, read as broadcast float4s.
+// the wavefronts of a workgroup taking MV_W x MV_E vectors at a time (MV_E per wavefront), so
+// that Pi and S pass through the CU once per MV_W x MV_E vectors instead of once per vector
+// (encode_kernel streams all 320 KB of both per 200-coordinate vector through the cache, 64
+// rows at a time, one 16-byte piece of each row per load).  The workgroup stages MV_KC columns
+// of Pi (then of S) in LDS, double-buffered and read by every wavefront; lane l owns rotation
+// rows and sketch rows l + 64c for its wavefront's MV_E vectors, which sit in LDS and are read
+// as broadcast float4s.
 //   - y: the same fp32 FMA chain per row as encode_kernel (k ascending), so the rotated values,
 //     and with them the records, are those encode_kernel writes;
 //   - norms, indices and residual: encode_kernel's steps, one vector after the other;
@@ -201,8 +204,10 @@ __global__ __launch_bounds__(kWave *kEncWaves) void encode_kernel(EncArgs a) {
 //     exact dot product.  Inside it (or where r = 0) the wavefront takes the exact products in
 //     fp64 and decides from their fp64 sum and its error bound, or else by the exact expansion.
 
-constexpr int kMultiWaves = 4;
-constexpr int kMultiVec = 8;
+constexpr int kMultiWaves = 4;  // MV_W
+constexpr int kMultiVec = 8;    // MV_E
+constexpr int kMultiCols = 8;   // MV_KC: columns of Pi or S per staged chunk
+constexpr int kMultiStride = 12;  // floats per staged row: 16-byte reads of 16 lanes on distinct banks
 
 template <int D>
 struct MultiLds {
@@ -212,14 +217,89 @@ struct MultiLds {
   double buf[D + 2];
 };
 
+// Columns [kc * MV_KC, kc * MV_KC + MV_KC) of the rows x D matrix W into dst[row * stride + col],
+// by the whole workgroup (two float4 per row).
+template <int D>
+__device__ __forceinline__ void multi_fetch(const float *W, int rows, int kc, float4 (&r)[2], int nthreads) {
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int f = threadIdx.x + nthreads * it;
+    r[it] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (f < 2 * rows) r[it] = reinterpret_cast<const float4 *>(W + (int64_t)(f >> 1) * D + kc * kMultiCols)[f & 1];
+  }
+}
+__device__ __forceinline__ void multi_stage(float *dst, int rows, const float4 (&r)[2], int nthreads) {
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int f = threadIdx.x + nthreads * it;
+    if (f < 2 * rows) *reinterpret_cast<float4 *>(dst + (f >> 1) * kMultiStride + 4 * (f & 1)) = r[it];
+  }
+}
+
+// acc[e][c] += sum over the chunk's columns of W[row(c)][k] * xs[e][k], k ascending, for the
+// lane's rows l + 64c (rows >= nrows read row 0 of the chunk; the caller discards them).
+template <int D, int CR>
+__device__ __forceinline__ void multi_chunk(const float *wl, const float (*xs)[D], int kc, int nrows,
+                                            float (&acc)[kMultiVec][CR]) {
+  const int lane = lane_id();
+  float4 p[CR][2];
+#pragma unroll
+  for (int c = 0; c < CR; ++c) {
+    const int i = lane + kWave * c;
+    const float *row = wl + (i < nrows ? i : 0) * kMultiStride;
+    p[c][0] = *reinterpret_cast<const float4 *>(row);
+    p[c][1] = *reinterpret_cast<const float4 *>(row + 4);
+  }
+#pragma unroll
+  for (int e = 0; e < kMultiVec; ++e) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float4 xv = *reinterpret_cast<const float4 *>(&xs[e][kc * kMultiCols + 4 * h]);
+#pragma unroll
+      for (int c = 0; c < CR; ++c) {
+        float a = acc[e][c];
+        a = fmaf(p[c][h].x, xv.x, a);
+        a = fmaf(p[c][h].y, xv.y, a);
+        a = fmaf(p[c][h].z, xv.z, a);
+        a = fmaf(p[c][h].w, xv.w, a);
+        acc[e][c] = a;
+      }
+    }
+  }
+}
+
+// acc = W xs over all D columns, W (rows x D) staged chunk by chunk in the two buffers wl; the
+// whole workgroup calls it (barriers inside).
+template <int D, int CR>
+__device__ void multi_product(const float *W, int rows, float *wl0, float *wl1, const float (*xs)[D],
+                              float (&acc)[kMultiVec][CR]) {
+  constexpr int NC = D / kMultiCols;
+  constexpr int NTH = kWave * kMultiWaves;
+  float4 r[2];
+  multi_fetch<D>(W, rows, 0, r, NTH);
+  __syncthreads();  // every wavefront is done with both buffers
+  multi_stage(wl0, rows, r, NTH);
+  __syncthreads();
+  for (int kc = 0; kc < NC; ++kc) {
+    float *cur = (kc & 1) ? wl1 : wl0;
+    float *nxt = (kc & 1) ? wl0 : wl1;
+    if (kc + 1 < NC) multi_fetch<D>(W, rows, kc + 1, r, NTH);
+    multi_chunk<D, CR>(cur, xs, kc, rows, acc);
+    if (kc + 1 < NC) multi_stage(nxt, rows, r, NTH);
+    __syncthreads();
+  }
+}
+
 template <int D, int BITS, int M, int TIN, bool PRE>
 __global__ __launch_bounds__(kWave *kMultiWaves) void encode_multi(EncArgs a) {
   constexpr int C = (D + kWave - 1) / kWave;
   constexpr int CM = (M + kWave - 1) / kWave;
   constexpr int EV = kMultiVec;
   constexpr int L = 1 << BITS;
-  static_assert(D % 4 == 0, "float4 rows");
-  __shared__ MultiLds<D> lds_all[kMultiWaves];
+  constexpr int ROWS = D > M ? D : M;
+  static_assert(D % kMultiCols == 0 && ROWS <= kWave * kMultiWaves, "staged chunks");
+  __shared__ __align__(16) MultiLds<D> lds_all[kMultiWaves];
+  __shared__ __align__(16) float wl[2][ROWS * kMultiStride];
   __shared__ float cbs[L];
   const int lane = lane_id();
   const int wid = threadIdx.x / kWave;
@@ -230,7 +310,7 @@ __global__ __launch_bounds__(kWave *kMultiWaves) void encode_multi(EncArgs a) {
   for (int j = 0; j < L - 1; ++j) th[j] = a.thresholds[j];
   __syncthreads();
 
-  // ||S_j|| of the lane's sketch rows, rounded up: 2 (D + 2) 2^-24 ||S_j|| (1 + 2^-16) per row
+  // 2 (D + 2) 2^-24 ||S_j|| (1 + 2^-16) for the lane's sketch rows
   float band[CM > 0 ? CM : 1];
 #pragma unroll
   for (int c = 0; c < (CM > 0 ? CM : 1); ++c) {
@@ -250,10 +330,11 @@ __global__ __launch_bounds__(kWave *kMultiWaves) void encode_multi(EncArgs a) {
 
   const int iw = (int)(a.idx_stride >> 2);
   const int sw = M > 0 ? (int)(a.sign_stride >> 2) : 0;
-  const int64_t groups = (a.n + EV - 1) / EV;
+  const int64_t groups = (a.n + EV * kMultiWaves - 1) / (EV * kMultiWaves);
 
-  for (int64_t grp = (int64_t)blockIdx.x * kMultiWaves + wid; grp < groups; grp += (int64_t)gridDim.x * kMultiWaves) {
-    const int64_t v0 = grp * EV;
+  // uniform over the workgroup: every wavefront runs the same number of staged products
+  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    const int64_t v0 = (grp * kMultiWaves + wid) * EV;
     // ---- load, the exact norms of the inputs, and the inputs staged for the rotation
     float y[EV][C];
     uint32_t n16[EV];
@@ -270,41 +351,17 @@ __global__ __launch_bounds__(kWave *kMultiWaves) void encode_multi(EncArgs a) {
       n16[e] = wave_norm_f16<D, C>(xin, s.terms, s.buf);
     }
     if constexpr (!PRE) {
-      wave_lds_fence();
 #pragma unroll
       for (int e = 0; e < EV; ++e)
 #pragma unroll
         for (int c = 0; c < C; ++c) y[e][c] = 0.0f;
-      const float4 *rows[C];
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int i = lane + kWave * c;
-        rows[c] = reinterpret_cast<const float4 *>(a.rot + (int64_t)(i < D ? i : 0) * D);
-      }
-      for (int k4 = 0; k4 < D / 4; ++k4) {
-        float4 p[C];
-#pragma unroll
-        for (int c = 0; c < C; ++c) p[c] = rows[c][k4];
-#pragma unroll
-        for (int e = 0; e < EV; ++e) {
-          const float4 xv = *reinterpret_cast<const float4 *>(&s.xs[e][4 * k4]);
-#pragma unroll
-          for (int c = 0; c < C; ++c) {
-            float acc = y[e][c];
-            acc = fmaf(p[c].x, xv.x, acc);
-            acc = fmaf(p[c].y, xv.y, acc);
-            acc = fmaf(p[c].z, xv.z, acc);
-            acc = fmaf(p[c].w, xv.w, acc);
-            y[e][c] = acc;
-          }
-        }
-      }
+      wave_lds_fence();
+      multi_product<D, C>(a.rot, D, wl[0], wl[1], s.xs, y);  // ends with a barrier
 #pragma unroll
       for (int e = 0; e < EV; ++e)
 #pragma unroll
         for (int c = 0; c < C; ++c)
           if (lane + kWave * c >= D) y[e][c] = 0.0f;
-      wave_lds_fence();  // every lane is done with the inputs before the residuals replace them
     }
     if (a.y_tap) {
 #pragma unroll
@@ -348,7 +405,7 @@ __global__ __launch_bounds__(kWave *kMultiWaves) void encode_multi(EncArgs a) {
     // ---- index words
 #pragma unroll
     for (int e = 0; e < EV; ++e) {
-      if (v0 + e >= a.n) break;  // uniform
+      if (v0 + e >= a.n) break;  // uniform over the wavefront
       for (int w = lane; w < iw; w += kWave) {
         uint32_t word = 0;
         const int b0 = 32 * w;
@@ -374,33 +431,10 @@ __global__ __launch_bounds__(kWave *kMultiWaves) void encode_multi(EncArgs a) {
       for (int e = 0; e < EV; ++e)
 #pragma unroll
         for (int c = 0; c < CM; ++c) z[e][c] = 0.0f;
-      const float4 *srow[CM];
-#pragma unroll
-      for (int c = 0; c < CM; ++c) {
-        const int j = lane + kWave * c;
-        srow[c] = reinterpret_cast<const float4 *>(a.sketch + (int64_t)(j < M ? j : 0) * D);
-      }
-      for (int k4 = 0; k4 < D / 4; ++k4) {
-        float4 p[CM];
-#pragma unroll
-        for (int c = 0; c < CM; ++c) p[c] = srow[c][k4];
-#pragma unroll
-        for (int e = 0; e < EV; ++e) {
-          const float4 rv = *reinterpret_cast<const float4 *>(&s.xs[e][4 * k4]);
-#pragma unroll
-          for (int c = 0; c < CM; ++c) {
-            float acc = z[e][c];
-            acc = fmaf(p[c].x, rv.x, acc);
-            acc = fmaf(p[c].y, rv.y, acc);
-            acc = fmaf(p[c].z, rv.z, acc);
-            acc = fmaf(p[c].w, rv.w, acc);
-            z[e][c] = acc;
-          }
-        }
-      }
+      multi_product<D, CM>(a.sketch, M, wl[0], wl[1], s.xs, z);  // ends with a barrier
 #pragma unroll
       for (int e = 0; e < EV; ++e) {
-        if (v0 + e >= a.n) break;  // uniform
+        if (v0 + e >= a.n) break;  // uniform over the wavefront
         uint64_t masks[CM];
 #pragma unroll
         for (int c = 0; c < CM; ++c) {
@@ -1495,7 +1529,7 @@ static int launch_enc_dm(const EncArgs &a, int dt, bool pre, hipStream_t st) {
     // one shared rotation outside append mode: several vectors per wavefront
     if (a.pos == nullptr && !(a.n_rot > 1 && a.vecs_per_rot > 0)) {
       int64_t blocks = (a.n + kMultiVec * kMultiWaves - 1) / (kMultiVec * kMultiWaves);
-      if (blocks > 256 * 8) blocks = 256 * 8;
+      if (blocks > 256 * 2) blocks = 256 * 2;
       dim3 grid((unsigned)blocks), block(kWave * kMultiWaves);
       if (pre) {
         if (dt != TQ_F32) return TQ_EINVAL;
