@@ -86,11 +86,16 @@ __global__ __launch_bounds__(256) void qprep_kernel(QprepArgs a) {
 
 // Tiled variant for 16 query heads that share one rotation (one shared rotation, or per-block
 // rotations with a multiple of 16 query heads per kv head): a block takes the 16 heads and
-// computes q~ = q Pi^T, then q^ = q~ S^T, staging 8-column tiles of Pi (or S) transposed in LDS
-// so that the output columns are read without bank conflicts.
+// computes q~ = q Pi^T, then q^ = q~ S^T, staging column tiles of Pi (or S) transposed in LDS
+// so that the output columns are read without bank conflicts.  The next tile is requested into
+// registers before the current one is used, so the block waits for one memory latency per
+// tile at most, and tiles of 32 columns (d a multiple of 32; else 8) keep the tile count low:
+// the prologue of a decode step is this chain of tiles.
 constexpr int kQpHeads = 16;
 constexpr int kQpHeadsMany = 64;
 constexpr int kQpKt = 8;  // a multiple of 4 dividing every supported d
+template <int D>
+constexpr int qp_kt() { return D % 32 == 0 ? 32 : kQpKt; }
 
 template <int D, int M, int HEADS>
 __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
@@ -102,7 +107,9 @@ __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
   constexpr int QSW = (D + 4) / 4 * 4;
   __shared__ __align__(16) float qs[HEADS][QSW];
   __shared__ float qhs[HEADS][(M > 0 ? M : 1) + 1];
-  __shared__ float rt[kQpKt][NOUT + 1];
+  constexpr int KT = qp_kt<D>();
+  constexpr int TLD = (NOUT * KT + 255) / 256;  // tile elements per thread
+  __shared__ float rt[KT][NOUT + 1];
   const int tid = threadIdx.x;
   const int64_t h0 = (int64_t)blockIdx.x * HEADS;
   // the rotation of the key block that head h0 reads (the same for all HEADS heads)
@@ -113,6 +120,23 @@ __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
     if (r > a.n_rot - 1) r = a.n_rot - 1;
     rot += r * D * D;
   }
+  // tile k0 of W (rows x D): columns k0 .. k0 + KT - 1 into registers, then transposed into rt
+  float pre[TLD];
+  auto fetch = [&](const float *W, int rows, int k0) {
+#pragma unroll
+    for (int u = 0; u < TLD; ++u) {
+      const int e = tid + 256 * u;
+      pre[u] = e < rows * KT ? W[(int64_t)(e / KT) * D + k0 + e % KT] : 0.0f;
+    }
+  };
+  auto stage = [&](int rows) {
+#pragma unroll
+    for (int u = 0; u < TLD; ++u) {
+      const int e = tid + 256 * u;
+      if (e < rows * KT) rt[e % KT][e / KT] = pre[u];
+    }
+  };
+  fetch(rot, D, 0);
   for (int e = tid; e < HEADS * D; e += 256) {
     int64_t h = h0 + e / D;
     if (h > a.n_heads - 1) h = a.n_heads - 1;
@@ -130,56 +154,19 @@ __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
   const int hs = tid / NOUT;
   const bool active = hs < TPC;
   float acc[HPT];
-  // ---- q~ = q Pi^T
-#pragma unroll
-  for (int j = 0; j < HPT; ++j) acc[j] = 0.0f;
-  for (int k0 = 0; k0 < D; k0 += kQpKt) {
-    __syncthreads();
-    for (int e = tid; e < D * kQpKt; e += 256) {
-      const int i = e / kQpKt, kk = e % kQpKt;
-      rt[kk][i] = rot[(int64_t)i * D + k0 + kk];
-    }
-    __syncthreads();
-    if (active && col < D) {
-#pragma unroll
-      for (int k4 = 0; k4 < kQpKt; k4 += 4) {
-        float r[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) r[t] = rt[k4 + t][col];
-#pragma unroll
-        for (int j = 0; j < HPT; ++j) {
-          const float4 x = *reinterpret_cast<const float4 *>(&qs[hs * HPT + j][k0 + k4]);
-          acc[j] = fmaf(r[0], x.x, acc[j]);
-          acc[j] = fmaf(r[1], x.y, acc[j]);
-          acc[j] = fmaf(r[2], x.z, acc[j]);
-          acc[j] = fmaf(r[3], x.w, acc[j]);
-        }
-      }
-    }
-  }
-  __syncthreads();
-  if (active && col < D) {
-#pragma unroll
-    for (int j = 0; j < HPT; ++j) {
-      const int64_t h = h0 + hs * HPT + j;
-      qs[hs * HPT + j][col] = acc[j];
-      if (h < a.n_heads && a.limbs == nullptr) a.qt[h * D + col] = acc[j];
-    }
-  }
-  if constexpr (M > 0) {
-    // ---- q^ = q~ S^T
+  // out[col] = sum_k W[col][k] in[k] over the staged tiles of W, k ascending (the next tile in
+  // flight while the current one is used)
+  auto product = [&](const float *W, int rows) {
 #pragma unroll
     for (int j = 0; j < HPT; ++j) acc[j] = 0.0f;
-    for (int k0 = 0; k0 < D; k0 += kQpKt) {
+    for (int k0 = 0; k0 < D; k0 += KT) {
       __syncthreads();
-      for (int e = tid; e < M * kQpKt; e += 256) {
-        const int i = e / kQpKt, kk = e % kQpKt;
-        rt[kk][i] = a.sketch[(int64_t)i * D + k0 + kk];
-      }
+      stage(rows);
       __syncthreads();
-      if (active && col < M) {
+      if (k0 + KT < D) fetch(W, rows, k0 + KT);
+      if (active && col < rows) {
 #pragma unroll
-        for (int k4 = 0; k4 < kQpKt; k4 += 4) {
+        for (int k4 = 0; k4 < KT; k4 += 4) {
           float r[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) r[t] = rt[k4 + t][col];
@@ -194,6 +181,22 @@ __global__ __launch_bounds__(256) void qprep_tiled(QprepArgs a) {
         }
       }
     }
+  };
+  // ---- q~ = q Pi^T
+  product(rot, D);
+  if constexpr (M > 0) fetch(a.sketch, M, 0);  // the first tile of S while q~ is stored
+  __syncthreads();
+  if (active && col < D) {
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) {
+      const int64_t h = h0 + hs * HPT + j;
+      qs[hs * HPT + j][col] = acc[j];
+      if (h < a.n_heads && a.limbs == nullptr) a.qt[h * D + col] = acc[j];
+    }
+  }
+  if constexpr (M > 0) {
+    // ---- q^ = q~ S^T
+    product(a.sketch, M);
     if (active && col < M) {
 #pragma unroll
       for (int j = 0; j < HPT; ++j) {
