@@ -466,6 +466,24 @@ struct CombArgs {
   float *out;
 };
 
+// sum_i W[i * ld + col] v[i] for i = 0 .. N - 1, i ascending (one fp32 FMA chain), with the
+// column's elements requested 32 at a time so that a chain waits for one load latency per 32
+// elements instead of one per few
+template <int N>
+__device__ __forceinline__ float column_dot(const float *W, int64_t ld, int col, const float *v, float acc) {
+  constexpr int B = 32;
+#pragma unroll 1
+  for (int i0 = 0; i0 < N; i0 += B) {
+    float w[B];
+#pragma unroll
+    for (int t = 0; t < B; ++t) w[t] = (i0 + t < N) ? W[(int64_t)(i0 + t) * ld + col] : 0.0f;
+#pragma unroll
+    for (int t = 0; t < B; ++t)
+      if (i0 + t < N) acc = fmaf(w[t], v[i0 + t], acc);
+  }
+  return acc;
+}
+
 template <int D, int VM>
 __global__ __launch_bounds__(256) void attend_combine(CombArgs a) {
   constexpr int NOUT = D + VM;
@@ -495,9 +513,7 @@ __global__ __launch_bounds__(256) void attend_combine(CombArgs a) {
   // u = A_rot + S_V^T A_sk in the rotated space (A_sk already carries sqrt(pi/2)/m)
   for (int i = lane; i < D; i += kWave) {
     float u = av[wid][i];
-    if constexpr (VM > 0) {
-      for (int j = 0; j < VM; ++j) u = fmaf(a.vsketch[(int64_t)j * D + i], av[wid][D + j], u);
-    }
+    if constexpr (VM > 0) u = column_dot<VM>(a.vsketch, D, i, &av[wid][D], u);
     uv[wid][i] = u;
   }
   wave_lds_fence();
@@ -510,11 +526,7 @@ __global__ __launch_bounds__(256) void attend_combine(CombArgs a) {
     if (rid > a.n_rot - 1) rid = a.n_rot - 1;
   }
   const float *R = a.vrot + rid * (int64_t)D * D;
-  for (int k = lane; k < D; k += kWave) {
-    float o = 0.0f;
-    for (int i = 0; i < D; ++i) o = fmaf(R[(int64_t)i * D + k], uv[wid][i], o);  // (Pi^T u)_k
-    a.out[hidx * D + k] = o;
-  }
+  for (int k = lane; k < D; k += kWave) a.out[hidx * D + k] = column_dot<D>(R, D, k, uv[wid], 0.0f);  // (Pi^T u)_k
 }
 
 // ------------------------------------------------------------------ host side
