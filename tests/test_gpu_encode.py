@@ -80,11 +80,12 @@ def test_pre_rotated_bit_exact(d, bits, m):
     assert norms[0] == 0
 
 
-@pytest.mark.parametrize("d", [64, 200])
-def test_exact_sign_fallback_with_crafted_sketch(d):
+@pytest.mark.parametrize("d,blocks", [(64, False), (200, False), (200, True)])
+def test_exact_sign_fallback_with_crafted_sketch(d, blocks):
     # rows of S whose dot product with r is exactly zero force the exact expansion path (d = 64:
-    # the MFMA encoder's band; d = 200: the several-vectors-per-wavefront encoder's fp32 band;
-    # 509 rows there, so that its last group of 8 vectors is a partial one)
+    # the MFMA encoder's band; d = 200: the several-vectors-per-wavefront encoder's fp32 band,
+    # 509 rows there, so that its last group of 8 vectors is a partial one; d = 200 with two
+    # rotation blocks: the one-wavefront-per-vector encoder's fp32 band, then its fp64 sum)
     bits, m = 2, d
     g = np.random.default_rng(5)
     S = g.standard_normal((m, d)).astype(np.float32)
@@ -97,7 +98,8 @@ def test_exact_sign_fallback_with_crafted_sketch(d):
     S[3, 4], S[3, 5], S[3, 6] = 2.0 ** 30, 1.0, -(2.0 ** 30)
     rot = np.eye(d, dtype=np.float32)
     cb = oc.lloyd_max_beta(d, bits)
-    lib = tq.codec_from_arrays(d, bits, m, rot, S, cb.centroids, cb.thresholds)
+    lib = tq.codec_from_arrays(d, bits, m, np.stack([rot, rot]) if blocks else rot, S, cb.centroids,
+                               cb.thresholds, vecs_per_rot=256 if blocks else 0)
     ora = oc.Codec(d, bits, m, rot[None], S, cb.centroids, cb.thresholds)
     y = synth.pre_rotated(512 if d == 64 else 509, d, seed=77)
     y[:, 1] = y[:, 0]  # r_0 == r_1: row 1 sums to exactly 0
