@@ -214,3 +214,42 @@ def test_scores_many_heads_asymmetric_codebook():
         err = rel_err_rows(got, want)
         say("  ", d, bits, m, "max rel err", err.max())
         assert err.max() <= TOL
+
+
+def test_full_size_esm2_all_pairs_sampled():
+    """The all-pairs scoring of the ESM-2-shaped cache in the bench's launch configuration: 33
+    layers x 20 heads, every one of the 1024 tokens a query head of its (layer, head), one rotation
+    per (layer, head) -- the query prep with 64 heads per workgroup (from 65536 query heads on) and
+    the bit-plane scan.  Seeded random code planes; 48 sampled (kv block, query) rows and the whole
+    last block against the oracle."""
+    w = synth.ESM2
+    say("scores full size all pairs", w.name)
+    seeds = [synth.esm2_basis_seed(l, h) for l in range(w.layers) for h in range(w.hkv)]
+    lib = tq.make_codec(w.d, w.k_bits, w.k_m, synth.SEED_ROT_K, synth.SEED_SKETCH_K, basis_seeds=seeds,
+                        vecs_per_rot=w.n_ctx)
+    ora = oc.make_codec(w.d, w.k_bits, w.k_m, synth.SEED_ROT_K, synth.SEED_SKETCH_K, basis_seeds=seeds,
+                        vecs_per_rot=w.n_ctx)
+    n_blk = w.layers * w.hkv
+    n_vec = n_blk * w.n_ctx
+    idx, sign, norms = synth.random_codes(n_vec, w.d, w.k_bits, w.k_m, lib.idx_stride, lib.sign_stride, seed=43)
+    codes = to_device_codes(tq, idx, sign, norms)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(44)
+    q = torch.randn((w.layers, w.hkv * w.n_ctx, w.d), generator=gen, device="cuda")
+    assert q.shape[0] * q.shape[1] >= 65536  # the 64-heads-per-workgroup query prep
+    logits = tq.scores(lib, q, codes, w.n_ctx, w.hkv)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(45)
+    picks = [(int(b), int(t)) for b, t in zip(g.integers(0, n_blk, 48), g.integers(0, w.n_ctx, 48))]
+    picks += [(n_blk - 1, t) for t in (0, 511, w.n_ctx - 1)]
+    worst = 0.0
+    for blk, t in picks:
+        l, h = divmod(blk, w.hkv)
+        sl = slice(blk * w.n_ctx, (blk + 1) * w.n_ctx)
+        qv = q[l, h * w.n_ctx + t].cpu().numpy().astype(np.float64)
+        want = oe.scores_one(qv, oracle_codes(idx[sl], sign[sl], norms[sl]), ora, blk)
+        got = logits[l, h * w.n_ctx + t].cpu().numpy()
+        err = rel_err_rows(got, want)
+        worst = max(worst, float(err))
+        assert err <= TOL, (blk, t, err)
+    say("  rows", len(picks), "max rel err", worst)
