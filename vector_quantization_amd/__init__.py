@@ -200,22 +200,23 @@ def _ptr(t):
 
 
 def _need(cond, msg):
+    """Raise ValueError(msg) unless cond; msg may be a callable, formatted only on failure."""
     if not cond:
-        raise ValueError(msg)
+        raise ValueError(msg() if callable(msg) else msg)
 
 
 def _check_tensor(t, name, dtype=None, shape=None, rows_contiguous=False):
     torch = _torch()
-    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _need(isinstance(t, torch.Tensor), lambda: f"{name} must be a torch tensor")
     if dtype is not None:
-        _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+        _need(t.dtype == dtype, lambda: f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None:
-        _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        _need(tuple(t.shape) == tuple(shape), lambda: f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if rows_contiguous:
         _need(t.dim() == 2 and (t.shape[0] <= 1 or t.stride(0) == t.shape[1]) and (t.shape[1] <= 1 or t.stride(1) == 1),
-              f"{name} must be a contiguous [n, bytes] plane")
+              lambda: f"{name} must be a contiguous [n, bytes] plane")
     else:
-        _need(t.is_contiguous(), f"{name} must be contiguous")
+        _need(t.is_contiguous(), lambda: f"{name} must be contiguous")
     return [(name, t)]
 
 
@@ -225,10 +226,12 @@ def _check_devices(named):
     for name, t in named:
         if t is None:
             continue
-        _need(t.device.type == "cuda", f"{name} must be on a CUDA device, got {t.device}")
+        d = t.device
         if dev is None:
-            dev = t.device
-        _need(t.device == dev, f"{name} is on {t.device}, the call's other tensors on {dev}")
+            _need(d.type == "cuda", lambda: f"{name} must be on a CUDA device, got {d}")
+            dev = d
+        else:
+            _need(d == dev, lambda: f"{name} is on {d}, the call's other tensors on {dev}")
 
 
 def _check_codec(codec, name="codec"):
@@ -243,53 +246,53 @@ def _check_codec(codec, name="codec"):
 def _check_codes(codes, codec, n_min, name="codes"):
     """Code planes of ``codec`` holding at least n_min records."""
     torch = _torch()
-    _need(isinstance(codes, Codes), f"{name} must be Codes")
+    _need(isinstance(codes, Codes), lambda: f"{name} must be Codes")
     n = codes.n
-    _need(n >= n_min, f"{name} holds {n} records, the call addresses {n_min}")
+    _need(n >= n_min, lambda: f"{name} holds {n} records, the call addresses {n_min}")
     out = _check_tensor(codes.idx, f"{name}.idx", dtype=torch.uint8, rows_contiguous=True)
-    _need(codes.idx.shape[1] >= codec.idx_stride, f"{name}.idx rows must hold >= {codec.idx_stride} bytes")
+    _need(codes.idx.shape[1] >= codec.idx_stride, lambda: f"{name}.idx rows must hold >= {codec.idx_stride} bytes")
     out += _check_tensor(codes.norms, f"{name}.norms", dtype=torch.int32, shape=(n,))
     if codec.m > 0:
-        _need(codes.sign is not None, f"{name}.sign is required (m = {codec.m})")
+        _need(codes.sign is not None, lambda: f"{name}.sign is required (m = {codec.m})")
         out += _check_tensor(codes.sign, f"{name}.sign", dtype=torch.uint8, rows_contiguous=True)
-        _need(codes.sign.shape[0] == n, f"{name}.sign must have {n} rows")
-        _need(codes.sign.shape[1] >= codec.sign_stride, f"{name}.sign rows must hold >= {codec.sign_stride} bytes")
+        _need(codes.sign.shape[0] == n, lambda: f"{name}.sign must have {n} rows")
+        _need(codes.sign.shape[1] >= codec.sign_stride, lambda: f"{name}.sign rows must hold >= {codec.sign_stride} bytes")
     return out
 
 
 def _check_polar_codes(codes, pc, n_min, name="codes"):
     torch = _torch()
-    _need(isinstance(codes, PolarCodes), f"{name} must be PolarCodes")
+    _need(isinstance(codes, PolarCodes), lambda: f"{name} must be PolarCodes")
     n = codes.n
-    _need(n >= n_min, f"{name} holds {n} records, the call addresses {n_min}")
+    _need(n >= n_min, lambda: f"{name} holds {n} records, the call addresses {n_min}")
     out = _check_tensor(codes.bits, f"{name}.bits", dtype=torch.uint8, rows_contiguous=True)
-    _need(codes.bits.shape[1] >= pc.stride, f"{name}.bits rows must hold >= {pc.stride} bytes")
+    _need(codes.bits.shape[1] >= pc.stride, lambda: f"{name}.bits rows must hold >= {pc.stride} bytes")
     out += _check_tensor(codes.norms, f"{name}.norms", dtype=torch.int32, shape=(n,))
     if pc.m > 0:
-        _need(codes.sign is not None, f"{name}.sign is required (m = {pc.m})")
+        _need(codes.sign is not None, lambda: f"{name}.sign is required (m = {pc.m})")
         out += _check_tensor(codes.sign, f"{name}.sign", dtype=torch.uint8, rows_contiguous=True)
-        _need(codes.sign.shape[0] == n, f"{name}.sign must have {n} rows")
-        _need(codes.sign.shape[1] >= pc.sign_stride, f"{name}.sign rows must hold >= {pc.sign_stride} bytes")
+        _need(codes.sign.shape[0] == n, lambda: f"{name}.sign must have {n} rows")
+        _need(codes.sign.shape[1] >= pc.sign_stride, lambda: f"{name}.sign rows must hold >= {pc.sign_stride} bytes")
     return out
 
 
 def _check_queries(q, d, name="q"):
     """fp32 [n_seq, hq, d], contiguous."""
     torch = _torch()
-    _need(isinstance(q, torch.Tensor) and q.dim() == 3 and q.shape[2] == d, f"{name} must be [n_seq, hq, {d}]")
+    _need(isinstance(q, torch.Tensor) and q.dim() == 3 and q.shape[2] == d, lambda: f"{name} must be [n_seq, hq, {d}]")
     return _check_tensor(q, name, dtype=torch.float32)
 
 
 def _check_heads(hq, hkv):
-    _need(hkv >= 1 and hq >= 1 and hq % hkv == 0, f"hq ({hq}) must be a positive multiple of hkv ({hkv})")
+    _need(hkv >= 1 and hq >= 1 and hq % hkv == 0, lambda: f"hq ({hq}) must be a positive multiple of hkv ({hkv})")
 
 
 def _check_rows(x, d, name="x"):
     """Rows [..., d] of fp32 / fp16 / bf16, each row contiguous."""
     torch = _torch()
-    _need(isinstance(x, torch.Tensor) and x.dim() >= 1 and x.shape[-1] == d, f"{name} must be [..., {d}]")
-    _need(str(x.dtype).replace("torch.", "") in _DT, f"{name} must be float32, float16 or bfloat16, got {x.dtype}")
-    _need(x.stride(-1) == 1 or x.shape[-1] == 1, f"{name} rows must be contiguous")
+    _need(isinstance(x, torch.Tensor) and x.dim() >= 1 and x.shape[-1] == d, lambda: f"{name} must be [..., {d}]")
+    _need(str(x.dtype).replace("torch.", "") in _DT, lambda: f"{name} must be float32, float16 or bfloat16, got {x.dtype}")
+    _need(x.stride(-1) == 1 or x.shape[-1] == 1, lambda: f"{name} rows must be contiguous")
     return [(name, x)]
 
 
@@ -560,7 +563,7 @@ def search_topk(codec: Codec, queries, db: Codes, n_db: int, k: int):
     """Top-k (index int64, score fp32) per query by estimated inner product."""
     torch = _torch()
     _need(isinstance(queries, torch.Tensor) and queries.dim() == 2 and queries.shape[1] == codec.d,
-          f"queries must be [n_q, {codec.d}]")
+          lambda: f"queries must be [n_q, {codec.d}]")
     named = _check_tensor(queries, "queries", dtype=torch.float32)
     n_q = queries.shape[0]
     _need(1 <= k <= 32 and k <= n_db, "k must be in 1 .. min(32, n_db)")
@@ -753,7 +756,7 @@ def polar_search_topk(pc: PolarCodec, queries, db: PolarCodes, n_db: int, k: int
     """Top-k (index int64, score fp32) per query by the polar estimate of <q, x>."""
     torch = _torch()
     _need(isinstance(queries, torch.Tensor) and queries.dim() == 2 and queries.shape[1] == pc.d,
-          f"queries must be [n_q, {pc.d}]")
+          lambda: f"queries must be [n_q, {pc.d}]")
     named = _check_tensor(queries, "queries", dtype=torch.float32)
     n_q = queries.shape[0]
     _need(1 <= k <= 32 and k <= n_db, "k must be in 1 .. min(32, n_db)")
