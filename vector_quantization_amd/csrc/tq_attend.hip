@@ -531,13 +531,13 @@ __global__ __launch_bounds__(256) void attend_combine(CombArgs a) {
 
 // ------------------------------------------------------------------ host side
 
-// Tokens per workgroup: as many as possible, up to 65536 (each workgroup builds the key tables
+// Tokens per workgroup: as many as possible, up to 131072 (each workgroup builds the key tables
 // once, and with one workgroup per CU those builds are not overlapped by another workgroup's
-// stream), as long as there are at least 512 workgroups (two per CU) when the context allows it.
+// stream), as long as there are at least 256 workgroups (one per CU) when the context allows it.
 static int att_chunk(const ScoreShape &s) {
   const int64_t pairs = s.n_seq * s.hkv;
-  int ch = 65536;
-  while (ch > 512 && pairs * ((s.n + ch - 1) / ch) < 512) ch /= 2;
+  int ch = 131072;
+  while (ch > 512 && pairs * ((s.n + ch - 1) / ch) < 256) ch /= 2;
   return ch;
 }
 
