@@ -531,17 +531,22 @@ __global__ __launch_bounds__(256) void attend_combine(CombArgs a) {
 
 // ------------------------------------------------------------------ host side
 
-// Tokens per workgroup: as many as possible, up to 131072 (each workgroup builds the key tables
-// once, and with one workgroup per CU those builds are not overlapped by another workgroup's
-// stream), as long as there are at least 256 workgroups (one per CU) when the context allows it.
+static int att_g(int g) { return g % 4 == 0 ? 4 : (g % 2 == 0 ? 2 : 1); }
+
+// Tokens per workgroup: as many as possible (each workgroup builds the key tables once), as long
+// as enough workgroups remain when the context allows it.  With four query heads per kv head the
+// tables take most of the LDS, one workgroup per CU, and nothing overlaps a workgroup's table
+// build: chunks of up to 131072 tokens while at least 256 workgroups (one per CU) remain.  With
+// fewer heads per workgroup, where several workgroups share a CU: up to 16384 tokens while at
+// least 512 remain.
 static int att_chunk(const ScoreShape &s) {
   const int64_t pairs = s.n_seq * s.hkv;
-  int ch = 131072;
-  while (ch > 512 && pairs * ((s.n + ch - 1) / ch) < 256) ch /= 2;
+  const bool one_per_cu = s.hkv > 0 && att_g(s.hq / s.hkv) == 4;
+  const int64_t min_wg = one_per_cu ? 256 : 512;
+  int ch = one_per_cu ? 131072 : 16384;
+  while (ch > 512 && pairs * ((s.n + ch - 1) / ch) < min_wg) ch /= 2;
   return ch;
 }
-
-static int att_g(int g) { return g % 4 == 0 ? 4 : (g % 2 == 0 ? 2 : 1); }
 
 size_t attend_workspace(const CodecView &kc, const CodecView &vc, const ScoreShape &s) {
   const int64_t nch = (s.n + att_chunk(s) - 1) / att_chunk(s);
