@@ -484,47 +484,95 @@ __device__ __forceinline__ float column_dot(const float *W, int64_t ld, int col,
   return acc;
 }
 
+// column_dot for H vectors at once: acc[h] = sum_i W[i * ld + col] v_h[i], i ascending (one FMA
+// chain per h, the same as column_dot's), each element of W requested once for all H.
+template <int N, int H>
+__device__ __forceinline__ void column_dot_n(const float *W, int64_t ld, int col, const float *const (&v)[H],
+                                             float (&acc)[H]) {
+  constexpr int B = 32;
+#pragma unroll 1
+  for (int i0 = 0; i0 < N; i0 += B) {
+    float w[B];
+#pragma unroll
+    for (int t = 0; t < B; ++t) w[t] = (i0 + t < N) ? W[(int64_t)(i0 + t) * ld + col] : 0.0f;
+#pragma unroll
+    for (int t = 0; t < B; ++t)
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+        if (i0 + t < N) acc[h] = fmaf(w[t], v[h][i0 + t], acc[h]);
+  }
+}
+
+// Four query heads per workgroup, one wavefront each: the chunks' states merged, S_V^T applied,
+// then Pi_V^T.  With one rotation for every head the workgroup applies Pi_V^T together: after a
+// barrier, wavefront w takes output columns w D/4 .. (w + 1) D/4 - 1 of all four heads, so each
+// element of Pi_V is read once per workgroup instead of once per head.
 template <int D, int VM>
 __global__ __launch_bounds__(256) void attend_combine(CombArgs a) {
   constexpr int NOUT = D + VM;
+  constexpr int CW = D / 4;         // output columns per wavefront in the shared product
+  constexpr int HPL = 4 * CW / kWave;  // heads per lane there
+  static_assert(D % 4 == 0 && kWave % CW == 0 && HPL >= 1, "columns over the lanes");
   __shared__ float av[4][NOUT];
   __shared__ float uv[4][D];
   const int lane = lane_id(), wid = threadIdx.x / kWave;
   const int64_t hidx = (int64_t)blockIdx.x * 4 + wid;
-  if (hidx >= a.n_heads) return;
-  const float *p = a.part + hidx * a.n_chunks * (int64_t)(2 + NOUT);
+  const bool shared_rot = !(a.n_rot > 1 && a.vecs_per_rot > 0);  // uniform over the grid
+  bool have = hidx < a.n_heads;  // uniform over the wavefront
+  const float *p = a.part + (have ? hidx : 0) * a.n_chunks * (int64_t)(2 + NOUT);
   float m = -INFINITY;
-  for (int c = lane; c < a.n_chunks; c += kWave) m = fmaxf(m, p[c * (2 + NOUT)]);
-  m = wave_max(m);
-  if (m == -INFINITY) {  // no cached token for this sequence: zero output
-    for (int k = lane; k < D; k += kWave) a.out[hidx * D + k] = 0.0f;
-    return;  // uniform over the wavefront
+  if (have) {
+    for (int c = lane; c < a.n_chunks; c += kWave) m = fmaxf(m, p[c * (2 + NOUT)]);
+    m = wave_max(m);
   }
-  float l = 0.0f;
-  for (int c = lane; c < a.n_chunks; c += kWave) l += exp2f(p[c * (2 + NOUT)] - m) * p[c * (2 + NOUT) + 1];
-  l = wave_sumf(l);
-  const float inv = 1.0f / l;
-  for (int o = lane; o < NOUT; o += kWave) {
-    float sacc = 0.0f;
-    for (int c = 0; c < a.n_chunks; ++c) sacc = fmaf(exp2f(p[c * (2 + NOUT)] - m), p[c * (2 + NOUT) + 2 + o], sacc);
-    av[wid][o] = sacc * inv;
+  have = have && m != -INFINITY;  // else no cached token for this sequence: zero output
+  if (have) {
+    float l = 0.0f;
+    for (int c = lane; c < a.n_chunks; c += kWave) l += exp2f(p[c * (2 + NOUT)] - m) * p[c * (2 + NOUT) + 1];
+    l = wave_sumf(l);
+    const float inv = 1.0f / l;
+    for (int o = lane; o < NOUT; o += kWave) {
+      float sacc = 0.0f;
+      for (int c = 0; c < a.n_chunks; ++c) sacc = fmaf(exp2f(p[c * (2 + NOUT)] - m), p[c * (2 + NOUT) + 2 + o], sacc);
+      av[wid][o] = sacc * inv;
+    }
+    wave_lds_fence();
+    // u = A_rot + S_V^T A_sk in the rotated space (A_sk already carries sqrt(pi/2)/m)
+    for (int i = lane; i < D; i += kWave) {
+      float u = av[wid][i];
+      if constexpr (VM > 0) u = column_dot<VM>(a.vsketch, D, i, &av[wid][D], u);
+      uv[wid][i] = u;
+    }
+  } else {
+    for (int i = lane; i < D; i += kWave) uv[wid][i] = 0.0f;  // Pi^T 0 = +0
   }
-  wave_lds_fence();
-  // u = A_rot + S_V^T A_sk in the rotated space (A_sk already carries sqrt(pi/2)/m)
-  for (int i = lane; i < D; i += kWave) {
-    float u = av[wid][i];
-    if constexpr (VM > 0) u = column_dot<VM>(a.vsketch, D, i, &av[wid][D], u);
-    uv[wid][i] = u;
+  if (shared_rot) {
+    __syncthreads();  // every wavefront's u is in LDS
+    const int col = wid * CW + lane % CW;
+    const int hg = lane / CW;  // heads hg HPL .. hg HPL + HPL - 1
+    const float *v[HPL];
+    float acc[HPL];
+#pragma unroll
+    for (int j = 0; j < HPL; ++j) {
+      v[j] = uv[hg * HPL + j];
+      acc[j] = 0.0f;
+    }
+    column_dot_n<D, HPL>(a.vrot, D, col, v, acc);  // (Pi^T u)_col
+#pragma unroll
+    for (int j = 0; j < HPL; ++j) {
+      const int64_t hj = (int64_t)blockIdx.x * 4 + hg * HPL + j;
+      if (hj < a.n_heads) a.out[hj * D + col] = acc[j];
+    }
+    return;
   }
+  if (hidx >= a.n_heads) return;  // uniform over the wavefront
   wave_lds_fence();
   const int64_t s = hidx / a.hq;
   const int h = (int)(hidx % a.hq);
   const int64_t blk = s * a.hkv + h / (a.hq / a.hkv);
   int64_t rid = 0;
-  if (a.n_rot > 1 && a.vecs_per_rot > 0) {
-    rid = (blk * a.n_ctx) / a.vecs_per_rot;
-    if (rid > a.n_rot - 1) rid = a.n_rot - 1;
-  }
+  rid = (blk * a.n_ctx) / a.vecs_per_rot;
+  if (rid > a.n_rot - 1) rid = a.n_rot - 1;
   const float *R = a.vrot + rid * (int64_t)D * D;
   for (int k = lane; k < D; k += kWave) a.out[hidx * D + k] = column_dot<D>(R, D, k, uv[wid], 0.0f);  // (Pi^T u)_k
 }
